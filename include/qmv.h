@@ -1,0 +1,203 @@
+/*
+ * qmv.h -- C ABI of the MI355X (gfx950) quantized decode matvec library.
+ *
+ * The library computes the decode hot path of llama.cpp-derived engines:
+ * small-batch matrix-vector products over block-quantized GGUF weights
+ * (Q8_0, q4_K, IQ4_XS) for 1..16 decode or speculative-verify tokens, and the
+ * expert-grouped MoE variant for up to 64 tokens (Castagna Veloce page,
+ * "Kernels for the MI50": i-quant MoE decode kernels for batches of up to 64
+ * tokens, and small-batch matvecs for K-quants, iq4_xs and Q8_0 with a split-K
+ * variant for 1 to 16 tokens).  Activations are quantized once to Q8 blocks
+ * and the same buffer is reused by every weight type and matrix (same page,
+ * "Fused operations": Q8 activations reused across weight types).  Weights are
+ * consumed in their compressed block form, never expanded (zhuai.tech GLM-5.3
+ * page, "Keep quantized weights compressed in memory").
+ *
+ * Conventions for every entry point
+ *   - W is n_rows x k (n_rows outputs, k the reduction length), rows stored
+ *     back to back in the GGUF block layout of its type, no padding:
+ *       Q8_0   : 34 B per 32 weights   (fp16 d, int8 q[32]),  w = d * q
+ *       q4_K   : 144 B per 256 weights (fp16 d, fp16 dmin, 12 B of packed
+ *                6-bit scale/min pairs, 128 B of nibbles),
+ *                w = d * sc_j * q - dmin * m_j for sub-block j of 32
+ *       IQ4_XS : 136 B per 256 weights (fp16 d, u16 scales_h, u8
+ *                scales_l[4], 128 B of 4-bit codebook indices),
+ *                w = d * (ls_j - 32) * CB[idx]
+ *   - All pointers except those documented as host pointers are DEVICE
+ *     pointers on the current HIP device.  The caller owns every buffer; the
+ *     library allocates nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  Every call only enqueues work on that stream and returns; it
+ *     never synchronizes.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns an error status and touches no memory.  A failed
+ *     launch returns QMV_ERR_HIP.  Device faults surface at the caller's next
+ *     synchronization.  No C++ exception crosses this interface.
+ *   - Calls on one stream are ordered; calls that share a workspace must not
+ *     run concurrently on different streams.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMV_ABI_VERSION 1
+
+typedef enum {
+  QMV_Q8_0 = 0,
+  QMV_Q4_K = 1,
+  QMV_IQ4_XS = 2
+} qmv_type;
+
+typedef enum {
+  QMV_OK = 0,
+  QMV_ERR_INVALID_ARG = 1, /* null pointer, bad size or stride, bad type  */
+  QMV_ERR_UNSUPPORTED = 2, /* valid but outside the supported token range */
+  QMV_ERR_MISALIGNED = 3,  /* a pointer breaks its documented alignment   */
+  QMV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required  */
+  QMV_ERR_HIP = 5          /* the HIP runtime reported an error           */
+} qmv_status;
+
+/* Limits of the decode path. */
+#define QMV_MAX_TOKENS 16       /* qmv_matvec: verify batches of 1..16     */
+#define QMV_MAX_MOE_TOKENS 64   /* qmv_moe_matvec: batches of 1..64 tokens */
+#define QMV_MAX_TOP_K 16
+#define QMV_MAX_EXPERTS 1024
+#define QMV_MAX_MOE_ROWS 65536  /* qmv_moe_matvec rows per expert           */
+#define QMV_MAX_MOE_K 16384     /* qmv_moe_matvec reduction length         */
+#define QMV_MAX_ACT_ROWS 65536  /* qmv_quantize_act rows per call          */
+
+int qmv_abi_version(void);
+const char* qmv_status_string(qmv_status status);
+
+/* Host-only size helpers: return 0 for invalid arguments. */
+size_t qmv_row_bytes(qmv_type type, int64_t k);
+
+/*
+ * Q8 activation buffer for n_tok rows of length k (k % 32 == 0), structure of
+ * arrays, each array 256-byte aligned relative to the buffer start:
+ *   offset 0                 : qs int8  [n_tok][k]      quantized values
+ *   qmv_act_offset_d(...)    : d  fp32  [n_tok][k/32]   block scales
+ *   qmv_act_offset_s(...)    : s  int32 [n_tok][k/32]   block sums of qs
+ * qmv_act_bytes() is the total size.  The buffer must be 256-byte aligned.
+ */
+size_t qmv_act_bytes(int64_t n_tok, int64_t k);
+size_t qmv_act_offset_d(int64_t n_tok, int64_t k);
+size_t qmv_act_offset_s(int64_t n_tok, int64_t k);
+
+/*
+ * qmv_quantize_act -- quantize activations to Q8 blocks of 32.
+ * Castagna Veloce page, "Fused operations" (Q8 activations made once and
+ * reused across weight types).  Per block of 32 values of a row:
+ *   amax = max |x|,  d = amax / 127 (fp32, correctly rounded),
+ *   q = x / d (fp32, correctly rounded) rounded half away from zero,
+ *       clamped to [-127, 127],   s = sum of q;
+ *   an all-zero block gives d = 0, q = 0, s = 0.
+ * x   : fp32 [n_tok][ldx] (device), 4-byte aligned, ldx >= k, finite values.
+ * xq  : activation buffer of qmv_act_bytes(n_tok, k) bytes (device, 256-byte
+ *       aligned); fully overwritten.
+ * 1 <= n_tok <= QMV_MAX_ACT_ROWS, k > 0, k % 32 == 0.
+ */
+qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, int64_t k, void* xq,
+                            void* stream);
+
+/*
+ * qmv_matvec -- y[t][n] = sum_k W[n][k] * xq[t][k] for t < n_tok.
+ * Castagna Veloce page, "Kernels for the MI50" (small-batch matvecs for 1 to
+ * 16 tokens, Q8_0 with a split-K variant); zhuai.tech GLM-5.3 page, "A single
+ * decode row is not a large matrix multiplication".
+ * Per 32-weight block the weights and activations meet in an exact integer
+ * dot product; the fp16 weight scales and fp32 activation scales are applied
+ * to that integer in fp32 and accumulated in fp32 (any order).
+ * w    : n_rows x k weights of `type` (device, 16-byte aligned).
+ * xq   : activation buffer made by qmv_quantize_act for (n_tok, k) (device).
+ * y    : fp32 [n_tok][ldy] (device, 4-byte aligned), ldy >= n_rows; columns
+ *        0..n_rows-1 of each row are overwritten, the rest are untouched.
+ * ws   : optional workspace (device, 256-byte aligned) enabling the split-K
+ *        path for few-row long-K shapes; NULL runs the single-pass kernel.
+ *        It must hold qmv_matvec_workspace_bytes(type, n_rows, k, n_tok)
+ *        bytes, be zero-filled once when allocated, and is left in that state
+ *        by every completed call (its counters reset themselves).  One
+ *        workspace may serve calls of different shapes, each needing no more
+ *        than its size, as long as those calls do not overlap in time.
+ * 1 <= n_tok <= QMV_MAX_TOKENS (else QMV_ERR_UNSUPPORTED); n_rows >= 1;
+ * k a positive multiple of 32 (Q8_0) or 256 (q4_K, IQ4_XS).
+ */
+size_t qmv_matvec_workspace_bytes(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok);
+qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int64_t k, const void* xq,
+                      int64_t n_tok, float* y, int64_t ldy, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * qmv_moe_matvec -- expert-grouped routed matvec.
+ * Castagna Veloce page, "Kernels for the MI50" (i-quant MoE decode kernels
+ * for batches of up to 64 tokens; expert-grouped quantized MoE: each active
+ * expert's weights are read once for all the tokens routed to it).
+ * w        : n_experts matrices of n_rows x k, back to back (device,
+ *            16-byte aligned).
+ * xq       : activation buffer with n_tok rows (x_per_slot = 0, e.g. the
+ *            gate/up input shared by a token's slots) or n_tok*top_k rows,
+ *            row t*top_k + s for slot s of token t (x_per_slot = 1, e.g. the
+ *            down-projection input of each slot).
+ * ids      : int32 [n_tok][top_k] expert of each slot (device).  An id
+ *            outside [0, n_experts) drops that slot: it contributes zero.
+ * route_w  : NULL, or fp32 [n_tok][top_k] routing weights (device).
+ * y        : route_w == NULL -> fp32 [n_tok][top_k][n_rows], one output row
+ *            per slot (dropped slots get zeros);
+ *            route_w != NULL -> fp32 [n_tok][n_rows],
+ *            y[t] = sum over valid slots s of route_w[t][s] * (W[ids[t][s]] x),
+ *            summed in slot order.
+ * ws       : workspace of qmv_moe_workspace_bytes(...) bytes (device,
+ *            256-byte aligned, zero-filled once when allocated; completed
+ *            calls leave its counters at zero; calls of different shapes may
+ *            share it if they do not overlap in time).  After a call, the
+ *            int32 at offset 0 holds the number of dropped slots of that call.
+ * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, 1 <= top_k <= QMV_MAX_TOP_K,
+ * 1 <= n_experts <= QMV_MAX_EXPERTS, n_rows <= QMV_MAX_MOE_ROWS and
+ * k <= QMV_MAX_MOE_K (else QMV_ERR_UNSUPPORTED); k as for qmv_matvec.
+ */
+size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows, int64_t k,
+                               int64_t n_tok, int64_t top_k);
+qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows,
+                          int64_t k, const void* xq, int x_per_slot, const int32_t* ids,
+                          const float* route_w, int64_t n_tok, int64_t top_k, float* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qmv_block_dots -- test hook: the exact integer partial of every 32-weight
+ * block, computed by the same device decode and dot routines as qmv_matvec.
+ * out : int32 [n_tok][n_rows][k/32][c] (device), c = 2 for q4_K
+ *       (A = sc_j * sum q*qx, B = m_j * s_b) and c = 1 otherwise
+ *       (Q8_0: sum qw*qx; IQ4_XS: (ls_j - 32) * sum CB[idx]*qx).
+ * 1 <= n_tok <= QMV_MAX_TOKENS.
+ */
+qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t k,
+                          const void* xq, int64_t n_tok, int32_t* out, void* stream);
+
+/*
+ * qmv_set_tuning -- process-wide A/B switches (Castagna Veloce page, "New
+ * features": each optimization can be switched off for A/B tests).  Keys:
+ *   "splitk"  : -1 automatic (default), 0 never, n >= 1 force n K-slices
+ *               whenever a workspace is given;
+ *   "variant" : -1 automatic (default), else an index into the kernel
+ *               variant table of qmv_matvec (see qmv_variant_name).
+ * The environment variables QMV_SPLITK and QMV_VARIANT set the same switches
+ * when the library loads.  Returns QMV_ERR_INVALID_ARG for an unknown key or
+ * value.
+ */
+qmv_status qmv_set_tuning(const char* key, int64_t value);
+/* Name of kernel variant `index`, or NULL past the end of the table. */
+const char* qmv_variant_name(int64_t index);
+/* The variant qmv_matvec would run for these arguments (-1 if invalid). */
+int64_t qmv_pick_variant(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

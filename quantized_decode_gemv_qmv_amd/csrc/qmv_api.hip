@@ -1,0 +1,323 @@
+// qmv_api.hip -- host side of the C ABI declared in include/qmv.h:
+// argument validation (before anything is enqueued), kernel-variant and
+// split-K choice, workspace layout, size queries and status strings.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "qmv_internal.h"
+#include "qmv.h"
+
+#define QMV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace qmv;
+
+constexpr int64_t kSplitMaxRows = 8192;   // split-K only for few-row shapes
+constexpr int kMaxSlices = 32;
+constexpr int64_t kMoeMaxUnits = 512;     // k <= 16384 for the MoE kernel
+
+std::atomic<int64_t> g_splitk{-1};
+std::atomic<int64_t> g_variant{-1};
+
+struct EnvInit {
+  EnvInit() {
+    if (const char* v = std::getenv("QMV_SPLITK")) {
+      if (!std::strcmp(v, "auto")) g_splitk = -1;
+      else if (!std::strcmp(v, "off")) g_splitk = 0;
+      else g_splitk = std::atoll(v);
+    }
+    if (const char* v = std::getenv("QMV_VARIANT")) g_variant = std::atoll(v);
+  }
+} g_env_init;
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+bool valid_type(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS; }
+
+int64_t block_k(int t) { return t == QMV_Q8_0 ? 32 : 256; }
+int64_t block_bytes(int t) { return t == QMV_Q8_0 ? 34 : (t == QMV_Q4_K ? 144 : 136); }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+ActView act_view(const void* xq, int64_t n_tok, int64_t k) {
+  const uint8_t* b = static_cast<const uint8_t*>(xq);
+  ActView v;
+  v.qs = reinterpret_cast<const int8_t*>(b);
+  v.d = reinterpret_cast<const float*>(b + qmv_act_offset_d(n_tok, k));
+  v.s = reinterpret_cast<const int32_t*>(b + qmv_act_offset_s(n_tok, k));
+  v.k = static_cast<int>(k);
+  v.nb = static_cast<int>(k / 32);
+  return v;
+}
+
+qmv_status check_weights(int type, const void* w, int64_t n_rows, int64_t k) {
+  if (!valid_type(type) || w == nullptr || n_rows < 1 || k < 1 || k % block_k(type) != 0)
+    return QMV_ERR_INVALID_ARG;
+  if (n_rows > INT32_MAX / 4 || k / 32 > INT32_MAX / 64) return QMV_ERR_INVALID_ARG;
+  if (!aligned(w, 16)) return QMV_ERR_MISALIGNED;
+  return QMV_OK;
+}
+
+int pick_lpr(int64_t units) { return units >= 256 ? 64 : (units >= 96 ? 32 : 16); }
+
+int variant_index(int lpr, int rows) {
+  for (int i = 0; i < kNumVariants; ++i)
+    if (kVariants[i].lpr == lpr && kVariants[i].rows == rows) return i;
+  return 0;
+}
+
+int auto_variant(int, int64_t n_rows, int64_t k, int64_t n_tok) {
+  const int64_t units = k / 32;
+  const int lpr = pick_lpr(units);
+  int rows = n_tok <= 4 ? 2 : 1;
+  // keep at least ~4 waves per compute unit before doubling rows per group
+  const int64_t waves_r2 = (n_rows + 2 * (64 / lpr) - 1) / (2 * (64 / lpr));
+  if (waves_r2 < 4 * device_cus()) rows = 1;
+  return variant_index(lpr, rows);
+}
+
+int choose_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
+  const int64_t forced = g_variant.load();
+  if (forced >= 0 && forced < kNumVariants) return static_cast<int>(forced);
+  return auto_variant(type, n_rows, k, n_tok);
+}
+
+int choose_slices(const Variant& v, int64_t n_rows, int64_t k) {
+  const int64_t units = k / 32;
+  const int64_t forced = g_splitk.load();
+  if (forced == 0) return 1;
+  const int64_t max_by_units = units / v.lpr;  // >= one unit per lane per slice
+  int64_t s;
+  if (forced > 0) {
+    s = forced;
+  } else {
+    const int64_t waves = (n_rows + (64 / v.lpr) * v.rows - 1) / ((64 / v.lpr) * v.rows);
+    const int64_t want = 8 * static_cast<int64_t>(device_cus());  // ~8 waves per CU
+    if (waves >= want / 2 || units < 4 * v.lpr) return 1;
+    s = (want + waves - 1) / waves;
+    s = s > units / (2 * v.lpr) ? units / (2 * v.lpr) : s;  // >= two units per lane
+  }
+  if (s > max_by_units) s = max_by_units;
+  if (s > kMaxSlices) s = kMaxSlices;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
+
+// Split-K workspace: [one counter per row tile][partials slices x T x N].
+// The counter area has a fixed size (every variant covers >= 4 rows per
+// workgroup, and split-K is limited to kSplitMaxRows rows), so calls of
+// different shapes can share one workspace: a call's partials never land on
+// the counters of another.
+constexpr int64_t kSplitCounterBytes = kSplitMaxRows;  // kSplitMaxRows / 4 ints
+
+// MoE workspace: [256 B status][counters of kMoeMaxRows / 4 row tiles][per-slot
+// outputs], fixed offsets for the same reason.
+constexpr int64_t kMoeMaxRows = 65536;
+constexpr int64_t kMoeStatusBytes = 256;
+constexpr int64_t kMoeCounterBytes = kMoeMaxRows;  // kMoeMaxRows / 4 ints
+constexpr int64_t kMoePartOffset = kMoeStatusBytes + kMoeCounterBytes;
+
+}  // namespace
+
+// ------------------------------------------------------------------ misc
+QMV_API int qmv_abi_version(void) { return QMV_ABI_VERSION; }
+
+QMV_API const char* qmv_status_string(qmv_status st) {
+  switch (st) {
+    case QMV_OK: return "QMV_OK";
+    case QMV_ERR_INVALID_ARG: return "QMV_ERR_INVALID_ARG: invalid argument";
+    case QMV_ERR_UNSUPPORTED: return "QMV_ERR_UNSUPPORTED: outside the supported range";
+    case QMV_ERR_MISALIGNED: return "QMV_ERR_MISALIGNED: pointer alignment";
+    case QMV_ERR_WORKSPACE: return "QMV_ERR_WORKSPACE: workspace missing or too small";
+    case QMV_ERR_HIP: return "QMV_ERR_HIP: HIP runtime error";
+    default: return "unknown qmv status";
+  }
+}
+
+QMV_API size_t qmv_row_bytes(qmv_type type, int64_t k) {
+  if (!valid_type(type) || k < 1 || k % block_k(type)) return 0;
+  return static_cast<size_t>(k / block_k(type) * block_bytes(type));
+}
+
+QMV_API size_t qmv_act_offset_d(int64_t n_tok, int64_t k) {
+  if (n_tok < 1 || k < 1 || k % 32) return 0;
+  return static_cast<size_t>(align256(n_tok * k));
+}
+QMV_API size_t qmv_act_offset_s(int64_t n_tok, int64_t k) {
+  if (n_tok < 1 || k < 1 || k % 32) return 0;
+  return static_cast<size_t>(align256(n_tok * k) + align256(n_tok * (k / 32) * 4));
+}
+QMV_API size_t qmv_act_bytes(int64_t n_tok, int64_t k) {
+  if (n_tok < 1 || k < 1 || k % 32) return 0;
+  return static_cast<size_t>(align256(n_tok * k) + 2 * align256(n_tok * (k / 32) * 4));
+}
+
+QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
+  if (key == nullptr) return QMV_ERR_INVALID_ARG;
+  if (!std::strcmp(key, "splitk")) {
+    if (value < -1) return QMV_ERR_INVALID_ARG;
+    g_splitk = value;
+    return QMV_OK;
+  }
+  if (!std::strcmp(key, "variant")) {
+    if (value < -1 || value >= kNumVariants) return QMV_ERR_INVALID_ARG;
+    g_variant = value;
+    return QMV_OK;
+  }
+  return QMV_ERR_INVALID_ARG;
+}
+
+QMV_API const char* qmv_variant_name(int64_t index) {
+  return (index >= 0 && index < kNumVariants) ? kVariants[index].name : nullptr;
+}
+
+QMV_API int64_t qmv_pick_variant(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok) {
+  if (!valid_type(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
+      n_tok > QMV_MAX_TOKENS)
+    return -1;
+  return choose_variant(type, n_rows, k, n_tok);
+}
+
+// ------------------------------------------------------------- quantize
+QMV_API qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, int64_t k,
+                                    void* xq, void* stream) {
+  if (x == nullptr || xq == nullptr || n_tok < 1 || k < 1 || k % 32 || ldx < k)
+    return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_ACT_ROWS || k > (int64_t)1 << 24) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(x, 4) || !aligned(xq, 256)) return QMV_ERR_MISALIGNED;
+  uint8_t* b = static_cast<uint8_t*>(xq);
+  hipError_t e = launch_quantize(x, ldx, static_cast<int>(n_tok), static_cast<int>(k),
+                                 reinterpret_cast<int8_t*>(b),
+                                 reinterpret_cast<float*>(b + qmv_act_offset_d(n_tok, k)),
+                                 reinterpret_cast<int32_t*>(b + qmv_act_offset_s(n_tok, k)),
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
+// --------------------------------------------------------------- matvec
+QMV_API size_t qmv_matvec_workspace_bytes(qmv_type type, int64_t n_rows, int64_t k,
+                                          int64_t n_tok) {
+  if (!valid_type(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
+      n_tok > QMV_MAX_TOKENS)
+    return 0;
+  if (n_rows > kSplitMaxRows) return 0;  // never split: no workspace needed
+  return static_cast<size_t>(kSplitCounterBytes +
+                             align256(int64_t(kMaxSlices) * n_tok * n_rows * 4));
+}
+
+QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int64_t k,
+                              const void* xq, int64_t n_tok, float* y, int64_t ldy, void* ws,
+                              size_t ws_bytes, void* stream) {
+  qmv_status st = check_weights(type, w, n_rows, k);
+  if (st != QMV_OK) return st;
+  if (xq == nullptr || y == nullptr || ldy < n_rows || n_tok < 1) return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_TOKENS) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(xq, 256) || !aligned(y, 4)) return QMV_ERR_MISALIGNED;
+  MatvecLaunch a{};
+  a.fmt = type;
+  a.w = static_cast<const uint8_t*>(w);
+  a.row_bytes = static_cast<int64_t>(qmv_row_bytes(type, k));
+  a.n_rows = static_cast<int>(n_rows);
+  a.units = static_cast<int>(k / 32);
+  a.x = act_view(xq, n_tok, k);
+  a.n_tok = static_cast<int>(n_tok);
+  a.y = y;
+  a.ldy = ldy;
+  a.variant = choose_variant(type, n_rows, k, n_tok);
+  a.slices = 1;
+  const size_t need = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok);
+  if (ws != nullptr && need > 0) {
+    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return QMV_ERR_MISALIGNED;
+    a.slices = choose_slices(kVariants[a.variant], n_rows, k);
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    a.cnt = reinterpret_cast<int*>(b);
+    a.part = reinterpret_cast<float*>(b + kSplitCounterBytes);
+  }
+  hipError_t e = launch_matvec(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
+QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t k,
+                                  const void* xq, int64_t n_tok, int32_t* out, void* stream) {
+  qmv_status st = check_weights(type, w, n_rows, k);
+  if (st != QMV_OK) return st;
+  if (xq == nullptr || out == nullptr || n_tok < 1) return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_TOKENS) return QMV_ERR_UNSUPPORTED;
+  if (n_tok * n_rows * (k / 32) > INT32_MAX) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(xq, 256) || !aligned(out, 4)) return QMV_ERR_MISALIGNED;
+  hipError_t e = launch_block_dots(type, static_cast<const uint8_t*>(w),
+                                   static_cast<int64_t>(qmv_row_bytes(type, k)),
+                                   static_cast<int>(n_rows), static_cast<int>(k / 32),
+                                   act_view(xq, n_tok, k), static_cast<int>(n_tok), out,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ MoE
+QMV_API size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows,
+                                       int64_t k, int64_t n_tok, int64_t top_k) {
+  if (!valid_type(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
+      n_tok > QMV_MAX_MOE_TOKENS || top_k < 1 || top_k > QMV_MAX_TOP_K || n_experts < 1 ||
+      n_experts > QMV_MAX_EXPERTS || k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows)
+    return 0;
+  return static_cast<size_t>(kMoePartOffset + align256(n_tok * top_k * n_rows * 4));
+}
+
+QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts,
+                                  int64_t n_rows, int64_t k, const void* xq, int x_per_slot,
+                                  const int32_t* ids, const float* route_w, int64_t n_tok,
+                                  int64_t top_k, float* y, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  qmv_status st = check_weights(type, w, n_rows, k);
+  if (st != QMV_OK) return st;
+  if (xq == nullptr || ids == nullptr || y == nullptr || ws == nullptr || n_tok < 1 ||
+      top_k < 1 || n_experts < 1 || (x_per_slot != 0 && x_per_slot != 1))
+    return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_MOE_TOKENS || top_k > QMV_MAX_TOP_K || n_experts > QMV_MAX_EXPERTS ||
+      k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows)
+    return QMV_ERR_UNSUPPORTED;
+  if (n_experts * n_rows > INT32_MAX) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(xq, 256) || !aligned(ids, 4) || !aligned(y, 4) ||
+      (route_w != nullptr && !aligned(route_w, 4)) || !aligned(ws, 256))
+    return QMV_ERR_MISALIGNED;
+  const size_t need = qmv_moe_workspace_bytes(type, n_experts, n_rows, k, n_tok, top_k);
+  if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+  const int64_t x_rows = x_per_slot ? n_tok * top_k : n_tok;
+  MoeLaunch a{};
+  a.fmt = type;
+  a.w = static_cast<const uint8_t*>(w);
+  a.row_bytes = static_cast<int64_t>(qmv_row_bytes(type, k));
+  a.n_experts = static_cast<int>(n_experts);
+  a.n_rows = static_cast<int>(n_rows);
+  a.units = static_cast<int>(k / 32);
+  a.x = act_view(xq, x_rows, k);
+  a.x_per_slot = x_per_slot;
+  a.ids = ids;
+  a.rw = route_w;
+  a.n_tok = static_cast<int>(n_tok);
+  a.top_k = static_cast<int>(top_k);
+  a.y = y;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  a.err = reinterpret_cast<int*>(b);
+  a.cnt = reinterpret_cast<int*>(b + kMoeStatusBytes);
+  a.part = reinterpret_cast<float*>(b + kMoePartOffset);
+  hipError_t e = launch_moe(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}

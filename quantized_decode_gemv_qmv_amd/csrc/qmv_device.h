@@ -1,0 +1,287 @@
+// qmv_device.h -- gfx950 device routines shared by the qmv kernels: block
+// field decoders, per-unit weight loads, integer dot products and lane
+// reductions.
+//
+// Work unit.  Every kernel walks a weight row in "units" of 32 weights, which
+// is one Q8_0 block or one eighth of a q4_K / IQ4_XS super-block.  A unit is
+// decoded into eight dwords of int8 weights, q[0..3] and q[4..7], that meet
+// sixteen activation bytes each in v_dot4 integer dot products:
+//   Q8_0   : block b               q[0..3] = w[0..15],  q[4..7] = w[16..31]
+//   IQ4_XS : sub-block c of sb     q[0..3] = idx low nibbles  -> w[0..15]
+//                                  q[4..7] = idx high nibbles -> w[16..31]
+//   q4_K   : 16 quant bytes c of sb (bytes 16c..16c+15 of the nibble area):
+//            low nibbles are weights 16h..16h+15 (h = c & 1) of sub-block
+//            j = 2 (c >> 1), high nibbles the same positions of sub-block j+1.
+// So one 16-byte quant load per lane feeds one unit, and the eight lanes of a
+// super-block read its 128 quant bytes as one contiguous 128-byte span.
+// (GGUF block layouts; the pages name the formats only -- Castagna Veloce
+// page, "Kernels for the MI50"; zhuai.tech GLM-5.3 page, "A single decode row
+// is not a large matrix multiplication".)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2 };
+
+template <int F> struct Fmt;
+template <> struct Fmt<FQ8_0> { static constexpr int QK = 32, BB = 34, UPB = 1; };
+template <> struct Fmt<FQ4_K> { static constexpr int QK = 256, BB = 144, UPB = 8; };
+template <> struct Fmt<FIQ4_XS> { static constexpr int QK = 256, BB = 136, UPB = 8; };
+
+// 16- and 8-byte vectors that only promise 4-byte alignment: gfx950 global
+// loads of several dwords need dword alignment only.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+
+// Weights are streamed once per call: load them non-temporally so they do
+// not evict the activations and headers that every row reuses.
+__device__ __forceinline__ u32x4 ld_w16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld_w8(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ uint32_t ld_w2(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(h16 & 0xFFFFu)));
+}
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+// ------------------------------------------------------------ raw unit loads
+template <int F> struct Raw;
+
+// Q8_0 blocks are 34 bytes, so a block starts at an address that is 0 or 2
+// mod 4.  At 0 mod 4 the block is read as 16 + 16 + 2 bytes and the quants
+// are realigned by two bytes; at 2 mod 4 the quants themselves are dword
+// aligned and the scale is a separate 2-byte load.  Neither form reads a byte
+// outside the block.
+template <> struct Raw<FQ8_0> {
+  u32x4 a, b;
+  uint32_t h;
+  uint32_t odd;
+};
+template <> struct Raw<FQ4_K> {
+  u32x4 q;    // 16 quant bytes of the unit
+  u32x4 hdr;  // d | dmin, S[0..3], S[4..7], S[8..11]
+};
+template <> struct Raw<FIQ4_XS> {
+  u32x4 q;    // 16 quant bytes of the unit (= one sub-block)
+  u32x2 hdr;  // d | scales_h, scales_l[0..3]
+};
+
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ8_0>& r) {
+  const uint8_t* p = row + 34 * u;
+  const uint32_t odd = (reinterpret_cast<uintptr_t>(p) >> 1) & 1u;
+  const uint8_t* base = odd ? p + 2 : p;
+  r.a = ld_w16(base);
+  r.b = ld_w16(base + 16);
+  r.h = ld_w2(odd ? p : p + 32);
+  r.odd = odd;
+}
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ4_K>& r) {
+  const uint8_t* blk = row + 144 * (u >> 3);
+  r.q = ld_w16(blk + 16 + 16 * (u & 7));
+  r.hdr = ld_w16(blk);
+}
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FIQ4_XS>& r) {
+  const uint8_t* blk = row + 136 * (u >> 3);
+  r.q = ld_w16(blk + 8 + 16 * (u & 7));
+  r.hdr = ld_w8(blk);
+}
+
+// --------------------------------------------------------------- decoding
+template <int F> struct Dec;
+
+template <> struct Dec<FQ8_0> {
+  uint32_t q[8];
+  float d;
+};
+template <> struct Dec<FIQ4_XS> {
+  uint32_t q[8];
+  float d;
+  int ls;  // effective sub-block scale, raw 6-bit value minus 32
+};
+template <> struct Dec<FQ4_K> {
+  uint32_t q[8];  // nibble values 0..15, one per byte
+  float d, dmin;
+  int sc0, sc1, m0, m1;  // sub-blocks j and j+1
+  int h;                 // which 16-weight half of the sub-blocks
+};
+
+__device__ __forceinline__ void decode_unit(const Raw<FQ8_0>& r, int, Dec<FQ8_0>& o) {
+  const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.h};
+  const uint32_t sh = r.odd ? 0u : 2u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.q[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], sh);
+  o.d = half_bits_to_float(r.odd ? r.h : r.a.x);
+}
+
+// IQ4_XS non-linear codebook, index -> int8 value, packed four per dword.
+constexpr uint32_t pk4(int a, int b, int c, int d) {
+  return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
+         ((uint32_t)(uint8_t)d << 24);
+}
+constexpr uint32_t IQ4_CB0 = pk4(-127, -104, -83, -65);
+constexpr uint32_t IQ4_CB1 = pk4(-49, -35, -22, -10);
+constexpr uint32_t IQ4_CB2 = pk4(1, 13, 25, 38);
+constexpr uint32_t IQ4_CB3 = pk4(53, 69, 89, 113);
+
+// Four 4-bit indices (one per byte, 0..15) -> four int8 codebook values with
+// three byte permutes: entries 0..7 and 8..15 are looked up by the low three
+// index bits, then bit 3 picks between the two results byte by byte.
+__device__ __forceinline__ uint32_t iq4_lookup(uint32_t n) {
+  const uint32_t sel = n & 0x07070707u;
+  const uint32_t lo = __builtin_amdgcn_perm(IQ4_CB1, IQ4_CB0, sel);
+  const uint32_t hi = __builtin_amdgcn_perm(IQ4_CB3, IQ4_CB2, sel);
+  const uint32_t pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
+  return __builtin_amdgcn_perm(hi, lo, pick);
+}
+
+__device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FIQ4_XS>& o) {
+  const int c = u & 7;
+  const uint32_t lo4 = (r.hdr.y >> (4 * c)) & 15u;            // scales_l nibble
+  const uint32_t hi2 = (r.hdr.x >> (16 + 2 * c)) & 3u;        // scales_h bits
+  o.ls = static_cast<int>(lo4 | (hi2 << 4)) - 32;
+  o.d = half_bits_to_float(r.hdr.x);
+  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.q[i] = iq4_lookup(v[i] & 0x0F0F0F0Fu);
+    o.q[4 + i] = iq4_lookup((v[i] >> 4) & 0x0F0F0F0Fu);
+  }
+}
+
+__device__ __forceinline__ uint32_t bfe(uint32_t v, uint32_t off, uint32_t w) {
+  return __builtin_amdgcn_ubfe(v, off, w);
+}
+
+// 6-bit scale and min of sub-block j from S[0..11] held in three dwords.
+__device__ __forceinline__ void q4k_scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
+                                              int& sc, int& m) {
+  const uint32_t jj = 8u * (j & 3);
+  const uint32_t sc_lo = bfe(s03, jj, 6), m_lo = bfe(s47, jj, 6);
+  const uint32_t sc_hi = bfe(s811, jj, 4) | (bfe(s03, jj + 6, 2) << 4);
+  const uint32_t m_hi = bfe(s811, jj + 4, 4) | (bfe(s47, jj + 6, 2) << 4);
+  sc = static_cast<int>(j < 4 ? sc_lo : sc_hi);
+  m = static_cast<int>(j < 4 ? m_lo : m_hi);
+}
+
+__device__ __forceinline__ void decode_unit(const Raw<FQ4_K>& r, int u, Dec<FQ4_K>& o) {
+  const int c = u & 7;
+  const int j = 2 * (c >> 1);
+  o.h = c & 1;
+  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, j, o.sc0, o.m0);
+  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, j + 1, o.sc1, o.m1);
+  o.d = half_bits_to_float(r.hdr.x);
+  o.dmin = half_bits_to_float(r.hdr.x >> 16);
+  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.q[i] = v[i] & 0x0F0F0F0Fu;
+    o.q[4 + i] = (v[i] >> 4) & 0x0F0F0F0Fu;
+  }
+}
+
+// ----------------------------------------------------- activation fragments
+// View of a Q8 activation buffer (structure of arrays, see qmv.h).
+struct Act {
+  const int8_t* qs;   // [rows][k]
+  const float* d;     // [rows][k/32]
+  const int32_t* s;   // [rows][k/32]
+  int k, nb;
+};
+
+// The 32 activation bytes a unit meets, as two 16-byte halves, plus scales.
+template <int F> struct XFrag {
+  u32x4 a, b;
+  float d0, d1;
+  int s0, s1;
+};
+
+template <int F>
+__device__ __forceinline__ void load_xfrag(const Act& x, int row, int u, XFrag<F>& f) {
+  if constexpr (F == FQ4_K) {
+    const int jb = 8 * (u >> 3) + 2 * ((u & 7) >> 1);  // 32-block of the low nibbles
+    const int8_t* p = x.qs + (int64_t)row * x.k + 32 * jb + 16 * (u & 1);
+    f.a = ld16(p);
+    f.b = ld16(p + 32);
+    const int64_t o = (int64_t)row * x.nb + jb;
+    f.d0 = x.d[o];
+    f.d1 = x.d[o + 1];
+    if ((u & 1) == 0) {
+      f.s0 = x.s[o];
+      f.s1 = x.s[o + 1];
+    } else {
+      f.s0 = 0;
+      f.s1 = 0;
+    }
+  } else {
+    const int8_t* p = x.qs + (int64_t)row * x.k + 32 * u;
+    f.a = ld16(p);
+    f.b = ld16(p + 16);
+    f.d0 = x.d[(int64_t)row * x.nb + u];
+    f.d1 = 0.f;
+    f.s0 = f.s1 = 0;
+  }
+}
+
+// Integer halves of one unit against one activation fragment:
+// lo = sum over q[0..3], hi = sum over q[4..7].
+template <int F>
+__device__ __forceinline__ void unit_int(const Dec<F>& w, const XFrag<F>& x, int& lo, int& hi) {
+  int a = 0, b = 0;
+  a = dot4(w.q[0], x.a.x, a);
+  a = dot4(w.q[1], x.a.y, a);
+  a = dot4(w.q[2], x.a.z, a);
+  a = dot4(w.q[3], x.a.w, a);
+  b = dot4(w.q[4], x.b.x, b);
+  b = dot4(w.q[5], x.b.y, b);
+  b = dot4(w.q[6], x.b.z, b);
+  b = dot4(w.q[7], x.b.w, b);
+  lo = a;
+  hi = b;
+}
+
+// fp32 contribution of one unit: the exact integer partial times the weight
+// and activation scales.
+__device__ __forceinline__ float unit_value(const Dec<FQ8_0>& w, const XFrag<FQ8_0>& x) {
+  int lo, hi;
+  unit_int(w, x, lo, hi);
+  return (w.d * x.d0) * static_cast<float>(lo + hi);
+}
+__device__ __forceinline__ float unit_value(const Dec<FIQ4_XS>& w, const XFrag<FIQ4_XS>& x) {
+  int lo, hi;
+  unit_int(w, x, lo, hi);
+  return (w.d * x.d0) * static_cast<float>(w.ls * (lo + hi));
+}
+__device__ __forceinline__ float unit_value(const Dec<FQ4_K>& w, const XFrag<FQ4_K>& x) {
+  int lo, hi;
+  unit_int(w, x, lo, hi);
+  const float pos = x.d0 * static_cast<float>(w.sc0 * lo) + x.d1 * static_cast<float>(w.sc1 * hi);
+  // the min term of a sub-block is counted once, by the h == 0 half
+  const float neg = x.d0 * static_cast<float>(w.m0 * x.s0) + x.d1 * static_cast<float>(w.m1 * x.s1);
+  return w.d * pos - w.dmin * neg;
+}
+
+// ------------------------------------------------------------- reductions
+// Sum over the LPR consecutive lanes of a lane group (LPR a power of two).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace qmv

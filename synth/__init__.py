@@ -175,13 +175,13 @@ def pack_q8_0(d: np.ndarray, q: np.ndarray) -> np.ndarray:
     return out.reshape(n, nb * 34)
 
 
-def pack_q4_k(d, dmin, sc, m, q) -> np.ndarray:
-    """d, dmin fp16 [N][S]; sc, m uint8 [N][S][8] in 0..63; q uint8 [N][K] in 0..15."""
-    n, k = q.shape
-    ns = k // 256
-    sc = sc.astype(np.uint8)
-    m = m.astype(np.uint8)
-    out = np.zeros((n, ns, 144), dtype=np.uint8)
+def q4_k_header(d, dmin, sc, m) -> np.ndarray:
+    """First 16 bytes of each q4_K super-block: fp16 d, fp16 dmin, 12 bytes of
+    packed 6-bit (scale, min) pairs.  d, dmin [N][S]; sc, m [N][S][8]."""
+    n, ns = np.shape(d)
+    sc = np.asarray(sc).astype(np.uint8)
+    m = np.asarray(m).astype(np.uint8)
+    out = np.zeros((n, ns, 16), dtype=np.uint8)
     out[:, :, 0:2] = np.ascontiguousarray(d, dtype=np.float16).view(np.uint8).reshape(n, ns, 2)
     out[:, :, 2:4] = np.ascontiguousarray(dmin, dtype=np.float16).view(np.uint8).reshape(n, ns, 2)
     s = np.zeros((n, ns, 12), dtype=np.uint8)
@@ -191,17 +191,26 @@ def pack_q4_k(d, dmin, sc, m, q) -> np.ndarray:
     s[:, :, 0:4] |= (sc[:, :, 4:8] >> 4) << 6
     s[:, :, 4:8] |= (m[:, :, 4:8] >> 4) << 6
     out[:, :, 4:16] = s
+    return out
+
+
+def pack_q4_k(d, dmin, sc, m, q) -> np.ndarray:
+    """d, dmin fp16 [N][S]; sc, m uint8 [N][S][8] in 0..63; q uint8 [N][K] in 0..15."""
+    n, k = q.shape
+    ns = k // 256
+    out = np.zeros((n, ns, 144), dtype=np.uint8)
+    out[:, :, 0:16] = q4_k_header(d, dmin, sc, m)
     qq = q.astype(np.uint8).reshape(n, ns, 4, 2, 32)  # chunk c, half h, i
     out[:, :, 16:144] = (qq[:, :, :, 0, :] | (qq[:, :, :, 1, :] << 4)).reshape(n, ns, 128)
     return out.reshape(n, ns * 144)
 
 
-def pack_iq4_xs(d, ls, idx) -> np.ndarray:
-    """d fp16 [N][S]; ls uint8 [N][S][8] raw 6-bit scales; idx uint8 [N][K] in 0..15."""
-    n, k = idx.shape
-    ns = k // 256
-    ls = ls.astype(np.uint16)
-    out = np.zeros((n, ns, 136), dtype=np.uint8)
+def iq4_xs_header(d, ls) -> np.ndarray:
+    """First 8 bytes of each IQ4_XS super-block: fp16 d, u16 scales_h (two
+    high bits per sub-block), scales_l[4] (low nibbles).  ls [N][S][8] raw."""
+    n, ns = np.shape(d)
+    ls = np.asarray(ls).astype(np.uint16)
+    out = np.zeros((n, ns, 8), dtype=np.uint8)
     out[:, :, 0:2] = np.ascontiguousarray(d, dtype=np.float16).view(np.uint8).reshape(n, ns, 2)
     sh = np.zeros((n, ns), dtype=np.uint16)
     for j in range(8):
@@ -210,6 +219,15 @@ def pack_iq4_xs(d, ls, idx) -> np.ndarray:
     out[:, :, 3] = (sh >> 8).astype(np.uint8)
     lo = (ls & 15).astype(np.uint8)
     out[:, :, 4:8] = lo[:, :, 0::2] | (lo[:, :, 1::2] << 4)
+    return out
+
+
+def pack_iq4_xs(d, ls, idx) -> np.ndarray:
+    """d fp16 [N][S]; ls uint8 [N][S][8] raw 6-bit scales; idx uint8 [N][K] in 0..15."""
+    n, k = idx.shape
+    ns = k // 256
+    out = np.zeros((n, ns, 136), dtype=np.uint8)
+    out[:, :, 0:8] = iq4_xs_header(d, ls)
     qq = idx.astype(np.uint8).reshape(n, ns, 8, 2, 16)  # sub-block j, half h, i
     out[:, :, 8:136] = (qq[:, :, :, 0, :] | (qq[:, :, :, 1, :] << 4)).reshape(n, ns, 128)
     return out.reshape(n, ns * 136)

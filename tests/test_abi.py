@@ -1,0 +1,139 @@
+"""The C-ABI library: it loads, exports every function include/qmv.h declares,
+answers the host-only size queries, and rejects invalid calls before any work
+is enqueued (every call here returns from host validation: no device is
+touched, so these run without a GPU)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import quantized_decode_gemv_qmv_amd as q
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 4
+FAKE = 0x10000000  # 256-byte aligned, never dereferenced by host validation
+
+
+@pytest.fixture(scope="module")
+def L():
+    return q.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = q.symbols()
+    assert len(declared) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", q.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert hasattr(L, s)
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.qmv_abi_version() == 1
+    for st in range(6):
+        assert L.qmv_status_string(st).decode().startswith("QMV_")
+    assert b"unknown" in L.qmv_status_string(99)
+
+
+@pytest.mark.parametrize("fmt,k,expect", [(0, 4096, 4352), (1, 4096, 2304), (2, 14336, 7616),
+                                          (0, 65536, 69632), (0, 5120, 5440), (2, 1536, 816),
+                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (3, 256, 0)])
+def test_row_bytes(fmt, k, expect):
+    assert q.row_bytes(fmt, k) == expect
+
+
+def test_act_layout():
+    for t, k in ((1, 32), (3, 4096), (16, 14336), (512, 1536)):
+        od, os_ = q.act_offsets(t, k)
+        total = q.act_bytes(t, k)
+        assert od % 256 == 0 and os_ % 256 == 0 and od >= t * k
+        assert os_ >= od + 4 * t * (k // 32) and total >= os_ + 4 * t * (k // 32)
+    assert q.act_bytes(0, 32) == 0 and q.act_bytes(1, 33) == 0
+
+
+def test_workspace_sizes():
+    assert q.matvec_workspace_bytes(0, 256, 65536, 1) > 256 * 4
+    assert q.matvec_workspace_bytes(0, 152064, 5120, 1) == 0  # many rows: never split
+    assert q.matvec_workspace_bytes(0, 256, 65536, 17) == 0
+    assert q.moe_workspace_bytes(2, 128, 3072, 4096, 64, 8) >= 64 * 8 * 3072 * 4
+    assert q.moe_workspace_bytes(2, 128, 3072, 4096, 65, 8) == 0
+
+
+def _mv(L, fmt=0, w=FAKE, n=4, k=32, xq=FAKE, t=1, y=FAKE, ldy=4, ws=None, wsb=0):
+    return L.qmv_matvec(fmt, w, n, k, xq, t, y, ldy, ws, wsb, None)
+
+
+def test_matvec_validation(L):
+    assert _mv(L, w=None) == INVALID
+    assert _mv(L, xq=None) == INVALID
+    assert _mv(L, y=None) == INVALID
+    assert _mv(L, fmt=7) == INVALID
+    assert _mv(L, n=0) == INVALID
+    assert _mv(L, k=48) == INVALID
+    assert _mv(L, fmt=1, k=32) == INVALID
+    assert _mv(L, ldy=3) == INVALID
+    assert _mv(L, t=0) == INVALID
+    assert _mv(L, t=17) == UNSUPPORTED
+    assert _mv(L, w=FAKE + 8) == MISALIGNED
+    assert _mv(L, xq=FAKE + 16) == MISALIGNED
+    assert _mv(L, y=FAKE + 2) == MISALIGNED
+    need = q.matvec_workspace_bytes(0, 4, 32, 1)
+    assert _mv(L, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert _mv(L, ws=FAKE + 64, wsb=need) == MISALIGNED
+
+
+def test_quantize_validation(L):
+    f = L.qmv_quantize_act
+    assert f(None, 32, 1, 32, FAKE, None) == INVALID
+    assert f(FAKE, 32, 1, 32, None, None) == INVALID
+    assert f(FAKE, 32, 0, 32, FAKE, None) == INVALID
+    assert f(FAKE, 32, 1, 48, FAKE, None) == INVALID
+    assert f(FAKE, 31, 1, 32, FAKE, None) == INVALID
+    assert f(FAKE, 32, 65537, 32, FAKE, None) == UNSUPPORTED
+    assert f(FAKE + 2, 32, 1, 32, FAKE, None) == MISALIGNED
+    assert f(FAKE, 32, 1, 32, FAKE + 4, None) == MISALIGNED
+
+
+def test_moe_validation(L):
+    f = L.qmv_moe_matvec
+    ws = q.moe_workspace_bytes(2, 8, 16, 256, 2, 2)
+
+    def call(**kw):
+        a = dict(fmt=2, w=FAKE, e=8, n=16, k=256, xq=FAKE, per_slot=0, ids=FAKE, rw=None, t=2,
+                 top_k=2, y=FAKE, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(a["fmt"], a["w"], a["e"], a["n"], a["k"], a["xq"], a["per_slot"], a["ids"], a["rw"],
+                 a["t"], a["top_k"], a["y"], a["ws"], a["wsb"], None)
+
+    assert call(ids=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(per_slot=2) == INVALID
+    assert call(top_k=0) == INVALID
+    assert call(t=65) == UNSUPPORTED
+    assert call(top_k=17) == UNSUPPORTED
+    assert call(e=1025) == UNSUPPORTED
+    assert call(k=32768) == UNSUPPORTED
+    assert call(ids=FAKE + 2) == MISALIGNED
+    assert call(rw=FAKE + 1) == MISALIGNED
+    assert call(wsb=ws - 1) == WORKSPACE
+
+
+def test_block_dots_validation(L):
+    f = L.qmv_block_dots
+    assert f(0, None, 4, 32, FAKE, 1, FAKE, None) == INVALID
+    assert f(0, FAKE, 4, 32, FAKE, 17, FAKE, None) == UNSUPPORTED
+    assert f(0, FAKE, 4, 32, FAKE, 1, FAKE + 1, None) == MISALIGNED
+
+
+def test_tuning_switches(L):
+    assert L.qmv_set_tuning(b"bogus", 0) == INVALID
+    assert L.qmv_set_tuning(None, 0) == INVALID
+    assert L.qmv_set_tuning(b"variant", len(q.variants())) == INVALID
+    assert L.qmv_set_tuning(b"splitk", -2) == INVALID
+    assert L.qmv_set_tuning(b"variant", -1) == OK
+    assert L.qmv_set_tuning(b"splitk", -1) == OK
+    assert q.variant_name(-1) is None and q.variant_name(len(q.variants())) is None
+    assert q.pick_variant(1, 14336, 4096, 1) >= 0
+    assert q.pick_variant(1, 14336, 4096, 17) == -1

@@ -1,0 +1,87 @@
+"""Edge shapes and values of qmv_matvec: one row, a few rows, ragged tails, a
+single block of K, Q8_0 rows whose blocks start at every alignment, all-zero
+activations, the int8 weight value -128 (valid in Q8_0 but never drawn by the
+generator), and zero sub-block scales."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_y, gpu, need_gpu, quantize, say, to_dev, x_host
+
+pytestmark = gpu
+
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS]
+
+
+def _check(qmv, fmt, w, n, k, x, what):
+    t = x.shape[0]
+    say(f"edge {what} fmt={fmt} N={n} K={k} T={t}")
+    xq = quantize(qmv, x)
+    y = qmv.matvec(fmt, to_dev(w), n, k, xq, t).cpu().numpy()
+    qs, d, s = oracle.quantize_act(x)
+    yr, mag = oracle.matvec(fmt, w, k, qs, d, s)
+    assert_y(y, yr, mag, what)
+    got = qmv.block_dots(fmt, to_dev(w), n, k, xq, t).cpu().numpy()
+    assert np.array_equal(got, oracle.block_dots(fmt, w, k, qs, s)), what
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [1, 3, 257])
+def test_row_counts(fmt, n):
+    qmv = need_gpu()
+    k = 256
+    for t in (1, 7, 16):
+        w = synth.make_weights(fmt, n, k, f"edge/{fmt}/{n}").data
+        _check(qmv, fmt, w, n, k, x_host(t, k, "edge/x"), f"rows {n}")
+
+
+@pytest.mark.parametrize("k", [32, 64, 96, 160, 2080])
+def test_q8_0_odd_block_counts(k):
+    """Rows of 34-byte blocks: odd block counts make rows start 2 mod 4."""
+    qmv = need_gpu()
+    n = 45
+    w = synth.make_weights(synth.Q8_0, n, k, f"edge/q8/{k}").data
+    for t in (1, 3, 16):
+        _check(qmv, synth.Q8_0, w, n, k, x_host(t, k, f"edge/q8x/{k}"), f"q8_0 K={k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_zero_activations(fmt):
+    qmv = need_gpu()
+    n, k = 50, 512
+    w = synth.make_weights(fmt, n, k, f"edge/z/{fmt}").data
+    x = np.zeros((3, k), np.float32)
+    x[1, 100] = 2.0  # one token with a single non-zero block
+    _check(qmv, fmt, w, n, k, x, "zero x")
+
+
+def test_q8_0_minus_128():
+    qmv = need_gpu()
+    n, k = 33, 1024
+    wf = synth.make_weights(synth.Q8_0, n, k, "edge/m128", q8_range=(-128, 127), keep_fields=True)
+    w = wf.data.copy()
+    w.reshape(n, k // 32, 34)[:, :, 2:] = 0x80  # every quant -128
+    w.reshape(n, k // 32, 34)[5, 3, 2:] = wf.q[5, 96:128].view(np.uint8)
+    x = x_host(4, k, "edge/m128x")
+    x[2, :32] = 127.0  # an activation block of all +127
+    _check(qmv, synth.Q8_0, w, n, k, x, "q8_0 -128")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS])
+def test_zero_and_extreme_scales(fmt):
+    qmv = need_gpu()
+    n, k = 20, 1024
+    ns = k // 256
+    q = synth.nibbles(synth.stream(f"edge/sc/{fmt}"), 0, n * k).reshape(n, k)
+    d = synth.scale_f16(synth.stream(f"edge/scd/{fmt}"), 0, n * ns).reshape(n, ns)
+    # raw 6-bit scales cover 0..63 (IQ4_XS 32 is an effective zero scale)
+    sc = (np.arange(n * ns * 8) % 64).astype(np.uint8).reshape(n, ns, 8)
+    if fmt == synth.Q4_K:
+        m = sc[:, :, ::-1].copy()
+        w = synth.pack_q4_k(d, d, sc, m, q)
+    else:
+        w = synth.pack_iq4_xs(d, sc, q)
+    for t in (1, 16):
+        _check(qmv, fmt, w, n, k, x_host(t, k, f"edge/scx/{fmt}"), "scales")

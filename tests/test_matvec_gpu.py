@@ -1,0 +1,157 @@
+"""qmv_matvec and qmv_block_dots against the oracle.
+
+  * integer partials of every 32-block: bit-exact (qmv_block_dots runs the
+    same device decode and dot routines as the matvec kernels);
+  * y: within 1e-4 of the sum of |per-block terms| of each output;
+  * small shapes at every token count 1..16 and every kernel variant, with
+    several row tiles and a ragged tail; the full workload shapes at their
+    token counts on sampled rows, in the launch configuration the bench
+    times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (assert_y, gpu, host_rows, need_gpu, quantize, sample_rows, say, to_dev,
+                      weights, x_host)
+
+pytestmark = gpu
+
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS]
+NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs"}
+
+
+def _oracle_y(fmt, w_host, k, x):
+    qs, d, s = oracle.quantize_act(x)
+    return oracle.matvec(fmt, w_host, k, qs, d, s)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=[NAMES[f] for f in FMTS])
+def test_block_dots_small(fmt):
+    qmv = need_gpu()
+    for n, k, t in ((37, 512, 3), (5, 256, 16), (64, 1024, 1)):
+        say(f"block_dots {NAMES[fmt]} N={n} K={k} T={t}")
+        w = synth.make_weights(fmt, n, k, f"bd/{fmt}/{n}").data
+        x = x_host(t, k, f"bdx/{fmt}/{k}")
+        xq = quantize(qmv, x)
+        got = qmv.block_dots(fmt, to_dev(w), n, k, xq, t).cpu().numpy()
+        qs, _, s = oracle.quantize_act(x)
+        ref = oracle.block_dots(fmt, w, k, qs, s)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=[NAMES[f] for f in FMTS])
+def test_every_token_count_and_variant(fmt):
+    """N = 333 rows (several tiles of every variant plus a ragged tail)."""
+    qmv = need_gpu()
+    n = 333
+    k = 1024 if fmt == synth.Q8_0 else 2048
+    w = synth.make_weights(fmt, n, k, f"tv/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(16, k, f"tvx/{fmt}")
+    try:
+        for v in range(len(qmv.variants())):
+            qmv.set_tuning("variant", v)
+            for t in range(1, 17):
+                say(f"matvec {NAMES[fmt]} variant {qmv.variant_name(v)} T={t}")
+                xq = quantize(qmv, x[:t])
+                y = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+                yr, mag = _oracle_y(fmt, w, k, x[:t])
+                assert_y(y, yr, mag, f"{NAMES[fmt]} v{v} T={t}")
+    finally:
+        qmv.set_tuning("variant", -1)
+
+
+FULL = [
+    ("q8_0_4096x4096", synth.Q8_0, 4096, 4096, (1,)),
+    ("q4_k_14336x4096", synth.Q4_K, 14336, 4096, (1, 2, 4, 8, 16)),
+    ("iq4_xs_4096x14336", synth.IQ4_XS, 4096, 14336, (1, 2, 4, 8, 16)),
+    ("q8_0_head_152064x5120", synth.Q8_0, 152064, 5120, (1, 2, 4, 8, 16)),
+]
+
+
+@pytest.mark.parametrize("name,fmt,n,k,tokens", FULL, ids=[c[0] for c in FULL])
+def test_full_shapes(name, fmt, n, k, tokens):
+    qmv = need_gpu()
+    say(f"full {name}: generating weights")
+    wd = weights(fmt, n, k, f"{name}/W")
+    rows = sample_rows(n, 640, f"rows/{name}")
+    w_rows = host_rows(wd, rows)
+    # the device generator agrees with the numpy generator on these rows
+    for r in (rows[0], rows[len(rows) // 2], rows[-1]):
+        ref = synth.make_weights(fmt, n, k, f"{name}/W", rows=(int(r), int(r) + 1)).data
+        assert np.array_equal(w_rows[np.searchsorted(rows, r)], ref[0])
+    x = x_host(max(tokens), k, f"{name}/x")
+    for t in tokens:
+        say(f"full {name} T={t}")
+        xq = quantize(qmv, x[:t])
+        y = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+        yr, mag = _oracle_y(fmt, w_rows, k, x[:t])
+        assert_y(y[:, rows], yr, mag, f"{name} T={t}")
+        # exact integer partials on a few aligned row ranges
+        rb = qmv.row_bytes(fmt, k)
+        for r0 in (0, (n // 2) & ~7, n - 8):
+            wsub = wd.view(-1)[r0 * rb:(r0 + 8) * rb]
+            got = qmv.block_dots(fmt, wsub, 8, k, xq, t).cpu().numpy()
+            qs, _, s = oracle.quantize_act(x[:t])
+            ref = oracle.block_dots(fmt, wsub.cpu().numpy(), k, qs, s)
+            assert np.array_equal(got, ref), (name, t, r0)
+
+
+def test_head_every_token_count_on_row_slice():
+    """The head at T = 1..16 on a 4096-row slice of its rows (K = 5120)."""
+    qmv = need_gpu()
+    n, k = 4096, 5120
+    wd = weights(synth.Q8_0, n, k, "q8_0_head_152064x5120/W")
+    w = wd.cpu().numpy()
+    x = x_host(16, k, "q8_0_head_152064x5120/x")
+    for t in range(1, 17):
+        say(f"head slice T={t}")
+        xq = quantize(qmv, x[:t])
+        y = qmv.matvec(synth.Q8_0, wd, n, k, xq, t).cpu().numpy()
+        yr, mag = _oracle_y(synth.Q8_0, w, k, x[:t])
+        assert_y(y, yr, mag, f"head slice T={t}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=[NAMES[f] for f in FMTS])
+def test_iq4_and_q4k_every_token_count_config_k(fmt):
+    """Every T = 1..16 at the workload's reduction length on a row slice."""
+    qmv = need_gpu()
+    k = {synth.Q8_0: 4096, synth.Q4_K: 4096, synth.IQ4_XS: 14336}[fmt]
+    n = 700
+    w = synth.make_weights(fmt, n, k, f"tk/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(16, k, f"tkx/{fmt}")
+    for t in range(1, 17):
+        xq = quantize(qmv, x[:t])
+        y = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+        yr, mag = _oracle_y(fmt, w, k, x[:t])
+        assert_y(y, yr, mag, f"{NAMES[fmt]} K={k} T={t}")
+
+
+def test_output_stride_leaves_padding():
+    qmv = need_gpu()
+    fmt, n, k, t = synth.IQ4_XS, 100, 512, 4
+    w = synth.make_weights(fmt, n, k, "ld/w").data
+    x = x_host(t, k, "ld/x")
+    y = torch.full((t, n + 28), 7.0, dtype=torch.float32, device="cuda")
+    qmv.matvec(fmt, to_dev(w), n, k, quantize(qmv, x), t, y=y)
+    yh = y.cpu().numpy()
+    yr, mag = _oracle_y(fmt, w, k, x)
+    assert_y(yh[:, :n], yr, mag, "ldy")
+    assert np.all(yh[:, n:] == 7.0)
+
+
+def test_reuses_one_activation_buffer_across_formats():
+    """One Q8 activation buffer serves all three weight types."""
+    qmv = need_gpu()
+    k, t = 4096, 3
+    x = x_host(t, k, "reuse/x")
+    xq = quantize(qmv, x)
+    for fmt in FMTS:
+        w = synth.make_weights(fmt, 96, k, f"reuse/{fmt}").data
+        y = qmv.matvec(fmt, to_dev(w), 96, k, xq, t).cpu().numpy()
+        yr, mag = _oracle_y(fmt, w, k, x)
+        assert_y(y, yr, mag, f"reuse {NAMES[fmt]}")

@@ -1,0 +1,85 @@
+"""Split-K path of qmv_matvec (few rows, long K) against the oracle, forced
+on and off, over repeated calls that must find the workspace counters reset."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_y, gpu, host_rows, need_gpu, quantize, say, to_dev, weights, x_host
+
+pytestmark = gpu
+
+
+def _ref(fmt, w, k, x):
+    qs, d, s = oracle.quantize_act(x)
+    return oracle.matvec(fmt, w, k, qs, d, s)
+
+
+def test_splitk_workload_256x65536():
+    """The few-row long-K workload (Q8_0 256 x 65536, one token)."""
+    qmv = need_gpu()
+    name, fmt, n, k = "q8_0_splitk_256x65536", synth.Q8_0, 256, 65536
+    wd = weights(fmt, n, k, f"{name}/W")
+    w = wd.cpu().numpy()
+    x = x_host(1, k, f"{name}/x")
+    yr, mag = _ref(fmt, w, k, x)
+    xq = quantize(qmv, x)
+    ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, 1), dtype=torch.uint8, device="cuda")
+    try:
+        for forced in (-1, 0, 2, 7, 16, 32, -1, 3):
+            qmv.set_tuning("splitk", forced)
+            for rep in range(3):
+                say(f"split-K {name} slices={forced} rep={rep}")
+                y = qmv.matvec(fmt, wd, n, k, xq, 1, ws=ws).cpu().numpy()
+                assert_y(y, yr, mag, f"splitk={forced} rep={rep}")
+        # no workspace: the single-pass kernel
+        qmv.set_tuning("splitk", -1)
+        y = qmv.matvec(fmt, wd, n, k, xq, 1).cpu().numpy()
+        assert_y(y, yr, mag, "no workspace")
+    finally:
+        qmv.set_tuning("splitk", -1)
+    # counters are back at zero after completed calls
+    torch.cuda.synchronize()
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS])
+def test_splitk_all_formats_and_token_counts(fmt):
+    qmv = need_gpu()
+    n, k = 77, 8192
+    w = synth.make_weights(fmt, n, k, f"sk/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(16, k, f"skx/{fmt}")
+    try:
+        for t in (1, 2, 5, 16):
+            xq = quantize(qmv, x[:t])
+            yr, mag = _ref(fmt, w, k, x[:t])
+            ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, t), dtype=torch.uint8,
+                             device="cuda")
+            for forced in (-1, 4, 9):
+                qmv.set_tuning("splitk", forced)
+                for rep in range(2):
+                    say(f"split-K fmt={fmt} T={t} slices={forced} rep={rep}")
+                    y = qmv.matvec(fmt, wd, n, k, xq, t, ws=ws).cpu().numpy()
+                    assert_y(y, yr, mag, f"fmt {fmt} T={t} split {forced}")
+    finally:
+        qmv.set_tuning("splitk", -1)
+
+
+def test_splitk_shares_workspace_across_shapes():
+    """One workspace, sized for the larger call, serves a smaller one next."""
+    qmv = need_gpu()
+    fmt = synth.IQ4_XS
+    big = qmv.matvec_workspace_bytes(fmt, 512, 16384, 4)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    try:
+        qmv.set_tuning("splitk", 8)
+        for n, k, t in ((512, 16384, 4), (40, 4096, 2), (512, 16384, 4)):
+            w = synth.make_weights(fmt, n, k, f"sws/{n}").data
+            x = x_host(t, k, f"swsx/{k}")
+            y = qmv.matvec(fmt, to_dev(w), n, k, quantize(qmv, x), t, ws=ws).cpu().numpy()
+            yr, mag = _ref(fmt, w, k, x)
+            assert_y(y, yr, mag, f"shared ws N={n} K={k}")
+    finally:
+        qmv.set_tuning("splitk", -1)
