@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized decode matvec on one MI355X.
+
+One step is one pass of the hot path over one batch of tokens: quantize the
+fp32 activations to Q8 blocks (qmv_quantize_act) and run the block-quantized
+matvec (qmv_matvec).  The default workload is the q4_K 14336 x 4096 matvec at
+one token; --workload / --tokens select the others.  Inputs are synthetic
+(seeded generator) and resident in HBM before timing starts.
+
+The weights are read from a ring of copies of at least 1 GiB, one copy per
+step, so every step streams its weights from HBM rather than from the 256 MB
+Infinity Cache.  Steps are captured in HIP graphs and replayed; exactly
+--steps steps are timed between two device synchronisations.
+
+Output: one JSON line.  `value` is weight bytes per step / time per step
+(GB/s).  `roofline` is the matvec kernel against the 8 TB/s HBM peak: its
+average duration comes from HIP events around back-to-back replays of the
+kernel alone over the same ring (the same figure rocprofv3's kernel trace
+reports), `traffic` from the rocprofv3 counter summary under profiles/ when
+it was taken from the current kernel sources.  `cpu_baseline` is the CPU
+oracle (test infrastructure) timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "weight GB/s & % HBM roofline, q4_K/IQ4_XS matvec at 1–16 tokens"
+
+# name: (format, rows, K, token counts of the workload)
+WORKLOADS = {
+    "q4_k_14336x4096": (1, 14336, 4096, (1, 2, 4, 8, 16)),
+    "iq4_xs_4096x14336": (2, 4096, 14336, (1, 2, 4, 8, 16)),
+    "q8_0_4096x4096": (0, 4096, 4096, (1,)),
+    "q8_0_splitk_256x65536": (0, 256, 65536, (1,)),
+    "q8_0_head_152064x5120": (0, 152064, 5120, (1, 2, 4, 8, 16)),
+}
+FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS"}
+KERNEL_SOURCES = ("qmv_device.h", "qmv_matvec.hip", "qmv_quant.hip", "qmv_api.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_decode_gemv_qmv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, tokens: int, src_hash: str):
+    """HBM bytes per launch from profiles/traffic_<workload>_t<T>.txt, if that
+    summary was taken from the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_t{tokens}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^kernel_sources_sha256_16:\s*(\S+)", text, re.M)
+    m_bytes = re.search(r"^traffic_bytes_per_launch:\s*([0-9.]+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+class Ring:
+    """Device-resident inputs of one workload: weight ring, activations,
+    buffers."""
+
+    def __init__(self, torch, qmv, fmt, n, k, t, name):
+        from synth import make_x
+        from synth.device import make_weights_t
+
+        self.fmt, self.n, self.k, self.t = fmt, n, k, t
+        w0 = make_weights_t(fmt, n, k, f"{name}/W", device="cuda")
+        self.weight_bytes = w0.numel()
+        self.copies = max(2, math.ceil((1 << 30) / self.weight_bytes))
+        self.w = [w0] + [w0.clone() for _ in range(self.copies - 1)]
+        xs = make_x(8 * t, k, f"{name}/x").reshape(8, t, k)
+        self.x = [torch.from_numpy(xs[i]).cuda() for i in range(8)]
+        self.xq = torch.empty(qmv.act_bytes(t, k), dtype=torch.uint8, device="cuda")
+        self.y = torch.empty((t, n), dtype=torch.float32, device="cuda")
+        wsb = qmv.matvec_workspace_bytes(fmt, n, k, t)
+        self.ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+
+    def step(self, qmv, i):
+        qmv.quantize_act(self.x[i % 8], out=self.xq)
+        qmv.matvec(self.fmt, self.w[i % self.copies], self.n, self.k, self.xq, self.t, y=self.y,
+                   ws=self.ws)
+
+    def matvec_only(self, qmv, i):
+        qmv.matvec(self.fmt, self.w[i % self.copies], self.n, self.k, self.xq, self.t, y=self.y,
+                   ws=self.ws)
+
+
+def capture(torch, fn, count, start=0):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(count):
+                fn(start + i)
+    torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def run_steps(torch, graphs, steps):
+    """Replays graphs covering exactly `steps` steps."""
+    g_full, per, g_tail = graphs
+    for _ in range(steps // per):
+        g_full.replay()
+    if g_tail is not None:
+        g_tail.replay()
+
+
+def kernel_us(torch, qmv, ring, reps=20):
+    """Average matvec duration: HIP events around back-to-back graph replays
+    of the kernel alone, cycling the weight ring."""
+    per = max(ring.copies, 32)
+    g = capture(torch, lambda i: ring.matvec_only(qmv, i), per)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * per)
+
+
+def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
+    """The CPU oracle (quantize + matvec, the same workload) on this host,
+    repeated until at least min_seconds of work."""
+    import oracle
+    import synth
+
+    rows = min(n, max(1, (64 << 20) // (k // (32 if fmt == 0 else 256) * (34, 144, 136)[fmt])))
+    w = synth.make_weights(fmt, n, k, f"{name}/W", rows=(0, rows)).data
+    x = synth.make_x(t, k, f"{name}/x")
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        qs, d, s = oracle.quantize_act(x)
+        oracle.matvec(fmt, w, k, qs, d, s)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el >= max_seconds:
+            break
+    return {"value": round(w.nbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{FMT_NAME[fmt]} {rows}x{k} matvec (rows 0..{rows - 1} of {n}) at {t} "
+                      f"token(s) incl. activation quantization, {reps} repetitions in {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="q4_k_14336x4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=1)
+    ap.add_argument("--all-tokens", action="store_true",
+                    help="also time the matvec at every token count of the workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (the matvec is "
+              "measured on one GPU's share of the weights; multi-GPU sharding is not built)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import quantized_decode_gemv_qmv_amd as qmv
+
+    qmv.lib()  # fails loudly without the HIP library
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    fmt, n, k, token_list = WORKLOADS[args.workload]
+    t = args.tokens
+    if not 1 <= t <= 16:
+        print("--tokens must be 1..16", file=sys.stderr)
+        return 2
+
+    log(f"bench: {args.workload} T={t}: generating inputs")
+    ring = Ring(torch, qmv, fmt, n, k, t, args.workload)
+    per = max(ring.copies, 64)
+    g_full = capture(torch, lambda i: ring.step(qmv, i), per)
+    tail = args.steps % per
+    g_tail = capture(torch, lambda i: ring.step(qmv, i), tail) if tail else None
+    graphs = (g_full, per, g_tail)
+
+    log(f"bench: warmup {args.warmup} steps")
+    run_steps(torch, (g_full, per, capture(torch, lambda i: ring.step(qmv, i), args.warmup % per)
+                      if args.warmup % per else None), args.warmup)
+    torch.cuda.synchronize()
+
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(torch, graphs, args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = ring.weight_bytes / (ms_per_step * 1e-3) / 1e9
+
+    kus = kernel_us(torch, qmv, ring)
+    achieved = ring.weight_bytes / (kus * 1e-6) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = recorded_traffic(args.workload, t, src_hash)
+    variant = qmv.variant_name(qmv.pick_variant(fmt, n, k, t))
+
+    by_tokens = []
+    if args.all_tokens:
+        for tt in token_list:
+            r2 = ring if tt == t else Ring(torch, qmv, fmt, n, k, tt, args.workload)
+            us = kernel_us(torch, qmv, r2)
+            by_tokens.append({"tokens": tt, "kernel_us": round(us, 3),
+                              "weight_GBps": round(r2.weight_bytes / (us * 1e-6) / 1e9, 1),
+                              "hbm_frac": round(r2.weight_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              "matvecs_per_s": round(1e6 / us, 1),
+                              "variant": qmv.variant_name(qmv.pick_variant(fmt, n, k, tt))})
+            log(f"bench: T={tt} kernel {us:.2f} us")
+            if r2 is not ring:
+                del r2
+                torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(fmt, n, k, t, args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{FMT_NAME[fmt]} matvec {n}x{k}, {t} token(s)", "format": FMT_NAME[fmt],
+                   "n_rows": n, "k": k, "tokens": t, "weight_bytes": ring.weight_bytes,
+                   "ring_copies": ring.copies, "step": "qmv_quantize_act + qmv_matvec",
+                   "matvec_variant": variant},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "matvecs_per_s": round(1e3 / ms_per_step, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_us": round(kus, 3),
+                     "algorithmic_bytes_per_launch": ring.weight_bytes,
+                     "kernel_sources_sha256_16": src_hash},
+        "cpu_baseline": cpu,
+    }
+    if by_tokens:
+        out["by_tokens"] = by_tokens
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -185,7 +185,11 @@ qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t 
  *   "splitk"  : -1 automatic (default), 0 never, n >= 1 force n K-slices
  *               whenever a workspace is given;
  *   "variant" : -1 automatic (default), else an index into the kernel
- *               variant table of qmv_matvec (see qmv_variant_name).
+ *               variant table of qmv_matvec (see qmv_variant_name); a
+ *               variant whose LDS staging does not fit the device runs the
+ *               lane-group kernel instead (qmv_pick_variant reports which);
+ *   "bpc"     : 0 automatic (default), else a cap on resident workgroups
+ *               per compute unit for the persistent streaming kernel.
  * The environment variables QMV_SPLITK and QMV_VARIANT set the same switches
  * when the library loads.  Returns QMV_ERR_INVALID_ARG for an unknown key or
  * value.

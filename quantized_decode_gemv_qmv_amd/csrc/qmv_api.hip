@@ -42,19 +42,40 @@ int64_t block_bytes(int t) { return t == QMV_Q8_0 ? 34 : (t == QMV_Q4_K ? 144 : 
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int device_cus() {
-  static std::atomic<int> cache[64];
+struct DeviceInfo {
+  int cus;
+  int64_t lds_per_cu;
+  int64_t lds_per_block;
+};
+
+// Properties of the current device, queried once per device.
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static DeviceInfo cache[64];
+  static bool have[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  cache[dev].store(cus, std::memory_order_relaxed);
-  return cus;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {256, 163840, 65536};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!have[dev]) {
+    int cus = 0, lcu = 0, lblk = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipDeviceGetAttribute(&lcu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        lcu <= 0)
+      lcu = 65536;
+    if (hipDeviceGetAttribute(&lblk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        lblk <= 0)
+      lblk = 65536;
+    cache[dev] = {cus, lcu, lblk};
+    have[dev] = true;
+  }
+  return cache[dev];
 }
+
+int device_cus() { return device_info().cus; }
 
 ActView act_view(const void* xq, int64_t n_tok, int64_t k) {
   const uint8_t* b = static_cast<const uint8_t*>(xq);
@@ -75,27 +96,78 @@ qmv_status check_weights(int type, const void* w, int64_t n_rows, int64_t k) {
   return QMV_OK;
 }
 
-int pick_lpr(int64_t units) { return units >= 256 ? 64 : (units >= 96 ? 32 : 16); }
-
-int variant_index(int lpr, int rows) {
+int find_variant(const char* name) {
   for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].lpr == lpr && kVariants[i].rows == rows) return i;
+    if (!std::strcmp(kVariants[i].name, name)) return i;
   return 0;
 }
 
-int auto_variant(int, int64_t n_rows, int64_t k, int64_t n_tok) {
+int token_capacity(int64_t n_tok) {
+  return n_tok <= 1 ? 1 : n_tok <= 2 ? 2 : n_tok <= 4 ? 4 : n_tok <= 8 ? 8 : 16;
+}
+
+// Whether a streaming variant's LDS staging fits one workgroup.
+bool stream_fits(int v, int64_t k, int64_t n_tok) {
+  const Variant& var = kVariants[v];
+  if (var.kind == 0) return true;
+  const size_t need =
+      stream_lds_bytes(var, (int64_t)qmv_act_bytes(n_tok, k), token_capacity(n_tok));
+  return (int64_t)need <= device_info().lds_per_block;
+}
+
+// Default kernel for a shape, from measurements on MI355X of every variant on
+// the workload shapes (Q8_0 4096x4096 and 152064x5120, q4_K 14336x4096,
+// IQ4_XS 4096x14336, Q8_0 256x65536; 1..16 tokens):
+//   - too few rows to give every compute unit several waves, long K: the
+//     streaming kernel with K split over a 16-wave workgroup;
+//   - up to four tokens: the flat kernel (one wave per row group, all loads
+//     issued at once), activations staged in LDS for Q8_0, prefetched from
+//     global memory for the 4-bit formats, units per lane sized so that one
+//     chunk covers the row;
+//   - more tokens: the variant that measured fastest for that format;
+// and the lane-group kernel when the activations do not fit in LDS.
+int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t units = k / 32;
-  const int lpr = pick_lpr(units);
-  int rows = n_tok <= 4 ? 2 : 1;
-  // keep at least ~4 waves per compute unit before doubling rows per group
-  const int64_t waves_r2 = (n_rows + 2 * (64 / lpr) - 1) / (2 * (64 / lpr));
-  if (waves_r2 < 4 * device_cus()) rows = 1;
-  return variant_index(lpr, rows);
+  const int cus = device_cus();
+  const int64_t nu = (units + 63) / 64;
+  const char* name;
+  if (n_rows < 4 * (int64_t)cus && units >= 256) {
+    name = "st_k16_r1_u2";
+  } else if (type == QMV_Q8_0) {
+    if (n_tok <= 4)
+      name = nu <= 2 ? "fl_w16_r1_u2_l" : nu <= 3 ? "fl_w16_r1_u3_l" : "fl_w4_r1_u4_g";
+    else
+      name = "lpr32_r2";
+  } else if (type == QMV_Q4_K) {
+    if (nu <= 2)
+      name = n_tok > 2 && n_tok <= 4 ? "st_w4_r2_u2" : "fl_w4_r2_u2_g";
+    else
+      name = n_tok <= 2 ? "fl_w4_r1_u4_g" : "lpr64_r2";
+  } else {
+    if (n_tok <= 1)
+      name = nu <= 2 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u4_g";
+    else if (n_tok <= 2)
+      name = nu <= 7 ? "fl_w4_r1_u7_g" : "fl_w4_r1_u4_g";
+    else if (n_tok <= 4)
+      name = "st_w16_r1_u2";
+    else if (n_tok <= 8)
+      name = "fl_w16_r1_u2_l";
+    else
+      name = "lpr64_r2";
+  }
+  int v = find_variant(name);
+  if (!stream_fits(v, k, n_tok)) v = find_variant("lpr64_r2");
+  return v;
 }
 
 int choose_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t forced = g_variant.load();
-  if (forced >= 0 && forced < kNumVariants) return static_cast<int>(forced);
+  if (forced >= 0 && forced < kNumVariants) {
+    // a forced streaming variant whose staging does not fit runs the
+    // lane-group kernel instead
+    return stream_fits((int)forced, k, n_tok) ? static_cast<int>(forced)
+                                              : find_variant("lpr64_r2");
+  }
   return auto_variant(type, n_rows, k, n_tok);
 }
 
@@ -175,6 +247,11 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
     g_splitk = value;
     return QMV_OK;
   }
+  if (!std::strcmp(key, "bpc")) {
+    if (value < 0 || value > 64) return QMV_ERR_INVALID_ARG;
+    set_blocks_per_cu(static_cast<int>(value));
+    return QMV_OK;
+  }
   if (!std::strcmp(key, "variant")) {
     if (value < -1 || value >= kNumVariants) return QMV_ERR_INVALID_ARG;
     g_variant = value;
@@ -241,11 +318,22 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
   a.ldy = ldy;
   a.variant = choose_variant(type, n_rows, k, n_tok);
   a.slices = 1;
+  a.xq = static_cast<const uint8_t*>(xq);
+  a.act_bytes = static_cast<int64_t>(qmv_act_bytes(n_tok, k));
+  a.off_d = static_cast<int64_t>(qmv_act_offset_d(n_tok, k));
+  a.off_s = static_cast<int64_t>(qmv_act_offset_s(n_tok, k));
+  const DeviceInfo dv = device_info();
+  a.cus = dv.cus;
+  a.lds_per_cu = dv.lds_per_cu;
   const size_t need = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok);
   if (ws != nullptr && need > 0) {
     if (ws_bytes < need) return QMV_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return QMV_ERR_MISALIGNED;
-    a.slices = choose_slices(kVariants[a.variant], n_rows, k);
+    // the cross-workgroup split-K path belongs to the lane-group kernel; it
+    // runs only when slices are forced (the streaming kernel splits K inside
+    // a workgroup and needs no workspace)
+    if (g_splitk.load() > 0 && kVariants[a.variant].kind != 0) a.variant = find_variant("lpr64_r2");
+    if (kVariants[a.variant].kind == 0) a.slices = choose_slices(kVariants[a.variant], n_rows, k);
     uint8_t* b = static_cast<uint8_t*>(ws);
     a.cnt = reinterpret_cast<int*>(b);
     a.part = reinterpret_cast<float*>(b + kSplitCounterBytes);

@@ -16,15 +16,44 @@ struct ActView {
   int nb;  // k / 32
 };
 
-// A dense matvec kernel configuration: lanes per row group and rows per group.
+// A dense matvec kernel configuration.
+//   kind 0: lane-group kernel (k_matvec) -- a wave is split into 64/lpr groups
+//           of lpr lanes; each group owns `rows` rows and walks units with
+//           stride lpr; activations are read from global memory;
+//   kind 1: streaming kernel (k_stream) -- workgroups of wpb waves, teams of
+//           ks waves (1 or wpb) per group of `rows` rows, `nu` units per lane
+//           per chunk, activations staged in LDS;
+//   kind 2: flat kernel (k_flat) -- one wave per group of `rows` rows for the
+//           whole grid at once, `nu` units per lane; activations prefetched
+//           from global memory (xl 0, up to 4 tokens) or staged in LDS (xl 1).
 struct Variant {
+  int kind;
   int lpr;
   int rows;
+  int nu;
+  int wpb;
+  int ks;
+  int xl;
   const char* name;
 };
 
 extern const Variant kVariants[];
 extern const int kNumVariants;
+
+// Kernel arguments of k_stream.
+struct StreamArgs {
+  const uint8_t* w;
+  int64_t row_bytes;
+  int n_rows;
+  int units;
+  const uint8_t* xq;  // activation buffer, copied whole into LDS
+  int act_bytes;
+  int off_d, off_s;   // byte offsets of d and s inside it
+  int k, nb;
+  int n_tok;
+  float* y;
+  int64_t ldy;
+};
 
 struct MatvecLaunch {
   int fmt;
@@ -37,6 +66,10 @@ struct MatvecLaunch {
   float* y;
   int64_t ldy;
   int variant;  // index into kVariants
+  const uint8_t* xq;  // the activation buffer and its layout
+  int64_t act_bytes, off_d, off_s;
+  int cus;            // compute units of the device
+  int64_t lds_per_cu; // LDS bytes per compute unit
   // split-K (slices > 1): partial sums [slices][n_tok][n_rows] and one
   // arrival counter per row tile, both in the caller's workspace
   int slices;
@@ -46,6 +79,14 @@ struct MatvecLaunch {
 
 // Rows covered by one 256-thread workgroup of a variant.
 inline int rows_per_wg(const Variant& v) { return 4 * (64 / v.lpr) * v.rows; }
+// Rows covered by one wave.
+inline int rows_per_wave(const Variant& v) { return (64 / v.lpr) * v.rows; }
+
+// LDS bytes k_stream needs for an activation buffer of act_bytes bytes and
+// a token capacity tm (the staged buffer plus the split-K reduction area).
+size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm);
+// Tuning: cap on k_stream workgroups per compute unit (0 = occupancy).
+void set_blocks_per_cu(int v);
 
 hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
                            int32_t* s, hipStream_t st);

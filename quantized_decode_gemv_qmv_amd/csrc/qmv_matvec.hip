@@ -1,63 +1,33 @@
-// qmv_matvec.hip -- activation Q8 quantizer, dense small-batch matvec (with
-// its split-K form) and the integer block-dot test kernel, for gfx950.
+// qmv_matvec.hip -- dense small-batch matvec kernels for gfx950.
 //
-// Matvec mapping.  A 256-thread workgroup is four waves; a wave is split into
-// 64/LPR lane groups and each group owns R consecutive rows.  The LPR lanes of
-// a group walk the row's 32-weight units with stride LPR, so for every unit
-// index the group reads a contiguous span of the row (16 bytes per lane for
-// q4_K / IQ4_XS quants, 34 bytes per lane for Q8_0 blocks) and every weight
-// byte is fetched from HBM exactly once.  The activation fragment of a unit is
-// loaded once per token and shared by the group's R rows; each decoded weight
-// unit is shared by all tokens (one weight read serves the whole verify
-// batch: zhuai.tech GLM-5.3 page, "MTP saves full-model execution rounds").
-// The weight loads of the next unit are issued before the current unit is
-// computed, so every wave keeps two units per row in flight.
+// Two kernel families compute y[t][n] = sum_k W[n][k] x[t][k] from the block
+// weights and the Q8 activation buffer; each decoded weight unit serves every
+// token of the batch (one weight read for the whole verify batch: zhuai.tech
+// GLM-5.3 page, "MTP saves full-model execution rounds").
+//
+// k_stream (the default).  The activation buffer is copied once per workgroup
+// into LDS, so activation reads never sit in the vector-memory queue behind
+// weight loads.  Work is split into jobs = (group of R rows, chunk of 64*NU
+// units): lane l of a wave takes units c*64*NU + l + 64*i (i < NU) of each of
+// the group's rows, so each weight load of the wave is one contiguous, fully
+// used span.  A wave keeps the next job's weight loads in flight while it
+// computes the current one; every load is unconditional (positions past the
+// end re-read a valid unit and are masked out), so the load counter never has
+// to drain early.  Teams of KS waves share a row group and split its chunks
+// (split-K inside one workgroup, reduced through LDS: no workspace, no
+// cross-workgroup synchronisation) -- used for few rows and long K (Castagna
+// Veloce page, "Kernels for the MI50": Q8_0 matvec with a split-K variant).
+// Lane sums are DPP row reductions plus four scalar reads.
+//
+// k_matvec (lane groups of LPR lanes per row, activations read from global
+// memory) remains for A/B comparison and for the cross-workgroup split-K path
+// that runs when the caller passes a workspace and forces slices.
 #include "qmv_device.h"
 #include "qmv_internal.h"
 
 namespace qmv {
 
-// ------------------------------------------------------ activation quantizer
-// One 32-lane half wave per block of 32 values: amax and the block sum are
-// half-wave reductions; the divisions are IEEE fp32 (no fast-math), and
-// roundf rounds halfway cases away from zero.
-__global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t ldx,
-                                                  int n_tok, int k, int8_t* __restrict__ qs,
-                                                  float* __restrict__ d, int32_t* __restrict__ s) {
-  const int nb = k / 32;
-  const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (blk >= (int64_t)n_tok * nb) return;  // whole half-waves leave together
-  const int i = threadIdx.x & 31;
-  const int64_t t = blk / nb, b = blk % nb;
-  const float v = x[t * ldx + 32 * b + i];
-  float amax = fabsf(v);
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-  const float db = amax / 127.0f;
-  int q = 0;
-  if (amax != 0.0f) {
-    q = static_cast<int>(roundf(v / db));
-    q = q > 127 ? 127 : (q < -127 ? -127 : q);
-  }
-  int sum = q;
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
-  qs[t * k + 32 * b + i] = static_cast<int8_t>(q);
-  if (i == 0) {
-    d[t * nb + b] = db;
-    s[t * nb + b] = sum;
-  }
-}
-
-hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
-                           int32_t* s, hipStream_t st) {
-  const int64_t blocks = (int64_t)n_tok * (k / 32);
-  const int64_t grid = (blocks + 7) / 8;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)grid), dim3(256), 0, st, x, ldx, n_tok, k, qs, d, s);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------- matvec
+// -------------------------------------------------------- lane-group kernel
 template <int F, int TM, int LPR, int R, bool SPLIT>
 __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, int64_t row_bytes,
                                                 int n_rows, int units, ActView xv, int n_tok,
@@ -166,12 +136,266 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, i
   }
 }
 
-// Variant table: (lanes per row group, rows per group).
+// ------------------------------------------------------- streaming kernel
+template <int F, int TM, int R, int NU, int WPB, int KS>
+__global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
+  static_assert(KS == 1 || KS == WPB, "a team is one wave or the whole workgroup");
+  static_assert(R * TM <= 64, "one output per lane");
+  constexpr int CH = 64 * NU;
+  constexpr int TPB = WPB / KS;  // teams per workgroup
+  constexpr int NT = 64 * WPB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int team = blockIdx.x * TPB + wave / KS;
+  const int n_teams = gridDim.x * TPB;
+  const int kw = wave % KS;
+  const int n_groups = (a.n_rows + R - 1) / R;
+  const int nch = (a.units + CH - 1) / CH;
+  const int mpw = (nch + KS - 1) / KS;  // chunks of one group per wave
+  const int my_groups = team < n_groups ? (n_groups - 1 - team) / n_teams + 1 : 0;
+  const int jobs = my_groups * mpw;
+  const int units = a.units;
+
+  // job j of this wave -> (row group, chunk)
+  auto job = [&](int j, int& g, int& c) {
+    const int i = j / mpw;
+    g = team + i * n_teams;
+    c = kw + KS * (j - i * mpw);
+  };
+  auto load_job = [&](int j, RawS<F> (&buf)[R][NU]) {
+    int g, c;
+    job(j, g, c);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* wr = a.w + (int64_t)min(g * R + r, a.n_rows - 1) * a.row_bytes;
+#pragma unroll
+      for (int q = 0; q < NU; ++q) load_unit_s(wr, min(c * CH + lane + 64 * q, units - 1), lane, buf[r][q]);
+    }
+  };
+
+  RawS<F> cur[R][NU];
+  if (jobs > 0) load_job(0, cur);
+
+  // stage the activation buffer (qs | d | s, the library layout) in LDS
+  {
+    const int n16 = a.act_bytes >> 4;
+    for (int base = 0; base < n16; base += 4 * NT) {
+      u32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + threadIdx.x + i * NT;
+        if (idx < n16) v[i] = ld16(a.xq + 16 * (int64_t)idx);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + threadIdx.x + i * NT;
+        if (idx < n16) reinterpret_cast<u32x4a*>(s_mem)[idx] = v[i];
+      }
+    }
+  }
+  __syncthreads();
+  const Act x{reinterpret_cast<const int8_t*>(s_mem),
+              reinterpret_cast<const float*>(s_mem + a.off_d),
+              reinterpret_cast<const int32_t*>(s_mem + a.off_s), a.k, a.nb};
+  float* red = reinterpret_cast<float*>(s_mem + a.act_bytes);  // [KS][R*TM]
+
+  float acc[R][TM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[r][t] = 0.f;
+
+  for (int j = 0; j < jobs; ++j) {
+    RawS<F> nxt[R][NU];
+    load_job(min(j + 1, jobs - 1), nxt);
+    int g, c;
+    job(j, g, c);
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int uraw = c * CH + lane + 64 * q;
+      const bool ok = uraw < units;
+      const int u = ok ? uraw : units - 1;
+      Dec<F> dec[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) decode_unit(expand(cur[r][q]), u, dec[r]);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        XFrag<F> xf;
+        load_xfrag<F>(x, t < a.n_tok ? t : a.n_tok - 1, u, xf);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float v = unit_value(dec[r], xf);
+          acc[r][t] += ok ? v : 0.f;
+        }
+      }
+    }
+    if (j % mpw == mpw - 1) {  // last chunk of the group: reduce and store
+      float outv = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          const float sv = wave_sum(acc[r][t]);
+          outv = lane == r * TM + t ? sv : outv;
+          acc[r][t] = 0.f;
+        }
+      const int r = lane / TM, t = lane % TM;
+      const int row = g * R + r;
+      if constexpr (KS == 1) {
+        if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
+      } else {
+        if (lane < R * TM) red[kw * R * TM + lane] = outv;
+        __syncthreads();
+        if (threadIdx.x < R * TM) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < KS; ++w) sum += red[w * R * TM + threadIdx.x];
+          const int rr = threadIdx.x / TM, tt = threadIdx.x % TM;
+          const int row2 = g * R + rr;
+          if (tt < a.n_tok && row2 < a.n_rows) a.y[(int64_t)tt * a.ldy + row2] = sum;
+        }
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int q = 0; q < NU; ++q) cur[r][q] = nxt[r][q];
+  }
+}
+
+// ------------------------------------------------------------ flat kernel
+// One wave per group of R rows, launched for every group at once (no
+// persistent loop): the wave issues all the weight loads of its first chunk
+// of 64*NU units (one chunk covers the row in the configurations it is
+// chosen for) and, with XL false, the activation fragments of the chunk right
+// behind them, so both latencies overlap; then it decodes, reduces with DPP
+// and stores.  XL true stages the activation buffer in LDS per workgroup
+// instead (for token counts whose fragments would not fit in registers).
+template <int F, int TM, int R, int NU, int WPB, bool XL>
+__global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
+  static_assert(R * TM <= 64, "one output per lane");
+  constexpr int CH = 64 * NU;
+  constexpr int NT = 64 * WPB;
+  constexpr int TX = XL ? 1 : TM;  // prefetched fragments per unit
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WPB + wave) * R;
+  const int units = a.units;
+  const int nch = (units + CH - 1) / CH;
+  const uint8_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
+
+  RawS<F> cur[R][NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+
+  const Act gx{reinterpret_cast<const int8_t*>(a.xq), reinterpret_cast<const float*>(a.xq + a.off_d),
+               reinterpret_cast<const int32_t*>(a.xq + a.off_s), a.k, a.nb};
+  const Act lx{reinterpret_cast<const int8_t*>(s_mem),
+               reinterpret_cast<const float*>(s_mem + a.off_d),
+               reinterpret_cast<const int32_t*>(s_mem + a.off_s), a.k, a.nb};
+  XFrag<F> xf[NU][TX];
+  if constexpr (XL) {
+    const int n16 = a.act_bytes >> 4;
+    for (int base = 0; base < n16; base += 4 * NT) {
+      u32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + threadIdx.x + i * NT;
+        if (idx < n16) v[i] = ld16(a.xq + 16 * (int64_t)idx);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + threadIdx.x + i * NT;
+        if (idx < n16) reinterpret_cast<u32x4a*>(s_mem)[idx] = v[i];
+      }
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int q = 0; q < NU; ++q)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        load_xfrag<F>(gx, t < a.n_tok ? t : a.n_tok - 1, min(lane + 64 * q, units - 1), xf[q][t]);
+  }
+
+  float acc[R][TM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[r][t] = 0.f;
+
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) {  // rows longer than one chunk: plain (unpipelined) loads
+#pragma unroll
+      for (int q = 0; q < NU; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          load_unit_s(wr[r], min(c * CH + lane + 64 * q, units - 1), lane, cur[r][q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int uraw = c * CH + lane + 64 * q;
+      const bool ok = uraw < units;
+      const int u = ok ? uraw : units - 1;
+      Dec<F> dec[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) decode_unit(expand(cur[r][q]), u, dec[r]);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int tt = t < a.n_tok ? t : a.n_tok - 1;
+        XFrag<F> f;
+        if constexpr (XL)
+          load_xfrag<F>(lx, tt, u, f);
+        else if (c == 0)
+          f = xf[q][t];
+        else
+          load_xfrag<F>(gx, tt, u, f);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float v = unit_value(dec[r], f);
+          acc[r][t] += ok ? v : 0.f;
+        }
+      }
+    }
+  }
+
+  float outv = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const float sv = wave_sum(acc[r][t]);
+      outv = lane == r * TM + t ? sv : outv;
+    }
+  const int r = lane / TM, t = lane % TM;
+  const int row = row0 + r;
+  if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
+}
+
+// Variant table.  Indices are part of the tuning interface (qmv_set_tuning).
+//   kind, lpr, rows, nu, wpb, ks, xl, name
 const Variant kVariants[] = {
-    {64, 1, "lpr64_r1"}, {64, 2, "lpr64_r2"}, {32, 1, "lpr32_r1"},
-    {32, 2, "lpr32_r2"}, {16, 1, "lpr16_r1"}, {16, 2, "lpr16_r2"},
+    {0, 64, 2, 0, 4, 1, 0, "lpr64_r2"},       {0, 32, 2, 0, 4, 1, 0, "lpr32_r2"},
+    {1, 64, 1, 2, 4, 1, 1, "st_w4_r1_u2"},    {1, 64, 2, 2, 4, 1, 1, "st_w4_r2_u2"},
+    {1, 64, 1, 3, 4, 1, 1, "st_w4_r1_u3"},    {1, 64, 1, 2, 16, 1, 1, "st_w16_r1_u2"},
+    {1, 64, 4, 1, 8, 1, 1, "st_w8_r4_u1"},    {1, 64, 1, 2, 16, 16, 1, "st_k16_r1_u2"},
+    {2, 64, 1, 2, 4, 1, 0, "fl_w4_r1_u2_g"},  {2, 64, 2, 2, 4, 1, 0, "fl_w4_r2_u2_g"},
+    {2, 64, 1, 3, 4, 1, 0, "fl_w4_r1_u3_g"},  {2, 64, 1, 4, 4, 1, 0, "fl_w4_r1_u4_g"},
+    {2, 64, 1, 7, 4, 1, 0, "fl_w4_r1_u7_g"},  {2, 64, 1, 2, 4, 1, 1, "fl_w4_r1_u2_l"},
+    {2, 64, 1, 2, 16, 1, 1, "fl_w16_r1_u2_l"}, {2, 64, 1, 3, 16, 1, 1, "fl_w16_r1_u3_l"},
+    {2, 64, 1, 7, 8, 1, 1, "fl_w8_r1_u7_l"},  {2, 64, 2, 2, 16, 1, 1, "fl_w16_r2_u2_l"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+static int g_bpc_override = 0;  // tuning: workgroups per CU cap (0 = occupancy)
+void set_blocks_per_cu(int v) { g_bpc_override = v; }
 
 template <int F, int TM, int LPR, int R>
 static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
@@ -190,15 +414,90 @@ static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm) {
+  if (v.kind == 2) return v.xl || tm > 4 ? static_cast<size_t>(act_bytes) : 0;
+  return static_cast<size_t>(act_bytes + (int64_t)v.ks * v.rows * tm * 4);
+}
+
+static StreamArgs stream_args(const MatvecLaunch& a) {
+  StreamArgs sa;
+  sa.w = a.w;
+  sa.row_bytes = a.row_bytes;
+  sa.n_rows = a.n_rows;
+  sa.units = a.units;
+  sa.xq = a.xq;
+  sa.act_bytes = (int)a.act_bytes;
+  sa.off_d = (int)a.off_d;
+  sa.off_s = (int)a.off_s;
+  sa.k = a.x.k;
+  sa.nb = a.x.nb;
+  sa.n_tok = a.n_tok;
+  sa.y = a.y;
+  sa.ldy = a.ldy;
+  return sa;
+}
+
+template <int F, int TM, int R, int NU, int WPB, int KS>
+static hipError_t run_stream(const MatvecLaunch& a, hipStream_t st) {
+  auto kern = k_stream<F, TM, R, NU, WPB, KS>;
+  const size_t lds = (size_t)a.act_bytes + (size_t)KS * R * TM * 4;
+  // resident workgroups per CU allowed by registers and waves, measured once
+  static const int occ = [&] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * WPB, 0) != hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  int bpc = g_bpc_override > 0 ? g_bpc_override : occ;
+  const int by_lds = (int)((size_t)a.lds_per_cu / (lds > 0 ? lds : 1));
+  if (bpc > by_lds) bpc = by_lds;
+  if (bpc < 1) bpc = 1;
+  constexpr int TPB = WPB / KS;
+  const int64_t groups = (a.n_rows + R - 1) / R;
+  const int64_t need = (groups + TPB - 1) / TPB;
+  const int64_t cap = (int64_t)a.cus * bpc;
+  const unsigned grid = (unsigned)(need < cap ? need : cap);
+  StreamArgs sa = stream_args(a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, st, sa);
+  return hipGetLastError();
+}
+
+template <int F, int TM, int R, int NU, int WPB, bool XL>
+static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
+  if constexpr (!XL && TM > 4) {
+    // fragments of more than four tokens do not fit in registers: stage them
+    return run_flat<F, TM, R, NU, WPB, true>(a, st);
+  } else {
+    const size_t lds = XL ? (size_t)a.act_bytes : 0;
+    const int64_t groups = (a.n_rows + R - 1) / R;
+    const unsigned grid = (unsigned)((groups + WPB - 1) / WPB);
+    StreamArgs sa = stream_args(a);
+    hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+    return hipGetLastError();
+  }
+}
+
 template <int F, int TM>
 static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
   switch (a.variant) {
-    case 0: return run_mv<F, TM, 64, 1>(a, st);
-    case 1: return run_mv<F, TM, 64, 2>(a, st);
-    case 2: return run_mv<F, TM, 32, 1>(a, st);
-    case 3: return run_mv<F, TM, 32, 2>(a, st);
-    case 4: return run_mv<F, TM, 16, 1>(a, st);
-    case 5: return run_mv<F, TM, 16, 2>(a, st);
+    case 0: return run_mv<F, TM, 64, 2>(a, st);
+    case 1: return run_mv<F, TM, 32, 2>(a, st);
+    case 2: return run_stream<F, TM, 1, 2, 4, 1>(a, st);
+    case 3: return run_stream<F, TM, 2, 2, 4, 1>(a, st);
+    case 4: return run_stream<F, TM, 1, 3, 4, 1>(a, st);
+    case 5: return run_stream<F, TM, 1, 2, 16, 1>(a, st);
+    case 6: return run_stream<F, TM, 4, 1, 8, 1>(a, st);
+    case 7: return run_stream<F, TM, 1, 2, 16, 16>(a, st);
+    case 8: return run_flat<F, TM, 1, 2, 4, false>(a, st);
+    case 9: return run_flat<F, TM, 2, 2, 4, false>(a, st);
+    case 10: return run_flat<F, TM, 1, 3, 4, false>(a, st);
+    case 11: return run_flat<F, TM, 1, 4, 4, false>(a, st);
+    case 12: return run_flat<F, TM, 1, 7, 4, false>(a, st);
+    case 13: return run_flat<F, TM, 1, 2, 4, true>(a, st);
+    case 14: return run_flat<F, TM, 1, 2, 16, true>(a, st);
+    case 15: return run_flat<F, TM, 1, 3, 16, true>(a, st);
+    case 16: return run_flat<F, TM, 1, 7, 8, true>(a, st);
+    case 17: return run_flat<F, TM, 2, 2, 16, true>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -219,78 +518,6 @@ hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st) {
     case FIQ4_XS: return run_mv_tokens<FIQ4_XS>(a, st);
     default: return hipErrorInvalidValue;
   }
-}
-
-// ------------------------------------------------------------- block dots
-// One thread per (token, row, 32-block), through the same load, decode and
-// integer dot routines as the matvec kernels.
-template <int F>
-__global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ w, int64_t row_bytes,
-                                                    int n_rows, int units, ActView xv, int n_tok,
-                                                    int32_t* __restrict__ out) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (int64_t)n_tok * n_rows * units) return;
-  const int b = (int)(gid % units);
-  const int row = (int)((gid / units) % n_rows);
-  const int t = (int)(gid / ((int64_t)units * n_rows));
-  const Act x{xv.qs, xv.d, xv.s, xv.k, xv.nb};
-  const uint8_t* wr = w + (int64_t)row * row_bytes;
-  if constexpr (F == FQ4_K) {
-    // 32-block b = sub-block jj of super-block sb lives in the low (jj even)
-    // or high (jj odd) nibbles of units 2*(jj/2) and 2*(jj/2)+1
-    const int sb = b >> 3, jj = b & 7;
-    const int u0 = 8 * sb + 2 * (jj >> 1);
-    int A = 0, B = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      Raw<F> raw;
-      Dec<F> dec;
-      XFrag<F> xf;
-      load_unit(wr, u0 + h, raw);
-      decode_unit(raw, u0 + h, dec);
-      load_xfrag<F>(x, t, u0 + h, xf);
-      int lo, hi;
-      unit_int(dec, xf, lo, hi);
-      A += (jj & 1) ? dec.sc1 * hi : dec.sc0 * lo;
-      if (h == 0) B = (jj & 1) ? dec.m1 * xf.s1 : dec.m0 * xf.s0;
-    }
-    out[2 * gid] = A;
-    out[2 * gid + 1] = B;
-  } else {
-    Raw<F> raw;
-    Dec<F> dec;
-    XFrag<F> xf;
-    load_unit(wr, b, raw);
-    decode_unit(raw, b, dec);
-    load_xfrag<F>(x, t, b, xf);
-    int lo, hi;
-    unit_int(dec, xf, lo, hi);
-    int p = lo + hi;
-    if constexpr (F == FIQ4_XS) p *= dec.ls;
-    out[gid] = p;
-  }
-}
-
-hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,
-                             ActView x, int n_tok, int32_t* out, hipStream_t st) {
-  const int64_t n = (int64_t)n_tok * n_rows * units;
-  const unsigned grid = (unsigned)((n + 255) / 256);
-  switch (fmt) {
-    case FQ8_0:
-      hipLaunchKernelGGL(k_block_dots<FQ8_0>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
-                         units, x, n_tok, out);
-      break;
-    case FQ4_K:
-      hipLaunchKernelGGL(k_block_dots<FQ4_K>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
-                         units, x, n_tok, out);
-      break;
-    case FIQ4_XS:
-      hipLaunchKernelGGL(k_block_dots<FIQ4_XS>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
-                         units, x, n_tok, out);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 }  // namespace qmv
