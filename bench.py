@@ -46,6 +46,10 @@ WORKLOADS = {
     "q8_0_head_152064x5120": (0, 152064, 5120, (1, 2, 4, 8, 16)),
 }
 FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS"}
+# MoE decode: 128 IQ4_XS experts, gate+up 3072 x 4096 and down 4096 x 1536 per
+# expert, top-8 routing
+MOE = dict(name="moe_iq4_xs_e128", experts=128, top_k=8, gate_up=(3072, 4096), down=(4096, 1536),
+           tokens=(1, 6, 16, 64))
 KERNEL_SOURCES = ("qmv_device.h", "qmv_matvec.hip", "qmv_quant.hip", "qmv_api.hip")
 
 
@@ -105,6 +109,63 @@ class Ring:
                    ws=self.ws)
 
 
+class MoeRing:
+    """Device-resident inputs of the MoE decode workload: two copies of the
+    expert tensors (alternating), 16 routings, activations and buffers."""
+
+    def __init__(self, torch, qmv, t):
+        from synth import make_routing, make_x
+        from synth.device import make_weights_t
+
+        e, self.top_k = MOE["experts"], MOE["top_k"]
+        self.t = t
+        (ng, kg), (nd, kd) = MOE["gate_up"], MOE["down"]
+        self.shape = (e, ng, kg, nd, kd)
+        name = MOE["name"]
+        gu = make_weights_t(2, e * ng, kg, f"{name}/gate_up", device="cuda")
+        dn = make_weights_t(2, e * nd, kd, f"{name}/down", device="cuda")
+        self.gu = [gu, gu.clone()]
+        self.dn = [dn, dn.clone()]
+        self.bytes_per_expert = (gu.numel() + dn.numel()) // e
+        self.routes = []
+        for r in range(16):
+            ids, rw = make_routing(t, e, self.top_k, f"{name}/route{r}")
+            self.routes.append((torch.from_numpy(ids).cuda(), torch.from_numpy(rw).cuda(),
+                                len(set(ids.reshape(-1).tolist()))))
+        xs = make_x(8 * t, kg, f"{name}/x").reshape(8, t, kg)
+        hs = make_x(8 * t * self.top_k, kd, f"{name}/h").reshape(8, t * self.top_k, kd)
+        self.x = [torch.from_numpy(xs[i]).cuda() for i in range(8)]
+        self.h = [torch.from_numpy(hs[i]).cuda() for i in range(8)]
+        self.xq = torch.empty(qmv.act_bytes(t, kg), dtype=torch.uint8, device="cuda")
+        self.hq = torch.empty(qmv.act_bytes(t * self.top_k, kd), dtype=torch.uint8, device="cuda")
+        self.y_gu = torch.empty((t, self.top_k, ng), dtype=torch.float32, device="cuda")
+        self.y_dn = torch.empty((t, nd), dtype=torch.float32, device="cuda")
+        self.ws_gu = torch.zeros(qmv.moe_workspace_bytes(2, e, ng, kg, t, self.top_k),
+                                 dtype=torch.uint8, device="cuda")
+        self.ws_dn = torch.zeros(qmv.moe_workspace_bytes(2, e, nd, kd, t, self.top_k),
+                                 dtype=torch.uint8, device="cuda")
+
+    def avg_bytes(self, steps):
+        """Weight bytes a step reads, averaged over the routings it cycles."""
+        return sum(self.routes[i % 16][2] for i in range(steps)) * self.bytes_per_expert / steps
+
+    def gate_up(self, qmv, i):
+        e, ng, kg, _, _ = self.shape
+        ids = self.routes[i % 16][0]
+        qmv.moe_matvec(2, self.gu[i % 2], e, ng, kg, self.xq, False, ids, None, self.ws_gu, y=self.y_gu)
+
+    def down(self, qmv, i):
+        e, _, _, nd, kd = self.shape
+        ids, rw, _ = self.routes[i % 16]
+        qmv.moe_matvec(2, self.dn[i % 2], e, nd, kd, self.hq, True, ids, rw, self.ws_dn, y=self.y_dn)
+
+    def step(self, qmv, i):
+        qmv.quantize_act(self.x[i % 8], out=self.xq)
+        self.gate_up(qmv, i)
+        qmv.quantize_act(self.h[i % 8], out=self.hq)
+        self.down(qmv, i)
+
+
 def capture(torch, fn, count, start=0):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -143,6 +204,118 @@ def kernel_us(torch, qmv, ring, reps=20):
     return e0.elapsed_time(e1) * 1e3 / (reps * per)
 
 
+def timed_replays(torch, fn, per, reps=10):
+    """Average time of one fn(i) over back-to-back replays of a graph of
+    `per` calls (HIP events around the replays)."""
+    g = capture(torch, fn, per)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * per)
+
+
+def moe_cpu_baseline(ring, min_seconds=10.0):
+    """The CPU oracle on the MoE step for this token count: quantize x and h,
+    gate+up and down routed matvecs over all rows (routing 0)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    e, ng, kg, nd, kd = ring.shape
+    ids, rw = synth.make_routing(ring.t, e, ring.top_k, f"{MOE['name']}/route0")
+    used = sorted(set(ids.reshape(-1).tolist()))
+    remap = {ex: i for i, ex in enumerate(used)}
+    # only the routed experts' weights are generated; ids are renumbered onto them
+    gu = np.concatenate([synth.make_weights(2, e * ng, kg, f"{MOE['name']}/gate_up",
+                                            rows=(ex * ng, (ex + 1) * ng)).data for ex in used])
+    dn = np.concatenate([synth.make_weights(2, e * nd, kd, f"{MOE['name']}/down",
+                                            rows=(ex * nd, (ex + 1) * nd)).data for ex in used])
+    ids2 = np.vectorize(remap.get)(ids).astype(np.int32)
+    x = synth.make_x(ring.t, kg, f"{MOE['name']}/x")
+    h = synth.make_x(ring.t * ring.top_k, kd, f"{MOE['name']}/h")
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(cores)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        qs, d, s = oracle.quantize_act(x)
+        oracle.moe_matvec(2, gu, len(used), ng, kg, qs, d, s, ids2, None, False)
+        qs, d, s = oracle.quantize_act(h)
+        oracle.moe_matvec(2, dn, len(used), nd, kd, qs, d, s, ids2, rw, True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    nbytes = len(used) * ring.bytes_per_expert
+    return {"value": round(nbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"MoE step at {ring.t} token(s) (routing 0, {len(used)} experts), {reps} repetitions "
+                      f"in {el:.1f} s"}
+
+
+def bench_moe(args, torch, qmv):
+    t = args.tokens
+    log(f"bench: MoE T={t}: generating inputs")
+    ring = MoeRing(torch, qmv, t)
+    per = 64
+    g_full = capture(torch, lambda i: ring.step(qmv, i), per)
+    tail = args.steps % per
+    g_tail = capture(torch, lambda i: ring.step(qmv, i), tail) if tail else None
+    warm_tail = args.warmup % per
+    run_steps(torch, (g_full, per, capture(torch, lambda i: ring.step(qmv, i), warm_tail)
+                      if warm_tail else None), args.warmup)
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} MoE steps")
+    t0 = time.perf_counter()
+    run_steps(torch, (g_full, per, g_tail), args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_bytes = ring.avg_bytes(args.steps)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    gu_us = timed_replays(torch, lambda i: ring.gate_up(qmv, i), per)
+    dn_us = timed_replays(torch, lambda i: ring.down(qmv, i), per)
+    avg_u = step_bytes / ring.bytes_per_expert
+    gu_bytes = avg_u * ring.gu[0].numel() / ring.shape[0]
+    dn_bytes = avg_u * ring.dn[0].numel() / ring.shape[0]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    cpu = None if args.no_cpu else moe_cpu_baseline(ring)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"MoE IQ4_XS 128 experts top-8, gate+up 3072x4096 + down 4096x1536, "
+                               f"{t} token(s)", "tokens": t, "avg_distinct_experts": round(avg_u, 2),
+                   "weight_bytes_per_step": round(step_bytes),
+                   "step": "quantize x + gate_up routed matvec + quantize h + down routed matvec"},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gate_up routed matvec", "kernel_us": round(gu_us, 3),
+                     "algorithmic_bytes_per_launch": round(gu_bytes)},
+        "down_kernel": {"kernel_us": round(dn_us, 3), "weight_GBps": round(dn_bytes / (dn_us * 1e-6) / 1e9, 1),
+                        "algorithmic_bytes_per_launch": round(dn_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
     """The CPU oracle (quantize + matvec, the same workload) on this host,
     repeated until at least min_seconds of work."""
@@ -173,7 +346,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="q4_k_14336x4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="q4_k_14336x4096", choices=sorted(WORKLOADS) + [MOE["name"]])
     ap.add_argument("--tokens", type=int, default=1)
     ap.add_argument("--all-tokens", action="store_true",
                     help="also time the matvec at every token count of the workload")
@@ -195,6 +368,11 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.workload == MOE["name"]:
+        if not 1 <= args.tokens <= 64:
+            print("--tokens must be 1..64 for the MoE workload", file=sys.stderr)
+            return 2
+        return bench_moe(args, torch, qmv)
     fmt, n, k, token_list = WORKLOADS[args.workload]
     t = args.tokens
     if not 1 <= t <= 16:

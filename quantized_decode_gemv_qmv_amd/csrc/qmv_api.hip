@@ -198,8 +198,9 @@ int choose_slices(const Variant& v, int64_t n_rows, int64_t k) {
 // the counters of another.
 constexpr int64_t kSplitCounterBytes = kSplitMaxRows;  // kSplitMaxRows / 4 ints
 
-// MoE workspace: [256 B status][counters of kMoeMaxRows / 4 row tiles][per-slot
-// outputs], fixed offsets for the same reason.
+// MoE workspace: [256 B status][reserved area][per-slot outputs of the
+// route-weighted combine], at fixed offsets so that calls of different shapes
+// can share one workspace.
 constexpr int64_t kMoeMaxRows = 65536;
 constexpr int64_t kMoeStatusBytes = 256;
 constexpr int64_t kMoeCounterBytes = kMoeMaxRows;  // kMoeMaxRows / 4 ints
@@ -404,7 +405,6 @@ QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_expert
   a.y = y;
   uint8_t* b = static_cast<uint8_t*>(ws);
   a.err = reinterpret_cast<int*>(b);
-  a.cnt = reinterpret_cast<int*>(b + kMoeStatusBytes);
   a.part = reinterpret_cast<float*>(b + kMoePartOffset);
   hipError_t e = launch_moe(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;

@@ -110,7 +110,6 @@ struct MoeLaunch {
   float* y;
   // workspace
   int* err;     // dropped-slot count of the call
-  int* cnt;     // one arrival counter per row tile (route-weighted combine)
   float* part;  // [n_tok * top_k][n_rows] per-slot outputs (combine only)
 };
 

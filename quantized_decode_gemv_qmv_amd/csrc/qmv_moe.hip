@@ -4,20 +4,25 @@
 // batches of up to 64 tokens, and expert-grouped quantized MoE where each
 // active expert runs once over all the tokens routed to it.
 //
-// Grid: x = row tiles of the expert matrices, y = rank a of an active expert
-// (upper bound min(n_experts, n_tok * top_k)).  Each workgroup rebuilds the
-// routing metadata it needs in LDS from the ids (at most 1024 slots), so the
-// whole call is one launch:
+// k_moe grid: x = row tiles of the expert matrices, y = rank a of an active
+// expert (upper bound min(n_experts, n_tok * top_k)).  Each workgroup rebuilds
+// the routing it needs in LDS from the ids (at most 1024 slots), so routing
+// costs no launch of its own:
 //   1. a bitmap of the experts that appear in ids; its population count is
 //      the number of active experts U, and the a-th set bit is this
 //      workgroup's expert e (workgroups with a >= U leave);
 //   2. the slots routed to e, compacted in slot order with wave ballots.
-// Each lane group then decodes its row's units of W[e] into registers once and
-// reuses them for every slot routed to e, so each active expert's weights are
-// read from HBM exactly once per call.
-// Route-weighted combine (y[t] = sum_s w[t][s] * y_slot): per-slot outputs go
-// to the workspace and the last workgroup to finish a row tile sums them in
-// slot order -- deterministic, no float atomics, no second launch.
+// A lane group of LPR lanes owns one row of W[e]: it issues all the loads of
+// the row at once (NU units per lane, block headers shared by lane quads),
+// decodes them into registers once and reuses them for every slot routed to
+// e, so each active expert's weights are read from HBM once per call.  The
+// next slot's activation fragments are fetched while the current slot is
+// computed.
+//
+// Route-weighted combine (y[t] = sum_s w[t][s] * y_slot): k_moe writes each
+// slot's output row to the workspace, and k_moe_combine sums them in slot
+// order -- deterministic, and the kernel boundary orders the two without any
+// device-wide fence.
 #include "qmv_device.h"
 #include "qmv_internal.h"
 
@@ -26,14 +31,25 @@ namespace qmv {
 constexpr int kMaxSlots = 64 * 16;
 constexpr int kMaxExperts = 1024;
 
-template <int F, int LPR, int UPL>
+// Sum over the LPR consecutive lanes of a lane group; every lane of the group
+// gets the result.
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v = sum8(v);
+  v += dpp_f<DPP_MIRROR>(v);  // 16-lane row sums
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPR == 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <int F, int LPR, int NU>
 __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
   constexpr int GPW = 64 / LPR;
   constexpr int RWG = 4 * GPW;  // rows per workgroup
   __shared__ uint32_t s_bits[kMaxExperts / 32];
   __shared__ int s_list[kMaxSlots];
   __shared__ int s_wcnt[4];
-  __shared__ int s_e, s_U, s_last;
+  __shared__ int s_e, s_U;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_slots = a.n_tok * a.top_k;
@@ -80,9 +96,9 @@ __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
   __syncthreads();
   const int U = s_U;
 
-  // Workgroups of active-expert rank 0 also own the outputs nobody else
-  // writes: dropped slots (per-slot mode) or, with no active expert at all,
-  // the whole combined output.
+  // Workgroups of active-expert rank 0 also write what no expert writes: the
+  // dropped-slot count (workgroup (0, 0)) and, with one output per slot, the
+  // zero rows of dropped slots.
   if (blockIdx.y == 0) {
     if (blockIdx.x == 0) {
       int dsum = dropped;
@@ -98,11 +114,6 @@ __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
         const int i = idx / RWG, row = r0 + idx % RWG;
         const int e = a.ids[i];
         if (row < a.n_rows && (e < 0 || e >= a.n_experts)) a.y[(int64_t)i * a.n_rows + row] = 0.f;
-      }
-    } else if (U == 0) {
-      for (int idx = tid; idx < a.n_tok * RWG; idx += 256) {
-        const int t = idx / RWG, row = r0 + idx % RWG;
-        if (row < a.n_rows) a.y[(int64_t)t * a.n_rows + row] = 0.f;
       }
     }
   }
@@ -124,108 +135,107 @@ __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
     __syncthreads();
   }
 
-  // this lane group's row of W[e], decoded once into registers
+  // this lane group's row of W[e]: every load issued at once, decoded once
   const int g = lane / LPR, gl = lane % LPR;
   const int row = r0 + wave * GPW + g;
-  const uint8_t* wr =
-      a.w + ((int64_t)e * a.n_rows + min(row, a.n_rows - 1)) * a.row_bytes;
+  const uint8_t* wr = a.w + ((int64_t)e * a.n_rows + min(row, a.n_rows - 1)) * a.row_bytes;
   const Act x{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
-  Dec<F> dec[UPL];
+  const int units = a.units;
+  Dec<F> dec[NU];
   {
-    Raw<F> raw[UPL];
+    RawS<F> raw[NU];
 #pragma unroll
-    for (int ui = 0; ui < UPL; ++ui) {
-      const int u = gl + LPR * ui;
-      if (u < a.units) load_unit(wr, u, raw[ui]);
-    }
+    for (int q = 0; q < NU; ++q) load_unit_s(wr, min(gl + LPR * q, units - 1), lane, raw[q]);
 #pragma unroll
-    for (int ui = 0; ui < UPL; ++ui) {
-      const int u = gl + LPR * ui;
-      if (u < a.units) decode_unit(raw[ui], u, dec[ui]);
-    }
+    for (int q = 0; q < NU; ++q) decode_unit(expand(raw[q]), min(gl + LPR * q, units - 1), dec[q]);
   }
 
+  auto slot_row = [&](int j) {
+    const int i = s_list[j];
+    return a.x_per_slot ? i : i / a.top_k;
+  };
+  XFrag<F> xf[NU];
+  if (n_e > 0) {
+    const int xr = slot_row(0);
+#pragma unroll
+    for (int q = 0; q < NU; ++q) load_xfrag<F>(x, xr, min(gl + LPR * q, units - 1), xf[q]);
+  }
   for (int j = 0; j < n_e; ++j) {
     const int i = s_list[j];
-    const int xr = a.x_per_slot ? i : i / a.top_k;
+    XFrag<F> nx[NU];
+    const int xr_next = slot_row(min(j + 1, n_e - 1));
+#pragma unroll
+    for (int q = 0; q < NU; ++q) load_xfrag<F>(x, xr_next, min(gl + LPR * q, units - 1), nx[q]);
     float acc = 0.f;
 #pragma unroll
-    for (int ui = 0; ui < UPL; ++ui) {
-      const int u = gl + LPR * ui;
-      if (u < a.units) {
-        XFrag<F> xf;
-        load_xfrag<F>(x, xr, u, xf);
-        acc += unit_value(dec[ui], xf);
-      }
+    for (int q = 0; q < NU; ++q) {
+      const float v = unit_value(dec[q], xf[q]);
+      acc += gl + LPR * q < units ? v : 0.f;
     }
-    acc = group_sum<LPR>(acc);
+    acc = lane_group_sum<LPR>(acc);
     if (gl == 0 && row < a.n_rows) {
-      if (a.rw == nullptr)
-        a.y[(int64_t)i * a.n_rows + row] = acc;
-      else
-        __hip_atomic_store(&a.part[(int64_t)i * a.n_rows + row], acc, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      float* out = a.rw == nullptr ? a.y : a.part;
+      out[(int64_t)i * a.n_rows + row] = acc;
     }
-  }
-
-  if (a.rw != nullptr) {
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&a.cnt[blockIdx.x], 1);
-      s_last = (prev == U - 1);
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      for (int idx = tid; idx < a.n_tok * RWG; idx += 256) {
-        const int t = idx / RWG, rr = r0 + idx % RWG;
-        if (rr >= a.n_rows) continue;
-        float sum = 0.f;
-        for (int s = 0; s < a.top_k; ++s) {
-          const int sl = t * a.top_k + s;
-          const int es = a.ids[sl];
-          if (es >= 0 && es < a.n_experts)
-            sum += a.rw[sl] * __hip_atomic_load(&a.part[(int64_t)sl * a.n_rows + rr],
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        a.y[(int64_t)t * a.n_rows + rr] = sum;
-      }
-      if (tid == 0) atomicExch(&a.cnt[blockIdx.x], 0);
-    }
+#pragma unroll
+    for (int q = 0; q < NU; ++q) xf[q] = nx[q];
   }
 }
 
-static int moe_lpr(int units) { return units <= 128 ? 16 : (units <= 256 ? 32 : 64); }
+// y[t][n] = sum over valid slots s, in slot order, of rw[t][s] * part[t*top_k+s][n].
+__global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.n_tok * a.n_rows) return;
+  const int t = (int)(idx / a.n_rows), n = (int)(idx % a.n_rows);
+  float sum = 0.f;
+  for (int s = 0; s < a.top_k; ++s) {
+    const int sl = t * a.top_k + s;
+    const int e = a.ids[sl];
+    if (e >= 0 && e < a.n_experts) sum += a.rw[sl] * a.part[(int64_t)sl * a.n_rows + n];
+  }
+  a.y[idx] = sum;
+}
+
+// Lanes per row and units per lane for a row of `units` units.
+static int moe_lpr(int units) { return units <= 64 ? 16 : 64; }
+static int moe_nu(int units) {
+  const int lpr = moe_lpr(units);
+  const int nu = (units + lpr - 1) / lpr;
+  return nu <= 1 ? 1 : nu <= 2 ? 2 : nu <= 3 ? 3 : nu <= 4 ? 4 : 8;
+}
 
 int moe_rows_per_wg(int, int units) { return 4 * (64 / moe_lpr(units)); }
 
-template <int F, int LPR, int UPL>
+template <int F, int LPR, int NU>
 static hipError_t run_moe(const MoeLaunch& a, hipStream_t st) {
   constexpr int RWG = 4 * (64 / LPR);
   const unsigned tiles = (unsigned)((a.n_rows + RWG - 1) / RWG);
   const int slots = a.n_tok * a.top_k;
   const unsigned ranks = (unsigned)(slots < a.n_experts ? slots : a.n_experts);
-  hipLaunchKernelGGL((k_moe<F, LPR, UPL>), dim3(tiles, ranks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_moe<F, LPR, NU>), dim3(tiles, ranks), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.rw == nullptr) return e;
+  const int64_t outs = (int64_t)a.n_tok * a.n_rows;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
-}
-
-template <int F, int LPR>
-static hipError_t run_moe_upl(const MoeLaunch& a, hipStream_t st) {
-  const int upl = (a.units + LPR - 1) / LPR;
-  if (upl <= 1) return run_moe<F, LPR, 1>(a, st);
-  if (upl <= 2) return run_moe<F, LPR, 2>(a, st);
-  if (upl <= 4) return run_moe<F, LPR, 4>(a, st);
-  if (upl <= 8) return run_moe<F, LPR, 8>(a, st);
-  return hipErrorInvalidValue;
 }
 
 template <int F>
 static hipError_t run_moe_fmt(const MoeLaunch& a, hipStream_t st) {
-  switch (moe_lpr(a.units)) {
-    case 16: return run_moe_upl<F, 16>(a, st);
-    case 32: return run_moe_upl<F, 32>(a, st);
-    default: return run_moe_upl<F, 64>(a, st);
+  const int lpr = moe_lpr(a.units), nu = moe_nu(a.units);
+  if (lpr == 16) {
+    switch (nu) {
+      case 1: return run_moe<F, 16, 1>(a, st);
+      case 2: return run_moe<F, 16, 2>(a, st);
+      case 3: return run_moe<F, 16, 3>(a, st);
+      default: return run_moe<F, 16, 4>(a, st);
+    }
+  }
+  switch (nu) {
+    case 2: return run_moe<F, 64, 2>(a, st);
+    case 3: return run_moe<F, 64, 3>(a, st);
+    case 4: return run_moe<F, 64, 4>(a, st);
+    default: return run_moe<F, 64, 8>(a, st);
   }
 }
 
