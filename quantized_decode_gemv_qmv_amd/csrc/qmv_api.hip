@@ -124,8 +124,9 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //     issued at once), activations staged in LDS for Q8_0, prefetched from
 //     global memory for the 4-bit formats, units per lane sized so that one
 //     chunk covers the row;
-//   - more tokens: the variant that measured fastest for that format;
-// and the lane-group kernel when the activations do not fit in LDS.
+//   - more tokens: the variant that measured fastest for that format
+//     (mostly the multi-token kernel, whose LDS staging is chunked and so
+//     fits any K, which also makes it the fallback).
 int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t units = k / 32;
   const int cus = device_cus();
@@ -137,26 +138,25 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     if (n_tok <= 4)
       name = nu <= 2 ? "fl_w16_r1_u2_l" : nu <= 3 ? "fl_w16_r1_u3_l" : "fl_w4_r1_u4_g";
     else
-      name = "lpr32_r2";
+      name = "mu_l8_r4_u1_w4";
   } else if (type == QMV_Q4_K) {
     if (nu <= 2)
-      name = n_tok > 2 && n_tok <= 4 ? "st_w4_r2_u2" : "fl_w4_r2_u2_g";
+      name = n_tok == 1 ? "fl_w4_r2_u2_g"
+             : n_tok <= 4 ? "mu_l16_r2_u1_w8_k2"
+             : n_tok <= 8 ? "fl_w4_r2_u2_g"
+                          : "mu_l16_r2_u1_w8_k2";
     else
-      name = n_tok <= 2 ? "fl_w4_r1_u4_g" : "lpr64_r2";
+      name = n_tok <= 2 ? "fl_w4_r1_u4_g" : "mu_l16_r2_u1_w8_k4";
   } else {
     if (n_tok <= 1)
-      name = nu <= 2 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u4_g";
-    else if (n_tok <= 2)
-      name = nu <= 7 ? "fl_w4_r1_u7_g" : "fl_w4_r1_u4_g";
-    else if (n_tok <= 4)
-      name = "st_w16_r1_u2";
+      name = nu <= 2 ? "fl_w4_r2_u2_g" : nu <= 7 ? "fl_w4_r1_u7_g" : "fl_w4_r1_u4_g";
     else if (n_tok <= 8)
-      name = "fl_w16_r1_u2_l";
+      name = "st_w16_r1_u2";
     else
-      name = "lpr64_r2";
+      name = "mu_l16_r2_u1_w8_k4";
   }
   int v = find_variant(name);
-  if (!stream_fits(v, k, n_tok)) v = find_variant("lpr64_r2");
+  if (!stream_fits(v, k, n_tok)) v = find_variant("mu_l16_r2_u1_w8_k4");
   return v;
 }
 

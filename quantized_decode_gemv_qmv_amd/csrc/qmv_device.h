@@ -64,6 +64,21 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
 }
 
+// DPP lane moves inside a 16-lane row (gfx9 encodings): swap neighbours,
+// swap pairs, mirror each 8-lane half, mirror the row.
+enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+
+// Every control used here reads a lane inside the same row, so no lane is
+// ever out of bounds; bound_ctrl lets the move skip initialising its target.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
 // ------------------------------------------------------------ raw unit loads
 template <int F> struct Raw;
 
@@ -86,24 +101,31 @@ template <> struct Raw<FIQ4_XS> {
   u32x2 hdr;  // d | scales_h, scales_l[0..3]
 };
 
+// Unit loads take the row base and 32-bit byte offsets inside the row, so a
+// row base held in scalar registers needs no per-lane 64-bit address math.
 __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ8_0>& r) {
-  const uint8_t* p = row + 34 * u;
-  const uint32_t odd = (reinterpret_cast<uintptr_t>(p) >> 1) & 1u;
-  const uint8_t* base = odd ? p + 2 : p;
-  r.a = ld_w16(base);
-  r.b = ld_w16(base + 16);
-  r.h = ld_w2(odd ? p : p + 32);
+  const uint32_t off = 34u * (uint32_t)u;
+  // the block's alignment mod 4 decides which of its two halves is dword
+  // aligned: the quants (address 2 mod 4) or the scale (0 mod 4)
+  const uint32_t odd = (((uint32_t)reinterpret_cast<uintptr_t>(row) + off) >> 1) & 1u;
+  const uint32_t qoff = odd ? off + 2 : off;
+  const uint32_t hoff = odd ? off : off + 32;
+  r.a = ld_w16(row + qoff);
+  r.b = ld_w16(row + (qoff + 16));
+  r.h = ld_w2(row + hoff);
   r.odd = odd;
 }
 __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ4_K>& r) {
-  const uint8_t* blk = row + 144 * (u >> 3);
-  r.q = ld_w16(blk + 16 + 16 * (u & 7));
-  r.hdr = ld_w16(blk);
+  const uint32_t blk = 144u * ((uint32_t)u >> 3);
+  const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
+  r.q = ld_w16(row + qoff);
+  r.hdr = ld_w16(row + blk);
 }
 __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FIQ4_XS>& r) {
-  const uint8_t* blk = row + 136 * (u >> 3);
-  r.q = ld_w16(blk + 8 + 16 * (u & 7));
-  r.hdr = ld_w8(blk);
+  const uint32_t blk = 136u * ((uint32_t)u >> 3);
+  const uint32_t qoff = blk + 8 + 16 * ((uint32_t)u & 7);
+  r.q = ld_w16(row + qoff);
+  r.hdr = ld_w8(row + blk);
 }
 
 // Shared-header unit loads, for kernels whose lanes are all active and whose
@@ -128,20 +150,23 @@ __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane,
   load_unit(row, u, r.r);
 }
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ4_K>& r) {
-  const uint8_t* blk = row + 144 * (u >> 3);
-  r.q = ld_w16(blk + 16 + 16 * (u & 7));
-  r.h = *reinterpret_cast<const uint32_t*>(blk + 4 * (lane & 3));
+  const uint32_t blk = 144u * ((uint32_t)u >> 3);
+  const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
+  const uint32_t hoff = blk + 4 * ((uint32_t)lane & 3);
+  r.q = ld_w16(row + qoff);
+  r.h = *reinterpret_cast<const uint32_t*>(row + hoff);
 }
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FIQ4_XS>& r) {
-  const uint8_t* blk = row + 136 * (u >> 3);
-  r.q = ld_w16(blk + 8 + 16 * (u & 7));
-  r.h = *reinterpret_cast<const uint32_t*>(blk + 4 * (lane & 1));
+  const uint32_t blk = 136u * ((uint32_t)u >> 3);
+  const uint32_t qoff = blk + 8 + 16 * ((uint32_t)u & 7);
+  const uint32_t hoff = blk + 4 * ((uint32_t)lane & 1);
+  r.q = ld_w16(row + qoff);
+  r.h = *reinterpret_cast<const uint32_t*>(row + hoff);
 }
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
 // quad_perm controls: broadcast lane k of each quad (k * 0x55), and the
@@ -170,13 +195,17 @@ template <> struct Dec<FQ8_0> {
 template <> struct Dec<FIQ4_XS> {
   uint32_t q[8];
   float d;
-  int ls;  // effective sub-block scale, raw 6-bit value minus 32
+  int ls;     // effective sub-block scale, raw 6-bit value minus 32
+  float dls;  // d * ls, exact in fp32 (11-bit times 6-bit significand)
 };
 template <> struct Dec<FQ4_K> {
   uint32_t q[8];  // nibble values 0..15, one per byte
   float d, dmin;
   int sc0, sc1, m0, m1;  // sub-blocks j and j+1
   int h;                 // which 16-weight half of the sub-blocks
+  // d * sc and dmin * m of both sub-blocks, exact in fp32, so that applying
+  // a unit to a token needs no integer multiply
+  float ws0, ws1, wm0, wm1;
 };
 
 __device__ __forceinline__ void decode_unit(const Raw<FQ8_0>& r, int, Dec<FQ8_0>& o) {
@@ -214,6 +243,7 @@ __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FI
   const uint32_t hi2 = (r.hdr.x >> (16 + 2 * c)) & 3u;        // scales_h bits
   o.ls = static_cast<int>(lo4 | (hi2 << 4)) - 32;
   o.d = half_bits_to_float(r.hdr.x);
+  o.dls = o.d * static_cast<float>(o.ls);
   const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -245,6 +275,55 @@ __device__ __forceinline__ void decode_unit(const Raw<FQ4_K>& r, int u, Dec<FQ4_
   q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, j + 1, o.sc1, o.m1);
   o.d = half_bits_to_float(r.hdr.x);
   o.dmin = half_bits_to_float(r.hdr.x >> 16);
+  o.ws0 = o.d * static_cast<float>(o.sc0);
+  o.ws1 = o.d * static_cast<float>(o.sc1);
+  o.wm0 = o.dmin * static_cast<float>(o.m0);
+  o.wm1 = o.dmin * static_cast<float>(o.m1);
+  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.q[i] = v[i] & 0x0F0F0F0Fu;
+    o.q[4 + i] = (v[i] >> 4) & 0x0F0F0F0Fu;
+  }
+}
+
+// Decoding from shared-header loads.  Q8_0 and IQ4_XS decode as usual.  For
+// q4_K the lanes of an aligned pair hold units 2p and 2p+1 of a super-block,
+// which use the same two sub-blocks (2p', 2p'+1 with p' = p mod 4): each lane
+// unpacks the 6-bit (scale, min) of one sub-block -- sub-block u mod 8 -- folds
+// it into fp32 with d and dmin, and takes the other from its pair neighbour
+// over DPP, instead of unpacking both.
+__device__ __forceinline__ void decode_unit_s(const RawS<FQ8_0>& s, int u, Dec<FQ8_0>& o) {
+  decode_unit(expand(s), u, o);
+}
+__device__ __forceinline__ void decode_unit_s(const RawS<FIQ4_XS>& s, int u, Dec<FIQ4_XS>& o) {
+  decode_unit(expand(s), u, o);
+}
+__device__ __forceinline__ void decode_unit_s(const RawS<FQ4_K>& s, int u, Dec<FQ4_K>& o) {
+  const Raw<FQ4_K> r = expand(s);
+  const int c = u & 7;
+  o.h = c & 1;
+  // one formula for both packings (no branch): the low 4 bits of the scale
+  // come from S[c] (c < 4) or S[c+4], of the min from S[c+4] or the high
+  // nibble of S[c+4]; the top 2 bits sit at bits 4-5 (c < 4) or 6-7 of S[c&3]
+  // and S[(c&3)+4]
+  const uint32_t jj = 8u * (uint32_t)(c & 3);
+  const uint32_t hb = 2u * (uint32_t)(c >> 2);
+  const uint32_t s03 = r.hdr.y, s47 = r.hdr.z, s811 = r.hdr.w;
+  const uint32_t lo_sc = c < 4 ? s03 : s811;
+  const uint32_t lo_m = c < 4 ? s47 : s811;
+  const uint32_t sc = bfe(lo_sc, jj, 4) | (bfe(s03, jj + 4 + hb, 2) << 4);
+  const uint32_t m = bfe(lo_m, jj + 2 * hb, 4) | (bfe(s47, jj + 4 + hb, 2) << 4);
+  o.d = half_bits_to_float(r.hdr.x);
+  o.dmin = half_bits_to_float(r.hdr.x >> 16);
+  const float ws = o.d * static_cast<float>(sc), wm = o.dmin * static_cast<float>(m);
+  const float ws_n = dpp_f<DPP_XOR1>(ws), wm_n = dpp_f<DPP_XOR1>(wm);
+  const bool even = (c & 1) == 0;
+  o.ws0 = even ? ws : ws_n;
+  o.ws1 = even ? ws_n : ws;
+  o.wm0 = even ? wm : wm_n;
+  o.wm1 = even ? wm_n : wm;
+  o.sc0 = o.sc1 = o.m0 = o.m1 = 0;  // integer fields are not used on this path
   const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -323,15 +402,16 @@ __device__ __forceinline__ float unit_value(const Dec<FQ8_0>& w, const XFrag<FQ8
 __device__ __forceinline__ float unit_value(const Dec<FIQ4_XS>& w, const XFrag<FIQ4_XS>& x) {
   int lo, hi;
   unit_int(w, x, lo, hi);
-  return (w.d * x.d0) * static_cast<float>(w.ls * (lo + hi));
+  return (w.dls * x.d0) * static_cast<float>(lo + hi);
 }
 __device__ __forceinline__ float unit_value(const Dec<FQ4_K>& w, const XFrag<FQ4_K>& x) {
   int lo, hi;
   unit_int(w, x, lo, hi);
-  const float pos = x.d0 * static_cast<float>(w.sc0 * lo) + x.d1 * static_cast<float>(w.sc1 * hi);
-  // the min term of a sub-block is counted once, by the h == 0 half
-  const float neg = x.d0 * static_cast<float>(w.m0 * x.s0) + x.d1 * static_cast<float>(w.m1 * x.s1);
-  return w.d * pos - w.dmin * neg;
+  // sub-block j: d x0 (d sc A' - dmin m s), with A' the integer dot; the min
+  // term of a sub-block is counted once, by the h == 0 unit (s is 0 otherwise)
+  const float t0 = w.ws0 * static_cast<float>(lo) - w.wm0 * static_cast<float>(x.s0);
+  const float t1 = w.ws1 * static_cast<float>(hi) - w.wm1 * static_cast<float>(x.s1);
+  return x.d0 * t0 + x.d1 * t1;
 }
 
 // ------------------------------------------------------------- reductions
@@ -341,19 +421,6 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int o = LPR / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
-}
-
-// DPP lane moves inside a 16-lane row (gfx9 encodings): swap neighbours,
-// swap pairs, mirror each 8-lane half, mirror the row.
-enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 // Sum over each aligned group of 8 lanes; every lane of the group gets it.
@@ -371,6 +438,17 @@ __device__ __forceinline__ float max8(float v) {
   v = fmaxf(v, dpp_f<DPP_XOR1>(v));
   v = fmaxf(v, dpp_f<DPP_XOR2>(v));
   return fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+}
+
+// Sum over the LPR consecutive lanes of a lane group (LPR 8, 16, 32 or 64,
+// every lane active); every lane of the group gets the result.
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v = sum8(v);
+  if constexpr (LPR >= 16) v += dpp_f<DPP_MIRROR>(v);  // 16-lane row sums
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPR == 64) v += __shfl_xor(v, 32, 64);
+  return v;
 }
 
 // Sum over all 64 lanes of a wave (every lane active): row sums with DPP,

@@ -146,7 +146,8 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
   constexpr int NT = 64 * WPB;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int team = blockIdx.x * TPB + wave / KS;
   const int n_teams = gridDim.x * TPB;
   const int kw = wave % KS;
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
       const int u = ok ? uraw : units - 1;
       Dec<F> dec[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) decode_unit(expand(cur[r][q]), u, dec[r]);
+      for (int r = 0; r < R; ++r) decode_unit_s(cur[r][q], u, dec[r]);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         XFrag<F> xf;
@@ -281,7 +282,8 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
   constexpr int TX = XL ? 1 : TM;  // prefetched fragments per unit
   extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row bases
   const int row0 = (blockIdx.x * WPB + wave) * R;
   const int units = a.units;
   const int nch = (units + CH - 1) / CH;
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
       const int u = ok ? uraw : units - 1;
       Dec<F> dec[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) decode_unit(expand(cur[r][q]), u, dec[r]);
+      for (int r = 0; r < R; ++r) decode_unit_s(cur[r][q], u, dec[r]);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         const int tt = t < a.n_tok ? t : a.n_tok - 1;
@@ -379,6 +381,163 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
   if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
 }
 
+// ------------------------------------------------------ multi-token kernel
+// For verify batches (several tokens): a lane group of LPR lanes owns R rows
+// and walks them with stride LPR*NU units, so a wave covers 64/LPR row groups
+// and each weight load of a group is one contiguous 16*LPR-byte span.  A team
+// of KS waves shares the same rows and splits their iterations (partial sums
+// meet in LDS at the end), which multiplies the waves in flight when rows are
+// few or tokens many.  The activations are staged in LDS chunk by chunk (kc
+// units of every token at a time, all waves of the workgroup in step); all
+// lane groups of a wave read the same few activation addresses, which LDS
+// serves as broadcasts.  Each decoded unit is applied to every token and each
+// activation fragment to the R rows.  The next iteration's weight loads are
+// issued before the current one is computed, across chunk boundaries too, so
+// staging a chunk overlaps the HBM latency of the weights that follow it.
+template <int F, int TM, int LPR, int R, int NU, int WPB, int KS>
+__global__ __launch_bounds__(64 * WPB) void k_multi(StreamArgs a) {
+  static_assert(R * TM <= 64 && LPR >= 8 && LPR % 8 == 0 && WPB % KS == 0, "layout");
+  constexpr int GPW = 64 / LPR;
+  constexpr int TEAMS = WPB / KS;
+  constexpr int NT = 64 * WPB;
+  constexpr int STEP = LPR * NU;
+  constexpr int NV = R * TM;  // outputs of a lane group
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int team = wave / KS, kw = wave % KS;
+  const int g = lane / LPR, gl = lane % LPR;
+  const int row0 = ((blockIdx.x * TEAMS + team) * GPW + g) * R;
+  const int units = a.units, kc = a.kc, T = a.n_tok;
+  const int ipc = kc / STEP;  // iterations per chunk
+  const int nchunk = (units + kc - 1) / kc;
+  const uint8_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
+
+  // LDS chunk: qs [T][kc*32] | d [T][kc] | s [T][kc]; then the team partials
+  const int qs_bytes = T * kc * 32;
+  float* ld_d = reinterpret_cast<float*>(s_mem + qs_bytes);
+  int32_t* ld_s = reinterpret_cast<int32_t*>(s_mem + qs_bytes + T * kc * 4);
+  float* red = reinterpret_cast<float*>(s_mem + T * kc * 40);
+  const Act xl{reinterpret_cast<const int8_t*>(s_mem), ld_d, ld_s, kc * 32, kc};
+  const float* gd = reinterpret_cast<const float*>(a.xq + a.off_d);
+  const int32_t* gs = reinterpret_cast<const int32_t*>(a.xq + a.off_s);
+
+  auto load_it = [&](int c, int cit, RawS<F> (&buf)[R][NU]) {
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int u = min(c * kc + cit * STEP + gl + LPR * q, units - 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) load_unit_s(wr[r], u, lane, buf[r][q]);
+    }
+  };
+  auto stage = [&](int c) {
+    const int c0 = c * kc, cu = min(kc, units - c0);
+    const int nq = 2 * cu;  // 16-byte pieces of one token's quants
+    for (int base = 0; base < T * nq; base += 4 * NT) {
+      u32x4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + threadIdx.x + i * NT;
+        const int t = idx / nq, p = idx - t * nq;
+        if (idx < T * nq) v[i] = ld16(a.xq + (int64_t)t * a.k + 32 * c0 + 16 * p);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + threadIdx.x + i * NT;
+        const int t = idx / nq, p = idx - t * nq;
+        if (idx < T * nq) *reinterpret_cast<u32x4a*>(s_mem + t * kc * 32 + 16 * p) = v[i];
+      }
+    }
+    for (int idx = threadIdx.x; idx < T * cu; idx += NT) {
+      const int t = idx / cu, p = idx - t * cu;
+      ld_d[t * kc + p] = gd[(int64_t)t * a.nb + c0 + p];
+      ld_s[t * kc + p] = gs[(int64_t)t * a.nb + c0 + p];
+    }
+  };
+
+  float acc[R][TM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[r][t] = 0.f;
+
+  RawS<F> cur[R][NU];
+  load_it(0, kw, cur);
+  for (int c = 0; c < nchunk; ++c) {
+    __syncthreads();  // every wave is done with the previous chunk
+    stage(c);
+    __syncthreads();
+    for (int cit = kw; cit < ipc; cit += KS) {
+      // prefetch this wave's next iteration (next chunk after the last one)
+      int nc = c, ncit = cit + KS;
+      if (ncit >= ipc) {
+        nc = c + 1 < nchunk ? c + 1 : c;
+        ncit = c + 1 < nchunk ? kw : cit;
+      }
+      RawS<F> nxt[R][NU];
+      load_it(nc, ncit, nxt);
+#pragma unroll
+      for (int q = 0; q < NU; ++q) {
+        const int ul = cit * STEP + gl + LPR * q;  // unit inside the chunk
+        const int uraw = c * kc + ul;
+        const bool ok = uraw < units;
+        const int u = ok ? uraw : units - 1;
+        Dec<F> dec[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) decode_unit_s(cur[r][q], u, dec[r]);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          XFrag<F> xf;
+          load_xfrag<F>(xl, t < T ? t : T - 1, ok ? ul : 0, xf);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float v = unit_value(dec[r], xf);
+            acc[r][t] += ok ? v : 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < NU; ++q) cur[r][q] = nxt[r][q];
+    }
+  }
+
+  if constexpr (KS == 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const float v = lane_group_sum<LPR>(acc[r][t]);
+        if (((r * TM + t) % LPR) == gl && t < T && row0 + r < a.n_rows)
+          a.y[(int64_t)t * a.ldy + row0 + r] = v;
+      }
+  } else {
+    // team partials: red[team][kw][g][v]
+    float* mine = red + ((team * KS + kw) * GPW + g) * NV;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const float v = lane_group_sum<LPR>(acc[r][t]);
+        if (((r * TM + t) % LPR) == gl) mine[r * TM + t] = v;
+      }
+    __syncthreads();
+    for (int i = threadIdx.x; i < TEAMS * GPW * NV; i += NT) {
+      const int tm = i / (GPW * NV), rest = i - tm * (GPW * NV);
+      const int gg = rest / NV, v = rest - gg * NV;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) sum += red[((tm * KS + w) * GPW + gg) * NV + v];
+      const int r = v / TM, t = v % TM;
+      const int row = ((blockIdx.x * TEAMS + tm) * GPW + gg) * R + r;
+      if (t < T && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = sum;
+    }
+  }
+}
+
 // Variant table.  Indices are part of the tuning interface (qmv_set_tuning).
 //   kind, lpr, rows, nu, wpb, ks, xl, name
 const Variant kVariants[] = {
@@ -391,6 +550,11 @@ const Variant kVariants[] = {
     {2, 64, 1, 7, 4, 1, 0, "fl_w4_r1_u7_g"},  {2, 64, 1, 2, 4, 1, 1, "fl_w4_r1_u2_l"},
     {2, 64, 1, 2, 16, 1, 1, "fl_w16_r1_u2_l"}, {2, 64, 1, 3, 16, 1, 1, "fl_w16_r1_u3_l"},
     {2, 64, 1, 7, 8, 1, 1, "fl_w8_r1_u7_l"},  {2, 64, 2, 2, 16, 1, 1, "fl_w16_r2_u2_l"},
+    {3, 16, 2, 2, 4, 1, 1, "mu_l16_r2_u2_w4"}, {3, 8, 2, 2, 4, 1, 1, "mu_l8_r2_u2_w4"},
+    {3, 16, 4, 1, 4, 1, 1, "mu_l16_r4_u1_w4"}, {3, 8, 4, 1, 4, 1, 1, "mu_l8_r4_u1_w4"},
+    {3, 16, 2, 2, 8, 1, 1, "mu_l16_r2_u2_w8"}, {3, 16, 1, 2, 4, 1, 1, "mu_l16_r1_u2_w4"},
+    {3, 16, 2, 1, 8, 4, 1, "mu_l16_r2_u1_w8_k4"}, {3, 8, 4, 1, 8, 4, 1, "mu_l8_r4_u1_w8_k4"},
+    {3, 16, 2, 1, 8, 2, 1, "mu_l16_r2_u1_w8_k2"}, {3, 8, 2, 1, 16, 8, 1, "mu_l8_r2_u1_w16_k8"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -415,6 +579,7 @@ static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
 }
 
 size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm) {
+  if (v.kind == 3) return 0;  // chunked to fit (kMultiLdsBudget)
   if (v.kind == 2) return v.xl || tm > 4 ? static_cast<size_t>(act_bytes) : 0;
   return static_cast<size_t>(act_bytes + (int64_t)v.ks * v.rows * tm * 4);
 }
@@ -434,6 +599,7 @@ static StreamArgs stream_args(const MatvecLaunch& a) {
   sa.n_tok = a.n_tok;
   sa.y = a.y;
   sa.ldy = a.ldy;
+  sa.kc = 0;
   return sa;
 }
 
@@ -477,6 +643,34 @@ static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
   }
 }
 
+// Units per LDS chunk of the multi-token kernel: as many as fit the budget,
+// a multiple of the units one iteration covers (and of 8, one super-block),
+// balanced over the chunks the row needs.
+int multi_chunk_units(int units, int n_tok, int step, int64_t lds_budget) {
+  const int per_unit = n_tok * 40;  // 32 quant bytes + scale + sum per token
+  const int lcm = step % 8 == 0 ? step : step * 8;
+  int kmax = (int)(lds_budget / per_unit) / lcm * lcm;
+  if (kmax < lcm) return 0;  // does not fit
+  const int need = (units + lcm - 1) / lcm * lcm;
+  if (kmax >= need) return need;
+  const int chunks = (units + kmax - 1) / kmax;
+  const int per = (units + chunks - 1) / chunks;
+  return (per + lcm - 1) / lcm * lcm;
+}
+
+template <int F, int TM, int LPR, int R, int NU, int WPB, int KS>
+static hipError_t run_multi(const MatvecLaunch& a, hipStream_t st) {
+  StreamArgs sa = stream_args(a);
+  constexpr int RWG = (WPB / KS) * (64 / LPR) * R;  // rows per workgroup
+  const int64_t red_bytes = (int64_t)WPB * (64 / LPR) * R * TM * 4;
+  sa.kc = multi_chunk_units(a.units, a.n_tok, LPR * NU, kMultiLdsBudget - red_bytes);
+  if (sa.kc <= 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t)a.n_tok * sa.kc * 40 + (KS > 1 ? red_bytes : 0);
+  const unsigned grid = (unsigned)((a.n_rows + RWG - 1) / RWG);
+  hipLaunchKernelGGL((k_multi<F, TM, LPR, R, NU, WPB, KS>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+  return hipGetLastError();
+}
+
 template <int F, int TM>
 static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
   switch (a.variant) {
@@ -498,6 +692,16 @@ static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
     case 15: return run_flat<F, TM, 1, 3, 16, true>(a, st);
     case 16: return run_flat<F, TM, 1, 7, 8, true>(a, st);
     case 17: return run_flat<F, TM, 2, 2, 16, true>(a, st);
+    case 18: return run_multi<F, TM, 16, 2, 2, 4, 1>(a, st);
+    case 19: return run_multi<F, TM, 8, 2, 2, 4, 1>(a, st);
+    case 20: return run_multi<F, TM, 16, 4, 1, 4, 1>(a, st);
+    case 21: return run_multi<F, TM, 8, 4, 1, 4, 1>(a, st);
+    case 22: return run_multi<F, TM, 16, 2, 2, 8, 1>(a, st);
+    case 23: return run_multi<F, TM, 16, 1, 2, 4, 1>(a, st);
+    case 24: return run_multi<F, TM, 16, 2, 1, 8, 4>(a, st);
+    case 25: return run_multi<F, TM, 8, 4, 1, 8, 4>(a, st);
+    case 26: return run_multi<F, TM, 16, 2, 1, 8, 2>(a, st);
+    case 27: return run_multi<F, TM, 8, 2, 1, 16, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,17 +31,6 @@ namespace qmv {
 constexpr int kMaxSlots = 64 * 16;
 constexpr int kMaxExperts = 1024;
 
-// Sum over the LPR consecutive lanes of a lane group; every lane of the group
-// gets the result.
-template <int LPR>
-__device__ __forceinline__ float lane_group_sum(float v) {
-  v = sum8(v);
-  v += dpp_f<DPP_MIRROR>(v);  // 16-lane row sums
-  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (LPR == 64) v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
 template <int F, int LPR, int NU>
 __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
   constexpr int GPW = 64 / LPR;
@@ -147,7 +136,7 @@ __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) load_unit_s(wr, min(gl + LPR * q, units - 1), lane, raw[q]);
 #pragma unroll
-    for (int q = 0; q < NU; ++q) decode_unit(expand(raw[q]), min(gl + LPR * q, units - 1), dec[q]);
+    for (int q = 0; q < NU; ++q) decode_unit_s(raw[q], min(gl + LPR * q, units - 1), dec[q]);
   }
 
   auto slot_row = [&](int j) {
