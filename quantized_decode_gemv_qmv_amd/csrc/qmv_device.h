@@ -2,13 +2,12 @@
 // field decoders, per-unit weight loads, integer dot products and lane
 // reductions.
 //
-// Work unit.  Every kernel walks a weight row in "units" of 32 weights, which
-// is one Q8_0 block or one eighth of a q4_K / IQ4_XS super-block.  A unit is
-// decoded into eight dwords of int8 weights, q[0..3] and q[4..7], that meet
-// sixteen activation bytes each in v_dot4 integer dot products:
-//   Q8_0   : block b               q[0..3] = w[0..15],  q[4..7] = w[16..31]
-//   IQ4_XS : sub-block c of sb     q[0..3] = idx low nibbles  -> w[0..15]
-//                                  q[4..7] = idx high nibbles -> w[16..31]
+// Work unit.  Every kernel walks a weight row in "units" of 16 quant bytes
+// (32 weights for Q8_0 and IQ4_XS, which is one 32-block; q4_K units hold the
+// same 16 positions of two sub-blocks):
+//   Q8_0   : block b                     weights 0..31 of block b
+//   IQ4_XS : sub-block c of sb           low nibbles -> weights 0..15,
+//                                        high nibbles -> weights 16..31
 //   q4_K   : 16 quant bytes c of sb (bytes 16c..16c+15 of the nibble area):
 //            low nibbles are weights 16h..16h+15 (h = c & 1) of sub-block
 //            j = 2 (c >> 1), high nibbles the same positions of sub-block j+1.
@@ -198,16 +197,6 @@ template <> struct Dec<FIQ4_XS> {
   int ls;     // effective sub-block scale, raw 6-bit value minus 32
   float dls;  // d * ls, exact in fp32 (11-bit times 6-bit significand)
 };
-template <> struct Dec<FQ4_K> {
-  uint32_t q[8];  // nibble values 0..15, one per byte
-  float d, dmin;
-  int sc0, sc1, m0, m1;  // sub-blocks j and j+1
-  int h;                 // which 16-weight half of the sub-blocks
-  // d * sc and dmin * m of both sub-blocks, exact in fp32, so that applying
-  // a unit to a token needs no integer multiply
-  float ws0, ws1, wm0, wm1;
-};
-
 __device__ __forceinline__ void decode_unit(const Raw<FQ8_0>& r, int, Dec<FQ8_0>& o) {
   const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.h};
   const uint32_t sh = r.odd ? 0u : 2u;
@@ -252,86 +241,6 @@ __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FI
   }
 }
 
-__device__ __forceinline__ uint32_t bfe(uint32_t v, uint32_t off, uint32_t w) {
-  return __builtin_amdgcn_ubfe(v, off, w);
-}
-
-// 6-bit scale and min of sub-block j from S[0..11] held in three dwords.
-__device__ __forceinline__ void q4k_scale_min(uint32_t s03, uint32_t s47, uint32_t s811, int j,
-                                              int& sc, int& m) {
-  const uint32_t jj = 8u * (j & 3);
-  const uint32_t sc_lo = bfe(s03, jj, 6), m_lo = bfe(s47, jj, 6);
-  const uint32_t sc_hi = bfe(s811, jj, 4) | (bfe(s03, jj + 6, 2) << 4);
-  const uint32_t m_hi = bfe(s811, jj + 4, 4) | (bfe(s47, jj + 6, 2) << 4);
-  sc = static_cast<int>(j < 4 ? sc_lo : sc_hi);
-  m = static_cast<int>(j < 4 ? m_lo : m_hi);
-}
-
-__device__ __forceinline__ void decode_unit(const Raw<FQ4_K>& r, int u, Dec<FQ4_K>& o) {
-  const int c = u & 7;
-  const int j = 2 * (c >> 1);
-  o.h = c & 1;
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, j, o.sc0, o.m0);
-  q4k_scale_min(r.hdr.y, r.hdr.z, r.hdr.w, j + 1, o.sc1, o.m1);
-  o.d = half_bits_to_float(r.hdr.x);
-  o.dmin = half_bits_to_float(r.hdr.x >> 16);
-  o.ws0 = o.d * static_cast<float>(o.sc0);
-  o.ws1 = o.d * static_cast<float>(o.sc1);
-  o.wm0 = o.dmin * static_cast<float>(o.m0);
-  o.wm1 = o.dmin * static_cast<float>(o.m1);
-  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o.q[i] = v[i] & 0x0F0F0F0Fu;
-    o.q[4 + i] = (v[i] >> 4) & 0x0F0F0F0Fu;
-  }
-}
-
-// Decoding from shared-header loads.  Q8_0 and IQ4_XS decode as usual.  For
-// q4_K the lanes of an aligned pair hold units 2p and 2p+1 of a super-block,
-// which use the same two sub-blocks (2p', 2p'+1 with p' = p mod 4): each lane
-// unpacks the 6-bit (scale, min) of one sub-block -- sub-block u mod 8 -- folds
-// it into fp32 with d and dmin, and takes the other from its pair neighbour
-// over DPP, instead of unpacking both.
-__device__ __forceinline__ void decode_unit_s(const RawS<FQ8_0>& s, int u, Dec<FQ8_0>& o) {
-  decode_unit(expand(s), u, o);
-}
-__device__ __forceinline__ void decode_unit_s(const RawS<FIQ4_XS>& s, int u, Dec<FIQ4_XS>& o) {
-  decode_unit(expand(s), u, o);
-}
-__device__ __forceinline__ void decode_unit_s(const RawS<FQ4_K>& s, int u, Dec<FQ4_K>& o) {
-  const Raw<FQ4_K> r = expand(s);
-  const int c = u & 7;
-  o.h = c & 1;
-  // one formula for both packings (no branch): the low 4 bits of the scale
-  // come from S[c] (c < 4) or S[c+4], of the min from S[c+4] or the high
-  // nibble of S[c+4]; the top 2 bits sit at bits 4-5 (c < 4) or 6-7 of S[c&3]
-  // and S[(c&3)+4]
-  const uint32_t jj = 8u * (uint32_t)(c & 3);
-  const uint32_t hb = 2u * (uint32_t)(c >> 2);
-  const uint32_t s03 = r.hdr.y, s47 = r.hdr.z, s811 = r.hdr.w;
-  const uint32_t lo_sc = c < 4 ? s03 : s811;
-  const uint32_t lo_m = c < 4 ? s47 : s811;
-  const uint32_t sc = bfe(lo_sc, jj, 4) | (bfe(s03, jj + 4 + hb, 2) << 4);
-  const uint32_t m = bfe(lo_m, jj + 2 * hb, 4) | (bfe(s47, jj + 4 + hb, 2) << 4);
-  o.d = half_bits_to_float(r.hdr.x);
-  o.dmin = half_bits_to_float(r.hdr.x >> 16);
-  const float ws = o.d * static_cast<float>(sc), wm = o.dmin * static_cast<float>(m);
-  const float ws_n = dpp_f<DPP_XOR1>(ws), wm_n = dpp_f<DPP_XOR1>(wm);
-  const bool even = (c & 1) == 0;
-  o.ws0 = even ? ws : ws_n;
-  o.ws1 = even ? ws_n : ws;
-  o.wm0 = even ? wm : wm_n;
-  o.wm1 = even ? wm_n : wm;
-  o.sc0 = o.sc1 = o.m0 = o.m1 = 0;  // integer fields are not used on this path
-  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o.q[i] = v[i] & 0x0F0F0F0Fu;
-    o.q[4 + i] = (v[i] >> 4) & 0x0F0F0F0Fu;
-  }
-}
-
 // ----------------------------------------------------- activation fragments
 // View of a Q8 activation buffer (structure of arrays, see qmv.h).
 struct Act {
@@ -341,77 +250,162 @@ struct Act {
   int k, nb;
 };
 
-// The 32 activation bytes a unit meets, as two 16-byte halves, plus scales.
-template <int F> struct XFrag {
-  u32x4 a, b;
-  float d0, d1;
-  int s0, s1;
+// ------------------------------------------------- own-block (paired) form
+// How every kernel applies a unit to a token.  Unit u always meets the 32
+// activations of 32-block u as its "own" block: for Q8_0 and IQ4_XS the unit
+// is that block; for q4_K unit u = 8s + c holds half h = c & 1 of sub-blocks
+// 2(c >> 1) and 2(c >> 1) + 1, and global sub-block u is one of those two
+// (the low nibbles when h = 0, the high nibbles when h = 1).  So a unit needs
+// one weight scale, and one activation scale per token.
+//
+// The eight weight dwords are split into a "first" and a "second" run of
+// four.  For q4_K the first run holds the nibbles of the partner sub-block
+// u ^ 1 (lane pairs hold units 2p, 2p+1, which share both sub-blocks) and the
+// second the nibbles of the own one.  A token's integer dot is then: the
+// first run against its activations, handed to the pair neighbour over DPP,
+// which adds its second run on top -- so each lane ends with the complete
+// 32-weight dot of its own sub-block, and a token costs eight v_dot4, one
+// move and one fp32 scale step per unit.  Kernels that use the pair exchange
+// keep both lanes of every pair active and on units 2p, 2p+1 of one row.
+template <int F> struct DecO {
+  uint32_t q[8];  // q[0..3] first run, q[4..7] second run
+  float sc;       // Q8_0: d; IQ4_XS: d * (ls - 32); q4_K: d * sc of sub-block u
+  float wm;       // q4_K: dmin * m of sub-block u (0 otherwise)
+  int isc, im;    // the integer scale (and q4_K min) of the unit, for tests
 };
 
+// Decode unit u (clamped index) for lane parity h; invalid units get zero
+// scales so that whatever they meet adds exactly nothing.  The fp32 scales are
+// exact products (an 11-bit half significand times a 6-bit integer).
+__device__ __forceinline__ void decode_own(const Raw<FQ8_0>& r, int u, int, bool ok, DecO<FQ8_0>& o) {
+  Dec<FQ8_0> d;
+  decode_unit(r, u, d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o.q[i] = d.q[i];
+  o.sc = ok ? d.d : 0.f;
+  o.wm = 0.f;
+  o.isc = 1;
+  o.im = 0;
+}
+__device__ __forceinline__ void decode_own(const Raw<FIQ4_XS>& r, int u, int, bool ok, DecO<FIQ4_XS>& o) {
+  Dec<FIQ4_XS> d;
+  decode_unit(r, u, d);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o.q[i] = d.q[i];
+  o.sc = ok ? d.dls : 0.f;
+  o.wm = 0.f;
+  o.isc = d.ls;
+  o.im = 0;
+}
+__device__ __forceinline__ uint32_t bfe(uint32_t v, uint32_t off, uint32_t w) {
+  return __builtin_amdgcn_ubfe(v, off, w);
+}
+// q4_K: the 6-bit (scale, min) of sub-block c of the super-block, one formula
+// for both packings (no branch): the low 4 bits of the scale come from S[c]
+// (c < 4) or S[c+4], of the min from S[c+4] or the high nibble of S[c+4]; the
+// top 2 bits sit at bits 4-5 (c < 4) or 6-7 of S[c&3] and S[(c&3)+4].
+__device__ __forceinline__ void decode_own(const Raw<FQ4_K>& r, int u, int h, bool ok, DecO<FQ4_K>& o) {
+  const int c = u & 7;  // own sub-block inside the super-block
+  const uint32_t jj = 8u * (uint32_t)(c & 3);
+  const uint32_t hb = 2u * (uint32_t)(c >> 2);
+  const uint32_t s03 = r.hdr.y, s47 = r.hdr.z, s811 = r.hdr.w;
+  const uint32_t lo_sc = c < 4 ? s03 : s811;
+  const uint32_t lo_m = c < 4 ? s47 : s811;
+  const uint32_t sc = bfe(lo_sc, jj, 4) | (bfe(s03, jj + 4 + hb, 2) << 4);
+  const uint32_t m = bfe(lo_m, jj + 2 * hb, 4) | (bfe(s47, jj + 4 + hb, 2) << 4);
+  const float ws = half_bits_to_float(r.hdr.x) * static_cast<float>(sc);
+  const float wm = half_bits_to_float(r.hdr.x >> 16) * static_cast<float>(m);
+  o.sc = ok ? ws : 0.f;
+  o.wm = ok ? wm : 0.f;
+  o.isc = static_cast<int>(sc);
+  o.im = static_cast<int>(m);
+  // h = 0: own = low nibbles, partner = high; h = 1 the other way round
+  const uint32_t sh_own = 4u * (uint32_t)h, sh_par = 4u - sh_own;
+  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.q[i] = (v[i] >> sh_par) & 0x0F0F0F0Fu;
+    o.q[4 + i] = (v[i] >> sh_own) & 0x0F0F0F0Fu;
+  }
+}
 template <int F>
-__device__ __forceinline__ void load_xfrag(const Act& x, int row, int u, XFrag<F>& f) {
+__device__ __forceinline__ void decode_own(const RawS<F>& s, int u, int h, bool ok, DecO<F>& o) {
+  decode_own(expand(s), u, h, ok, o);
+}
+
+// The activation runs of unit u for one token and the (d, d*s) pair of its
+// own 32-block, from a Q8 activation buffer in the library layout (global
+// memory or an LDS copy of it).
+struct XO {
+  u32x4 f, s;
+  float2 p;
+};
+template <int F>
+__device__ __forceinline__ void load_xo(const Act& x, int row, int u, XO& o) {
+  const int8_t* base = x.qs + (int64_t)row * x.k;
+  const int64_t i = (int64_t)row * x.nb + u;
   if constexpr (F == FQ4_K) {
-    const int jb = 8 * (u >> 3) + 2 * ((u & 7) >> 1);  // 32-block of the low nibbles
-    const int8_t* p = x.qs + (int64_t)row * x.k + 32 * jb + 16 * (u & 1);
-    f.a = ld16(p);
-    f.b = ld16(p + 32);
-    // jb is even and K/32 is a multiple of 8, so the (d, d) and (s, s) pairs
-    // are 8-byte aligned: one load each
-    const int64_t o = (int64_t)row * x.nb + jb;
-    const float2 dd = *reinterpret_cast<const float2*>(x.d + o);
-    const int2 ss = *reinterpret_cast<const int2*>(x.s + o);
-    f.d0 = dd.x;
-    f.d1 = dd.y;
-    // the min term of a sub-block is counted once, by the h == 0 unit
-    f.s0 = (u & 1) == 0 ? ss.x : 0;
-    f.s1 = (u & 1) == 0 ? ss.y : 0;
+    const int h = u & 1;
+    o.f = ld16(base + 32 * (u ^ 1) + 16 * h);
+    o.s = ld16(base + 32 * u + 16 * h);
+    const float d = x.d[i];
+    o.p = make_float2(d, d * static_cast<float>(x.s[i]));
   } else {
-    const int8_t* p = x.qs + (int64_t)row * x.k + 32 * u;
-    f.a = ld16(p);
-    f.b = ld16(p + 16);
-    f.d0 = x.d[(int64_t)row * x.nb + u];
-    f.d1 = 0.f;
-    f.s0 = f.s1 = 0;
+    o.f = ld16(base + 32 * u);
+    o.s = ld16(base + 32 * u + 16);
+    o.p = make_float2(x.d[i], 0.f);
   }
 }
 
-// Integer halves of one unit against one activation fragment:
-// lo = sum over q[0..3], hi = sum over q[4..7].
+// Exact integer dot of the own 32-block against one token's activation runs
+// (xf meets q[0..3], xs meets q[4..7]), in two steps so that a caller can
+// interleave rows: own_first gives the first run's dot, which the caller
+// hands through own_pass (the DPP move between pair lanes for q4_K) to
+// own_second.
 template <int F>
-__device__ __forceinline__ void unit_int(const Dec<F>& w, const XFrag<F>& x, int& lo, int& hi) {
-  int a = 0, b = 0;
-  a = dot4(w.q[0], x.a.x, a);
-  a = dot4(w.q[1], x.a.y, a);
-  a = dot4(w.q[2], x.a.z, a);
-  a = dot4(w.q[3], x.a.w, a);
-  b = dot4(w.q[4], x.b.x, b);
-  b = dot4(w.q[5], x.b.y, b);
-  b = dot4(w.q[6], x.b.z, b);
-  b = dot4(w.q[7], x.b.w, b);
-  lo = a;
-  hi = b;
+__device__ __forceinline__ int own_first(const DecO<F>& w, const u32x4& xf) {
+  int a = 0;
+  a = dot4(w.q[0], xf.x, a);
+  a = dot4(w.q[1], xf.y, a);
+  a = dot4(w.q[2], xf.z, a);
+  return dot4(w.q[3], xf.w, a);
+}
+template <int F>
+__device__ __forceinline__ int own_pass(int a) {
+  if constexpr (F == FQ4_K) return dpp_i<DPP_XOR1>(a);  // partner's part of the own block
+  return a;
+}
+template <int F>
+__device__ __forceinline__ int own_second(const DecO<F>& w, const u32x4& xs, int a) {
+  a = dot4(w.q[4], xs.x, a);
+  a = dot4(w.q[5], xs.y, a);
+  a = dot4(w.q[6], xs.z, a);
+  return dot4(w.q[7], xs.w, a);
 }
 
-// fp32 contribution of one unit: the exact integer partial times the weight
-// and activation scales.
-__device__ __forceinline__ float unit_value(const Dec<FQ8_0>& w, const XFrag<FQ8_0>& x) {
-  int lo, hi;
-  unit_int(w, x, lo, hi);
-  return (w.d * x.d0) * static_cast<float>(lo + hi);
+// acc += d_x * (w.sc * A - w.wm * s_x), with p = (d_x, d_x * s_x).
+template <int F>
+__device__ __forceinline__ float own_apply(const DecO<F>& w, int dotv, float2 p, float acc) {
+  acc = fmaf(static_cast<float>(dotv), p.x * w.sc, acc);
+  if constexpr (F == FQ4_K) acc = fmaf(-w.wm, p.y, acc);
+  return acc;
 }
-__device__ __forceinline__ float unit_value(const Dec<FIQ4_XS>& w, const XFrag<FIQ4_XS>& x) {
-  int lo, hi;
-  unit_int(w, x, lo, hi);
-  return (w.dls * x.d0) * static_cast<float>(lo + hi);
-}
-__device__ __forceinline__ float unit_value(const Dec<FQ4_K>& w, const XFrag<FQ4_K>& x) {
-  int lo, hi;
-  unit_int(w, x, lo, hi);
-  // sub-block j: d x0 (d sc A' - dmin m s), with A' the integer dot; the min
-  // term of a sub-block is counted once, by the h == 0 unit (s is 0 otherwise)
-  const float t0 = w.ws0 * static_cast<float>(lo) - w.wm0 * static_cast<float>(x.s0);
-  const float t1 = w.ws1 * static_cast<float>(hi) - w.wm1 * static_cast<float>(x.s1);
-  return x.d0 * t0 + x.d1 * t1;
+
+// Where the activation runs of unit u (32-block u) come from, as 16-byte
+// pieces (block b, half hb) of a token's quants: Q8_0 / IQ4_XS take (u, 0)
+// then (u, 1); q4_K takes (u ^ 1, u & 1) then (u, u & 1).  Inverted for
+// staging: piece (b, hb) is the second run of unit b if hb matches the
+// format's rule, else the first run of unit b ^ 1 (q4_K) / b (others).
+template <int F>
+__device__ __forceinline__ void own_piece_slot(int b, int hb, int& unit, int& run) {
+  if constexpr (F == FQ4_K) {
+    const bool second = hb == (b & 1);
+    unit = second ? b : (b ^ 1);
+    run = second ? 1 : 0;
+  } else {
+    unit = b;
+    run = hb;
+  }
 }
 
 // ------------------------------------------------------------- reductions

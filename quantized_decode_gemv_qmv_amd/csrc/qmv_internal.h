@@ -23,12 +23,13 @@ struct ActView {
 //   kind 1: streaming kernel (k_stream) -- workgroups of wpb waves, teams of
 //           ks waves (1 or wpb) per group of `rows` rows, `nu` units per lane
 //           per chunk, activations staged in LDS;
-//   kind 3: multi-token kernel (k_multi) -- lane groups of lpr lanes own
-//           `rows` rows, `nu` units per lane per iteration, wpb waves per
-//           workgroup, activations staged in LDS chunk by chunk;
 //   kind 2: flat kernel (k_flat) -- one wave per group of `rows` rows for the
 //           whole grid at once, `nu` units per lane; activations prefetched
-//           from global memory (xl 0, up to 4 tokens) or staged in LDS (xl 1).
+//           from global memory (xl 0, up to 4 tokens) or staged in LDS (xl 1);
+//   kind 3: multi-token kernel (k_mt) -- lane groups of 16 lanes own `rows`
+//           rows, one unit per lane per iteration, wpb waves per workgroup in
+//           teams of ks waves that split K, activations staged in LDS chunk
+//           by chunk.
 struct Variant {
   int kind;
   int lpr;
@@ -56,10 +57,10 @@ struct StreamArgs {
   int n_tok;
   float* y;
   int64_t ldy;
-  int kc;  // k_multi: units per LDS chunk
+  int kc;  // k_mt: units per LDS chunk
 };
 
-// LDS bytes k_multi stages per chunk at most (two workgroups per compute unit).
+// LDS bytes k_mt stages per chunk at most (two workgroups per compute unit).
 constexpr int64_t kMultiLdsBudget = 80 * 1024;
 
 struct MatvecLaunch {

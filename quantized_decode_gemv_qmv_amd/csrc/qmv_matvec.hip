@@ -1,23 +1,28 @@
 // qmv_matvec.hip -- dense small-batch matvec kernels for gfx950.
 //
-// Two kernel families compute y[t][n] = sum_k W[n][k] x[t][k] from the block
-// weights and the Q8 activation buffer; each decoded weight unit serves every
-// token of the batch (one weight read for the whole verify batch: zhuai.tech
-// GLM-5.3 page, "MTP saves full-model execution rounds").
+// The kernels compute y[t][n] = sum_k W[n][k] x[t][k] from the block weights
+// and the Q8 activation buffer; each decoded weight unit serves every token of
+// the batch (one weight read for the whole verify batch: zhuai.tech GLM-5.3
+// page, "MTP saves full-model execution rounds").  All of them apply units in
+// the own-block form of qmv_device.h.
 //
-// k_stream (the default).  The activation buffer is copied once per workgroup
-// into LDS, so activation reads never sit in the vector-memory queue behind
-// weight loads.  Work is split into jobs = (group of R rows, chunk of 64*NU
-// units): lane l of a wave takes units c*64*NU + l + 64*i (i < NU) of each of
-// the group's rows, so each weight load of the wave is one contiguous, fully
-// used span.  A wave keeps the next job's weight loads in flight while it
-// computes the current one; every load is unconditional (positions past the
-// end re-read a valid unit and are masked out), so the load counter never has
-// to drain early.  Teams of KS waves share a row group and split its chunks
-// (split-K inside one workgroup, reduced through LDS: no workspace, no
-// cross-workgroup synchronisation) -- used for few rows and long K (Castagna
-// Veloce page, "Kernels for the MI50": Q8_0 matvec with a split-K variant).
-// Lane sums are DPP row reductions plus four scalar reads.
+// k_flat (one or a few tokens): one wave per row group, the whole grid at
+// once, every weight load of the wave issued up front.
+//
+// k_mt (several tokens): lane groups with LDS-staged activations, chunked so
+// that any K fits.
+//
+// k_stream: persistent waves over (row group, chunk) jobs with the activation
+// buffer copied once per workgroup into LDS.  Lane l of a wave takes units
+// c*64*NU + l + 64*i (i < NU) of each of the group's rows, so each weight load
+// of the wave is one contiguous, fully used span, and the next job's loads
+// stay in flight while the current one is computed; every load is
+// unconditional (positions past the end re-read a valid unit and carry zero
+// scales), so the load counter never has to drain early.  Teams of KS waves
+// share a row group and split its chunks (split-K inside one workgroup,
+// reduced through LDS: no workspace, no cross-workgroup synchronisation) --
+// used for few rows and long K (Castagna Veloce page, "Kernels for the MI50":
+// Q8_0 matvec with a split-K variant).
 //
 // k_matvec (lane groups of LPR lanes per row, activations read from global
 // memory) remains for A/B comparison and for the cross-workgroup split-K path
@@ -55,6 +60,8 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, i
     ue = min(units, ub + ups);
   }
 
+  // ub and ue are even (slices are multiples of eight units), so both lanes
+  // of every pair run the same iterations
   int u = ub + gl;
   Raw<F> cur[R];
   if (u < ue) {
@@ -68,16 +75,19 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, i
 #pragma unroll
       for (int r = 0; r < R; ++r) load_unit(wr[r], un, nxt[r]);
     }
-    Dec<F> dec[R];
+    DecO<F> dec[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) decode_unit(cur[r], u, dec[r]);
+    for (int r = 0; r < R; ++r) decode_own(cur[r], u, gl & 1, true, dec[r]);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       if (t < n_tok) {
-        XFrag<F> xf;
-        load_xfrag<F>(x, t, u, xf);
+        XO xo;
+        load_xo<F>(x, t, u, xo);
+        int dv[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][t] += unit_value(dec[r], xf);
+        for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(own_first(dec[r], xo.f));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][t] = own_apply(dec[r], own_second(dec[r], xo.s, dv[r]), xo.p, acc[r][t]);
       }
     }
 #pragma unroll
@@ -217,18 +227,18 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
       const int uraw = c * CH + lane + 64 * q;
       const bool ok = uraw < units;
       const int u = ok ? uraw : units - 1;
-      Dec<F> dec[R];
+      DecO<F> dec[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) decode_unit_s(cur[r][q], u, dec[r]);
+      for (int r = 0; r < R; ++r) decode_own(cur[r][q], u, lane & 1, ok, dec[r]);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
-        XFrag<F> xf;
-        load_xfrag<F>(x, t < a.n_tok ? t : a.n_tok - 1, u, xf);
+        XO xo;
+        load_xo<F>(x, t < a.n_tok ? t : a.n_tok - 1, u, xo);
+        int dv[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float v = unit_value(dec[r], xf);
-          acc[r][t] += ok ? v : 0.f;
-        }
+        for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(own_first(dec[r], xo.f));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][t] = own_apply(dec[r], own_second(dec[r], xo.s, dv[r]), xo.p, acc[r][t]);
       }
     }
     if (j % mpw == mpw - 1) {  // last chunk of the group: reduce and store
@@ -274,8 +284,8 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
 // behind them, so both latencies overlap; then it decodes, reduces with DPP
 // and stores.  XL true stages the activation buffer in LDS per workgroup
 // instead (for token counts whose fragments would not fit in registers).
-template <int F, int TM, int R, int NU, int WPB, bool XL>
-__global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
+template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC = 8>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC))) void k_flat(StreamArgs a) {
   static_assert(R * TM <= 64, "one output per lane");
   constexpr int CH = 64 * NU;
   constexpr int NT = 64 * WPB;
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
   const Act lx{reinterpret_cast<const int8_t*>(s_mem),
                reinterpret_cast<const float*>(s_mem + a.off_d),
                reinterpret_cast<const int32_t*>(s_mem + a.off_s), a.k, a.nb};
-  XFrag<F> xf[NU][TX];
+  XO xf[NU][TX];
   if constexpr (XL) {
     const int n16 = a.act_bytes >> 4;
     for (int base = 0; base < n16; base += 4 * NT) {
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
     for (int q = 0; q < NU; ++q)
 #pragma unroll
       for (int t = 0; t < TM; ++t)
-        load_xfrag<F>(gx, t < a.n_tok ? t : a.n_tok - 1, min(lane + 64 * q, units - 1), xf[q][t]);
+        load_xo<F>(gx, t < a.n_tok ? t : a.n_tok - 1, min(lane + 64 * q, units - 1), xf[q][t]);
   }
 
   float acc[R][TM];
@@ -346,24 +356,24 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
       const int uraw = c * CH + lane + 64 * q;
       const bool ok = uraw < units;
       const int u = ok ? uraw : units - 1;
-      Dec<F> dec[R];
+      DecO<F> dec[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) decode_unit_s(cur[r][q], u, dec[r]);
+      for (int r = 0; r < R; ++r) decode_own(cur[r][q], u, lane & 1, ok, dec[r]);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         const int tt = t < a.n_tok ? t : a.n_tok - 1;
-        XFrag<F> f;
+        XO f;
         if constexpr (XL)
-          load_xfrag<F>(lx, tt, u, f);
+          load_xo<F>(lx, tt, u, f);
         else if (c == 0)
           f = xf[q][t];
         else
-          load_xfrag<F>(gx, tt, u, f);
+          load_xo<F>(gx, tt, u, f);
+        int dv[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float v = unit_value(dec[r], f);
-          acc[r][t] += ok ? v : 0.f;
-        }
+        for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(own_first(dec[r], f.f));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][t] = own_apply(dec[r], own_second(dec[r], f.s, dv[r]), f.p, acc[r][t]);
       }
     }
   }
@@ -381,79 +391,98 @@ __global__ __launch_bounds__(64 * WPB) void k_flat(StreamArgs a) {
   if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
 }
 
+// Division of small non-negative ints by a divisor fixed for a loop:
+// q = umulhi(n, ceil(2^32 / d)), exact whenever n * d < 2^32 (here n and d
+// stay below 2^16).  Saves the long integer division sequence per element.
+struct FastDiv {
+  uint32_t d, m;
+  __device__ explicit FastDiv(int dv) : d((uint32_t)dv), m(dv > 1 ? 0xFFFFFFFFu / (uint32_t)dv + 1u : 0u) {}
+  __device__ int div(int n) const { return d == 1u ? n : (int)__umulhi((uint32_t)n, m); }
+};
+
 // ------------------------------------------------------ multi-token kernel
-// For verify batches (several tokens): a lane group of LPR lanes owns R rows
-// and walks them with stride LPR*NU units, so a wave covers 64/LPR row groups
-// and each weight load of a group is one contiguous 16*LPR-byte span.  A team
-// of KS waves shares the same rows and splits their iterations (partial sums
-// meet in LDS at the end), which multiplies the waves in flight when rows are
-// few or tokens many.  The activations are staged in LDS chunk by chunk (kc
-// units of every token at a time, all waves of the workgroup in step); all
-// lane groups of a wave read the same few activation addresses, which LDS
-// serves as broadcasts.  Each decoded unit is applied to every token and each
-// activation fragment to the R rows.  The next iteration's weight loads are
-// issued before the current one is computed, across chunk boundaries too, so
-// staging a chunk overlaps the HBM latency of the weights that follow it.
-template <int F, int TM, int LPR, int R, int NU, int WPB, int KS>
-__global__ __launch_bounds__(64 * WPB) void k_multi(StreamArgs a) {
-  static_assert(R * TM <= 64 && LPR >= 8 && LPR % 8 == 0 && WPB % KS == 0, "layout");
-  constexpr int GPW = 64 / LPR;
+// For verify batches (several tokens).  A lane group of 16 lanes owns R rows
+// and walks them one unit per lane per iteration (each weight load of a group
+// is one contiguous 256-byte span); a wave holds four such groups.  A team of
+// KS waves shares the same rows and splits the iterations (partial sums meet
+// in LDS at the end), which multiplies the waves in flight when rows are few
+// or tokens many.  The activations are staged in LDS chunk by chunk (kc units
+// of every token at a time, all waves of the workgroup in step), and the next
+// iteration's weight loads are issued before the current one is computed,
+// across chunk boundaries too.  Each decoded unit is applied to every token
+// and each activation run to the R rows, in the own-block form: eight v_dot4,
+// one DPP move (q4_K) and one fp32 scale step per (row, token, unit); units
+// past the row end carry zero scales instead of a per-token select.  The LDS
+// chunk holds, per unit, the first and the second activation run of every
+// token and the (d, d*s) pair of its 32-block, token-minor with an odd token
+// stride: a lane finds all its tokens at fixed offsets from one address, and
+// the 16 lanes of a group, which read 16 consecutive units, cover every LDS
+// bank once (the four groups of a wave read the same addresses).
+template <int TM>
+constexpr int mt_stride() { return TM % 2 == 0 ? TM + 1 : TM; }
+
+template <int F, int TM, int R, int WPB, int KS>
+__global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
+  constexpr int LPR = 16, GPW = 4;
+  static_assert(R * TM <= 64 && WPB % KS == 0, "layout");
   constexpr int TEAMS = WPB / KS;
   constexpr int NT = 64 * WPB;
-  constexpr int STEP = LPR * NU;
-  constexpr int NV = R * TM;  // outputs of a lane group
+  constexpr int NV = R * TM;
+  constexpr int US = mt_stride<TM>();  // token slots per unit
   extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int team = wave / KS, kw = wave % KS;
-  const int g = lane / LPR, gl = lane % LPR;
+  const int g = lane / LPR, gl = lane % LPR, h = lane & 1;
   const int row0 = ((blockIdx.x * TEAMS + team) * GPW + g) * R;
   const int units = a.units, kc = a.kc, T = a.n_tok;
-  const int ipc = kc / STEP;  // iterations per chunk
+  const int ipc = kc / LPR;
   const int nchunk = (units + kc - 1) / kc;
   const uint8_t* wr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
 
-  // LDS chunk: qs [T][kc*32] | d [T][kc] | s [T][kc]; then the team partials
-  const int qs_bytes = T * kc * 32;
-  float* ld_d = reinterpret_cast<float*>(s_mem + qs_bytes);
-  int32_t* ld_s = reinterpret_cast<int32_t*>(s_mem + qs_bytes + T * kc * 4);
-  float* red = reinterpret_cast<float*>(s_mem + T * kc * 40);
-  const Act xl{reinterpret_cast<const int8_t*>(s_mem), ld_d, ld_s, kc * 32, kc};
+  // LDS chunk: first runs [kc][US] x 16 B | second runs [kc][US] x 16 B |
+  // (d, d*s) [kc][US] x 8 B; then the team partials
+  u32x4a* ld_f = reinterpret_cast<u32x4a*>(s_mem);
+  u32x4a* ld_s = ld_f + kc * US;
+  float2* ld_p = reinterpret_cast<float2*>(ld_s + kc * US);
+  float* red = reinterpret_cast<float*>(s_mem + kc * US * 40);
   const float* gd = reinterpret_cast<const float*>(a.xq + a.off_d);
   const int32_t* gs = reinterpret_cast<const int32_t*>(a.xq + a.off_s);
 
-  auto load_it = [&](int c, int cit, RawS<F> (&buf)[R][NU]) {
+  auto load_it = [&](int c, int cit, RawS<F> (&buf)[R]) {
+    const int u = min(c * kc + cit * LPR + gl, units - 1);
 #pragma unroll
-    for (int q = 0; q < NU; ++q) {
-      const int u = min(c * kc + cit * STEP + gl + LPR * q, units - 1);
-#pragma unroll
-      for (int r = 0; r < R; ++r) load_unit_s(wr[r], u, lane, buf[r][q]);
-    }
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], u, lane, buf[r]);
   };
   auto stage = [&](int c) {
     const int c0 = c * kc, cu = min(kc, units - c0);
-    const int nq = 2 * cu;  // 16-byte pieces of one token's quants
+    const int nq = 2 * cu;  // 16-byte pieces of one token's quants in the chunk
+    const FastDiv dq(nq), du(cu);
     for (int base = 0; base < T * nq; base += 4 * NT) {
       u32x4 v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = base + threadIdx.x + i * NT;
-        const int t = idx / nq, p = idx - t * nq;
-        if (idx < T * nq) v[i] = ld16(a.xq + (int64_t)t * a.k + 32 * c0 + 16 * p);
+        const int t = dq.div(idx), pc = idx - t * nq;
+        if (idx < T * nq) v[i] = ld16(a.xq + (int64_t)t * a.k + 32 * c0 + 16 * pc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = base + threadIdx.x + i * NT;
-        const int t = idx / nq, p = idx - t * nq;
-        if (idx < T * nq) *reinterpret_cast<u32x4a*>(s_mem + t * kc * 32 + 16 * p) = v[i];
+        const int t = dq.div(idx), pc = idx - t * nq;
+        int un, run;
+        own_piece_slot<F>(pc >> 1, pc & 1, un, run);
+        if (idx < T * nq) (run ? ld_s : ld_f)[un * US + t] = v[i];
       }
     }
     for (int idx = threadIdx.x; idx < T * cu; idx += NT) {
-      const int t = idx / cu, p = idx - t * cu;
-      ld_d[t * kc + p] = gd[(int64_t)t * a.nb + c0 + p];
-      ld_s[t * kc + p] = gs[(int64_t)t * a.nb + c0 + p];
+      const int t = du.div(idx), pc = idx - t * cu;
+      const float d = gd[(int64_t)t * a.nb + c0 + pc];
+      const int sx = gs[(int64_t)t * a.nb + c0 + pc];
+      ld_p[pc * US + t] = make_float2(d, d * static_cast<float>(sx));
     }
   };
 
@@ -463,45 +492,48 @@ __global__ __launch_bounds__(64 * WPB) void k_multi(StreamArgs a) {
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[r][t] = 0.f;
 
-  RawS<F> cur[R][NU];
+  RawS<F> cur[R];
   load_it(0, kw, cur);
   for (int c = 0; c < nchunk; ++c) {
     __syncthreads();  // every wave is done with the previous chunk
     stage(c);
     __syncthreads();
     for (int cit = kw; cit < ipc; cit += KS) {
-      // prefetch this wave's next iteration (next chunk after the last one)
       int nc = c, ncit = cit + KS;
       if (ncit >= ipc) {
         nc = c + 1 < nchunk ? c + 1 : c;
         ncit = c + 1 < nchunk ? kw : cit;
       }
-      RawS<F> nxt[R][NU];
+      RawS<F> nxt[R];
       load_it(nc, ncit, nxt);
+      const int ul = cit * LPR + gl;  // unit inside the chunk
+      const int uraw = c * kc + ul;
+      const bool ok = uraw < units;
+      const int u = ok ? uraw : units - 1;
+      const int li = ok ? ul : 0;  // a staged slot, for units past the end
+      DecO<F> dec[R];
 #pragma unroll
-      for (int q = 0; q < NU; ++q) {
-        const int ul = cit * STEP + gl + LPR * q;  // unit inside the chunk
-        const int uraw = c * kc + ul;
-        const bool ok = uraw < units;
-        const int u = ok ? uraw : units - 1;
-        Dec<F> dec[R];
+      for (int r = 0; r < R; ++r) decode_own(cur[r], u, h, ok, dec[r]);
+      const u32x4a* pf = ld_f + li * US;
+      const u32x4a* ps = ld_s + li * US;
+      const float2* pp = ld_p + li * US;
 #pragma unroll
-        for (int r = 0; r < R; ++r) decode_unit_s(cur[r][q], u, dec[r]);
+      for (int t = 0; t < TM; ++t) {
+        // token slots past the call's token count (t >= T) hold stale LDS
+        // bytes: they only feed acc[.][t], which is never stored
+        const u32x4 xf = pf[t];
+        const u32x4 xs = ps[t];
+        const float2 p = pp[t];
+        int dv[R];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-          XFrag<F> xf;
-          load_xfrag<F>(xl, t < T ? t : T - 1, ok ? ul : 0, xf);
+        for (int r = 0; r < R; ++r) dv[r] = own_first(dec[r], xf);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const float v = unit_value(dec[r], xf);
-            acc[r][t] += ok ? v : 0.f;
-          }
-        }
+        for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(dv[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][t] = own_apply(dec[r], own_second(dec[r], xs, dv[r]), p, acc[r][t]);
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int q = 0; q < NU; ++q) cur[r][q] = nxt[r][q];
+      for (int r = 0; r < R; ++r) cur[r] = nxt[r];
     }
   }
 
@@ -515,7 +547,6 @@ __global__ __launch_bounds__(64 * WPB) void k_multi(StreamArgs a) {
           a.y[(int64_t)t * a.ldy + row0 + r] = v;
       }
   } else {
-    // team partials: red[team][kw][g][v]
     float* mine = red + ((team * KS + kw) * GPW + g) * NV;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -550,11 +581,11 @@ const Variant kVariants[] = {
     {2, 64, 1, 7, 4, 1, 0, "fl_w4_r1_u7_g"},  {2, 64, 1, 2, 4, 1, 1, "fl_w4_r1_u2_l"},
     {2, 64, 1, 2, 16, 1, 1, "fl_w16_r1_u2_l"}, {2, 64, 1, 3, 16, 1, 1, "fl_w16_r1_u3_l"},
     {2, 64, 1, 7, 8, 1, 1, "fl_w8_r1_u7_l"},  {2, 64, 2, 2, 16, 1, 1, "fl_w16_r2_u2_l"},
-    {3, 16, 2, 2, 4, 1, 1, "mu_l16_r2_u2_w4"}, {3, 8, 2, 2, 4, 1, 1, "mu_l8_r2_u2_w4"},
-    {3, 16, 4, 1, 4, 1, 1, "mu_l16_r4_u1_w4"}, {3, 8, 4, 1, 4, 1, 1, "mu_l8_r4_u1_w4"},
-    {3, 16, 2, 2, 8, 1, 1, "mu_l16_r2_u2_w8"}, {3, 16, 1, 2, 4, 1, 1, "mu_l16_r1_u2_w4"},
-    {3, 16, 2, 1, 8, 4, 1, "mu_l16_r2_u1_w8_k4"}, {3, 8, 4, 1, 8, 4, 1, "mu_l8_r4_u1_w8_k4"},
-    {3, 16, 2, 1, 8, 2, 1, "mu_l16_r2_u1_w8_k2"}, {3, 8, 2, 1, 16, 8, 1, "mu_l8_r2_u1_w16_k8"},
+    {3, 16, 2, 1, 8, 2, 1, "mt_r2_w8_k2"},    {3, 16, 2, 1, 8, 4, 1, "mt_r2_w8_k4"},
+    {3, 16, 4, 1, 8, 2, 1, "mt_r4_w8_k2"},    {3, 16, 4, 1, 8, 4, 1, "mt_r4_w8_k4"},
+    {3, 16, 2, 1, 4, 1, 1, "mt_r2_w4_k1"},    {3, 16, 4, 1, 4, 1, 1, "mt_r4_w4_k1"},
+    {3, 16, 1, 1, 8, 4, 1, "mt_r1_w8_k4"},    {3, 16, 2, 1, 16, 8, 1, "mt_r2_w16_k8"},
+    {3, 16, 2, 1, 16, 4, 1, "mt_r2_w16_k4"},  {3, 16, 1, 1, 16, 8, 1, "mt_r1_w16_k8"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -566,7 +597,9 @@ static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
   constexpr int RWG = 4 * (64 / LPR) * R;
   const unsigned tiles = (unsigned)((a.n_rows + RWG - 1) / RWG);
   if (a.slices > 1) {
-    const int ups = (a.units + a.slices - 1) / a.slices;
+    // units per slice, a multiple of eight so that every slice starts on a
+    // super-block (lane pairs and header quads stay inside one slice)
+    const int ups = ((a.units + a.slices - 1) / a.slices + 7) & ~7;
     hipLaunchKernelGGL((k_matvec<F, TM, LPR, R, true>), dim3(tiles, (unsigned)a.slices), dim3(256),
                        0, st, a.w, a.row_bytes, a.n_rows, a.units, a.x, a.n_tok, a.y, a.ldy, ups,
                        a.part, a.cnt);
@@ -628,17 +661,17 @@ static hipError_t run_stream(const MatvecLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int F, int TM, int R, int NU, int WPB, bool XL>
+template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC = 8>
 static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
   if constexpr (!XL && TM > 4) {
     // fragments of more than four tokens do not fit in registers: stage them
-    return run_flat<F, TM, R, NU, WPB, true>(a, st);
+    return run_flat<F, TM, R, NU, WPB, true, OCC>(a, st);
   } else {
     const size_t lds = XL ? (size_t)a.act_bytes : 0;
     const int64_t groups = (a.n_rows + R - 1) / R;
     const unsigned grid = (unsigned)((groups + WPB - 1) / WPB);
     StreamArgs sa = stream_args(a);
-    hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+    hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC>), dim3(grid), dim3(64 * WPB), lds, st, sa);
     return hipGetLastError();
   }
 }
@@ -658,16 +691,17 @@ int multi_chunk_units(int units, int n_tok, int step, int64_t lds_budget) {
   return (per + lcm - 1) / lcm * lcm;
 }
 
-template <int F, int TM, int LPR, int R, int NU, int WPB, int KS>
-static hipError_t run_multi(const MatvecLaunch& a, hipStream_t st) {
+template <int F, int TM, int R, int WPB, int KS>
+static hipError_t run_mt(const MatvecLaunch& a, hipStream_t st) {
   StreamArgs sa = stream_args(a);
-  constexpr int RWG = (WPB / KS) * (64 / LPR) * R;  // rows per workgroup
-  const int64_t red_bytes = (int64_t)WPB * (64 / LPR) * R * TM * 4;
-  sa.kc = multi_chunk_units(a.units, a.n_tok, LPR * NU, kMultiLdsBudget - red_bytes);
+  constexpr int RWG = (WPB / KS) * 4 * R;  // rows per workgroup
+  const int64_t red_bytes = KS > 1 ? (int64_t)WPB * 4 * R * TM * 4 : 0;
+  constexpr int US = mt_stride<TM>();
+  sa.kc = multi_chunk_units(a.units, US, 16, kMultiLdsBudget - red_bytes);
   if (sa.kc <= 0) return hipErrorInvalidValue;
-  const size_t lds = (size_t)a.n_tok * sa.kc * 40 + (KS > 1 ? red_bytes : 0);
+  const size_t lds = (size_t)US * sa.kc * 40 + red_bytes;
   const unsigned grid = (unsigned)((a.n_rows + RWG - 1) / RWG);
-  hipLaunchKernelGGL((k_multi<F, TM, LPR, R, NU, WPB, KS>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+  hipLaunchKernelGGL((k_mt<F, TM, R, WPB, KS>), dim3(grid), dim3(64 * WPB), lds, st, sa);
   return hipGetLastError();
 }
 
@@ -686,22 +720,22 @@ static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
     case 9: return run_flat<F, TM, 2, 2, 4, false>(a, st);
     case 10: return run_flat<F, TM, 1, 3, 4, false>(a, st);
     case 11: return run_flat<F, TM, 1, 4, 4, false>(a, st);
-    case 12: return run_flat<F, TM, 1, 7, 4, false>(a, st);
+    case 12: return run_flat<F, TM, 1, 7, 4, false, 4>(a, st);
     case 13: return run_flat<F, TM, 1, 2, 4, true>(a, st);
     case 14: return run_flat<F, TM, 1, 2, 16, true>(a, st);
     case 15: return run_flat<F, TM, 1, 3, 16, true>(a, st);
     case 16: return run_flat<F, TM, 1, 7, 8, true>(a, st);
     case 17: return run_flat<F, TM, 2, 2, 16, true>(a, st);
-    case 18: return run_multi<F, TM, 16, 2, 2, 4, 1>(a, st);
-    case 19: return run_multi<F, TM, 8, 2, 2, 4, 1>(a, st);
-    case 20: return run_multi<F, TM, 16, 4, 1, 4, 1>(a, st);
-    case 21: return run_multi<F, TM, 8, 4, 1, 4, 1>(a, st);
-    case 22: return run_multi<F, TM, 16, 2, 2, 8, 1>(a, st);
-    case 23: return run_multi<F, TM, 16, 1, 2, 4, 1>(a, st);
-    case 24: return run_multi<F, TM, 16, 2, 1, 8, 4>(a, st);
-    case 25: return run_multi<F, TM, 8, 4, 1, 8, 4>(a, st);
-    case 26: return run_multi<F, TM, 16, 2, 1, 8, 2>(a, st);
-    case 27: return run_multi<F, TM, 8, 2, 1, 16, 8>(a, st);
+    case 18: return run_mt<F, TM, 2, 8, 2>(a, st);
+    case 19: return run_mt<F, TM, 2, 8, 4>(a, st);
+    case 20: return run_mt<F, TM, 4, 8, 2>(a, st);
+    case 21: return run_mt<F, TM, 4, 8, 4>(a, st);
+    case 22: return run_mt<F, TM, 2, 4, 1>(a, st);
+    case 23: return run_mt<F, TM, 4, 4, 1>(a, st);
+    case 24: return run_mt<F, TM, 1, 8, 4>(a, st);
+    case 25: return run_mt<F, TM, 2, 16, 8>(a, st);
+    case 26: return run_mt<F, TM, 2, 16, 4>(a, st);
+    case 27: return run_mt<F, TM, 1, 16, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,8 +14,9 @@
 //   2. the slots routed to e, compacted in slot order with wave ballots.
 // A lane group of LPR lanes owns one row of W[e]: it issues all the loads of
 // the row at once (NU units per lane, block headers shared by lane quads),
-// decodes them into registers once and reuses them for every slot routed to
-// e, so each active expert's weights are read from HBM once per call.  The
+// decodes them into registers once and applies them, in the own-block form of
+// qmv_device.h, to every slot routed to e, so each active expert's weights
+// are read from HBM once per call.  The
 // next slot's activation fragments are fetched while the current slot is
 // computed.
 //
@@ -130,37 +131,38 @@ __global__ __launch_bounds__(256) void k_moe(MoeLaunch a) {
   const uint8_t* wr = a.w + ((int64_t)e * a.n_rows + min(row, a.n_rows - 1)) * a.row_bytes;
   const Act x{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
   const int units = a.units;
-  Dec<F> dec[NU];
+  DecO<F> dec[NU];
   {
     RawS<F> raw[NU];
 #pragma unroll
     for (int q = 0; q < NU; ++q) load_unit_s(wr, min(gl + LPR * q, units - 1), lane, raw[q]);
 #pragma unroll
-    for (int q = 0; q < NU; ++q) decode_unit_s(raw[q], min(gl + LPR * q, units - 1), dec[q]);
+    for (int q = 0; q < NU; ++q)
+      decode_own(raw[q], min(gl + LPR * q, units - 1), gl & 1, gl + LPR * q < units, dec[q]);
   }
 
   auto slot_row = [&](int j) {
     const int i = s_list[j];
     return a.x_per_slot ? i : i / a.top_k;
   };
-  XFrag<F> xf[NU];
+  XO xf[NU];
   if (n_e > 0) {
     const int xr = slot_row(0);
 #pragma unroll
-    for (int q = 0; q < NU; ++q) load_xfrag<F>(x, xr, min(gl + LPR * q, units - 1), xf[q]);
+    for (int q = 0; q < NU; ++q) load_xo<F>(x, xr, min(gl + LPR * q, units - 1), xf[q]);
   }
   for (int j = 0; j < n_e; ++j) {
     const int i = s_list[j];
-    XFrag<F> nx[NU];
+    XO nx[NU];
     const int xr_next = slot_row(min(j + 1, n_e - 1));
 #pragma unroll
-    for (int q = 0; q < NU; ++q) load_xfrag<F>(x, xr_next, min(gl + LPR * q, units - 1), nx[q]);
+    for (int q = 0; q < NU; ++q) load_xo<F>(x, xr_next, min(gl + LPR * q, units - 1), nx[q]);
     float acc = 0.f;
+    int dv[NU];
 #pragma unroll
-    for (int q = 0; q < NU; ++q) {
-      const float v = unit_value(dec[q], xf[q]);
-      acc += gl + LPR * q < units ? v : 0.f;
-    }
+    for (int q = 0; q < NU; ++q) dv[q] = own_pass<F>(own_first(dec[q], xf[q].f));
+#pragma unroll
+    for (int q = 0; q < NU; ++q) acc = own_apply(dec[q], own_second(dec[q], xf[q].s, dv[q]), xf[q].p, acc);
     acc = lane_group_sum<LPR>(acc);
     if (gl == 0 && row < a.n_rows) {
       float* out = a.rw == nullptr ? a.y : a.part;

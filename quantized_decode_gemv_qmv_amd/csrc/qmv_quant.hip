@@ -60,8 +60,11 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t
 }
 
 // ------------------------------------------------------------- block dots
-// One thread per (token, row, 32-block), through the same load, decode and
-// integer dot routines as the matvec kernels.
+// One thread per (token, row, 32-block), through the same weight decode,
+// activation fetch and paired integer dot (own_first, own_pass, own_second)
+// as the matvec kernels: thread b holds unit b, whose own block is 32-block b,
+// and the threads of a pair (b even, b + 1) sit side by side in one wave
+// (K / 32 is even for q4_K, so no pair is split by a row or by the grid end).
 template <int F>
 __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ w, int64_t row_bytes,
                                                     int n_rows, int units, ActView xv, int n_tok,
@@ -73,39 +76,19 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ 
   const int t = (int)(gid / ((int64_t)units * n_rows));
   const Act x{xv.qs, xv.d, xv.s, xv.k, xv.nb};
   const uint8_t* wr = w + (int64_t)row * row_bytes;
+  Raw<F> raw;
+  DecO<F> dec;
+  XO xo;
+  load_unit(wr, b, raw);
+  decode_own(raw, b, b & 1, true, dec);
+  load_xo<F>(x, t, b, xo);
+  const int dot = own_second(dec, xo.s, own_pass<F>(own_first(dec, xo.f)));
   if constexpr (F == FQ4_K) {
-    // 32-block b = sub-block jj of super-block sb lives in the low (jj even)
-    // or high (jj odd) nibbles of units 2*(jj/2) and 2*(jj/2)+1
-    const int sb = b >> 3, jj = b & 7;
-    const int u0 = 8 * sb + 2 * (jj >> 1);
-    int A = 0, B = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      Raw<F> raw;
-      Dec<F> dec;
-      XFrag<F> xf;
-      load_unit(wr, u0 + h, raw);
-      decode_unit(raw, u0 + h, dec);
-      load_xfrag<F>(x, t, u0 + h, xf);
-      int lo, hi;
-      unit_int(dec, xf, lo, hi);
-      A += (jj & 1) ? dec.sc1 * hi : dec.sc0 * lo;
-      if (h == 0) B = (jj & 1) ? dec.m1 * xf.s1 : dec.m0 * xf.s0;
-    }
-    out[2 * gid] = A;
-    out[2 * gid + 1] = B;
+    // sub-block b: scale times the integer dot, and min times the block sum
+    out[2 * gid] = dec.isc * dot;
+    out[2 * gid + 1] = dec.im * x.s[(int64_t)t * x.nb + b];
   } else {
-    Raw<F> raw;
-    Dec<F> dec;
-    XFrag<F> xf;
-    load_unit(wr, b, raw);
-    decode_unit(raw, b, dec);
-    load_xfrag<F>(x, t, b, xf);
-    int lo, hi;
-    unit_int(dec, xf, lo, hi);
-    int p = lo + hi;
-    if constexpr (F == FIQ4_XS) p *= dec.ls;
-    out[gid] = p;
+    out[gid] = dec.isc * dot;  // Q8_0: isc = 1; IQ4_XS: the signed sub-block scale
   }
 }
 

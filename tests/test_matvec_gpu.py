@@ -64,6 +64,31 @@ def test_every_token_count_and_variant(fmt):
         qmv.set_tuning("variant", -1)
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=[NAMES[f] for f in FMTS])
+def test_chunked_variants_long_k(fmt):
+    """The LDS-chunked multi-token kernels on a row several chunks long
+    (K = 14336 at 16 tokens), with a ragged token count and row tail."""
+    qmv = need_gpu()
+    n, k = 77, 14336
+    w = synth.make_weights(fmt, n, k, f"lk/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(16, k, f"lkx/{fmt}")
+    chunked = [v for v in range(len(qmv.variants()))
+               if qmv.variant_name(v).startswith("mt_")]
+    assert chunked
+    try:
+        for v in chunked:
+            qmv.set_tuning("variant", v)
+            for t in (16, 5, 2):
+                say(f"matvec long K {NAMES[fmt]} variant {qmv.variant_name(v)} T={t}")
+                xq = quantize(qmv, x[:t])
+                y = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+                yr, mag = _oracle_y(fmt, w, k, x[:t])
+                assert_y(y, yr, mag, f"{NAMES[fmt]} {qmv.variant_name(v)} T={t}")
+    finally:
+        qmv.set_tuning("variant", -1)
+
+
 FULL = [
     ("q8_0_4096x4096", synth.Q8_0, 4096, 4096, (1,)),
     ("q4_k_14336x4096", synth.Q4_K, 14336, 4096, (1, 2, 4, 8, 16)),
