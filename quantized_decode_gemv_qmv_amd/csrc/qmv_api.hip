@@ -120,10 +120,9 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 // IQ4_XS 4096x14336, Q8_0 256x65536; 1..16 tokens):
 //   - too few rows to give every compute unit several waves, long K: the
 //     streaming kernel with K split over a 16-wave workgroup;
-//   - one token (four for Q8_0): the flat kernel (one wave per row group,
-//     all loads issued at once), activations staged in LDS for Q8_0,
-//     prefetched from global memory for the 4-bit formats, units per lane
-//     sized so that one chunk covers the row;
+//   - up to two tokens (four for Q8_0): the flat kernel (one wave per row
+//     group, all loads issued at once), its units per lane sized so that one
+//     chunk covers the row;
 //   - more tokens: the multi-token kernel, its shape picked by rows per
 //     compute unit -- many rows: several rows per lane group and no K split;
 //     fewer: K split over more waves so that every compute unit still gets a
@@ -134,22 +133,16 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int cus = device_cus();
   const int64_t nu = (units + 63) / 64;
   const int64_t rpc = n_rows / cus;  // rows per compute unit
-  const char* multi = rpc >= 128 ? "mt_r4_w4_k1" : rpc >= 32 ? "mt_r2_w8_k2" : rpc >= 16 ? "mt_r2_w16_k8" : "mt_r1_w16_k8";
   const char* name;
   if (n_rows < 4 * (int64_t)cus && units >= 256) {
     name = "st_k16_r1_u2";
-  } else if (type == QMV_Q8_0) {
-    if (n_tok <= 4)
-      name = nu <= 2 ? "fl_w16_r1_u2_l" : nu <= 3 ? "fl_w16_r1_u3_l" : "fl_w4_r1_u4_g";
-    else
-      name = multi;
-  } else if (n_tok <= 1) {
-    if (type == QMV_Q4_K)
-      name = nu <= 2 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u4_g";
-    else
-      name = nu <= 2 ? "fl_w4_r2_u2_g" : nu <= 7 ? "fl_w4_r1_u7_g" : "fl_w4_r1_u4_g";
+  } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2)) {
+    name = nu <= 2 ? (type == QMV_Q8_0 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_g")
+           : nu <= 3 ? "fl_w16_r1_u3_l"
+           : nu <= 7 ? "fl_w8_r1_u7_l"
+                     : "fl_w4_r1_u4_g";
   } else {
-    name = multi;
+    name = rpc >= 128 ? "mt_r4_w4_k1" : rpc >= 32 ? "mt_r2_w8_k2" : rpc >= 16 ? "mt_r2_w16_k8" : "mt_r1_w16_k8";
   }
   int v = find_variant(name);
   if (!stream_fits(v, k, n_tok)) v = find_variant("mt_r2_w8_k4");

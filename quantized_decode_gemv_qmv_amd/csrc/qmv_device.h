@@ -34,6 +34,7 @@ template <> struct Fmt<FIQ4_XS> { static constexpr int QK = 256, BB = 136, UPB =
 // loads of several dwords need dword alignment only.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // Weight loads.  Plain cached loads: a Q8_0 block is read by three
 // instructions (two 16-byte halves and the scale) that share cache lines,
@@ -455,6 +456,30 @@ __device__ __forceinline__ float wave_sum(float v) {
           __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
          (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
           __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+
+// ----------------------------------------------------- activation quantizer
+// One Q8 activation block of 32 values held by an aligned group of 8 lanes,
+// four values per lane (Castagna Veloce page, "Fused operations"): amax and
+// the quant sum are 8-lane DPP reductions; d = amax / 127 and x / d are IEEE
+// fp32 divisions (the library is built without fast-math) and roundf rounds
+// halfway cases away from zero.  Returns the lane's four quants packed into a
+// dword; every lane of the group gets d and the sum.
+__device__ __forceinline__ uint32_t q8_block8(const float (&vv)[4], float& db, int& sum) {
+  float amax = fmaxf(fmaxf(fabsf(vv[0]), fabsf(vv[1])), fmaxf(fabsf(vv[2]), fabsf(vv[3])));
+  amax = max8(amax);
+  db = amax / 127.0f;
+  int q[4] = {0, 0, 0, 0};
+  if (amax != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = static_cast<int>(roundf(vv[i] / db));
+      q[i] = r > 127 ? 127 : (r < -127 ? -127 : r);
+    }
+  }
+  sum = sum8(q[0] + q[1] + q[2] + q[3]);
+  return (uint32_t)(q[0] & 255) | ((uint32_t)(q[1] & 255) << 8) | ((uint32_t)(q[2] & 255) << 16) |
+         ((uint32_t)(q[3] & 255) << 24);
 }
 
 }  // namespace qmv

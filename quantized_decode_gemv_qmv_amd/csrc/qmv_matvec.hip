@@ -301,40 +301,50 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
 #pragma unroll
   for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
 
-  RawS<F> cur[R][NU];
-#pragma unroll
-  for (int q = 0; q < NU; ++q)
-#pragma unroll
-    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
-
   const Act gx{reinterpret_cast<const int8_t*>(a.xq), reinterpret_cast<const float*>(a.xq + a.off_d),
                reinterpret_cast<const int32_t*>(a.xq + a.off_s), a.k, a.nb};
   const Act lx{reinterpret_cast<const int8_t*>(s_mem),
                reinterpret_cast<const float*>(s_mem + a.off_d),
                reinterpret_cast<const int32_t*>(s_mem + a.off_s), a.k, a.nb};
   XO xf[NU][TX];
+  // Load order.  Vector-memory loads complete in issue order, so the small,
+  // cache-resident activation loads go first -- the fragments themselves, or
+  // the first batch of the LDS copy -- and the weight units follow in the
+  // order they are computed: unit q can then be decoded while units q+1.. are
+  // still on their way from HBM, and the LDS copy is written (and its
+  // barrier passed) while all the weights are.  Scheduling barriers keep the
+  // compiler from interleaving the phases.  The first batch is loaded
+  // unconditionally with clamped indices: a branch around a load makes the
+  // compiler wait for its value where the branches join.
+  const int n16 = a.act_bytes >> 4;  // LDS copy: 16-byte pieces
+  u32x4 stg[4];
   if constexpr (XL) {
-    const int n16 = a.act_bytes >> 4;
-    for (int base = 0; base < n16; base += 4 * NT) {
-      u32x4 v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = base + threadIdx.x + i * NT;
-        if (idx < n16) v[i] = ld16(a.xq + 16 * (int64_t)idx);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = base + threadIdx.x + i * NT;
-        if (idx < n16) reinterpret_cast<u32x4a*>(s_mem)[idx] = v[i];
-      }
-    }
-    __syncthreads();
+    for (int i = 0; i < 4; ++i) stg[i] = ld16(a.xq + 16 * (int64_t)min((int)threadIdx.x + i * NT, n16 - 1));
   } else {
 #pragma unroll
     for (int q = 0; q < NU; ++q)
 #pragma unroll
       for (int t = 0; t < TM; ++t)
         load_xo<F>(gx, t < a.n_tok ? t : a.n_tok - 1, min(lane + 64 * q, units - 1), xf[q][t]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  RawS<F> cur[R][NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (XL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (i * NT < n16 && idx < n16) reinterpret_cast<u32x4a*>(s_mem)[idx] = stg[i];
+    }
+    for (int idx = threadIdx.x + 4 * NT; idx < n16; idx += NT)  // large buffers
+      reinterpret_cast<u32x4a*>(s_mem)[idx] = ld16(a.xq + 16 * (int64_t)idx);
+    __syncthreads();
   }
 
   float acc[R][TM];
@@ -421,9 +431,10 @@ struct FastDiv {
 template <int TM>
 constexpr int mt_stride() { return TM % 2 == 0 ? TM + 1 : TM; }
 
-template <int F, int TM, int R, int WPB, int KS>
+template <int F, int TM, int R, int NU, int WPB, int KS>
 __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
   constexpr int LPR = 16, GPW = 4;
+  constexpr int STEP = LPR * NU;  // units a lane group covers per iteration
   static_assert(R * TM <= 64 && WPB % KS == 0, "layout");
   constexpr int TEAMS = WPB / KS;
   constexpr int NT = 64 * WPB;
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
   const int g = lane / LPR, gl = lane % LPR, h = lane & 1;
   const int row0 = ((blockIdx.x * TEAMS + team) * GPW + g) * R;
   const int units = a.units, kc = a.kc, T = a.n_tok;
-  const int ipc = kc / LPR;
+  const int ipc = kc / STEP;
   const int nchunk = (units + kc - 1) / kc;
   const uint8_t* wr[R];
 #pragma unroll
@@ -452,10 +463,13 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
   const float* gd = reinterpret_cast<const float*>(a.xq + a.off_d);
   const int32_t* gs = reinterpret_cast<const int32_t*>(a.xq + a.off_s);
 
-  auto load_it = [&](int c, int cit, RawS<F> (&buf)[R]) {
-    const int u = min(c * kc + cit * LPR + gl, units - 1);
+  auto load_it = [&](int c, int cit, RawS<F> (&buf)[R][NU]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) load_unit_s(wr[r], u, lane, buf[r]);
+    for (int q = 0; q < NU; ++q) {
+      const int u = min(c * kc + cit * STEP + gl + LPR * q, units - 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) load_unit_s(wr[r], u, lane, buf[r][q]);
+    }
   };
   auto stage = [&](int c) {
     const int c0 = c * kc, cu = min(kc, units - c0);
@@ -492,7 +506,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[r][t] = 0.f;
 
-  RawS<F> cur[R];
+  RawS<F> cur[R][NU];
   load_it(0, kw, cur);
   for (int c = 0; c < nchunk; ++c) {
     __syncthreads();  // every wave is done with the previous chunk
@@ -504,36 +518,41 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
         nc = c + 1 < nchunk ? c + 1 : c;
         ncit = c + 1 < nchunk ? kw : cit;
       }
-      RawS<F> nxt[R];
+      RawS<F> nxt[R][NU];
       load_it(nc, ncit, nxt);
-      const int ul = cit * LPR + gl;  // unit inside the chunk
-      const int uraw = c * kc + ul;
-      const bool ok = uraw < units;
-      const int u = ok ? uraw : units - 1;
-      const int li = ok ? ul : 0;  // a staged slot, for units past the end
-      DecO<F> dec[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) decode_own(cur[r], u, h, ok, dec[r]);
-      const u32x4a* pf = ld_f + li * US;
-      const u32x4a* ps = ld_s + li * US;
-      const float2* pp = ld_p + li * US;
+      for (int q = 0; q < NU; ++q) {
+        const int ul = cit * STEP + gl + LPR * q;  // unit inside the chunk
+        const int uraw = c * kc + ul;
+        const bool ok = uraw < units;
+        const int u = ok ? uraw : units - 1;
+        const int li = ok ? ul : 0;  // a staged slot, for units past the end
+        DecO<F> dec[R];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        // token slots past the call's token count (t >= T) hold stale LDS
-        // bytes: they only feed acc[.][t], which is never stored
-        const u32x4 xf = pf[t];
-        const u32x4 xs = ps[t];
-        const float2 p = pp[t];
-        int dv[R];
+        for (int r = 0; r < R; ++r) decode_own(cur[r][q], u, h, ok, dec[r]);
+        const u32x4a* pf = ld_f + li * US;
+        const u32x4a* ps = ld_s + li * US;
+        const float2* pp = ld_p + li * US;
 #pragma unroll
-        for (int r = 0; r < R; ++r) dv[r] = own_first(dec[r], xf);
+        for (int t = 0; t < TM; ++t) {
+          // token slots past the call's token count (t >= T) hold stale LDS
+          // bytes: they only feed acc[.][t], which is never stored
+          const u32x4 xf = pf[t];
+          const u32x4 xs = ps[t];
+          const float2 p = pp[t];
+          int dv[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(dv[r]);
+          for (int r = 0; r < R; ++r) dv[r] = own_first(dec[r], xf);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][t] = own_apply(dec[r], own_second(dec[r], xs, dv[r]), p, acc[r][t]);
+          for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(dv[r]);
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r][t] = own_apply(dec[r], own_second(dec[r], xs, dv[r]), p, acc[r][t]);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) cur[r] = nxt[r];
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < NU; ++q) cur[r][q] = nxt[r][q];
     }
   }
 
@@ -582,10 +601,13 @@ const Variant kVariants[] = {
     {2, 64, 1, 2, 16, 1, 1, "fl_w16_r1_u2_l"}, {2, 64, 1, 3, 16, 1, 1, "fl_w16_r1_u3_l"},
     {2, 64, 1, 7, 8, 1, 1, "fl_w8_r1_u7_l"},  {2, 64, 2, 2, 16, 1, 1, "fl_w16_r2_u2_l"},
     {3, 16, 2, 1, 8, 2, 1, "mt_r2_w8_k2"},    {3, 16, 2, 1, 8, 4, 1, "mt_r2_w8_k4"},
-    {3, 16, 4, 1, 8, 2, 1, "mt_r4_w8_k2"},    {3, 16, 4, 1, 8, 4, 1, "mt_r4_w8_k4"},
-    {3, 16, 2, 1, 4, 1, 1, "mt_r2_w4_k1"},    {3, 16, 4, 1, 4, 1, 1, "mt_r4_w4_k1"},
-    {3, 16, 1, 1, 8, 4, 1, "mt_r1_w8_k4"},    {3, 16, 2, 1, 16, 8, 1, "mt_r2_w16_k8"},
-    {3, 16, 2, 1, 16, 4, 1, "mt_r2_w16_k4"},  {3, 16, 1, 1, 16, 8, 1, "mt_r1_w16_k8"},
+    {3, 16, 4, 1, 8, 2, 1, "mt_r4_w8_k2"},    {3, 16, 4, 1, 4, 1, 1, "mt_r4_w4_k1"},
+    {3, 16, 2, 1, 4, 1, 1, "mt_r2_w4_k1"},    {3, 16, 1, 1, 8, 4, 1, "mt_r1_w8_k4"},
+    {3, 16, 2, 1, 16, 8, 1, "mt_r2_w16_k8"},  {3, 16, 1, 1, 16, 8, 1, "mt_r1_w16_k8"},
+    {3, 16, 2, 2, 8, 2, 1, "mt_r2_u2_w8_k2"}, {3, 16, 2, 2, 8, 1, 1, "mt_r2_u2_w8_k1"},
+    {3, 16, 2, 2, 16, 4, 1, "mt_r2_u2_w16_k4"}, {3, 16, 1, 2, 8, 2, 1, "mt_r1_u2_w8_k2"},
+    {3, 16, 2, 4, 8, 2, 1, "mt_r2_u4_w8_k2"}, {3, 16, 2, 2, 4, 1, 1, "mt_r2_u2_w4_k1"},
+    {3, 16, 1, 2, 16, 4, 1, "mt_r1_u2_w16_k4"}, {3, 16, 1, 4, 16, 4, 1, "mt_r1_u4_w16_k4"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -691,17 +713,17 @@ int multi_chunk_units(int units, int n_tok, int step, int64_t lds_budget) {
   return (per + lcm - 1) / lcm * lcm;
 }
 
-template <int F, int TM, int R, int WPB, int KS>
+template <int F, int TM, int R, int NU, int WPB, int KS>
 static hipError_t run_mt(const MatvecLaunch& a, hipStream_t st) {
   StreamArgs sa = stream_args(a);
   constexpr int RWG = (WPB / KS) * 4 * R;  // rows per workgroup
   const int64_t red_bytes = KS > 1 ? (int64_t)WPB * 4 * R * TM * 4 : 0;
   constexpr int US = mt_stride<TM>();
-  sa.kc = multi_chunk_units(a.units, US, 16, kMultiLdsBudget - red_bytes);
+  sa.kc = multi_chunk_units(a.units, US, 16 * NU, kMultiLdsBudget - red_bytes);
   if (sa.kc <= 0) return hipErrorInvalidValue;
   const size_t lds = (size_t)US * sa.kc * 40 + red_bytes;
   const unsigned grid = (unsigned)((a.n_rows + RWG - 1) / RWG);
-  hipLaunchKernelGGL((k_mt<F, TM, R, WPB, KS>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+  hipLaunchKernelGGL((k_mt<F, TM, R, NU, WPB, KS>), dim3(grid), dim3(64 * WPB), lds, st, sa);
   return hipGetLastError();
 }
 
@@ -726,16 +748,22 @@ static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
     case 15: return run_flat<F, TM, 1, 3, 16, true>(a, st);
     case 16: return run_flat<F, TM, 1, 7, 8, true>(a, st);
     case 17: return run_flat<F, TM, 2, 2, 16, true>(a, st);
-    case 18: return run_mt<F, TM, 2, 8, 2>(a, st);
-    case 19: return run_mt<F, TM, 2, 8, 4>(a, st);
-    case 20: return run_mt<F, TM, 4, 8, 2>(a, st);
-    case 21: return run_mt<F, TM, 4, 8, 4>(a, st);
-    case 22: return run_mt<F, TM, 2, 4, 1>(a, st);
-    case 23: return run_mt<F, TM, 4, 4, 1>(a, st);
-    case 24: return run_mt<F, TM, 1, 8, 4>(a, st);
-    case 25: return run_mt<F, TM, 2, 16, 8>(a, st);
-    case 26: return run_mt<F, TM, 2, 16, 4>(a, st);
-    case 27: return run_mt<F, TM, 1, 16, 8>(a, st);
+    case 18: return run_mt<F, TM, 2, 1, 8, 2>(a, st);
+    case 19: return run_mt<F, TM, 2, 1, 8, 4>(a, st);
+    case 20: return run_mt<F, TM, 4, 1, 8, 2>(a, st);
+    case 21: return run_mt<F, TM, 4, 1, 4, 1>(a, st);
+    case 22: return run_mt<F, TM, 2, 1, 4, 1>(a, st);
+    case 23: return run_mt<F, TM, 1, 1, 8, 4>(a, st);
+    case 24: return run_mt<F, TM, 2, 1, 16, 8>(a, st);
+    case 25: return run_mt<F, TM, 1, 1, 16, 8>(a, st);
+    case 26: return run_mt<F, TM, 2, 2, 8, 2>(a, st);
+    case 27: return run_mt<F, TM, 2, 2, 8, 1>(a, st);
+    case 28: return run_mt<F, TM, 2, 2, 16, 4>(a, st);
+    case 29: return run_mt<F, TM, 1, 2, 8, 2>(a, st);
+    case 30: return run_mt<F, TM, 2, 4, 8, 2>(a, st);
+    case 31: return run_mt<F, TM, 2, 2, 4, 1>(a, st);
+    case 32: return run_mt<F, TM, 1, 2, 16, 4>(a, st);
+    case 33: return run_mt<F, TM, 1, 4, 16, 4>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,15 +5,10 @@
 
 namespace qmv {
 
-typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
-
 // ------------------------------------------------------ activation quantizer
 // Q8 activation blocks (Castagna Veloce page, "Fused operations": activations
 // quantized once and reused by every weight type).  Eight lanes per block of
-// 32 values, four values per lane from one 16-byte load: the block's max |x|
-// and the sum of its quants are 8-lane DPP reductions inside a row, so no
-// lane exchange leaves the DPP network.  Divisions are IEEE fp32 (the library
-// is built without fast-math) and roundf rounds halfway cases away from zero.
+// 32 values, four values per lane from one 16-byte load, through q8_block8.
 // Lanes past the last block redo the last block and store nothing, which keeps
 // every lane of a reduction group active.
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, int64_t ldx,
@@ -28,20 +23,9 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ x, i
   const int64_t t = blk / nb, b = blk % nb;
   const f32x4 v = *reinterpret_cast<const f32x4*>(x + t * ldx + 32 * b + 4 * j);
   const float vv[4] = {v.x, v.y, v.z, v.w};
-  float amax = fmaxf(fmaxf(fabsf(vv[0]), fabsf(vv[1])), fmaxf(fabsf(vv[2]), fabsf(vv[3])));
-  amax = max8(amax);
-  const float db = amax / 127.0f;
-  int q[4] = {0, 0, 0, 0};
-  if (amax != 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = static_cast<int>(roundf(vv[i] / db));
-      q[i] = r > 127 ? 127 : (r < -127 ? -127 : r);
-    }
-  }
-  const int sum = sum8(q[0] + q[1] + q[2] + q[3]);
-  const uint32_t packed = (uint32_t)(q[0] & 255) | ((uint32_t)(q[1] & 255) << 8) |
-                          ((uint32_t)(q[2] & 255) << 16) | ((uint32_t)(q[3] & 255) << 24);
+  float db;
+  int sum;
+  const uint32_t packed = q8_block8(vv, db, sum);
   if (valid) {
     *reinterpret_cast<uint32_t*>(qs + t * k + 32 * b + 4 * j) = packed;
     if (j == 0) {
