@@ -386,12 +386,16 @@ QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_expert
   a.n_rows = static_cast<int>(n_rows);
   a.units = static_cast<int>(k / 32);
   a.x = act_view(xq, x_rows, k);
+  a.x_rows = static_cast<int>(x_rows);
   a.x_per_slot = x_per_slot;
   a.ids = ids;
   a.rw = route_w;
   a.n_tok = static_cast<int>(n_tok);
   a.top_k = static_cast<int>(top_k);
   a.y = y;
+  const DeviceInfo dv = device_info();
+  a.cus = dv.cus;
+  a.lds_per_cu = dv.lds_per_cu;
   uint8_t* b = static_cast<uint8_t*>(ws);
   a.err = reinterpret_cast<int*>(b);
   a.part = reinterpret_cast<float*>(b + kMoePartOffset);

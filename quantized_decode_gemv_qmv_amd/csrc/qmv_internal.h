@@ -116,12 +116,15 @@ struct MoeLaunch {
   int n_tok;
   int top_k;
   float* y;
+  int cus;  // compute units of the device (persistent grid size)
+  int64_t lds_per_cu;
+  int ts;      // slot rows staged in LDS at a time (set at launch)
+  int x_rows;  // rows of the activation buffer
   // workspace
   int* err;     // dropped-slot count of the call
   float* part;  // [n_tok * top_k][n_rows] per-slot outputs (combine only)
 };
 
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t st);
-int moe_rows_per_wg(int fmt, int units);
 
 }  // namespace qmv
