@@ -50,7 +50,7 @@ FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS"}
 # expert, top-8 routing
 MOE = dict(name="moe_iq4_xs_e128", experts=128, top_k=8, gate_up=(3072, 4096), down=(4096, 1536),
            tokens=(1, 6, 16, 64))
-KERNEL_SOURCES = ("qmv_device.h", "qmv_matvec.hip", "qmv_quant.hip", "qmv_api.hip")
+KERNEL_SOURCES = ("qmv_device.h", "qmv_matvec.hip", "qmv_mfma.hip", "qmv_quant.hip", "qmv_api.hip")
 
 
 def log(msg: str) -> None:

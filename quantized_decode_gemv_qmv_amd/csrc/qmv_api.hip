@@ -123,16 +123,19 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //   - up to two tokens (four for Q8_0): the flat kernel (one wave per row
 //     group, all loads issued at once), its units per lane sized so that one
 //     chunk covers the row;
-//   - more tokens: the multi-token kernel, its shape picked by rows per
-//     compute unit -- many rows: several rows per lane group and no K split;
-//     fewer: K split over more waves so that every compute unit still gets a
-//     full workgroup.  Its LDS staging is chunked and so fits any K, which
-//     also makes it the fallback.
+//   - 3..8 tokens: the matrix-core kernel for IQ4_XS (and q4_K from five
+//     tokens), 16-wave workgroups with K split so that about 4096 waves
+//     cover the rows; otherwise the multi-token vector kernel;
+//   - 9..16 tokens: the matrix-core kernel, 8-wave workgroups with a
+//     four-deep load ring (the register budget of the 16-token tiles).
+//   The vector multi-token kernel's LDS staging is chunked and so fits any
+//   K, which also makes it the fallback.
 int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t units = k / 32;
   const int cus = device_cus();
   const int64_t nu = (units + 63) / 64;
   const int64_t rpc = n_rows / cus;  // rows per compute unit
+  const int64_t tiles = (n_rows + 15) / 16;
   const char* name;
   if (n_rows < 4 * (int64_t)cus && units >= 256) {
     name = "st_k16_r1_u2";
@@ -141,6 +144,12 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
            : nu <= 3 ? "fl_w16_r1_u3_l"
            : nu <= 7 ? "fl_w8_r1_u7_l"
                      : "fl_w4_r1_u4_g";
+  } else if (n_tok > 8) {
+    const int64_t per = 16 * (int64_t)cus / tiles;  // waves of K split per row tile
+    name = per >= 8 ? "mx_w8_k8_r4" : per >= 4 ? "mx_w8_k4_r4" : "mx_w8_k1_r4";
+  } else if (type == QMV_IQ4_XS || (type == QMV_Q4_K && n_tok > 4)) {
+    const int64_t per = 16 * (int64_t)cus / tiles;
+    name = per >= 16 ? "mx_w16_k16_r2" : per >= 8 ? "mx_w16_k8_r2" : "mx_w16_k4_r2";
   } else {
     name = rpc >= 128 ? "mt_r4_w4_k1" : rpc >= 32 ? "mt_r2_w8_k2" : rpc >= 16 ? "mt_r2_w16_k8" : "mt_r1_w16_k8";
   }

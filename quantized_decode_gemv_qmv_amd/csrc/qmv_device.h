@@ -409,6 +409,15 @@ __device__ __forceinline__ void own_piece_slot(int b, int hb, int& unit, int& ru
   }
 }
 
+// Division of small non-negative ints by a divisor fixed for a loop:
+// q = umulhi(n, ceil(2^32 / d)), exact whenever n * d < 2^32 (here n and d
+// stay below 2^16).  Saves the long integer division sequence per element.
+struct FastDiv {
+  uint32_t d, m;
+  __device__ explicit FastDiv(int dv) : d((uint32_t)dv), m(dv > 1 ? 0xFFFFFFFFu / (uint32_t)dv + 1u : 0u) {}
+  __device__ int div(int n) const { return d == 1u ? n : (int)__umulhi((uint32_t)n, m); }
+};
+
 // ------------------------------------------------------------- reductions
 // Sum over the LPR consecutive lanes of a lane group (LPR a power of two).
 template <int LPR>

@@ -29,7 +29,10 @@ struct ActView {
 //   kind 3: multi-token kernel (k_mt) -- lane groups of 16 lanes own `rows`
 //           rows, one unit per lane per iteration, wpb waves per workgroup in
 //           teams of ks waves that split K, activations staged in LDS chunk
-//           by chunk.
+//           by chunk;
+//   kind 4: matrix-core kernel (k_mx) -- a wave owns 16 rows, wpb waves per
+//           workgroup in teams of ks waves that split K, int8 MFMA per
+//           32-block, activations staged in LDS chunk by chunk.
 struct Variant {
   int kind;
   int lpr;
@@ -99,6 +102,7 @@ void set_blocks_per_cu(int v);
 hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
                            int32_t* s, hipStream_t st);
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
+hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,
                              ActView x, int n_tok, int32_t* out, hipStream_t st);
 

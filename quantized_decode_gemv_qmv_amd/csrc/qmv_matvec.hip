@@ -401,15 +401,6 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
 }
 
-// Division of small non-negative ints by a divisor fixed for a loop:
-// q = umulhi(n, ceil(2^32 / d)), exact whenever n * d < 2^32 (here n and d
-// stay below 2^16).  Saves the long integer division sequence per element.
-struct FastDiv {
-  uint32_t d, m;
-  __device__ explicit FastDiv(int dv) : d((uint32_t)dv), m(dv > 1 ? 0xFFFFFFFFu / (uint32_t)dv + 1u : 0u) {}
-  __device__ int div(int n) const { return d == 1u ? n : (int)__umulhi((uint32_t)n, m); }
-};
-
 // ------------------------------------------------------ multi-token kernel
 // For verify batches (several tokens).  A lane group of 16 lanes owns R rows
 // and walks them one unit per lane per iteration (each weight load of a group
@@ -608,6 +599,9 @@ const Variant kVariants[] = {
     {3, 16, 2, 2, 16, 4, 1, "mt_r2_u2_w16_k4"}, {3, 16, 1, 2, 8, 2, 1, "mt_r1_u2_w8_k2"},
     {3, 16, 2, 4, 8, 2, 1, "mt_r2_u4_w8_k2"}, {3, 16, 2, 2, 4, 1, 1, "mt_r2_u2_w4_k1"},
     {3, 16, 1, 2, 16, 4, 1, "mt_r1_u2_w16_k4"}, {3, 16, 1, 4, 16, 4, 1, "mt_r1_u4_w16_k4"},
+    {4, 16, 1, 2, 16, 4, 1, "mx_w16_k4_r2"},  {4, 16, 1, 2, 16, 8, 1, "mx_w16_k8_r2"},
+    {4, 16, 1, 2, 16, 16, 1, "mx_w16_k16_r2"}, {4, 16, 1, 4, 8, 1, 1, "mx_w8_k1_r4"},
+    {4, 16, 1, 4, 8, 4, 1, "mx_w8_k4_r4"},    {4, 16, 1, 4, 8, 8, 1, "mx_w8_k8_r4"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -634,7 +628,7 @@ static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
 }
 
 size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm) {
-  if (v.kind == 3) return 0;  // chunked to fit (kMultiLdsBudget)
+  if (v.kind >= 3) return 0;  // chunked to fit (kMultiLdsBudget)
   if (v.kind == 2) return v.xl || tm > 4 ? static_cast<size_t>(act_bytes) : 0;
   return static_cast<size_t>(act_bytes + (int64_t)v.ks * v.rows * tm * 4);
 }
@@ -778,6 +772,7 @@ static hipError_t run_mv_tokens(const MatvecLaunch& a, hipStream_t st) {
 }
 
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st) {
+  if (kVariants[a.variant].kind == 4) return launch_mx(a, st);
   switch (a.fmt) {
     case FQ8_0: return run_mv_tokens<FQ8_0>(a, st);
     case FQ4_K: return run_mv_tokens<FQ4_K>(a, st);

@@ -1,0 +1,538 @@
+// qmv_mfma.hip -- matrix-core matvec for verify batches (several tokens) on
+// gfx950.
+//
+// With a few tokens the vector-ALU kernels spend most of their issue slots on
+// the int8 dot products (eight v_dot4 per row, token and 32-block).  Here the
+// dots run on the matrix cores instead: one v_mfma_i32_16x16x64_i8 multiplies
+// 16 weight rows by a 64-wide slice of K for 16 "activation rows".  Its
+// result must stay per 32-block, because every 32-block carries its own
+// weight and activation scale (Castagna Veloce page, "Kernels for the MI50":
+// block-quantized dots; the tolerance and exact integer partials are per
+// block).  So each activation row m of the MFMA stands for one (block, token)
+// pair and holds that token's activations only in the K slots that carry the
+// block's weights, zeros elsewhere: D[m][n] is then exactly the integer dot of
+// block(m) of row n with token(m).
+//
+// Operand layout (measured on gfx950: lane l supplies A row l%16 and B column
+// l%16 for its 16 K slots of group s = l/16; it receives D[4s + r][l%16],
+// r = 0..3).  B = weights: lane (n, s) holds 16 decoded int8 weights of row n.
+// A = activations, staged in LDS.  The slot-to-weight assignment only has to
+// agree between A and B, so each format keeps the bytes of one 16-byte load:
+//
+//   q4_K (2 blocks per MFMA, m = 8j + t, 8 tokens per group): lane s holds
+//     16 weights of one sub-block, weights 16(s%2)..+15, and the two lanes
+//     s = 2j, 2j+1 together hold block j of the MFMA.  Lane s loads bytes
+//     16(s%2)..+15 of nibble pair 2p + s/2 of span p (sub-blocks 4p + 2(s/2)
+//     and its neighbour); the low-nibble MFMA then holds sub-blocks 4p and
+//     4p+2, the high-nibble one 4p+1 and 4p+3.
+//   IQ4_XS, Q8_0 (4 blocks per MFMA, m = 4j + t, 4 tokens per group): lane s
+//     loads 32-block 4p+s of span p (IQ4_XS: its 16 index bytes; Q8_0: its
+//     32 quants); the first MFMA takes its weights 0..15 (low nibbles / first
+//     16 quants), the second 16..31, and both accumulate into one result.
+// Activation rows therefore carry data in half (q4_K) or a quarter (IQ4_XS,
+// Q8_0) of the lanes; the other lanes' A registers are zeroed once and never
+// loaded (the LDS reads run under an execution mask).
+//
+// A lane's outputs are always one row, one block and four tokens, and the
+// block is one whose bytes the lane loaded itself, so its weight scale comes
+// from its own registers; the four activation scales are one 16-byte LDS
+// read from a block-major copy.  Each result then costs a conversion and one
+// or two FMAs per value.
+//
+// Schedule (as in the vector-ALU multi-token kernel): a wave owns 16 rows;
+// teams of KS waves split a row's super-blocks; the activations are staged in
+// LDS in chunks that all waves of the workgroup walk in step; the next
+// super-block's weight loads are issued before the current one is computed.
+#include "qmv_device.h"
+#include "qmv_internal.h"
+
+namespace qmv {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int F> constexpr int mx_tg() { return F == FQ4_K ? 8 : 4; }  // tokens per group
+
+// Raw bytes of one lane for one super-block (8 consecutive 32-blocks).
+template <int F> struct MxRaw;
+template <> struct MxRaw<FQ4_K> {
+  u32x4 q[2];  // span p = 0, 1: bytes 64p + 16s .. +15 of the nibble area
+  u32x4 hdr;   // d | dmin, 12 bytes of packed 6-bit scales and mins
+};
+template <> struct MxRaw<FIQ4_XS> {
+  u32x4 q[2];  // span p: the 16 index bytes of sub-block 4p + s
+  u32x2 hdr;   // d | scales_h, scales_l[0..3]
+};
+template <> struct MxRaw<FQ8_0> {
+  Raw<FQ8_0> b[2];  // span p: 32-block 8i + 4p + s
+};
+
+// Loads of one lane for the super-block starting at unit u0: `base` is the
+// wave-uniform address of the tile's first row, `off` the lane's row offset
+// (32 bits, so that the address is a scalar base plus a vector offset).
+__device__ __forceinline__ void mx_load(const uint8_t* base, uint32_t off, int u0, int s, int, MxRaw<FQ4_K>& r) {
+  const uint32_t blk = off + 144u * ((uint32_t)u0 >> 3);
+  r.hdr = ld_w16(base + blk);
+  r.q[0] = ld_w16(base + (blk + 16 + 16 * (uint32_t)s));
+  r.q[1] = ld_w16(base + (blk + 80 + 16 * (uint32_t)s));
+}
+__device__ __forceinline__ void mx_load(const uint8_t* base, uint32_t off, int u0, int s, int, MxRaw<FIQ4_XS>& r) {
+  const uint32_t blk = off + 136u * ((uint32_t)u0 >> 3);
+  r.hdr = ld_w8(base + blk);
+  r.q[0] = ld_w16(base + (blk + 8 + 16 * (uint32_t)s));
+  r.q[1] = ld_w16(base + (blk + 72 + 16 * (uint32_t)s));
+}
+// Q8_0 rows need not be a whole number of super-blocks: units past the row
+// end re-read the last unit (their scale is zeroed at decode).
+__device__ __forceinline__ void mx_load(const uint8_t* base, uint32_t off, int u0, int s, int units, MxRaw<FQ8_0>& r) {
+  load_unit(base + off, min(u0 + s, units - 1), r.b[0]);
+  load_unit(base + off, min(u0 + 4 + s, units - 1), r.b[1]);
+}
+
+// Decoded weights of one span for one lane: B operands of the two MFMA
+// halves and the scales of the lane's output blocks.
+struct MxDec {
+  u32x4 b[2];
+  float dw[2];  // weight scale of the output block of half h (IQ4_XS, Q8_0: both the same)
+  float wm[2];  // q4_K: dmin * m of that block
+};
+
+// q4_K: 6-bit (scale, min) of sub-block c (0..7) from the 12 packed bytes.
+__device__ __forceinline__ void q4k_scale_min(const u32x4& hdr, int c, uint32_t& sc, uint32_t& m) {
+  const uint32_t jj = 8u * (uint32_t)(c & 3);
+  const uint32_t hb = 2u * (uint32_t)(c >> 2);
+  const uint32_t s03 = hdr.y, s47 = hdr.z, s811 = hdr.w;
+  const uint32_t lo_sc = c < 4 ? s03 : s811;
+  const uint32_t lo_m = c < 4 ? s47 : s811;
+  sc = bfe(lo_sc, jj, 4) | (bfe(s03, jj + 4 + hb, 2) << 4);
+  m = bfe(lo_m, jj + 2 * hb, 4) | (bfe(s47, jj + 4 + hb, 2) << 4);
+}
+
+// p = span (0, 1), s = lane group, u0 = first unit of the super-block.
+__device__ __forceinline__ void mx_decode(const MxRaw<FQ4_K>& r, int p, int s, int, int, MxDec& o) {
+  const u32x4 q = r.q[p];
+  o.b[0] = u32x4{q.x & 0x0F0F0F0Fu, q.y & 0x0F0F0F0Fu, q.z & 0x0F0F0F0Fu, q.w & 0x0F0F0F0Fu};
+  o.b[1] = u32x4{(q.x >> 4) & 0x0F0F0F0Fu, (q.y >> 4) & 0x0F0F0F0Fu, (q.z >> 4) & 0x0F0F0F0Fu,
+                 (q.w >> 4) & 0x0F0F0F0Fu};
+  const float d = half_bits_to_float(r.hdr.x), dmin = half_bits_to_float(r.hdr.x >> 16);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t sc, m;
+    q4k_scale_min(r.hdr, 4 * p + 2 * (s >> 1) + h, sc, m);
+    o.dw[h] = d * static_cast<float>(sc);
+    o.wm[h] = dmin * static_cast<float>(m);
+  }
+}
+__device__ __forceinline__ void mx_decode(const MxRaw<FIQ4_XS>& r, int p, int s, int, int, MxDec& o) {
+  const u32x4 q = r.q[p];
+  o.b[0] = u32x4{iq4_lookup(q.x & 0x0F0F0F0Fu), iq4_lookup(q.y & 0x0F0F0F0Fu),
+                 iq4_lookup(q.z & 0x0F0F0F0Fu), iq4_lookup(q.w & 0x0F0F0F0Fu)};
+  o.b[1] = u32x4{iq4_lookup((q.x >> 4) & 0x0F0F0F0Fu), iq4_lookup((q.y >> 4) & 0x0F0F0F0Fu),
+                 iq4_lookup((q.z >> 4) & 0x0F0F0F0Fu), iq4_lookup((q.w >> 4) & 0x0F0F0F0Fu)};
+  const int c = 4 * p + s;
+  const uint32_t lo4 = (r.hdr.y >> (4 * c)) & 15u;
+  const uint32_t hi2 = (r.hdr.x >> (16 + 2 * c)) & 3u;
+  o.dw[0] = o.dw[1] = half_bits_to_float(r.hdr.x) * static_cast<float>(static_cast<int>(lo4 | (hi2 << 4)) - 32);
+  o.wm[0] = o.wm[1] = 0.f;
+}
+__device__ __forceinline__ void mx_decode(const MxRaw<FQ8_0>& r, int p, int s, int u0, int units, MxDec& o) {
+  Dec<FQ8_0> d;
+  decode_unit(r.b[p], 0, d);
+  o.b[0] = u32x4{d.q[0], d.q[1], d.q[2], d.q[3]};
+  o.b[1] = u32x4{d.q[4], d.q[5], d.q[6], d.q[7]};
+  const bool ok = u0 + 4 * p + s < units;
+  o.dw[0] = o.dw[1] = ok ? d.d : 0.f;
+  o.wm[0] = o.wm[1] = 0.f;
+}
+
+__device__ __forceinline__ i32x4 mfma64(const u32x4& a, const u32x4& b, i32x4 c) {
+  const i32x4 av = __builtin_bit_cast(i32x4, a);
+  const i32x4 bv = __builtin_bit_cast(i32x4, b);
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+}
+
+// Work of one wave: its team's row tiles tile0 + i * gridDim.x * TEAMS
+// (rounds i), and in each tile the super-blocks sb = kw, kw + KS, .. of the
+// row.  A chunk holds ipc super-blocks, a multiple of KS, so the wave's
+// super-blocks fall into the chunks in order.  Items q = i * n_it + j are
+// loaded PF items ahead of the one computed.
+template <int F, int TM, int WPB, int KS, int PF, bool CH>
+__global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
+  constexpr int TG = mx_tg<F>();
+  constexpr int NG = (TM + TG - 1) / TG;  // token groups
+  constexpr int TMP = NG * TG;            // staged token rows
+  constexpr int TEAMS = WPB / KS;
+  constexpr int NT = 64 * WPB;
+  constexpr bool Q4K = F == FQ4_K;
+  constexpr bool P2 = Q4K;  // two blocks per MFMA (q4_K), else four
+  constexpr int SB = 4;            // staged 16-byte pieces per thread kept in flight
+  // LDS, block-major: block b of the chunk holds its 32 quant bytes of every
+  // token at b * BS + t * 32 (BS skewed by 16 bytes), its activation scales
+  // d at dl[b * TMP + t] and (q4_K) d * s at sl[b * TMP + t]
+  constexpr int BS = TMP * 32 + 16;
+  static_assert(WPB % KS == 0, "teams");
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int team = wave / KS, kw = wave % KS;
+  const int n = lane & 15, s = lane >> 4;
+  const int units = a.units, kc = a.kc, T = a.n_tok;
+  const int nsb = (units + 7) >> 3;  // super-blocks of a row
+  const int ipc = kc >> 3;           // super-blocks per chunk
+  const int nchunk = CH ? (nsb + ipc - 1) / ipc : 1;  // CH: several chunks, one round
+  const int tiles = (a.n_rows + 15) >> 4;
+  const int tstride = gridDim.x * TEAMS;
+  const int tile0 = (int)blockIdx.x * TEAMS + team;
+  // rounds of the workgroup (barriers) and of this team (its tiles)
+  const int rounds_wg = (tiles - (int)blockIdx.x * TEAMS + tstride - 1) / tstride;
+  const int rounds_tm = tile0 < tiles ? (tiles - tile0 + tstride - 1) / tstride : 0;
+  const int n_it = nsb > kw ? (nsb - kw + KS - 1) / KS : 0;  // super-blocks per tile
+
+  uint8_t* xl = s_mem;
+  const int zoff = kc * BS;  // 16 zero bytes
+  float* dl = reinterpret_cast<float*>(s_mem + zoff + 16);
+  float* sl = dl + kc * TMP;
+  float* red = sl + (Q4K ? kc * TMP : 0);
+  if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(s_mem + zoff)[threadIdx.x] = 0u;
+  const float* gd = reinterpret_cast<const float*>(a.xq + a.off_d);
+  const int32_t* gs = reinterpret_cast<const int32_t*>(a.xq + a.off_s);
+
+  // Lane coordinates.  A row m = lane & 15 stands for block jA of the MFMA
+  // and token tA of the group; its slots in K group s carry data only where
+  // lane group s holds block jA's weights (vA).  The lane's results
+  // D[4s + r][n] are for tokens oTok + r of the group and, for MFMA mu, block
+  // oBlk + mu * dB of the span.  aLane / oLane: the lane's LDS byte offsets
+  // of its A slots and of its activation scales for the span's first block,
+  // token group 0 and mu = 0; aMu / oMu: the step for mu = 1.
+  const int m = lane & 15;
+  const int jA = P2 ? (m >> 3) : (m >> 2);
+  const int tA = P2 ? (m & 7) : (m & 3);
+  const bool vA = P2 ? (jA == (s >> 1)) : (jA == s);
+  constexpr int aMu = P2 ? BS : 16;
+  constexpr int oMu = P2 ? TMP * 4 : 0;
+  const int aLane = (P2 ? 2 * jA : jA) * BS + tA * 32 + (P2 ? 16 * (s & 1) : 0);
+  const int oTok = P2 ? 4 * (s & 1) : 0;
+  const int oLane = (P2 ? 2 * (s >> 1) : s) * TMP * 4 + oTok * 4;
+
+  // Staging of chunk c: quants and scales.  stage_issue loads the first SB
+  // pieces of each thread (the caller may queue weight loads behind them);
+  // stage_store stores them and moves the rest.
+  u32x4 sv[SB];
+  auto piece = [&](int c, int idx, const FastDiv& dq) -> const uint8_t* {
+    const int t = dq.div(idx), pc = idx - t * (int)dq.d;
+    return a.xq + (uint32_t)(min(t, T - 1) * a.k + 32 * (c * kc) + 16 * pc);
+  };
+  auto stage_issue = [&](int c) {
+    const int nq = 2 * min(kc, units - c * kc), total = TMP * nq;
+    const FastDiv dq(nq);
+#pragma unroll
+    for (int i = 0; i < SB; ++i) sv[i] = ld16(piece(c, min((int)threadIdx.x + i * NT, total - 1), dq));
+  };
+  auto stage_store = [&](int c) {
+    const int c0 = c * kc, cu = min(kc, units - c0);
+    const int nq = 2 * cu, total = TMP * nq;
+    const FastDiv dq(nq);
+    auto put = [&](int idx, const u32x4& v) {
+      const int t = dq.div(idx), pc = idx - t * nq;
+      *reinterpret_cast<u32x4a*>(xl + (pc >> 1) * BS + t * 32 + 16 * (pc & 1)) = v;
+    };
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const int idx = (int)threadIdx.x + i * NT;
+      if (idx < total) put(idx, sv[i]);
+    }
+    for (int base = SB * NT; base < total; base += SB * NT) {
+      u32x4 v[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) v[i] = ld16(piece(c, min(base + (int)threadIdx.x + i * NT, total - 1), dq));
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int idx = base + (int)threadIdx.x + i * NT;
+        if (idx < total) put(idx, v[i]);
+      }
+    }
+    for (int base = 0; base < kc * TMP; base += 4 * NT) {
+      float dv[4];
+      int iv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + (int)threadIdx.x + i * NT;
+        const int b = idx / TMP, t = idx - b * TMP;  // TMP is a power of two
+        const int gi = min(t, T - 1) * a.nb + c0 + min(b, cu - 1);
+        dv[i] = gd[gi];
+        iv[i] = gs[gi];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base + (int)threadIdx.x + i * NT;
+        const bool ok = idx / TMP < cu;
+        if (idx < kc * TMP) {
+          dl[idx] = ok ? dv[i] : 0.f;
+          if constexpr (Q4K) sl[idx] = ok ? dv[i] * static_cast<float>(iv[i]) : 0.f;
+        }
+      }
+    }
+  };
+
+  // the wave's items (round i, super-block j of the tile), loaded PF ahead;
+  // items past the end re-load the last one
+  int hi = 0, hj = 0;  // next item to load
+  auto load_next = [&](MxRaw<F>& r) {
+    const int tile = min(tile0 + min(hi, max(rounds_tm - 1, 0)) * tstride, tiles - 1);
+    const uint8_t* base = a.w + (int64_t)tile * 16 * a.row_bytes;
+    const uint32_t off = (uint32_t)(min(n, a.n_rows - 1 - tile * 16) * (int)a.row_bytes);
+    mx_load(base, off, 8 * min(kw + hj * KS, nsb - 1), s, units, r);
+    if (++hj >= n_it) {
+      hj = 0;
+      ++hi;
+    }
+  };
+
+  float acc[NG][4];
+  // A operands: zero in the lanes that carry no data, which never load them
+  u32x4 A[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+
+  // One super-block of one row tile: the two spans' MFMAs and scale steps.
+  auto compute = [&](const MxRaw<F>& cur, int sb, int c) {
+    const int u0 = 8 * sb;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p > 0) __builtin_amdgcn_sched_barrier(0);  // spans one after the other
+      MxDec dec;
+      mx_decode(cur, p, s, u0, units, dec);
+      const int bl = 8 * (sb - c * ipc) + 4 * p;  // chunk-local first block of the span
+      const int ab = (vA ? bl * BS + aLane : zoff);
+      const int ob = bl * TMP * 4 + oLane;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g > 0) __builtin_amdgcn_sched_barrier(0);
+        if (vA) {
+          A[0] = ld16(xl + ab + g * TG * 32);
+          A[1] = ld16(xl + ab + g * TG * 32 + aMu);
+        }
+        if constexpr (P2) {
+#pragma unroll
+          for (int mu = 0; mu < 2; ++mu) {
+            const i32x4 dv = mfma64(A[mu], dec.b[mu], i32x4{0, 0, 0, 0});
+            const int o = ob + mu * oMu + g * TG * 4;
+            const f32x4 fx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(dl) + o);
+            const float fxa[4] = {fx.x, fx.y, fx.z, fx.w};
+            if constexpr (Q4K) {
+              const f32x4 fs = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(sl) + o);
+              const float fsa[4] = {fs.x, fs.y, fs.z, fs.w};
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[mu] * fxa[r], acc[g][r]);
+                acc[g][r] = fmaf(-dec.wm[mu], fsa[r], acc[g][r]);
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[mu] * fxa[r], acc[g][r]);
+            }
+          }
+        } else {
+          i32x4 dv = mfma64(A[0], dec.b[0], i32x4{0, 0, 0, 0});
+          dv = mfma64(A[1], dec.b[1], dv);
+          const f32x4 fx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(dl) + ob + g * TG * 4);
+          const float fxa[4] = {fx.x, fx.y, fx.z, fx.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[0] * fxa[r], acc[g][r]);
+        }
+      }
+    }
+  };
+
+  // Ring of PF loaded super-blocks: item q of the wave sits in slot q % PF
+  // (relative to the rotation at chunk and round ends); each slot is reloaded
+  // with the item PF ahead right after it has been computed.
+  MxRaw<F> ring[PF];
+  stage_issue(0);
+#pragma unroll
+  for (int k = 0; k < PF; ++k) load_next(ring[k]);
+  stage_store(0);
+  __syncthreads();
+
+  for (int i = 0; i < rounds_wg; ++i) {
+    const int tile = tile0 + i * tstride;
+    const bool have = i < rounds_tm;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[g][r] = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      if (CH && (c > 0 || i > 0)) {  // several chunks: restage
+        __syncthreads();  // every wave is done with the previous chunk
+        stage_issue(c);
+        stage_store(c);
+        __syncthreads();
+      }
+      const int sb0 = c * ipc + kw;
+      const int sb_end = min((c + 1) * ipc, nsb);
+      const int njc = have && sb0 < sb_end ? (sb_end - sb0 + KS - 1) / KS : 0;
+      for (int j0 = 0; j0 < njc; j0 += PF) {
+#pragma unroll
+        for (int kk = 0; kk < PF; ++kk) {
+          if (j0 + kk < njc) {
+            compute(ring[kk], sb0 + (j0 + kk) * KS, c);
+            load_next(ring[kk]);
+          }
+        }
+      }
+      // the wave's next item sits in slot njc % PF: rotate it to slot 0
+      for (int x = njc % PF; x > 0; --x) {
+        const MxRaw<F> t0 = ring[0];
+#pragma unroll
+        for (int k = 0; k + 1 < PF; ++k) ring[k] = ring[k + 1];
+        ring[PF - 1] = t0;
+      }
+    }
+
+    // Sum over the lanes that hold the other blocks of the same row and
+    // tokens (two blocks per MFMA: lane ^ 32; Q8_0: lanes ^ 16, ^ 32).  Then
+    // with two blocks per MFMA lanes s = 0, 1 hold tokens 8g + 4s + r; Q8_0:
+    // every lane holds tokens 4g + r and lane group s stores group g = s.
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = acc[g][r];
+        if constexpr (!P2) v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        acc[g][r] = v;
+      }
+    if constexpr (KS == 1) {
+      const int row = tile * 16 + n;
+      if (have && row < a.n_rows) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = P2 ? g * 8 + 4 * s + r : g * 4 + r;
+            const bool mine = P2 ? s < 2 : s == (g & 3);
+            if (mine && t < T) a.y[(int64_t)t * a.ldy + row] = acc[g][r];
+          }
+      }
+    } else {
+      // team partials through LDS: red[team][kw][TMP][16], summed in wave order
+      float* mine_red = red + ((team * KS + kw) * TMP) * 16;
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = P2 ? g * 8 + 4 * s + r : g * 4 + r;
+          const bool mine = P2 ? s < 2 : s == (g & 3);
+          if (mine) mine_red[t * 16 + n] = acc[g][r];
+        }
+      __syncthreads();
+      for (int q = threadIdx.x; q < TEAMS * TMP * 16; q += NT) {
+        const int tm = q / (TMP * 16), rest = q - tm * (TMP * 16);
+        const int t = rest >> 4, nn = rest & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < KS; ++w) sum += red[((tm * KS + w) * TMP) * 16 + rest];
+        const int tl = (int)blockIdx.x * TEAMS + tm + i * tstride;  // that team's tile
+        const int row = tl * 16 + nn;
+        if (tl < tiles && t < T && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = sum;
+      }
+      __syncthreads();  // the partials area is reused by the next round
+    }
+  }
+}
+
+// Units (32-blocks) per LDS chunk: a multiple of `step` (whole super-blocks,
+// an equal share for every wave of a team), as many as the budget allows,
+// balanced over the chunks a row needs.
+static int mx_chunk_units(int units, int per_unit, int step, int64_t budget) {
+  int kmax = (int)(budget / per_unit) / step * step;
+  if (kmax < step) return 0;
+  const int need = (units + step - 1) / step * step;
+  if (kmax >= need) return need;
+  const int chunks = (units + kmax - 1) / kmax;
+  const int per = (units + chunks - 1) / chunks;
+  return (per + step - 1) / step * step;
+}
+
+// LDS budget of one k_mx workgroup: the whole activation buffer when it fits
+// in 144 KB (then one workgroup per compute unit stages it once and walks
+// its row tiles), else chunks.
+constexpr int64_t kMxLdsBudget = 144 * 1024;
+
+template <int F, int TM, int WPB, int KS, int PF>
+static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
+  constexpr int TG = mx_tg<F>();
+  constexpr int TMP = ((TM + TG - 1) / TG) * TG;
+  constexpr int TEAMS = WPB / KS;
+  StreamArgs sa{};
+  sa.w = a.w;
+  sa.row_bytes = a.row_bytes;
+  sa.n_rows = a.n_rows;
+  sa.units = a.units;
+  sa.xq = a.xq;
+  sa.act_bytes = (int)a.act_bytes;
+  sa.off_d = (int)a.off_d;
+  sa.off_s = (int)a.off_s;
+  sa.k = a.x.k;
+  sa.nb = a.x.nb;
+  sa.n_tok = a.n_tok;
+  sa.y = a.y;
+  sa.ldy = a.ldy;
+  const int64_t fixed = 16 + (KS > 1 ? (int64_t)WPB * TMP * 16 * 4 : 0);
+  const int per_unit = (TMP * 32 + 16) + TMP * 4 * (F == FQ4_K ? 2 : 1);
+  sa.kc = mx_chunk_units(a.units, per_unit, 8 * KS, kMxLdsBudget - fixed);
+  if (sa.kc <= 0) return hipErrorInvalidValue;
+  const size_t lds = (size_t)sa.kc * per_unit + fixed;
+  const int64_t tiles = (a.n_rows + 15) / 16;
+  const int64_t need = (tiles + TEAMS - 1) / TEAMS;
+  if (sa.kc >= a.units) {
+    // one K chunk: persistent, as many workgroups as fit at once
+    const int64_t per_cu = (int64_t)a.lds_per_cu / (int64_t)lds;
+    const int64_t cap = (int64_t)a.cus * (per_cu < 1 ? 1 : per_cu);
+    const int64_t grid = need < cap ? need : cap;
+    hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false>), dim3((unsigned)grid), dim3(64 * WPB), lds, st, sa);
+  } else {
+    // several chunks: one row tile per team, the chunks walked once
+    hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, true>), dim3((unsigned)need), dim3(64 * WPB), lds, st, sa);
+  }
+  return hipGetLastError();
+}
+
+// variant fields: wpb = waves per workgroup, ks = waves splitting K, nu =
+// super-blocks in the load ring
+template <int F, int TM>
+static hipError_t run_mx_shape(const MatvecLaunch& a, const Variant& v, hipStream_t st) {
+  if (v.wpb == 16 && v.nu == 2) {
+    switch (v.ks) {
+      case 4: return run_mx<F, TM, 16, 4, 2>(a, st);
+      case 8: return run_mx<F, TM, 16, 8, 2>(a, st);
+      case 16: return run_mx<F, TM, 16, 16, 2>(a, st);
+    }
+  } else if (v.wpb == 8 && v.nu == 4) {
+    switch (v.ks) {
+      case 1: return run_mx<F, TM, 8, 1, 4>(a, st);
+      case 4: return run_mx<F, TM, 8, 4, 4>(a, st);
+      case 8: return run_mx<F, TM, 8, 8, 4>(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int F>
+static hipError_t run_mx_tokens(const MatvecLaunch& a, const Variant& v, hipStream_t st) {
+  if (a.n_tok <= 4) return run_mx_shape<F, 4>(a, v, st);
+  if (a.n_tok <= 8) return run_mx_shape<F, 8>(a, v, st);
+  return run_mx_shape<F, 16>(a, v, st);
+}
+
+hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st) {
+  const Variant& v = kVariants[a.variant];
+  switch (a.fmt) {
+    case FQ8_0: return run_mx_tokens<FQ8_0>(a, v, st);
+    case FQ4_K: return run_mx_tokens<FQ4_K>(a, v, st);
+    case FIQ4_XS: return run_mx_tokens<FIQ4_XS>(a, v, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qmv
