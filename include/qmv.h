@@ -189,9 +189,12 @@ qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t 
  *               variant whose LDS staging does not fit the device runs the
  *               lane-group kernel instead (qmv_pick_variant reports which);
  *   "bpc"     : 0 automatic (default), else a cap on resident workgroups
- *               per compute unit for the persistent streaming kernel.
- * The environment variables QMV_SPLITK and QMV_VARIANT set the same switches
- * when the library loads.  Returns QMV_ERR_INVALID_ARG for an unknown key or
+ *               per compute unit for the persistent streaming kernel;
+ *   "moe_kernel": 0 automatic (default), 1 the vector-ALU expert-grouped
+ *               kernel, 2 the matrix-core one (which falls back to the
+ *               vector-ALU kernel when its staged rows do not fit in LDS).
+ * The environment variables QMV_SPLITK, QMV_VARIANT and QMV_MOE_KERNEL set
+ * the same switches when the library loads.  Returns QMV_ERR_INVALID_ARG for an unknown key or
  * value.
  */
 qmv_status qmv_set_tuning(const char* key, int64_t value);

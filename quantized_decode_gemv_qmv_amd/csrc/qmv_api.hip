@@ -30,6 +30,10 @@ struct EnvInit {
       else g_splitk = std::atoll(v);
     }
     if (const char* v = std::getenv("QMV_VARIANT")) g_variant = std::atoll(v);
+    if (const char* v = std::getenv("QMV_MOE_KERNEL")) {
+      const int k = std::atoi(v);
+      if (k >= 0 && k <= 2) set_moe_kernel(k);
+    }
   }
 } g_env_init;
 
@@ -249,6 +253,11 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "bpc")) {
     if (value < 0 || value > 64) return QMV_ERR_INVALID_ARG;
     set_blocks_per_cu(static_cast<int>(value));
+    return QMV_OK;
+  }
+  if (!std::strcmp(key, "moe_kernel")) {
+    if (value < 0 || value > 2) return QMV_ERR_INVALID_ARG;
+    set_moe_kernel(static_cast<int>(value));
     return QMV_OK;
   }
   if (!std::strcmp(key, "variant")) {

@@ -130,5 +130,7 @@ struct MoeLaunch {
 };
 
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t st);
+// Tuning: MoE kernel (0 automatic, 1 vector-ALU, 2 matrix-core).
+void set_moe_kernel(int v);
 
 }  // namespace qmv

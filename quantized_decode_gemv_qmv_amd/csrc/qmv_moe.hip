@@ -31,33 +31,27 @@
 // device-wide fence.
 #include "qmv_device.h"
 #include "qmv_internal.h"
+#include "qmv_mfma.h"
 
 namespace qmv {
 
 constexpr int kMaxSlots = 64 * 16;
 constexpr int kMaxExperts = 1024;
 
-template <int F, int LPR, int NU, int WPB, bool WHOLE>
-__global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
-  constexpr int GPW = 64 / LPR;
-  constexpr int RWG = WPB * GPW;  // rows per tile (one per lane group)
-  constexpr int NT = 64 * WPB;
-  // staged slot rows; during the sort the same bytes hold the ids
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_act[];
-  int* s_id = reinterpret_cast<int*>(s_act);  // ids, -1 for dropped slots
-  __shared__ int s_cnt[kMaxExperts];   // slots per expert, then running offsets
-  __shared__ int s_slot[kMaxSlots];    // slots grouped by expert
-  __shared__ int s_exp[kMaxExperts];   // active experts in id order
-  __shared__ int s_beg[kMaxExperts + 1];  // their first entry in s_slot
-  __shared__ int s_U, s_drop;
-
+// Routing in LDS, built by every workgroup of a MoE kernel from the ids (a
+// counting sort of the slots by expert): s_exp[0..U) the active experts in id
+// order, s_slot[s_beg[r]..s_beg[r+1]) the slots routed to the r-th of them.
+// Dropped slots (ids outside [0, E)) are counted; workgroup 0 reports the
+// count in the workspace and, with one output row per slot, the other
+// workgroups zero those rows.  s_id needs kMaxSlots ints of scratch.
+template <int NT>
+__device__ void moe_route(const MoeLaunch& a, int* s_id, int* s_cnt, int* s_slot, int* s_exp, int* s_beg,
+                          int* s_U, int* s_drop) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_slots = a.n_tok * a.top_k;
   const int E = a.n_experts;
-
-  // ---- 1. counting sort of the slots by expert
   for (int e = tid; e < E; e += NT) s_cnt[e] = 0;
-  if (tid == 0) s_drop = 0;
+  if (tid == 0) *s_drop = 0;
   __syncthreads();
   for (int i = tid; i < n_slots; i += NT) {
     const int e = a.ids[i];
@@ -66,7 +60,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
     if (ok)
       atomicAdd(&s_cnt[e], 1);
     else
-      atomicAdd(&s_drop, 1);
+      atomicAdd(s_drop, 1);
   }
   __syncthreads();
   if (wave == 0) {
@@ -100,7 +94,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
       off += c;
     }
     if (lane == 63) {
-      s_U = iact;
+      *s_U = iact;
       s_beg[iact] = isum;
     }
   }
@@ -110,18 +104,32 @@ __global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
     if (e >= 0) s_slot[atomicAdd(&s_cnt[e], 1)] = i;  // order inside an expert is free
   }
   __syncthreads();
-  const int U = s_U;
-
-  // what no item writes: the dropped-slot count, and with one output per
-  // slot the zero rows of dropped slots
-  if (blockIdx.x == 0 && tid == 0) a.err[0] = s_drop;
-  if (s_drop > 0 && a.rw == nullptr) {
+  if (blockIdx.x == 0 && tid == 0) a.err[0] = *s_drop;
+  if (*s_drop > 0 && a.rw == nullptr) {
     for (int i = 0; i < n_slots; ++i)
       if (s_id[i] < 0)
         for (int r = blockIdx.x * NT + tid; r < a.n_rows; r += gridDim.x * NT)
           a.y[(int64_t)i * a.n_rows + r] = 0.f;
   }
-  __syncthreads();  // the ids are dead: their bytes take staged rows next
+  __syncthreads();  // s_id is dead from here on
+}
+
+template <int F, int LPR, int NU, int WPB, bool WHOLE>
+__global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
+  constexpr int GPW = 64 / LPR;
+  constexpr int RWG = WPB * GPW;  // rows per tile (one per lane group)
+  constexpr int NT = 64 * WPB;
+  // staged slot rows; during the sort the same bytes hold the ids
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_act[];
+  __shared__ int s_cnt[kMaxExperts];      // slots per expert, then running offsets
+  __shared__ int s_slot[kMaxSlots];       // slots grouped by expert
+  __shared__ int s_exp[kMaxExperts];      // active experts in id order
+  __shared__ int s_beg[kMaxExperts + 1];  // their first entry in s_slot
+  __shared__ int s_U, s_drop;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  moe_route<NT>(a, reinterpret_cast<int*>(s_act), s_cnt, s_slot, s_exp, s_beg, &s_U, &s_drop);
+  const int U = s_U;
 
   // ---- 2. work items: (active expert, chunk of rows)
   const int tiles = (a.n_rows + RWG - 1) / RWG;
@@ -234,6 +242,213 @@ __global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
   }
 }
 
+// Expert-grouped matrix-core kernel, for calls where experts receive several
+// slots (the 16-64 token batches).  The dense matrix-core kernel's tile -- 16
+// weight rows, one v_mfma_i32_16x16x64_i8 per token group and 64-wide slice
+// of K, the per-32-block dots kept apart by zero-masked activation rows (see
+// qmv_mfma.hip) -- with the activation rows of an expert's slots as its
+// tokens.  Work items are (active expert, chunk of row tiles), walked with
+// stride gridDim.x after the routing sort; per item the workgroup stages up
+// to TMP of the expert's slot rows (block-major, the whole K) in LDS, and its
+// waves walk the chunk's tiles, each tile over the whole K with the next
+// super-block's weights in flight.  More slots than TMP go in further groups,
+// each reading the expert's rows again.
+template <int F, int TM, int WPB>
+__global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
+  constexpr int TG = mx_tg<F>();
+  constexpr int NG = (TM + TG - 1) / TG;  // token groups
+  constexpr int TMP = NG * TG;            // staged slot rows
+  constexpr int NT = 64 * WPB;
+  constexpr bool Q4K = F == FQ4_K;
+  constexpr bool P2 = Q4K;  // two blocks per MFMA (q4_K), else four
+  constexpr int BS = TMP * 32 + 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_act[];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_slot[kMaxSlots];
+  __shared__ int s_exp[kMaxExperts];
+  __shared__ int s_beg[kMaxExperts + 1];
+  __shared__ int s_U, s_drop;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  moe_route<NT>(a, reinterpret_cast<int*>(s_act), s_cnt, s_slot, s_exp, s_beg, &s_U, &s_drop);
+  const int U = s_U;
+
+  const int n = lane & 15, s = lane >> 4;
+  const int units = a.units, nb = a.x.nb, K = a.x.k;
+  const int nsb = (units + 7) >> 3;
+  const int kb = 8 * nsb;  // staged blocks
+  uint8_t* xl = s_act;
+  const int zoff = kb * BS;
+  float* dl = reinterpret_cast<float*>(s_act + zoff + 16);
+  float* sl = dl + kb * TMP;
+  if (tid < 4) reinterpret_cast<uint32_t*>(s_act + zoff)[tid] = 0u;
+
+  // lane coordinates, as in the dense kernel
+  const int m = lane & 15;
+  const int jA = P2 ? (m >> 3) : (m >> 2);
+  const int tA = P2 ? (m & 7) : (m & 3);
+  const bool vA = P2 ? (jA == (s >> 1)) : (jA == s);
+  constexpr int aMu = P2 ? BS : 16;
+  constexpr int oMu = P2 ? TMP * 4 : 0;
+  const int aLane = (P2 ? 2 * jA : jA) * BS + tA * 32 + (P2 ? 16 * (s & 1) : 0);
+  const int oTok = P2 ? 4 * (s & 1) : 0;
+  const int oLane = (P2 ? 2 * (s >> 1) : s) * TMP * 4 + oTok * 4;
+
+  const int tiles = (a.n_rows + 15) >> 4;
+  const int tpc = max(1, (int)(((int64_t)U * tiles + 2 * gridDim.x - 1) / (2 * gridDim.x)));
+  const int chunks = (tiles + tpc - 1) / tpc;
+  const int nitems = U * chunks;
+  auto x_row = [&](int i) { return a.x_per_slot ? i : i / a.top_k; };
+  float* out = a.rw == nullptr ? a.y : a.part;
+
+  float acc[NG][4];
+  u32x4 A[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int rank = item / chunks;
+    const int e = s_exp[rank];
+    const int b0 = s_beg[rank], n_e = s_beg[rank + 1] - b0;
+    const int t0 = (item - rank * chunks) * tpc, t1 = min(t0 + tpc, tiles);
+    const uint8_t* we = a.w + (int64_t)e * a.n_rows * a.row_bytes;
+    for (int g0 = 0; g0 < n_e; g0 += TMP) {
+      const int ng = min(TMP, n_e - g0);
+      const int ngr = (ng + TG - 1) / TG;  // token groups with a slot
+      __syncthreads();  // the previous group's rows are no longer read
+      {
+        // stage the group's slot rows: quants block-major, scales zero past
+        // ng; loads go out four per thread before their stores
+        const int pr = K >> 4;  // 16-byte pieces per row
+        const FastDiv dp(pr);
+        for (int base = 0; base < TMP * pr; base += 4 * NT) {
+          u32x4 v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = min(base + tid + q * NT, TMP * pr - 1);
+            const int j = dp.div(idx), pc = idx - j * pr;
+            const int xr = x_row(s_slot[b0 + g0 + min(j, ng - 1)]);
+            v[q] = ld16(a.x.qs + (int64_t)xr * K + 16 * pc);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = base + tid + q * NT;
+            const int j = dp.div(idx), pc = idx - j * pr;
+            if (idx < TMP * pr) *reinterpret_cast<u32x4a*>(xl + (pc >> 1) * BS + j * 32 + 16 * (pc & 1)) = v[q];
+          }
+        }
+        for (int base = 0; base < kb * TMP; base += 4 * NT) {
+          float dv[4];
+          int iv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = base + tid + q * NT;
+            const int b = idx / TMP, j = idx - b * TMP;  // TMP is a power of two
+            const int xr = x_row(s_slot[b0 + g0 + min(j, ng - 1)]);
+            const int64_t gi = (int64_t)xr * nb + min(b, nb - 1);
+            dv[q] = a.x.d[gi];
+            iv[q] = a.x.s[gi];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = base + tid + q * NT;
+            const int b = idx / TMP, j = idx - b * TMP;
+            const bool ok = j < ng && b < nb;
+            if (idx < kb * TMP) {
+              dl[idx] = ok ? dv[q] : 0.f;
+              if constexpr (Q4K) sl[idx] = ok ? dv[q] * static_cast<float>(iv[q]) : 0.f;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // the wave's tiles of the chunk, each over all of K, next load in flight
+      int lt = t0 + wave, lsb = 0;  // next (tile, super-block) to load
+      auto load_next = [&](MxRaw<F>& r) {
+        const int t = min(lt, t1 - 1);
+        const uint8_t* base = we + (int64_t)t * 16 * a.row_bytes;
+        const uint32_t off = (uint32_t)(min(n, a.n_rows - 1 - t * 16) * (int)a.row_bytes);
+        mx_load(base, off, 8 * lsb, s, units, r);
+        if (++lsb >= nsb) {
+          lsb = 0;
+          lt += WPB;
+        }
+      };
+      if (t0 + wave >= t1) continue;
+      MxRaw<F> cur;
+      load_next(cur);
+      for (int t = t0 + wave; t < t1; t += WPB) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[g][r] = 0.f;
+        for (int sb = 0; sb < nsb; ++sb) {
+          MxRaw<F> nxt;
+          load_next(nxt);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            if (p > 0) __builtin_amdgcn_sched_barrier(0);
+            MxDec dec;
+            mx_decode(cur, p, s, 8 * sb, units, dec);
+            const int bl = 8 * sb + 4 * p;
+            const int ab = vA ? bl * BS + aLane : zoff;
+            const int ob = bl * TMP * 4 + oLane;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+              if (g >= ngr) break;
+              if (g > 0) __builtin_amdgcn_sched_barrier(0);
+              if (vA) {
+                A[0] = ld16(xl + ab + g * TG * 32);
+                A[1] = ld16(xl + ab + g * TG * 32 + aMu);
+              }
+              if constexpr (P2) {
+#pragma unroll
+                for (int mu = 0; mu < 2; ++mu) {
+                  const i32x4 dv = mfma64(A[mu], dec.b[mu], i32x4{0, 0, 0, 0});
+                  const int o = ob + mu * oMu + g * TG * 4;
+                  const f32x4 fx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(dl) + o);
+                  const f32x4 fs = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(sl) + o);
+                  const float fxa[4] = {fx.x, fx.y, fx.z, fx.w}, fsa[4] = {fs.x, fs.y, fs.z, fs.w};
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) {
+                    acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[mu] * fxa[r], acc[g][r]);
+                    acc[g][r] = fmaf(-dec.wm[mu], fsa[r], acc[g][r]);
+                  }
+                }
+              } else {
+                i32x4 dv = mfma64(A[0], dec.b[0], i32x4{0, 0, 0, 0});
+                dv = mfma64(A[1], dec.b[1], dv);
+                const f32x4 fx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(dl) + ob + g * TG * 4);
+                const float fxa[4] = {fx.x, fx.y, fx.z, fx.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[0] * fxa[r], acc[g][r]);
+              }
+            }
+          }
+          cur = nxt;
+        }
+        // lanes holding the other blocks of the same row and slots, then the
+        // slot outputs (see the dense kernel for the lane layout)
+        const int row = t * 16 + n;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (g >= ngr) break;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = acc[g][r];
+            if constexpr (!P2) v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            const int j = P2 ? g * 8 + 4 * s + r : g * 4 + r;
+            const bool mine = P2 ? s < 2 : s == (g & 3);
+            if (mine && j < ng && row < a.n_rows) out[(int64_t)s_slot[b0 + g0 + j] * a.n_rows + row] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
 // y[t][n] = sum over valid slots s, in slot order, of rw[t][s] * part[t*top_k+s][n].
 __global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -341,11 +556,70 @@ static hipError_t run_moe_fmt(const MoeLaunch& a, hipStream_t st) {
   }
 }
 
+// Matrix-core launch: TM staged slot rows per group (TMP after rounding to
+// token groups), 8-wave workgroups, a persistent grid sized by occupancy.
+template <int F, int TM>
+static hipError_t run_moe_mx(const MoeLaunch& a0, hipStream_t st) {
+  constexpr int WPB = 8;
+  constexpr int TG = mx_tg<F>();
+  constexpr int TMP = ((TM + TG - 1) / TG) * TG;
+  MoeLaunch a = a0;
+  auto kern = k_moe_mx<F, TM, WPB>;
+  const int64_t kb = 8 * (int64_t)((a.units + 7) / 8);
+  size_t lds = (size_t)(kb * (TMP * 32 + 16) + 16 + kb * TMP * 4 * (F == FQ4_K ? 2 : 1));
+  if (lds < (size_t)kMaxSlots * 4) lds = (size_t)kMaxSlots * 4;  // the ids during the sort
+  struct Occ {
+    int regs;
+    size_t static_lds;
+  };
+  static const Occ occ0 = [&] {
+    Occ o{1, 0};
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * WPB, 0) == hipSuccess && n > 0) o.regs = n;
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) == hipSuccess)
+      o.static_lds = fa.sharedSizeBytes;
+    return o;
+  }();
+  if (occ0.static_lds + lds > (size_t)a.lds_per_cu) return hipErrorInvalidValue;
+  int occ = occ0.regs;
+  const int by_lds = (int)((size_t)a.lds_per_cu / (occ0.static_lds + lds));
+  if (occ > by_lds) occ = by_lds;
+  if (occ < 1) occ = 1;
+  const int64_t slots = (int64_t)a.n_tok * a.top_k;
+  const int64_t tiles = (a.n_rows + 15) / 16;
+  const int64_t max_items = (slots < a.n_experts ? slots : a.n_experts) * tiles;
+  const int64_t cap = (int64_t)a.cus * occ;
+  const unsigned grid = (unsigned)(max_items < cap ? max_items : cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.rw == nullptr) return e;
+  const int64_t outs = (int64_t)a.n_tok * a.n_rows;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+static int g_moe_kernel = 0;  // tuning: 0 automatic, 1 vector-ALU kernel, 2 matrix-core kernel
+void set_moe_kernel(int v) { g_moe_kernel = v; }
+
+// The matrix-core kernel when experts receive several slots (from 16
+// tokens, top-8 of 128 experts: about one slot per active expert at 16
+// tokens, four at 64), with 4 (8 from 17 tokens) slot rows per group.
+template <int F>
+static hipError_t run_moe_any(const MoeLaunch& a, hipStream_t st) {
+  const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && a.n_tok >= 16);
+  if (mx) {
+    const hipError_t e = a.n_tok <= 16 ? run_moe_mx<F, 4>(a, st) : run_moe_mx<F, 8>(a, st);
+    if (e != hipErrorInvalidValue) return e;  // else the staged rows do not fit: vector kernel
+  }
+  return run_moe_fmt<F>(a, st);
+}
+
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t st) {
   switch (a.fmt) {
-    case FQ8_0: return run_moe_fmt<FQ8_0>(a, st);
-    case FQ4_K: return run_moe_fmt<FQ4_K>(a, st);
-    case FIQ4_XS: return run_moe_fmt<FIQ4_XS>(a, st);
+    case FQ8_0: return run_moe_any<FQ8_0>(a, st);
+    case FQ4_K: return run_moe_any<FQ4_K>(a, st);
+    case FIQ4_XS: return run_moe_any<FIQ4_XS>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

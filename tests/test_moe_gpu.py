@@ -37,20 +37,29 @@ def _rows_of_experts(w_dev, n_rows, rows):
     return v.index_select(1, idx).contiguous().cpu().numpy()
 
 
+@pytest.fixture(params=[1, 2], ids=["vector", "matrix"])
+def moe_kernel(request):
+    """Run a test with the vector-ALU and with the matrix-core MoE kernel."""
+    qmv = need_gpu()
+    qmv.set_tuning("moe_kernel", request.param)
+    yield request.param
+    qmv.set_tuning("moe_kernel", 0)
+
+
 def _ws(qmv, n_rows, k, t):
     return torch.zeros(qmv.moe_workspace_bytes(synth.IQ4_XS, E, n_rows, k, t, TOP_K),
                        dtype=torch.uint8, device="cuda")
 
 
 @pytest.mark.parametrize("t", [1, 6, 16, 64])
-def test_moe_workload(experts, t):
+def test_moe_workload(experts, t, moe_kernel):
     qmv = need_gpu()
     gu, dn = experts
     ids, rw = synth.make_routing(t, E, TOP_K, f"{NAME}/route")
     ids_d, rw_d = to_dev(ids), to_dev(rw)
 
     # gate+up: x per token, one output per slot
-    say(f"MoE gate_up T={t}")
+    say(f"MoE gate_up T={t} kernel={moe_kernel}")
     n, k = GU
     x = x_host(t, k, f"{NAME}/x")
     xq = quantize(qmv, x)
@@ -99,12 +108,12 @@ CASES = {
 @pytest.mark.parametrize("case", sorted(CASES))
 @pytest.mark.parametrize("per_slot", [False, True])
 @pytest.mark.parametrize("weighted", [False, True])
-def test_moe_routing_edges(small, case, per_slot, weighted):
+def test_moe_routing_edges(small, case, per_slot, weighted, moe_kernel):
     qmv = need_gpu()
     w, wd = small
     ids = CASES[case]
     t, top_k = ids.shape
-    say(f"MoE edge {case} per_slot={per_slot} weighted={weighted}")
+    say(f"MoE edge {case} per_slot={per_slot} weighted={weighted} kernel={moe_kernel}")
     rw = None
     if weighted:
         rw = synth.normal_f32(synth.stream(f"moe_small/rw/{case}"), 0, t * top_k).reshape(t, top_k)
@@ -143,3 +152,29 @@ def test_moe_matches_dense_calls(small):
                                 qs, d, s)
         assert_y(y[0, s_][None], yr, mag, f"slot {s_}")
         assert_y(yd, yr, mag, f"dense {e}")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K], ids=["q8_0", "q4_K"])
+def test_moe_other_formats(fmt, moe_kernel):
+    """Both MoE kernels on Q8_0 and q4_K experts (K = 512, a hot expert that
+    takes more slots than one staged group, weighted and per-slot calls)."""
+    qmv = need_gpu()
+    e_n, n, k = 5, 48, 512
+    w = synth.make_weights(fmt, e_n * n, k, f"moe_fmt/{fmt}").data
+    wd = to_dev(w)
+    ids = np.array([[1, 3], [3, 0], [3, 4], [2, 3], [3, 1], [0, 3], [3, 2], [4, 3], [3, 0], [1, 3],
+                    [3, 4], [2, 3], [3, 1], [0, 3], [3, 2], [4, 3], [3, 4], [1, 3]], np.int32)
+    t, top_k = ids.shape
+    rw = synth.normal_f32(synth.stream(f"moe_fmt/rw/{fmt}"), 0, t * top_k).reshape(t, top_k)
+    for per_slot, weighted in ((False, False), (True, True)):
+        say(f"MoE fmt {fmt} per_slot={per_slot} weighted={weighted} kernel={moe_kernel}")
+        x = x_host(t * top_k if per_slot else t, k, f"moe_fmt/x/{per_slot}")
+        xq = quantize(qmv, x)
+        ws = torch.zeros(qmv.moe_workspace_bytes(fmt, e_n, n, k, t, top_k), dtype=torch.uint8,
+                         device="cuda")
+        y = qmv.moe_matvec(fmt, wd, e_n, n, k, xq, per_slot, to_dev(ids),
+                           to_dev(rw) if weighted else None, ws)
+        qs, d, s = oracle.quantize_act(x)
+        yr, mag = oracle.moe_matvec(fmt, w, e_n, n, k, qs, d, s, ids, rw if weighted else None,
+                                    per_slot)
+        assert_y(y.cpu().numpy().reshape(yr.shape), yr, mag, f"fmt {fmt} per_slot={per_slot}")
