@@ -48,8 +48,8 @@ WORKLOADS = {
 FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS"}
 # MoE decode: 128 IQ4_XS experts, gate+up 3072 x 4096 and down 4096 x 1536 per
 # expert, top-8 routing
-MOE = dict(name="moe_iq4_xs_e128", experts=128, top_k=8, gate_up=(3072, 4096), down=(4096, 1536),
-           tokens=(1, 6, 16, 64))
+MOE = dict(name="moe_iq4_xs_e128", ffn_name="moe_ffn_iq4_xs_e128", experts=128, top_k=8,
+           gate_up=(3072, 4096), down=(4096, 1536), tokens=(1, 6, 16, 64))
 KERNEL_SOURCES = ("qmv_device.h", "qmv_matvec.hip", "qmv_mfma.hip", "qmv_quant.hip", "qmv_api.hip")
 
 
@@ -165,6 +165,15 @@ class MoeRing:
         qmv.quantize_act(self.h[i % 8], out=self.hq)
         self.down(qmv, i)
 
+    def ffn_step(self, qmv, i):
+        """The MoE FFN: the down projection's input is SwiGLU of the gate+up
+        output, quantized to Q8 in one kernel."""
+        qmv.quantize_act(self.x[i % 8], out=self.xq)
+        self.gate_up(qmv, i)
+        _, ng, _, _, kd = self.shape
+        qmv.swiglu_quantize(self.y_gu.view(self.t * self.top_k, ng), kd, out=self.hq)
+        self.down(qmv, i)
+
 
 def capture(torch, fn, count, start=0):
     s = torch.cuda.Stream()
@@ -220,9 +229,10 @@ def timed_replays(torch, fn, per, reps=10):
     return e0.elapsed_time(e1) * 1e3 / (reps * per)
 
 
-def moe_cpu_baseline(ring, min_seconds=10.0):
+def moe_cpu_baseline(ring, min_seconds=10.0, ffn=False):
     """The CPU oracle on the MoE step for this token count: quantize x and h,
-    gate+up and down routed matvecs over all rows (routing 0)."""
+    gate+up and down routed matvecs over all rows (routing 0); with ffn, h is
+    SwiGLU of the gate+up output."""
     import numpy as np
 
     import oracle
@@ -245,7 +255,9 @@ def moe_cpu_baseline(ring, min_seconds=10.0):
     reps, t0 = 0, time.perf_counter()
     while True:
         qs, d, s = oracle.quantize_act(x)
-        oracle.moe_matvec(2, gu, len(used), ng, kg, qs, d, s, ids2, None, False)
+        y_gu, _ = oracle.moe_matvec(2, gu, len(used), ng, kg, qs, d, s, ids2, None, False)
+        if ffn:
+            h = oracle.swiglu(y_gu.reshape(ring.t * ring.top_k, ng).astype(np.float32), kd).astype(np.float32)
         qs, d, s = oracle.quantize_act(h)
         oracle.moe_matvec(2, dn, len(used), nd, kd, qs, d, s, ids2, rw, True)
         reps += 1
@@ -259,17 +271,17 @@ def moe_cpu_baseline(ring, min_seconds=10.0):
                       f"in {el:.1f} s"}
 
 
-def bench_moe(args, torch, qmv):
+def bench_moe(args, torch, qmv, ffn=False):
     t = args.tokens
-    log(f"bench: MoE T={t}: generating inputs")
+    log(f"bench: MoE{' FFN' if ffn else ''} T={t}: generating inputs")
     ring = MoeRing(torch, qmv, t)
     per = 64
-    g_full = capture(torch, lambda i: ring.step(qmv, i), per)
+    step = (lambda i: ring.ffn_step(qmv, i)) if ffn else (lambda i: ring.step(qmv, i))
+    g_full = capture(torch, step, per)
     tail = args.steps % per
-    g_tail = capture(torch, lambda i: ring.step(qmv, i), tail) if tail else None
+    g_tail = capture(torch, step, tail) if tail else None
     warm_tail = args.warmup % per
-    run_steps(torch, (g_full, per, capture(torch, lambda i: ring.step(qmv, i), warm_tail)
-                      if warm_tail else None), args.warmup)
+    run_steps(torch, (g_full, per, capture(torch, step, warm_tail) if warm_tail else None), args.warmup)
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} MoE steps")
     t0 = time.perf_counter()
@@ -285,7 +297,7 @@ def bench_moe(args, torch, qmv):
     gu_bytes = avg_u * ring.gu[0].numel() / ring.shape[0]
     dn_bytes = avg_u * ring.dn[0].numel() / ring.shape[0]
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    cpu = None if args.no_cpu else moe_cpu_baseline(ring)
+    cpu = None if args.no_cpu else moe_cpu_baseline(ring, ffn=ffn)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -299,10 +311,12 @@ def bench_moe(args, torch, qmv):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"MoE IQ4_XS 128 experts top-8, gate+up 3072x4096 + down 4096x1536, "
-                               f"{t} token(s)", "tokens": t, "avg_distinct_experts": round(avg_u, 2),
-                   "weight_bytes_per_step": round(step_bytes),
-                   "step": "quantize x + gate_up routed matvec + quantize h + down routed matvec"},
+        "config": {"workload": f"MoE{' FFN' if ffn else ''} IQ4_XS 128 experts top-8, gate+up 3072x4096 + "
+                               f"down 4096x1536, {t} token(s)", "tokens": t,
+                   "avg_distinct_experts": round(avg_u, 2), "weight_bytes_per_step": round(step_bytes),
+                   "step": ("quantize x + gate_up routed matvec + SwiGLU and Q8 of its output + down routed "
+                            "matvec" if ffn else
+                            "quantize x + gate_up routed matvec + quantize h + down routed matvec")},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -346,7 +360,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="q4_k_14336x4096", choices=sorted(WORKLOADS) + [MOE["name"]])
+    ap.add_argument("--workload", default="q4_k_14336x4096",
+                    choices=sorted(WORKLOADS) + [MOE["name"], MOE["ffn_name"]])
     ap.add_argument("--tokens", type=int, default=1)
     ap.add_argument("--all-tokens", action="store_true",
                     help="also time the matvec at every token count of the workload")
@@ -368,11 +383,11 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
-    if args.workload == MOE["name"]:
+    if args.workload in (MOE["name"], MOE["ffn_name"]):
         if not 1 <= args.tokens <= 64:
             print("--tokens must be 1..64 for the MoE workload", file=sys.stderr)
             return 2
-        return bench_moe(args, torch, qmv)
+        return bench_moe(args, torch, qmv, ffn=args.workload == MOE["ffn_name"])
     fmt, n, k, token_list = WORKLOADS[args.workload]
     t = args.tokens
     if not 1 <= t <= 16:

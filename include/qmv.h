@@ -107,6 +107,26 @@ qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, int64_t 
                             void* stream);
 
 /*
+ * qmv_swiglu_quantize -- the step between a MoE gate+up and down projection:
+ * SwiGLU of each row, quantized to Q8 blocks for the down projection.
+ * Castagna Veloce page, "Fused operations" (gate/up + SwiGLU kernels for the
+ * verify batches; Q8 activations made once).  For row r:
+ *   g = gu[r][0 .. n_ff-1], u = gu[r][n_ff .. 2 n_ff - 1]  (gate rows first
+ *   in a gate+up tensor, as qmv_moe_matvec produces them per slot),
+ *   h = g / (1 + exp(-g)) * u  in fp32,
+ * then the Q8 blocks of h exactly as qmv_quantize_act makes them.
+ * gu    : fp32 [rows][ldg] (device), 4-byte aligned, ldg >= 2 n_ff, finite.
+ * xq    : activation buffer of qmv_act_bytes(rows, n_ff) bytes (device,
+ *         256-byte aligned); fully overwritten.
+ * h_out : NULL, or fp32 [rows][n_ff] (device, 16-byte aligned) that receives
+ *         the h values the blocks were made from.
+ * 1 <= rows <= QMV_MAX_ACT_ROWS, n_ff > 0, n_ff % 32 == 0.
+ * Asynchronous on `stream`; allocates nothing.
+ */
+qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t rows, int64_t n_ff, void* xq,
+                               float* h_out, void* stream);
+
+/*
  * qmv_matvec -- y[t][n] = sum_k W[n][k] * xq[t][k] for t < n_tok.
  * Castagna Veloce page, "Kernels for the MI50" (small-batch matvecs for 1 to
  * 16 tokens, Q8_0 with a split-K variant); zhuai.tech GLM-5.3 page, "A single

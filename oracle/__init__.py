@@ -49,10 +49,11 @@ def _load():
     lib.oracle_block_dots.argtypes = [I, P, I64, I64, P, P, I64, P]
     lib.oracle_matvec.argtypes = [I, P, I64, I64, P, P, P, I64, P, P]
     lib.oracle_moe_matvec.argtypes = [I, P, I64, I64, I64, P, P, P, I, P, P, I64, I64, P, P]
+    lib.oracle_swiglu.argtypes = [P, I64, I64, I64, P]
     lib.oracle_threads.restype = I
     lib.oracle_set_threads.argtypes = [I]
     for f in ("oracle_unpack", "oracle_dequant", "oracle_quantize_act", "oracle_block_dots",
-              "oracle_matvec", "oracle_moe_matvec"):
+              "oracle_matvec", "oracle_moe_matvec", "oracle_swiglu"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -166,3 +167,14 @@ def moe_matvec(fmt: int, w: np.ndarray, n_experts: int, n_rows: int, k: int, qs,
     _check(_load().oracle_moe_matvec(fmt, _p(w), n_experts, n_rows, k, _p(qs), _p(d), _p(s),
                                      int(bool(x_per_slot)), _p(ids), _p(rw), t, top_k, _p(y), _p(mag)))
     return y, mag
+
+
+def swiglu(gu: np.ndarray, n_ff: int) -> np.ndarray:
+    """gu fp32 [R][>= 2 n_ff] (gate | up) -> h fp64 [R][n_ff] = silu(g) * u."""
+    gu = np.ascontiguousarray(gu, dtype=np.float32)
+    if gu.ndim == 1:
+        gu = gu[None]
+    r, ld = gu.shape
+    h = np.zeros((r, n_ff), dtype=np.float64)
+    _check(_load().oracle_swiglu(_p(gu), ld, r, n_ff, _p(h)))
+    return h

@@ -381,6 +381,27 @@ int oracle_moe_matvec(int fmt, const uint8_t* w, int64_t n_experts, int64_t n_ro
   return 0;
 }
 
+/*
+ * SwiGLU of a gate+up output (Castagna Veloce page, "Fused operations": the
+ * gate/up + SwiGLU fusion of the verify batches).  Row r of gu holds the gate
+ * half in columns 0..n_ff-1 and the up half in n_ff..2n_ff-1 (one gate+up
+ * tensor per expert, gate rows first); h = silu(g) * u with
+ * silu(g) = g / (1 + exp(-g)), in fp64 from the fp32 inputs.  The pages give
+ * no formula; this is the usual SwiGLU.  The h rows are quantized to Q8
+ * activations with oracle_quantize_act by the caller.
+ */
+int oracle_swiglu(const float* gu, int64_t ldg, int64_t rows, int64_t n_ff, double* h) {
+  if (n_ff < 1 || ldg < 2 * n_ff || rows < 0) return 1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < n_ff; ++i) {
+      const double g = gu[r * ldg + i];
+      const double u = gu[r * ldg + n_ff + i];
+      const double e = exp(-g);  /* +inf for very negative g: silu -> -0 */
+      h[r * n_ff + i] = g / (1.0 + e) * u;
+    }
+  return 0;
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

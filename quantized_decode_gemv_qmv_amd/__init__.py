@@ -21,7 +21,7 @@ __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
     "moe_workspace_bytes", "quantize_act", "matvec", "moe_matvec", "block_dots",
-    "set_tuning", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
+    "set_tuning", "swiglu_quantize", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
 Q8_0, Q4_K, IQ4_XS = 0, 1, 2
@@ -72,6 +72,7 @@ def lib():
         "qmv_act_offset_d": ([I64, I64], SZ),
         "qmv_act_offset_s": ([I64, I64], SZ),
         "qmv_quantize_act": ([P, I64, I64, I64, P, P], I),
+        "qmv_swiglu_quantize": ([P, I64, I64, I64, P, P, P], I),
         "qmv_matvec_workspace_bytes": ([I, I64, I64, I64], SZ),
         "qmv_matvec": ([I, P, I64, I64, P, I64, P, I64, P, SZ, P], I),
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
@@ -133,6 +134,24 @@ def act_fields(xq: torch.Tensor, n_tok: int, k: int):
     d = xq[od: od + 4 * n_tok * nb].view(torch.float32).view(n_tok, nb)
     s = xq[os_: os_ + 4 * n_tok * nb].view(torch.int32).view(n_tok, nb)
     return qs, d, s
+
+
+def swiglu_quantize(gu: torch.Tensor, n_ff: int, out: torch.Tensor | None = None,
+                    h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """gu fp32 [R][>= 2 n_ff] (gate | up) -> Q8 activation buffer of
+    h = silu(gate) * up [R][n_ff]; h_out (fp32 [R][n_ff]) receives h."""
+    _need(gu, torch.float32, "gu")
+    if gu.dim() != 2 or gu.stride(1) != 1:
+        raise ValueError("gu must be a 2-D tensor with unit column stride")
+    rows = gu.shape[0]
+    if out is None:
+        out = torch.empty(act_bytes(rows, n_ff), dtype=torch.uint8, device=gu.device)
+    if h_out is not None:
+        _need(h_out, torch.float32, "h_out")
+    ldg = gu.stride(0) if rows > 1 else gu.shape[1]  # a single row's stride is arbitrary
+    _check(lib().qmv_swiglu_quantize(_ptr(gu), ldg, rows, n_ff, _ptr(out), _ptr(h_out),
+                                     _stream(stream)), "qmv_swiglu_quantize")
+    return out
 
 
 def matvec_workspace_bytes(fmt: int, n_rows: int, k: int, n_tok: int) -> int:

@@ -295,6 +295,22 @@ QMV_API qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, 
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 
+QMV_API qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t rows, int64_t n_ff,
+                                       void* xq, float* h_out, void* stream) {
+  if (gu == nullptr || xq == nullptr || rows < 1 || n_ff < 1 || n_ff % 32 || ldg < 2 * n_ff)
+    return QMV_ERR_INVALID_ARG;
+  if (rows > QMV_MAX_ACT_ROWS || n_ff > (int64_t)1 << 24) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(gu, 4) || !aligned(xq, 256) || (h_out != nullptr && !aligned(h_out, 16)))
+    return QMV_ERR_MISALIGNED;
+  uint8_t* b = static_cast<uint8_t*>(xq);
+  hipError_t e = launch_swiglu_quantize(gu, ldg, static_cast<int>(rows), static_cast<int>(n_ff),
+                                        reinterpret_cast<int8_t*>(b),
+                                        reinterpret_cast<float*>(b + qmv_act_offset_d(rows, n_ff)),
+                                        reinterpret_cast<int32_t*>(b + qmv_act_offset_s(rows, n_ff)), h_out,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
 // --------------------------------------------------------------- matvec
 QMV_API size_t qmv_matvec_workspace_bytes(qmv_type type, int64_t n_rows, int64_t k,
                                           int64_t n_tok) {

@@ -101,6 +101,8 @@ void set_blocks_per_cu(int v);
 
 hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
                            int32_t* s, hipStream_t st);
+hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_ff, int8_t* qs, float* d,
+                                  int32_t* s, float* h_out, hipStream_t st);
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,

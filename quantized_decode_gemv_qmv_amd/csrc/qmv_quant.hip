@@ -43,6 +43,55 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t
   return hipGetLastError();
 }
 
+// --------------------------------------------------------- SwiGLU + Q8
+// The step between a gate+up and a down projection (Castagna Veloce page,
+// "Fused operations": gate/up + SwiGLU kernels for the verify batches, and
+// Q8 activations made once): h = silu(g) * u over the gate and up halves of
+// each row of gu, with silu(g) = g / (1 + exp(-g)) in fp32 (accurate expf
+// and IEEE division), then the Q8 activation blocks of h exactly as
+// k_quantize makes them.  Eight lanes per block of 32, four values per lane.
+// h_out (optional) receives the fp32 h the blocks were made from.
+__global__ __launch_bounds__(256) void k_swiglu_quantize(const float* __restrict__ gu, int64_t ldg,
+                                                         int rows, int n_ff, int8_t* __restrict__ qs,
+                                                         float* __restrict__ d, int32_t* __restrict__ s,
+                                                         float* __restrict__ h_out) {
+  const int nb = n_ff / 32;
+  const int64_t total = (int64_t)rows * nb;
+  int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const bool valid = blk < total;
+  if (!valid) blk = total - 1;
+  const int j = threadIdx.x & 7;
+  const int64_t r = blk / nb, b = blk % nb;
+  const float* row = gu + r * ldg + 32 * b + 4 * j;
+  const f32x4 g = *reinterpret_cast<const f32x4*>(row);
+  const f32x4 u = *reinterpret_cast<const f32x4*>(row + n_ff);
+  const float gg[4] = {g.x, g.y, g.z, g.w}, uu[4] = {u.x, u.y, u.z, u.w};
+  float hv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hv[i] = gg[i] / (1.0f + expf(-gg[i])) * uu[i];
+  float db;
+  int sum;
+  const uint32_t packed = q8_block8(hv, db, sum);
+  if (valid) {
+    const int64_t o = r * n_ff + 32 * b + 4 * j;
+    *reinterpret_cast<uint32_t*>(qs + o) = packed;
+    if (h_out != nullptr) *reinterpret_cast<f32x4*>(h_out + o) = f32x4{hv[0], hv[1], hv[2], hv[3]};
+    if (j == 0) {
+      d[r * nb + b] = db;
+      s[r * nb + b] = sum;
+    }
+  }
+}
+
+hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_ff, int8_t* qs, float* d,
+                                  int32_t* s, float* h_out, hipStream_t st) {
+  const int64_t blocks = (int64_t)rows * (n_ff / 32);
+  const int64_t grid = (blocks + 31) / 32;
+  hipLaunchKernelGGL(k_swiglu_quantize, dim3((unsigned)grid), dim3(256), 0, st, gu, ldg, rows, n_ff, qs, d, s,
+                     h_out);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- block dots
 // One thread per (token, row, 32-block), through the same weight decode,
 // activation fetch and paired integer dot (own_first, own_pass, own_second)

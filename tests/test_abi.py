@@ -96,6 +96,19 @@ def test_quantize_validation(L):
     assert f(FAKE, 32, 1, 32, FAKE + 4, None) == MISALIGNED
 
 
+def test_swiglu_quantize_validation(L):
+    f = L.qmv_swiglu_quantize
+    assert f(None, 64, 1, 32, FAKE, None, None) == INVALID
+    assert f(FAKE, 64, 1, 32, None, None, None) == INVALID
+    assert f(FAKE, 64, 0, 32, FAKE, None, None) == INVALID
+    assert f(FAKE, 96, 1, 48, FAKE, None, None) == INVALID
+    assert f(FAKE, 63, 1, 32, FAKE, None, None) == INVALID
+    assert f(FAKE, 64, 65537, 32, FAKE, None, None) == UNSUPPORTED
+    assert f(FAKE + 2, 64, 1, 32, FAKE, None, None) == MISALIGNED
+    assert f(FAKE, 64, 1, 32, FAKE + 4, None, None) == MISALIGNED
+    assert f(FAKE, 64, 1, 32, FAKE, FAKE + 4, None) == MISALIGNED
+
+
 def test_moe_validation(L):
     f = L.qmv_moe_matvec
     ws = q.moe_workspace_bytes(2, 8, 16, 256, 2, 2)
@@ -134,6 +147,8 @@ def test_tuning_switches(L):
     assert L.qmv_set_tuning(b"splitk", -2) == INVALID
     assert L.qmv_set_tuning(b"variant", -1) == OK
     assert L.qmv_set_tuning(b"splitk", -1) == OK
+    assert L.qmv_set_tuning(b"moe_kernel", 3) == INVALID
+    assert L.qmv_set_tuning(b"moe_kernel", 0) == OK
     assert q.variant_name(-1) is None and q.variant_name(len(q.variants())) is None
     assert q.pick_variant(1, 14336, 4096, 1) >= 0
     assert q.pick_variant(1, 14336, 4096, 17) == -1

@@ -171,8 +171,33 @@ def pin_moe_against_dense_loop():
     assert np.array_equal(y1[perm], y2)
 
 
+def pin_swiglu():
+    """SwiGLU against values and identities that do not restate its formula:
+    the logistic function at 1 (sigma(1) = 0.7310585786300049, a tabulated
+    constant), silu(0) = 0, silu(x) - silu(-x) = x (x sigma(x) + x sigma(-x)),
+    linearity in the up half, silu(x) -> x and -> -0 far out."""
+    n = 4
+    gu = np.array([[1.0, 0.0, 3.0, -2.5, 1.0, 7.0, 1.0, 1.0]], np.float32)
+    h = oracle.swiglu(gu, n)
+    assert abs(h[0, 0] - 0.7310585786300049) < 1e-15
+    assert h[0, 1] == 0.0
+    g = synth.make_x(3, 64, "swiglu/g").astype(np.float32) * np.float32(4.0)
+    u = synth.make_x(3, 64, "swiglu/u").astype(np.float32)
+    ones = np.ones_like(g)
+    hp = oracle.swiglu(np.concatenate([g, ones], 1), 64)
+    hn = oracle.swiglu(np.concatenate([-g, ones], 1), 64)
+    assert np.allclose(hp - hn, g.astype(np.float64), rtol=0, atol=1e-14 * (1 + np.abs(g).max()))
+    hu = oracle.swiglu(np.concatenate([g, u], 1), 64)
+    assert np.allclose(hu, hp * u.astype(np.float64), rtol=1e-15, atol=0)
+    far = oracle.swiglu(np.array([[60.0, -800.0, 2.0, 5.0]], np.float32), 2)
+    assert abs(far[0, 0] - 120.0) < 1e-12 and far[0, 1] == 0.0 and np.signbit(far[0, 1])
+    # the gate/up halves are taken from their own columns of a wider row
+    wide = np.concatenate([g, u, np.full_like(g, 9.0)], 1)
+    assert np.array_equal(oracle.swiglu(wide, 64), hu)
+
+
 PINS = [pin_act_cases, pin_act_invariants, pin_integer_special_case, pin_brute_force,
-        pin_quantization_bound, pin_moe_against_dense_loop]
+        pin_quantization_bound, pin_moe_against_dense_loop, pin_swiglu]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -211,6 +236,8 @@ MUTANTS = {
     "q8_reversed_operand": ("p += blk.q[i] * qx[32 * b + i];", "p += blk.q[i] * qx[32 * b + 31 - i];"),
     "block_sum_dropped": ("sum += qi;", "sum += 0;"),
     "fp16_exponent": ("e - 25", "e - 24"),
+    "silu_sign": ("exp(-g);  /*", "exp(g);  /*"),
+    "swiglu_up_column": ("gu[r * ldg + n_ff + i]", "gu[r * ldg + i]"),
 }
 
 
