@@ -50,10 +50,13 @@ def _load():
     lib.oracle_matvec.argtypes = [I, P, I64, I64, P, P, P, I64, P, P]
     lib.oracle_moe_matvec.argtypes = [I, P, I64, I64, I64, P, P, P, I, P, P, I64, I64, P, P]
     lib.oracle_swiglu.argtypes = [P, I64, I64, I64, P]
+    lib.oracle_router_topk.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, P]
+    lib.oracle_topk_from_logits.argtypes = [P, I64, I64, I64, P, P]
     lib.oracle_threads.restype = I
     lib.oracle_set_threads.argtypes = [I]
     for f in ("oracle_unpack", "oracle_dequant", "oracle_quantize_act", "oracle_block_dots",
-              "oracle_matvec", "oracle_moe_matvec", "oracle_swiglu"):
+              "oracle_matvec", "oracle_moe_matvec", "oracle_swiglu", "oracle_router_topk",
+              "oracle_topk_from_logits"):
         getattr(lib, f).restype = I
     _lib = lib
     return lib
@@ -178,3 +181,31 @@ def swiglu(gu: np.ndarray, n_ff: int) -> np.ndarray:
     h = np.zeros((r, n_ff), dtype=np.float64)
     _check(_load().oracle_swiglu(_p(gu), ld, r, n_ff, _p(h)))
     return h
+
+
+def router_topk(x: np.ndarray, wr: np.ndarray, top_k: int):
+    """x fp32 [T][K], router weights fp32 [E][K] -> (ids int32 [T][top_k],
+    w fp64 [T][top_k], logits fp64 [T][E])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None]
+    wr = np.ascontiguousarray(wr, dtype=np.float32)
+    t, k = x.shape
+    e = wr.shape[0]
+    assert wr.shape == (e, k)
+    ids = np.zeros((t, top_k), np.int32)
+    w = np.zeros((t, top_k), np.float64)
+    logits = np.zeros((t, e), np.float64)
+    _check(_load().oracle_router_topk(_p(x), k, t, k, _p(wr), e, top_k, _p(ids), _p(w), _p(logits)))
+    return ids, w, logits
+
+
+def topk_from_logits(logits: np.ndarray, top_k: int):
+    """fp32 logits [T][E] -> (ids int32 [T][top_k], w fp64 [T][top_k]) by the
+    same selection and normalization as router_topk."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    t, e = logits.shape
+    ids = np.zeros((t, top_k), np.int32)
+    w = np.zeros((t, top_k), np.float64)
+    _check(_load().oracle_topk_from_logits(_p(logits), t, e, top_k, _p(ids), _p(w)))
+    return ids, w

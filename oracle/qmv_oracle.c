@@ -402,6 +402,71 @@ int oracle_swiglu(const float* gu, int64_t ldg, int64_t rows, int64_t n_ff, doub
   return 0;
 }
 
+/*
+ * Router and top-k (Castagna Veloce page, "Fused operations": router matvec,
+ * gating, top-k and weight normalization in one kernel).  The pages give no
+ * formula; the readings: router weights fp32 [E][K]; logits l = W x in fp64;
+ * the top_k experts by logit, a larger logit first and on equal logits the
+ * lower expert index first; weights = softmax over the selected logits (the
+ * same as a softmax over all E renormalized over the selected ones).
+ * ids int32 [T][top_k], w double [T][top_k], logits double [T][E].
+ */
+int oracle_router_topk(const float* x, int64_t ldx, int64_t n_tok, int64_t k, const float* wr,
+                       int64_t n_experts, int64_t top_k, int32_t* ids, double* w, double* logits) {
+  if (n_tok < 0 || k < 1 || ldx < k || n_experts < 1 || top_k < 1 || top_k > n_experts) return 1;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    double* l = logits + t * n_experts;
+    for (int64_t e = 0; e < n_experts; ++e) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < k; ++i) acc += (double)wr[e * k + i] * (double)x[t * ldx + i];
+      l[e] = acc;
+    }
+    /* selection: top_k passes, each taking the best expert not yet taken */
+    for (int64_t j = 0; j < top_k; ++j) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < n_experts; ++e) {
+        int taken = 0;
+        for (int64_t q = 0; q < j; ++q)
+          if (ids[t * top_k + q] == (int32_t)e) taken = 1;
+        if (taken) continue;
+        if (best < 0 || l[e] > l[best]) best = e;  /* strict: ties keep the lower index */
+      }
+      ids[t * top_k + j] = (int32_t)best;
+    }
+    double m = l[ids[t * top_k]], sum = 0.0;
+    for (int64_t j = 0; j < top_k; ++j) sum += exp(l[ids[t * top_k + j]] - m);
+    for (int64_t j = 0; j < top_k; ++j) w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m) / sum;
+  }
+  return 0;
+}
+
+/* The selection and weights of oracle_router_topk, from given logits (fp32,
+ * as a kernel computes them): the reference for checking a kernel's choice
+ * against its own logits. */
+int oracle_topk_from_logits(const float* logits, int64_t n_tok, int64_t n_experts, int64_t top_k,
+                            int32_t* ids, double* w) {
+  if (n_tok < 0 || n_experts < 1 || top_k < 1 || top_k > n_experts) return 1;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    const float* l = logits + t * n_experts;
+    for (int64_t j = 0; j < top_k; ++j) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < n_experts; ++e) {
+        int taken = 0;
+        for (int64_t q = 0; q < j; ++q)
+          if (ids[t * top_k + q] == (int32_t)e) taken = 1;
+        if (taken) continue;
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      ids[t * top_k + j] = (int32_t)best;
+    }
+    const double m = l[ids[t * top_k]];
+    double sum = 0.0;
+    for (int64_t j = 0; j < top_k; ++j) sum += exp((double)l[ids[t * top_k + j]] - m);
+    for (int64_t j = 0; j < top_k; ++j) w[t * top_k + j] = exp((double)l[ids[t * top_k + j]] - m) / sum;
+  }
+  return 0;
+}
+
 int oracle_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

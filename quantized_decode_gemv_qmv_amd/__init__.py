@@ -21,7 +21,7 @@ __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
     "moe_workspace_bytes", "quantize_act", "matvec", "moe_matvec", "block_dots",
-    "set_tuning", "swiglu_quantize", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
+    "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
 Q8_0, Q4_K, IQ4_XS = 0, 1, 2
@@ -73,6 +73,7 @@ def lib():
         "qmv_act_offset_s": ([I64, I64], SZ),
         "qmv_quantize_act": ([P, I64, I64, I64, P, P], I),
         "qmv_swiglu_quantize": ([P, I64, I64, I64, P, P, P], I),
+        "qmv_router_topk": ([P, I64, I64, I64, P, I64, I64, P, P, P, P], I),
         "qmv_matvec_workspace_bytes": ([I, I64, I64, I64], SZ),
         "qmv_matvec": ([I, P, I64, I64, P, I64, P, I64, P, SZ, P], I),
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
@@ -152,6 +153,27 @@ def swiglu_quantize(gu: torch.Tensor, n_ff: int, out: torch.Tensor | None = None
     _check(lib().qmv_swiglu_quantize(_ptr(gu), ldg, rows, n_ff, _ptr(out), _ptr(h_out),
                                      _stream(stream)), "qmv_swiglu_quantize")
     return out
+
+
+def router_topk(x: torch.Tensor, wr: torch.Tensor, top_k: int, ids: torch.Tensor | None = None,
+                weights: torch.Tensor | None = None, logits: torch.Tensor | None = None, stream=None):
+    """x fp32 [T][K], router weights fp32 [E][K] -> (ids int32 [T][top_k],
+    weights fp32 [T][top_k]); logits (fp32 [T][E]) receives the router
+    logits."""
+    _need(x, torch.float32, "x")
+    _need(wr, torch.float32, "wr")
+    n_tok, k = x.shape
+    e = wr.shape[0]
+    if ids is None:
+        ids = torch.empty((n_tok, top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((n_tok, top_k), dtype=torch.float32, device=x.device)
+    if logits is not None:
+        _need(logits, torch.float32, "logits")
+    ldx = x.stride(0) if n_tok > 1 else k
+    _check(lib().qmv_router_topk(_ptr(x), ldx, n_tok, k, _ptr(wr), e, top_k, _ptr(ids), _ptr(weights),
+                                 _ptr(logits), _stream(stream)), "qmv_router_topk")
+    return ids, weights
 
 
 def matvec_workspace_bytes(fmt: int, n_rows: int, k: int, n_tok: int) -> int:

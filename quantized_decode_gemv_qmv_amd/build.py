@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqmv.so")
-SOURCES = ["qmv_api.hip", "qmv_quant.hip", "qmv_matvec.hip", "qmv_mfma.hip", "qmv_moe.hip"]
+SOURCES = ["qmv_api.hip", "qmv_quant.hip", "qmv_matvec.hip", "qmv_mfma.hip", "qmv_moe.hip", "qmv_router.hip"]
 ARCH = os.environ.get("QMV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -103,6 +103,8 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t
                            int32_t* s, hipStream_t st);
 hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_ff, int8_t* qs, float* d,
                                   int32_t* s, float* h_out, hipStream_t st);
+hipError_t launch_router_topk(const float* x, int64_t ldx, int n_tok, int k, const float* wr, int n_experts,
+                              int top_k, int32_t* ids, float* w, float* logits, hipStream_t st);
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,

@@ -196,8 +196,39 @@ def pin_swiglu():
     assert np.array_equal(oracle.swiglu(wide, 64), hu)
 
 
+def pin_router_topk():
+    """Router + top-k against hand-built cases: one-hot router rows make the
+    logits equal chosen values exactly; ties go to the lower expert; the
+    weights are a softmax of the chosen logits (checked as ratios
+    w_i / w_j = exp(l_i - l_j) and a sum of 1); numpy's int64 matrix product
+    on integer inputs gives the logits exactly."""
+    e, k = 8, 64
+    wr = np.zeros((e, k), np.float32)
+    for i in range(e):
+        wr[i, i] = 1.0
+    x = np.zeros((2, k), np.float32)
+    x[0, :e] = [0.5, 3.0, -1.0, 3.0, 2.0, 0.0, 7.0, 2.0]
+    x[1, :e] = [1.0] * e  # all tied: experts 0, 1, 2 in order
+    ids, w, logits = oracle.router_topk(x, wr, 3)
+    assert ids.tolist() == [[6, 1, 3], [0, 1, 2]]
+    assert np.array_equal(logits[0], x[0, :e].astype(np.float64))
+    assert abs(w[0].sum() - 1.0) < 1e-15 and np.allclose(w[1], 1.0 / 3.0, rtol=1e-15)
+    assert abs(w[0, 0] / w[0, 1] - np.exp(4.0)) < 1e-12 and abs(w[0, 1] / w[0, 2] - 1.0) < 1e-15
+    rng_x = synth.randint(synth.stream("router/x"), 0, 3 * k, -9, 9).reshape(3, k)
+    rng_w = synth.randint(synth.stream("router/w"), 0, 16 * k, -9, 9).reshape(16, k)
+    ids, w, logits = oracle.router_topk(rng_x.astype(np.float32), rng_w.astype(np.float32), 5)
+    ref = rng_x.astype(np.int64) @ rng_w.astype(np.int64).T
+    assert np.array_equal(logits, ref.astype(np.float64))
+    for t in range(3):
+        order = sorted(range(16), key=lambda i: (-ref[t, i], i))[:5]
+        assert ids[t].tolist() == order
+    # the selection from given logits agrees with the one from the matvec
+    ids2, w2 = oracle.topk_from_logits(logits.astype(np.float32), 5)
+    assert np.array_equal(ids2, ids) and np.allclose(w2, w, rtol=1e-15)
+
+
 PINS = [pin_act_cases, pin_act_invariants, pin_integer_special_case, pin_brute_force,
-        pin_quantization_bound, pin_moe_against_dense_loop, pin_swiglu]
+        pin_quantization_bound, pin_moe_against_dense_loop, pin_swiglu, pin_router_topk]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -238,6 +269,9 @@ MUTANTS = {
     "fp16_exponent": ("e - 25", "e - 24"),
     "silu_sign": ("exp(-g);  /*", "exp(g);  /*"),
     "swiglu_up_column": ("gu[r * ldg + n_ff + i]", "gu[r * ldg + i]"),
+    "topk_tie_upper": ("if (best < 0 || l[e] > l[best]) best = e;  /* strict", "if (best < 0 || l[e] >= l[best]) best = e;  /* strict"),
+    "softmax_unnormalized": ("w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m) / sum;\n  }\n  return 0;\n}\n\n/* The selection", "w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m);\n  }\n  return 0;\n}\n\n/* The selection"),
+    "router_transposed": ("acc += (double)wr[e * k + i] * (double)x[t * ldx + i];", "acc += (double)wr[i * n_experts + e] * (double)x[t * ldx + i];"),
 }
 
 
