@@ -114,6 +114,8 @@ class MoeRing:
     expert tensors (alternating), 16 routings, activations and buffers."""
 
     def __init__(self, torch, qmv, t):
+        import numpy as np
+
         from synth import make_routing, make_x
         from synth.device import make_weights_t
 
@@ -144,6 +146,14 @@ class MoeRing:
                                  dtype=torch.uint8, device="cuda")
         self.ws_dn = torch.zeros(qmv.moe_workspace_bytes(2, e, nd, kd, t, self.top_k),
                                  dtype=torch.uint8, device="cuda")
+        # router fp32 [E][K] with N(0, 1/K) entries, so that the logits of an
+        # N(0,1) token are about N(0,1) as in the routing of this workload
+        self.wr_host = make_x(e, kg, f"{name}/router") * np.float32(1.0 / math.sqrt(kg))
+        self.wr = torch.from_numpy(self.wr_host).cuda()
+        self.r_ids = torch.empty((t, self.top_k), dtype=torch.int32, device="cuda")
+        self.r_w = torch.empty((t, self.top_k), dtype=torch.float32, device="cuda")
+        self.r_logits = torch.empty((t, e), dtype=torch.float32, device="cuda")
+        self.router_u = None
 
     def avg_bytes(self, steps):
         """Weight bytes a step reads, averaged over the routings it cycles."""
@@ -165,14 +175,34 @@ class MoeRing:
         qmv.quantize_act(self.h[i % 8], out=self.hq)
         self.down(qmv, i)
 
+    def router(self, qmv, i):
+        qmv.router_topk(self.x[i % 8], self.wr, self.top_k, ids=self.r_ids, weights=self.r_w,
+                        logits=self.r_logits)
+
     def ffn_step(self, qmv, i):
-        """The MoE FFN: the down projection's input is SwiGLU of the gate+up
-        output, quantized to Q8 in one kernel."""
+        """The MoE FFN: router and top-k, then the routed gate+up; the down
+        projection's input is SwiGLU of the gate+up output, quantized to Q8
+        in one kernel, and its outputs are combined with the router's
+        weights."""
+        e, ng, kg, nd, kd = self.shape
+        self.router(qmv, i)
         qmv.quantize_act(self.x[i % 8], out=self.xq)
-        self.gate_up(qmv, i)
-        _, ng, _, _, kd = self.shape
+        qmv.moe_matvec(2, self.gu[i % 2], e, ng, kg, self.xq, False, self.r_ids, None, self.ws_gu, y=self.y_gu)
         qmv.swiglu_quantize(self.y_gu.view(self.t * self.top_k, ng), kd, out=self.hq)
-        self.down(qmv, i)
+        qmv.moe_matvec(2, self.dn[i % 2], e, nd, kd, self.hq, True, self.r_ids, self.r_w, self.ws_dn,
+                       y=self.y_dn)
+
+    def ffn_bytes(self, qmv, steps):
+        """Weight bytes an FFN step reads (routed experts + the fp32 router),
+        averaged over the steps; the router's picks per input are read back
+        once, outside any timed region."""
+        if self.router_u is None:
+            self.router_u = []
+            for i in range(8):
+                self.router(qmv, i)
+                self.router_u.append(len(set(self.r_ids.cpu().reshape(-1).tolist())))
+        u = sum(self.router_u[i % 8] for i in range(steps)) / steps
+        return u * self.bytes_per_expert + self.wr.numel() * 4, u
 
 
 def capture(torch, fn, count, start=0):
@@ -239,7 +269,12 @@ def moe_cpu_baseline(ring, min_seconds=10.0, ffn=False):
     import synth
 
     e, ng, kg, nd, kd = ring.shape
-    ids, rw = synth.make_routing(ring.t, e, ring.top_k, f"{MOE['name']}/route0")
+    x = synth.make_x(ring.t, kg, f"{MOE['name']}/x")
+    if ffn:  # routed by the router on the first input
+        ids, rw, _ = oracle.router_topk(x, ring.wr_host, ring.top_k)
+        rw = rw.astype(np.float32)
+    else:
+        ids, rw = synth.make_routing(ring.t, e, ring.top_k, f"{MOE['name']}/route0")
     used = sorted(set(ids.reshape(-1).tolist()))
     remap = {ex: i for i, ex in enumerate(used)}
     # only the routed experts' weights are generated; ids are renumbered onto them
@@ -248,12 +283,13 @@ def moe_cpu_baseline(ring, min_seconds=10.0, ffn=False):
     dn = np.concatenate([synth.make_weights(2, e * nd, kd, f"{MOE['name']}/down",
                                             rows=(ex * nd, (ex + 1) * nd)).data for ex in used])
     ids2 = np.vectorize(remap.get)(ids).astype(np.int32)
-    x = synth.make_x(ring.t, kg, f"{MOE['name']}/x")
     h = synth.make_x(ring.t * ring.top_k, kd, f"{MOE['name']}/h")
     cores = len(os.sched_getaffinity(0))
     oracle.set_threads(cores)
     reps, t0 = 0, time.perf_counter()
     while True:
+        if ffn:
+            oracle.router_topk(x, ring.wr_host, ring.top_k)
         qs, d, s = oracle.quantize_act(x)
         y_gu, _ = oracle.moe_matvec(2, gu, len(used), ng, kg, qs, d, s, ids2, None, False)
         if ffn:
@@ -264,10 +300,11 @@ def moe_cpu_baseline(ring, min_seconds=10.0, ffn=False):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    nbytes = len(used) * ring.bytes_per_expert
+    nbytes = len(used) * ring.bytes_per_expert + (ring.wr_host.nbytes if ffn else 0)
     return {"value": round(nbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"MoE step at {ring.t} token(s) (routing 0, {len(used)} experts), {reps} repetitions "
+            "sample": f"MoE{' FFN' if ffn else ''} step at {ring.t} token(s) "
+                      f"({'router on the first input' if ffn else 'routing 0'}, {len(used)} experts), {reps} repetitions "
                       f"in {el:.1f} s"}
 
 
@@ -289,11 +326,18 @@ def bench_moe(args, torch, qmv, ffn=False):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    step_bytes = ring.avg_bytes(args.steps)
+    if ffn:
+        step_bytes, avg_u = ring.ffn_bytes(qmv, args.steps)
+    else:
+        step_bytes = ring.avg_bytes(args.steps)
+        avg_u = step_bytes / ring.bytes_per_expert
+    step_u = avg_u
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     gu_us = timed_replays(torch, lambda i: ring.gate_up(qmv, i), per)
     dn_us = timed_replays(torch, lambda i: ring.down(qmv, i), per)
-    avg_u = step_bytes / ring.bytes_per_expert
+    router_us = timed_replays(torch, lambda i: ring.router(qmv, i), per) if ffn else None
+    if ffn:  # the kernel figures below use the synthetic routings of the plain MoE step
+        avg_u = ring.avg_bytes(args.steps) / ring.bytes_per_expert
     gu_bytes = avg_u * ring.gu[0].numel() / ring.shape[0]
     dn_bytes = avg_u * ring.dn[0].numel() / ring.shape[0]
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
@@ -313,9 +357,10 @@ def bench_moe(args, torch, qmv, ffn=False):
         "data": "synthetic",
         "config": {"workload": f"MoE{' FFN' if ffn else ''} IQ4_XS 128 experts top-8, gate+up 3072x4096 + "
                                f"down 4096x1536, {t} token(s)", "tokens": t,
-                   "avg_distinct_experts": round(avg_u, 2), "weight_bytes_per_step": round(step_bytes),
-                   "step": ("quantize x + gate_up routed matvec + SwiGLU and Q8 of its output + down routed "
-                            "matvec" if ffn else
+                   "avg_distinct_experts": round(step_u, 2),
+                   "weight_bytes_per_step": round(step_bytes),
+                   "step": ("router + top-k (fp32 router 128x4096) + quantize x + gate_up routed matvec + SwiGLU "
+                            "and Q8 of its output + down routed matvec weighted by the router" if ffn else
                             "quantize x + gate_up routed matvec + quantize h + down routed matvec")},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -324,6 +369,7 @@ def bench_moe(args, torch, qmv, ffn=False):
                      "algorithmic_bytes_per_launch": round(gu_bytes)},
         "down_kernel": {"kernel_us": round(dn_us, 3), "weight_GBps": round(dn_bytes / (dn_us * 1e-6) / 1e9, 1),
                         "algorithmic_bytes_per_launch": round(dn_bytes)},
+        **({"router_us": round(router_us, 3)} if ffn else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

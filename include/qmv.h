@@ -127,10 +127,10 @@ qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t rows, int64
                                float* h_out, void* stream);
 
 /*
- * qmv_router_topk -- MoE router and top-k in one kernel: the routing ids and
- * weights that qmv_moe_matvec takes.  Castagna Veloce page, "Fused
- * operations" (router matvec, gating, top-k and weight normalization in one
- * kernel).  For token t:
+ * qmv_router_topk -- MoE router and top-k: the routing ids and weights that
+ * qmv_moe_matvec takes.  Castagna Veloce page, "Fused operations" (router
+ * matvec, gating, top-k and weight normalization fused for decode).  For
+ * token t:
  *   l[e] = sum_i wr[e][i] x[t][i]            (fp32 sums),
  *   ids[t][0..top_k-1] = the top_k experts by l, a larger logit first and on
  *                        equal logits the lower expert index first,
@@ -139,8 +139,9 @@ qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t rows, int64
  * x       : fp32 [n_tok][ldx] (device), 16-byte aligned, ldx >= k, ldx % 4 == 0.
  * wr      : fp32 router weights [n_experts][k] (device), 16-byte aligned.
  * ids     : int32 [n_tok][top_k] (device); weights: fp32 [n_tok][top_k].
- * logits  : NULL, or fp32 [n_tok][n_experts] (device) receiving l.
- * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, k % 4 == 0, k <= 16384,
+ * logits  : fp32 [n_tok][n_experts] (device), receives l (the selection
+ *           reads it back: two launches on `stream`).
+ * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, k % 4 == 0, k <= 2^24,
  * 1 <= top_k <= min(n_experts, QMV_MAX_TOP_K), n_experts <= QMV_MAX_EXPERTS.
  * Asynchronous on `stream`; allocates nothing.
  */

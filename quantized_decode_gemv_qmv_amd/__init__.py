@@ -158,8 +158,8 @@ def swiglu_quantize(gu: torch.Tensor, n_ff: int, out: torch.Tensor | None = None
 def router_topk(x: torch.Tensor, wr: torch.Tensor, top_k: int, ids: torch.Tensor | None = None,
                 weights: torch.Tensor | None = None, logits: torch.Tensor | None = None, stream=None):
     """x fp32 [T][K], router weights fp32 [E][K] -> (ids int32 [T][top_k],
-    weights fp32 [T][top_k]); logits (fp32 [T][E]) receives the router
-    logits."""
+    weights fp32 [T][top_k]); logits (fp32 [T][E], allocated when None)
+    receives the router logits."""
     _need(x, torch.float32, "x")
     _need(wr, torch.float32, "wr")
     n_tok, k = x.shape
@@ -168,8 +168,9 @@ def router_topk(x: torch.Tensor, wr: torch.Tensor, top_k: int, ids: torch.Tensor
         ids = torch.empty((n_tok, top_k), dtype=torch.int32, device=x.device)
     if weights is None:
         weights = torch.empty((n_tok, top_k), dtype=torch.float32, device=x.device)
-    if logits is not None:
-        _need(logits, torch.float32, "logits")
+    if logits is None:
+        logits = torch.empty((n_tok, e), dtype=torch.float32, device=x.device)
+    _need(logits, torch.float32, "logits")
     ldx = x.stride(0) if n_tok > 1 else k
     _check(lib().qmv_router_topk(_ptr(x), ldx, n_tok, k, _ptr(wr), e, top_k, _ptr(ids), _ptr(weights),
                                  _ptr(logits), _stream(stream)), "qmv_router_topk")

@@ -113,19 +113,20 @@ def test_router_topk_validation(L):
     f = L.qmv_router_topk
 
     def call(**kw):
-        a = dict(x=FAKE, ldx=64, t=2, k=64, wr=FAKE, e=8, top_k=2, ids=FAKE, w=FAKE, logits=None)
+        a = dict(x=FAKE, ldx=64, t=2, k=64, wr=FAKE, e=8, top_k=2, ids=FAKE, w=FAKE, logits=FAKE)
         a.update(kw)
         return f(a["x"], a["ldx"], a["t"], a["k"], a["wr"], a["e"], a["top_k"], a["ids"], a["w"],
                  a["logits"], None)
 
     assert call(x=None) == INVALID
     assert call(ids=None) == INVALID
+    assert call(logits=None) == INVALID
     assert call(k=62, ldx=64) == INVALID
     assert call(ldx=63) == INVALID
     assert call(top_k=9) == INVALID
     assert call(top_k=0) == INVALID
     assert call(t=65) == UNSUPPORTED
-    assert call(k=16388, ldx=16388) == UNSUPPORTED
+    assert call(k=(1 << 24) + 4, ldx=(1 << 24) + 4) == UNSUPPORTED
     assert call(e=2000, top_k=2) == UNSUPPORTED
     assert call(e=64, top_k=17) == UNSUPPORTED
     assert call(x=FAKE + 4) == MISALIGNED
