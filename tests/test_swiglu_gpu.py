@@ -4,7 +4,7 @@ down matvec), against the oracle.
 
 The fp32 h = silu(g) * u of the GPU is compared with the oracle's fp64 h
 within 4e-7 relative (a few fp32 roundings and the exp's own error), plus
-3e-37 |u| absolute: for g < -88.7 exp(-g) overflows fp32 and silu(g) comes out
+3e-37 max(|u|, 1) absolute: for g < -88.7 exp(-g) overflows fp32 and silu(g) comes out
 as -0, where its true magnitude is below 89 e^-88.7 < 3e-37.  The Q8
 blocks are an integer decision taken from that fp32 h, so they are compared
 bit-exactly with the oracle's quantization of the GPU's own h; each stage of
@@ -32,7 +32,7 @@ def _check_swiglu(qmv, gu: np.ndarray, n_ff: int, what: str):
     h_ref = oracle.swiglu(gu, n_ff)
     err = np.abs(h.astype(np.float64) - h_ref)
     u = np.abs(gu[:, n_ff:2 * n_ff].astype(np.float64))
-    bad = err > H_REL * np.abs(h_ref) + 3e-37 * np.maximum(u, 1.0)
+    bad = err > H_REL * np.abs(h_ref) + 3e-37 * np.maximum(np.abs(u), 1.0)
     assert not bad.any(), (what, np.argwhere(bad)[:3], h[bad][:3], h_ref[bad][:3])
     qs, d, s = qmv.act_fields(xq, rows, n_ff)
     qs_r, d_r, s_r = oracle.quantize_act(h)
