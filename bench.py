@@ -37,9 +37,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "weight GB/s & % HBM roofline, q4_K/IQ4_XS matvec at 1–16 tokens"
 
-# name: (format, rows, K, token counts of the workload)
+# name: (format, rows, K, token counts of the workload[, sibling matrices])
 WORKLOADS = {
     "q4_k_14336x4096": (1, 14336, 4096, (1, 2, 4, 8, 16)),
+    # gate and up projections as two separate tensors sharing one activation
+    # buffer, one qmv_matvec_batch launch
+    "q4_k_siblings_2x14336x4096": (1, 14336, 4096, (1, 2, 4, 8, 16), 2),
     "iq4_xs_4096x14336": (2, 4096, 14336, (1, 2, 4, 8, 16)),
     "q8_0_4096x4096": (0, 4096, 4096, (1,)),
     "q8_0_splitk_256x65536": (0, 256, 65536, (1,)),
@@ -83,30 +86,42 @@ class Ring:
     """Device-resident inputs of one workload: weight ring, activations,
     buffers."""
 
-    def __init__(self, torch, qmv, fmt, n, k, t, name):
+    def __init__(self, torch, qmv, fmt, n, k, t, name, mats=1):
         from synth import make_x
         from synth.device import make_weights_t
 
-        self.fmt, self.n, self.k, self.t = fmt, n, k, t
-        w0 = make_weights_t(fmt, n, k, f"{name}/W", device="cuda")
-        self.weight_bytes = w0.numel()
+        self.fmt, self.n, self.k, self.t, self.mats = fmt, n, k, t, mats
+        # mats == 1: one matrix per copy; else `mats` sibling matrices
+        # (separate tensors) per copy, run as one batched launch
+        w0 = [make_weights_t(fmt, n, k, f"{name}/W" if mats == 1 else f"{name}/W{j}", device="cuda")
+              for j in range(mats)]
+        self.weight_bytes = sum(w.numel() for w in w0)
         self.copies = max(2, math.ceil((1 << 30) / self.weight_bytes))
-        self.w = [w0] + [w0.clone() for _ in range(self.copies - 1)]
+        self.w = [w0] + [[w.clone() for w in w0] for _ in range(self.copies - 1)]
         xs = make_x(8 * t, k, f"{name}/x").reshape(8, t, k)
         self.x = [torch.from_numpy(xs[i]).cuda() for i in range(8)]
         self.xq = torch.empty(qmv.act_bytes(t, k), dtype=torch.uint8, device="cuda")
-        self.y = torch.empty((t, n), dtype=torch.float32, device="cuda")
-        wsb = qmv.matvec_workspace_bytes(fmt, n, k, t)
+        self.y = [torch.empty((t, n), dtype=torch.float32, device="cuda") for _ in range(mats)]
+        wsb = qmv.matvec_workspace_bytes(fmt, n, k, t) if mats == 1 else 0
         self.ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
 
     def step(self, qmv, i):
         qmv.quantize_act(self.x[i % 8], out=self.xq)
-        qmv.matvec(self.fmt, self.w[i % self.copies], self.n, self.k, self.xq, self.t, y=self.y,
-                   ws=self.ws)
+        self.matvec_only(qmv, i)
 
     def matvec_only(self, qmv, i):
-        qmv.matvec(self.fmt, self.w[i % self.copies], self.n, self.k, self.xq, self.t, y=self.y,
-                   ws=self.ws)
+        w = self.w[i % self.copies]
+        if self.mats == 1:
+            qmv.matvec(self.fmt, w[0], self.n, self.k, self.xq, self.t, y=self.y[0], ws=self.ws)
+        else:
+            qmv.matvec_batch(self.fmt, [(w[j], self.n, self.y[j], None) for j in range(self.mats)],
+                             self.k, self.xq, self.t)
+
+    def separate(self, qmv, i):
+        """The sibling matrices as separate qmv_matvec launches (comparison)."""
+        w = self.w[i % self.copies]
+        for j in range(self.mats):
+            qmv.matvec(self.fmt, w[j], self.n, self.k, self.xq, self.t, y=self.y[j])
 
 
 class MoeRing:
@@ -434,14 +449,15 @@ def main() -> int:
             print("--tokens must be 1..64 for the MoE workload", file=sys.stderr)
             return 2
         return bench_moe(args, torch, qmv, ffn=args.workload == MOE["ffn_name"])
-    fmt, n, k, token_list = WORKLOADS[args.workload]
+    fmt, n, k, token_list, *rest = WORKLOADS[args.workload]
+    mats = rest[0] if rest else 1
     t = args.tokens
     if not 1 <= t <= 16:
         print("--tokens must be 1..16", file=sys.stderr)
         return 2
 
     log(f"bench: {args.workload} T={t}: generating inputs")
-    ring = Ring(torch, qmv, fmt, n, k, t, args.workload)
+    ring = Ring(torch, qmv, fmt, n, k, t, args.workload, mats)
     per = max(ring.copies, 64)
     g_full = capture(torch, lambda i: ring.step(qmv, i), per)
     tail = args.steps % per
@@ -466,18 +482,24 @@ def main() -> int:
     achieved = ring.weight_bytes / (kus * 1e-6) / 1e9
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(args.workload, t, src_hash)
-    variant = qmv.variant_name(qmv.pick_variant(fmt, n, k, t))
+    # a batch of equal matrices runs the variant of their stacked rows (each
+    # matrix padded to a multiple of 64 rows)
+    variant = qmv.variant_name(qmv.pick_variant(fmt, mats * ((n + 63) // 64 * 64) if mats > 1 else n, k, t))
 
     by_tokens = []
     if args.all_tokens:
         for tt in token_list:
-            r2 = ring if tt == t else Ring(torch, qmv, fmt, n, k, tt, args.workload)
+            r2 = ring if tt == t else Ring(torch, qmv, fmt, n, k, tt, args.workload, mats)
             us = kernel_us(torch, qmv, r2)
-            by_tokens.append({"tokens": tt, "kernel_us": round(us, 3),
-                              "weight_GBps": round(r2.weight_bytes / (us * 1e-6) / 1e9, 1),
-                              "hbm_frac": round(r2.weight_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                              "matvecs_per_s": round(1e6 / us, 1),
-                              "variant": qmv.variant_name(qmv.pick_variant(fmt, n, k, tt))})
+            rec = {"tokens": tt, "kernel_us": round(us, 3),
+                   "weight_GBps": round(r2.weight_bytes / (us * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(r2.weight_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "matvecs_per_s": round(1e6 / us, 1),
+                   "variant": qmv.variant_name(qmv.pick_variant(fmt, mats * n, k, tt))}
+            if mats > 1:
+                rec["separate_launches_us"] = round(timed_replays(torch, lambda i: r2.separate(qmv, i),
+                                                                  max(r2.copies, 32)), 3)
+            by_tokens.append(rec)
             log(f"bench: T={tt} kernel {us:.2f} us")
             if r2 is not ring:
                 del r2
@@ -501,9 +523,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{FMT_NAME[fmt]} matvec {n}x{k}, {t} token(s)", "format": FMT_NAME[fmt],
-                   "n_rows": n, "k": k, "tokens": t, "weight_bytes": ring.weight_bytes,
-                   "ring_copies": ring.copies, "step": "qmv_quantize_act + qmv_matvec",
+        "config": {"workload": (f"{FMT_NAME[fmt]} matvec {n}x{k}, {t} token(s)" if mats == 1 else
+                                f"{mats} sibling {FMT_NAME[fmt]} matvecs {n}x{k} in one launch, {t} token(s)"),
+                   "format": FMT_NAME[fmt], "n_rows": n, "k": k, "tokens": t, "matrices": mats,
+                   "weight_bytes": ring.weight_bytes, "ring_copies": ring.copies,
+                   "step": "qmv_quantize_act + " + ("qmv_matvec" if mats == 1 else "qmv_matvec_batch"),
                    "matvec_variant": variant},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "matvecs_per_s": round(1e3 / ms_per_step, 1),

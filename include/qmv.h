@@ -177,6 +177,43 @@ qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int64_t k, c
                       void* stream);
 
 /*
+ * qmv_matvec_batch -- sibling matvecs over one activation buffer in one
+ * launch, each optionally plus a residual:
+ *   y_i[t][n] = sum_k W_i[n][k] * xq[t][k]  (+ residual_i[t][n])
+ * for every item i and t < n_tok.  Castagna Veloce page, "Fused operations"
+ * (batched sibling matvecs and Q8 activations reused across weight types;
+ * matvec + residual add kernels for the verify batches).  Every item has the
+ * same weight type and reduction length k; each item's arithmetic is that of
+ * qmv_matvec, and the residual is added to the fp32 sum once, at the end.
+ * items  : HOST array of n_items descriptors, read during the call only:
+ *   w        n_rows x k weights of `type` (device, 16-byte aligned);
+ *   n_rows   >= 1;
+ *   y        fp32 [n_tok][ldy] (device, 4-byte aligned), ldy >= n_rows;
+ *            columns 0..n_rows-1 of each row are overwritten;
+ *   residual NULL, or fp32 [n_tok][ldr] (device, 4-byte aligned),
+ *            ldr >= n_rows; it may be the item's own y with ldr == ldy
+ *            (accumulate in place), otherwise it must not overlap any
+ *            item's y.
+ * The y extents of different items must not overlap.
+ * xq     : activation buffer made by qmv_quantize_act for (n_tok, k).
+ * 1 <= n_items <= QMV_MAX_BATCH and 1 <= n_tok <= QMV_MAX_TOKENS (else
+ * QMV_ERR_UNSUPPORTED); k as for qmv_matvec; overlapping outputs or a bad
+ * descriptor give QMV_ERR_INVALID_ARG.  No workspace, no split-K across
+ * workgroups.  Asynchronous on `stream`; allocates nothing.
+ */
+#define QMV_MAX_BATCH 8
+typedef struct {
+  const void* w;
+  int64_t n_rows;
+  float* y;
+  int64_t ldy;
+  const float* residual;
+  int64_t ldr;
+} qmv_matvec_item;
+qmv_status qmv_matvec_batch(qmv_type type, const qmv_matvec_item* items, int64_t n_items, int64_t k,
+                            const void* xq, int64_t n_tok, void* stream);
+
+/*
  * qmv_moe_matvec -- expert-grouped routed matvec.
  * Castagna Veloce page, "Kernels for the MI50" (i-quant MoE decode kernels
  * for batches of up to 64 tokens; expert-grouped quantized MoE: each active

@@ -48,6 +48,7 @@ def _load():
     lib.oracle_quantize_act.argtypes = [P, I64, I64, I64, P, P, P]
     lib.oracle_block_dots.argtypes = [I, P, I64, I64, P, P, I64, P]
     lib.oracle_matvec.argtypes = [I, P, I64, I64, P, P, P, I64, P, P]
+    lib.oracle_matvec_residual.argtypes = [I, P, I64, I64, P, P, P, I64, P, I64, P, P]
     lib.oracle_moe_matvec.argtypes = [I, P, I64, I64, I64, P, P, P, I, P, P, I64, I64, P, P]
     lib.oracle_swiglu.argtypes = [P, I64, I64, I64, P]
     lib.oracle_router_topk.argtypes = [P, I64, I64, I64, P, I64, I64, P, P, P]
@@ -55,7 +56,7 @@ def _load():
     lib.oracle_threads.restype = I
     lib.oracle_set_threads.argtypes = [I]
     for f in ("oracle_unpack", "oracle_dequant", "oracle_quantize_act", "oracle_block_dots",
-              "oracle_matvec", "oracle_moe_matvec", "oracle_swiglu", "oracle_router_topk",
+              "oracle_matvec", "oracle_matvec_residual", "oracle_moe_matvec", "oracle_swiglu", "oracle_router_topk",
               "oracle_topk_from_logits"):
         getattr(lib, f).restype = I
     _lib = lib
@@ -136,8 +137,9 @@ def block_dots(fmt: int, w: np.ndarray, k: int, qs: np.ndarray, s: np.ndarray) -
     return out
 
 
-def matvec(fmt: int, w: np.ndarray, k: int, qs, d, s):
-    """(y, mag) fp64 [T][N]: y the reference output, mag the sum of |terms|."""
+def matvec(fmt: int, w: np.ndarray, k: int, qs, d, s, residual: np.ndarray | None = None):
+    """(y, mag) fp64 [T][N]: y the reference output, mag the sum of |terms|.
+    With a residual (fp32 [T][N]) it is one more term: y + r, mag + |r|."""
     w = _w2d(fmt, w, k)
     qs = np.ascontiguousarray(qs, dtype=np.int8)
     d = np.ascontiguousarray(d, dtype=np.float32)
@@ -145,7 +147,13 @@ def matvec(fmt: int, w: np.ndarray, k: int, qs, d, s):
     t = qs.shape[0]
     y = np.zeros((t, w.shape[0]))
     mag = np.zeros((t, w.shape[0]))
-    _check(_load().oracle_matvec(fmt, _p(w), w.shape[0], k, _p(qs), _p(d), _p(s), t, _p(y), _p(mag)))
+    if residual is None:
+        _check(_load().oracle_matvec(fmt, _p(w), w.shape[0], k, _p(qs), _p(d), _p(s), t, _p(y), _p(mag)))
+    else:
+        r = np.ascontiguousarray(residual, dtype=np.float32)
+        assert r.shape == (t, w.shape[0])
+        _check(_load().oracle_matvec_residual(fmt, _p(w), w.shape[0], k, _p(qs), _p(d), _p(s), t, _p(r),
+                                              r.shape[1], _p(y), _p(mag)))
     return y, mag
 
 

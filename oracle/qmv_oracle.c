@@ -330,6 +330,22 @@ int oracle_matvec(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, const in
   return 0;
 }
 
+/* Matvec plus a residual (Castagna Veloce page, "Fused operations": matvec +
+ * residual add): y[t][n] = sum of the terms of (t, n) + res[t][n], the
+ * residual being one more term of the sum (mag gains |res[t][n]|). */
+int oracle_matvec_residual(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, const int8_t* qs,
+                           const float* d, const int32_t* s, int64_t n_tok, const float* res,
+                           int64_t ldr, double* y, double* mag) {
+  if (oracle_matvec(fmt, w, n_rows, k, qs, d, s, n_tok, y, mag) != 0) return -1;
+  for (int64_t t = 0; t < n_tok; ++t)
+    for (int64_t n = 0; n < n_rows; ++n) {
+      const double rv = (double)res[t * ldr + n];
+      y[t * n_rows + n] += rv;
+      mag[t * n_rows + n] += fabs(rv);
+    }
+  return 0;
+}
+
 /* Expert-routed matvec (Castagna Veloce page, "Kernels for the MI50": MoE
  * decode for up to 64 tokens, one pass per expert over its routed tokens).
  * w = [n_experts][n_rows][row bytes].  Slot (t, s) uses expert ids[t][s] and

@@ -20,19 +20,26 @@ import torch
 __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
-    "moe_workspace_bytes", "quantize_act", "matvec", "moe_matvec", "block_dots",
+    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_batch", "moe_matvec", "block_dots",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
 Q8_0, Q4_K, IQ4_XS = 0, 1, 2
 MAX_TOKENS = 16
 MAX_MOE_TOKENS = 64
+MAX_BATCH = 8
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_PKG)
 _LIB = os.path.join(_PKG, "libqmv.so")
 _HEADER = os.path.join(_ROOT, "include", "qmv.h")
 _lib = None
+
+
+class _Item(ctypes.Structure):
+    """qmv_matvec_item of include/qmv.h."""
+    _fields_ = [("w", ctypes.c_void_p), ("n_rows", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64), ("residual", ctypes.c_void_p), ("ldr", ctypes.c_int64)]
 
 
 class QmvError(RuntimeError):
@@ -76,6 +83,7 @@ def lib():
         "qmv_router_topk": ([P, I64, I64, I64, P, I64, I64, P, P, P, P], I),
         "qmv_matvec_workspace_bytes": ([I, I64, I64, I64], SZ),
         "qmv_matvec": ([I, P, I64, I64, P, I64, P, I64, P, SZ, P], I),
+        "qmv_matvec_batch": ([I, ctypes.POINTER(_Item), I64, I64, P, I64, P], I),
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
@@ -225,6 +233,36 @@ def matvec(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor, n_t
     _check(lib().qmv_matvec(fmt, _ptr(w), n_rows, k, _ptr(xq), n_tok, _ptr(y), ldy,
                             _ptr(ws), wsz, _stream(stream)), "qmv_matvec")
     return y
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]  # a single row's stride is arbitrary
+
+
+def matvec_batch(fmt: int, items, k: int, xq: torch.Tensor, n_tok: int, stream=None) -> list:
+    """Sibling matvecs over one activation buffer in one launch.  ``items`` is
+    a sequence of (w, n_rows, y, residual): y (fp32 [T][>= n_rows], allocated
+    when None) receives W xq, plus residual (fp32 [T][>= n_rows]) when it is
+    not None; residual may be y itself.  Returns the list of y."""
+    _need(xq, torch.uint8, "xq")
+    arr = (_Item * max(1, len(items)))()
+    outs = []
+    for i, (w, n_rows, y, res) in enumerate(items):
+        _need(w, torch.uint8, "w")
+        if w.numel() < n_rows * row_bytes(fmt, k):
+            raise ValueError("w holds fewer than n_rows rows")
+        if y is None:
+            y = torch.empty((n_tok, n_rows), dtype=torch.float32, device=w.device)
+        for name, t in (("y", y), ("residual", res)):
+            if t is not None and (t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2
+                                  or t.stride(1) != 1):
+                raise ValueError(f"{name} must be a float32 CUDA tensor [T][ld] with unit column stride")
+        arr[i] = _Item(w.data_ptr(), n_rows, y.data_ptr(), _ld(y),
+                       None if res is None else res.data_ptr(), 0 if res is None else _ld(res))
+        outs.append(y)
+    _check(lib().qmv_matvec_batch(fmt, arr, len(items), k, _ptr(xq), n_tok, _stream(stream)),
+           "qmv_matvec_batch")
+    return outs
 
 
 def moe_matvec(fmt: int, w: torch.Tensor, n_experts: int, n_rows: int, k: int,

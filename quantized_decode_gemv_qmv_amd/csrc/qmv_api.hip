@@ -384,6 +384,82 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 
+// Byte extent [lo, hi) of an fp32 [n_tok][ld] output touching n columns.
+static void extent(const float* p, int64_t n_tok, int64_t ld, int64_t n, uintptr_t& lo, uintptr_t& hi) {
+  lo = reinterpret_cast<uintptr_t>(p);
+  hi = lo + static_cast<uintptr_t>(((n_tok - 1) * ld + n) * 4);
+}
+
+QMV_API qmv_status qmv_matvec_batch(qmv_type type, const qmv_matvec_item* items, int64_t n_items,
+                                    int64_t k, const void* xq, int64_t n_tok, void* stream) {
+  if (!valid_type(type) || items == nullptr || n_items < 1 || xq == nullptr || n_tok < 1)
+    return QMV_ERR_INVALID_ARG;
+  if (n_items > QMV_MAX_BATCH || n_tok > QMV_MAX_TOKENS) return QMV_ERR_UNSUPPORTED;
+  static_assert(QMV_MAX_BATCH <= kMaxBatch, "segment table");
+  MatvecLaunch a{};
+  int64_t rows = 0;  // launch rows so far (each matrix starts on a kSegAlign boundary)
+  for (int64_t i = 0; i < n_items; ++i) {
+    const qmv_matvec_item& it = items[i];
+    const qmv_status st = check_weights(type, it.w, it.n_rows, k);
+    if (st != QMV_OK) return st;
+    if (it.y == nullptr || it.ldy < it.n_rows || (it.residual != nullptr && it.ldr < it.n_rows))
+      return QMV_ERR_INVALID_ARG;
+    if (!aligned(it.y, 4) || (it.residual != nullptr && !aligned(it.residual, 4))) return QMV_ERR_MISALIGNED;
+    rows = (rows + kSegAlign - 1) / kSegAlign * kSegAlign;
+    RowSeg& sg = a.seg.s[i];
+    sg.first = static_cast<int>(rows);
+    sg.rows = static_cast<int>(it.n_rows);
+    sg.w = static_cast<const uint8_t*>(it.w);
+    sg.y = it.y;
+    sg.ldy = it.ldy;
+    sg.res = it.residual;
+    sg.ldr = it.residual != nullptr ? it.ldr : 0;
+    rows += it.n_rows;
+    if (rows > INT32_MAX / 4) return QMV_ERR_INVALID_ARG;
+  }
+  // outputs pairwise disjoint; a residual is its own output or disjoint from all
+  for (int64_t i = 0; i < n_items; ++i) {
+    uintptr_t lo, hi;
+    extent(items[i].y, n_tok, items[i].ldy, items[i].n_rows, lo, hi);
+    for (int64_t j = 0; j < n_items; ++j) {
+      uintptr_t l2, h2;
+      if (j != i) {
+        extent(items[j].y, n_tok, items[j].ldy, items[j].n_rows, l2, h2);
+        if (lo < h2 && l2 < hi) return QMV_ERR_INVALID_ARG;
+      }
+      const float* r = items[j].residual;
+      if (r == nullptr || (j == i && r == items[i].y && items[i].ldr == items[i].ldy)) continue;
+      extent(r, n_tok, items[j].ldr, items[j].n_rows, l2, h2);
+      if (lo < h2 && l2 < hi) return QMV_ERR_INVALID_ARG;
+    }
+  }
+  if (!aligned(xq, 256)) return QMV_ERR_MISALIGNED;
+  a.seg.n = static_cast<int>(n_items);
+  a.fmt = type;
+  a.w = a.seg.s[0].w;
+  a.row_bytes = static_cast<int64_t>(qmv_row_bytes(type, k));
+  a.n_rows = static_cast<int>(rows);
+  a.units = static_cast<int>(k / 32);
+  a.x = act_view(xq, n_tok, k);
+  a.n_tok = static_cast<int>(n_tok);
+  a.y = a.seg.s[0].y;
+  a.ldy = a.seg.s[0].ldy;
+  // the lane-group kernel (kind 0) has no segment table: a forced variant of
+  // that kind gives way to the automatic choice
+  a.variant = choose_variant(type, rows, k, n_tok);
+  if (kVariants[a.variant].kind == 0) a.variant = auto_variant(type, rows, k, n_tok);
+  a.slices = 1;
+  a.xq = static_cast<const uint8_t*>(xq);
+  a.act_bytes = static_cast<int64_t>(qmv_act_bytes(n_tok, k));
+  a.off_d = static_cast<int64_t>(qmv_act_offset_d(n_tok, k));
+  a.off_s = static_cast<int64_t>(qmv_act_offset_s(n_tok, k));
+  const DeviceInfo dv = device_info();
+  a.cus = dv.cus;
+  a.lds_per_cu = dv.lds_per_cu;
+  hipError_t e = launch_matvec(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
 QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t k,
                                   const void* xq, int64_t n_tok, int32_t* out, void* stream) {
   qmv_status st = check_weights(type, w, n_rows, k);

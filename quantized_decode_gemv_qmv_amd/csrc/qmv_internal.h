@@ -47,6 +47,30 @@ struct Variant {
 extern const Variant kVariants[];
 extern const int kNumVariants;
 
+// The matrix a launch row belongs to: its weights, output and residual, its
+// first launch row and its row count.
+struct RowSeg {
+  const uint8_t* w;
+  float* y;
+  const float* res;  // NULL, or fp32 [n_tok][ldr] added to the outputs
+  int64_t ldy, ldr;
+  int first, rows;
+};
+
+// Matrices of one batched launch (sibling matvecs sharing an activation
+// buffer): stacked along the launch's rows, matrix i taking launch rows
+// s[i].first .. s[i].first + s[i].rows - 1.  Every first row is a multiple of
+// kSegAlign, which every kernel's per-wave (and per-workgroup reduction) row
+// span divides, so a wave never straddles two matrices; launch rows between
+// one matrix's end and the next one's start only re-read valid rows and
+// store nothing.
+constexpr int kMaxBatch = 8;
+constexpr int kSegAlign = 64;
+struct Segs {
+  int n;  // 0: a single matrix, described by the w / y / res fields around
+  RowSeg s[kMaxBatch];
+};
+
 // Kernel arguments of k_stream.
 struct StreamArgs {
   const uint8_t* w;
@@ -61,7 +85,40 @@ struct StreamArgs {
   float* y;
   int64_t ldy;
   int kc;  // k_mt: units per LDS chunk
+  const float* res;  // NULL, or fp32 [n_tok][ldr] added to the outputs
+  int64_t ldr;
+  Segs seg;
 };
+
+#ifdef __HIPCC__
+// Segment of launch row `row`, a wave-uniform value.  SEG false (a launch of
+// one matrix, never with a residual) compiles to the single-matrix fields
+// and a constant null residual; kernels take SEG as a
+// template flag so that single-matrix launches carry no table code.  With
+// SEG, the index is counted from the first rows and the one entry is then
+// read from the kernel arguments.
+template <bool SEG>
+__device__ inline RowSeg row_seg(const StreamArgs& a, int row) {
+  if constexpr (!SEG) return RowSeg{a.w, a.y, nullptr, a.ldy, 0, 0, a.n_rows};  // no residual either
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxBatch; ++j) i += (j < a.seg.n && row >= a.seg.s[j].first) ? 1 : 0;
+  return a.seg.s[i];
+}
+// Weight row of launch row `row` inside its segment (clamped to the last row).
+__device__ inline const uint8_t* seg_wrow(const RowSeg& s, int64_t row_bytes, int row) {
+  return s.w + (int64_t)min(row - s.first, s.rows - 1) * row_bytes;
+}
+// Output (t, launch row `row`) = v plus the residual, if the row is one of
+// the segment's rows.
+__device__ inline void seg_store(const RowSeg& s, int t, int row, float v) {
+  const int lr = row - s.first;
+  if (lr < s.rows) {
+    if (s.res != nullptr) v += s.res[(int64_t)t * s.ldr + lr];
+    s.y[(int64_t)t * s.ldy + lr] = v;
+  }
+}
+#endif
 
 // LDS bytes k_mt stages per chunk at most (two workgroups per compute unit).
 constexpr int64_t kMultiLdsBudget = 80 * 1024;
@@ -76,6 +133,9 @@ struct MatvecLaunch {
   int n_tok;
   float* y;
   int64_t ldy;
+  const float* res;  // NULL, or fp32 [n_tok][ldr] added to y
+  int64_t ldr;
+  Segs seg;         // batched launch (seg.n > 0): the matrices; n_rows the launch rows
   int variant;  // index into kVariants
   const uint8_t* xq;  // the activation buffer and its layout
   int64_t act_bytes, off_d, off_s;

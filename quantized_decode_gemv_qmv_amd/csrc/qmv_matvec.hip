@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, i
 }
 
 // ------------------------------------------------------- streaming kernel
-template <int F, int TM, int R, int NU, int WPB, int KS>
+template <int F, int TM, int R, int NU, int WPB, int KS, bool SEG>
 __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
   static_assert(KS == 1 || KS == WPB, "a team is one wave or the whole workgroup");
   static_assert(R * TM <= 64, "one output per lane");
@@ -177,9 +177,10 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
   auto load_job = [&](int j, RawS<F> (&buf)[R][NU]) {
     int g, c;
     job(j, g, c);
+    const RowSeg sg = row_seg<SEG>(a, g * R);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint8_t* wr = a.w + (int64_t)min(g * R + r, a.n_rows - 1) * a.row_bytes;
+      const uint8_t* wr = seg_wrow(sg, a.row_bytes, g * R + r);
 #pragma unroll
       for (int q = 0; q < NU; ++q) load_unit_s(wr, min(c * CH + lane + 64 * q, units - 1), lane, buf[r][q]);
     }
@@ -253,8 +254,9 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
         }
       const int r = lane / TM, t = lane % TM;
       const int row = g * R + r;
+      const RowSeg sg = row_seg<SEG>(a, g * R);
       if constexpr (KS == 1) {
-        if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
+        if (lane < R * TM && t < a.n_tok) seg_store(sg, t, row, outv);
       } else {
         if (lane < R * TM) red[kw * R * TM + lane] = outv;
         __syncthreads();
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
           for (int w = 0; w < KS; ++w) sum += red[w * R * TM + threadIdx.x];
           const int rr = threadIdx.x / TM, tt = threadIdx.x % TM;
           const int row2 = g * R + rr;
-          if (tt < a.n_tok && row2 < a.n_rows) a.y[(int64_t)tt * a.ldy + row2] = sum;
+          if (tt < a.n_tok) seg_store(sg, tt, row2, sum);
         }
         __syncthreads();
       }
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
 // behind them, so both latencies overlap; then it decodes, reduces with DPP
 // and stores.  XL true stages the activation buffer in LDS per workgroup
 // instead (for token counts whose fragments would not fit in registers).
-template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC = 8>
+template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC, bool SEG>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC))) void k_flat(StreamArgs a) {
   static_assert(R * TM <= 64, "one output per lane");
   constexpr int CH = 64 * NU;
@@ -297,9 +299,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   const int row0 = (blockIdx.x * WPB + wave) * R;
   const int units = a.units;
   const int nch = (units + CH - 1) / CH;
+  const RowSeg sg = row_seg<SEG>(a, row0);
   const uint8_t* wr[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
+  for (int r = 0; r < R; ++r) wr[r] = seg_wrow(sg, a.row_bytes, row0 + r);
 
   const Act gx{reinterpret_cast<const int8_t*>(a.xq), reinterpret_cast<const float*>(a.xq + a.off_d),
                reinterpret_cast<const int32_t*>(a.xq + a.off_s), a.k, a.nb};
@@ -334,6 +337,17 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   for (int q = 0; q < NU; ++q)
 #pragma unroll
     for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+  // batched launches: the residual of the lane's output, loaded right behind
+  // the weights and unconditionally (a branch around a load would wait for
+  // every load before it): with no residual the same valid address of the
+  // output is read and its value ignored
+  float rv = 0.f;
+  if constexpr (SEG) {
+    const int o_r = lane < R * TM ? lane / TM : 0, o_t = min(lane % TM, a.n_tok - 1);
+    const int o_lr = min(row0 - sg.first + o_r, sg.rows - 1);
+    const float* rp = sg.res != nullptr ? sg.res + (int64_t)o_t * sg.ldr + o_lr : sg.y + (int64_t)o_t * sg.ldy + o_lr;
+    rv = *rp;
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (XL) {
@@ -397,8 +411,9 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
       outv = lane == r * TM + t ? sv : outv;
     }
   const int r = lane / TM, t = lane % TM;
-  const int row = row0 + r;
-  if (lane < R * TM && t < a.n_tok && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = outv;
+  const int lr = row0 + r - sg.first;
+  if (lane < R * TM && t < a.n_tok && lr < sg.rows)
+    sg.y[(int64_t)t * sg.ldy + lr] = SEG && sg.res != nullptr ? outv + rv : outv;
 }
 
 // ------------------------------------------------------ multi-token kernel
@@ -422,7 +437,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
 template <int TM>
 constexpr int mt_stride() { return TM % 2 == 0 ? TM + 1 : TM; }
 
-template <int F, int TM, int R, int NU, int WPB, int KS>
+template <int F, int TM, int R, int NU, int WPB, int KS, bool SEG>
 __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
   constexpr int LPR = 16, GPW = 4;
   constexpr int STEP = LPR * NU;  // units a lane group covers per iteration
@@ -441,9 +456,11 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
   const int units = a.units, kc = a.kc, T = a.n_tok;
   const int ipc = kc / STEP;
   const int nchunk = (units + kc - 1) / kc;
+  // a workgroup's rows (at most 64, a power of two) lie in one matrix
+  const RowSeg sg = row_seg<SEG>(a, (int)blockIdx.x * TEAMS * GPW * R);
   const uint8_t* wr[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
+  for (int r = 0; r < R; ++r) wr[r] = seg_wrow(sg, a.row_bytes, row0 + r);
 
   // LDS chunk: first runs [kc][US] x 16 B | second runs [kc][US] x 16 B |
   // (d, d*s) [kc][US] x 8 B; then the team partials
@@ -553,8 +570,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         const float v = lane_group_sum<LPR>(acc[r][t]);
-        if (((r * TM + t) % LPR) == gl && t < T && row0 + r < a.n_rows)
-          a.y[(int64_t)t * a.ldy + row0 + r] = v;
+        if (((r * TM + t) % LPR) == gl && t < T) seg_store(sg, t, row0 + r, v);
       }
   } else {
     float* mine = red + ((team * KS + kw) * GPW + g) * NV;
@@ -574,7 +590,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
       for (int w = 0; w < KS; ++w) sum += red[((tm * KS + w) * GPW + gg) * NV + v];
       const int r = v / TM, t = v % TM;
       const int row = ((blockIdx.x * TEAMS + tm) * GPW + gg) * R + r;
-      if (t < T && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = sum;
+      if (t < T) seg_store(sg, t, row, sum);
     }
   }
 }
@@ -649,12 +665,15 @@ static StreamArgs stream_args(const MatvecLaunch& a) {
   sa.y = a.y;
   sa.ldy = a.ldy;
   sa.kc = 0;
+  sa.res = a.res;
+  sa.ldr = a.ldr;
+  sa.seg = a.seg;
   return sa;
 }
 
-template <int F, int TM, int R, int NU, int WPB, int KS>
-static hipError_t run_stream(const MatvecLaunch& a, hipStream_t st) {
-  auto kern = k_stream<F, TM, R, NU, WPB, KS>;
+template <int F, int TM, int R, int NU, int WPB, int KS, bool SEG>
+static hipError_t run_stream_seg(const MatvecLaunch& a, hipStream_t st) {
+  auto kern = k_stream<F, TM, R, NU, WPB, KS, SEG>;
   const size_t lds = (size_t)a.act_bytes + (size_t)KS * R * TM * 4;
   // resident workgroups per CU allowed by registers and waves, measured once
   static const int occ = [&] {
@@ -677,6 +696,14 @@ static hipError_t run_stream(const MatvecLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Every launcher instantiates its kernel twice: for one matrix and for a
+// batched launch with a segment table.
+template <int F, int TM, int R, int NU, int WPB, int KS>
+static hipError_t run_stream(const MatvecLaunch& a, hipStream_t st) {
+  return a.seg.n > 0 ? run_stream_seg<F, TM, R, NU, WPB, KS, true>(a, st)
+                     : run_stream_seg<F, TM, R, NU, WPB, KS, false>(a, st);
+}
+
 template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC = 8>
 static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
   if constexpr (!XL && TM > 4) {
@@ -687,7 +714,10 @@ static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
     const int64_t groups = (a.n_rows + R - 1) / R;
     const unsigned grid = (unsigned)((groups + WPB - 1) / WPB);
     StreamArgs sa = stream_args(a);
-    hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+    if (a.seg.n > 0)
+      hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, true>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+    else
+      hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false>), dim3(grid), dim3(64 * WPB), lds, st, sa);
     return hipGetLastError();
   }
 }
@@ -717,7 +747,10 @@ static hipError_t run_mt(const MatvecLaunch& a, hipStream_t st) {
   if (sa.kc <= 0) return hipErrorInvalidValue;
   const size_t lds = (size_t)US * sa.kc * 40 + red_bytes;
   const unsigned grid = (unsigned)((a.n_rows + RWG - 1) / RWG);
-  hipLaunchKernelGGL((k_mt<F, TM, R, NU, WPB, KS>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+  if (a.seg.n > 0)
+    hipLaunchKernelGGL((k_mt<F, TM, R, NU, WPB, KS, true>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+  else
+    hipLaunchKernelGGL((k_mt<F, TM, R, NU, WPB, KS, false>), dim3(grid), dim3(64 * WPB), lds, st, sa);
   return hipGetLastError();
 }
 

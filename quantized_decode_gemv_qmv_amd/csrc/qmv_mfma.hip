@@ -53,7 +53,7 @@ namespace qmv {
 // row.  A chunk holds ipc super-blocks, a multiple of KS, so the wave's
 // super-blocks fall into the chunks in order.  Items q = i * n_it + j are
 // loaded PF items ahead of the one computed.
-template <int F, int TM, int WPB, int KS, int PF, bool CH>
+template <int F, int TM, int WPB, int KS, int PF, bool CH, bool SEG>
 __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   constexpr int TG = mx_tg<F>();
   constexpr int NG = (TM + TG - 1) / TG;  // token groups
@@ -175,10 +175,30 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   // the wave's items (round i, super-block j of the tile), loaded PF ahead;
   // items past the end re-load the last one
   int hi = 0, hj = 0;  // next item to load
+  // batched launches: the loaded tile's matrix rows, i.e. the base of the
+  // tile's first row (clamped into its matrix) and the lane's offset from
+  // it, kept until the tile changes
+  int ltile = -1;
+  const uint8_t* lbase = a.w;
+  uint32_t loff = 0;
   auto load_next = [&](MxRaw<F>& r) {
     const int tile = min(tile0 + min(hi, max(rounds_tm - 1, 0)) * tstride, tiles - 1);
-    const uint8_t* base = a.w + (int64_t)tile * 16 * a.row_bytes;
-    const uint32_t off = (uint32_t)(min(n, a.n_rows - 1 - tile * 16) * (int)a.row_bytes);
+    const uint8_t* base;
+    uint32_t off;
+    if constexpr (SEG) {
+      if (tile != ltile) {
+        ltile = tile;
+        const RowSeg sg = row_seg<SEG>(a, tile * 16);
+        const int tb = min(tile * 16 - sg.first, sg.rows - 1);
+        lbase = sg.w + (int64_t)tb * a.row_bytes;
+        loff = (uint32_t)(min(n, sg.rows - 1 - tb) * (int)a.row_bytes);
+      }
+      base = lbase;
+      off = loff;
+    } else {
+      base = a.w + (int64_t)tile * 16 * a.row_bytes;
+      off = (uint32_t)(min(n, a.n_rows - 1 - tile * 16) * (int)a.row_bytes);
+    }
     mx_load(base, off, 8 * min(kw + hj * KS, nsb - 1), s, units, r);
     if (++hj >= n_it) {
       hj = 0;
@@ -302,14 +322,15 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
       }
     if constexpr (KS == 1) {
       const int row = tile * 16 + n;
-      if (have && row < a.n_rows) {
+      if (have) {
+        const RowSeg sg = row_seg<SEG>(a, tile * 16);
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = P2 ? g * 8 + 4 * s + r : g * 4 + r;
             const bool mine = P2 ? s < 2 : s == (g & 3);
-            if (mine && t < T) a.y[(int64_t)t * a.ldy + row] = acc[g][r];
+            if (mine && t < T) seg_store(sg, t, row, acc[g][r]);
           }
       }
     } else {
@@ -332,7 +353,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
         for (int w = 0; w < KS; ++w) sum += red[((tm * KS + w) * TMP) * 16 + rest];
         const int tl = (int)blockIdx.x * TEAMS + tm + i * tstride;  // that team's tile
         const int row = tl * 16 + nn;
-        if (tl < tiles && t < T && row < a.n_rows) a.y[(int64_t)t * a.ldy + row] = sum;
+        if (tl < tiles && t < T) seg_store(row_seg<SEG>(a, tl * 16), t, row, sum);
       }
       __syncthreads();  // the partials area is reused by the next round
     }
@@ -376,6 +397,9 @@ static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
   sa.n_tok = a.n_tok;
   sa.y = a.y;
   sa.ldy = a.ldy;
+  sa.res = a.res;
+  sa.ldr = a.ldr;
+  sa.seg = a.seg;
   const int64_t fixed = 16 + (KS > 1 ? (int64_t)WPB * TMP * 16 * 4 : 0);
   const int per_unit = (TMP * 32 + 16) + TMP * 4 * (F == FQ4_K ? 2 : 1);
   sa.kc = mx_chunk_units(a.units, per_unit, 8 * KS, kMxLdsBudget - fixed);
@@ -388,10 +412,16 @@ static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
     const int64_t per_cu = (int64_t)a.lds_per_cu / (int64_t)lds;
     const int64_t cap = (int64_t)a.cus * (per_cu < 1 ? 1 : per_cu);
     const int64_t grid = need < cap ? need : cap;
-    hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false>), dim3((unsigned)grid), dim3(64 * WPB), lds, st, sa);
+    if (a.seg.n > 0)
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false, true>), dim3((unsigned)grid), dim3(64 * WPB), lds, st, sa);
+    else
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false, false>), dim3((unsigned)grid), dim3(64 * WPB), lds, st, sa);
   } else {
     // several chunks: one row tile per team, the chunks walked once
-    hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, true>), dim3((unsigned)need), dim3(64 * WPB), lds, st, sa);
+    if (a.seg.n > 0)
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, true, true>), dim3((unsigned)need), dim3(64 * WPB), lds, st, sa);
+    else
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, true, false>), dim3((unsigned)need), dim3(64 * WPB), lds, st, sa);
   }
   return hipGetLastError();
 }

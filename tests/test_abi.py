@@ -177,3 +177,42 @@ def test_tuning_switches(L):
     assert q.variant_name(-1) is None and q.variant_name(len(q.variants())) is None
     assert q.pick_variant(1, 14336, 4096, 1) >= 0
     assert q.pick_variant(1, 14336, 4096, 17) == -1
+
+
+def test_matvec_batch_validation(L):
+    f = L.qmv_matvec_batch
+    Item = q._Item
+
+    def call(items, fmt=0, k=32, xq=FAKE, t=2):
+        arr = (Item * max(1, len(items)))(*items)
+        return f(fmt, arr, len(items), k, xq, t, None)
+
+    def it(w=FAKE, n=4, y=FAKE, ldy=4, res=None, ldr=0):
+        return Item(w, n, y, ldy, res, ldr)
+
+    base = [it(y=FAKE), it(y=FAKE + 4096)]
+    assert f(0, None, 1, 32, FAKE, 1, None) == INVALID
+    assert call([]) == INVALID
+    assert call(base, fmt=5) == INVALID
+    assert call(base, xq=None) == INVALID
+    assert call(base, t=0) == INVALID
+    assert call(base, t=17) == UNSUPPORTED
+    assert call([it(y=FAKE + 4096 * i) for i in range(9)]) == UNSUPPORTED
+    assert call([it(w=None)]) == INVALID
+    assert call([it(n=0)]) == INVALID
+    assert call([it(ldy=3)]) == INVALID
+    assert call([it(y=None)]) == INVALID
+    assert call([it(res=FAKE + 8192, ldr=3)]) == INVALID
+    assert call(base, k=48) == INVALID
+    assert call(base, fmt=1, k=32) == INVALID
+    assert call([it(w=FAKE + 8)]) == MISALIGNED
+    assert call([it(y=FAKE + 2)]) == MISALIGNED
+    assert call([it(res=FAKE + 8194, ldr=4)]) == MISALIGNED
+    assert call(base, xq=FAKE + 16) == MISALIGNED
+    # outputs: [T=2][ldy=4] of 4 columns span 32 bytes
+    assert call([it(y=FAKE), it(y=FAKE + 28)]) == INVALID      # overlapping outputs
+    assert call([it(y=FAKE, ldy=8), it(y=FAKE + 16)]) == INVALID  # interleaved rows overlap the extent
+    assert call([it(y=FAKE, res=FAKE + 16, ldr=4)]) == INVALID  # residual overlapping its own output
+    assert call([it(y=FAKE, res=FAKE + 4096, ldr=4), it(y=FAKE + 4096)]) == INVALID  # another item's output
+    assert call([it(y=FAKE, res=FAKE, ldr=8, ldy=4)]) == INVALID  # in place needs the same stride
+

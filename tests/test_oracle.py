@@ -97,6 +97,21 @@ def pin_integer_special_case():
         assert np.array_equal(y, ref.astype(np.float64)), fmt
 
 
+def pin_residual():
+    """Matvec + residual in the integer special case: y equals numpy's int64
+    W x plus the (integer-valued, distinct per output) residual exactly, and
+    the residual adds |r| to the tolerance magnitude."""
+    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768)):
+        data, w_int = _int_weights(fmt, 7, k, seed=fmt)
+        x = _int_acts(3, k, seed=fmt)
+        qs, d, s = oracle.quantize_act(x.astype(np.float32))
+        r = (np.arange(21, dtype=np.int64).reshape(3, 7) * 37 - 400)
+        y, mag = oracle.matvec(fmt, data, k, qs, d, s, residual=r.astype(np.float32))
+        y0, mag0 = oracle.matvec(fmt, data, k, qs, d, s)
+        assert np.array_equal(y, (x @ w_int.T + r).astype(np.float64)), fmt
+        assert np.array_equal(mag - mag0, np.abs(r).astype(np.float64)), fmt
+
+
 def _dense_from_fields(wf):
     n, k = wf.data.shape[0], wf.k
     if wf.fmt == synth.Q8_0:
@@ -227,7 +242,7 @@ def pin_router_topk():
     assert np.array_equal(ids2, ids) and np.allclose(w2, w, rtol=1e-15)
 
 
-PINS = [pin_act_cases, pin_act_invariants, pin_integer_special_case, pin_brute_force,
+PINS = [pin_act_cases, pin_act_invariants, pin_integer_special_case, pin_residual, pin_brute_force,
         pin_quantization_bound, pin_moe_against_dense_loop, pin_swiglu, pin_router_topk]
 
 
@@ -271,6 +286,8 @@ MUTANTS = {
     "swiglu_up_column": ("gu[r * ldg + n_ff + i]", "gu[r * ldg + i]"),
     "topk_tie_upper": ("if (best < 0 || l[e] > l[best]) best = e;  /* strict", "if (best < 0 || l[e] >= l[best]) best = e;  /* strict"),
     "softmax_unnormalized": ("w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m) / sum;\n  }\n  return 0;\n}\n\n/* The selection", "w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m);\n  }\n  return 0;\n}\n\n/* The selection"),
+    "residual_dropped": ("y[t * n_rows + n] += rv;", "y[t * n_rows + n] += 0.0;"),
+    "residual_columns_reversed": ("(double)res[t * ldr + n];", "(double)res[t * ldr + n_rows - 1 - n];"),
     "router_transposed": ("acc += (double)wr[e * k + i] * (double)x[t * ldx + i];", "acc += (double)wr[i * n_experts + e] * (double)x[t * ldx + i];"),
 }
 
