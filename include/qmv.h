@@ -23,6 +23,14 @@
  *       IQ4_XS : 136 B per 256 weights (fp16 d, u16 scales_h, u8
  *                scales_l[4], 128 B of 4-bit codebook indices),
  *                w = d * (ls_j - 32) * CB[idx]
+ *       q5_K   : 176 B per 256 weights (the q4_K header, 32 B qh, 128 B of
+ *                nibbles in the q4_K order; the fifth bit of weight 64c + i
+ *                is bit 2c of qh[i], of weight 64c + 32 + i bit 2c + 1),
+ *                w = d * sc_j * q - dmin * m_j with q in 0..31
+ *                (another K-quant of the small-batch matvecs: Castagna
+ *                Veloce page, "Kernels for the MI50"; qmv_matvec,
+ *                qmv_matvec_batch and qmv_block_dots take it,
+ *                qmv_moe_matvec does not)
  *   - All pointers except those documented as host pointers are DEVICE
  *     pointers on the current HIP device.  The caller owns every buffer; the
  *     library allocates nothing and keeps no pointer after a call returns.
@@ -51,7 +59,8 @@ extern "C" {
 typedef enum {
   QMV_Q8_0 = 0,
   QMV_Q4_K = 1,
-  QMV_IQ4_XS = 2
+  QMV_IQ4_XS = 2,
+  QMV_Q5_K = 3
 } qmv_type;
 
 typedef enum {
@@ -239,7 +248,8 @@ qmv_status qmv_matvec_batch(qmv_type type, const qmv_matvec_item* items, int64_t
  *            int32 at offset 0 holds the number of dropped slots of that call.
  * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, 1 <= top_k <= QMV_MAX_TOP_K,
  * 1 <= n_experts <= QMV_MAX_EXPERTS, n_rows <= QMV_MAX_MOE_ROWS and
- * k <= QMV_MAX_MOE_K (else QMV_ERR_UNSUPPORTED); k as for qmv_matvec.
+ * k <= QMV_MAX_MOE_K (else QMV_ERR_UNSUPPORTED); k as for qmv_matvec; type
+ * Q8_0, q4_K or IQ4_XS (q5_K: QMV_ERR_UNSUPPORTED).
  */
 size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows, int64_t k,
                                int64_t n_tok, int64_t top_k);
@@ -251,7 +261,7 @@ qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts, int64
 /*
  * qmv_block_dots -- test hook: the exact integer partial of every 32-weight
  * block, computed by the same device decode and dot routines as qmv_matvec.
- * out : int32 [n_tok][n_rows][k/32][c] (device), c = 2 for q4_K
+ * out : int32 [n_tok][n_rows][k/32][c] (device), c = 2 for q4_K and q5_K
  *       (A = sc_j * sum q*qx, B = m_j * s_b) and c = 1 otherwise
  *       (Q8_0: sum qw*qx; IQ4_XS: (ls_j - 32) * sum CB[idx]*qx).
  * 1 <= n_tok <= QMV_MAX_TOKENS.

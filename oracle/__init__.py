@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB = os.path.join(_HERE, "liboqmv.so")
 
-Q8_0, Q4_K, IQ4_XS = 0, 1, 2
+Q8_0, Q4_K, IQ4_XS, Q5_K = 0, 1, 2, 3
 _lib = None
 
 
@@ -126,12 +126,12 @@ def quantize_act(x: np.ndarray):
 
 
 def block_dots(fmt: int, w: np.ndarray, k: int, qs: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """int32 [T][N][K/32][c], c = 2 for q4_K (A, B) else 1."""
+    """int32 [T][N][K/32][c], c = 2 for q4_K and q5_K (A, B) else 1."""
     w = _w2d(fmt, w, k)
     qs = np.ascontiguousarray(qs, dtype=np.int8)
     s = np.ascontiguousarray(s, dtype=np.int32)
     t = qs.shape[0]
-    nc = 2 if fmt == Q4_K else 1
+    nc = 2 if fmt in (Q4_K, Q5_K) else 1
     out = np.zeros((t, w.shape[0], k // 32, nc), dtype=np.int32)
     _check(_load().oracle_block_dots(fmt, _p(w), w.shape[0], k, _p(qs), _p(s), t, _p(out)))
     return out

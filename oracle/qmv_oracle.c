@@ -19,7 +19,12 @@
  *     rounded), q = round-half-away-from-zero(x / d) (fp32 division) clamped to
  *     [-127, 127], s = sum of q; an all-zero block has d = 0 and q = 0;
  *   - q4_K weight  = d * sc_j * q - dmin * m_j   (the min is subtracted);
- *   - IQ4_XS weight = d * (ls_j - 32) * CB[idx]  (raw 6-bit scale minus 32).
+ *   - IQ4_XS weight = d * (ls_j - 32) * CB[idx]  (raw 6-bit scale minus 32);
+ *   - q5_K (176 B): the q4_K header (d, dmin, the same 12 bytes of 6-bit
+ *     scale/min pairs), then 32 bytes qh, then the 128 nibble bytes in the
+ *     q4_K order; weight 64c + i of chunk c takes bit 2c of qh[i] as its
+ *     fifth bit (value 16), weight 64c + 32 + i bit 2c + 1;
+ *     q5_K weight = d * sc_j * q - dmin * m_j with q in 0..31.
  *
  * Per 32-weight block b the integer partials are
  *   Q8_0  : P = sum_i qw_i qx_i
@@ -38,7 +43,10 @@
 #include <omp.h>
 #endif
 
-enum { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_IQ4_XS = 2 };
+enum { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_IQ4_XS = 2, FMT_Q5_K = 3 };
+
+/* K-quants with a per-sub-block min (q4_K, q5_K): two terms per block. */
+static int has_min(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q5_K; }
 
 /* The 16-entry non-linear int8 codebook of IQ4_XS (shared with IQ4_NL). */
 static const int IQ4_CODEBOOK[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
@@ -64,6 +72,7 @@ int64_t oracle_row_bytes(int fmt, int64_t k) {
     case FMT_Q8_0: return k % 32 ? -1 : (k / 32) * 34;
     case FMT_Q4_K: return k % 256 ? -1 : (k / 256) * 144;
     case FMT_IQ4_XS: return k % 256 ? -1 : (k / 256) * 136;
+    case FMT_Q5_K: return k % 256 ? -1 : (k / 256) * 176;
     default: return -1;
   }
 }
@@ -78,7 +87,9 @@ static void decode_q8_0(const uint8_t* b, q8_0_block* o) {
   for (int i = 0; i < 32; ++i) o->q[i] = (int8_t)b[2 + i];
 }
 
-static void decode_q4_k(const uint8_t* b, q4_k_block* o) {
+/* The 16-byte header shared by q4_K and q5_K: fp16 d, fp16 dmin and the 8
+ * packed 6-bit (scale, min) pairs. */
+static void decode_kmin_header(const uint8_t* b, q4_k_block* o) {
   o->d = half_to_double(rd16(b));
   o->dmin = half_to_double(rd16(b + 2));
   const uint8_t* S = b + 4;
@@ -90,11 +101,28 @@ static void decode_q4_k(const uint8_t* b, q4_k_block* o) {
     o->sc[j] = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
     o->m[j] = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
   }
+}
+
+static void decode_q4_k(const uint8_t* b, q4_k_block* o) {
+  decode_kmin_header(b, o);
   const uint8_t* Q = b + 16;
   for (int c = 0; c < 4; ++c)
     for (int i = 0; i < 32; ++i) {
       o->q[64 * c + i] = Q[32 * c + i] & 15;
       o->q[64 * c + 32 + i] = Q[32 * c + i] >> 4;
+    }
+}
+
+/* q5_K: the q4_K nibbles plus a fifth bit per weight from the qh bytes. */
+static void decode_q5_k(const uint8_t* b, q4_k_block* o) {
+  decode_kmin_header(b, o);
+  const uint8_t* H = b + 16;
+  const uint8_t* Q = b + 48;
+  for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 32; ++i) {
+      int lo = Q[32 * c + i] & 15, hi = Q[32 * c + i] >> 4;
+      o->q[64 * c + i] = lo + 16 * ((H[i] >> (2 * c)) & 1);
+      o->q[64 * c + 32 + i] = hi + 16 * ((H[i] >> (2 * c + 1)) & 1);
     }
 }
 
@@ -127,10 +155,13 @@ int oracle_unpack(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double* 
         d[n * (k / 32) + b] = blk.d;
         for (int i = 0; i < 32; ++i) q[n * k + 32 * b + i] = blk.q[i];
       }
-    } else if (fmt == FMT_Q4_K) {
+    } else if (has_min(fmt)) {
       for (int64_t b = 0; b < k / 256; ++b) {
         q4_k_block blk;
-        decode_q4_k(row + b * 144, &blk);
+        if (fmt == FMT_Q4_K)
+          decode_q4_k(row + b * 144, &blk);
+        else
+          decode_q5_k(row + b * 176, &blk);
         int64_t sb = n * (k / 256) + b;
         d[sb] = blk.d;
         dmin[sb] = blk.dmin;
@@ -164,10 +195,13 @@ int oracle_dequant(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double*
         decode_q8_0(row + b * 34, &blk);
         for (int i = 0; i < 32; ++i) o[32 * b + i] = blk.d * blk.q[i];
       }
-    } else if (fmt == FMT_Q4_K) {
+    } else if (has_min(fmt)) {
       for (int64_t b = 0; b < k / 256; ++b) {
         q4_k_block blk;
-        decode_q4_k(row + b * 144, &blk);
+        if (fmt == FMT_Q4_K)
+          decode_q4_k(row + b * 144, &blk);
+        else
+          decode_q5_k(row + b * 176, &blk);
         for (int i = 0; i < 256; ++i)
           o[256 * b + i] = blk.d * blk.sc[i / 32] * blk.q[i] - blk.dmin * blk.m[i / 32];
       }
@@ -219,7 +253,7 @@ int oracle_quantize_act(const float* x, int64_t ldx, int64_t n_tok, int64_t k, i
 
 /* --------------------------------------------------- per-block integer dots */
 /* Integer partials of one row against one token, for every 32-block b of K.
- * out[b*nc + 0] = P (or A for q4_K), out[b*nc + 1] = B (q4_K only). */
+ * out[b*nc + 0] = P (or A for q4_K, q5_K), out[b*nc + 1] = B (those two only). */
 static void row_block_dots(int fmt, const uint8_t* row, int64_t k, const int8_t* qx,
                            const int32_t* sx, int32_t* out) {
   if (fmt == FMT_Q8_0) {
@@ -230,10 +264,13 @@ static void row_block_dots(int fmt, const uint8_t* row, int64_t k, const int8_t*
       for (int i = 0; i < 32; ++i) p += blk.q[i] * qx[32 * b + i];
       out[b] = p;
     }
-  } else if (fmt == FMT_Q4_K) {
+  } else if (has_min(fmt)) {
     for (int64_t sb = 0; sb < k / 256; ++sb) {
       q4_k_block blk;
-      decode_q4_k(row + sb * 144, &blk);
+      if (fmt == FMT_Q4_K)
+        decode_q4_k(row + sb * 144, &blk);
+      else
+        decode_q5_k(row + sb * 176, &blk);
       for (int j = 0; j < 8; ++j) {
         int64_t b = sb * 8 + j;
         int32_t a = 0;
@@ -256,12 +293,12 @@ static void row_block_dots(int fmt, const uint8_t* row, int64_t k, const int8_t*
   }
 }
 
-/* out int32 [n_tok][n_rows][k/32][nc], nc = 2 for q4_K (A, B), else 1. */
+/* out int32 [n_tok][n_rows][k/32][nc], nc = 2 for q4_K and q5_K (A, B), else 1. */
 int oracle_block_dots(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, const int8_t* qs,
                       const int32_t* s, int64_t n_tok, int32_t* out) {
   int64_t rb = oracle_row_bytes(fmt, k);
   if (rb < 0) return -1;
-  int64_t nb = k / 32, nc = fmt == FMT_Q4_K ? 2 : 1;
+  int64_t nb = k / 32, nc = has_min(fmt) ? 2 : 1;
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < n_rows; ++n)
     for (int64_t t = 0; t < n_tok; ++t)
@@ -274,11 +311,11 @@ static void row_block_scales(int fmt, const uint8_t* row, int64_t k, double* dw,
   if (fmt == FMT_Q8_0) {
     for (int64_t b = 0; b < k / 32; ++b) dw[b] = half_to_double(rd16(row + b * 34));
   } else {
-    int64_t bb = fmt == FMT_Q4_K ? 144 : 136;
+    int64_t bb = oracle_row_bytes(fmt, 256);
     for (int64_t sb = 0; sb < k / 256; ++sb)
       for (int j = 0; j < 8; ++j) {
         dw[sb * 8 + j] = half_to_double(rd16(row + sb * bb));
-        if (fmt == FMT_Q4_K) dm[sb * 8 + j] = half_to_double(rd16(row + sb * bb + 2));
+        if (has_min(fmt)) dm[sb * 8 + j] = half_to_double(rd16(row + sb * bb + 2));
       }
   }
 }
@@ -292,7 +329,7 @@ static void row_terms(int fmt, const uint8_t* row, int64_t k, const int8_t* qx, 
   row_block_scales(fmt, row, k, dw, dm);
   double acc = 0.0, am = 0.0;
   for (int64_t b = 0; b < k / 32; ++b) {
-    if (fmt == FMT_Q4_K) {
+    if (has_min(fmt)) {
       double tp = dw[b] * (double)dx[b] * (double)ibuf[2 * b];
       double tm = -dm[b] * (double)dx[b] * (double)ibuf[2 * b + 1];
       acc += tp + tm;

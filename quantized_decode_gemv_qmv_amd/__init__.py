@@ -18,13 +18,13 @@ import re
 import torch
 
 __all__ = [
-    "Q8_0", "Q4_K", "IQ4_XS", "QmvError", "lib", "library_path", "symbols",
+    "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
     "moe_workspace_bytes", "quantize_act", "matvec", "matvec_batch", "moe_matvec", "block_dots",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
-Q8_0, Q4_K, IQ4_XS = 0, 1, 2
+Q8_0, Q4_K, IQ4_XS, Q5_K = 0, 1, 2, 3
 MAX_TOKENS = 16
 MAX_MOE_TOKENS = 64
 MAX_BATCH = 8
@@ -299,7 +299,7 @@ def block_dots(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor,
     """Exact integer partial of every 32-block: int32 [T][N][K/32][c]."""
     _need(w, torch.uint8, "w")
     _need(xq, torch.uint8, "xq")
-    nc = 2 if fmt == Q4_K else 1
+    nc = 2 if fmt in (Q4_K, Q5_K) else 1
     if out is None:
         out = torch.empty((n_tok, n_rows, k // 32, nc), dtype=torch.int32, device=w.device)
     _need(out, torch.int32, "out")

@@ -15,7 +15,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqmv.so")
-SOURCES = ["qmv_api.hip", "qmv_quant.hip", "qmv_matvec.hip", "qmv_mfma.hip", "qmv_moe.hip", "qmv_router.hip"]
+# (source, object, extra flags): the dense vector kernels are compiled once per
+# weight format so that those instantiations build in parallel
+FORMATS = {0: "q8_0", 1: "q4_k", 2: "iq4_xs", 3: "q5_k"}
+SOURCES = ([(s, os.path.splitext(s)[0], []) for s in
+            ("qmv_api.hip", "qmv_variants.hip", "qmv_quant.hip", "qmv_mfma.hip", "qmv_moe.hip", "qmv_router.hip")]
+           + [("qmv_matvec.hip", f"qmv_matvec_{n}", [f"-DQMV_MATVEC_FMT={f}"]) for f, n in FORMATS.items()])
 ARCH = os.environ.get("QMV_OFFLOAD_ARCH", "gfx950")
 
 
@@ -30,9 +35,10 @@ def flags() -> list[str]:
             "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry, extra: list[str]) -> str:
+    src, name, defs = entry
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [hipcc(), *flags(), *defs, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass warns that it does not know the packed-fp32 target feature
     noise = "'-packed-fp32-ops' is not a recognized feature"
@@ -47,7 +53,7 @@ def _compile(src: str, extra: list[str]) -> str:
 def build(extra: list[str] | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra or [])
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, 16, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -39,10 +39,19 @@ struct EnvInit {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-bool valid_type(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS; }
+bool valid_type(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS || t == QMV_Q5_K; }
 
 int64_t block_k(int t) { return t == QMV_Q8_0 ? 32 : 256; }
-int64_t block_bytes(int t) { return t == QMV_Q8_0 ? 34 : (t == QMV_Q4_K ? 144 : 136); }
+int64_t block_bytes(int t) {
+  switch (t) {
+    case QMV_Q8_0: return 34;
+    case QMV_Q4_K: return 144;
+    case QMV_IQ4_XS: return 136;
+    default: return 176;  // q5_K
+  }
+}
+// Formats the matrix-core kernels and the MoE kernels decode.
+bool has_mfma(int t) { return t != QMV_Q5_K; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -131,7 +140,9 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //     tokens), 16-wave workgroups with K split so that about 4096 waves
 //     cover the rows; otherwise the multi-token vector kernel;
 //   - 9..16 tokens: the matrix-core kernel, 8-wave workgroups with a
-//     four-deep load ring (the register budget of the 16-token tiles).
+//     four-deep load ring (the register budget of the 16-token tiles);
+//   - q5_K has no matrix-core decode: the multi-token vector kernel from
+//     three tokens.
 //   The vector multi-token kernel's LDS staging is chunked and so fits any
 //   K, which also makes it the fallback.
 int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
@@ -148,7 +159,7 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
            : nu <= 3 ? "fl_w16_r1_u3_l"
            : nu <= 7 ? "fl_w8_r1_u7_l"
                      : "fl_w4_r1_u4_g";
-  } else if (n_tok > 8) {
+  } else if (n_tok > 8 && has_mfma(type)) {
     const int64_t per = 16 * (int64_t)cus / tiles;  // waves of K split per row tile
     name = per >= 8 ? "mx_w8_k8_r4" : per >= 4 ? "mx_w8_k4_r4" : "mx_w8_k1_r4";
   } else if (type == QMV_IQ4_XS || (type == QMV_Q4_K && n_tok > 4)) {
@@ -164,6 +175,8 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
 
 int choose_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t forced = g_variant.load();
+  if (forced >= 0 && forced < kNumVariants && kVariants[forced].kind == 4 && !has_mfma(type))
+    return auto_variant(type, n_rows, k, n_tok);  // no matrix-core decode of this format
   if (forced >= 0 && forced < kNumVariants) {
     // a forced streaming variant whose staging does not fit runs the
     // lane-group kernel instead
@@ -479,7 +492,7 @@ QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, 
 // ------------------------------------------------------------------ MoE
 QMV_API size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows,
                                        int64_t k, int64_t n_tok, int64_t top_k) {
-  if (!valid_type(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
+  if (!valid_type(type) || !has_mfma(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
       n_tok > QMV_MAX_MOE_TOKENS || top_k < 1 || top_k > QMV_MAX_TOP_K || n_experts < 1 ||
       n_experts > QMV_MAX_EXPERTS || k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows)
     return 0;
@@ -497,7 +510,7 @@ QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_expert
       top_k < 1 || n_experts < 1 || (x_per_slot != 0 && x_per_slot != 1))
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_MOE_TOKENS || top_k > QMV_MAX_TOP_K || n_experts > QMV_MAX_EXPERTS ||
-      k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows)
+      k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows || !has_mfma(type))
     return QMV_ERR_UNSUPPORTED;
   if (n_experts * n_rows > INT32_MAX) return QMV_ERR_UNSUPPORTED;
   if (!aligned(xq, 256) || !aligned(ids, 4) || !aligned(y, 4) ||

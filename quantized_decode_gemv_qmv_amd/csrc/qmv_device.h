@@ -11,6 +11,8 @@
 //   q4_K   : 16 quant bytes c of sb (bytes 16c..16c+15 of the nibble area):
 //            low nibbles are weights 16h..16h+15 (h = c & 1) of sub-block
 //            j = 2 (c >> 1), high nibbles the same positions of sub-block j+1.
+//   q5_K   : as q4_K, plus the 16 qh bytes 16h..16h+15 that carry the fifth
+//            bit of those positions (bit j for sub-block j, j + 1 for j + 1).
 // So one 16-byte quant load per lane feeds one unit, and the eight lanes of a
 // super-block read its 128 quant bytes as one contiguous 128-byte span.
 // (GGUF block layouts; the pages name the formats only -- Castagna Veloce
@@ -23,12 +25,17 @@
 
 namespace qmv {
 
-enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2 };
+enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2, FQ5_K = 3 };
+
+// K-quants with a per-sub-block min (q4_K, q5_K): paired own-block form, two
+// integer partials per block.
+template <int F> constexpr bool kmin() { return F == FQ4_K || F == FQ5_K; }
 
 template <int F> struct Fmt;
 template <> struct Fmt<FQ8_0> { static constexpr int QK = 32, BB = 34, UPB = 1; };
 template <> struct Fmt<FQ4_K> { static constexpr int QK = 256, BB = 144, UPB = 8; };
 template <> struct Fmt<FIQ4_XS> { static constexpr int QK = 256, BB = 136, UPB = 8; };
+template <> struct Fmt<FQ5_K> { static constexpr int QK = 256, BB = 176, UPB = 8; };
 
 // 16- and 8-byte vectors that only promise 4-byte alignment: gfx950 global
 // loads of several dwords need dword alignment only.
@@ -100,6 +107,11 @@ template <> struct Raw<FIQ4_XS> {
   u32x4 q;    // 16 quant bytes of the unit (= one sub-block)
   u32x2 hdr;  // d | scales_h, scales_l[0..3]
 };
+template <> struct Raw<FQ5_K> {
+  u32x4 q;    // 16 nibble bytes of the unit
+  u32x4 hdr;  // the q4_K header
+  u32x4 qh;   // the 16 qh bytes of the unit's positions
+};
 
 // Unit loads take the row base and 32-bit byte offsets inside the row, so a
 // row base held in scalar registers needs no per-lane 64-bit address math.
@@ -119,6 +131,15 @@ __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ4_K>&
   const uint32_t blk = 144u * ((uint32_t)u >> 3);
   const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
   r.q = ld_w16(row + qoff);
+  r.hdr = ld_w16(row + blk);
+}
+// q5_K super-block: header (16 B) | qh (32 B) | nibbles (128 B); every piece
+// is 16-byte aligned (176 = 11 x 16).
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ5_K>& r) {
+  const uint32_t blk = 176u * ((uint32_t)u >> 3);
+  const uint32_t qoff = blk + 48 + 16 * ((uint32_t)u & 7);
+  r.q = ld_w16(row + qoff);
+  r.qh = ld_w16(row + blk + 16 + 16 * ((uint32_t)u & 1));
   r.hdr = ld_w16(row + blk);
 }
 __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FIQ4_XS>& r) {
@@ -145,6 +166,11 @@ template <> struct RawS<FIQ4_XS> {
   u32x4 q;
   uint32_t h;
 };
+template <> struct RawS<FQ5_K> {
+  u32x4 q;
+  uint32_t h;
+  u32x4 qh;
+};
 
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ8_0>& r) {
   load_unit(row, u, r.r);
@@ -154,6 +180,14 @@ __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane,
   const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
   const uint32_t hoff = blk + 4 * ((uint32_t)lane & 3);
   r.q = ld_w16(row + qoff);
+  r.h = *reinterpret_cast<const uint32_t*>(row + hoff);
+}
+__device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ5_K>& r) {
+  const uint32_t blk = 176u * ((uint32_t)u >> 3);
+  const uint32_t qoff = blk + 48 + 16 * ((uint32_t)u & 7);
+  const uint32_t hoff = blk + 4 * ((uint32_t)lane & 3);
+  r.q = ld_w16(row + qoff);
+  r.qh = ld_w16(row + blk + 16 + 16 * ((uint32_t)u & 1));
   r.h = *reinterpret_cast<const uint32_t*>(row + hoff);
 }
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FIQ4_XS>& r) {
@@ -174,6 +208,13 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
 __device__ __forceinline__ Raw<FQ4_K> expand(const RawS<FQ4_K>& s) {
   Raw<FQ4_K> r;
   r.q = s.q;
+  r.hdr = u32x4{dpp_u<0x00>(s.h), dpp_u<0x55>(s.h), dpp_u<0xAA>(s.h), dpp_u<0xFF>(s.h)};
+  return r;
+}
+__device__ __forceinline__ Raw<FQ5_K> expand(const RawS<FQ5_K>& s) {
+  Raw<FQ5_K> r;
+  r.q = s.q;
+  r.qh = s.qh;
   r.hdr = u32x4{dpp_u<0x00>(s.h), dpp_u<0x55>(s.h), dpp_u<0xAA>(s.h), dpp_u<0xFF>(s.h)};
   return r;
 }
@@ -305,21 +346,41 @@ __device__ __forceinline__ uint32_t bfe(uint32_t v, uint32_t off, uint32_t w) {
 // for both packings (no branch): the low 4 bits of the scale come from S[c]
 // (c < 4) or S[c+4], of the min from S[c+4] or the high nibble of S[c+4]; the
 // top 2 bits sit at bits 4-5 (c < 4) or 6-7 of S[c&3] and S[(c&3)+4].
-__device__ __forceinline__ void decode_own(const Raw<FQ4_K>& r, int u, int h, bool ok, DecO<FQ4_K>& o) {
+template <int F>
+__device__ __forceinline__ void decode_kmin_scales(const u32x4& hdr, int u, bool ok, DecO<F>& o) {
   const int c = u & 7;  // own sub-block inside the super-block
   const uint32_t jj = 8u * (uint32_t)(c & 3);
   const uint32_t hb = 2u * (uint32_t)(c >> 2);
-  const uint32_t s03 = r.hdr.y, s47 = r.hdr.z, s811 = r.hdr.w;
+  const uint32_t s03 = hdr.y, s47 = hdr.z, s811 = hdr.w;
   const uint32_t lo_sc = c < 4 ? s03 : s811;
   const uint32_t lo_m = c < 4 ? s47 : s811;
   const uint32_t sc = bfe(lo_sc, jj, 4) | (bfe(s03, jj + 4 + hb, 2) << 4);
   const uint32_t m = bfe(lo_m, jj + 2 * hb, 4) | (bfe(s47, jj + 4 + hb, 2) << 4);
-  const float ws = half_bits_to_float(r.hdr.x) * static_cast<float>(sc);
-  const float wm = half_bits_to_float(r.hdr.x >> 16) * static_cast<float>(m);
+  const float ws = half_bits_to_float(hdr.x) * static_cast<float>(sc);
+  const float wm = half_bits_to_float(hdr.x >> 16) * static_cast<float>(m);
   o.sc = ok ? ws : 0.f;
   o.wm = ok ? wm : 0.f;
   o.isc = static_cast<int>(sc);
   o.im = static_cast<int>(m);
+}
+// q5_K: the q4_K scales and nibbles, each weight's fifth bit from its qh byte
+// (bit j of the byte for sub-block j of the super-block).  As for q4_K, h = 0
+// makes the low nibbles (sub-block j0) the own run, h = 1 the high ones.
+__device__ __forceinline__ void decode_own(const Raw<FQ5_K>& r, int u, int h, bool ok, DecO<FQ5_K>& o) {
+  decode_kmin_scales(r.hdr, u, ok, o);
+  const uint32_t j0 = 2u * (((uint32_t)u & 7) >> 1);  // low-nibble sub-block of the unit
+  const uint32_t sh_own = 4u * (uint32_t)h, sh_par = 4u - sh_own;
+  const uint32_t b_own = j0 + (uint32_t)h, b_par = j0 + 1u - (uint32_t)h;
+  const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
+  const uint32_t hv[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.q[i] = ((v[i] >> sh_par) & 0x0F0F0F0Fu) | (((hv[i] >> b_par) & 0x01010101u) << 4);
+    o.q[4 + i] = ((v[i] >> sh_own) & 0x0F0F0F0Fu) | (((hv[i] >> b_own) & 0x01010101u) << 4);
+  }
+}
+__device__ __forceinline__ void decode_own(const Raw<FQ4_K>& r, int u, int h, bool ok, DecO<FQ4_K>& o) {
+  decode_kmin_scales(r.hdr, u, ok, o);
   // h = 0: own = low nibbles, partner = high; h = 1 the other way round
   const uint32_t sh_own = 4u * (uint32_t)h, sh_par = 4u - sh_own;
   const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
@@ -345,7 +406,7 @@ template <int F>
 __device__ __forceinline__ void load_xo(const Act& x, int row, int u, XO& o) {
   const int8_t* base = x.qs + (int64_t)row * x.k;
   const int64_t i = (int64_t)row * x.nb + u;
-  if constexpr (F == FQ4_K) {
+  if constexpr (kmin<F>()) {
     const int h = u & 1;
     o.f = ld16(base + 32 * (u ^ 1) + 16 * h);
     o.s = ld16(base + 32 * u + 16 * h);
@@ -373,7 +434,7 @@ __device__ __forceinline__ int own_first(const DecO<F>& w, const u32x4& xf) {
 }
 template <int F>
 __device__ __forceinline__ int own_pass(int a) {
-  if constexpr (F == FQ4_K) return dpp_i<DPP_XOR1>(a);  // partner's part of the own block
+  if constexpr (kmin<F>()) return dpp_i<DPP_XOR1>(a);  // partner's part of the own block
   return a;
 }
 template <int F>
@@ -388,7 +449,7 @@ __device__ __forceinline__ int own_second(const DecO<F>& w, const u32x4& xs, int
 template <int F>
 __device__ __forceinline__ float own_apply(const DecO<F>& w, int dotv, float2 p, float acc) {
   acc = fmaf(static_cast<float>(dotv), p.x * w.sc, acc);
-  if constexpr (F == FQ4_K) acc = fmaf(-w.wm, p.y, acc);
+  if constexpr (kmin<F>()) acc = fmaf(-w.wm, p.y, acc);
   return acc;
 }
 
@@ -399,7 +460,7 @@ __device__ __forceinline__ float own_apply(const DecO<F>& w, int dotv, float2 p,
 // format's rule, else the first run of unit b ^ 1 (q4_K) / b (others).
 template <int F>
 __device__ __forceinline__ void own_piece_slot(int b, int hb, int& unit, int& run) {
-  if constexpr (F == FQ4_K) {
+  if constexpr (kmin<F>()) {
     const bool second = hb == (b & 1);
     unit = second ? b : (b ^ 1);
     run = second ? 1 : 0;

@@ -158,6 +158,7 @@ inline int rows_per_wave(const Variant& v) { return (64 / v.lpr) * v.rows; }
 size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm);
 // Tuning: cap on k_stream workgroups per compute unit (0 = occupancy).
 void set_blocks_per_cu(int v);
+int blocks_per_cu();
 
 hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
                            int32_t* s, hipStream_t st);
@@ -166,6 +167,9 @@ hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_
 hipError_t launch_router_topk(const float* x, int64_t ldx, int n_tok, int k, const float* wr, int n_experts,
                               int top_k, int32_t* ids, float* w, float* logits, hipStream_t st);
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
+// The vector-ALU kernels of format F (one translation unit per format).
+template <int F>
+hipError_t launch_vector(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,
                              ActView x, int n_tok, int32_t* out, hipStream_t st);

@@ -595,35 +595,6 @@ __global__ __launch_bounds__(64 * WPB) void k_mt(StreamArgs a) {
   }
 }
 
-// Variant table.  Indices are part of the tuning interface (qmv_set_tuning).
-//   kind, lpr, rows, nu, wpb, ks, xl, name
-const Variant kVariants[] = {
-    {0, 64, 2, 0, 4, 1, 0, "lpr64_r2"},       {0, 32, 2, 0, 4, 1, 0, "lpr32_r2"},
-    {1, 64, 1, 2, 4, 1, 1, "st_w4_r1_u2"},    {1, 64, 2, 2, 4, 1, 1, "st_w4_r2_u2"},
-    {1, 64, 1, 3, 4, 1, 1, "st_w4_r1_u3"},    {1, 64, 1, 2, 16, 1, 1, "st_w16_r1_u2"},
-    {1, 64, 4, 1, 8, 1, 1, "st_w8_r4_u1"},    {1, 64, 1, 2, 16, 16, 1, "st_k16_r1_u2"},
-    {2, 64, 1, 2, 4, 1, 0, "fl_w4_r1_u2_g"},  {2, 64, 2, 2, 4, 1, 0, "fl_w4_r2_u2_g"},
-    {2, 64, 1, 3, 4, 1, 0, "fl_w4_r1_u3_g"},  {2, 64, 1, 4, 4, 1, 0, "fl_w4_r1_u4_g"},
-    {2, 64, 1, 7, 4, 1, 0, "fl_w4_r1_u7_g"},  {2, 64, 1, 2, 4, 1, 1, "fl_w4_r1_u2_l"},
-    {2, 64, 1, 2, 16, 1, 1, "fl_w16_r1_u2_l"}, {2, 64, 1, 3, 16, 1, 1, "fl_w16_r1_u3_l"},
-    {2, 64, 1, 7, 8, 1, 1, "fl_w8_r1_u7_l"},  {2, 64, 2, 2, 16, 1, 1, "fl_w16_r2_u2_l"},
-    {3, 16, 2, 1, 8, 2, 1, "mt_r2_w8_k2"},    {3, 16, 2, 1, 8, 4, 1, "mt_r2_w8_k4"},
-    {3, 16, 4, 1, 8, 2, 1, "mt_r4_w8_k2"},    {3, 16, 4, 1, 4, 1, 1, "mt_r4_w4_k1"},
-    {3, 16, 2, 1, 4, 1, 1, "mt_r2_w4_k1"},    {3, 16, 1, 1, 8, 4, 1, "mt_r1_w8_k4"},
-    {3, 16, 2, 1, 16, 8, 1, "mt_r2_w16_k8"},  {3, 16, 1, 1, 16, 8, 1, "mt_r1_w16_k8"},
-    {3, 16, 2, 2, 8, 2, 1, "mt_r2_u2_w8_k2"}, {3, 16, 2, 2, 8, 1, 1, "mt_r2_u2_w8_k1"},
-    {3, 16, 2, 2, 16, 4, 1, "mt_r2_u2_w16_k4"}, {3, 16, 1, 2, 8, 2, 1, "mt_r1_u2_w8_k2"},
-    {3, 16, 2, 4, 8, 2, 1, "mt_r2_u4_w8_k2"}, {3, 16, 2, 2, 4, 1, 1, "mt_r2_u2_w4_k1"},
-    {3, 16, 1, 2, 16, 4, 1, "mt_r1_u2_w16_k4"}, {3, 16, 1, 4, 16, 4, 1, "mt_r1_u4_w16_k4"},
-    {4, 16, 1, 2, 16, 4, 1, "mx_w16_k4_r2"},  {4, 16, 1, 2, 16, 8, 1, "mx_w16_k8_r2"},
-    {4, 16, 1, 2, 16, 16, 1, "mx_w16_k16_r2"}, {4, 16, 1, 4, 8, 1, 1, "mx_w8_k1_r4"},
-    {4, 16, 1, 4, 8, 4, 1, "mx_w8_k4_r4"},    {4, 16, 1, 4, 8, 8, 1, "mx_w8_k8_r4"},
-};
-const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
-static int g_bpc_override = 0;  // tuning: workgroups per CU cap (0 = occupancy)
-void set_blocks_per_cu(int v) { g_bpc_override = v; }
-
 template <int F, int TM, int LPR, int R>
 static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
   constexpr int RWG = 4 * (64 / LPR) * R;
@@ -641,12 +612,6 @@ static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
                        (float*)nullptr, (int*)nullptr);
   }
   return hipGetLastError();
-}
-
-size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm) {
-  if (v.kind >= 3) return 0;  // chunked to fit (kMultiLdsBudget)
-  if (v.kind == 2) return v.xl || tm > 4 ? static_cast<size_t>(act_bytes) : 0;
-  return static_cast<size_t>(act_bytes + (int64_t)v.ks * v.rows * tm * 4);
 }
 
 static StreamArgs stream_args(const MatvecLaunch& a) {
@@ -682,7 +647,7 @@ static hipError_t run_stream_seg(const MatvecLaunch& a, hipStream_t st) {
       n = 1;
     return n;
   }();
-  int bpc = g_bpc_override > 0 ? g_bpc_override : occ;
+  int bpc = blocks_per_cu() > 0 ? blocks_per_cu() : occ;
   const int by_lds = (int)((size_t)a.lds_per_cu / (lds > 0 ? lds : 1));
   if (bpc > by_lds) bpc = by_lds;
   if (bpc < 1) bpc = 1;
@@ -725,7 +690,7 @@ static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
 // Units per LDS chunk of the multi-token kernel: as many as fit the budget,
 // a multiple of the units one iteration covers (and of 8, one super-block),
 // balanced over the chunks the row needs.
-int multi_chunk_units(int units, int n_tok, int step, int64_t lds_budget) {
+static int multi_chunk_units(int units, int n_tok, int step, int64_t lds_budget) {
   const int per_unit = n_tok * 40;  // 32 quant bytes + scale + sum per token
   const int lcm = step % 8 == 0 ? step : step * 8;
   int kmax = (int)(lds_budget / per_unit) / lcm * lcm;
@@ -804,14 +769,15 @@ static hipError_t run_mv_tokens(const MatvecLaunch& a, hipStream_t st) {
   return run_mv_variant<F, 16>(a, st);
 }
 
-hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st) {
-  if (kVariants[a.variant].kind == 4) return launch_mx(a, st);
-  switch (a.fmt) {
-    case FQ8_0: return run_mv_tokens<FQ8_0>(a, st);
-    case FQ4_K: return run_mv_tokens<FQ4_K>(a, st);
-    case FIQ4_XS: return run_mv_tokens<FIQ4_XS>(a, st);
-    default: return hipErrorInvalidValue;
-  }
+// This translation unit is compiled once per weight format (QMV_MATVEC_FMT),
+// so that the formats' kernels build in parallel; each copy defines the
+// vector-kernel entry of its format.
+#ifndef QMV_MATVEC_FMT
+#error "compile qmv_matvec.hip with -DQMV_MATVEC_FMT=<format id>"
+#endif
+template <>
+hipError_t launch_vector<QMV_MATVEC_FMT>(const MatvecLaunch& a, hipStream_t st) {
+  return run_mv_tokens<QMV_MATVEC_FMT>(a, st);
 }
 
 }  // namespace qmv

@@ -97,7 +97,7 @@ hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_
 // activation fetch and paired integer dot (own_first, own_pass, own_second)
 // as the matvec kernels: thread b holds unit b, whose own block is 32-block b,
 // and the threads of a pair (b even, b + 1) sit side by side in one wave
-// (K / 32 is even for q4_K, so no pair is split by a row or by the grid end).
+// (K / 32 is even for q4_K and q5_K, so no pair is split by a row or by the grid end).
 template <int F>
 __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ w, int64_t row_bytes,
                                                     int n_rows, int units, ActView xv, int n_tok,
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ 
   decode_own(raw, b, b & 1, true, dec);
   load_xo<F>(x, t, b, xo);
   const int dot = own_second(dec, xo.s, own_pass<F>(own_first(dec, xo.f)));
-  if constexpr (F == FQ4_K) {
+  if constexpr (kmin<F>()) {
     // sub-block b: scale times the integer dot, and min times the block sum
     out[2 * gid] = dec.isc * dot;
     out[2 * gid + 1] = dec.im * x.s[(int64_t)t * x.nb + b];
@@ -140,6 +140,10 @@ hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n
       break;
     case FIQ4_XS:
       hipLaunchKernelGGL(k_block_dots<FIQ4_XS>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
+                         units, x, n_tok, out);
+      break;
+    case FQ5_K:
+      hipLaunchKernelGGL(k_block_dots<FQ5_K>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
                          units, x, n_tok, out);
       break;
     default: return hipErrorInvalidValue;

@@ -37,6 +37,10 @@ layout, so this is the plain GGUF reading)
   IQ4_XS 136 B / 256 weights: fp16 d | u16 scales_h | u8 scales_l[4] | 128 B
                              nibbles (sub-block j uses bytes 16j..16j+15: low
                              nibble -> weight 32j+i, high -> weight 32j+16+i)
+  q5_K  176 B / 256 weights: the q4_K header (16 B) | 32 B qh | 128 B nibbles
+                             in the q4_K order; the fifth bit (value 16) of
+                             weight 64c+i is bit 2c of qh[i], of weight
+                             64c+32+i bit 2c+1 of qh[i]
 """
 from __future__ import annotations
 
@@ -49,16 +53,16 @@ __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "FMT_NAMES", "BLOCK_WEIGHTS", "BLOCK_BYTES",
     "row_bytes", "Stream", "stream", "draw_u64", "uniform01", "randint",
     "nibbles", "normal_f32", "scale_f16",
-    "pack_q8_0", "pack_q4_k", "pack_iq4_xs",
+    "pack_q8_0", "pack_q4_k", "pack_iq4_xs", "pack_q5_k", "Q5_K",
     "WeightFields", "make_weights", "make_x", "make_routing",
     "CONFIGS", "config",
 ]
 
 # format ids, shared by convention with the C interfaces
-Q8_0, Q4_K, IQ4_XS = 0, 1, 2
-FMT_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", IQ4_XS: "iq4_xs"}
-BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, IQ4_XS: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, IQ4_XS: 136}
+Q8_0, Q4_K, IQ4_XS, Q5_K = 0, 1, 2, 3
+FMT_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", IQ4_XS: "iq4_xs", Q5_K: "q5_K"}
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, IQ4_XS: 256, Q5_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, IQ4_XS: 136, Q5_K: 176}
 
 
 def row_bytes(fmt: int, k: int) -> int:
@@ -205,6 +209,24 @@ def pack_q4_k(d, dmin, sc, m, q) -> np.ndarray:
     return out.reshape(n, ns * 144)
 
 
+def pack_q5_k(d, dmin, sc, m, q) -> np.ndarray:
+    """d, dmin fp16 [N][S]; sc, m uint8 [N][S][8] in 0..63; q uint8 [N][K] in 0..31."""
+    n, k = q.shape
+    ns = k // 256
+    out = np.zeros((n, ns, 176), dtype=np.uint8)
+    out[:, :, 0:16] = q4_k_header(d, dmin, sc, m)
+    qq = q.astype(np.uint8).reshape(n, ns, 4, 2, 32)  # chunk c, half h, i
+    hi = (qq >> 4) & 1
+    qh = np.zeros((n, ns, 32), dtype=np.uint8)
+    for c in range(4):
+        qh |= hi[:, :, c, 0, :] << (2 * c)
+        qh |= hi[:, :, c, 1, :] << (2 * c + 1)
+    out[:, :, 16:48] = qh
+    lo = qq & 15
+    out[:, :, 48:176] = (lo[:, :, :, 0, :] | (lo[:, :, :, 1, :] << 4)).reshape(n, ns, 128)
+    return out.reshape(n, ns * 176)
+
+
 def iq4_xs_header(d, ls) -> np.ndarray:
     """First 8 bytes of each IQ4_XS super-block: fp16 d, u16 scales_h (two
     high bits per sub-block), scales_l[4] (low nibbles).  ls [N][S][8] raw."""
@@ -243,9 +265,9 @@ class WeightFields:
     data: np.ndarray                    # uint8 [rows][row_bytes]
     d: np.ndarray | None = None         # fp16 scales
     dmin: np.ndarray | None = None      # fp16 (q4_K)
-    sc: np.ndarray | None = None        # 6-bit scales (q4_K) / raw ls (IQ4_XS)
-    m: np.ndarray | None = None         # 6-bit mins (q4_K)
-    q: np.ndarray | None = None         # int8 (Q8_0) / nibbles (q4_K, IQ4_XS)
+    sc: np.ndarray | None = None        # 6-bit scales (q4_K, q5_K) / raw ls (IQ4_XS)
+    m: np.ndarray | None = None         # 6-bit mins (q4_K, q5_K)
+    q: np.ndarray | None = None         # int8 (Q8_0) / nibbles (q4_K, IQ4_XS) / 5-bit (q5_K)
 
 
 def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
@@ -256,6 +278,7 @@ def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
     Q8_0  : d ~ fp16 U[1e-3,1e-2], q ~ U{-127..127}
     q4_K  : d, dmin ~ fp16 U[1e-3,1e-2], scale and min ~ U{0..63}, q ~ U{0..15}
     IQ4_XS: d ~ fp16 U[1e-3,1e-2], raw 6-bit scale ~ U{0..63}, index ~ U{0..15}
+    q5_K  : as q4_K with q ~ U{0..31}
     """
     r0, r1 = rows if rows is not None else (0, n_rows)
     assert 0 <= r0 <= r1 <= n_rows
@@ -273,12 +296,15 @@ def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
         return wf
     ns = k // 256
     d = scale_f16(stream(name + "/d", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)
-    q = nibbles(stream(name + "/q", seed), r0 * k, n * k).reshape(n, k)
-    if fmt == Q4_K:
+    if fmt == Q5_K:
+        q = randint(stream(name + "/q", seed), r0 * k, n * k, 0, 31).astype(np.uint8).reshape(n, k)
+    else:
+        q = nibbles(stream(name + "/q", seed), r0 * k, n * k).reshape(n, k)
+    if fmt in (Q4_K, Q5_K):
         dmin = scale_f16(stream(name + "/dmin", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)
         sc = randint(stream(name + "/sc", seed), r0 * ns * 8, n * ns * 8, 0, 63).astype(np.uint8).reshape(n, ns, 8)
         m = randint(stream(name + "/m", seed), r0 * ns * 8, n * ns * 8, 0, 63).astype(np.uint8).reshape(n, ns, 8)
-        data = pack_q4_k(d, dmin, sc, m, q)
+        data = (pack_q4_k if fmt == Q4_K else pack_q5_k)(d, dmin, sc, m, q)
         wf = WeightFields(fmt, (r0, r1), k, data)
         if keep_fields:
             wf.d, wf.dmin, wf.sc, wf.m, wf.q = d, dmin, sc, m, q
@@ -330,6 +356,9 @@ CONFIGS = {
     "q8_0_splitk_256x65536": dict(fmt=Q8_0, n=256, k=65536, tokens=(1,)),
     # Q8_0 output head
     "q8_0_head_152064x5120": dict(fmt=Q8_0, n=152064, k=5120, tokens=(1, 2, 4, 8, 16)),
+    # q5_K at the q4_K FFN-up shape (a further K-quant of the same small-batch
+    # matvecs; no workload of its own)
+    "q5_k_14336x4096": dict(fmt=Q5_K, n=14336, k=4096, tokens=(1, 2, 4, 8, 16)),
 }
 
 

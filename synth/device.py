@@ -14,7 +14,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (IQ4_XS, Q4_K, Q8_0, _GAMMA, _M1, _M2, Stream, iq4_xs_header, q4_k_header,
+from . import (IQ4_XS, Q4_K, Q5_K, Q8_0, _GAMMA, _M1, _M2, Stream, iq4_xs_header, q4_k_header,
                randint, row_bytes, scale_f16, stream)
 
 __all__ = ["draw_u64", "randint_t", "nibbles_t", "make_weights_t"]
@@ -90,13 +90,24 @@ def make_weights_t(fmt: int, n_rows: int, k: int, name: str, seed: int = 0, devi
             continue
         ns = k // 256
         d = scale_f16(stream(name + "/d", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)
-        q = nibbles_t(stream(name + "/q", seed), r0 * k, n * k, device)
-        if fmt == Q4_K:
+        if fmt == Q5_K:
+            q = randint_t(stream(name + "/q", seed), r0 * k, n * k, 0, 31, device).to(torch.uint8)
+        else:
+            q = nibbles_t(stream(name + "/q", seed), r0 * k, n * k, device)
+        if fmt in (Q4_K, Q5_K):
             dmin = scale_f16(stream(name + "/dmin", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)
             sc = randint(stream(name + "/sc", seed), r0 * ns * 8, n * ns * 8, 0, 63).reshape(n, ns, 8)
             m = randint(stream(name + "/m", seed), r0 * ns * 8, n * ns * 8, 0, 63).reshape(n, ns, 8)
             hdr, hb = q4_k_header(d, dmin, sc, m), 16
             qq = q.reshape(n, ns, 4, 2, 32)   # chunk c, half h, i
+            if fmt == Q5_K:  # fifth bits -> qh (bit 2c: low half of chunk c, 2c+1: high half)
+                fifth = (qq >> 4) & 1
+                qh = torch.zeros((n, ns, 32), dtype=torch.uint8, device=device)
+                for c in range(4):
+                    qh |= fifth[:, :, c, 0, :] << (2 * c)
+                    qh |= fifth[:, :, c, 1, :] << (2 * c + 1)
+                qq = qq & 15
+                hb = 48
         elif fmt == IQ4_XS:
             ls = randint(stream(name + "/ls", seed), r0 * ns * 8, n * ns * 8, 0, 63).reshape(n, ns, 8)
             hdr, hb = iq4_xs_header(d, ls), 8
@@ -104,6 +115,10 @@ def make_weights_t(fmt: int, n_rows: int, k: int, name: str, seed: int = 0, devi
         else:
             raise ValueError(f"unknown format {fmt}")
         blk = out[r0:r1].view(n, ns, rb // ns)
-        blk[:, :, 0:hb] = torch.from_numpy(hdr).to(device)
+        if fmt == Q5_K:
+            blk[:, :, 0:16] = torch.from_numpy(hdr).to(device)
+            blk[:, :, 16:48] = qh
+        else:
+            blk[:, :, 0:hb] = torch.from_numpy(hdr).to(device)
         blk[:, :, hb:] = (qq.select(-2, 0) | (qq.select(-2, 1) << 4)).reshape(n, ns, 128)
     return out

@@ -39,7 +39,8 @@ def test_abi_version_and_status_strings(L):
 
 @pytest.mark.parametrize("fmt,k,expect", [(0, 4096, 4352), (1, 4096, 2304), (2, 14336, 7616),
                                           (0, 65536, 69632), (0, 5120, 5440), (2, 1536, 816),
-                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (3, 256, 0)])
+                                          (3, 4096, 2816), (3, 288, 0),
+                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (4, 256, 0)])
 def test_row_bytes(fmt, k, expect):
     assert q.row_bytes(fmt, k) == expect
 
@@ -59,6 +60,7 @@ def test_workspace_sizes():
     assert q.matvec_workspace_bytes(0, 256, 65536, 17) == 0
     assert q.moe_workspace_bytes(2, 128, 3072, 4096, 64, 8) >= 64 * 8 * 3072 * 4
     assert q.moe_workspace_bytes(2, 128, 3072, 4096, 65, 8) == 0
+    assert q.moe_workspace_bytes(3, 128, 3072, 4096, 4, 8) == 0  # q5_K: no MoE kernel
 
 
 def _mv(L, fmt=0, w=FAKE, n=4, k=32, xq=FAKE, t=1, y=FAKE, ldy=4, ws=None, wsb=0):
@@ -156,6 +158,7 @@ def test_moe_validation(L):
     assert call(ids=FAKE + 2) == MISALIGNED
     assert call(rw=FAKE + 1) == MISALIGNED
     assert call(wsb=ws - 1) == WORKSPACE
+    assert call(fmt=3) == UNSUPPORTED  # q5_K experts are not supported
 
 
 def test_block_dots_validation(L):
@@ -177,6 +180,16 @@ def test_tuning_switches(L):
     assert q.variant_name(-1) is None and q.variant_name(len(q.variants())) is None
     assert q.pick_variant(1, 14336, 4096, 1) >= 0
     assert q.pick_variant(1, 14336, 4096, 17) == -1
+    # q5_K has no matrix-core decode: never a matrix-core variant, even forced
+    for t in range(1, 17):
+        assert not q.variant_name(q.pick_variant(3, 14336, 4096, t)).startswith("mx_")
+    mx = [i for i, n in enumerate(q.variants()) if n.startswith("mx_")]
+    try:
+        q.set_tuning("variant", mx[0])
+        assert not q.variant_name(q.pick_variant(3, 14336, 4096, 8)).startswith("mx_")
+        assert q.variant_name(q.pick_variant(1, 14336, 4096, 8)).startswith("mx_")
+    finally:
+        q.set_tuning("variant", -1)
 
 
 def test_matvec_batch_validation(L):

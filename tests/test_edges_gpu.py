@@ -12,7 +12,7 @@ from gpu_util import assert_y, gpu, need_gpu, quantize, say, to_dev, x_host
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS]
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K]
 
 
 def _check(qmv, fmt, w, n, k, x, what):
@@ -69,7 +69,7 @@ def test_q8_0_minus_128():
     _check(qmv, synth.Q8_0, w, n, k, x, "q8_0 -128")
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS])
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q5_K])
 def test_zero_and_extreme_scales(fmt):
     qmv = need_gpu()
     n, k = 20, 1024
@@ -78,9 +78,11 @@ def test_zero_and_extreme_scales(fmt):
     d = synth.scale_f16(synth.stream(f"edge/scd/{fmt}"), 0, n * ns).reshape(n, ns)
     # raw 6-bit scales cover 0..63 (IQ4_XS 32 is an effective zero scale)
     sc = (np.arange(n * ns * 8) % 64).astype(np.uint8).reshape(n, ns, 8)
-    if fmt == synth.Q4_K:
+    if fmt == synth.Q5_K:  # 5-bit values: every fifth bit pattern
+        q = synth.randint(synth.stream(f"edge/sc5/{fmt}"), 0, n * k, 0, 31).astype(np.uint8).reshape(n, k)
+    if fmt in (synth.Q4_K, synth.Q5_K):
         m = sc[:, :, ::-1].copy()
-        w = synth.pack_q4_k(d, d, sc, m, q)
+        w = (synth.pack_q4_k if fmt == synth.Q4_K else synth.pack_q5_k)(d, d, sc, m, q)
     else:
         w = synth.pack_iq4_xs(d, sc, q)
     for t in (1, 16):

@@ -46,6 +46,26 @@ def test_hand_block_q4_k():
     assert np.array_equal(w, 1.0 * np.array(blk["sc"])[j] * q[0] - 0.5 * np.array(blk["m"])[j])
 
 
+def test_hand_block_q5_k():
+    blk = hand_blocks()["q5_k"]
+    q = np.array([[(k + k // 16) % 32 for k in range(256)]], dtype=np.uint8)
+    sc = np.array([[blk["sc"]]], dtype=np.uint8)
+    m = np.array([[blk["m"]]], dtype=np.uint8)
+    packed = synth.pack_q5_k(_f16([[blk["d"][0]]]), _f16([[blk["dmin"][0]]]), sc, m, q)
+    assert packed.tobytes() == blk["hex"]
+    f = oracle.unpack(synth.Q5_K, np.frombuffer(blk["hex"], np.uint8), 256)
+    assert f["d"][0, 0] == 1.0 and f["dmin"][0, 0] == 0.5
+    assert f["sc"][0, 0].tolist() == [int(v) for v in blk["sc"]]
+    assert f["m"][0, 0].tolist() == [int(v) for v in blk["m"]]
+    assert np.array_equal(f["q"][0], q[0])
+    w = oracle.dequant(synth.Q5_K, np.frombuffer(blk["hex"], np.uint8), 256)[0]
+    j = np.arange(256) // 32
+    assert np.array_equal(w, 1.0 * np.array(blk["sc"])[j] * q[0] - 0.5 * np.array(blk["m"])[j])
+    # the header and the nibble bytes are those of the q4_K block with q % 16
+    q4 = hand_blocks()["q4_k"]["hex"]
+    assert blk["hex"][:16] == q4[:16] and blk["hex"][48:] == q4[16:]
+
+
 def test_hand_block_iq4_xs():
     blk = hand_blocks()["iq4_xs"]
     q = _pattern_q()[None]
@@ -94,15 +114,18 @@ def test_iq4_xs_scale_packing_exhaustive():
         assert np.array_equal(synth.pack_iq4_xs(d, f["sc"].astype(np.uint8), q), data)
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS])
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q5_K])
 def test_weight_order_ramp(fmt):
     """A ramp of weight values survives pack -> oracle decode in weight order."""
     k = 512
-    q = np.array([[(7 * i + r) % 16 for i in range(k)] for r in range(3)], np.uint8)
+    span = 32 if fmt == synth.Q5_K else 16
+    q = np.array([[(7 * i + r) % span for i in range(k)] for r in range(3)], np.uint8)
     d = np.ones((3, 2), np.float16)
     sc = np.ones((3, 2, 8), np.uint8)
     if fmt == synth.Q4_K:
         data = synth.pack_q4_k(d, d, sc, sc, q)
+    elif fmt == synth.Q5_K:
+        data = synth.pack_q5_k(d, d, sc, sc, q)
     else:
         data = synth.pack_iq4_xs(d, sc, q)
     f = oracle.unpack(fmt, data, k)

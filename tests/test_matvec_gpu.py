@@ -19,8 +19,8 @@ from gpu_util import (assert_y, gpu, host_rows, need_gpu, quantize, sample_rows,
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS]
-NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs"}
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K]
+NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K"}
 
 
 def _oracle_y(fmt, w_host, k, x):
@@ -94,6 +94,7 @@ FULL = [
     ("q4_k_14336x4096", synth.Q4_K, 14336, 4096, (1, 2, 4, 8, 16)),
     ("iq4_xs_4096x14336", synth.IQ4_XS, 4096, 14336, (1, 2, 4, 8, 16)),
     ("q8_0_head_152064x5120", synth.Q8_0, 152064, 5120, (1, 2, 4, 8, 16)),
+    ("q5_k_14336x4096", synth.Q5_K, 14336, 4096, (1, 2, 4, 8, 16)),
 ]
 
 
@@ -144,7 +145,7 @@ def test_head_every_token_count_on_row_slice():
 def test_iq4_and_q4k_every_token_count_config_k(fmt):
     """Every T = 1..16 at the workload's reduction length on a row slice."""
     qmv = need_gpu()
-    k = {synth.Q8_0: 4096, synth.Q4_K: 4096, synth.IQ4_XS: 14336}[fmt]
+    k = {synth.Q8_0: 4096, synth.Q4_K: 4096, synth.IQ4_XS: 14336, synth.Q5_K: 4096}[fmt]
     n = 700
     w = synth.make_weights(fmt, n, k, f"tk/{fmt}").data
     wd = to_dev(w)
@@ -170,7 +171,7 @@ def test_output_stride_leaves_padding():
 
 
 def test_reuses_one_activation_buffer_across_formats():
-    """One Q8 activation buffer serves all three weight types."""
+    """One Q8 activation buffer serves every weight type."""
     qmv = need_gpu()
     k, t = 4096, 3
     x = x_host(t, k, "reuse/x")

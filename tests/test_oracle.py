@@ -70,9 +70,12 @@ def _int_weights(fmt, n, k, seed):
     sc = synth.randint(synth.stream("isc", seed), 0, n * ns * 8, 0, 63).reshape(n, ns, 8)
     one = np.ones((n, ns), np.float16)
     j = np.repeat(sc, 32, axis=2).reshape(n, k)
-    if fmt == synth.Q4_K:
+    if fmt == synth.Q5_K:  # 5-bit values
+        q = synth.randint(synth.stream("iq5", seed), 0, n * k, 0, 31).reshape(n, k).astype(np.int64)
+    if fmt in (synth.Q4_K, synth.Q5_K):
         m = synth.randint(synth.stream("im", seed), 0, n * ns * 8, 0, 63).reshape(n, ns, 8)
-        data = synth.pack_q4_k(one, one, sc.astype(np.uint8), m.astype(np.uint8), q.astype(np.uint8))
+        pack = synth.pack_q4_k if fmt == synth.Q4_K else synth.pack_q5_k
+        data = pack(one, one, sc.astype(np.uint8), m.astype(np.uint8), q.astype(np.uint8))
         return data, j * q - np.repeat(m, 32, axis=2).reshape(n, k)
     data = synth.pack_iq4_xs(one, sc.astype(np.uint8), q.astype(np.uint8))
     return data, (j - 32) * CB[q]
@@ -87,7 +90,7 @@ def _int_acts(t, k, seed):
 
 
 def pin_integer_special_case():
-    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768)):
+    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512)):
         data, w_int = _int_weights(fmt, 7, k, seed=fmt)
         x = _int_acts(3, k, seed=fmt)
         qs, d, s = oracle.quantize_act(x.astype(np.float32))
@@ -101,7 +104,7 @@ def pin_residual():
     """Matvec + residual in the integer special case: y equals numpy's int64
     W x plus the (integer-valued, distinct per output) residual exactly, and
     the residual adds |r| to the tolerance magnitude."""
-    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768)):
+    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512)):
         data, w_int = _int_weights(fmt, 7, k, seed=fmt)
         x = _int_acts(3, k, seed=fmt)
         qs, d, s = oracle.quantize_act(x.astype(np.float32))
@@ -118,7 +121,7 @@ def _dense_from_fields(wf):
         return np.repeat(wf.d.astype(np.float64), 32, axis=1) * wf.q.astype(np.float64)
     d = np.repeat(wf.d.astype(np.float64), 256, axis=1)
     sc = np.repeat(wf.sc.astype(np.float64), 32, axis=2).reshape(n, k)
-    if wf.fmt == synth.Q4_K:
+    if wf.fmt in (synth.Q4_K, synth.Q5_K):
         dmin = np.repeat(wf.dmin.astype(np.float64), 256, axis=1)
         m = np.repeat(wf.m.astype(np.float64), 32, axis=2).reshape(n, k)
         return d * sc * wf.q - dmin * m
@@ -127,7 +130,7 @@ def _dense_from_fields(wf):
 
 def pin_brute_force():
     for fmt, k in ((synth.Q8_0, 32), (synth.Q8_0, 256), (synth.Q4_K, 256), (synth.Q4_K, 512),
-                   (synth.IQ4_XS, 256), (synth.IQ4_XS, 512)):
+                   (synth.IQ4_XS, 256), (synth.IQ4_XS, 512), (synth.Q5_K, 256), (synth.Q5_K, 512)):
         wf = synth.make_weights(fmt, 8, k, f"bf{fmt}", keep_fields=True)
         x = synth.make_x(3, k, f"bfx{fmt}")
         qs, d, s = oracle.quantize_act(x)
@@ -140,7 +143,7 @@ def pin_brute_force():
 
 
 def pin_quantization_bound():
-    for fmt, k in ((synth.Q8_0, 512), (synth.Q4_K, 1024), (synth.IQ4_XS, 1024)):
+    for fmt, k in ((synth.Q8_0, 512), (synth.Q4_K, 1024), (synth.IQ4_XS, 1024), (synth.Q5_K, 1024)):
         wf = synth.make_weights(fmt, 6, k, f"qb{fmt}", keep_fields=True)
         x = synth.make_x(2, k, f"qbx{fmt}")
         qs, d, s = oracle.quantize_act(x)
@@ -273,6 +276,8 @@ MUTANTS = {
     "min_dropped": ("acc += tp + tm;", "acc += tp;"),
     "q4k_nibble_swap": ("o->q[64 * c + i] = Q[32 * c + i] & 15;", "o->q[64 * c + i] = Q[32 * c + i] >> 4;"),
     "q4k_scale_hi_bits": ("((S[j - 4] >> 6) << 4)", "((S[j] >> 6) << 4)"),
+    "q5k_high_bit_swapped": ("16 * ((H[i] >> (2 * c)) & 1);", "16 * ((H[i] >> (2 * c + 1)) & 1);"),
+    "q5k_high_bit_dropped": ("hi + 16 * ((H[i] >> (2 * c + 1)) & 1);", "hi;"),
     "iq4_offset": ("(blk.ls[j] - 32) * p", "(blk.ls[j] - 31) * p"),
     "iq4_scales_h": ("(((sh >> (2 * j)) & 3) << 4)", "(((sh >> j) & 3) << 4)"),
     "iq4_nibble_half": ("o->idx[32 * j + 16 + i] = Q[16 * j + i] >> 4;", "o->idx[32 * j + 16 + i] = Q[16 * j + i] & 15;"),
