@@ -31,6 +31,13 @@
  *                Veloce page, "Kernels for the MI50"; qmv_matvec,
  *                qmv_matvec_batch and qmv_block_dots take it,
  *                qmv_moe_matvec does not)
+ *       q6_K   : 210 B per 256 weights (128 B ql, 64 B qh, int8 scales[16],
+ *                fp16 d); weight 128h + 32j + l (half h, quarter j, l < 32)
+ *                stores q = nibble of ql[64h + 32(j & 1) + l] (low for j < 2)
+ *                + 16 * bits 2j..2j+1 of qh[32h + l], and
+ *                w = d * scales[(128h + 32j + l) / 16] * (q - 32)
+ *                (same page and entry points as q5_K; blocks are 210 B, so
+ *                rows need not be 4-byte aligned: only the base pointer is)
  *   - All pointers except those documented as host pointers are DEVICE
  *     pointers on the current HIP device.  The caller owns every buffer; the
  *     library allocates nothing and keeps no pointer after a call returns.
@@ -60,7 +67,8 @@ typedef enum {
   QMV_Q8_0 = 0,
   QMV_Q4_K = 1,
   QMV_IQ4_XS = 2,
-  QMV_Q5_K = 3
+  QMV_Q5_K = 3,
+  QMV_Q6_K = 4
 } qmv_type;
 
 typedef enum {
@@ -249,7 +257,7 @@ qmv_status qmv_matvec_batch(qmv_type type, const qmv_matvec_item* items, int64_t
  * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, 1 <= top_k <= QMV_MAX_TOP_K,
  * 1 <= n_experts <= QMV_MAX_EXPERTS, n_rows <= QMV_MAX_MOE_ROWS and
  * k <= QMV_MAX_MOE_K (else QMV_ERR_UNSUPPORTED); k as for qmv_matvec; type
- * Q8_0, q4_K or IQ4_XS (q5_K: QMV_ERR_UNSUPPORTED).
+ * Q8_0, q4_K or IQ4_XS (q5_K, q6_K: QMV_ERR_UNSUPPORTED).
  */
 size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows, int64_t k,
                                int64_t n_tok, int64_t top_k);
@@ -263,6 +271,7 @@ qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts, int64
  * block, computed by the same device decode and dot routines as qmv_matvec.
  * out : int32 [n_tok][n_rows][k/32][c] (device), c = 2 for q4_K and q5_K
  *       (A = sc_j * sum q*qx, B = m_j * s_b) and c = 1 otherwise
+ *       (q6_K: sum over the block of scales[i/16] * (q_i - 32) * qx_i)
  *       (Q8_0: sum qw*qx; IQ4_XS: (ls_j - 32) * sum CB[idx]*qx).
  * 1 <= n_tok <= QMV_MAX_TOKENS.
  */

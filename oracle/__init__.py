@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB = os.path.join(_HERE, "liboqmv.so")
 
-Q8_0, Q4_K, IQ4_XS, Q5_K = 0, 1, 2, 3
+Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K = 0, 1, 2, 3, 4
 _lib = None
 
 
@@ -98,7 +98,8 @@ def unpack(fmt: int, w: np.ndarray, k: int) -> dict:
     nsb = k // 32 if fmt == Q8_0 else k // 256
     d = np.zeros((n, nsb))
     dmin = np.zeros((n, nsb))
-    sc = np.zeros((n, nsb, 8), dtype=np.int32)
+    nsc = 16 if fmt == Q6_K else 8  # q6_K: one scale per 16 weights
+    sc = np.zeros((n, nsb, nsc), dtype=np.int32)
     m = np.zeros((n, nsb, 8), dtype=np.int32)
     q = np.zeros((n, k), dtype=np.int32)
     _check(_load().oracle_unpack(fmt, _p(w), n, k, _p(d), _p(dmin), _p(sc), _p(m), _p(q)))

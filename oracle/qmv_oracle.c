@@ -24,7 +24,13 @@
  *     scale/min pairs), then 32 bytes qh, then the 128 nibble bytes in the
  *     q4_K order; weight 64c + i of chunk c takes bit 2c of qh[i] as its
  *     fifth bit (value 16), weight 64c + 32 + i bit 2c + 1;
- *     q5_K weight = d * sc_j * q - dmin * m_j with q in 0..31.
+ *     q5_K weight = d * sc_j * q - dmin * m_j with q in 0..31;
+ *   - q6_K (210 B): 128 B ql, 64 B qh, 16 int8 scales, fp16 d; weight
+ *     128h + 32j + l (half h, quarter j, l < 32) stores the 6-bit value
+ *     q = (nibble of ql[64h + 32(j & 1) + l], low for j < 2, high otherwise)
+ *         + 16 * (bits 2j..2j+1 of qh[32h + l]),
+ *     and weight i of the super-block is d * scales[i / 16] * (q - 32).
+ *     Its integer partial per 32-block is P = sum_i scales[i/16] (q_i - 32) qx_i.
  *
  * Per 32-weight block b the integer partials are
  *   Q8_0  : P = sum_i qw_i qx_i
@@ -43,7 +49,7 @@
 #include <omp.h>
 #endif
 
-enum { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_IQ4_XS = 2, FMT_Q5_K = 3 };
+enum { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_IQ4_XS = 2, FMT_Q5_K = 3, FMT_Q6_K = 4 };
 
 /* K-quants with a per-sub-block min (q4_K, q5_K): two terms per block. */
 static int has_min(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q5_K; }
@@ -73,6 +79,7 @@ int64_t oracle_row_bytes(int fmt, int64_t k) {
     case FMT_Q4_K: return k % 256 ? -1 : (k / 256) * 144;
     case FMT_IQ4_XS: return k % 256 ? -1 : (k / 256) * 136;
     case FMT_Q5_K: return k % 256 ? -1 : (k / 256) * 176;
+    case FMT_Q6_K: return k % 256 ? -1 : (k / 256) * 210;
     default: return -1;
   }
 }
@@ -81,6 +88,7 @@ int64_t oracle_row_bytes(int fmt, int64_t k) {
 typedef struct { double d; int q[32]; } q8_0_block;
 typedef struct { double d, dmin; int sc[8], m[8], q[256]; } q4_k_block;
 typedef struct { double d; int ls[8], idx[256]; } iq4_xs_block;
+typedef struct { double d; int sc[16], q[256]; } q6_k_block;  /* q: stored 0..63 */
 
 static void decode_q8_0(const uint8_t* b, q8_0_block* o) {
   o->d = half_to_double(rd16(b));
@@ -126,6 +134,20 @@ static void decode_q5_k(const uint8_t* b, q4_k_block* o) {
     }
 }
 
+static void decode_q6_k(const uint8_t* b, q6_k_block* o) {
+  const uint8_t* L = b;
+  const uint8_t* H = b + 128;
+  for (int i = 0; i < 16; ++i) o->sc[i] = (int8_t)b[192 + i];
+  o->d = half_to_double(rd16(b + 208));
+  for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < 4; ++j)
+      for (int l = 0; l < 32; ++l) {
+        int nib = (L[64 * h + 32 * (j & 1) + l] >> (4 * (j >> 1))) & 15;
+        int two = (H[32 * h + l] >> (2 * j)) & 3;
+        o->q[128 * h + 32 * j + l] = nib + 16 * two;
+      }
+}
+
 static void decode_iq4_xs(const uint8_t* b, iq4_xs_block* o) {
   o->d = half_to_double(rd16(b));
   int sh = rd16(b + 2);
@@ -140,6 +162,7 @@ static void decode_iq4_xs(const uint8_t* b, iq4_xs_block* o) {
 }
 
 /* Fields of every block of n_rows rows.  Q8_0: d[N][K/32], q[N][K].
+ * q6_K: d [N][K/256], sc [N][K/256][16] (int8 scales), q [N][K] (0..63).
  * q4_K: d, dmin [N][K/256], sc, m [N][K/256][8], q[N][K] (0..15).
  * IQ4_XS: d [N][K/256], sc = raw ls [N][K/256][8], q = idx [N][K]. */
 int oracle_unpack(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double* d, double* dmin,
@@ -166,6 +189,15 @@ int oracle_unpack(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double* 
         d[sb] = blk.d;
         dmin[sb] = blk.dmin;
         for (int j = 0; j < 8; ++j) { sc[sb * 8 + j] = blk.sc[j]; m[sb * 8 + j] = blk.m[j]; }
+        for (int i = 0; i < 256; ++i) q[n * k + 256 * b + i] = blk.q[i];
+      }
+    } else if (fmt == FMT_Q6_K) {
+      for (int64_t b = 0; b < k / 256; ++b) {
+        q6_k_block blk;
+        decode_q6_k(row + b * 210, &blk);
+        int64_t sb = n * (k / 256) + b;
+        d[sb] = blk.d;
+        for (int j = 0; j < 16; ++j) sc[sb * 16 + j] = blk.sc[j];
         for (int i = 0; i < 256; ++i) q[n * k + 256 * b + i] = blk.q[i];
       }
     } else {
@@ -204,6 +236,12 @@ int oracle_dequant(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double*
           decode_q5_k(row + b * 176, &blk);
         for (int i = 0; i < 256; ++i)
           o[256 * b + i] = blk.d * blk.sc[i / 32] * blk.q[i] - blk.dmin * blk.m[i / 32];
+      }
+    } else if (fmt == FMT_Q6_K) {
+      for (int64_t b = 0; b < k / 256; ++b) {
+        q6_k_block blk;
+        decode_q6_k(row + b * 210, &blk);
+        for (int i = 0; i < 256; ++i) o[256 * b + i] = blk.d * blk.sc[i / 16] * (blk.q[i] - 32);
       }
     } else {
       for (int64_t b = 0; b < k / 256; ++b) {
@@ -279,6 +317,20 @@ static void row_block_dots(int fmt, const uint8_t* row, int64_t k, const int8_t*
         out[2 * b + 1] = blk.m[j] * sx[b];
       }
     }
+  } else if (fmt == FMT_Q6_K) {
+    for (int64_t sb = 0; sb < k / 256; ++sb) {
+      q6_k_block blk;
+      decode_q6_k(row + sb * 210, &blk);
+      for (int j = 0; j < 8; ++j) {
+        int64_t b = sb * 8 + j;
+        int32_t p = 0;
+        for (int i = 0; i < 32; ++i) {
+          int w = 32 * j + i;
+          p += blk.sc[w / 16] * (blk.q[w] - 32) * qx[32 * b + i];
+        }
+        out[b] = p;
+      }
+    }
   } else {
     for (int64_t sb = 0; sb < k / 256; ++sb) {
       iq4_xs_block blk;
@@ -312,9 +364,10 @@ static void row_block_scales(int fmt, const uint8_t* row, int64_t k, double* dw,
     for (int64_t b = 0; b < k / 32; ++b) dw[b] = half_to_double(rd16(row + b * 34));
   } else {
     int64_t bb = oracle_row_bytes(fmt, 256);
+    int64_t d_at = fmt == FMT_Q6_K ? 208 : 0;  /* q6_K keeps d at the end */
     for (int64_t sb = 0; sb < k / 256; ++sb)
       for (int j = 0; j < 8; ++j) {
-        dw[sb * 8 + j] = half_to_double(rd16(row + sb * bb));
+        dw[sb * 8 + j] = half_to_double(rd16(row + sb * bb + d_at));
         if (has_min(fmt)) dm[sb * 8 + j] = half_to_double(rd16(row + sb * bb + 2));
       }
   }

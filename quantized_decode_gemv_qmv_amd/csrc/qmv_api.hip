@@ -39,7 +39,9 @@ struct EnvInit {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-bool valid_type(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS || t == QMV_Q5_K; }
+bool valid_type(int t) {
+  return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS || t == QMV_Q5_K || t == QMV_Q6_K;
+}
 
 int64_t block_k(int t) { return t == QMV_Q8_0 ? 32 : 256; }
 int64_t block_bytes(int t) {
@@ -47,11 +49,12 @@ int64_t block_bytes(int t) {
     case QMV_Q8_0: return 34;
     case QMV_Q4_K: return 144;
     case QMV_IQ4_XS: return 136;
-    default: return 176;  // q5_K
+    case QMV_Q5_K: return 176;
+    default: return 210;  // q6_K
   }
 }
 // Formats the matrix-core kernels and the MoE kernels decode.
-bool has_mfma(int t) { return t != QMV_Q5_K; }
+bool has_mfma(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -141,8 +144,8 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //     cover the rows; otherwise the multi-token vector kernel;
 //   - 9..16 tokens: the matrix-core kernel, 8-wave workgroups with a
 //     four-deep load ring (the register budget of the 16-token tiles);
-//   - q5_K has no matrix-core decode: the multi-token vector kernel from
-//     three tokens.
+//   - q5_K and q6_K have no matrix-core decode: the multi-token vector
+//     kernel from three tokens.
 //   The vector multi-token kernel's LDS staging is chunked and so fits any
 //   K, which also makes it the fallback.
 int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {

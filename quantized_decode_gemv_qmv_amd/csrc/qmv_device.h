@@ -13,6 +13,10 @@
 //            j = 2 (c >> 1), high nibbles the same positions of sub-block j+1.
 //   q5_K   : as q4_K, plus the 16 qh bytes 16h..16h+15 that carry the fifth
 //            bit of those positions (bit j for sub-block j, j + 1 for j + 1).
+//   q6_K   : 32-block u (half f = (u & 7) >> 2, quarter j = u & 3) and its
+//            partner u ^ 2 take the low and high nibbles of the same 32 ql
+//            bytes; the unit holds positions 16h..16h+15, h = (u >> 1) & 1,
+//            of both: 16 ql bytes and the 16 qh bytes of those positions.
 // So one 16-byte quant load per lane feeds one unit, and the eight lanes of a
 // super-block read its 128 quant bytes as one contiguous 128-byte span.
 // (GGUF block layouts; the pages name the formats only -- Castagna Veloce
@@ -25,17 +29,21 @@
 
 namespace qmv {
 
-enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2, FQ5_K = 3 };
+enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2, FQ5_K = 3, FQ6_K = 4 };
 
 // K-quants with a per-sub-block min (q4_K, q5_K): paired own-block form, two
 // integer partials per block.
 template <int F> constexpr bool kmin() { return F == FQ4_K || F == FQ5_K; }
+// Formats whose unit pairs lanes u and u ^ 1 (the K-quants with a min) or
+// u and u ^ 2 (q6_K); the others hold a whole 32-block per lane.
+template <int F> constexpr int pair_xor() { return kmin<F>() ? 1 : (F == FQ6_K ? 2 : 0); }
 
 template <int F> struct Fmt;
 template <> struct Fmt<FQ8_0> { static constexpr int QK = 32, BB = 34, UPB = 1; };
 template <> struct Fmt<FQ4_K> { static constexpr int QK = 256, BB = 144, UPB = 8; };
 template <> struct Fmt<FIQ4_XS> { static constexpr int QK = 256, BB = 136, UPB = 8; };
 template <> struct Fmt<FQ5_K> { static constexpr int QK = 256, BB = 176, UPB = 8; };
+template <> struct Fmt<FQ6_K> { static constexpr int QK = 256, BB = 210, UPB = 8; };
 
 // 16- and 8-byte vectors that only promise 4-byte alignment: gfx950 global
 // loads of several dwords need dword alignment only.
@@ -112,6 +120,11 @@ template <> struct Raw<FQ5_K> {
   u32x4 hdr;  // the q4_K header
   u32x4 qh;   // the 16 qh bytes of the unit's positions
 };
+template <> struct Raw<FQ6_K> {
+  u32x4 ql, qh;        // the 16 ql and 16 qh bytes of the unit's positions
+  int sc_own, sc_par;  // int8 scales of those positions in the own and partner block
+  uint32_t d;          // fp16 bits of the super-block scale
+};
 
 // Unit loads take the row base and 32-bit byte offsets inside the row, so a
 // row base held in scalar registers needs no per-lane 64-bit address math.
@@ -132,6 +145,31 @@ __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ4_K>&
   const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
   r.q = ld_w16(row + qoff);
   r.hdr = ld_w16(row + blk);
+}
+// 16 bytes at byte offset off of a row whose base is 16-byte aligned, where
+// row + off may be 2 mod 4 (q6_K blocks are 210 bytes): five dwords from the
+// aligned address at or below it, realigned.  A q6_K ql or qh piece ends at
+// least 18 bytes before its block's end, and a piece at 2 mod 4 starts at
+// least 2 bytes after the row base, so both extra bytes read stay in the row.
+__device__ __forceinline__ u32x4 ld16_a2(const uint8_t* row, uint32_t off) {
+  const uint8_t* p = row + off;
+  const uint32_t sh = (uint32_t)reinterpret_cast<uintptr_t>(p) & 3u;  // 0 or 2
+  const uint8_t* a = p - sh;
+  const u32x4 v = ld_w16(a);
+  const uint32_t e = *reinterpret_cast<const uint32_t*>(a + 16);
+  return u32x4{__builtin_amdgcn_alignbyte(v.y, v.x, sh), __builtin_amdgcn_alignbyte(v.z, v.y, sh),
+               __builtin_amdgcn_alignbyte(v.w, v.z, sh), __builtin_amdgcn_alignbyte(e, v.w, sh)};
+}
+// q6_K super-block: ql (128 B) | qh (64 B) | int8 scales[16] | fp16 d.
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ6_K>& r) {
+  const uint32_t blk = 210u * ((uint32_t)u >> 3);
+  const uint32_t c = (uint32_t)u & 7, f = c >> 2, j = c & 3, h = (c >> 1) & 1;
+  r.ql = ld16_a2(row, blk + 64 * f + 32 * (j & 1) + 16 * h);
+  r.qh = ld16_a2(row, blk + 128 + 32 * f + 16 * h);
+  const uint32_t s_own = 8 * f + 2 * j + h;  // the partner's is s_own ^ 4
+  r.sc_own = *reinterpret_cast<const int8_t*>(row + blk + 192 + s_own);
+  r.sc_par = *reinterpret_cast<const int8_t*>(row + blk + 192 + (s_own ^ 4));
+  r.d = ld_w2(row + blk + 208);
 }
 // q5_K super-block: header (16 B) | qh (32 B) | nibbles (128 B); every piece
 // is 16-byte aligned (176 = 11 x 16).
@@ -173,6 +211,9 @@ template <> struct RawS<FQ5_K> {
 };
 
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ8_0>& r) {
+  load_unit(row, u, r.r);
+}
+__device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ6_K>& r) {
   load_unit(row, u, r.r);
 }
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ4_K>& r) {
@@ -225,6 +266,7 @@ __device__ __forceinline__ Raw<FIQ4_XS> expand(const RawS<FIQ4_XS>& s) {
   return r;
 }
 __device__ __forceinline__ Raw<FQ8_0> expand(const RawS<FQ8_0>& s) { return s.r; }
+__device__ __forceinline__ Raw<FQ6_K> expand(const RawS<FQ6_K>& s) { return s.r; }
 
 // --------------------------------------------------------------- decoding
 template <int F> struct Dec;
@@ -311,9 +353,11 @@ struct Act {
 // keep both lanes of every pair active and on units 2p, 2p+1 of one row.
 template <int F> struct DecO {
   uint32_t q[8];  // q[0..3] first run, q[4..7] second run
-  float sc;       // Q8_0: d; IQ4_XS: d * (ls - 32); q4_K: d * sc of sub-block u
-  float wm;       // q4_K: dmin * m of sub-block u (0 otherwise)
-  int isc, im;    // the integer scale (and q4_K min) of the unit, for tests
+  float sc;       // Q8_0, q6_K: d; IQ4_XS: d * (ls - 32); q4_K, q5_K: d * sc of sub-block u
+  float wm;       // q4_K, q5_K: dmin * m of sub-block u (0 otherwise)
+  int isc, im;    // the integer scale (and q4_K / q5_K min) of the unit; q6_K: the
+                  // int8 scale of the own run's 16 positions
+  int iscp;       // q6_K: the int8 scale of the first run's 16 positions
 };
 
 // Decode unit u (clamped index) for lane parity h; invalid units get zero
@@ -390,6 +434,29 @@ __device__ __forceinline__ void decode_own(const Raw<FQ4_K>& r, int u, int h, bo
     o.q[4 + i] = (v[i] >> sh_own) & 0x0F0F0F0Fu;
   }
 }
+// q6_K: the stored 6-bit values of both runs (nibble plus two qh bits, the
+// quarter's bits 2j..2j+1), minus 32 byte by byte as (v + 96) ^ 128 (no
+// carry leaves a byte: v + 96 <= 159), so each byte is the signed value
+// q - 32 in -32..31.  The int8 scales multiply the two runs' dots.
+__device__ __forceinline__ uint32_t q6_byte_values(uint32_t ql, uint32_t qh, uint32_t nsh, uint32_t hsh) {
+  const uint32_t v = ((ql >> nsh) & 0x0F0F0F0Fu) | (((qh >> hsh) & 0x03030303u) << 4);
+  return (v + 0x60606060u) ^ 0x80808080u;
+}
+__device__ __forceinline__ void decode_own(const Raw<FQ6_K>& r, int u, int, bool ok, DecO<FQ6_K>& o) {
+  const uint32_t j = (uint32_t)u & 3, jp = j ^ 2;
+  const uint32_t ql[4] = {r.ql.x, r.ql.y, r.ql.z, r.ql.w};
+  const uint32_t qh[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.q[i] = q6_byte_values(ql[i], qh[i], 4 * (jp >> 1), 2 * jp);
+    o.q[4 + i] = q6_byte_values(ql[i], qh[i], 4 * (j >> 1), 2 * j);
+  }
+  o.sc = ok ? half_bits_to_float(r.d) : 0.f;
+  o.wm = 0.f;
+  o.isc = r.sc_own;
+  o.iscp = r.sc_par;
+  o.im = 0;
+}
 template <int F>
 __device__ __forceinline__ void decode_own(const RawS<F>& s, int u, int h, bool ok, DecO<F>& o) {
   decode_own(expand(s), u, h, ok, o);
@@ -412,6 +479,11 @@ __device__ __forceinline__ void load_xo(const Act& x, int row, int u, XO& o) {
     o.s = ld16(base + 32 * u + 16 * h);
     const float d = x.d[i];
     o.p = make_float2(d, d * static_cast<float>(x.s[i]));
+  } else if constexpr (F == FQ6_K) {
+    const int h = (u >> 1) & 1;
+    o.f = ld16(base + 32 * (u ^ 2) + 16 * h);
+    o.s = ld16(base + 32 * u + 16 * h);
+    o.p = make_float2(x.d[i], 0.f);
   } else {
     o.f = ld16(base + 32 * u);
     o.s = ld16(base + 32 * u + 16);
@@ -430,15 +502,26 @@ __device__ __forceinline__ int own_first(const DecO<F>& w, const u32x4& xf) {
   a = dot4(w.q[0], xf.x, a);
   a = dot4(w.q[1], xf.y, a);
   a = dot4(w.q[2], xf.z, a);
-  return dot4(w.q[3], xf.w, a);
+  a = dot4(w.q[3], xf.w, a);
+  if constexpr (F == FQ6_K) a *= w.iscp;  // the partner's half, scaled for it
+  return a;
 }
 template <int F>
 __device__ __forceinline__ int own_pass(int a) {
-  if constexpr (kmin<F>()) return dpp_i<DPP_XOR1>(a);  // partner's part of the own block
+  if constexpr (pair_xor<F>() == 1) return dpp_i<DPP_XOR1>(a);  // partner's part of the own block
+  if constexpr (pair_xor<F>() == 2) return dpp_i<DPP_XOR2>(a);
   return a;
 }
 template <int F>
 __device__ __forceinline__ int own_second(const DecO<F>& w, const u32x4& xs, int a) {
+  if constexpr (F == FQ6_K) {
+    int b = 0;
+    b = dot4(w.q[4], xs.x, b);
+    b = dot4(w.q[5], xs.y, b);
+    b = dot4(w.q[6], xs.z, b);
+    b = dot4(w.q[7], xs.w, b);
+    return a + b * w.isc;
+  }
   a = dot4(w.q[4], xs.x, a);
   a = dot4(w.q[5], xs.y, a);
   a = dot4(w.q[6], xs.z, a);
@@ -455,14 +538,19 @@ __device__ __forceinline__ float own_apply(const DecO<F>& w, int dotv, float2 p,
 
 // Where the activation runs of unit u (32-block u) come from, as 16-byte
 // pieces (block b, half hb) of a token's quants: Q8_0 / IQ4_XS take (u, 0)
-// then (u, 1); q4_K takes (u ^ 1, u & 1) then (u, u & 1).  Inverted for
-// staging: piece (b, hb) is the second run of unit b if hb matches the
-// format's rule, else the first run of unit b ^ 1 (q4_K) / b (others).
+// then (u, 1); q4_K and q5_K take (u ^ 1, u & 1) then (u, u & 1); q6_K takes
+// (u ^ 2, h) then (u, h) with h = (u >> 1) & 1.  Inverted for staging: piece
+// (b, hb) is the second run of unit b if hb matches the format's rule, else
+// the first run of unit b ^ 1 (q4_K, q5_K), b ^ 2 (q6_K) or b (others).
 template <int F>
 __device__ __forceinline__ void own_piece_slot(int b, int hb, int& unit, int& run) {
   if constexpr (kmin<F>()) {
     const bool second = hb == (b & 1);
     unit = second ? b : (b ^ 1);
+    run = second ? 1 : 0;
+  } else if constexpr (F == FQ6_K) {  // unit b holds positions ((b >> 1) & 1) of b and b ^ 2
+    const bool second = hb == ((b >> 1) & 1);
+    unit = second ? b : (b ^ 2);
     run = second ? 1 : 0;
   } else {
     unit = b;

@@ -97,7 +97,8 @@ hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_
 // activation fetch and paired integer dot (own_first, own_pass, own_second)
 // as the matvec kernels: thread b holds unit b, whose own block is 32-block b,
 // and the threads of a pair (b even, b + 1) sit side by side in one wave
-// (K / 32 is even for q4_K and q5_K, so no pair is split by a row or by the grid end).
+// (K / 32 is a multiple of 8 for the 256-weight formats, so no pair or q6_K
+// quad is split by a row or by the grid end).
 template <int F>
 __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ w, int64_t row_bytes,
                                                     int n_rows, int units, ActView xv, int n_tok,
@@ -120,6 +121,8 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ 
     // sub-block b: scale times the integer dot, and min times the block sum
     out[2 * gid] = dec.isc * dot;
     out[2 * gid + 1] = dec.im * x.s[(int64_t)t * x.nb + b];
+  } else if constexpr (F == FQ6_K) {
+    out[gid] = dot;  // the 16-weight scales are applied inside the paired dot
   } else {
     out[gid] = dec.isc * dot;  // Q8_0: isc = 1; IQ4_XS: the signed sub-block scale
   }
@@ -144,6 +147,10 @@ hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n
       break;
     case FQ5_K:
       hipLaunchKernelGGL(k_block_dots<FQ5_K>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
+                         units, x, n_tok, out);
+      break;
+    case FQ6_K:
+      hipLaunchKernelGGL(k_block_dots<FQ6_K>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
                          units, x, n_tok, out);
       break;
     default: return hipErrorInvalidValue;

@@ -51,6 +51,7 @@ hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st) {
     case FQ4_K: return launch_vector<FQ4_K>(a, st);
     case FIQ4_XS: return launch_vector<FIQ4_XS>(a, st);
     case FQ5_K: return launch_vector<FQ5_K>(a, st);
+    case FQ6_K: return launch_vector<FQ6_K>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

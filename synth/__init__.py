@@ -41,6 +41,11 @@ layout, so this is the plain GGUF reading)
                              in the q4_K order; the fifth bit (value 16) of
                              weight 64c+i is bit 2c of qh[i], of weight
                              64c+32+i bit 2c+1 of qh[i]
+  q6_K  210 B / 256 weights: 128 B ql | 64 B qh | int8 scales[16] | fp16 d;
+                             weight 128h + 32j + l (half h, quarter j, l < 32)
+                             is the nibble of ql[64h + 32(j & 1) + l] (low for
+                             j < 2, high otherwise) plus 16 x bits 2j..2j+1 of
+                             qh[32h + l], minus 32, times scales[8h + 2j + l/16]
 """
 from __future__ import annotations
 
@@ -53,16 +58,16 @@ __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "FMT_NAMES", "BLOCK_WEIGHTS", "BLOCK_BYTES",
     "row_bytes", "Stream", "stream", "draw_u64", "uniform01", "randint",
     "nibbles", "normal_f32", "scale_f16",
-    "pack_q8_0", "pack_q4_k", "pack_iq4_xs", "pack_q5_k", "Q5_K",
+    "pack_q8_0", "pack_q4_k", "pack_iq4_xs", "pack_q5_k", "pack_q6_k", "Q5_K", "Q6_K",
     "WeightFields", "make_weights", "make_x", "make_routing",
     "CONFIGS", "config",
 ]
 
 # format ids, shared by convention with the C interfaces
-Q8_0, Q4_K, IQ4_XS, Q5_K = 0, 1, 2, 3
-FMT_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", IQ4_XS: "iq4_xs", Q5_K: "q5_K"}
-BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, IQ4_XS: 256, Q5_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, IQ4_XS: 136, Q5_K: 176}
+Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K = 0, 1, 2, 3, 4
+FMT_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", IQ4_XS: "iq4_xs", Q5_K: "q5_K", Q6_K: "q6_K"}
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, IQ4_XS: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, IQ4_XS: 136, Q5_K: 176, Q6_K: 210}
 
 
 def row_bytes(fmt: int, k: int) -> int:
@@ -227,6 +232,27 @@ def pack_q5_k(d, dmin, sc, m, q) -> np.ndarray:
     return out.reshape(n, ns * 176)
 
 
+def pack_q6_k(d, sc, q) -> np.ndarray:
+    """d fp16 [N][S]; sc int8 [N][S][16] (one scale per 16 weights); q uint8
+    [N][K] in 0..63 (the stored 6-bit value; the weight is sc * (q - 32))."""
+    n, k = q.shape
+    ns = k // 256
+    out = np.zeros((n, ns, 210), dtype=np.uint8)
+    qq = q.astype(np.uint8).reshape(n, ns, 2, 4, 32)  # half h, quarter j, l
+    lo, hi2 = qq & 15, qq >> 4
+    ql = np.zeros((n, ns, 2, 2, 32), dtype=np.uint8)  # half, ql run (j & 1), l
+    for j in range(4):
+        ql[:, :, :, j & 1, :] |= lo[:, :, :, j, :] << (4 * (j >> 1))
+    out[:, :, 0:128] = ql.reshape(n, ns, 128)
+    qh = np.zeros((n, ns, 2, 32), dtype=np.uint8)
+    for j in range(4):
+        qh |= hi2[:, :, :, j, :] << (2 * j)
+    out[:, :, 128:192] = qh.reshape(n, ns, 64)
+    out[:, :, 192:208] = np.asarray(sc).astype(np.int8).view(np.uint8).reshape(n, ns, 16)
+    out[:, :, 208:210] = np.ascontiguousarray(d, dtype=np.float16).view(np.uint8).reshape(n, ns, 2)
+    return out.reshape(n, ns * 210)
+
+
 def iq4_xs_header(d, ls) -> np.ndarray:
     """First 8 bytes of each IQ4_XS super-block: fp16 d, u16 scales_h (two
     high bits per sub-block), scales_l[4] (low nibbles).  ls [N][S][8] raw."""
@@ -265,9 +291,9 @@ class WeightFields:
     data: np.ndarray                    # uint8 [rows][row_bytes]
     d: np.ndarray | None = None         # fp16 scales
     dmin: np.ndarray | None = None      # fp16 (q4_K)
-    sc: np.ndarray | None = None        # 6-bit scales (q4_K, q5_K) / raw ls (IQ4_XS)
+    sc: np.ndarray | None = None        # 6-bit scales (q4_K, q5_K) / raw ls (IQ4_XS) / int8 (q6_K)
     m: np.ndarray | None = None         # 6-bit mins (q4_K, q5_K)
-    q: np.ndarray | None = None         # int8 (Q8_0) / nibbles (q4_K, IQ4_XS) / 5-bit (q5_K)
+    q: np.ndarray | None = None         # int8 (Q8_0) / nibbles (q4_K, IQ4_XS) / 5-bit (q5_K) / 6-bit (q6_K)
 
 
 def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
@@ -279,6 +305,8 @@ def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
     q4_K  : d, dmin ~ fp16 U[1e-3,1e-2], scale and min ~ U{0..63}, q ~ U{0..15}
     IQ4_XS: d ~ fp16 U[1e-3,1e-2], raw 6-bit scale ~ U{0..63}, index ~ U{0..15}
     q5_K  : as q4_K with q ~ U{0..31}
+    q6_K  : d ~ fp16 U[1e-3,1e-2], int8 scale per 16 weights ~ U{-127..127},
+            stored 6-bit q ~ U{0..63}
     """
     r0, r1 = rows if rows is not None else (0, n_rows)
     assert 0 <= r0 <= r1 <= n_rows
@@ -296,6 +324,14 @@ def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
         return wf
     ns = k // 256
     d = scale_f16(stream(name + "/d", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)
+    if fmt == Q6_K:
+        q = randint(stream(name + "/q", seed), r0 * k, n * k, 0, 63).astype(np.uint8).reshape(n, k)
+        sc = randint(stream(name + "/sc", seed), r0 * ns * 16, n * ns * 16, -127, 127).astype(np.int8).reshape(n, ns, 16)
+        data = pack_q6_k(d, sc, q)
+        wf = WeightFields(fmt, (r0, r1), k, data)
+        if keep_fields:
+            wf.d, wf.sc, wf.q = d, sc, q
+        return wf
     if fmt == Q5_K:
         q = randint(stream(name + "/q", seed), r0 * k, n * k, 0, 31).astype(np.uint8).reshape(n, k)
     else:
@@ -359,6 +395,7 @@ CONFIGS = {
     # q5_K at the q4_K FFN-up shape (a further K-quant of the same small-batch
     # matvecs; no workload of its own)
     "q5_k_14336x4096": dict(fmt=Q5_K, n=14336, k=4096, tokens=(1, 2, 4, 8, 16)),
+    "q6_k_14336x4096": dict(fmt=Q6_K, n=14336, k=4096, tokens=(1, 2, 4, 8, 16)),
 }
 
 

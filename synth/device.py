@@ -14,8 +14,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (IQ4_XS, Q4_K, Q5_K, Q8_0, _GAMMA, _M1, _M2, Stream, iq4_xs_header, q4_k_header,
-               randint, row_bytes, scale_f16, stream)
+from . import (IQ4_XS, Q4_K, Q5_K, Q6_K, Q8_0, _GAMMA, _M1, _M2, Stream, iq4_xs_header, pack_q6_k,
+               q4_k_header, randint, row_bytes, scale_f16, stream)
 
 __all__ = ["draw_u64", "randint_t", "nibbles_t", "make_weights_t"]
 
@@ -90,6 +90,11 @@ def make_weights_t(fmt: int, n_rows: int, k: int, name: str, seed: int = 0, devi
             continue
         ns = k // 256
         d = scale_f16(stream(name + "/d", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)
+        if fmt == Q6_K:  # packed on the host (the quants are drawn there too)
+            q6 = randint_t(stream(name + "/q", seed), r0 * k, n * k, 0, 63, "cpu").to(torch.uint8)
+            sc = randint(stream(name + "/sc", seed), r0 * ns * 16, n * ns * 16, -127, 127).reshape(n, ns, 16)
+            out[r0:r1] = torch.from_numpy(pack_q6_k(d, sc, q6.numpy().reshape(n, k))).to(device)
+            continue
         if fmt == Q5_K:
             q = randint_t(stream(name + "/q", seed), r0 * k, n * k, 0, 31, device).to(torch.uint8)
         else:

@@ -39,8 +39,8 @@ def test_abi_version_and_status_strings(L):
 
 @pytest.mark.parametrize("fmt,k,expect", [(0, 4096, 4352), (1, 4096, 2304), (2, 14336, 7616),
                                           (0, 65536, 69632), (0, 5120, 5440), (2, 1536, 816),
-                                          (3, 4096, 2816), (3, 288, 0),
-                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (4, 256, 0)])
+                                          (3, 4096, 2816), (3, 288, 0), (4, 4096, 3360), (4, 256, 210),
+                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (5, 256, 0)])
 def test_row_bytes(fmt, k, expect):
     assert q.row_bytes(fmt, k) == expect
 
@@ -61,6 +61,7 @@ def test_workspace_sizes():
     assert q.moe_workspace_bytes(2, 128, 3072, 4096, 64, 8) >= 64 * 8 * 3072 * 4
     assert q.moe_workspace_bytes(2, 128, 3072, 4096, 65, 8) == 0
     assert q.moe_workspace_bytes(3, 128, 3072, 4096, 4, 8) == 0  # q5_K: no MoE kernel
+    assert q.moe_workspace_bytes(4, 128, 3072, 4096, 4, 8) == 0  # q6_K neither
 
 
 def _mv(L, fmt=0, w=FAKE, n=4, k=32, xq=FAKE, t=1, y=FAKE, ldy=4, ws=None, wsb=0):
@@ -159,6 +160,7 @@ def test_moe_validation(L):
     assert call(rw=FAKE + 1) == MISALIGNED
     assert call(wsb=ws - 1) == WORKSPACE
     assert call(fmt=3) == UNSUPPORTED  # q5_K experts are not supported
+    assert call(fmt=4) == UNSUPPORTED  # nor q6_K ones
 
 
 def test_block_dots_validation(L):
@@ -183,6 +185,7 @@ def test_tuning_switches(L):
     # q5_K has no matrix-core decode: never a matrix-core variant, even forced
     for t in range(1, 17):
         assert not q.variant_name(q.pick_variant(3, 14336, 4096, t)).startswith("mx_")
+        assert not q.variant_name(q.pick_variant(4, 14336, 4096, t)).startswith("mx_")
     mx = [i for i, n in enumerate(q.variants()) if n.startswith("mx_")]
     try:
         q.set_tuning("variant", mx[0])

@@ -12,7 +12,7 @@ from gpu_util import assert_y, gpu, need_gpu, quantize, say, to_dev, x_host
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K]
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K]
 
 
 def _check(qmv, fmt, w, n, k, x, what):
@@ -69,7 +69,7 @@ def test_q8_0_minus_128():
     _check(qmv, synth.Q8_0, w, n, k, x, "q8_0 -128")
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q5_K])
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K])
 def test_zero_and_extreme_scales(fmt):
     qmv = need_gpu()
     n, k = 20, 1024
@@ -78,6 +78,15 @@ def test_zero_and_extreme_scales(fmt):
     d = synth.scale_f16(synth.stream(f"edge/scd/{fmt}"), 0, n * ns).reshape(n, ns)
     # raw 6-bit scales cover 0..63 (IQ4_XS 32 is an effective zero scale)
     sc = (np.arange(n * ns * 8) % 64).astype(np.uint8).reshape(n, ns, 8)
+    if fmt == synth.Q6_K:  # every int8 scale (-128 included, never drawn) and 6-bit value
+        q6 = synth.randint(synth.stream(f"edge/sc6/{fmt}"), 0, n * k, 0, 63).astype(np.uint8).reshape(n, k)
+        sc6 = ((np.arange(n * ns * 16) % 256) - 128).astype(np.int8).reshape(n, ns, 16)
+        q6[0, :64] = 0   # q - 32 = -32 throughout a block pair
+        q6[1, :64] = 63  # q - 32 = +31
+        w = synth.pack_q6_k(d, sc6, q6)
+        for t in (1, 16):
+            _check(qmv, fmt, w, n, k, x_host(t, k, f"edge/scx/{fmt}"), "scales")
+        return
     if fmt == synth.Q5_K:  # 5-bit values: every fifth bit pattern
         q = synth.randint(synth.stream(f"edge/sc5/{fmt}"), 0, n * k, 0, 31).astype(np.uint8).reshape(n, k)
     if fmt in (synth.Q4_K, synth.Q5_K):

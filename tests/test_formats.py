@@ -66,6 +66,22 @@ def test_hand_block_q5_k():
     assert blk["hex"][:16] == q4[:16] and blk["hex"][48:] == q4[16:]
 
 
+def test_hand_block_q6_k():
+    blk = hand_blocks()["q6_k"]
+    q = np.array([[(k + k // 16) % 64 for k in range(256)]], dtype=np.uint8)
+    sc = np.array([[blk["sc"]]], dtype=np.int8)
+    packed = synth.pack_q6_k(_f16([[blk["d"][0]]]), sc, q)
+    assert packed.tobytes() == blk["hex"]
+    f = oracle.unpack(synth.Q6_K, np.frombuffer(blk["hex"], np.uint8), 256)
+    assert f["d"][0, 0] == 0.5
+    assert f["sc"][0, 0].tolist() == [int(v) for v in blk["sc"]]
+    assert np.array_equal(f["q"][0], q[0])
+    # weight = d * scales[k // 16] * (q - 32)
+    w = oracle.dequant(synth.Q6_K, np.frombuffer(blk["hex"], np.uint8), 256)[0]
+    g = np.arange(256) // 16
+    assert np.array_equal(w, 0.5 * np.array(blk["sc"])[g] * (q[0].astype(np.float64) - 32))
+
+
 def test_hand_block_iq4_xs():
     blk = hand_blocks()["iq4_xs"]
     q = _pattern_q()[None]
@@ -114,11 +130,11 @@ def test_iq4_xs_scale_packing_exhaustive():
         assert np.array_equal(synth.pack_iq4_xs(d, f["sc"].astype(np.uint8), q), data)
 
 
-@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q5_K])
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K])
 def test_weight_order_ramp(fmt):
     """A ramp of weight values survives pack -> oracle decode in weight order."""
     k = 512
-    span = 32 if fmt == synth.Q5_K else 16
+    span = {synth.Q5_K: 32, synth.Q6_K: 64}.get(fmt, 16)
     q = np.array([[(7 * i + r) % span for i in range(k)] for r in range(3)], np.uint8)
     d = np.ones((3, 2), np.float16)
     sc = np.ones((3, 2, 8), np.uint8)
@@ -126,6 +142,8 @@ def test_weight_order_ramp(fmt):
         data = synth.pack_q4_k(d, d, sc, sc, q)
     elif fmt == synth.Q5_K:
         data = synth.pack_q5_k(d, d, sc, sc, q)
+    elif fmt == synth.Q6_K:
+        data = synth.pack_q6_k(d, np.ones((3, 2, 16), np.int8), q)
     else:
         data = synth.pack_iq4_xs(d, sc, q)
     f = oracle.unpack(fmt, data, k)

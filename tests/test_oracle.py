@@ -66,6 +66,11 @@ def _int_weights(fmt, n, k, seed):
         data = synth.pack_q8_0(np.ones((n, k // 32), np.float16), q.astype(np.int8))
         return data, q
     ns = k // 256
+    if fmt == synth.Q6_K:  # int8 scale per 16 weights times (q - 32)
+        q = synth.randint(synth.stream("iq6", seed), 0, n * k, 0, 63).reshape(n, k)
+        sc = synth.randint(synth.stream("isc6", seed), 0, n * ns * 16, -127, 127).reshape(n, ns, 16)
+        data = synth.pack_q6_k(np.ones((n, ns), np.float16), sc.astype(np.int8), q.astype(np.uint8))
+        return data, np.repeat(sc, 16, axis=2).reshape(n, k) * (q - 32)
     q = synth.nibbles(synth.stream("iq", seed), 0, n * k).reshape(n, k).astype(np.int64)
     sc = synth.randint(synth.stream("isc", seed), 0, n * ns * 8, 0, 63).reshape(n, ns, 8)
     one = np.ones((n, ns), np.float16)
@@ -90,7 +95,8 @@ def _int_acts(t, k, seed):
 
 
 def pin_integer_special_case():
-    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512)):
+    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512),
+                   (synth.Q6_K, 512)):
         data, w_int = _int_weights(fmt, 7, k, seed=fmt)
         x = _int_acts(3, k, seed=fmt)
         qs, d, s = oracle.quantize_act(x.astype(np.float32))
@@ -104,7 +110,8 @@ def pin_residual():
     """Matvec + residual in the integer special case: y equals numpy's int64
     W x plus the (integer-valued, distinct per output) residual exactly, and
     the residual adds |r| to the tolerance magnitude."""
-    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512)):
+    for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512),
+                   (synth.Q6_K, 512)):
         data, w_int = _int_weights(fmt, 7, k, seed=fmt)
         x = _int_acts(3, k, seed=fmt)
         qs, d, s = oracle.quantize_act(x.astype(np.float32))
@@ -119,6 +126,9 @@ def _dense_from_fields(wf):
     n, k = wf.data.shape[0], wf.k
     if wf.fmt == synth.Q8_0:
         return np.repeat(wf.d.astype(np.float64), 32, axis=1) * wf.q.astype(np.float64)
+    if wf.fmt == synth.Q6_K:
+        g = np.repeat(wf.sc.astype(np.float64), 16, axis=2).reshape(n, k)
+        return np.repeat(wf.d.astype(np.float64), 256, axis=1) * g * (wf.q.astype(np.float64) - 32)
     d = np.repeat(wf.d.astype(np.float64), 256, axis=1)
     sc = np.repeat(wf.sc.astype(np.float64), 32, axis=2).reshape(n, k)
     if wf.fmt in (synth.Q4_K, synth.Q5_K):
@@ -130,7 +140,8 @@ def _dense_from_fields(wf):
 
 def pin_brute_force():
     for fmt, k in ((synth.Q8_0, 32), (synth.Q8_0, 256), (synth.Q4_K, 256), (synth.Q4_K, 512),
-                   (synth.IQ4_XS, 256), (synth.IQ4_XS, 512), (synth.Q5_K, 256), (synth.Q5_K, 512)):
+                   (synth.IQ4_XS, 256), (synth.IQ4_XS, 512), (synth.Q5_K, 256), (synth.Q5_K, 512),
+                   (synth.Q6_K, 256), (synth.Q6_K, 512)):
         wf = synth.make_weights(fmt, 8, k, f"bf{fmt}", keep_fields=True)
         x = synth.make_x(3, k, f"bfx{fmt}")
         qs, d, s = oracle.quantize_act(x)
@@ -143,7 +154,8 @@ def pin_brute_force():
 
 
 def pin_quantization_bound():
-    for fmt, k in ((synth.Q8_0, 512), (synth.Q4_K, 1024), (synth.IQ4_XS, 1024), (synth.Q5_K, 1024)):
+    for fmt, k in ((synth.Q8_0, 512), (synth.Q4_K, 1024), (synth.IQ4_XS, 1024), (synth.Q5_K, 1024),
+                   (synth.Q6_K, 1024)):
         wf = synth.make_weights(fmt, 6, k, f"qb{fmt}", keep_fields=True)
         x = synth.make_x(2, k, f"qbx{fmt}")
         qs, d, s = oracle.quantize_act(x)
@@ -278,6 +290,11 @@ MUTANTS = {
     "q4k_scale_hi_bits": ("((S[j - 4] >> 6) << 4)", "((S[j] >> 6) << 4)"),
     "q5k_high_bit_swapped": ("16 * ((H[i] >> (2 * c)) & 1);", "16 * ((H[i] >> (2 * c + 1)) & 1);"),
     "q5k_high_bit_dropped": ("hi + 16 * ((H[i] >> (2 * c + 1)) & 1);", "hi;"),
+    "q6k_offset": ("blk.d * blk.sc[i / 16] * (blk.q[i] - 32)", "blk.d * blk.sc[i / 16] * (blk.q[i] - 31)"),
+    "q6k_dot_offset": ("(blk.q[w] - 32) * qx[32 * b + i]", "(blk.q[w] - 31) * qx[32 * b + i]"),
+    "q6k_scale_group": ("p += blk.sc[w / 16]", "p += blk.sc[w / 32]"),
+    "q6k_high_bits": ("int two = (H[32 * h + l] >> (2 * j)) & 3;", "int two = (H[32 * h + l] >> j) & 3;"),
+    "q6k_d_offset": ("fmt == FMT_Q6_K ? 208 : 0", "fmt == FMT_Q6_K ? 206 : 0"),
     "iq4_offset": ("(blk.ls[j] - 32) * p", "(blk.ls[j] - 31) * p"),
     "iq4_scales_h": ("(((sh >> (2 * j)) & 3) << 4)", "(((sh >> j) & 3) << 4)"),
     "iq4_nibble_half": ("o->idx[32 * j + 16 + i] = Q[16 * j + i] >> 4;", "o->idx[32 * j + 16 + i] = Q[16 * j + i] & 15;"),
