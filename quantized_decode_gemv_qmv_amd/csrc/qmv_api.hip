@@ -144,8 +144,9 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //     cover the rows; otherwise the multi-token vector kernel;
 //   - 9..16 tokens: the matrix-core kernel, 8-wave workgroups with a
 //     four-deep load ring (the register budget of the 16-token tiles);
-//   - q5_K and q6_K have no matrix-core decode: the multi-token vector
-//     kernel from three tokens.
+//   - q5_K and q6_K have no matrix-core decode: from three tokens the
+//     multi-token vector kernel (q5_K, and q6_K on long rows) or the flat
+//     one (q6_K while one chunk of 128 units per lane covers the row).
 //   The vector multi-token kernel's LDS staging is chunked and so fits any
 //   K, which also makes it the fallback.
 int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
@@ -162,7 +163,14 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
            : nu <= 3 ? "fl_w16_r1_u3_l"
            : nu <= 7 ? "fl_w8_r1_u7_l"
                      : "fl_w4_r1_u4_g";
-  } else if (n_tok > 8 && has_mfma(type)) {
+  } else if (!has_mfma(type)) {
+    // q5_K, q6_K (measured on 14336 x 4096 at 3..16 tokens): q6_K keeps the
+    // flat kernel while one chunk covers the row, q5_K the multi-token one
+    if (type == QMV_Q6_K && nu <= 2)
+      name = n_tok > 8 ? "fl_w16_r1_u2_l" : n_tok > 4 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u2_l";
+    else
+      name = n_tok > 8 ? "mt_r4_w8_k2" : "mt_r2_w8_k2";
+  } else if (n_tok > 8) {
     const int64_t per = 16 * (int64_t)cus / tiles;  // waves of K split per row tile
     name = per >= 8 ? "mx_w8_k8_r4" : per >= 4 ? "mx_w8_k4_r4" : "mx_w8_k1_r4";
   } else if (type == QMV_IQ4_XS || (type == QMV_Q4_K && n_tok > 4)) {
