@@ -120,6 +120,12 @@ class Ring:
             qmv.matvec_batch(self.fmt, [(w[j], self.n, self.y[j], None) for j in range(self.mats)],
                              self.k, self.xq, self.t)
 
+    def fused(self, qmv, i):
+        """One matrix from fp32 activations: qmv_matvec_x (the matvec
+        workgroups quantize x themselves at one or two tokens)."""
+        qmv.matvec_x(self.fmt, self.w[i % self.copies][0], self.n, self.k, self.x[i % 8], xq=self.xq,
+                     y=self.y[0])
+
     def separate(self, qmv, i):
         """The sibling matrices as separate qmv_matvec launches (comparison)."""
         w = self.w[i % self.copies]
@@ -483,6 +489,9 @@ def main() -> int:
 
     kus = kernel_us(torch, qmv, ring)
     achieved = ring.weight_bytes / (kus * 1e-6) / 1e9
+    # the same step through qmv_matvec_x (fp32 activations in, quantization
+    # fused into the matvec where that is faster)
+    fused_us = timed_replays(torch, lambda i: ring.fused(qmv, i), max(ring.copies, 32)) if mats == 1 else None
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(args.workload, t, src_hash)
     # a batch of equal matrices runs the variant of their stacked rows (each
@@ -534,6 +543,8 @@ def main() -> int:
                    "matvec_variant": variant},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "matvecs_per_s": round(1e3 / ms_per_step, 1),
+        **({"matvec_x_step_us": round(fused_us, 3),
+            "matvec_x_step_GBps": round(ring.weight_bytes / (fused_us * 1e-6) / 1e9, 1)} if fused_us else {}),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(kus, 3),

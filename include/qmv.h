@@ -194,6 +194,28 @@ qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int64_t k, c
                       void* stream);
 
 /*
+ * qmv_matvec_x -- the decode step of one matrix from fp32 activations:
+ *   xq = Q8(x) exactly as qmv_quantize_act makes it, then
+ *   y[t][n] = sum_k W[n][k] * xq[t][k]  exactly as qmv_matvec computes it.
+ * Castagna Veloce page, "Fused operations" (Q8 activations; fused kernels for
+ * the verify batches) and zhuai.tech GLM-5.3 page, "A faster kernel can
+ * still leave the full chain slower" (fewer launches and handoffs).  Where
+ * that measured faster (Q8_0 rows of up to 4096 weights at one or two
+ * tokens, q4_K ones at one token) the matvec workgroups quantize x
+ * themselves, in the one launch, and one of them writes xq; otherwise the
+ * call runs the quantizer and then the matvec (two launches, same results).
+ * x    : fp32 [n_tok][ldx] (device), 16-byte aligned, ldx >= k, ldx % 4 == 0,
+ *        finite values.
+ * xq   : activation buffer of qmv_act_bytes(n_tok, k) bytes (device, 256-byte
+ *        aligned); receives Q8(x) for reuse by later calls (another matrix
+ *        over the same activations).
+ * w, n_rows, k, n_tok, y, ldy: as for qmv_matvec (no split-K workspace).
+ * Asynchronous on `stream`; allocates nothing.
+ */
+qmv_status qmv_matvec_x(qmv_type type, const void* w, int64_t n_rows, int64_t k, const float* x,
+                        int64_t ldx, int64_t n_tok, float* y, int64_t ldy, void* xq, void* stream);
+
+/*
  * qmv_matvec_batch -- sibling matvecs over one activation buffer in one
  * launch, each optionally plus a residual:
  *   y_i[t][n] = sum_k W_i[n][k] * xq[t][k]  (+ residual_i[t][n])

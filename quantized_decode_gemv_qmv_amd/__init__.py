@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
-    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_batch", "moe_matvec", "block_dots",
+    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
@@ -84,6 +84,7 @@ def lib():
         "qmv_matvec_workspace_bytes": ([I, I64, I64, I64], SZ),
         "qmv_matvec": ([I, P, I64, I64, P, I64, P, I64, P, SZ, P], I),
         "qmv_matvec_batch": ([I, ctypes.POINTER(_Item), I64, I64, P, I64, P], I),
+        "qmv_matvec_x": ([I, P, I64, I64, P, I64, I64, P, I64, P, P], I),
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
@@ -233,6 +234,30 @@ def matvec(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor, n_t
     _check(lib().qmv_matvec(fmt, _ptr(w), n_rows, k, _ptr(xq), n_tok, _ptr(y), ldy,
                             _ptr(ws), wsz, _stream(stream)), "qmv_matvec")
     return y
+
+
+def matvec_x(fmt: int, w: torch.Tensor, n_rows: int, k: int, x: torch.Tensor,
+             xq: torch.Tensor | None = None, y: torch.Tensor | None = None, stream=None):
+    """The decode step from fp32 x [T][K]: (y [T][N] = W Q8(x), xq = Q8(x)).
+    One launch for one or two tokens (the matvec quantizes x itself)."""
+    _need(w, torch.uint8, "w")
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    if x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a float32 CUDA tensor with unit column stride")
+    n_tok = x.shape[0]
+    if xq is None:
+        xq = torch.empty(act_bytes(n_tok, k), dtype=torch.uint8, device=x.device)
+    _need(xq, torch.uint8, "xq")
+    if y is None:
+        y = torch.empty((n_tok, n_rows), dtype=torch.float32, device=w.device)
+    if y.dtype != torch.float32 or not y.is_cuda or y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be a float32 CUDA tensor [T][ldy] with unit column stride")
+    if w.numel() < n_rows * row_bytes(fmt, k):
+        raise ValueError("w holds fewer than n_rows rows")
+    _check(lib().qmv_matvec_x(fmt, _ptr(w), n_rows, k, _ptr(x), _ld(x), n_tok, _ptr(y), _ld(y), _ptr(xq),
+                              _stream(stream)), "qmv_matvec_x")
+    return y, xq
 
 
 def _ld(t: torch.Tensor) -> int:

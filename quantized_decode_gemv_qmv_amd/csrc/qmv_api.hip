@@ -408,6 +408,69 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 
+// The LDS-staged flat variant that quantizes its own activations for a
+// shape, or -1 for two launches.  Every workgroup re-reads and re-quantizes
+// all of x before its weights can be used, which only pays for short rows
+// and few tokens: measured on MI355X, Q8_0 4096 x 4096 at 1 / 2 tokens went
+// 7.4 -> 5.6 / 8.0 -> 6.6 us per step and q4_K 14336 x 4096 at one token
+// 10.0 -> 9.8 us, while q4_K at two tokens and IQ4_XS 4096 x 14336 were
+// slower fused.  So: sixteen-wave workgroups (the fewest quantizing copies),
+// Q8_0 at up to two tokens and q4_K at one, rows of at most 128 blocks.  A
+// forced LDS-staged flat variant is honoured (tests).
+static int fused_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
+  if (n_tok > 2) return -1;
+  const int64_t forced = g_variant.load();
+  int v = -1;
+  if (forced >= 0 && forced < kNumVariants && kVariants[forced].kind == 2 && kVariants[forced].xl)
+    v = static_cast<int>(forced);
+  else if (k / 32 <= 128 && n_rows >= 4 * (int64_t)device_cus() && type == QMV_Q8_0)
+    v = find_variant("fl_w16_r1_u2_l");
+  else if (k / 32 <= 128 && n_rows >= 4 * (int64_t)device_cus() && type == QMV_Q4_K && n_tok == 1)
+    v = find_variant("fl_w16_r2_u2_l");
+  if (v < 0 || !stream_fits(v, k, n_tok)) return -1;
+  return v;
+}
+
+QMV_API qmv_status qmv_matvec_x(qmv_type type, const void* w, int64_t n_rows, int64_t k, const float* x,
+                                int64_t ldx, int64_t n_tok, float* y, int64_t ldy, void* xq, void* stream) {
+  qmv_status st = check_weights(type, w, n_rows, k);
+  if (st != QMV_OK) return st;
+  if (x == nullptr || xq == nullptr || y == nullptr || ldy < n_rows || n_tok < 1 || ldx < k || ldx % 4)
+    return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_TOKENS) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(xq, 256) || !aligned(y, 4)) return QMV_ERR_MISALIGNED;
+  const int v = fused_variant(type, n_rows, k, n_tok);
+  if (v < 0) {  // two launches
+    st = qmv_quantize_act(x, ldx, n_tok, k, xq, stream);
+    if (st != QMV_OK) return st;
+    return qmv_matvec(type, w, n_rows, k, xq, n_tok, y, ldy, nullptr, 0, stream);
+  }
+  MatvecLaunch a{};
+  a.fmt = type;
+  a.w = static_cast<const uint8_t*>(w);
+  a.row_bytes = static_cast<int64_t>(qmv_row_bytes(type, k));
+  a.n_rows = static_cast<int>(n_rows);
+  a.units = static_cast<int>(k / 32);
+  a.x = act_view(xq, n_tok, k);
+  a.n_tok = static_cast<int>(n_tok);
+  a.y = y;
+  a.ldy = ldy;
+  a.qx = true;
+  a.xf = x;
+  a.ldx = ldx;
+  a.variant = v;
+  a.slices = 1;
+  a.xq = static_cast<const uint8_t*>(xq);
+  a.act_bytes = static_cast<int64_t>(qmv_act_bytes(n_tok, k));
+  a.off_d = static_cast<int64_t>(qmv_act_offset_d(n_tok, k));
+  a.off_s = static_cast<int64_t>(qmv_act_offset_s(n_tok, k));
+  const DeviceInfo dv = device_info();
+  a.cus = dv.cus;
+  a.lds_per_cu = dv.lds_per_cu;
+  hipError_t e = launch_matvec(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
 // Byte extent [lo, hi) of an fp32 [n_tok][ld] output touching n columns.
 static void extent(const float* p, int64_t n_tok, int64_t ld, int64_t n, uintptr_t& lo, uintptr_t& hi) {
   lo = reinterpret_cast<uintptr_t>(p);

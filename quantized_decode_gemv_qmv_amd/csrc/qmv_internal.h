@@ -88,6 +88,11 @@ struct StreamArgs {
   const float* res;  // NULL, or fp32 [n_tok][ldr] added to the outputs
   int64_t ldr;
   Segs seg;
+  // flat kernel quantizing its own activations: fp32 x [n_tok][ldx], and the
+  // Q8 buffer that workgroup 0 also writes out (the layout of xq)
+  const float* x;
+  int64_t ldx;
+  uint8_t* xq_out;
 };
 
 #ifdef __HIPCC__
@@ -136,6 +141,11 @@ struct MatvecLaunch {
   const float* res;  // NULL, or fp32 [n_tok][ldr] added to y
   int64_t ldr;
   Segs seg;         // batched launch (seg.n > 0): the matrices; n_rows the launch rows
+  // quantize-in-kernel launch (qx): fp32 x [n_tok][ldx] and the Q8 buffer
+  // written beside it (xq then points at that buffer too)
+  bool qx;
+  const float* xf;
+  int64_t ldx;
   int variant;  // index into kVariants
   const uint8_t* xq;  // the activation buffer and its layout
   int64_t act_bytes, off_d, off_s;

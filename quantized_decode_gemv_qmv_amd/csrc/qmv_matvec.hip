@@ -286,9 +286,18 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
 // behind them, so both latencies overlap; then it decodes, reduces with DPP
 // and stores.  XL true stages the activation buffer in LDS per workgroup
 // instead (for token counts whose fragments would not fit in registers).
-template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC, bool SEG>
+//
+// QX (with XL, one or two tokens): the workgroup makes the Q8 activation
+// blocks itself from fp32 x, straight into the LDS copy, with the same block
+// routine as the quantizer kernel (so the blocks are identical).  Its x loads
+// go out before the weight loads and the quantization runs while the weights
+// are on their way; workgroup 0 also writes the blocks to a.xq_out.
+template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC, bool SEG, int QXP = 0>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC))) void k_flat(StreamArgs a) {
   static_assert(R * TM <= 64, "one output per lane");
+  constexpr bool QX = QXP > 0;  // QXP: x passes held in registers ahead of the weight loads
+  static_assert(!QX || (XL && !SEG), "quantizing into the LDS copy");
+  constexpr int QP = QX ? QXP : 1;
   constexpr int CH = 64 * NU;
   constexpr int NT = 64 * WPB;
   constexpr int TX = XL ? 1 : TM;  // prefetched fragments per unit
@@ -321,7 +330,20 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   // compiler wait for its value where the branches join.
   const int n16 = a.act_bytes >> 4;  // LDS copy: 16-byte pieces
   u32x4 stg[4];
-  if constexpr (XL) {
+  // QX: block p * (NT / 8) + threadIdx.x / 8 of the n_tok * nb blocks, four
+  // values per lane (clamped to the last block: the loads stay unconditional)
+  const int q_blocks = a.n_tok * a.nb;
+  const int q_passes = (q_blocks + NT / 8 - 1) / (NT / 8);
+  f32x4 xv[QX ? QP : 1];
+  auto x_piece = [&](int p) -> const float* {
+    const int blk = min(p * (NT / 8) + ((int)threadIdx.x >> 3), q_blocks - 1);
+    const int t = blk / a.nb, b = blk - t * a.nb;
+    return a.x + (int64_t)t * a.ldx + 32 * b + 4 * ((int)threadIdx.x & 7);
+  };
+  if constexpr (QX) {
+#pragma unroll
+    for (int p = 0; p < QP; ++p) xv[p] = *reinterpret_cast<const f32x4*>(x_piece(min(p, q_passes - 1)));
+  } else if constexpr (XL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) stg[i] = ld16(a.xq + 16 * (int64_t)min((int)threadIdx.x + i * NT, n16 - 1));
   } else {
@@ -350,7 +372,36 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  if constexpr (XL) {
+  if constexpr (QX) {
+    auto put = [&](int p, const f32x4& v) {
+      const int blk = p * (NT / 8) + ((int)threadIdx.x >> 3);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      float db;
+      int sum;
+      const uint32_t packed = q8_block8(vv, db, sum);
+      if (blk < q_blocks) {
+        const int t = blk / a.nb, b = blk - t * a.nb, j = (int)threadIdx.x & 7;
+        const int qo = t * a.k + 32 * b + 4 * j;
+        *reinterpret_cast<uint32_t*>(s_mem + qo) = packed;
+        if (j == 0) {
+          reinterpret_cast<float*>(s_mem + a.off_d)[blk] = db;
+          reinterpret_cast<int32_t*>(s_mem + a.off_s)[blk] = sum;
+        }
+        if (a.xq_out != nullptr && blockIdx.x == 0) {
+          *reinterpret_cast<uint32_t*>(a.xq_out + qo) = packed;
+          if (j == 0) {
+            reinterpret_cast<float*>(a.xq_out + a.off_d)[blk] = db;
+            reinterpret_cast<int32_t*>(a.xq_out + a.off_s)[blk] = sum;
+          }
+        }
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < QP; ++p)
+      if (p < q_passes) put(p, xv[p]);
+    for (int p = QP; p < q_passes; ++p) put(p, *reinterpret_cast<const f32x4*>(x_piece(p)));  // long rows
+    __syncthreads();
+  } else if constexpr (XL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = threadIdx.x + i * NT;
@@ -633,6 +684,9 @@ static StreamArgs stream_args(const MatvecLaunch& a) {
   sa.res = a.res;
   sa.ldr = a.ldr;
   sa.seg = a.seg;
+  sa.x = nullptr;
+  sa.ldx = 0;
+  sa.xq_out = nullptr;
   return sa;
 }
 
@@ -679,10 +733,33 @@ static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
     const int64_t groups = (a.n_rows + R - 1) / R;
     const unsigned grid = (unsigned)((groups + WPB - 1) / WPB);
     StreamArgs sa = stream_args(a);
-    if (a.seg.n > 0)
+    if (a.qx) {
+      // quantize-in-kernel launches: LDS-staged variants at one or two tokens
+      if constexpr (XL && TM <= 2) {
+        sa.x = a.xf;
+        sa.ldx = a.ldx;
+        sa.xq_out = const_cast<uint8_t*>(a.xq);
+        const int passes = (int)((a.n_tok * (a.units) + 8 * WPB - 1) / (8 * WPB));  // 8 blocks per wave
+        if (passes <= 1)
+          hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false, 1>), dim3(grid), dim3(64 * WPB), lds, st,
+                             sa);
+        else if (passes <= 2)
+          hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false, 2>), dim3(grid), dim3(64 * WPB), lds, st,
+                             sa);
+        else if (passes <= 4)
+          hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false, 4>), dim3(grid), dim3(64 * WPB), lds, st,
+                             sa);
+        else
+          hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false, 8>), dim3(grid), dim3(64 * WPB), lds, st,
+                             sa);
+      } else {
+        return hipErrorInvalidValue;  // the entry point only sends XL variants at <= 2 tokens
+      }
+    } else if (a.seg.n > 0) {
       hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, true>), dim3(grid), dim3(64 * WPB), lds, st, sa);
-    else
+    } else {
       hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+    }
     return hipGetLastError();
   }
 }

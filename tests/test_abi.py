@@ -195,6 +195,29 @@ def test_tuning_switches(L):
         q.set_tuning("variant", -1)
 
 
+def test_matvec_x_validation(L):
+    f = L.qmv_matvec_x
+
+    def call(**kw):
+        a = dict(fmt=1, w=FAKE, n=4, k=256, x=FAKE, ldx=256, t=1, y=FAKE, ldy=4, xq=FAKE)
+        a.update(kw)
+        return f(a["fmt"], a["w"], a["n"], a["k"], a["x"], a["ldx"], a["t"], a["y"], a["ldy"], a["xq"], None)
+
+    assert call(x=None) == INVALID
+    assert call(xq=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(fmt=9) == INVALID
+    assert call(k=96) == INVALID
+    assert call(ldx=252) == INVALID
+    assert call(ldx=258) == INVALID  # rows of x must keep 16-byte alignment
+    assert call(ldy=3) == INVALID
+    assert call(t=0) == INVALID
+    assert call(t=17) == UNSUPPORTED
+    assert call(x=FAKE + 4) == MISALIGNED
+    assert call(xq=FAKE + 128) == MISALIGNED
+    assert call(w=FAKE + 8) == MISALIGNED
+
+
 def test_matvec_batch_validation(L):
     f = L.qmv_matvec_batch
     Item = q._Item
