@@ -299,15 +299,32 @@ constexpr uint32_t IQ4_CB1 = pk4(-49, -35, -22, -10);
 constexpr uint32_t IQ4_CB2 = pk4(1, 13, 25, 38);
 constexpr uint32_t IQ4_CB3 = pk4(53, 69, 89, 113);
 
-// Four 4-bit indices (one per byte, 0..15) -> four int8 codebook values with
-// three byte permutes: entries 0..7 and 8..15 are looked up by the low three
-// index bits, then bit 3 picks between the two results byte by byte.
-__device__ __forceinline__ uint32_t iq4_lookup(uint32_t n) {
-  const uint32_t sel = n & 0x07070707u;
-  const uint32_t lo = __builtin_amdgcn_perm(IQ4_CB1, IQ4_CB0, sel);
-  const uint32_t hi = __builtin_amdgcn_perm(IQ4_CB3, IQ4_CB2, sel);
-  const uint32_t pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
-  return __builtin_amdgcn_perm(hi, lo, pick);
+// Codebook lookup of 4-bit indices (one per byte, 0..15) -> int8 values, four
+// at a time with three byte permutes: entries 0..7 and 8..15 are looked up by
+// the low three index bits, then bit 3 picks between the two results byte by
+// byte (the pick selector is byte i + 4 * bit 3 of index i).
+// The identity byte selector 0x03020100 in a vector register.  gfx9 VOP3
+// instructions take no literal operand, so with the constant in a register the
+// mask-and-or of each pick selector is one v_and_or_b32 (mask from a scalar
+// register) instead of an and and an or with literals.  The asm only hides the
+// value from constant folding; it has no side effect and is hoisted.
+__device__ __forceinline__ uint32_t perm_identity() {
+  uint32_t c;
+  asm("v_mov_b32 %0, 0x3020100" : "=v"(c));
+  return c;
+}
+
+// Both nibbles of four index bytes -> the codebook values of the low nibbles
+// (lo) and of the high nibbles (hi).
+__device__ __forceinline__ void iq4_lookup2(uint32_t v, uint32_t ident, uint32_t& lo, uint32_t& hi) {
+  const uint32_t s0 = v & 0x07070707u;
+  const uint32_t p0 = ((v >> 1) & 0x04040404u) | ident;
+  const uint32_t s1 = (v >> 4) & 0x07070707u;
+  const uint32_t p1 = ((v >> 5) & 0x04040404u) | ident;
+  lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(IQ4_CB3, IQ4_CB2, s0),
+                             __builtin_amdgcn_perm(IQ4_CB1, IQ4_CB0, s0), p0);
+  hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(IQ4_CB3, IQ4_CB2, s1),
+                             __builtin_amdgcn_perm(IQ4_CB1, IQ4_CB0, s1), p1);
 }
 
 __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FIQ4_XS>& o) {
@@ -317,11 +334,11 @@ __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FI
   o.ls = static_cast<int>(lo4 | (hi2 << 4)) - 32;
   o.d = half_bits_to_float(r.hdr.x);
   o.dls = o.d * static_cast<float>(o.ls);
+  const uint32_t ident = perm_identity();
   const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    o.q[i] = iq4_lookup(v[i] & 0x0F0F0F0Fu);
-    o.q[4 + i] = iq4_lookup((v[i] >> 4) & 0x0F0F0F0Fu);
+    iq4_lookup2(v[i], ident, o.q[i], o.q[4 + i]);
   }
 }
 
