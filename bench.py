@@ -42,6 +42,7 @@ WORKLOADS = {
     "q4_k_14336x4096": (1, 14336, 4096, (1, 2, 4, 8, 16)),
     "q5_k_14336x4096": (3, 14336, 4096, (1, 2, 4, 8, 16)),
     "q6_k_14336x4096": (4, 14336, 4096, (1, 2, 4, 8, 16)),
+    "q8g128_head_152064x5120": (5, 152064, 5120, (1, 2, 4, 8, 16)),
     # gate and up projections as two separate tensors sharing one activation
     # buffer, one qmv_matvec_batch launch
     "q4_k_siblings_2x14336x4096": (1, 14336, 4096, (1, 2, 4, 8, 16), 2),
@@ -50,7 +51,7 @@ WORKLOADS = {
     "q8_0_splitk_256x65536": (0, 256, 65536, (1,)),
     "q8_0_head_152064x5120": (0, 152064, 5120, (1, 2, 4, 8, 16)),
 }
-FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS", 3: "q5_K", 4: "q6_K"}
+FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS", 3: "q5_K", 4: "q6_K", 5: "Q8G128"}
 # MoE decode: 128 IQ4_XS experts, gate+up 3072 x 4096 and down 4096 x 1536 per
 # expert, top-8 routing
 MOE = dict(name="moe_iq4_xs_e128", ffn_name="moe_ffn_iq4_xs_e128", experts=128, top_k=8,
@@ -406,7 +407,7 @@ def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
     import oracle
     import synth
 
-    rows = min(n, max(1, (64 << 20) // (k // (32 if fmt == 0 else 256) * (34, 144, 136, 176, 210)[fmt])))
+    rows = min(n, max(1, (64 << 20) // (k // (32, 256, 256, 256, 256, 128)[fmt] * (34, 144, 136, 176, 210, 130)[fmt])))
     w = synth.make_weights(fmt, n, k, f"{name}/W", rows=(0, rows)).data
     x = synth.make_x(t, k, f"{name}/x")
     cores = len(os.sched_getaffinity(0))

@@ -38,6 +38,10 @@
  *                w = d * scales[(128h + 32j + l) / 16] * (q - 32)
  *                (same page and entry points as q5_K; blocks are 210 B, so
  *                rows need not be 4-byte aligned: only the base pointer is)
+ *       Q8G128 : 130 B per 128 weights (fp16 d, int8 q[128]), w = d * q: the
+ *                int8 LM-head format named on the zhuai.tech GLM-5.3 page
+ *                ("LM Head uses Q8G128", read as Q8_0 with groups of 128);
+ *                k a multiple of 128; same entry points as q5_K
  *   - All pointers except those documented as host pointers are DEVICE
  *     pointers on the current HIP device.  The caller owns every buffer; the
  *     library allocates nothing and keeps no pointer after a call returns.
@@ -68,7 +72,8 @@ typedef enum {
   QMV_Q4_K = 1,
   QMV_IQ4_XS = 2,
   QMV_Q5_K = 3,
-  QMV_Q6_K = 4
+  QMV_Q6_K = 4,
+  QMV_Q8G128 = 5
 } qmv_type;
 
 typedef enum {
@@ -186,7 +191,7 @@ qmv_status qmv_router_topk(const float* x, int64_t ldx, int64_t n_tok, int64_t k
  *        workspace may serve calls of different shapes, each needing no more
  *        than its size, as long as those calls do not overlap in time.
  * 1 <= n_tok <= QMV_MAX_TOKENS (else QMV_ERR_UNSUPPORTED); n_rows >= 1;
- * k a positive multiple of 32 (Q8_0) or 256 (q4_K, IQ4_XS).
+ * k a positive multiple of 32 (Q8_0), 128 (Q8G128) or 256 (the others).
  */
 size_t qmv_matvec_workspace_bytes(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok);
 qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int64_t k, const void* xq,
@@ -279,7 +284,7 @@ qmv_status qmv_matvec_batch(qmv_type type, const qmv_matvec_item* items, int64_t
  * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, 1 <= top_k <= QMV_MAX_TOP_K,
  * 1 <= n_experts <= QMV_MAX_EXPERTS, n_rows <= QMV_MAX_MOE_ROWS and
  * k <= QMV_MAX_MOE_K (else QMV_ERR_UNSUPPORTED); k as for qmv_matvec; type
- * Q8_0, q4_K or IQ4_XS (q5_K, q6_K: QMV_ERR_UNSUPPORTED).
+ * Q8_0, q4_K or IQ4_XS (q5_K, q6_K, Q8G128: QMV_ERR_UNSUPPORTED).
  */
 size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows, int64_t k,
                                int64_t n_tok, int64_t top_k);

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB = os.path.join(_HERE, "liboqmv.so")
 
-Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K = 0, 1, 2, 3, 4
+Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K, Q8G128 = 0, 1, 2, 3, 4, 5
 _lib = None
 
 
@@ -95,7 +95,7 @@ def _w2d(fmt, w, k):
 def unpack(fmt: int, w: np.ndarray, k: int) -> dict:
     w = _w2d(fmt, w, k)
     n = w.shape[0]
-    nsb = k // 32 if fmt == Q8_0 else k // 256
+    nsb = k // 32 if fmt == Q8_0 else (k // 128 if fmt == Q8G128 else k // 256)
     d = np.zeros((n, nsb))
     dmin = np.zeros((n, nsb))
     nsc = 16 if fmt == Q6_K else 8  # q6_K: one scale per 16 weights

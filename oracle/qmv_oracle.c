@@ -30,7 +30,10 @@
  *     q = (nibble of ql[64h + 32(j & 1) + l], low for j < 2, high otherwise)
  *         + 16 * (bits 2j..2j+1 of qh[32h + l]),
  *     and weight i of the super-block is d * scales[i / 16] * (q - 32).
- *     Its integer partial per 32-block is P = sum_i scales[i/16] (q_i - 32) qx_i.
+ *     Its integer partial per 32-block is P = sum_i scales[i/16] (q_i - 32) qx_i;
+ *   - Q8G128 (130 B): fp16 d, int8 q[128]: weight = d * q for a group of 128
+ *     (the int8 LM-head format the zhuai.tech page names, read as Q8_0 with
+ *     128-weight groups); its 32-blocks dot like Q8_0 and share the group's d.
  *
  * Per 32-weight block b the integer partials are
  *   Q8_0  : P = sum_i qw_i qx_i
@@ -49,7 +52,7 @@
 #include <omp.h>
 #endif
 
-enum { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_IQ4_XS = 2, FMT_Q5_K = 3, FMT_Q6_K = 4 };
+enum { FMT_Q8_0 = 0, FMT_Q4_K = 1, FMT_IQ4_XS = 2, FMT_Q5_K = 3, FMT_Q6_K = 4, FMT_Q8G128 = 5 };
 
 /* K-quants with a per-sub-block min (q4_K, q5_K): two terms per block. */
 static int has_min(int fmt) { return fmt == FMT_Q4_K || fmt == FMT_Q5_K; }
@@ -80,6 +83,7 @@ int64_t oracle_row_bytes(int fmt, int64_t k) {
     case FMT_IQ4_XS: return k % 256 ? -1 : (k / 256) * 136;
     case FMT_Q5_K: return k % 256 ? -1 : (k / 256) * 176;
     case FMT_Q6_K: return k % 256 ? -1 : (k / 256) * 210;
+    case FMT_Q8G128: return k % 128 ? -1 : (k / 128) * 130;
     default: return -1;
   }
 }
@@ -89,6 +93,12 @@ typedef struct { double d; int q[32]; } q8_0_block;
 typedef struct { double d, dmin; int sc[8], m[8], q[256]; } q4_k_block;
 typedef struct { double d; int ls[8], idx[256]; } iq4_xs_block;
 typedef struct { double d; int sc[16], q[256]; } q6_k_block;  /* q: stored 0..63 */
+typedef struct { double d; int q[128]; } q8g128_block;
+
+static void decode_q8g128(const uint8_t* b, q8g128_block* o) {
+  o->d = half_to_double(rd16(b));
+  for (int i = 0; i < 128; ++i) o->q[i] = (int8_t)b[2 + i];
+}
 
 static void decode_q8_0(const uint8_t* b, q8_0_block* o) {
   o->d = half_to_double(rd16(b));
@@ -178,6 +188,13 @@ int oracle_unpack(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double* 
         d[n * (k / 32) + b] = blk.d;
         for (int i = 0; i < 32; ++i) q[n * k + 32 * b + i] = blk.q[i];
       }
+    } else if (fmt == FMT_Q8G128) {
+      for (int64_t g = 0; g < k / 128; ++g) {
+        q8g128_block blk;
+        decode_q8g128(row + g * 130, &blk);
+        d[n * (k / 128) + g] = blk.d;
+        for (int i = 0; i < 128; ++i) q[n * k + 128 * g + i] = blk.q[i];
+      }
     } else if (has_min(fmt)) {
       for (int64_t b = 0; b < k / 256; ++b) {
         q4_k_block blk;
@@ -226,6 +243,12 @@ int oracle_dequant(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, double*
         q8_0_block blk;
         decode_q8_0(row + b * 34, &blk);
         for (int i = 0; i < 32; ++i) o[32 * b + i] = blk.d * blk.q[i];
+      }
+    } else if (fmt == FMT_Q8G128) {
+      for (int64_t g = 0; g < k / 128; ++g) {
+        q8g128_block blk;
+        decode_q8g128(row + g * 130, &blk);
+        for (int i = 0; i < 128; ++i) o[128 * g + i] = blk.d * blk.q[i];
       }
     } else if (has_min(fmt)) {
       for (int64_t b = 0; b < k / 256; ++b) {
@@ -302,6 +325,16 @@ static void row_block_dots(int fmt, const uint8_t* row, int64_t k, const int8_t*
       for (int i = 0; i < 32; ++i) p += blk.q[i] * qx[32 * b + i];
       out[b] = p;
     }
+  } else if (fmt == FMT_Q8G128) {
+    for (int64_t g = 0; g < k / 128; ++g) {
+      q8g128_block blk;
+      decode_q8g128(row + g * 130, &blk);
+      for (int j = 0; j < 4; ++j) {
+        int32_t p = 0;
+        for (int i = 0; i < 32; ++i) p += blk.q[32 * j + i] * qx[128 * g + 32 * j + i];
+        out[4 * g + j] = p;
+      }
+    }
   } else if (has_min(fmt)) {
     for (int64_t sb = 0; sb < k / 256; ++sb) {
       q4_k_block blk;
@@ -362,6 +395,8 @@ int oracle_block_dots(int fmt, const uint8_t* w, int64_t n_rows, int64_t k, cons
 static void row_block_scales(int fmt, const uint8_t* row, int64_t k, double* dw, double* dm) {
   if (fmt == FMT_Q8_0) {
     for (int64_t b = 0; b < k / 32; ++b) dw[b] = half_to_double(rd16(row + b * 34));
+  } else if (fmt == FMT_Q8G128) {
+    for (int64_t b = 0; b < k / 32; ++b) dw[b] = half_to_double(rd16(row + (b / 4) * 130));
   } else {
     int64_t bb = oracle_row_bytes(fmt, 256);
     int64_t d_at = fmt == FMT_Q6_K ? 208 : 0;  /* q6_K keeps d at the end */

@@ -18,13 +18,13 @@ import re
 import torch
 
 __all__ = [
-    "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "QmvError", "lib", "library_path", "symbols",
+    "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "Q8G128", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
     "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
-Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K = 0, 1, 2, 3, 4
+Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K, Q8G128 = 0, 1, 2, 3, 4, 5
 MAX_TOKENS = 16
 MAX_MOE_TOKENS = 64
 MAX_BATCH = 8

@@ -40,16 +40,17 @@ struct EnvInit {
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 bool valid_type(int t) {
-  return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS || t == QMV_Q5_K || t == QMV_Q6_K;
+  return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS || t == QMV_Q5_K || t == QMV_Q6_K || t == QMV_Q8G128;
 }
 
-int64_t block_k(int t) { return t == QMV_Q8_0 ? 32 : 256; }
+int64_t block_k(int t) { return t == QMV_Q8_0 ? 32 : (t == QMV_Q8G128 ? 128 : 256); }
 int64_t block_bytes(int t) {
   switch (t) {
     case QMV_Q8_0: return 34;
     case QMV_Q4_K: return 144;
     case QMV_IQ4_XS: return 136;
     case QMV_Q5_K: return 176;
+    case QMV_Q8G128: return 130;
     default: return 210;  // q6_K
   }
 }
@@ -132,8 +133,9 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 }
 
 // Default kernel for a shape, from measurements on MI355X of every variant on
-// the workload shapes (Q8_0 4096x4096 and 152064x5120, q4_K 14336x4096,
-// IQ4_XS 4096x14336, Q8_0 256x65536; 1..16 tokens):
+// the workload shapes (Q8_0 4096x4096, 14336x4096 and 152064x5120, q4_K,
+// q5_K and q6_K 14336x4096, IQ4_XS 4096x14336, Q8_0 256x65536, Q8G128
+// 152064x5120, 14336x4096, 4096x4096 and 4096x14336; 1..16 tokens):
 //   - too few rows to give every compute unit several waves, long K: the
 //     streaming kernel with K split over a 16-wave workgroup;
 //   - up to two tokens (four for Q8_0): the flat kernel (one wave per row
@@ -142,11 +144,19 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //   - 3..8 tokens: the matrix-core kernel for IQ4_XS (and q4_K from five
 //     tokens), 16-wave workgroups with K split so that about 4096 waves
 //     cover the rows; otherwise the multi-token vector kernel;
-//   - 9..16 tokens: the matrix-core kernel, 8-wave workgroups with a
-//     four-deep load ring (the register budget of the 16-token tiles);
+//   - 9..16 tokens: the matrix-core kernel (for Q8_0 only from 128 rows
+//     per compute unit), 8-wave workgroups with a four-deep load ring (the
+//     register budget of the 16-token tiles);
 //   - q5_K and q6_K have no matrix-core decode: from three tokens the
 //     multi-token vector kernel (q5_K, and q6_K on long rows) or the flat
-//     one (q6_K while one chunk of 128 units per lane covers the row).
+//     one (q6_K while one chunk of 128 units per lane covers the row);
+//   - Q8_0 at 5..8 tokens (and from nine on fewer than 128 rows per
+//     compute unit), Q8G128 (no matrix-core decode either) from three: by
+//     rows per compute unit, the flat kernel with 16-wave
+//     workgroups on many rows (the multi-token one from nine tokens), the
+//     multi-token kernel with two rows per lane group in between, and the
+//     flat kernel (or, on long rows from nine tokens, the multi-token one
+//     splitting K four ways) on few rows.
 //   The vector multi-token kernel's LDS staging is chunked and so fits any
 //   K, which also makes it the fallback.
 int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
@@ -159,17 +169,32 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   if (n_rows < 4 * (int64_t)cus && units >= 256) {
     name = "st_k16_r1_u2";
   } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2)) {
-    name = nu <= 2 ? (type == QMV_Q8_0 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_g")
+    name = nu <= 2 ? (type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_g")
            : nu <= 3 ? "fl_w16_r1_u3_l"
            : nu <= 7 ? "fl_w8_r1_u7_l"
                      : "fl_w4_r1_u4_g";
-  } else if (!has_mfma(type)) {
+  } else if (type == QMV_Q4_K && n_tok == 3 && nu <= 2) {
+    name = "fl_w4_r1_u2_l";  // measured 11.25 against 11.59 us for the multi-token kernel
+  } else if (type == QMV_Q5_K || type == QMV_Q6_K) {
     // q5_K, q6_K (measured on 14336 x 4096 at 3..16 tokens): q6_K keeps the
     // flat kernel while one chunk covers the row, q5_K the multi-token one
     if (type == QMV_Q6_K && nu <= 2)
       name = n_tok > 8 ? "fl_w16_r1_u2_l" : n_tok > 4 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u2_l";
     else
       name = n_tok > 8 ? "mt_r4_w8_k2" : "mt_r2_w8_k2";
+  } else if ((type == QMV_Q8_0 && (n_tok <= 8 || rpc < 128)) || type == QMV_Q8G128) {
+    // Q8_0 at 5..8 tokens (and beyond on fewer than 128 rows per compute
+    // unit, where its matrix-core kernel is slower), Q8G128 (no matrix-core
+    // decode) from three: measured on 152064x5120, 14336x4096, 4096x4096
+    // and 4096x14336
+    if (rpc >= 128)
+      name = n_tok > 8 ? "mt_r4_w4_k1" : nu <= 2 ? "fl_w16_r1_u2_l" : "fl_w16_r1_u3_l";
+    else if (rpc >= 32)
+      name = "mt_r2_w4_k1";
+    else if (nu <= 2 && n_tok <= 4)
+      name = "fl_w4_r1_u2_l";
+    else
+      name = n_tok > 8 && nu > 2 ? "mt_r1_w8_k4" : "fl_w16_r1_u2_l";
   } else if (n_tok > 8) {
     const int64_t per = 16 * (int64_t)cus / tiles;  // waves of K split per row tile
     name = per >= 8 ? "mx_w8_k8_r4" : per >= 4 ? "mx_w8_k4_r4" : "mx_w8_k1_r4";

@@ -13,6 +13,8 @@
 //            j = 2 (c >> 1), high nibbles the same positions of sub-block j+1.
 //   q5_K   : as q4_K, plus the 16 qh bytes 16h..16h+15 that carry the fifth
 //            bit of those positions (bit j for sub-block j, j + 1 for j + 1).
+//   Q8G128 : 32-block u = quarter u & 3 of group u >> 2 (130 B: fp16 d,
+//            int8 q[128]); the group's scale is shared by its four units
 //   q6_K   : 32-block u (half f = (u & 7) >> 2, quarter j = u & 3) and its
 //            partner u ^ 2 take the low and high nibbles of the same 32 ql
 //            bytes; the unit holds positions 16h..16h+15, h = (u >> 1) & 1,
@@ -29,7 +31,7 @@
 
 namespace qmv {
 
-enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2, FQ5_K = 3, FQ6_K = 4 };
+enum : int { FQ8_0 = 0, FQ4_K = 1, FIQ4_XS = 2, FQ5_K = 3, FQ6_K = 4, FQ8G128 = 5 };
 
 // K-quants with a per-sub-block min (q4_K, q5_K): paired own-block form, two
 // integer partials per block.
@@ -44,6 +46,7 @@ template <> struct Fmt<FQ4_K> { static constexpr int QK = 256, BB = 144, UPB = 8
 template <> struct Fmt<FIQ4_XS> { static constexpr int QK = 256, BB = 136, UPB = 8; };
 template <> struct Fmt<FQ5_K> { static constexpr int QK = 256, BB = 176, UPB = 8; };
 template <> struct Fmt<FQ6_K> { static constexpr int QK = 256, BB = 210, UPB = 8; };
+template <> struct Fmt<FQ8G128> { static constexpr int QK = 128, BB = 130, UPB = 4; };
 
 // 16- and 8-byte vectors that only promise 4-byte alignment: gfx950 global
 // loads of several dwords need dword alignment only.
@@ -120,6 +123,12 @@ template <> struct Raw<FQ5_K> {
   u32x4 hdr;  // the q4_K header
   u32x4 qh;   // the 16 qh bytes of the unit's positions
 };
+template <> struct Raw<FQ8G128> {
+  u32x4 a, b;    // the unit's 32 quants, from the dword at or below them
+  uint32_t h;    // its last two quants (used when the quants start 2 mod 4)
+  uint32_t odd;  // 1: the quants are dword aligned
+  uint32_t d;    // fp16 bits of the group scale
+};
 template <> struct Raw<FQ6_K> {
   u32x4 ql, qh;        // the 16 ql and 16 qh bytes of the unit's positions
   int sc_own, sc_par;  // int8 scales of those positions in the own and partner block
@@ -145,6 +154,20 @@ __device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ4_K>&
   const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
   r.q = ld_w16(row + qoff);
   r.hdr = ld_w16(row + blk);
+}
+// Q8G128 groups are 130 bytes, so a unit's 32 quants start 0 or 2 mod 4.  At
+// 2 mod 4 they are read as the 32 bytes from two bytes below them (the last
+// two bytes of the previous unit, or the group's scale) plus a 2-byte load of
+// their last two, and realigned; no byte outside the group is read.
+__device__ __forceinline__ void load_unit(const uint8_t* row, int u, Raw<FQ8G128>& r) {
+  const uint32_t goff = 130u * ((uint32_t)u >> 2);
+  const uint32_t q0 = goff + 2 + 32 * ((uint32_t)u & 3);
+  const uint32_t mis = ((uint32_t)reinterpret_cast<uintptr_t>(row) + q0) & 2u;
+  r.a = ld_w16(row + (q0 - mis));
+  r.b = ld_w16(row + (q0 - mis + 16));
+  r.h = ld_w2(row + q0 + 30);
+  r.odd = mis ? 0u : 1u;
+  r.d = ld_w2(row + goff);
 }
 // 16 bytes at byte offset off of a row whose base is 16-byte aligned, where
 // row + off may be 2 mod 4 (q6_K blocks are 210 bytes): five dwords from the
@@ -216,6 +239,9 @@ __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane,
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ6_K>& r) {
   load_unit(row, u, r.r);
 }
+__device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ8G128>& r) {
+  load_unit(row, u, r.r);
+}
 __device__ __forceinline__ void load_unit_s(const uint8_t* row, int u, int lane, RawS<FQ4_K>& r) {
   const uint32_t blk = 144u * ((uint32_t)u >> 3);
   const uint32_t qoff = blk + 16 + 16 * ((uint32_t)u & 7);
@@ -267,6 +293,7 @@ __device__ __forceinline__ Raw<FIQ4_XS> expand(const RawS<FIQ4_XS>& s) {
 }
 __device__ __forceinline__ Raw<FQ8_0> expand(const RawS<FQ8_0>& s) { return s.r; }
 __device__ __forceinline__ Raw<FQ6_K> expand(const RawS<FQ6_K>& s) { return s.r; }
+__device__ __forceinline__ Raw<FQ8G128> expand(const RawS<FQ8G128>& s) { return s.r; }
 
 // --------------------------------------------------------------- decoding
 template <int F> struct Dec;
@@ -450,6 +477,16 @@ __device__ __forceinline__ void decode_own(const Raw<FQ4_K>& r, int u, int h, bo
     o.q[i] = (v[i] >> sh_par) & 0x0F0F0F0Fu;
     o.q[4 + i] = (v[i] >> sh_own) & 0x0F0F0F0Fu;
   }
+}
+__device__ __forceinline__ void decode_own(const Raw<FQ8G128>& r, int, int, bool ok, DecO<FQ8G128>& o) {
+  const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.h};
+  const uint32_t sh = r.odd ? 0u : 2u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o.q[j] = __builtin_amdgcn_alignbyte(w[j + 1], w[j], sh);
+  o.sc = ok ? half_bits_to_float(r.d) : 0.f;
+  o.wm = 0.f;
+  o.isc = 1;
+  o.im = 0;
 }
 // q6_K: the stored 6-bit values of both runs (nibble plus two qh bits, the
 // quarter's bits 2j..2j+1), minus 32 byte by byte as (v + 96) ^ 128 (no

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ 
   } else if constexpr (F == FQ6_K) {
     out[gid] = dot;  // the 16-weight scales are applied inside the paired dot
   } else {
-    out[gid] = dec.isc * dot;  // Q8_0: isc = 1; IQ4_XS: the signed sub-block scale
+    out[gid] = dec.isc * dot;  // Q8_0, Q8G128: isc = 1; IQ4_XS: the signed sub-block scale
   }
 }
 
@@ -151,6 +151,10 @@ hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n
       break;
     case FQ6_K:
       hipLaunchKernelGGL(k_block_dots<FQ6_K>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
+                         units, x, n_tok, out);
+      break;
+    case FQ8G128:
+      hipLaunchKernelGGL(k_block_dots<FQ8G128>, dim3(grid), dim3(256), 0, st, w, row_bytes, n_rows,
                          units, x, n_tok, out);
       break;
     default: return hipErrorInvalidValue;

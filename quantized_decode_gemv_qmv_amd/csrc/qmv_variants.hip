@@ -52,6 +52,7 @@ hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st) {
     case FIQ4_XS: return launch_vector<FIQ4_XS>(a, st);
     case FQ5_K: return launch_vector<FQ5_K>(a, st);
     case FQ6_K: return launch_vector<FQ6_K>(a, st);
+    case FQ8G128: return launch_vector<FQ8G128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

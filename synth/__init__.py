@@ -41,6 +41,10 @@ layout, so this is the plain GGUF reading)
                              in the q4_K order; the fifth bit (value 16) of
                              weight 64c+i is bit 2c of qh[i], of weight
                              64c+32+i bit 2c+1 of qh[i]
+  Q8G128 130 B / 128 weights: fp16 d | int8 q[128] (int8 groups of 128 with
+                             one scale: the LM-head format the zhuai.tech page
+                             names; this layout is the Q8_0 one with 128-weight
+                             groups)
   q6_K  210 B / 256 weights: 128 B ql | 64 B qh | int8 scales[16] | fp16 d;
                              weight 128h + 32j + l (half h, quarter j, l < 32)
                              is the nibble of ql[64h + 32(j & 1) + l] (low for
@@ -58,16 +62,16 @@ __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "FMT_NAMES", "BLOCK_WEIGHTS", "BLOCK_BYTES",
     "row_bytes", "Stream", "stream", "draw_u64", "uniform01", "randint",
     "nibbles", "normal_f32", "scale_f16",
-    "pack_q8_0", "pack_q4_k", "pack_iq4_xs", "pack_q5_k", "pack_q6_k", "Q5_K", "Q6_K",
+    "pack_q8_0", "pack_q4_k", "pack_iq4_xs", "pack_q5_k", "pack_q6_k", "pack_q8g128", "Q5_K", "Q6_K", "Q8G128",
     "WeightFields", "make_weights", "make_x", "make_routing",
     "CONFIGS", "config",
 ]
 
 # format ids, shared by convention with the C interfaces
-Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K = 0, 1, 2, 3, 4
-FMT_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", IQ4_XS: "iq4_xs", Q5_K: "q5_K", Q6_K: "q6_K"}
-BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, IQ4_XS: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, IQ4_XS: 136, Q5_K: 176, Q6_K: 210}
+Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K, Q8G128 = 0, 1, 2, 3, 4, 5
+FMT_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", IQ4_XS: "iq4_xs", Q5_K: "q5_K", Q6_K: "q6_K", Q8G128: "q8g128"}
+BLOCK_WEIGHTS = {Q8_0: 32, Q4_K: 256, IQ4_XS: 256, Q5_K: 256, Q6_K: 256, Q8G128: 128}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, IQ4_XS: 136, Q5_K: 176, Q6_K: 210, Q8G128: 130}
 
 
 def row_bytes(fmt: int, k: int) -> int:
@@ -232,6 +236,16 @@ def pack_q5_k(d, dmin, sc, m, q) -> np.ndarray:
     return out.reshape(n, ns * 176)
 
 
+def pack_q8g128(d: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """d fp16 [N][K/128], q int8 [N][K] -> bytes [N][K/128*130]."""
+    n, k = q.shape
+    ng = k // 128
+    out = np.empty((n, ng, 130), dtype=np.uint8)
+    out[:, :, 0:2] = np.ascontiguousarray(d, dtype=np.float16).view(np.uint8).reshape(n, ng, 2)
+    out[:, :, 2:130] = q.astype(np.int8).view(np.uint8).reshape(n, ng, 128)
+    return out.reshape(n, ng * 130)
+
+
 def pack_q6_k(d, sc, q) -> np.ndarray:
     """d fp16 [N][S]; sc int8 [N][S][16] (one scale per 16 weights); q uint8
     [N][K] in 0..63 (the stored 6-bit value; the weight is sc * (q - 32))."""
@@ -302,6 +316,7 @@ def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
     """Weights of an n_rows x k matrix (rows r0..r1-1 only if `rows` is given).
 
     Q8_0  : d ~ fp16 U[1e-3,1e-2], q ~ U{-127..127}
+    Q8G128: as Q8_0, one d per 128 weights
     q4_K  : d, dmin ~ fp16 U[1e-3,1e-2], scale and min ~ U{0..63}, q ~ U{0..15}
     IQ4_XS: d ~ fp16 U[1e-3,1e-2], raw 6-bit scale ~ U{0..63}, index ~ U{0..15}
     q5_K  : as q4_K with q ~ U{0..31}
@@ -313,11 +328,11 @@ def make_weights(fmt: int, n_rows: int, k: int, name: str, seed: int = 0,
     n = r1 - r0
     row_bytes(fmt, k)  # validates k
     lo, hi = scale_range
-    if fmt == Q8_0:
-        nb = k // 32
+    if fmt in (Q8_0, Q8G128):
+        nb = k // BLOCK_WEIGHTS[fmt]
         d = scale_f16(stream(name + "/d", seed), r0 * nb, n * nb, lo, hi).reshape(n, nb)
         q = randint(stream(name + "/q", seed), r0 * k, n * k, *q8_range).astype(np.int8).reshape(n, k)
-        data = pack_q8_0(d, q)
+        data = (pack_q8_0 if fmt == Q8_0 else pack_q8g128)(d, q)
         wf = WeightFields(fmt, (r0, r1), k, data)
         if keep_fields:
             wf.d, wf.q = d, q
@@ -396,6 +411,8 @@ CONFIGS = {
     # matvecs; no workload of its own)
     "q5_k_14336x4096": dict(fmt=Q5_K, n=14336, k=4096, tokens=(1, 2, 4, 8, 16)),
     "q6_k_14336x4096": dict(fmt=Q6_K, n=14336, k=4096, tokens=(1, 2, 4, 8, 16)),
+    # the output head in the int8 group-of-128 format
+    "q8g128_head_152064x5120": dict(fmt=Q8G128, n=152064, k=5120, tokens=(1, 2, 4, 8, 16)),
 }
 
 

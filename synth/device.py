@@ -14,8 +14,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (IQ4_XS, Q4_K, Q5_K, Q6_K, Q8_0, _GAMMA, _M1, _M2, Stream, iq4_xs_header, pack_q6_k,
-               q4_k_header, randint, row_bytes, scale_f16, stream)
+from . import (BLOCK_BYTES, BLOCK_WEIGHTS, IQ4_XS, Q4_K, Q5_K, Q6_K, Q8_0, Q8G128, _GAMMA, _M1, _M2, Stream,
+               iq4_xs_header, pack_q6_k, q4_k_header, randint, row_bytes, scale_f16, stream)
 
 __all__ = ["draw_u64", "randint_t", "nibbles_t", "make_weights_t"]
 
@@ -80,13 +80,14 @@ def make_weights_t(fmt: int, n_rows: int, k: int, name: str, seed: int = 0, devi
     for r0 in range(0, n_rows, rows_per):
         r1 = min(n_rows, r0 + rows_per)
         n = r1 - r0
-        if fmt == Q8_0:
-            nb = k // 32
+        if fmt in (Q8_0, Q8G128):
+            qk, bb = BLOCK_WEIGHTS[fmt], BLOCK_BYTES[fmt]
+            nb = k // qk
             d = scale_f16(stream(name + "/d", seed), r0 * nb, n * nb, lo, hi)
             q = randint_t(stream(name + "/q", seed), r0 * k, n * k, *q8_range, device)
-            blk = out[r0:r1].view(n, nb, 34)
+            blk = out[r0:r1].view(n, nb, bb)
             blk[:, :, 0:2] = torch.from_numpy(d.view(np.uint8).reshape(n, nb, 2)).to(device)
-            blk[:, :, 2:34] = q.to(torch.int8).view(torch.uint8).reshape(n, nb, 32)
+            blk[:, :, 2:bb] = q.to(torch.int8).view(torch.uint8).reshape(n, nb, qk)
             continue
         ns = k // 256
         d = scale_f16(stream(name + "/d", seed), r0 * ns, n * ns, lo, hi).reshape(n, ns)

@@ -40,7 +40,8 @@ def test_abi_version_and_status_strings(L):
 @pytest.mark.parametrize("fmt,k,expect", [(0, 4096, 4352), (1, 4096, 2304), (2, 14336, 7616),
                                           (0, 65536, 69632), (0, 5120, 5440), (2, 1536, 816),
                                           (3, 4096, 2816), (3, 288, 0), (4, 4096, 3360), (4, 256, 210),
-                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (5, 256, 0)])
+                                          (5, 5120, 5200), (5, 128, 130), (5, 96, 0),
+                                          (0, 48, 0), (1, 288, 0), (2, 0, 0), (6, 256, 0)])
 def test_row_bytes(fmt, k, expect):
     assert q.row_bytes(fmt, k) == expect
 
@@ -62,6 +63,7 @@ def test_workspace_sizes():
     assert q.moe_workspace_bytes(2, 128, 3072, 4096, 65, 8) == 0
     assert q.moe_workspace_bytes(3, 128, 3072, 4096, 4, 8) == 0  # q5_K: no MoE kernel
     assert q.moe_workspace_bytes(4, 128, 3072, 4096, 4, 8) == 0  # q6_K neither
+    assert q.moe_workspace_bytes(5, 128, 3072, 4096, 4, 8) == 0  # nor Q8G128
 
 
 def _mv(L, fmt=0, w=FAKE, n=4, k=32, xq=FAKE, t=1, y=FAKE, ldy=4, ws=None, wsb=0):
@@ -76,6 +78,8 @@ def test_matvec_validation(L):
     assert _mv(L, n=0) == INVALID
     assert _mv(L, k=48) == INVALID
     assert _mv(L, fmt=1, k=32) == INVALID
+    assert _mv(L, fmt=5, k=32) == INVALID  # Q8G128 rows hold whole 128-groups
+    assert _mv(L, fmt=6) == INVALID
     assert _mv(L, ldy=3) == INVALID
     assert _mv(L, t=0) == INVALID
     assert _mv(L, t=17) == UNSUPPORTED
@@ -161,6 +165,7 @@ def test_moe_validation(L):
     assert call(wsb=ws - 1) == WORKSPACE
     assert call(fmt=3) == UNSUPPORTED  # q5_K experts are not supported
     assert call(fmt=4) == UNSUPPORTED  # nor q6_K ones
+    assert call(fmt=5) == UNSUPPORTED  # nor Q8G128 ones
 
 
 def test_block_dots_validation(L):

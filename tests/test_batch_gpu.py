@@ -25,8 +25,9 @@ from gpu_util import (assert_y, gpu, host_rows, need_gpu, quantize, sample_rows,
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K]
-NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K", synth.Q6_K: "q6_K"}
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K, synth.Q8G128]
+NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K", synth.Q6_K: "q6_K",
+         synth.Q8G128: "q8g128"}
 SENTINEL = -12345.0
 
 

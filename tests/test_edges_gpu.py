@@ -1,5 +1,5 @@
 """Edge shapes and values of qmv_matvec: one row, a few rows, ragged tails, a
-single block of K, Q8_0 rows whose blocks start at every alignment, all-zero
+single block of K, Q8_0 and Q8G128 rows whose blocks start at every alignment, all-zero
 activations, the int8 weight value -128 (valid in Q8_0 but never drawn by the
 generator), and zero sub-block scales."""
 import numpy as np
@@ -12,7 +12,7 @@ from gpu_util import assert_y, gpu, need_gpu, quantize, say, to_dev, x_host
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K]
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K, synth.Q8G128]
 
 
 def _check(qmv, fmt, w, n, k, x, what):
@@ -45,6 +45,18 @@ def test_q8_0_odd_block_counts(k):
     w = synth.make_weights(synth.Q8_0, n, k, f"edge/q8/{k}").data
     for t in (1, 3, 16):
         _check(qmv, synth.Q8_0, w, n, k, x_host(t, k, f"edge/q8x/{k}"), f"q8_0 K={k}")
+
+
+@pytest.mark.parametrize("k", [128, 384, 640, 5120])
+def test_q8g128_group_counts(k):
+    """Rows of 130-byte groups: odd rows (and, with an odd group count, every
+    other group) start 2 mod 4, so the quants of every unit are read both
+    dword aligned and realigned; the int8 value -128 included."""
+    qmv = need_gpu()
+    n = 45
+    w = synth.make_weights(synth.Q8G128, n, k, f"edge/q8g/{k}", q8_range=(-128, 127)).data
+    for t in (1, 3, 16):
+        _check(qmv, synth.Q8G128, w, n, k, x_host(t, k, f"edge/q8gx/{k}"), f"q8g128 K={k}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -82,6 +82,23 @@ def test_hand_block_q6_k():
     assert np.array_equal(w, 0.5 * np.array(blk["sc"])[g] * (q[0].astype(np.float64) - 32))
 
 
+def test_hand_block_q8g128():
+    blk = hand_blocks()["q8g128"]
+    q = np.array([[i - 64 for i in range(128)]], dtype=np.int8)
+    assert synth.pack_q8g128(_f16([[blk["d"][0]]]), q).tobytes() == blk["hex"]
+    f = oracle.unpack(synth.Q8G128, np.frombuffer(blk["hex"], np.uint8), 128)
+    assert f["d"][0, 0] == 0.5 and f["q"][0].tolist() == q[0].tolist()
+    w = oracle.dequant(synth.Q8G128, np.frombuffer(blk["hex"], np.uint8), 128)
+    assert w[0].tolist() == [(i - 64) / 2 for i in range(128)]
+
+
+def test_q8g128_group_scales_in_order():
+    """Three groups with scales 1, 2, 4: each weight takes its own group's."""
+    q = np.ones((1, 384), np.int8)
+    w = oracle.dequant(synth.Q8G128, synth.pack_q8g128(_f16([[1.0, 2.0, 4.0]]), q), 384)[0]
+    assert w.tolist() == [1.0] * 128 + [2.0] * 128 + [4.0] * 128
+
+
 def test_hand_block_iq4_xs():
     blk = hand_blocks()["iq4_xs"]
     q = _pattern_q()[None]

@@ -23,8 +23,9 @@ from gpu_util import assert_y, gpu, host_rows, need_gpu, sample_rows, say, to_de
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K]
-NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K", synth.Q6_K: "q6_K"}
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K, synth.Q8G128]
+NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K", synth.Q6_K: "q6_K",
+         synth.Q8G128: "q8g128"}
 
 
 def _check_xq(qmv, xq, x):
@@ -83,6 +84,7 @@ def test_fused_edges():
         (synth.Q4_K, 1, 256, 2), (synth.IQ4_XS, 3, 256, 1),   # one super-block, one row
         (synth.Q4_K, 64, 14336, 2),                           # more quantization passes than registers hold
         (synth.IQ4_XS, 40, 14336, 2), (synth.Q6_K, 9, 768, 2),
+        (synth.Q8G128, 5, 128, 2), (synth.Q8G128, 33, 5120, 1),   # 130-byte rows; the head's K
     ]
     for fmt, n, k, t in cases:
         say(f"matvec_x edge {NAMES[fmt]} N={n} K={k} T={t}")

@@ -19,8 +19,9 @@ from gpu_util import (assert_y, gpu, host_rows, need_gpu, quantize, sample_rows,
 
 pytestmark = gpu
 
-FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K]
-NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K", synth.Q6_K: "q6_K"}
+FMTS = [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K, synth.Q8G128]
+NAMES = {synth.Q8_0: "q8_0", synth.Q4_K: "q4_K", synth.IQ4_XS: "iq4_xs", synth.Q5_K: "q5_K", synth.Q6_K: "q6_K",
+         synth.Q8G128: "q8g128"}
 
 
 def _oracle_y(fmt, w_host, k, x):
@@ -96,6 +97,7 @@ FULL = [
     ("q8_0_head_152064x5120", synth.Q8_0, 152064, 5120, (1, 2, 4, 8, 16)),
     ("q5_k_14336x4096", synth.Q5_K, 14336, 4096, (1, 2, 4, 8, 16)),
     ("q6_k_14336x4096", synth.Q6_K, 14336, 4096, (1, 2, 4, 8, 16)),
+    ("q8g128_head_152064x5120", synth.Q8G128, 152064, 5120, (1, 2, 4, 8, 16)),
 ]
 
 
@@ -146,7 +148,8 @@ def test_head_every_token_count_on_row_slice():
 def test_iq4_and_q4k_every_token_count_config_k(fmt):
     """Every T = 1..16 at the workload's reduction length on a row slice."""
     qmv = need_gpu()
-    k = {synth.Q8_0: 4096, synth.Q4_K: 4096, synth.IQ4_XS: 14336, synth.Q5_K: 4096, synth.Q6_K: 4096}[fmt]
+    k = {synth.Q8_0: 4096, synth.Q4_K: 4096, synth.IQ4_XS: 14336, synth.Q5_K: 4096, synth.Q6_K: 4096,
+         synth.Q8G128: 5120}[fmt]
     n = 700
     w = synth.make_weights(fmt, n, k, f"tk/{fmt}").data
     wd = to_dev(w)

@@ -61,9 +61,10 @@ def pin_act_invariants():
 
 def _int_weights(fmt, n, k, seed):
     """Weights whose dequantized values are integers: every fp16 scale is 1."""
-    if fmt == synth.Q8_0:
+    if fmt in (synth.Q8_0, synth.Q8G128):
         q = synth.randint(synth.stream("iq", seed), 0, n * k, -127, 127).reshape(n, k)
-        data = synth.pack_q8_0(np.ones((n, k // 32), np.float16), q.astype(np.int8))
+        pack = synth.pack_q8_0 if fmt == synth.Q8_0 else synth.pack_q8g128
+        data = pack(np.ones((n, k // synth.BLOCK_WEIGHTS[fmt]), np.float16), q.astype(np.int8))
         return data, q
     ns = k // 256
     if fmt == synth.Q6_K:  # int8 scale per 16 weights times (q - 32)
@@ -96,7 +97,7 @@ def _int_acts(t, k, seed):
 
 def pin_integer_special_case():
     for fmt, k in ((synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512),
-                   (synth.Q6_K, 512)):
+                   (synth.Q6_K, 512), (synth.Q8G128, 384)):
         data, w_int = _int_weights(fmt, 7, k, seed=fmt)
         x = _int_acts(3, k, seed=fmt)
         qs, d, s = oracle.quantize_act(x.astype(np.float32))
@@ -124,8 +125,8 @@ def pin_residual():
 
 def _dense_from_fields(wf):
     n, k = wf.data.shape[0], wf.k
-    if wf.fmt == synth.Q8_0:
-        return np.repeat(wf.d.astype(np.float64), 32, axis=1) * wf.q.astype(np.float64)
+    if wf.fmt in (synth.Q8_0, synth.Q8G128):
+        return np.repeat(wf.d.astype(np.float64), synth.BLOCK_WEIGHTS[wf.fmt], axis=1) * wf.q.astype(np.float64)
     if wf.fmt == synth.Q6_K:
         g = np.repeat(wf.sc.astype(np.float64), 16, axis=2).reshape(n, k)
         return np.repeat(wf.d.astype(np.float64), 256, axis=1) * g * (wf.q.astype(np.float64) - 32)
@@ -141,7 +142,7 @@ def _dense_from_fields(wf):
 def pin_brute_force():
     for fmt, k in ((synth.Q8_0, 32), (synth.Q8_0, 256), (synth.Q4_K, 256), (synth.Q4_K, 512),
                    (synth.IQ4_XS, 256), (synth.IQ4_XS, 512), (synth.Q5_K, 256), (synth.Q5_K, 512),
-                   (synth.Q6_K, 256), (synth.Q6_K, 512)):
+                   (synth.Q6_K, 256), (synth.Q6_K, 512), (synth.Q8G128, 128), (synth.Q8G128, 640)):
         wf = synth.make_weights(fmt, 8, k, f"bf{fmt}", keep_fields=True)
         x = synth.make_x(3, k, f"bfx{fmt}")
         qs, d, s = oracle.quantize_act(x)
@@ -155,7 +156,7 @@ def pin_brute_force():
 
 def pin_quantization_bound():
     for fmt, k in ((synth.Q8_0, 512), (synth.Q4_K, 1024), (synth.IQ4_XS, 1024), (synth.Q5_K, 1024),
-                   (synth.Q6_K, 1024)):
+                   (synth.Q6_K, 1024), (synth.Q8G128, 1024)):
         wf = synth.make_weights(fmt, 6, k, f"qb{fmt}", keep_fields=True)
         x = synth.make_x(2, k, f"qbx{fmt}")
         qs, d, s = oracle.quantize_act(x)
@@ -295,6 +296,8 @@ MUTANTS = {
     "q6k_scale_group": ("p += blk.sc[w / 16]", "p += blk.sc[w / 32]"),
     "q6k_high_bits": ("int two = (H[32 * h + l] >> (2 * j)) & 3;", "int two = (H[32 * h + l] >> j) & 3;"),
     "q6k_d_offset": ("fmt == FMT_Q6_K ? 208 : 0", "fmt == FMT_Q6_K ? 206 : 0"),
+    "q8g128_group_of_64": ("half_to_double(rd16(row + (b / 4) * 130))", "half_to_double(rd16(row + (b / 2) * 130))"),
+    "q8g128_quant_offset": ("i < 128; ++i) o->q[i] = (int8_t)b[2 + i];", "i < 128; ++i) o->q[i] = (int8_t)b[1 + i];"),
     "iq4_offset": ("(blk.ls[j] - 32) * p", "(blk.ls[j] - 31) * p"),
     "iq4_scales_h": ("(((sh >> (2 * j)) & 3) << 4)", "(((sh >> j) & 3) << 4)"),
     "iq4_nibble_half": ("o->idx[32 * j + 16 + i] = Q[16 * j + i] >> 4;", "o->idx[32 * j + 16 + i] = Q[16 * j + i] & 15;"),

@@ -44,7 +44,7 @@ def test_splitk_workload_256x65536():
     assert int(ws[:256].view(torch.int32).abs().sum()) == 0
 
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K, synth.Q8G128])
 def test_splitk_all_formats_and_token_counts(fmt):
     qmv = need_gpu()
     n, k = 77, 8192

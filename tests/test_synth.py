@@ -19,7 +19,7 @@ def test_streams_and_seeds_differ():
 
 
 @pytest.mark.parametrize("fmt,k", [(synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512),
-                                   (synth.Q6_K, 512)])
+                                   (synth.Q6_K, 512), (synth.Q8G128, 384)])
 def test_row_ranges_match_full_generation(fmt, k):
     full = synth.make_weights(fmt, 13, k, "C/W").data
     part = synth.make_weights(fmt, 13, k, "C/W", rows=(5, 11)).data
@@ -27,7 +27,7 @@ def test_row_ranges_match_full_generation(fmt, k):
 
 
 @pytest.mark.parametrize("fmt,k", [(synth.Q8_0, 96), (synth.Q4_K, 512), (synth.IQ4_XS, 768), (synth.Q5_K, 512),
-                                   (synth.Q6_K, 512)])
+                                   (synth.Q6_K, 512), (synth.Q8G128, 384)])
 def test_torch_generator_matches_numpy(fmt, k):
     from synth.device import make_weights_t
     ref = synth.make_weights(fmt, 11, k, "C/T").data
