@@ -401,9 +401,27 @@ def bench_moe(args, torch, qmv, ffn=False):
     return 0
 
 
+def device_info(torch):
+    """The GPU, its runtime and its clocks as the driver reports them (the
+    clocks are read, never set)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "clocks": None}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        cards = json.loads(r.stdout) if r.returncode == 0 else {}
+        card = next(iter(cards.values())) if cards else {}
+        info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()} or None
+    except Exception:  # no rocm-smi or unreadable output: clocks stay unrecorded
+        pass
+    return info
+
+
 def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
     """The CPU oracle (quantize + matvec, the same workload) on this host,
-    repeated until at least min_seconds of work."""
+    repeated until at least min_seconds of work; then the quantization alone
+    and the matvec on one thread, each for a few seconds."""
     import oracle
     import synth
 
@@ -420,10 +438,28 @@ def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
         el = time.perf_counter() - t0
         if el >= min_seconds or el >= max_seconds:
             break
-    return {"value": round(w.nbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+    value = w.nbytes * reps / el / 1e9
+    qreps, t0 = 0, time.perf_counter()
+    while qreps < 3 or time.perf_counter() - t0 < 1.0:
+        oracle.quantize_act(x)
+        qreps += 1
+    quant_s = (time.perf_counter() - t0) / qreps
+    rows1 = max(1, rows // 8)
+    oracle.set_threads(1)
+    reps1, t0 = 0, time.perf_counter()
+    while reps1 < 1 or time.perf_counter() - t0 < 3.0:
+        oracle.matvec(fmt, w[:rows1], k, qs, d, s)
+        reps1 += 1
+    el1 = time.perf_counter() - t0
+    oracle.set_threads(cores)
+    return {"value": round(value, 3), "unit": "GB/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"{FMT_NAME[fmt]} {rows}x{k} matvec (rows 0..{rows - 1} of {n}) at {t} "
-                      f"token(s) incl. activation quantization, {reps} repetitions in {el:.1f} s"}
+                      f"token(s) incl. activation quantization, {reps} repetitions in {el:.1f} s",
+            "quantize_us_per_call": round(quant_s * 1e6, 1),
+            "matvec_s_per_call": round(el / reps - quant_s, 4),
+            "value_1_thread": round(w[:rows1].nbytes * reps1 / el1 / 1e9, 3),
+            "sample_1_thread": f"rows 0..{rows1 - 1}, matvec only, {reps1} repetitions in {el1:.1f} s"}
 
 
 def main() -> int:
@@ -493,11 +529,20 @@ def main() -> int:
     # the same step through qmv_matvec_x (fp32 activations in, quantization
     # fused into the matvec where that is faster)
     fused_us = timed_replays(torch, lambda i: ring.fused(qmv, i), max(ring.copies, 32)) if mats == 1 else None
+    # the plain read of the same weight bytes (qmv_stream_read over the same
+    # ring): the practical ceiling of one launch streaming them
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    read_us = timed_replays(torch, lambda i: [qmv.stream_read(w.view(-1), sink) for w in ring.w[i % ring.copies]],
+                            max(ring.copies, 32), reps=20)
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(args.workload, t, src_hash)
     # a batch of equal matrices runs the variant of their stacked rows (each
     # matrix padded to a multiple of 64 rows)
-    variant = qmv.variant_name(qmv.pick_variant(fmt, mats * ((n + 63) // 64 * 64) if mats > 1 else n, k, t))
+    if mats > 1:
+        variant, slices = qmv.variant_name(qmv.pick_variant(fmt, mats * ((n + 63) // 64 * 64), k, t)), 1
+    else:
+        vi, slices = qmv.matvec_plan(fmt, n, k, t, ring.ws is not None)
+        variant = qmv.variant_name(vi)
 
     by_tokens = []
     if args.all_tokens:
@@ -508,7 +553,8 @@ def main() -> int:
                    "weight_GBps": round(r2.weight_bytes / (us * 1e-6) / 1e9, 1),
                    "hbm_frac": round(r2.weight_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "matvecs_per_s": round(1e6 / us, 1),
-                   "variant": qmv.variant_name(qmv.pick_variant(fmt, mats * n, k, tt))}
+                   "variant": qmv.variant_name(qmv.matvec_plan(fmt, n, k, tt, r2.ws is not None)[0]
+                                               if mats == 1 else qmv.pick_variant(fmt, mats * n, k, tt))}
             if mats > 1:
                 rec["separate_launches_us"] = round(timed_replays(torch, lambda i: r2.separate(qmv, i),
                                                                   max(r2.copies, 32)), 3)
@@ -541,7 +587,7 @@ def main() -> int:
                    "format": FMT_NAME[fmt], "n_rows": n, "k": k, "tokens": t, "matrices": mats,
                    "weight_bytes": ring.weight_bytes, "ring_copies": ring.copies,
                    "step": "qmv_quantize_act + " + ("qmv_matvec" if mats == 1 else "qmv_matvec_batch"),
-                   "matvec_variant": variant},
+                   "matvec_variant": variant, "k_slices_over_workgroups": slices},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "matvecs_per_s": round(1e3 / ms_per_step, 1),
         **({"matvec_x_step_us": round(fused_us, 3),
@@ -551,6 +597,12 @@ def main() -> int:
                      "traffic": traffic, "kernel_us": round(kus, 3),
                      "algorithmic_bytes_per_launch": ring.weight_bytes,
                      "kernel_sources_sha256_16": src_hash},
+        "read_ceiling": {"kernel_us": round(read_us, 3),
+                         "GBps": round(ring.weight_bytes / (read_us * 1e-6) / 1e9, 1),
+                         "frac_of_peak": round(ring.weight_bytes / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "matvec_frac_of_ceiling": round(read_us / kus, 4),
+                         "launches": mats},
+        "device": device_info(torch),
         "cpu_baseline": cpu,
     }
     if by_tokens:

@@ -306,6 +306,21 @@ qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t 
                           const void* xq, int64_t n_tok, int32_t* out, void* stream);
 
 /*
+ * qmv_stream_read -- measurement hook: reads the `bytes` bytes at p (device)
+ * once with non-temporal 16-byte loads (256-lane workgroups, four loads per
+ * lane in flight, lanes on adjacent pieces: the fastest plain read measured
+ * on MI355X), and computes nothing from them: the practical ceiling of a
+ * kernel streaming the same bytes.  Decode kernels are measured by weight
+ * bytes over kernel time (zhuai.tech GLM-5.3 page, "Performance optimization
+ * chain"); this gives the same figure for a kernel with no decode at all.
+ * sink : one uint32 (device); written only if the fold of the bytes hits a
+ *        fixed 32-bit value, so in practice never.
+ * bytes a positive multiple of 16 (else QMV_ERR_INVALID_ARG); p 16-byte and
+ * sink 4-byte aligned (else QMV_ERR_MISALIGNED).
+ */
+qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * qmv_set_tuning -- process-wide A/B switches (Castagna Veloce page, "New
  * features": each optimization can be switched off for A/B tests).  Keys:
  *   "splitk"  : -1 automatic (default), 0 never, n >= 1 force n K-slices
@@ -314,6 +329,11 @@ qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t 
  *               variant table of qmv_matvec (see qmv_variant_name); a
  *               variant whose LDS staging does not fit the device runs the
  *               lane-group kernel instead (qmv_pick_variant reports which);
+ *   "mx_slices": -1 automatic (default), 0 never, 2..32 force that many
+ *               K slices for the matrix-core kernel's split over
+ *               workgroups (it needs a workspace; automatic splits only
+ *               rows too long for one LDS chunk on too few row tiles to
+ *               fill the device);
  *   "bpc"     : 0 automatic (default), else a cap on resident workgroups
  *               per compute unit for the persistent streaming kernel;
  *   "moe_kernel": 0 automatic (default), 1 the vector-ALU expert-grouped
@@ -326,8 +346,14 @@ qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t 
 qmv_status qmv_set_tuning(const char* key, int64_t value);
 /* Name of kernel variant `index`, or NULL past the end of the table. */
 const char* qmv_variant_name(int64_t index);
-/* The variant qmv_matvec would run for these arguments (-1 if invalid). */
+/* The variant qmv_matvec would run for these arguments without a workspace
+ * (-1 if invalid). */
 int64_t qmv_pick_variant(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok);
+/* What qmv_matvec would run with (with_workspace != 0) or without a
+ * workspace of qmv_matvec_workspace_bytes bytes: *variant the kernel variant,
+ * *slices the K slices split over workgroups (1: no split).  Host only. */
+qmv_status qmv_matvec_plan(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok, int with_workspace,
+                           int64_t* variant, int* slices);
 
 #ifdef __cplusplus
 }

@@ -20,8 +20,8 @@ import torch
 __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "Q8G128", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
-    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots",
-    "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "MAX_TOKENS", "MAX_MOE_TOKENS",
+    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots", "stream_read",
+    "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "matvec_plan", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
 Q8_0, Q4_K, IQ4_XS, Q5_K, Q6_K, Q8G128 = 0, 1, 2, 3, 4, 5
@@ -88,9 +88,11 @@ def lib():
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
+        "qmv_stream_read": ([P, I64, P, P], I),
         "qmv_set_tuning": ([ctypes.c_char_p, I64], I),
         "qmv_variant_name": ([I64], ctypes.c_char_p),
         "qmv_pick_variant": ([I, I64, I64, I64], I64),
+        "qmv_matvec_plan": ([I, I64, I64, I64, I, ctypes.POINTER(I64), ctypes.POINTER(I)], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -333,6 +335,16 @@ def block_dots(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor,
     return out
 
 
+def stream_read(t: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Read every byte of t once (the plain-read ceiling of a weight stream)."""
+    _need(t, torch.uint8, "t")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=t.device)
+    _need(sink, torch.int32, "sink")
+    _check(lib().qmv_stream_read(_ptr(t), t.numel(), _ptr(sink), _stream(stream)), "qmv_stream_read")
+    return sink
+
+
 # ------------------------------------------------------------------ tuning
 def set_tuning(key: str, value: int) -> None:
     _check(lib().qmv_set_tuning(key.encode(), int(value)), f"qmv_set_tuning({key})")
@@ -353,3 +365,11 @@ def variants() -> list[str]:
 
 def pick_variant(fmt: int, n_rows: int, k: int, n_tok: int) -> int:
     return int(lib().qmv_pick_variant(fmt, n_rows, k, n_tok))
+
+
+def matvec_plan(fmt: int, n_rows: int, k: int, n_tok: int, with_workspace: bool) -> tuple[int, int]:
+    """(kernel variant, K slices over workgroups) qmv_matvec would run."""
+    v, s = ctypes.c_int64(), ctypes.c_int()
+    _check(lib().qmv_matvec_plan(fmt, n_rows, k, n_tok, int(with_workspace), ctypes.byref(v), ctypes.byref(s)),
+           "qmv_matvec_plan")
+    return int(v.value), int(s.value)

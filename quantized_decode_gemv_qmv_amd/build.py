@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libqmv.so")
 # weight format so that those instantiations build in parallel
 FORMATS = {0: "q8_0", 1: "q4_k", 2: "iq4_xs", 3: "q5_k", 4: "q6_k", 5: "q8g128"}
 SOURCES = ([(s, os.path.splitext(s)[0], []) for s in
-            ("qmv_api.hip", "qmv_variants.hip", "qmv_quant.hip", "qmv_mfma.hip", "qmv_moe.hip", "qmv_router.hip")]
+            ("qmv_api.hip", "qmv_variants.hip", "qmv_quant.hip", "qmv_mfma.hip", "qmv_moe.hip", "qmv_router.hip",
+             "qmv_measure.hip")]
            + [("qmv_matvec.hip", f"qmv_matvec_{n}", [f"-DQMV_MATVEC_FMT={f}"]) for f, n in FORMATS.items()])
 ARCH = os.environ.get("QMV_OFFLOAD_ARCH", "gfx950")
 

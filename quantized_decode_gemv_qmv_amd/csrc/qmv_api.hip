@@ -16,7 +16,6 @@ namespace {
 using namespace qmv;
 
 constexpr int64_t kSplitMaxRows = 8192;   // split-K only for few-row shapes
-constexpr int kMaxSlices = 32;
 constexpr int64_t kMoeMaxUnits = 512;     // k <= 16384 for the MoE kernel
 
 std::atomic<int64_t> g_splitk{-1};
@@ -242,6 +241,56 @@ int choose_slices(const Variant& v, int64_t n_rows, int64_t k) {
   return s < 1 ? 1 : static_cast<int>(s);
 }
 
+// The kernel of a qmv_matvec call and its cross-workgroup K slices (1:
+// none); split says whether the call uses the workspace.
+struct Plan {
+  int variant;
+  int slices;
+  bool split;
+};
+
+// With a workspace, rows too long for one LDS chunk on few row tiles run the
+// matrix-core variant measured fastest split over workgroups (4096 x 14336:
+// IQ4_XS 16 tokens 25.3 -> 19.4 us, q4_K 16 tokens 29.8 -> 26.5 us, q4_K
+// 8 tokens 18.5 -> 16.1 us), when its plan splits; -1 otherwise.
+int split_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
+  const char* name = type == QMV_IQ4_XS && n_tok > 8 ? "mx_w16_k4_r2"
+                     : type == QMV_Q4_K && n_tok > 8 ? "mx_w8_k1_r4"
+                     : type == QMV_Q4_K && n_tok > 4 ? "mx_w8_k4_r4"
+                                                      : nullptr;
+  if (name == nullptr) return -1;
+  const int v = find_variant(name);
+  const DeviceInfo dv = device_info();
+  int ups = 0;
+  return mx_split_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].ks, (int)(k / 32), (int)n_rows, dv.cus,
+                       dv.lds_per_cu, &ups) >= 2
+             ? v
+             : -1;
+}
+
+Plan make_plan(int type, int64_t n_rows, int64_t k, int64_t n_tok, bool use_ws) {
+  Plan p{choose_variant(type, n_rows, k, n_tok), 1, false};
+  if (!use_ws || g_splitk.load() == 0) return p;
+  p.split = true;
+  // forced slices belong to the lane-group kernel's split (the streaming
+  // kernels split K inside a workgroup and need no workspace)
+  if (g_splitk.load() > 0 && kVariants[p.variant].kind != 0) p.variant = find_variant("lpr64_r2");
+  if (kVariants[p.variant].kind == 0) {
+    p.slices = choose_slices(kVariants[p.variant], n_rows, k);
+  } else if (kVariants[p.variant].kind == 4) {
+    if (g_variant.load() < 0) {
+      const int sv = split_variant(type, n_rows, k, n_tok);
+      if (sv >= 0) p.variant = sv;
+    }
+    const DeviceInfo dv = device_info();
+    int ups = 0;
+    const int s = mx_split_plan(type, (int)n_tok, kVariants[p.variant].wpb, kVariants[p.variant].ks, (int)(k / 32),
+                                (int)n_rows, dv.cus, dv.lds_per_cu, &ups);
+    p.slices = s >= 2 ? s : 1;
+  }
+  return p;
+}
+
 // Split-K workspace: [one counter per row tile][partials slices x T x N].
 // The counter area has a fixed size (every variant covers >= 4 rows per
 // workgroup, and split-K is limited to kSplitMaxRows rows), so calls of
@@ -299,6 +348,11 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
     g_splitk = value;
     return QMV_OK;
   }
+  if (!std::strcmp(key, "mx_slices")) {
+    if (value < -1 || value == 1 || value > kMaxSlices) return QMV_ERR_INVALID_ARG;
+    set_mx_slices(static_cast<int>(value));
+    return QMV_OK;
+  }
   if (!std::strcmp(key, "bpc")) {
     if (value < 0 || value > 64) return QMV_ERR_INVALID_ARG;
     set_blocks_per_cu(static_cast<int>(value));
@@ -326,6 +380,19 @@ QMV_API int64_t qmv_pick_variant(qmv_type type, int64_t n_rows, int64_t k, int64
       n_tok > QMV_MAX_TOKENS)
     return -1;
   return choose_variant(type, n_rows, k, n_tok);
+}
+
+QMV_API qmv_status qmv_matvec_plan(qmv_type type, int64_t n_rows, int64_t k, int64_t n_tok, int with_workspace,
+                                   int64_t* variant, int* slices) {
+  if (!valid_type(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 || variant == nullptr ||
+      slices == nullptr)
+    return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_TOKENS) return QMV_ERR_UNSUPPORTED;
+  const bool use_ws = with_workspace != 0 && qmv_matvec_workspace_bytes(type, n_rows, k, n_tok) > 0;
+  const Plan p = make_plan(type, n_rows, k, n_tok, use_ws);
+  *variant = p.variant;
+  *slices = p.slices;
+  return QMV_OK;
 }
 
 // ------------------------------------------------------------- quantize
@@ -407,8 +474,6 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
   a.n_tok = static_cast<int>(n_tok);
   a.y = y;
   a.ldy = ldy;
-  a.variant = choose_variant(type, n_rows, k, n_tok);
-  a.slices = 1;
   a.xq = static_cast<const uint8_t*>(xq);
   a.act_bytes = static_cast<int64_t>(qmv_act_bytes(n_tok, k));
   a.off_d = static_cast<int64_t>(qmv_act_offset_d(n_tok, k));
@@ -417,14 +482,15 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
   a.cus = dv.cus;
   a.lds_per_cu = dv.lds_per_cu;
   const size_t need = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok);
-  if (ws != nullptr && need > 0) {
+  const bool use_ws = ws != nullptr && need > 0;
+  if (use_ws) {
     if (ws_bytes < need) return QMV_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return QMV_ERR_MISALIGNED;
-    // the cross-workgroup split-K path belongs to the lane-group kernel; it
-    // runs only when slices are forced (the streaming kernel splits K inside
-    // a workgroup and needs no workspace)
-    if (g_splitk.load() > 0 && kVariants[a.variant].kind != 0) a.variant = find_variant("lpr64_r2");
-    if (kVariants[a.variant].kind == 0) a.slices = choose_slices(kVariants[a.variant], n_rows, k);
+  }
+  const Plan p = make_plan(type, n_rows, k, n_tok, use_ws);
+  a.variant = p.variant;
+  a.slices = kVariants[p.variant].kind == 0 ? p.slices : 1;  // k_mx plans its own split
+  if (p.split) {
     uint8_t* b = static_cast<uint8_t*>(ws);
     a.cnt = reinterpret_cast<int*>(b);
     a.part = reinterpret_cast<float*>(b + kSplitCounterBytes);
@@ -585,6 +651,15 @@ QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, 
                                    static_cast<int>(n_rows), static_cast<int>(k / 32),
                                    act_view(xq, n_tok, k), static_cast<int>(n_tok), out,
                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
+QMV_API qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* stream) {
+  if (p == nullptr || sink == nullptr || bytes < 16 || bytes % 16) return QMV_ERR_INVALID_ARG;
+  if (bytes / 16 > (int64_t)INT32_MAX * 1024) return QMV_ERR_UNSUPPORTED;  // grid limit
+  if (!aligned(p, 16) || !aligned(sink, 4)) return QMV_ERR_MISALIGNED;
+  hipError_t e = launch_stream_read(static_cast<const uint8_t*>(p), bytes, 0x9e3779b9u, sink,
+                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 

@@ -93,6 +93,12 @@ struct StreamArgs {
   const float* x;
   int64_t ldx;
   uint8_t* xq_out;
+  // k_mx split over workgroups along K (gridDim.y slices of ups units):
+  // partial sums [slices][n_tok][n_rows] and one arrival counter per
+  // workgroup column, in the caller's workspace
+  int ups;
+  float* part;
+  int* cnt;
 };
 
 #ifdef __HIPCC__
@@ -124,6 +130,10 @@ __device__ inline void seg_store(const RowSeg& s, int t, int row, float v) {
   }
 }
 #endif
+
+// K slices of a cross-workgroup split at most (the split-K workspace holds
+// the partial sums of this many).
+constexpr int kMaxSlices = 32;
 
 // LDS bytes k_mt stages per chunk at most (two workgroups per compute unit).
 constexpr int64_t kMultiLdsBudget = 80 * 1024;
@@ -169,6 +179,15 @@ size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm);
 // Tuning: cap on k_stream workgroups per compute unit (0 = occupancy).
 void set_blocks_per_cu(int v);
 int blocks_per_cu();
+// Tuning: K slices of the matrix-core kernel's cross-workgroup split
+// (-1 automatic, 0 never, n >= 2 that many, when a workspace is given).
+void set_mx_slices(int v);
+int mx_slices();
+// Cross-workgroup K split of k_mx for format fmt, n_tok tokens and a
+// variant of wpb waves in teams of ks: the slice count (>= 2, units per
+// slice in *ups) or 0 for no split.
+int mx_split_plan(int fmt, int n_tok, int wpb, int ks, int units, int n_rows, int cus, int64_t lds_per_cu,
+                  int* ups);
 
 hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
                            int32_t* s, hipStream_t st);
@@ -181,6 +200,7 @@ hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
 template <int F>
 hipError_t launch_vector(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
+hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, uint32_t key, uint32_t* sink, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,
                              ActView x, int n_tok, int32_t* out, hipStream_t st);
 

@@ -43,6 +43,14 @@
 // teams of KS waves split a row's super-blocks; the activations are staged in
 // LDS in chunks that all waves of the workgroup walk in step; the next
 // super-block's weight loads are issued before the current one is computed.
+//
+// With few rows and a long row (fewer row tiles than compute units can hold
+// workgroups, activations that need several chunks), and a caller workspace,
+// K is split over workgroups instead (SPLIT): workgroup column y covers the
+// units y * ups .. +ups of its row tiles, staged once as one chunk, and
+// writes fp32 partial sums; the last workgroup of a column to finish sums
+// the slices in slice order (the same result on every call) and re-arms the
+// column's counter.  Nothing waits on another workgroup.
 #include "qmv_internal.h"
 #include "qmv_mfma.h"
 
@@ -53,8 +61,9 @@ namespace qmv {
 // row.  A chunk holds ipc super-blocks, a multiple of KS, so the wave's
 // super-blocks fall into the chunks in order.  Items q = i * n_it + j are
 // loaded PF items ahead of the one computed.
-template <int F, int TM, int WPB, int KS, int PF, bool CH, bool SEG>
+template <int F, int TM, int WPB, int KS, int PF, bool CH, bool SEG, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
+  static_assert(!SPLIT || (!CH && !SEG), "a split launch stages one chunk of one matrix");
   constexpr int TG = mx_tg<F>();
   constexpr int NG = (TM + TG - 1) / TG;  // token groups
   constexpr int TMP = NG * TG;            // staged token rows
@@ -74,7 +83,12 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int team = wave / KS, kw = wave % KS;
   const int n = lane & 15, s = lane >> 4;
-  const int units = a.units, kc = a.kc, T = a.n_tok;
+  // SPLIT: this workgroup's K slice starts at unit ub; `units` counts the
+  // slice's units and every unit index below is relative to it
+  const int ub = SPLIT ? (int)blockIdx.y * a.ups : 0;
+  const int units = SPLIT ? min(a.ups, a.units - ub) : a.units;
+  const int kc = a.kc, T = a.n_tok;
+  const uint8_t* const wsl = a.w + (SPLIT ? (int64_t)(ub / Fmt<F>::UPB) * Fmt<F>::BB : 0);
   const int nsb = (units + 7) >> 3;  // super-blocks of a row
   const int ipc = kc >> 3;           // super-blocks per chunk
   const int nchunk = CH ? (nsb + ipc - 1) / ipc : 1;  // CH: several chunks, one round
@@ -118,7 +132,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   u32x4 sv[SB];
   auto piece = [&](int c, int idx, const FastDiv& dq) -> const uint8_t* {
     const int t = dq.div(idx), pc = idx - t * (int)dq.d;
-    return a.xq + (uint32_t)(min(t, T - 1) * a.k + 32 * (c * kc) + 16 * pc);
+    return a.xq + (uint32_t)(min(t, T - 1) * a.k + 32 * (ub + c * kc) + 16 * pc);
   };
   auto stage_issue = [&](int c) {
     const int nq = 2 * min(kc, units - c * kc), total = TMP * nq;
@@ -156,7 +170,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int idx = base + (int)threadIdx.x + i * NT;
         const int b = idx / TMP, t = idx - b * TMP;  // TMP is a power of two
-        const int gi = min(t, T - 1) * a.nb + c0 + min(b, cu - 1);
+        const int gi = min(t, T - 1) * a.nb + ub + c0 + min(b, cu - 1);
         dv[i] = gd[gi];
         iv[i] = gs[gi];
       }
@@ -196,7 +210,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
       base = lbase;
       off = loff;
     } else {
-      base = a.w + (int64_t)tile * 16 * a.row_bytes;
+      base = wsl + (int64_t)tile * 16 * a.row_bytes;
       off = (uint32_t)(min(n, a.n_rows - 1 - tile * 16) * (int)a.row_bytes);
     }
     mx_load(base, off, 8 * min(kw + hj * KS, nsb - 1), s, units, r);
@@ -330,7 +344,15 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
           for (int r = 0; r < 4; ++r) {
             const int t = P2 ? g * 8 + 4 * s + r : g * 4 + r;
             const bool mine = P2 ? s < 2 : s == (g & 3);
-            if (mine && t < T) seg_store(sg, t, row, acc[g][r]);
+            if (mine && t < T) {
+              if constexpr (SPLIT) {
+                if (row < a.n_rows)
+                  __hip_atomic_store(&a.part[((int64_t)blockIdx.y * T + t) * a.n_rows + row], acc[g][r],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              } else {
+                seg_store(sg, t, row, acc[g][r]);
+              }
+            }
           }
       }
     } else {
@@ -353,9 +375,48 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
         for (int w = 0; w < KS; ++w) sum += red[((tm * KS + w) * TMP) * 16 + rest];
         const int tl = (int)blockIdx.x * TEAMS + tm + i * tstride;  // that team's tile
         const int row = tl * 16 + nn;
-        if (tl < tiles && t < T) seg_store(row_seg<SEG>(a, tl * 16), t, row, sum);
+        if constexpr (SPLIT) {
+          if (row < a.n_rows && t < T)
+            __hip_atomic_store(&a.part[((int64_t)blockIdx.y * T + t) * a.n_rows + row], sum,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (tl < tiles && t < T) {
+          seg_store(row_seg<SEG>(a, tl * 16), t, row, sum);
+        }
       }
       __syncthreads();  // the partials area is reused by the next round
+    }
+  }
+
+  if constexpr (SPLIT) {
+    // The last workgroup of this column (its TEAMS row tiles) to finish sums
+    // the slices' partials in slice order.  The partials are stored and
+    // loaded with device-scope atomic accesses, which the gfx950 L2 writes
+    // through and reloads (the sc1 bit), so they meet at the device's
+    // coherence point without a device-scope fence: each lane waits for its
+    // stores to be acknowledged before the barrier that precedes the
+    // counter update, and the sums are loaded only after the counter's
+    // value was seen.  (A device-scope fence here would write back and
+    // invalidate this XCD's whole L2 once per workgroup: measured 10x
+    // slower overall.)
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(&a.cnt[blockIdx.x], 1) == (int)gridDim.y - 1;
+    __syncthreads();
+    if (s_last) {
+      constexpr int RW = TEAMS * 16;
+      const int r0 = (int)blockIdx.x * RW;
+      for (int q = threadIdx.x; q < T * RW; q += NT) {
+        const int t = q / RW, row = r0 + (q - t * RW);
+        if (row < a.n_rows) {
+          float sum = 0.f;
+          for (int sl = 0; sl < (int)gridDim.y; ++sl)
+            sum += __hip_atomic_load(&a.part[((int64_t)sl * T + t) * a.n_rows + row], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          a.y[(int64_t)t * a.ldy + row] = sum;
+        }
+      }
+      if (threadIdx.x == 0) atomicExch(&a.cnt[blockIdx.x], 0);
     }
   }
 }
@@ -377,6 +438,49 @@ static int mx_chunk_units(int units, int per_unit, int step, int64_t budget) {
 // in 144 KB (then one workgroup per compute unit stages it once and walks
 // its row tiles), else chunks.
 constexpr int64_t kMxLdsBudget = 144 * 1024;
+
+// LDS bytes per staged unit and fixed LDS bytes of a k_mx workgroup.
+static int mx_per_unit(int fmt, int tmp) { return (tmp * 32 + 16) + tmp * 4 * (fmt == FQ4_K ? 2 : 1); }
+static int64_t mx_fixed(int wpb, int ks, int tmp) { return 16 + (ks > 1 ? (int64_t)wpb * tmp * 16 * 4 : 0); }
+
+int mx_split_plan(int fmt, int n_tok, int wpb, int ks, int units, int n_rows, int cus, int64_t lds_per_cu,
+                  int* ups_out) {
+  const int tg = fmt == FQ4_K ? 8 : 4;
+  const int tm = n_tok <= 4 ? 4 : n_tok <= 8 ? 8 : 16;
+  const int tmp = (tm + tg - 1) / tg * tg;
+  const int per_unit = mx_per_unit(fmt, tmp);
+  const int64_t fixed = mx_fixed(wpb, ks, tmp);
+  const int step = 8 * ks;
+  const int forced = mx_slices();
+  if (forced == 0) return 0;
+  // a slice is whole wave shares and fits one chunk in the LDS of 2 (8-wave)
+  // or 1 (16-wave) workgroups per compute unit, 64 bytes left for the
+  // arrival flag
+  const int64_t wgs = wpb <= 8 ? 2 : 1;
+  const int64_t budget = (kMxLdsBudget < lds_per_cu / wgs ? kMxLdsBudget : lds_per_cu / wgs) - 64 - fixed;
+  const int ups_max = (int)(budget / per_unit) / step * step;
+  if (ups_max < step) return 0;
+  int want = forced;
+  if (forced < 0) {
+    // automatic: rows that need several chunks unsplit, on fewer row-tile
+    // workgroups than compute units, split into as many slices as give
+    // every compute unit a workgroup -- if one chunk per slice fits in
+    // that many (measured on 4096 x 14336, q4_K and IQ4_XS at 5..16
+    // tokens: more, thinner slices cost more than the restaging they save)
+    if (mx_chunk_units(units, per_unit, step, kMxLdsBudget - fixed) >= units) return 0;
+    const int64_t cols = ((int64_t)(n_rows + 15) / 16 + wpb / ks - 1) / (wpb / ks);
+    const int64_t fill = (cus + cols - 1) / cols;
+    const int64_t s_lds = (units + ups_max - 1) / ups_max;
+    if (fill < 2 || s_lds > fill) return 0;
+    want = (int)(fill < kMaxSlices ? fill : kMaxSlices);
+  }
+  int ups = ((units + want - 1) / want + step - 1) / step * step;
+  if (ups > ups_max) ups = ups_max;  // a forced count too small to fit: more slices
+  const int slices = (units + ups - 1) / ups;
+  if (slices < 2 || slices > kMaxSlices) return 0;
+  *ups_out = ups;
+  return slices;
+}
 
 template <int F, int TM, int WPB, int KS, int PF>
 static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
@@ -400,13 +504,27 @@ static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
   sa.res = a.res;
   sa.ldr = a.ldr;
   sa.seg = a.seg;
-  const int64_t fixed = 16 + (KS > 1 ? (int64_t)WPB * TMP * 16 * 4 : 0);
-  const int per_unit = (TMP * 32 + 16) + TMP * 4 * (F == FQ4_K ? 2 : 1);
+  const int64_t fixed = mx_fixed(WPB, KS, TMP);
+  const int per_unit = mx_per_unit(F, TMP);
   sa.kc = mx_chunk_units(a.units, per_unit, 8 * KS, kMxLdsBudget - fixed);
   if (sa.kc <= 0) return hipErrorInvalidValue;
   const size_t lds = (size_t)sa.kc * per_unit + fixed;
   const int64_t tiles = (a.n_rows + 15) / 16;
   const int64_t need = (tiles + TEAMS - 1) / TEAMS;
+  if (a.part != nullptr && a.cnt != nullptr && a.seg.n == 0) {
+    int ups = 0;
+    const int slices = mx_split_plan(F, a.n_tok, WPB, KS, a.units, a.n_rows, a.cus, a.lds_per_cu, &ups);
+    if (slices >= 2) {
+      sa.kc = ups;
+      sa.ups = ups;
+      sa.part = a.part;
+      sa.cnt = a.cnt;
+      const size_t lds_s = (size_t)ups * per_unit + fixed;
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false, false, true>), dim3((unsigned)need, (unsigned)slices),
+                         dim3(64 * WPB), lds_s, st, sa);
+      return hipGetLastError();
+    }
+  }
   if (sa.kc >= a.units) {
     // one K chunk: persistent, as many workgroups as fit at once
     const int64_t per_cu = (int64_t)a.lds_per_cu / (int64_t)lds;

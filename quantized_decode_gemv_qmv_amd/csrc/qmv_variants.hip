@@ -38,6 +38,10 @@ static int g_bpc_override = 0;  // tuning: workgroups per CU cap (0 = occupancy)
 void set_blocks_per_cu(int v) { g_bpc_override = v; }
 int blocks_per_cu() { return g_bpc_override; }
 
+static int g_mx_slices = -1;  // tuning: matrix-core cross-workgroup K slices
+void set_mx_slices(int v) { g_mx_slices = v; }
+int mx_slices() { return g_mx_slices; }
+
 size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm) {
   if (v.kind >= 3) return 0;  // chunked to fit (kMultiLdsBudget)
   if (v.kind == 2) return v.xl || tm > 4 ? static_cast<size_t>(act_bytes) : 0;

@@ -175,6 +175,29 @@ def test_block_dots_validation(L):
     assert f(0, FAKE, 4, 32, FAKE, 1, FAKE + 1, None) == MISALIGNED
 
 
+def test_matvec_plan():
+    # few rows, long K, a workspace: the matrix-core kernel split over workgroups
+    v, s = q.matvec_plan(2, 4096, 14336, 16, True)
+    assert q.variant_name(v).startswith("mx_") and s >= 1
+    v0, s0 = q.matvec_plan(2, 4096, 14336, 16, False)
+    assert s0 == 1 and v0 == q.pick_variant(2, 4096, 14336, 16)
+    # many rows: never a workspace
+    assert q.matvec_plan(0, 152064, 5120, 16, True)[1] == 1
+    with pytest.raises(q.QmvError):
+        q.matvec_plan(1, 4096, 300, 1, True)
+
+
+def test_stream_read_validation(L):
+    f = L.qmv_stream_read
+    assert f(None, 4096, FAKE, None) == INVALID
+    assert f(FAKE, 4096, None, None) == INVALID
+    assert f(FAKE, 0, FAKE, None) == INVALID
+    assert f(FAKE, 8, FAKE, None) == INVALID
+    assert f(FAKE, 4104, FAKE, None) == INVALID  # not a multiple of 16
+    assert f(FAKE + 8, 4096, FAKE, None) == MISALIGNED
+    assert f(FAKE, 4096, FAKE + 2, None) == MISALIGNED
+
+
 def test_tuning_switches(L):
     assert L.qmv_set_tuning(b"bogus", 0) == INVALID
     assert L.qmv_set_tuning(None, 0) == INVALID

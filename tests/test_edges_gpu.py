@@ -108,3 +108,23 @@ def test_zero_and_extreme_scales(fmt):
         w = synth.pack_iq4_xs(d, sc, q)
     for t in (1, 16):
         _check(qmv, fmt, w, n, k, x_host(t, k, f"edge/scx/{fmt}"), "scales")
+
+
+def test_stream_read_covers_every_byte():
+    """The read hook loads every 16-byte piece, the ragged last workgroup's
+    included: a piece whose dwords fold to the hook's key (and nothing else
+    non-zero in that lane's loads) makes it store the key; otherwise it
+    stores nothing."""
+    qmv = need_gpu()
+    key = 0x9E3779B9
+    for nbytes in (16, 4096, 4096 * 3 + 48, 17825792):
+        for piece in (0, nbytes // 16 - 1):
+            say(f"stream_read bytes={nbytes} piece={piece}")
+            t = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+            sink = qmv.stream_read(t)
+            torch.cuda.synchronize()
+            assert int(sink[0]) == 0
+            t.view(torch.int32)[4 * piece + 1] = np.array(key, np.uint32).view(np.int32).item()
+            sink = qmv.stream_read(t)
+            torch.cuda.synchronize()
+            assert np.array(int(sink[0]), np.int32).view(np.uint32) == key, (nbytes, piece)

@@ -113,10 +113,13 @@ def test_full_shapes(name, fmt, n, k, tokens):
         ref = synth.make_weights(fmt, n, k, f"{name}/W", rows=(int(r), int(r) + 1)).data
         assert np.array_equal(w_rows[np.searchsorted(rows, r)], ref[0])
     x = x_host(max(tokens), k, f"{name}/x")
+    # the bench's launch configuration: a split-K workspace where the shape takes one
+    wsb = qmv.matvec_workspace_bytes(fmt, n, k, max(tokens))
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
     for t in tokens:
         say(f"full {name} T={t}")
         xq = quantize(qmv, x[:t])
-        y = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+        y = qmv.matvec(fmt, wd, n, k, xq, t, ws=ws).cpu().numpy()
         yr, mag = _oracle_y(fmt, w_rows, k, x[:t])
         assert_y(y[:, rows], yr, mag, f"{name} T={t}")
         # exact integer partials on a few aligned row ranges

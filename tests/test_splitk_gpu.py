@@ -83,3 +83,41 @@ def test_splitk_shares_workspace_across_shapes():
             assert_y(y, yr, mag, f"shared ws N={n} K={k}")
     finally:
         qmv.set_tuning("splitk", -1)
+
+
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS])
+def test_matrix_core_split_over_workgroups(fmt):
+    """The matrix-core kernel with K split over workgroups (a workspace and
+    rows longer than one LDS chunk): every matrix-core variant, token counts
+    of the three tile sizes, a ragged last row tile, repeated calls that must
+    find the counters re-armed and give the same bits, and the unsplit kernel
+    (no workspace) within the same tolerance."""
+    qmv = need_gpu()
+    n, k = 300, 14336
+    w = synth.make_weights(fmt, n, k, f"mxs/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(16, k, f"mxsx/{fmt}")
+    ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, 16), dtype=torch.uint8, device="cuda")
+    mx = [v for v in range(len(qmv.variants())) if qmv.variant_name(v).startswith("mx_")]
+    assert mx
+    try:
+        for v in mx:
+            qmv.set_tuning("variant", v)
+            for t in (16, 9, 5, 3, 1):
+                say(f"matrix-core split fmt={fmt} {qmv.variant_name(v)} T={t}")
+                xq = quantize(qmv, x[:t])
+                yr, mag = _ref(fmt, w, k, x[:t])
+                first = None
+                for rep in range(2):
+                    y = qmv.matvec(fmt, wd, n, k, xq, t, ws=ws)
+                    assert_y(y.cpu().numpy(), yr, mag, f"{qmv.variant_name(v)} T={t} rep={rep}")
+                    if first is None:
+                        first = y.clone()
+                    else:
+                        assert torch.equal(y, first), f"{qmv.variant_name(v)} T={t}"
+                y0 = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+                assert_y(y0, yr, mag, f"{qmv.variant_name(v)} T={t} unsplit")
+    finally:
+        qmv.set_tuning("variant", -1)
+    torch.cuda.synchronize()
+    assert int(ws[:2048 * 4].view(torch.int32).abs().sum()) == 0  # counters re-armed
