@@ -119,8 +119,13 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, i
   if constexpr (SPLIT) {
     // The last workgroup of a row tile to finish sums the slices in slice
     // order (deterministic) and re-arms the tile's counter for the next call.
+    // Partials are stored and loaded with device-scope atomic accesses (the
+    // gfx950 L2 writes them through and reloads them), so waiting for this
+    // lane's stores before the barrier and the counter update is enough; a
+    // device-scope fence would write back and invalidate the XCD's L2 once
+    // per workgroup.
     __shared__ int s_last;
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero
     __syncthreads();
     if (threadIdx.x == 0) {
       const int prev = atomicAdd(&cnt[blockIdx.x], 1);
@@ -128,7 +133,6 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ w, i
     }
     __syncthreads();
     if (s_last) {
-      __threadfence();
       constexpr int RWG = 4 * GPW * R;
       const int r0 = blockIdx.x * RWG;
       for (int i = threadIdx.x; i < n_tok * RWG; i += 256) {
