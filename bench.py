@@ -407,6 +407,8 @@ def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
             "hip": torch.version.hip, "torch": torch.__version__, "clocks": None}
+    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return info  # under a profiler: its preload would follow rocm-smi into a new program
     try:
         import subprocess
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
