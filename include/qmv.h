@@ -334,6 +334,9 @@ qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* s
  *               workgroups (it needs a workspace; automatic splits only
  *               rows too long for one LDS chunk on too few row tiles to
  *               fill the device);
+ *   "flat_split": 0 (default) or 1: let the LDS-staged flat kernel split K
+ *               over workgroups (with a workspace) where its workgroups would
+ *               not fill the device or a row needs several chunks;
  *   "bpc"     : 0 automatic (default), else a cap on resident workgroups
  *               per compute unit for the persistent streaming kernel;
  *   "moe_kernel": 0 automatic (default), 1 the vector-ALU expert-grouped

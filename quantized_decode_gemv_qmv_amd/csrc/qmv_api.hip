@@ -19,6 +19,13 @@ constexpr int64_t kSplitMaxRows = 8192;   // split-K only for few-row shapes
 constexpr int64_t kMoeMaxUnits = 512;     // k <= 16384 for the MoE kernel
 
 std::atomic<int64_t> g_splitk{-1};
+// The flat kernel's split over workgroups is off by default: its cross-
+// workgroup handoff adds a few microseconds at the end of kernels that take
+// 5-10 us (256 x 65536 Q8_0, one token: 10.3 us split, 7.4 us for the
+// streaming kernel's in-workgroup split), and the variant choice above
+// avoids the shapes where it won.
+std::atomic<int64_t> g_flat_split{0};
+bool flat_split_enabled() { return g_flat_split.load() != 0; }
 std::atomic<int64_t> g_variant{-1};
 
 struct EnvInit {
@@ -165,8 +172,22 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t rpc = n_rows / cus;  // rows per compute unit
   const int64_t tiles = (n_rows + 15) / 16;
   const char* name;
-  if (n_rows < 4 * (int64_t)cus && units >= 256) {
-    name = "st_k16_r1_u2";
+  const bool kq = type == QMV_Q4_K || type == QMV_Q5_K || type == QMV_Q6_K;
+  if (n_rows <= 4 * (int64_t)cus && units >= 256 && n_tok <= (kq ? 2 : 4)) {
+    // few rows, long K (measured on 256 x 32768 and 256 x 65536 Q8_0 / q4_K,
+    // 512 x 16384 Q8_0 / IQ4_XS, 1024 x 8192 IQ4_XS at 1..4 tokens): up to
+    // one row per compute unit the streaming kernel with K split over a
+    // 16-wave workgroup, while its LDS staging fits; else the flat kernel
+    // with one row per wave and four-wave workgroups (1024 x 8192 IQ4_XS at
+    // one token: 3.4 us against 7.1 us for the eight-wave variant)
+    name = n_rows <= cus && stream_fits(find_variant("st_k16_r1_u2"), k, n_tok) ? "st_k16_r1_u2" : "fl_w4_r1_u4_g";
+  } else if (n_rows < 4 * (int64_t)cus && units >= 256) {
+    // the same shapes at more tokens: where the streaming kernel's staging
+    // does not fit, the matrix-core kernel (q4_K 256 x 65536 at four tokens:
+    // 15.8 us against 46 us for the multi-token vector kernel)
+    name = stream_fits(find_variant("st_k16_r1_u2"), k, n_tok) ? "st_k16_r1_u2"
+           : has_mfma(type)                                     ? "mx_w8_k8_r4"
+                                                                : "mt_r2_w8_k4";
   } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2)) {
     name = nu <= 2 ? (type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_g")
            : nu <= 3 ? "fl_w16_r1_u3_l"
@@ -247,7 +268,29 @@ struct Plan {
   int variant;
   int slices;
   bool split;
+  int ups;  // flat kernel split: units per slice
 };
+
+// Flat-kernel (LDS-staged) split over workgroups: where the row is longer
+// than one chunk (64 * nu units per lane) or the variant's workgroup columns
+// leave compute units without a workgroup, slices of whole super-blocks of
+// at most one chunk, as many as give every compute unit a workgroup.
+// Returns the slice count (1: no split) and the units per slice in *ups.
+int flat_split(const Variant& v, int64_t n_rows, int64_t units, int64_t n_tok, int* ups) {
+  const int64_t ch = 64 * (int64_t)v.nu;
+  const int64_t cols = (n_rows + (int64_t)v.wpb * v.rows - 1) / ((int64_t)v.wpb * v.rows);
+  const int64_t cus = device_cus();
+  const int64_t s_min = (units + ch - 1) / ch;
+  const int64_t fill = (cus + cols - 1) / cols;
+  int64_t s = s_min > fill ? s_min : fill;
+  if (s < 2) return 1;
+  int64_t u = ((units + s - 1) / s + 7) / 8 * 8;
+  if (u > ch) u = ch / 8 * 8;
+  s = (units + u - 1) / u;
+  if (s < 2 || s > kMaxSlices || n_tok * u * 40 > device_info().lds_per_block) return 1;
+  *ups = static_cast<int>(u);
+  return static_cast<int>(s);
+}
 
 // With a workspace, rows too long for one LDS chunk on few row tiles run the
 // matrix-core variant measured fastest split over workgroups (4096 x 14336:
@@ -269,7 +312,7 @@ int split_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
 }
 
 Plan make_plan(int type, int64_t n_rows, int64_t k, int64_t n_tok, bool use_ws) {
-  Plan p{choose_variant(type, n_rows, k, n_tok), 1, false};
+  Plan p{choose_variant(type, n_rows, k, n_tok), 1, false, 0};
   if (!use_ws || g_splitk.load() == 0) return p;
   p.split = true;
   // forced slices belong to the lane-group kernel's split (the streaming
@@ -287,6 +330,8 @@ Plan make_plan(int type, int64_t n_rows, int64_t k, int64_t n_tok, bool use_ws) 
     const int s = mx_split_plan(type, (int)n_tok, kVariants[p.variant].wpb, kVariants[p.variant].ks, (int)(k / 32),
                                 (int)n_rows, dv.cus, dv.lds_per_cu, &ups);
     p.slices = s >= 2 ? s : 1;
+  } else if (kVariants[p.variant].kind == 2 && kVariants[p.variant].xl && flat_split_enabled()) {
+    p.slices = flat_split(kVariants[p.variant], n_rows, k / 32, n_tok, &p.ups);
   }
   return p;
 }
@@ -351,6 +396,11 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
   if (!std::strcmp(key, "mx_slices")) {
     if (value < -1 || value == 1 || value > kMaxSlices) return QMV_ERR_INVALID_ARG;
     set_mx_slices(static_cast<int>(value));
+    return QMV_OK;
+  }
+  if (!std::strcmp(key, "flat_split")) {
+    if (value < 0 || value > 1) return QMV_ERR_INVALID_ARG;
+    g_flat_split = value;
     return QMV_OK;
   }
   if (!std::strcmp(key, "bpc")) {
@@ -490,6 +540,10 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
   const Plan p = make_plan(type, n_rows, k, n_tok, use_ws);
   a.variant = p.variant;
   a.slices = kVariants[p.variant].kind == 0 ? p.slices : 1;  // k_mx plans its own split
+  if (kVariants[p.variant].kind == 2 && p.slices > 1) {
+    a.fslices = p.slices;
+    a.fups = p.ups;
+  }
   if (p.split) {
     uint8_t* b = static_cast<uint8_t*>(ws);
     a.cnt = reinterpret_cast<int*>(b);

@@ -161,6 +161,8 @@ struct MatvecLaunch {
   int64_t act_bytes, off_d, off_s;
   int cus;            // compute units of the device
   int64_t lds_per_cu; // LDS bytes per compute unit
+  // flat kernel split over workgroups (fslices > 1): slices of fups units
+  int fslices, fups;
   // split-K (slices > 1): partial sums [slices][n_tok][n_rows] and one
   // arrival counter per row tile, both in the caller's workspace
   int slices;

@@ -296,11 +296,16 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
 // routine as the quantizer kernel (so the blocks are identical).  Its x loads
 // go out before the weight loads and the quantization runs while the weights
 // are on their way; workgroup 0 also writes the blocks to a.xq_out.
-template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC, bool SEG, int QXP = 0>
+template <int F, int TM, int R, int NU, int WPB, bool XL, int OCC, bool SEG, int QXP = 0, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC))) void k_flat(StreamArgs a) {
   static_assert(R * TM <= 64, "one output per lane");
   constexpr bool QX = QXP > 0;  // QXP: x passes held in registers ahead of the weight loads
   static_assert(!QX || (XL && !SEG), "quantizing into the LDS copy");
+  // SPLIT: K split over workgroups -- workgroup column y covers units
+  // y * ups .. +ups (one chunk) of its rows, stages only that slice of the
+  // activations, and writes fp32 partials that the column's last workgroup
+  // sums in slice order (the arrival protocol of k_matvec)
+  static_assert(!SPLIT || (XL && !SEG && !QX), "a split launch stages a slice of one matrix's activations");
   constexpr int QP = QX ? QXP : 1;
   constexpr int CH = 64 * NU;
   constexpr int NT = 64 * WPB;
@@ -310,18 +315,25 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row bases
   const int row0 = (blockIdx.x * WPB + wave) * R;
-  const int units = a.units;
+  // SPLIT: unit indices below are relative to the slice's first unit ub
+  const int ub = SPLIT ? (int)blockIdx.y * a.ups : 0;
+  const int units = SPLIT ? min(a.ups, a.units - ub) : a.units;
   const int nch = (units + CH - 1) / CH;
   const RowSeg sg = row_seg<SEG>(a, row0);
   const uint8_t* wr[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) wr[r] = seg_wrow(sg, a.row_bytes, row0 + r);
+  for (int r = 0; r < R; ++r)
+    wr[r] = seg_wrow(sg, a.row_bytes, row0 + r) + (SPLIT ? (int64_t)(ub / Fmt<F>::UPB) * Fmt<F>::BB : 0);
 
   const Act gx{reinterpret_cast<const int8_t*>(a.xq), reinterpret_cast<const float*>(a.xq + a.off_d),
                reinterpret_cast<const int32_t*>(a.xq + a.off_s), a.k, a.nb};
-  const Act lx{reinterpret_cast<const int8_t*>(s_mem),
-               reinterpret_cast<const float*>(s_mem + a.off_d),
-               reinterpret_cast<const int32_t*>(s_mem + a.off_s), a.k, a.nb};
+  // the LDS copy: the whole buffer, or (SPLIT) the slice's quants [T][ups * 32]
+  // then its d [T][ups] and s [T][ups]
+  const int sk = SPLIT ? a.ups * 32 : a.k, snb = SPLIT ? a.ups : a.nb;
+  const int soff_d = SPLIT ? a.n_tok * sk : a.off_d;
+  const int soff_s = SPLIT ? soff_d + a.n_tok * snb * 4 : a.off_s;
+  const Act lx{reinterpret_cast<const int8_t*>(s_mem), reinterpret_cast<const float*>(s_mem + soff_d),
+               reinterpret_cast<const int32_t*>(s_mem + soff_s), sk, snb};
   XO xf[NU][TX];
   // Load order.  Vector-memory loads complete in issue order, so the small,
   // cache-resident activation loads go first -- the fragments themselves, or
@@ -344,9 +356,39 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
     const int t = blk / a.nb, b = blk - t * a.nb;
     return a.x + (int64_t)t * a.ldx + 32 * b + 4 * ((int)threadIdx.x & 7);
   };
+  // SPLIT staging: pq 16-byte quant pieces per token and one (d, s) pair per
+  // unit and token; the first batch (four pieces, one pair per thread) is
+  // loaded here, ahead of the weights, with clamped indices
+  const int pq = 2 * units, nq = a.n_tok * pq, ns = a.n_tok * units;
+  const float* gd = reinterpret_cast<const float*>(a.xq + a.off_d);
+  const int32_t* gs = reinterpret_cast<const int32_t*>(a.xq + a.off_s);
+  auto sq_src = [&](int idx) -> const uint8_t* {
+    const int t = idx / pq, p = idx - t * pq;
+    return a.xq + (int64_t)t * a.k + 32 * ub + 16 * p;
+  };
+  auto sq_dst = [&](int idx) -> u32x4a* {
+    const int t = idx / pq, p = idx - t * pq;
+    return reinterpret_cast<u32x4a*>(s_mem + t * sk + 16 * p);
+  };
+  auto ss_src = [&](int idx) -> int {
+    const int t = idx / units;
+    return t * a.nb + ub + (idx - t * units);
+  };
+  auto ss_dst = [&](int idx) -> int {
+    const int t = idx / units;
+    return t * snb + (idx - t * units);
+  };
+  float sdv = 0.f;
+  int32_t ssv = 0;
   if constexpr (QX) {
 #pragma unroll
     for (int p = 0; p < QP; ++p) xv[p] = *reinterpret_cast<const f32x4*>(x_piece(min(p, q_passes - 1)));
+  } else if constexpr (SPLIT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stg[i] = ld16(sq_src(min((int)threadIdx.x + i * NT, nq - 1)));
+    const int si = ss_src(min((int)threadIdx.x, ns - 1));
+    sdv = gd[si];
+    ssv = gs[si];
   } else if constexpr (XL) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) stg[i] = ld16(a.xq + 16 * (int64_t)min((int)threadIdx.x + i * NT, n16 - 1));
@@ -404,6 +446,24 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
     for (int p = 0; p < QP; ++p)
       if (p < q_passes) put(p, xv[p]);
     for (int p = QP; p < q_passes; ++p) put(p, *reinterpret_cast<const f32x4*>(x_piece(p)));  // long rows
+    __syncthreads();
+  } else if constexpr (SPLIT) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = threadIdx.x + i * NT;
+      if (idx < nq) *sq_dst(idx) = stg[i];
+    }
+    for (int idx = threadIdx.x + 4 * NT; idx < nq; idx += NT) *sq_dst(idx) = ld16(sq_src(idx));
+    float* ld = reinterpret_cast<float*>(s_mem + soff_d);
+    int32_t* ls = reinterpret_cast<int32_t*>(s_mem + soff_s);
+    if ((int)threadIdx.x < ns) {
+      ld[ss_dst(threadIdx.x)] = sdv;
+      ls[ss_dst(threadIdx.x)] = ssv;
+    }
+    for (int idx = threadIdx.x + NT; idx < ns; idx += NT) {
+      ld[ss_dst(idx)] = gd[ss_src(idx)];
+      ls[ss_dst(idx)] = gs[ss_src(idx)];
+    }
     __syncthreads();
   } else if constexpr (XL) {
 #pragma unroll
@@ -467,8 +527,38 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
     }
   const int r = lane / TM, t = lane % TM;
   const int lr = row0 + r - sg.first;
-  if (lane < R * TM && t < a.n_tok && lr < sg.rows)
+  if constexpr (SPLIT) {
+    if (lane < R * TM && t < a.n_tok && lr < sg.rows)
+      __hip_atomic_store(&a.part[((int64_t)blockIdx.y * a.n_tok + t) * a.n_rows + lr], outv, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    // The column's last workgroup sums the slices in slice order.  The
+    // partials are device-scope atomic accesses (written through and
+    // reloaded by the L2), so each lane only waits for its stores to be
+    // acknowledged before the barrier and the counter update; a device-scope
+    // fence would write back and invalidate the XCD's L2.
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(&a.cnt[blockIdx.x], 1) == (int)gridDim.y - 1;
+    __syncthreads();
+    if (s_last) {
+      constexpr int RW = WPB * R;
+      const int r0 = (int)blockIdx.x * RW;
+      for (int q = threadIdx.x; q < a.n_tok * RW; q += NT) {
+        const int tq = q / RW, row = r0 + (q - tq * RW);
+        if (row < a.n_rows) {
+          float sum = 0.f;
+          for (int sl = 0; sl < (int)gridDim.y; ++sl)
+            sum += __hip_atomic_load(&a.part[((int64_t)sl * a.n_tok + tq) * a.n_rows + row], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          a.y[(int64_t)tq * a.ldy + row] = sum;
+        }
+      }
+      if (threadIdx.x == 0) atomicExch(&a.cnt[blockIdx.x], 0);
+    }
+  } else if (lane < R * TM && t < a.n_tok && lr < sg.rows) {
     sg.y[(int64_t)t * sg.ldy + lr] = SEG && sg.res != nullptr ? outv + rv : outv;
+  }
 }
 
 // ------------------------------------------------------ multi-token kernel
@@ -761,6 +851,18 @@ static hipError_t run_flat(const MatvecLaunch& a, hipStream_t st) {
       }
     } else if (a.seg.n > 0) {
       hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, true>), dim3(grid), dim3(64 * WPB), lds, st, sa);
+    } else if (a.fslices > 1) {
+      if constexpr (XL) {
+        // K split over workgroups: a.fslices slices of a.fups units
+        sa.ups = a.fups;
+        sa.part = a.part;
+        sa.cnt = a.cnt;
+        const size_t lds_s = (size_t)a.n_tok * a.fups * 40;
+        hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false, 0, true>), dim3(grid, (unsigned)a.fslices),
+                           dim3(64 * WPB), lds_s, st, sa);
+      } else {
+        return hipErrorInvalidValue;  // only LDS-staged variants split
+      }
     } else {
       hipLaunchKernelGGL((k_flat<F, TM, R, NU, WPB, XL, OCC, false>), dim3(grid), dim3(64 * WPB), lds, st, sa);
     }

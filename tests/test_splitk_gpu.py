@@ -121,3 +121,70 @@ def test_matrix_core_split_over_workgroups(fmt):
         qmv.set_tuning("variant", -1)
     torch.cuda.synchronize()
     assert int(ws[:2048 * 4].view(torch.int32).abs().sum()) == 0  # counters re-armed
+
+
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q5_K, synth.Q6_K, synth.Q8G128])
+def test_flat_split_over_workgroups(fmt):
+    """The LDS-staged flat kernel with K split over workgroups (a workspace,
+    and rows longer than one chunk or too few rows to give every compute unit
+    a workgroup): every such variant forced, 1/3/8 tokens, a ragged row count,
+    repeated calls that must give the same bits and re-arm the counters."""
+    qmv = need_gpu()
+    n, k = 77, 8192
+    w = synth.make_weights(fmt, n, k, f"fls/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(8, k, f"flsx/{fmt}")
+    ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, 8), dtype=torch.uint8, device="cuda")
+    staged = [v for v in range(len(qmv.variants()))
+              if qmv.variant_name(v).startswith("fl_") and qmv.variant_name(v).endswith("_l")]
+    assert staged
+    split_seen = 0
+    qmv.set_tuning("flat_split", 1)
+    try:
+        for v in staged:
+            qmv.set_tuning("variant", v)
+            for t in (1, 3, 8):
+                split_seen += qmv.matvec_plan(fmt, n, k, t, True)[1] > 1
+                say(f"flat split fmt={fmt} {qmv.variant_name(v)} T={t}")
+                xq = quantize(qmv, x[:t])
+                yr, mag = _ref(fmt, w, k, x[:t])
+                first = None
+                for rep in range(2):
+                    y = qmv.matvec(fmt, wd, n, k, xq, t, ws=ws)
+                    assert_y(y.cpu().numpy(), yr, mag, f"{qmv.variant_name(v)} T={t} rep={rep}")
+                    if first is None:
+                        first = y.clone()
+                    else:
+                        assert torch.equal(y, first), f"{qmv.variant_name(v)} T={t}"
+    finally:
+        qmv.set_tuning("variant", -1)
+        qmv.set_tuning("flat_split", 0)
+    assert split_seen > 0
+    torch.cuda.synchronize()
+    assert int(ws[:2048 * 4].view(torch.int32).abs().sum()) == 0  # counters re-armed
+
+
+def test_flat_split_workload_256x65536():
+    """The few-row long-K workload through every LDS-staged flat variant
+    split over workgroups, one token, sampled against the oracle in full."""
+    qmv = need_gpu()
+    name, fmt, n, k = "q8_0_splitk_256x65536", synth.Q8_0, 256, 65536
+    wd = weights(fmt, n, k, f"{name}/W")
+    w = wd.cpu().numpy()
+    x = x_host(1, k, f"{name}/x")
+    yr, mag = _ref(fmt, w, k, x)
+    xq = quantize(qmv, x)
+    ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, 1), dtype=torch.uint8, device="cuda")
+    staged = [v for v in range(len(qmv.variants()))
+              if qmv.variant_name(v).startswith("fl_") and qmv.variant_name(v).endswith("_l")]
+    qmv.set_tuning("flat_split", 1)
+    try:
+        for v in staged:
+            qmv.set_tuning("variant", v)
+            assert qmv.matvec_plan(fmt, n, k, 1, True)[1] > 1
+            say(f"flat split {name} {qmv.variant_name(v)}")
+            y = qmv.matvec(fmt, wd, n, k, xq, 1, ws=ws).cpu().numpy()
+            assert_y(y, yr, mag, qmv.variant_name(v))
+    finally:
+        qmv.set_tuning("variant", -1)
+        qmv.set_tuning("flat_split", 0)
