@@ -190,26 +190,27 @@ __global__ __launch_bounds__(64 * WPB) void k_stream(StreamArgs a) {
     }
   };
 
+  // Stage the activation buffer (qs | d | s, the library layout) in LDS.
+  // Vector-memory loads retire in issue order, so the first SBS pieces of
+  // each thread (cache-resident) are loaded ahead of the first job's weights
+  // with clamped indices: the LDS copy and its barrier then complete while
+  // the weights are in flight instead of after them.
+  constexpr int SBS = 6;
+  const int n16 = a.act_bytes >> 4;
+  u32x4 sv[SBS];
+#pragma unroll
+  for (int i = 0; i < SBS; ++i) sv[i] = ld16(a.xq + 16 * (int64_t)min((int)threadIdx.x + i * NT, n16 - 1));
+  __builtin_amdgcn_sched_barrier(0);
   RawS<F> cur[R][NU];
   if (jobs > 0) load_job(0, cur);
-
-  // stage the activation buffer (qs | d | s, the library layout) in LDS
-  {
-    const int n16 = a.act_bytes >> 4;
-    for (int base = 0; base < n16; base += 4 * NT) {
-      u32x4 v[4];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = base + threadIdx.x + i * NT;
-        if (idx < n16) v[i] = ld16(a.xq + 16 * (int64_t)idx);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = base + threadIdx.x + i * NT;
-        if (idx < n16) reinterpret_cast<u32x4a*>(s_mem)[idx] = v[i];
-      }
-    }
+  for (int i = 0; i < SBS; ++i) {
+    const int idx = threadIdx.x + i * NT;
+    if (idx < n16) reinterpret_cast<u32x4a*>(s_mem)[idx] = sv[i];
   }
+  for (int idx = threadIdx.x + SBS * NT; idx < n16; idx += NT)  // large buffers
+    reinterpret_cast<u32x4a*>(s_mem)[idx] = ld16(a.xq + 16 * (int64_t)idx);
   __syncthreads();
   const Act x{reinterpret_cast<const int8_t*>(s_mem),
               reinterpret_cast<const float*>(s_mem + a.off_d),
