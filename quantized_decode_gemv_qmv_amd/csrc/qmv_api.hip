@@ -61,7 +61,10 @@ int64_t block_bytes(int t) {
   }
 }
 // Formats the matrix-core kernels and the MoE kernels decode.
-bool has_mfma(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS; }
+// Formats with a matrix-core decode (dense kernels), and those the
+// expert-grouped MoE kernels take.
+bool has_mfma(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS || t == QMV_Q8G128; }
+bool moe_format(int t) { return t == QMV_Q8_0 || t == QMV_Q4_K || t == QMV_IQ4_XS; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -142,23 +145,24 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 // the workload shapes (Q8_0 4096x4096, 14336x4096 and 152064x5120, q4_K,
 // q5_K and q6_K 14336x4096, IQ4_XS 4096x14336, Q8_0 256x65536, Q8G128
 // 152064x5120, 14336x4096, 4096x4096 and 4096x14336; 1..16 tokens):
-//   - too few rows to give every compute unit several waves, long K: the
-//     streaming kernel with K split over a 16-wave workgroup;
+//   - up to 1024 rows of at least 256 blocks, few tokens: up to one row
+//     per compute unit the streaming kernel with K split over a 16-wave
+//     workgroup (while its staging fits), else the flat kernel with one
+//     row per wave in four-wave workgroups;
 //   - up to two tokens (four for Q8_0): the flat kernel (one wave per row
 //     group, all loads issued at once), its units per lane sized so that one
 //     chunk covers the row;
 //   - 3..8 tokens: the matrix-core kernel for IQ4_XS (and q4_K from five
 //     tokens), 16-wave workgroups with K split so that about 4096 waves
 //     cover the rows; otherwise the multi-token vector kernel;
-//   - 9..16 tokens: the matrix-core kernel (for Q8_0 only from 128 rows
-//     per compute unit), 8-wave workgroups with a four-deep load ring (the
+//   - 9..16 tokens: the matrix-core kernel (for Q8_0 and Q8G128 only from
+//     128 rows per compute unit), 8-wave workgroups with a four-deep load ring (the
 //     register budget of the 16-token tiles);
 //   - q5_K and q6_K have no matrix-core decode: from three tokens the
 //     multi-token vector kernel (q5_K, and q6_K on long rows) or the flat
 //     one (q6_K while one chunk of 128 units per lane covers the row);
-//   - Q8_0 at 5..8 tokens (and from nine on fewer than 128 rows per
-//     compute unit), Q8G128 (no matrix-core decode either) from three: by
-//     rows per compute unit, the flat kernel with 16-wave
+//   - Q8_0 at 5..8 tokens, Q8G128 at 3..8 (and both from nine on fewer
+//     than 128 rows per compute unit): by rows per compute unit, the flat kernel with 16-wave
 //     workgroups on many rows (the multi-token one from nine tokens), the
 //     multi-token kernel with two rows per lane group in between, and the
 //     flat kernel (or, on long rows from nine tokens, the multi-token one
@@ -202,11 +206,10 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
       name = n_tok > 8 ? "fl_w16_r1_u2_l" : n_tok > 4 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u2_l";
     else
       name = n_tok > 8 ? "mt_r4_w8_k2" : "mt_r2_w8_k2";
-  } else if ((type == QMV_Q8_0 && (n_tok <= 8 || rpc < 128)) || type == QMV_Q8G128) {
-    // Q8_0 at 5..8 tokens (and beyond on fewer than 128 rows per compute
-    // unit, where its matrix-core kernel is slower), Q8G128 (no matrix-core
-    // decode) from three: measured on 152064x5120, 14336x4096, 4096x4096
-    // and 4096x14336
+  } else if ((type == QMV_Q8_0 || type == QMV_Q8G128) && (n_tok <= 8 || rpc < 128)) {
+    // Q8_0 at 5..8 tokens, Q8G128 at 3..8 (and both beyond on fewer than
+    // 128 rows per compute unit, where the matrix-core kernel is slower):
+    // measured on 152064x5120, 14336x4096, 4096x4096 and 4096x14336
     if (rpc >= 128)
       name = n_tok > 8 ? "mt_r4_w4_k1" : nu <= 2 ? "fl_w16_r1_u2_l" : "fl_w16_r1_u3_l";
     else if (rpc >= 32)
@@ -720,7 +723,7 @@ QMV_API qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink,
 // ------------------------------------------------------------------ MoE
 QMV_API size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t n_rows,
                                        int64_t k, int64_t n_tok, int64_t top_k) {
-  if (!valid_type(type) || !has_mfma(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
+  if (!valid_type(type) || !moe_format(type) || n_rows < 1 || k < 1 || k % block_k(type) || n_tok < 1 ||
       n_tok > QMV_MAX_MOE_TOKENS || top_k < 1 || top_k > QMV_MAX_TOP_K || n_experts < 1 ||
       n_experts > QMV_MAX_EXPERTS || k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows)
     return 0;
@@ -738,7 +741,7 @@ QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_expert
       top_k < 1 || n_experts < 1 || (x_per_slot != 0 && x_per_slot != 1))
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_MOE_TOKENS || top_k > QMV_MAX_TOP_K || n_experts > QMV_MAX_EXPERTS ||
-      k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows || !has_mfma(type))
+      k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows || !moe_format(type))
     return QMV_ERR_UNSUPPORTED;
   if (n_experts * n_rows > INT32_MAX) return QMV_ERR_UNSUPPORTED;
   if (!aligned(xq, 256) || !aligned(ids, 4) || !aligned(y, 4) ||

@@ -27,6 +27,9 @@ template <> struct MxRaw<FIQ4_XS> {
 template <> struct MxRaw<FQ8_0> {
   Raw<FQ8_0> b[2];  // span p: 32-block 8i + 4p + s
 };
+template <> struct MxRaw<FQ8G128> {
+  Raw<FQ8G128> b[2];  // span p: 32-block 8i + 4p + s (a quarter of group 2i + p)
+};
 
 // Loads of one lane for the super-block starting at unit u0: `base` is the
 // wave-uniform address of the tile's first row, `off` the lane's row offset
@@ -46,6 +49,15 @@ __device__ __forceinline__ void mx_load(const uint8_t* base, uint32_t off, int u
 // Q8_0 rows need not be a whole number of super-blocks: units past the row
 // end re-read the last unit (their scale is zeroed at decode).
 __device__ __forceinline__ void mx_load(const uint8_t* base, uint32_t off, int u0, int s, int units, MxRaw<FQ8_0>& r) {
+  load_unit(base + off, min(u0 + s, units - 1), r.b[0]);
+  load_unit(base + off, min(u0 + 4 + s, units - 1), r.b[1]);
+}
+
+// Q8G128: a super-block is two 128-weight groups; span p is group 2i + p and
+// lane group s its quarter s.  Rows need not be a whole number of
+// super-blocks: units past the row end re-read the last unit (their scale is
+// zeroed at decode).
+__device__ __forceinline__ void mx_load(const uint8_t* base, uint32_t off, int u0, int s, int units, MxRaw<FQ8G128>& r) {
   load_unit(base + off, min(u0 + s, units - 1), r.b[0]);
   load_unit(base + off, min(u0 + 4 + s, units - 1), r.b[1]);
 }
@@ -107,6 +119,16 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FQ8_0>& r, int p, int s, i
   o.b[1] = u32x4{d.q[4], d.q[5], d.q[6], d.q[7]};
   const bool ok = u0 + 4 * p + s < units;
   o.dw[0] = o.dw[1] = ok ? d.d : 0.f;
+  o.wm[0] = o.wm[1] = 0.f;
+}
+
+__device__ __forceinline__ void mx_decode(const MxRaw<FQ8G128>& r, int p, int s, int u0, int units, MxDec& o) {
+  const bool ok = u0 + 4 * p + s < units;
+  DecO<FQ8G128> d;
+  decode_own(r.b[p], 0, 0, ok, d);
+  o.b[0] = u32x4{d.q[0], d.q[1], d.q[2], d.q[3]};
+  o.b[1] = u32x4{d.q[4], d.q[5], d.q[6], d.q[7]};
+  o.dw[0] = o.dw[1] = d.sc;
   o.wm[0] = o.wm[1] = 0.f;
 }
 

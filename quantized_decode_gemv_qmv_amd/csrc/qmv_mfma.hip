@@ -577,6 +577,7 @@ hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st) {
     case FQ8_0: return run_mx_tokens<FQ8_0>(a, v, st);
     case FQ4_K: return run_mx_tokens<FQ4_K>(a, v, st);
     case FIQ4_XS: return run_mx_tokens<FIQ4_XS>(a, v, st);
+    case FQ8G128: return run_mx_tokens<FQ8G128>(a, v, st);
     default: return hipErrorInvalidValue;
   }
 }

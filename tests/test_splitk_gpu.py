@@ -85,7 +85,7 @@ def test_splitk_shares_workspace_across_shapes():
         qmv.set_tuning("splitk", -1)
 
 
-@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS])
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS, synth.Q8G128])
 def test_matrix_core_split_over_workgroups(fmt):
     """The matrix-core kernel with K split over workgroups (a workspace and
     rows longer than one LDS chunk): every matrix-core variant, token counts
