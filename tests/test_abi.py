@@ -207,6 +207,11 @@ def test_tuning_switches(L):
     assert L.qmv_set_tuning(b"splitk", -1) == OK
     assert L.qmv_set_tuning(b"moe_kernel", 3) == INVALID
     assert L.qmv_set_tuning(b"moe_kernel", 0) == OK
+    for bad in (-2, 1, 33):
+        assert L.qmv_set_tuning(b"mx_slices", bad) == INVALID
+    assert L.qmv_set_tuning(b"mx_slices", -1) == OK
+    assert L.qmv_set_tuning(b"flat_split", 2) == INVALID
+    assert L.qmv_set_tuning(b"flat_split", 0) == OK
     assert q.variant_name(-1) is None and q.variant_name(len(q.variants())) is None
     assert q.pick_variant(1, 14336, 4096, 1) >= 0
     assert q.pick_variant(1, 14336, 4096, 17) == -1

@@ -188,3 +188,30 @@ def test_flat_split_workload_256x65536():
     finally:
         qmv.set_tuning("variant", -1)
         qmv.set_tuning("flat_split", 0)
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS])
+def test_matrix_core_forced_slice_counts(fmt):
+    """Forced K slice counts of the matrix-core split (tuning key mx_slices),
+    including counts whose slices would not fit and so take more, on a
+    single-chunk and a multi-chunk row; 0 turns the split off."""
+    qmv = need_gpu()
+    v16 = qmv.variants().index("mx_w16_k4_r2")
+    try:
+        qmv.set_tuning("variant", v16)
+        for n, k in ((96, 4096), (200, 14336)):
+            w = synth.make_weights(fmt, n, k, f"mxf/{fmt}/{k}").data
+            wd = to_dev(w)
+            x = x_host(16, k, f"mxfx/{k}")
+            ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, 16), dtype=torch.uint8, device="cuda")
+            for t in (16, 6):
+                xq = quantize(qmv, x[:t])
+                yr, mag = _ref(fmt, w, k, x[:t])
+                for sl in (0, 2, 3, 5, 32, -1):
+                    qmv.set_tuning("mx_slices", sl)
+                    say(f"forced mx slices fmt={fmt} N={n} K={k} T={t} slices={sl}")
+                    y = qmv.matvec(fmt, wd, n, k, xq, t, ws=ws).cpu().numpy()
+                    assert_y(y, yr, mag, f"N={n} K={k} T={t} slices={sl}")
+    finally:
+        qmv.set_tuning("mx_slices", -1)
+        qmv.set_tuning("variant", -1)
