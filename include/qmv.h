@@ -214,11 +214,15 @@ qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int64_t k, c
  * xq   : activation buffer of qmv_act_bytes(n_tok, k) bytes (device, 256-byte
  *        aligned); receives Q8(x) for reuse by later calls (another matrix
  *        over the same activations).
- * w, n_rows, k, n_tok, y, ldy: as for qmv_matvec (no split-K workspace).
+ * w, n_rows, k, n_tok, y, ldy, ws, ws_bytes: as for qmv_matvec (the
+ *        workspace, optional, serves the two-launch path's matvec; every
+ *        argument, the workspace's included, is validated before anything
+ *        is enqueued).
  * Asynchronous on `stream`; allocates nothing.
  */
 qmv_status qmv_matvec_x(qmv_type type, const void* w, int64_t n_rows, int64_t k, const float* x,
-                        int64_t ldx, int64_t n_tok, float* y, int64_t ldy, void* xq, void* stream);
+                        int64_t ldx, int64_t n_tok, float* y, int64_t ldy, void* xq, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /*
  * qmv_matvec_batch -- sibling matvecs over one activation buffer in one

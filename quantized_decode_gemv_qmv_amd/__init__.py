@@ -84,7 +84,7 @@ def lib():
         "qmv_matvec_workspace_bytes": ([I, I64, I64, I64], SZ),
         "qmv_matvec": ([I, P, I64, I64, P, I64, P, I64, P, SZ, P], I),
         "qmv_matvec_batch": ([I, ctypes.POINTER(_Item), I64, I64, P, I64, P], I),
-        "qmv_matvec_x": ([I, P, I64, I64, P, I64, I64, P, I64, P, P], I),
+        "qmv_matvec_x": ([I, P, I64, I64, P, I64, I64, P, I64, P, P, SZ, P], I),
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
@@ -239,7 +239,8 @@ def matvec(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor, n_t
 
 
 def matvec_x(fmt: int, w: torch.Tensor, n_rows: int, k: int, x: torch.Tensor,
-             xq: torch.Tensor | None = None, y: torch.Tensor | None = None, stream=None):
+             xq: torch.Tensor | None = None, y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+             stream=None):
     """The decode step from fp32 x [T][K]: (y [T][N] = W Q8(x), xq = Q8(x)).
     One launch for one or two tokens (the matvec quantizes x itself)."""
     _need(w, torch.uint8, "w")
@@ -257,8 +258,10 @@ def matvec_x(fmt: int, w: torch.Tensor, n_rows: int, k: int, x: torch.Tensor,
         raise ValueError("y must be a float32 CUDA tensor [T][ldy] with unit column stride")
     if w.numel() < n_rows * row_bytes(fmt, k):
         raise ValueError("w holds fewer than n_rows rows")
+    if ws is not None:
+        _need(ws, torch.uint8, "ws")
     _check(lib().qmv_matvec_x(fmt, _ptr(w), n_rows, k, _ptr(x), _ld(x), n_tok, _ptr(y), _ld(y), _ptr(xq),
-                              _stream(stream)), "qmv_matvec_x")
+                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "qmv_matvec_x")
     return y, xq
 
 

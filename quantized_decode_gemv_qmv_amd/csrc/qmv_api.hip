@@ -580,18 +580,25 @@ static int fused_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
 }
 
 QMV_API qmv_status qmv_matvec_x(qmv_type type, const void* w, int64_t n_rows, int64_t k, const float* x,
-                                int64_t ldx, int64_t n_tok, float* y, int64_t ldy, void* xq, void* stream) {
+                                int64_t ldx, int64_t n_tok, float* y, int64_t ldy, void* xq, void* ws,
+                                size_t ws_bytes, void* stream) {
   qmv_status st = check_weights(type, w, n_rows, k);
   if (st != QMV_OK) return st;
   if (x == nullptr || xq == nullptr || y == nullptr || ldy < n_rows || n_tok < 1 || ldx < k || ldx % 4)
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_TOKENS) return QMV_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(xq, 256) || !aligned(y, 4)) return QMV_ERR_MISALIGNED;
+  // the workspace as qmv_matvec checks it, before the quantizer is enqueued
+  const size_t need = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok);
+  if (ws != nullptr && need > 0) {
+    if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return QMV_ERR_MISALIGNED;
+  }
   const int v = fused_variant(type, n_rows, k, n_tok);
   if (v < 0) {  // two launches
     st = qmv_quantize_act(x, ldx, n_tok, k, xq, stream);
     if (st != QMV_OK) return st;
-    return qmv_matvec(type, w, n_rows, k, xq, n_tok, y, ldy, nullptr, 0, stream);
+    return qmv_matvec(type, w, n_rows, k, xq, n_tok, y, ldy, ws, ws_bytes, stream);
   }
   MatvecLaunch a{};
   a.fmt = type;

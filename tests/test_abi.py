@@ -232,9 +232,10 @@ def test_matvec_x_validation(L):
     f = L.qmv_matvec_x
 
     def call(**kw):
-        a = dict(fmt=1, w=FAKE, n=4, k=256, x=FAKE, ldx=256, t=1, y=FAKE, ldy=4, xq=FAKE)
+        a = dict(fmt=1, w=FAKE, n=4, k=256, x=FAKE, ldx=256, t=1, y=FAKE, ldy=4, xq=FAKE, ws=None, wsb=0)
         a.update(kw)
-        return f(a["fmt"], a["w"], a["n"], a["k"], a["x"], a["ldx"], a["t"], a["y"], a["ldy"], a["xq"], None)
+        return f(a["fmt"], a["w"], a["n"], a["k"], a["x"], a["ldx"], a["t"], a["y"], a["ldy"], a["xq"], a["ws"],
+                 a["wsb"], None)
 
     assert call(x=None) == INVALID
     assert call(xq=None) == INVALID
@@ -248,6 +249,10 @@ def test_matvec_x_validation(L):
     assert call(t=17) == UNSUPPORTED
     assert call(x=FAKE + 4) == MISALIGNED
     assert call(xq=FAKE + 128) == MISALIGNED
+    need = q.matvec_workspace_bytes(1, 4, 256, 1)
+    assert need > 0
+    assert call(ws=FAKE, wsb=need - 1) == WORKSPACE  # checked before the quantizer is enqueued
+    assert call(ws=FAKE + 64, wsb=need) == MISALIGNED
     assert call(w=FAKE + 8) == MISALIGNED
 
 

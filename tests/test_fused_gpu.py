@@ -122,3 +122,26 @@ def test_fused_full_shapes(name, fmt, n, k):
         qs, d, s = _check_xq(qmv, xq, x[:t])
         yr, mag = oracle.matvec(fmt, wh, k, qs, d, s)
         assert_y(y.cpu().numpy()[:, rows], yr, mag, f"{name} T={t}")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q4_K, synth.IQ4_XS, synth.Q8_0])
+def test_fused_with_workspace_matches_split_matvec(fmt):
+    """With a split-K workspace the two-launch path runs the same split
+    matvec as qmv_matvec with that workspace: the same bits, on a few-row
+    long-K shape at every tile size."""
+    qmv = need_gpu()
+    n, k = 300, 14336
+    w = synth.make_weights(fmt, n, k, f"fws/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(16, k, f"fwsx/{fmt}")
+    ws = torch.zeros(qmv.matvec_workspace_bytes(fmt, n, k, 16), dtype=torch.uint8, device="cuda")
+    for t in (1, 5, 16):
+        say(f"matvec_x with workspace {NAMES[fmt]} T={t}")
+        xt = to_dev(x[:t])
+        y, xq = qmv.matvec_x(fmt, wd, n, k, xt, ws=ws)
+        ref = qmv.matvec(fmt, wd, n, k, qmv.quantize_act(xt), t, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"T={t}"
+        qs, d, s = _check_xq(qmv, xq, x[:t])
+        yr, mag = oracle.matvec(fmt, w, k, qs, d, s)
+        assert_y(y.cpu().numpy(), yr, mag, f"{NAMES[fmt]} T={t} ws")
