@@ -1,14 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized decode matvec on one MI355X.
 
-One step is one pass of the hot path over one batch of tokens: the fp32
-activations quantized to Q8 blocks and the block-quantized matvec, through
-the library's decode-step entry point qmv_matvec_x (which fuses the
-quantization into the matvec where that is faster, else runs
-qmv_quantize_act then qmv_matvec, with the split-K workspace where the shape
-takes one); sibling matrices run qmv_quantize_act then qmv_matvec_batch.  The
-two-launch step is reported beside it.  The default workload is the q4_K
-14336 x 4096 matvec at one token; --workload / --tokens select the others.  Inputs are synthetic
+One step is one pass of the hot path over one batch of tokens: quantize the
+fp32 activations to Q8 blocks (qmv_quantize_act) and run the block-quantized
+matvec (qmv_matvec, with the split-K workspace where the shape takes one;
+qmv_matvec_batch for sibling matrices), so that the roofline's kernel is the
+matvec the step runs.  The same step through qmv_matvec_x (the quantization
+fused into the matvec where that is faster) is reported beside it.  The
+default workload is the q4_K 14336 x 4096 matvec at one token; --workload /
+--tokens select the others.  Inputs are synthetic
 (seeded generator) and resident in HBM before timing starts.
 
 The weights are read from a ring of copies of at least 1 GiB, one copy per
@@ -114,16 +114,6 @@ class Ring:
         self.ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
 
     def step(self, qmv, i):
-        """One decode step from fp32 activations: qmv_matvec_x for one
-        matrix (quantization fused into the matvec where that is faster,
-        else quantize then the matvec, with the workspace), quantize then
-        qmv_matvec_batch for siblings."""
-        if self.mats == 1:
-            self.fused(qmv, i)
-        else:
-            self.two_launch(qmv, i)
-
-    def two_launch(self, qmv, i):
         qmv.quantize_act(self.x[i % 8], out=self.xq)
         self.matvec_only(qmv, i)
 
@@ -542,8 +532,9 @@ def main() -> int:
 
     kus = kernel_us(torch, qmv, ring)
     achieved = ring.weight_bytes / (kus * 1e-6) / 1e9
-    # the step as two launches (qmv_quantize_act, then qmv_matvec) for comparison
-    two_us = timed_replays(torch, lambda i: ring.two_launch(qmv, i), max(ring.copies, 32)) if mats == 1 else None
+    # the same step through qmv_matvec_x (fp32 activations in, quantization
+    # fused into the matvec where that is faster)
+    fused_us = timed_replays(torch, lambda i: ring.fused(qmv, i), max(ring.copies, 32)) if mats == 1 else None
     # the plain read of the same weight bytes (qmv_stream_read over the same
     # ring): the practical ceiling of one launch streaming them
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -601,14 +592,12 @@ def main() -> int:
                                 f"{mats} sibling {FMT_NAME[fmt]} matvecs {n}x{k} in one launch, {t} token(s)"),
                    "format": FMT_NAME[fmt], "n_rows": n, "k": k, "tokens": t, "matrices": mats,
                    "weight_bytes": ring.weight_bytes, "ring_copies": ring.copies,
-                   "step": ("qmv_matvec_x (fp32 x in; the Q8 quantization fused into the matvec where faster, "
-                            "else qmv_quantize_act then the matvec)" if mats == 1 else
-                            "qmv_quantize_act + qmv_matvec_batch"),
+                   "step": "qmv_quantize_act + " + ("qmv_matvec" if mats == 1 else "qmv_matvec_batch"),
                    "matvec_variant": variant, "k_slices_over_workgroups": slices},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "matvecs_per_s": round(1e3 / ms_per_step, 1),
-        **({"two_launch_step_us": round(two_us, 3),
-            "two_launch_step_GBps": round(ring.weight_bytes / (two_us * 1e-6) / 1e9, 1)} if two_us else {}),
+        **({"matvec_x_step_us": round(fused_us, 3),
+            "matvec_x_step_GBps": round(ring.weight_bytes / (fused_us * 1e-6) / 1e9, 1)} if fused_us else {}),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(kus, 3),
