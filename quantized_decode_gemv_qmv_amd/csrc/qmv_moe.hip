@@ -450,16 +450,30 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
 }
 
 // y[t][n] = sum over valid slots s, in slot order, of rw[t][s] * part[t*top_k+s][n].
+// Every slot's id, route weight and output are loaded before any is used (a
+// slot's output row exists whether or not its id is valid), so the loads
+// are in flight together instead of one id-then-output round trip per slot;
+// the valid slots are then summed in slot order.
+constexpr int kCombineMaxTopK = 16;
 __global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)a.n_tok * a.n_rows) return;
   const int t = (int)(idx / a.n_rows), n = (int)(idx % a.n_rows);
-  float sum = 0.f;
-  for (int s = 0; s < a.top_k; ++s) {
-    const int sl = t * a.top_k + s;
-    const int e = a.ids[sl];
-    if (e >= 0 && e < a.n_experts) sum += a.rw[sl] * a.part[(int64_t)sl * a.n_rows + n];
+  int e[kCombineMaxTopK];
+  float wv[kCombineMaxTopK], pv[kCombineMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kCombineMaxTopK; ++s) {
+    if (s < a.top_k) {  // uniform over the grid
+      const int sl = t * a.top_k + s;
+      e[s] = a.ids[sl];
+      wv[s] = a.rw[sl];
+      pv[s] = a.part[(int64_t)sl * a.n_rows + n];
+    }
   }
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kCombineMaxTopK; ++s)
+    if (s < a.top_k && e[s] >= 0 && e[s] < a.n_experts) sum += wv[s] * pv[s];
   a.y[idx] = sum;
 }
 
