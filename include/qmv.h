@@ -184,7 +184,11 @@ qmv_status qmv_router_topk(const float* x, int64_t ldx, int64_t n_tok, int64_t k
  * y    : fp32 [n_tok][ldy] (device, 4-byte aligned), ldy >= n_rows; columns
  *        0..n_rows-1 of each row are overwritten, the rest are untouched.
  * ws   : optional workspace (device, 256-byte aligned) enabling the split-K
- *        path for few-row long-K shapes; NULL runs the single-pass kernel.
+ *        paths for few-row long-K shapes (K split over the workgroups of
+ *        one launch); NULL runs the single-pass kernel.  A split call sums
+ *        in another order than the single-pass kernel, so its fp32 result
+ *        may differ from that one's in rounding (both within the stated
+ *        tolerance); it is the same on every call with the same arguments.
  *        It must hold qmv_matvec_workspace_bytes(type, n_rows, k, n_tok)
  *        bytes, be zero-filled once when allocated, and is left in that state
  *        by every completed call (its counters reset themselves).  One
