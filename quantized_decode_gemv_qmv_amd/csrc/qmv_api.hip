@@ -192,6 +192,8 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     name = stream_fits(find_variant("st_k16_r1_u2"), k, n_tok) ? "st_k16_r1_u2"
            : has_mfma(type)                                     ? "mx_w8_k8_r4"
                                                                 : "mt_r2_w8_k4";
+  } else if (type == QMV_Q8G128 && n_tok == 2 && rpc >= 128) {
+    name = "st_w4_r1_u3";  // the head at two tokens: 144.0 / 142.0 us against 151.0 / 150.4 (two boxes)
   } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2)) {
     name = nu <= 2 ? (type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_g")
            : nu <= 3 ? "fl_w16_r1_u3_l"
