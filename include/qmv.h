@@ -349,7 +349,9 @@ qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* s
  *               per compute unit for the persistent streaming kernel;
  *   "moe_kernel": 0 automatic (default), 1 the vector-ALU expert-grouped
  *               kernel, 2 the matrix-core one (which falls back to the
- *               vector-ALU kernel when its staged rows do not fit in LDS).
+ *               vector-ALU kernel when its staged rows do not fit in LDS),
+ *               3 the few-slot flat kernel (each slot's expert rows
+ *               streamed without grouping slots by expert).
  * The environment variables QMV_SPLITK, QMV_VARIANT and QMV_MOE_KERNEL set
  * the same switches when the library loads.  Returns QMV_ERR_INVALID_ARG for an unknown key or
  * value.

@@ -38,7 +38,7 @@ struct EnvInit {
     if (const char* v = std::getenv("QMV_VARIANT")) g_variant = std::atoll(v);
     if (const char* v = std::getenv("QMV_MOE_KERNEL")) {
       const int k = std::atoi(v);
-      if (k >= 0 && k <= 2) set_moe_kernel(k);
+      if (k >= 0 && k <= 3) set_moe_kernel(k);
     }
   }
 } g_env_init;
@@ -414,7 +414,7 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
     return QMV_OK;
   }
   if (!std::strcmp(key, "moe_kernel")) {
-    if (value < 0 || value > 2) return QMV_ERR_INVALID_ARG;
+    if (value < 0 || value > 3) return QMV_ERR_INVALID_ARG;
     set_moe_kernel(static_cast<int>(value));
     return QMV_OK;
   }

@@ -477,6 +477,73 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
   a.y[idx] = sum;
 }
 
+// Few-slot routed matvec (decode): with about one slot per routed expert
+// there is no weight reuse to group for, and k_moe's routing sort and
+// per-item staging only delay the weight stream.  k_moe_flat reads its
+// slot's expert id once and streams that expert's rows as the dense flat
+// kernel does: workgroup (x, y) takes rows x * WPB * R .. of slot y, each
+// lane issuing every weight load of its R rows (NU units per row) at once,
+// behind its activation fragments (cache-resident).  A duplicated expert is
+// read once per slot.  Outputs per slot, written as k_moe writes them (to y,
+// or to the workspace for the combine); a dropped slot's row is zero.
+template <int F, int NU, int R, int WPB>
+__global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.y;
+  const int e = a.ids[slot];
+  const bool valid = e >= 0 && e < a.n_experts;
+  const int units = a.units;
+  const int row0 = (blockIdx.x * WPB + wave) * R;
+  const int xr = a.x_per_slot ? slot : slot / a.top_k;
+  const Act gx{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
+  XO xf[NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lane + 64 * q, units - 1), xf[q]);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    wr[r] = a.w + ((int64_t)(valid ? e : 0) * a.n_rows + min(row0 + r, a.n_rows - 1)) * a.row_bytes;
+  RawS<F> cur[R][NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+  __builtin_amdgcn_sched_barrier(0);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int q = 0; q < NU; ++q) {
+    const int uraw = lane + 64 * q;
+    const bool ok = uraw < units;
+    const int u = ok ? uraw : units - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      DecO<F> dec;
+      decode_own(cur[r][q], u, lane & 1, ok, dec);
+      const int dv = own_pass<F>(own_first(dec, xf[q].f));
+      acc[r] = own_apply(dec, own_second(dec, xf[q].s, dv), xf[q].p, acc[r]);
+    }
+  }
+  float outv = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float sv = wave_sum(acc[r]);
+    outv = lane == r ? sv : outv;
+  }
+  if (lane < R && row0 + lane < a.n_rows) {
+    float* out = a.rw == nullptr ? a.y : a.part;
+    out[(int64_t)slot * a.n_rows + row0 + lane] = valid ? outv : 0.f;
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    int drop = 0;
+    for (int i = 0; i < a.n_tok * a.top_k; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
+    a.err[0] = drop;
+  }
+}
+
 // Lanes per row and units per lane for a row of `units` units.
 static int moe_lpr(int units) { return units <= 64 ? 16 : 64; }
 static int moe_nu(int units) {
@@ -613,14 +680,47 @@ static hipError_t run_moe_mx(const MoeLaunch& a0, hipStream_t st) {
   return hipGetLastError();
 }
 
-static int g_moe_kernel = 0;  // tuning: 0 automatic, 1 vector-ALU kernel, 2 matrix-core kernel
+template <int F, int NU, int R>
+static hipError_t run_moe_flat(const MoeLaunch& a, hipStream_t st) {
+  constexpr int WPB = 4;
+  const int64_t slots = (int64_t)a.n_tok * a.top_k;
+  const unsigned gx = (unsigned)((a.n_rows + R * WPB - 1) / (R * WPB));
+  hipLaunchKernelGGL((k_moe_flat<F, NU, R, WPB>), dim3(gx, (unsigned)slots), dim3(64 * WPB), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.rw == nullptr) return e;
+  const int64_t outs = (int64_t)a.n_tok * a.n_rows;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// One row chunk per lane: NU = units / 64 rounded up (at most 8: k <= 16384);
+// two rows per wave when a row is at most two units per lane.
+template <int F>
+static hipError_t run_moe_flat_fmt(const MoeLaunch& a, hipStream_t st) {
+  const int nu = (a.units + 63) / 64;
+  switch (nu) {
+    case 1: return run_moe_flat<F, 1, 2>(a, st);
+    case 2: return run_moe_flat<F, 2, 2>(a, st);
+    case 3: return run_moe_flat<F, 3, 1>(a, st);
+    case 4: return run_moe_flat<F, 4, 1>(a, st);
+    default: return run_moe_flat<F, 8, 1>(a, st);
+  }
+}
+
+static int g_moe_kernel = 0;  // tuning: 0 automatic, 1 vector-ALU, 2 matrix-core, 3 few-slot flat kernel
 void set_moe_kernel(int v) { g_moe_kernel = v; }
 
-// The matrix-core kernel when experts receive several slots (from 16
-// tokens, top-8 of 128 experts: about one slot per active expert at 16
-// tokens, four at 64), with 4 (8 from 17 tokens) slot rows per group.
+// The few-slot flat kernel while grouping slots by expert saves less than
+// its routing costs (measured on 128 experts, top-8: one activation row per
+// token, 3072 x 4096 rows, up to 16 tokens -- 16.1 -> 12.3 us at one token,
+// 150.1 -> 145.2 us at 16, 286 against 207 us at 32; one row per slot,
+// 4096 x 1536, up to 6 tokens -- 13.6 -> 11.6 us at one, 49 against 54 us at
+// 8); then the matrix-core kernel when experts receive several slots (from
+// 16 tokens), with 4 (8 from 17 tokens) slot rows per group.
 template <int F>
 static hipError_t run_moe_any(const MoeLaunch& a, hipStream_t st) {
+  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= (a.x_per_slot ? 6 : 16)))
+    return run_moe_flat_fmt<F>(a, st);
   const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && a.n_tok >= 16);
   if (mx) {
     const hipError_t e = a.n_tok <= 16 ? run_moe_mx<F, 4>(a, st) : run_moe_mx<F, 8>(a, st);

@@ -205,7 +205,7 @@ def test_tuning_switches(L):
     assert L.qmv_set_tuning(b"splitk", -2) == INVALID
     assert L.qmv_set_tuning(b"variant", -1) == OK
     assert L.qmv_set_tuning(b"splitk", -1) == OK
-    assert L.qmv_set_tuning(b"moe_kernel", 3) == INVALID
+    assert L.qmv_set_tuning(b"moe_kernel", 4) == INVALID
     assert L.qmv_set_tuning(b"moe_kernel", 0) == OK
     for bad in (-2, 1, 33):
         assert L.qmv_set_tuning(b"mx_slices", bad) == INVALID

@@ -37,9 +37,10 @@ def _rows_of_experts(w_dev, n_rows, rows):
     return v.index_select(1, idx).contiguous().cpu().numpy()
 
 
-@pytest.fixture(params=[1, 2], ids=["vector", "matrix"])
+@pytest.fixture(params=[1, 2, 3], ids=["vector", "matrix", "flat"])
 def moe_kernel(request):
-    """Run a test with the vector-ALU and with the matrix-core MoE kernel."""
+    """Run a test with the vector-ALU, the matrix-core and the few-slot flat
+    MoE kernel."""
     qmv = need_gpu()
     qmv.set_tuning("moe_kernel", request.param)
     yield request.param
