@@ -103,6 +103,8 @@ CASES = {
     "dropped": np.array([[0, -1, 2], [6, 1, 1000], [3, 3, -7]], np.int32),
     "all_dropped": np.array([[-1, 6], [7, -2]], np.int32),
     "single_token": np.array([[5, 0, 1, 2]], np.int32),
+    "single_token_dropped": np.array([[5, -1, 1000, 2, 5]], np.int32),  # and a duplicate
+    "single_token_all_dropped": np.array([[-1, 1000]], np.int32),
 }
 
 
