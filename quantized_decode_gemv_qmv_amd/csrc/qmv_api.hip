@@ -74,27 +74,32 @@ struct DeviceInfo {
   int64_t lds_per_block;
 };
 
-// Properties of the current device, queried once per device.
+// Properties of the current device, queried once per device.  Without a
+// device (host-only size and plan queries) and for attributes the runtime
+// does not report, those of the MI355X (gfx950) the library is built for:
+// 256 compute units, 160 KiB of LDS per compute unit and per workgroup.
+constexpr int kDefaultCus = 256;
+constexpr int64_t kDefaultLds = 160 * 1024;
 DeviceInfo device_info() {
   static std::mutex mu;
   static DeviceInfo cache[64];
   static bool have[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {256, 163840, 65536};
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return {kDefaultCus, kDefaultLds, kDefaultLds};
   std::lock_guard<std::mutex> lock(mu);
   if (!have[dev]) {
     int cus = 0, lcu = 0, lblk = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
-      cus = 256;
+      cus = kDefaultCus;
     if (hipDeviceGetAttribute(&lcu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
             hipSuccess ||
         lcu <= 0)
-      lcu = 65536;
+      lcu = kDefaultLds;
     if (hipDeviceGetAttribute(&lblk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
             hipSuccess ||
         lblk <= 0)
-      lblk = 65536;
+      lblk = kDefaultLds;
     cache[dev] = {cus, lcu, lblk};
     have[dev] = true;
   }

@@ -187,6 +187,34 @@ def test_matvec_plan():
         q.matvec_plan(1, 4096, 300, 1, True)
 
 
+# The kernel and K split qmv_matvec runs for the workload shapes, as the
+# variant rules in the library choose them from the sweeps (host-only: the
+# library describes an MI355X when no device is present).  (type, rows, K,
+# tokens, with workspace) -> (variant, slices)
+PLANS = [
+    ((1, 14336, 4096, 1, False), ("fl_w4_r2_u2_g", 1)),
+    ((1, 14336, 4096, 16, False), ("mx_w8_k4_r4", 1)),
+    ((2, 4096, 14336, 1, True), ("fl_w8_r1_u7_l", 1)),
+    ((2, 4096, 14336, 16, True), ("mx_w16_k4_r2", 4)),   # split over workgroups with a workspace
+    ((2, 4096, 14336, 16, False), ("mx_w8_k8_r4", 1)),
+    ((1, 4096, 14336, 16, True), ("mx_w8_k1_r4", 8)),
+    ((0, 4096, 4096, 1, True), ("fl_w4_r1_u2_l", 1)),
+    ((0, 256, 65536, 1, True), ("st_k16_r1_u2", 1)),     # split inside one workgroup
+    ((2, 1024, 8192, 1, True), ("fl_w4_r1_u4_g", 1)),
+    ((0, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),
+    ((5, 152064, 5120, 2, False), ("st_w4_r1_u3", 1)),
+    ((5, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),
+    ((4, 14336, 4096, 16, False), ("fl_w16_r1_u2_l", 1)),  # q6_K: vector kernels only
+]
+
+
+@pytest.mark.parametrize("args,expect", PLANS, ids=[f"{a[0]}-{a[1]}x{a[2]}-T{a[3]}{'-ws' if a[4] else ''}"
+                                                     for a, _ in PLANS])
+def test_plans_of_the_workload_shapes(args, expect):
+    v, s = q.matvec_plan(*args)
+    assert (q.variant_name(v), s) == expect
+
+
 def test_stream_read_validation(L):
     f = L.qmv_stream_read
     assert f(None, 4096, FAKE, None) == INVALID
