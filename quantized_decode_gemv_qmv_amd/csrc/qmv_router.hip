@@ -155,14 +155,17 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
   __syncthreads();
   for (int e = tid; e < n_experts; e += 256) {
     const uint64_t me = s_key[e];
-    int rank = 0;
+    // four partial counts, sixteen keys per step: the LDS reads of a step
+    // are in flight together
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
 #pragma unroll 4
     for (int j = 0; j < n4; j += 4) {
-      rank += s_key[j] > me ? 1 : 0;
-      rank += s_key[j + 1] > me ? 1 : 0;
-      rank += s_key[j + 2] > me ? 1 : 0;
-      rank += s_key[j + 3] > me ? 1 : 0;
+      r0 += s_key[j] > me ? 1 : 0;
+      r1 += s_key[j + 1] > me ? 1 : 0;
+      r2 += s_key[j + 2] > me ? 1 : 0;
+      r3 += s_key[j + 3] > me ? 1 : 0;
     }
+    const int rank = (r0 + r1) + (r2 + r3);
     if (rank < top_k) {
       s_pv[rank] = s_val[e];
       s_pi[rank] = e;
@@ -189,7 +192,7 @@ static void launch_logits(const float* x, int64_t ldx, int n_tok, int k, const f
 hipError_t launch_router_topk(const float* x, int64_t ldx, int n_tok, int k, const float* wr, int n_experts,
                               int top_k, int32_t* ids, float* w, float* logits, hipStream_t st) {
   // token groups of up to 4 (each workgroup then reads 4 x rows, 4 expert rows)
-  if (n_tok == 1) launch_logits<2, 1>(x, ldx, n_tok, k, wr, n_experts, logits, st);
+  if (n_tok == 1) launch_logits<1, 1>(x, ldx, n_tok, k, wr, n_experts, logits, st);
   else if (n_tok == 2) launch_logits<2, 2>(x, ldx, n_tok, k, wr, n_experts, logits, st);
   else launch_logits<4, 4>(x, ldx, n_tok, k, wr, n_experts, logits, st);
   hipError_t e = hipGetLastError();
