@@ -163,13 +163,18 @@ qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t rows, int64
  * ids     : int32 [n_tok][top_k] (device); weights: fp32 [n_tok][top_k].
  * logits  : fp32 [n_tok][n_experts] (device), receives l (the selection
  *           reads it back: two launches on `stream`).
+ * xq      : NULL, or an activation buffer of qmv_act_bytes(n_tok, k) bytes
+ *           (device, 256-byte aligned) that receives Q8(x) exactly as
+ *           qmv_quantize_act makes it (the router reads all of x anyway; the
+ *           routed gate+up projection takes this buffer, which saves the
+ *           quantizer's launch).  Requires k % 32 == 0.
  * 1 <= n_tok <= QMV_MAX_MOE_TOKENS, k % 4 == 0, k <= 2^24,
  * 1 <= top_k <= min(n_experts, QMV_MAX_TOP_K), n_experts <= QMV_MAX_EXPERTS.
  * Asynchronous on `stream`; allocates nothing.
  */
 qmv_status qmv_router_topk(const float* x, int64_t ldx, int64_t n_tok, int64_t k, const float* wr,
                            int64_t n_experts, int64_t top_k, int32_t* ids, float* weights, float* logits,
-                           void* stream);
+                           void* xq, void* stream);
 
 /*
  * qmv_matvec -- y[t][n] = sum_k W[n][k] * xq[t][k] for t < n_tok.

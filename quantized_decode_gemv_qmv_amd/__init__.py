@@ -80,7 +80,7 @@ def lib():
         "qmv_act_offset_s": ([I64, I64], SZ),
         "qmv_quantize_act": ([P, I64, I64, I64, P, P], I),
         "qmv_swiglu_quantize": ([P, I64, I64, I64, P, P, P], I),
-        "qmv_router_topk": ([P, I64, I64, I64, P, I64, I64, P, P, P, P], I),
+        "qmv_router_topk": ([P, I64, I64, I64, P, I64, I64, P, P, P, P, P], I),
         "qmv_matvec_workspace_bytes": ([I, I64, I64, I64], SZ),
         "qmv_matvec": ([I, P, I64, I64, P, I64, P, I64, P, SZ, P], I),
         "qmv_matvec_batch": ([I, ctypes.POINTER(_Item), I64, I64, P, I64, P], I),
@@ -167,11 +167,16 @@ def swiglu_quantize(gu: torch.Tensor, n_ff: int, out: torch.Tensor | None = None
 
 
 def router_topk(x: torch.Tensor, wr: torch.Tensor, top_k: int, ids: torch.Tensor | None = None,
-                weights: torch.Tensor | None = None, logits: torch.Tensor | None = None, stream=None):
+                weights: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                xq: torch.Tensor | None = None, stream=None):
     """x fp32 [T][K], router weights fp32 [E][K] -> (ids int32 [T][top_k],
     weights fp32 [T][top_k]); logits (fp32 [T][E], allocated when None)
-    receives the router logits."""
-    _need(x, torch.float32, "x")
+    receives the router logits, xq (optional) the Q8 blocks of x.  x may
+    have a row stride beyond K (a multiple of 4)."""
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    if x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a float32 CUDA tensor with unit column stride")
     _need(wr, torch.float32, "wr")
     n_tok, k = x.shape
     e = wr.shape[0]
@@ -183,8 +188,12 @@ def router_topk(x: torch.Tensor, wr: torch.Tensor, top_k: int, ids: torch.Tensor
         logits = torch.empty((n_tok, e), dtype=torch.float32, device=x.device)
     _need(logits, torch.float32, "logits")
     ldx = x.stride(0) if n_tok > 1 else k
+    if xq is not None:
+        _need(xq, torch.uint8, "xq")
+        if xq.numel() < act_bytes(n_tok, k):
+            raise ValueError("activation buffer too small")
     _check(lib().qmv_router_topk(_ptr(x), ldx, n_tok, k, _ptr(wr), e, top_k, _ptr(ids), _ptr(weights),
-                                 _ptr(logits), _stream(stream)), "qmv_router_topk")
+                                 _ptr(logits), _ptr(xq), _stream(stream)), "qmv_router_topk")
     return ids, weights
 
 

@@ -489,19 +489,23 @@ QMV_API qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t row
 
 QMV_API qmv_status qmv_router_topk(const float* x, int64_t ldx, int64_t n_tok, int64_t k, const float* wr,
                                    int64_t n_experts, int64_t top_k, int32_t* ids, float* weights,
-                                   float* logits, void* stream) {
+                                   float* logits, void* xq, void* stream) {
   if (x == nullptr || wr == nullptr || ids == nullptr || weights == nullptr || logits == nullptr || n_tok < 1 ||
       k < 1 ||
-      k % 4 || ldx < k || ldx % 4 || n_experts < 1 || top_k < 1 || top_k > n_experts)
+      k % 4 || ldx < k || ldx % 4 || n_experts < 1 || top_k < 1 || top_k > n_experts || (xq != nullptr && k % 32))
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_MOE_TOKENS || k > (int64_t(1) << 24) || n_experts > QMV_MAX_EXPERTS ||
       top_k > QMV_MAX_TOP_K)
     return QMV_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(wr, 16) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(logits, 4))
+  if (!aligned(x, 16) || !aligned(wr, 16) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(logits, 4) ||
+      (xq != nullptr && !aligned(xq, 256)))
     return QMV_ERR_MISALIGNED;
+  ActView xv{};
+  if (xq != nullptr) xv = act_view(xq, n_tok, k);
   hipError_t e = launch_router_topk(x, ldx, static_cast<int>(n_tok), static_cast<int>(k), wr,
                                     static_cast<int>(n_experts), static_cast<int>(top_k), ids, weights, logits,
-                                    static_cast<hipStream_t>(stream));
+                                    const_cast<int8_t*>(xv.qs), const_cast<float*>(xv.d),
+                                    const_cast<int32_t*>(xv.s), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 

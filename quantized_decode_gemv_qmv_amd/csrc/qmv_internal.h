@@ -196,7 +196,8 @@ hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t
 hipError_t launch_swiglu_quantize(const float* gu, int64_t ldg, int rows, int n_ff, int8_t* qs, float* d,
                                   int32_t* s, float* h_out, hipStream_t st);
 hipError_t launch_router_topk(const float* x, int64_t ldx, int n_tok, int k, const float* wr, int n_experts,
-                              int top_k, int32_t* ids, float* w, float* logits, hipStream_t st);
+                              int top_k, int32_t* ids, float* w, float* logits, int8_t* xq_qs, float* xq_d,
+                              int32_t* xq_s, hipStream_t st);
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
 // The vector-ALU kernels of format F (one translation unit per format).
 template <int F>

@@ -9,7 +9,11 @@
 // lane accumulates the EG x TG products of its columns in registers, a
 // butterfly across the wave leaves each lane with one product's wave sum, and
 // the eight wave sums meet in LDS.  The router weights are read once per token
-// group, spread over n_experts / EG workgroups.
+// group, spread over n_experts / EG workgroups.  Optionally the workgroups
+// of the first expert group also write the Q8 activation blocks of their
+// tokens: the eight lanes holding a 32-column block run the quantizer's
+// block routine on the x values they loaded (the same values and steps as
+// k_quantize, so the same bytes).
 // k_router_select takes one workgroup per token: each expert's rank is the
 // number of experts with a larger logit, or an equal one and a lower index
 // (one 64-bit key compare per expert); ranks below top_k are the picks in
@@ -87,7 +91,10 @@ template <int EG, int TG>
 __global__ __launch_bounds__(64 * kRouterWaves) void k_router_logits(const float* __restrict__ x, int64_t ldx,
                                                                      int n_tok, int k,
                                                                      const float* __restrict__ wr,
-                                                                     int n_experts, float* __restrict__ logits) {
+                                                                     int n_experts, float* __restrict__ logits,
+                                                                     int8_t* __restrict__ xq_qs,
+                                                                     float* __restrict__ xq_d,
+                                                                     int32_t* __restrict__ xq_s) {
   constexpr int P = EG * TG;
   static_assert(P <= 64 && (P & (P - 1)) == 0, "products per lane: a power of two up to 64");
   __shared__ float red[kRouterWaves][64];
@@ -98,17 +105,43 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_logits(const float
   for (int i = 0; i < P; ++i) acc[i] = 0.f;
 
   constexpr int kStep = 4 * 64 * kRouterWaves;  // columns per round of the workgroup
+  // Q8 blocks of x: workgroups of the first expert group, uniform per
+  // workgroup.  The eight lanes 8i..8i+7 hold the 32 columns of one block
+  // (k % 32 == 0), so a block is either wholly inside the loop or wholly out.
+  const bool qx = xq_qs != nullptr && blockIdx.x == 0;
+  const int nb = k / 32;
+  auto put = [&](const RouterChunk<EG, TG>& ch, int col) {
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      if (t0 + t < n_tok) {  // uniform
+        const float vv[4] = {ch.x[t].x, ch.x[t].y, ch.x[t].z, ch.x[t].w};
+        float db;
+        int sum;
+        const uint32_t packed = q8_block8(vv, db, sum);
+        *reinterpret_cast<uint32_t*>(xq_qs + (int64_t)(t0 + t) * k + col) = packed;
+        if ((lane & 7) == 0) {
+          xq_d[(int64_t)(t0 + t) * nb + col / 32] = db;
+          xq_s[(int64_t)(t0 + t) * nb + col / 32] = sum;
+        }
+      }
+    }
+  };
   int c = 4 * (lane + 64 * wave);
   for (; c + kStep < k; c += 2 * kStep) {  // two chunks in flight
     RouterChunk<EG, TG> a, b;
     a.load(x, ldx, n_tok, t0, k, wr, n_experts, e0, c);
     b.load(x, ldx, n_tok, t0, k, wr, n_experts, e0, c + kStep);
+    if (qx) {
+      put(a, c);
+      put(b, c + kStep);
+    }
     a.fma(acc);
     b.fma(acc);
   }
   if (c < k) {
     RouterChunk<EG, TG> a;
     a.load(x, ldx, n_tok, t0, k, wr, n_experts, e0, c);
+    if (qx) put(a, c);
     a.fma(acc);
   }
   const float r = fold_all<P>(acc, lane);
@@ -183,18 +216,19 @@ __global__ __launch_bounds__(256) void k_router_select(const float* __restrict__
 
 template <int EG, int TG>
 static void launch_logits(const float* x, int64_t ldx, int n_tok, int k, const float* wr, int n_experts,
-                          float* logits, hipStream_t st) {
+                          float* logits, int8_t* xq_qs, float* xq_d, int32_t* xq_s, hipStream_t st) {
   const dim3 grid((unsigned)((n_experts + EG - 1) / EG), (unsigned)((n_tok + TG - 1) / TG));
   hipLaunchKernelGGL((k_router_logits<EG, TG>), grid, dim3(64 * kRouterWaves), 0, st, x, ldx, n_tok, k, wr,
-                     n_experts, logits);
+                     n_experts, logits, xq_qs, xq_d, xq_s);
 }
 
 hipError_t launch_router_topk(const float* x, int64_t ldx, int n_tok, int k, const float* wr, int n_experts,
-                              int top_k, int32_t* ids, float* w, float* logits, hipStream_t st) {
+                              int top_k, int32_t* ids, float* w, float* logits, int8_t* xq_qs, float* xq_d,
+                              int32_t* xq_s, hipStream_t st) {
   // token groups of up to 4 (each workgroup then reads 4 x rows, 4 expert rows)
-  if (n_tok == 1) launch_logits<1, 1>(x, ldx, n_tok, k, wr, n_experts, logits, st);
-  else if (n_tok == 2) launch_logits<2, 2>(x, ldx, n_tok, k, wr, n_experts, logits, st);
-  else launch_logits<4, 4>(x, ldx, n_tok, k, wr, n_experts, logits, st);
+  if (n_tok == 1) launch_logits<1, 1>(x, ldx, n_tok, k, wr, n_experts, logits, xq_qs, xq_d, xq_s, st);
+  else if (n_tok == 2) launch_logits<2, 2>(x, ldx, n_tok, k, wr, n_experts, logits, xq_qs, xq_d, xq_s, st);
+  else launch_logits<4, 4>(x, ldx, n_tok, k, wr, n_experts, logits, xq_qs, xq_d, xq_s, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_router_select, dim3((unsigned)n_tok), dim3(256), 0, st, logits, n_experts, top_k, ids, w);

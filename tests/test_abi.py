@@ -120,10 +120,10 @@ def test_router_topk_validation(L):
     f = L.qmv_router_topk
 
     def call(**kw):
-        a = dict(x=FAKE, ldx=64, t=2, k=64, wr=FAKE, e=8, top_k=2, ids=FAKE, w=FAKE, logits=FAKE)
+        a = dict(x=FAKE, ldx=64, t=2, k=64, wr=FAKE, e=8, top_k=2, ids=FAKE, w=FAKE, logits=FAKE, xq=None)
         a.update(kw)
         return f(a["x"], a["ldx"], a["t"], a["k"], a["wr"], a["e"], a["top_k"], a["ids"], a["w"],
-                 a["logits"], None)
+                 a["logits"], a["xq"], None)
 
     assert call(x=None) == INVALID
     assert call(ids=None) == INVALID
@@ -138,6 +138,8 @@ def test_router_topk_validation(L):
     assert call(e=64, top_k=17) == UNSUPPORTED
     assert call(x=FAKE + 4) == MISALIGNED
     assert call(wr=FAKE + 8) == MISALIGNED
+    assert call(xq=FAKE, k=48, ldx=48) == INVALID  # Q8 blocks need k % 32 == 0
+    assert call(xq=FAKE + 64) == MISALIGNED
     assert call(logits=FAKE + 2) == MISALIGNED
 
 

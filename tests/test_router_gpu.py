@@ -6,7 +6,11 @@ logit within 1e-4 of the sum of |w_i x_i| (the matvec tolerance).  Which
 experts are chosen is an integer decision taken from those fp32 logits, so the
 ids must equal the oracle's selection from the GPU's own logits exactly (same
 order rule: larger logit first, lower index on ties), and the weights the
-oracle's softmax of those logits within 1e-6 relative."""
+oracle's softmax of those logits within 1e-6 relative.
+
+With an activation buffer the router also writes the Q8 blocks of x: those
+bytes must equal the oracle's quantization of x and qmv_quantize_act's output
+exactly."""
 import numpy as np
 import pytest
 import torch
@@ -71,9 +75,9 @@ def test_router_feeds_moe():
     e_n, n, k, top_k, t = 6, 40, 512, 2, 3
     x = synth.make_x(t, k, "router_moe/x")
     wr = synth.make_x(e_n, k, "router_moe/wr")
-    ids_d, w_d = qmv.router_topk(to_dev(x), to_dev(wr), top_k)
+    xq = torch.empty(qmv.act_bytes(t, k), dtype=torch.uint8, device="cuda")
+    ids_d, w_d = qmv.router_topk(to_dev(x), to_dev(wr), top_k, xq=xq)
     w = synth.make_weights(synth.IQ4_XS, e_n * n, k, "router_moe/w").data
-    xq = qmv.quantize_act(to_dev(x))
     ws = torch.zeros(qmv.moe_workspace_bytes(synth.IQ4_XS, e_n, n, k, t, top_k), dtype=torch.uint8,
                      device="cuda")
     y = qmv.moe_matvec(synth.IQ4_XS, to_dev(w), e_n, n, k, xq, False, ids_d, w_d, ws).cpu().numpy()
@@ -81,3 +85,30 @@ def test_router_feeds_moe():
     yr, mag = oracle.moe_matvec(synth.IQ4_XS, w, e_n, n, k, qs, d, s, ids_d.cpu().numpy(),
                                 w_d.cpu().numpy(), False)
     assert np.all(np.abs(y - yr) <= 1e-4 * mag)
+
+
+@pytest.mark.parametrize("t,k,e", [(1, 4096, 128), (2, 4096, 128), (3, 1056, 7), (4, 32, 3), (5, 96, 40),
+                                   (16, 2048, 64), (64, 4096, 128), (1, 5120, 1)])
+def test_router_writes_q8_of_x(t, k, e):
+    """The optional Q8 output: every token, every block, with a zero block and
+    a row stride beyond K; K spans the kernel's two-chunk loop and its tail."""
+    qmv = need_gpu()
+    say(f"router xq T={t} K={k} E={e}")
+    x = synth.make_x(t, k, f"router_xq/{t}/{k}")
+    x[0, :32] = 0.0
+    wr = synth.make_x(e, k, f"router_xq/w/{e}/{k}")
+    xb = torch.zeros((t, k + 64), dtype=torch.float32, device="cuda")
+    xb[:, :k] = to_dev(x)
+    xq = torch.full((qmv.act_bytes(t, k),), 0xA5, dtype=torch.uint8, device="cuda")
+    logits_d = torch.empty((t, e), dtype=torch.float32, device="cuda")
+    ids_d, _ = qmv.router_topk(xb[:, :k], to_dev(wr), min(2, e), logits=logits_d, xq=xq)
+    ref = qmv.quantize_act(xb[:, :k])
+    torch.cuda.synchronize()
+    for got, want in zip(qmv.act_fields(xq, t, k), qmv.act_fields(ref, t, k)):
+        assert torch.equal(got, want)
+    qs, d, s = oracle.quantize_act(x)
+    g_qs, g_d, g_s = (a.cpu().numpy() for a in qmv.act_fields(xq, t, k))
+    assert np.array_equal(g_qs, qs) and np.array_equal(g_d, d) and np.array_equal(g_s, s)
+    # the selection is unchanged by the extra output
+    ids2, _ = qmv.router_topk(xb[:, :k], to_dev(wr), min(2, e))
+    assert torch.equal(ids_d, ids2)
