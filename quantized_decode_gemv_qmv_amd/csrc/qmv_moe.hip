@@ -567,6 +567,20 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat_comb(MoeLaunch a) {
     ev[s] = a.ids[sl];
     wv[s] = a.rw[sl];
   }
+  // With one unit per lane every slot's activation fragments fit beside the
+  // weights: issued first (cache-resident), so no slot waits for a second
+  // round trip.  Wider rows load each slot's fragments when it is used.
+  constexpr bool kPre = NU == 1;
+  XO xp[kPre ? TK : 1][NU];
+  if constexpr (kPre) {
+#pragma unroll
+    for (int s = 0; s < TK; ++s) {
+      const int xr = a.x_per_slot ? t * a.top_k + min(s, a.top_k - 1) : t;
+#pragma unroll
+      for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lane + 64 * q, units - 1), xp[s][q]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
   RawS<F> cur[TK][R][NU];
 #pragma unroll
   for (int s = 0; s < TK; ++s) {
@@ -586,12 +600,15 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat_comb(MoeLaunch a) {
   for (int s = 0; s < TK; ++s) {
     __builtin_amdgcn_sched_barrier(0);  // slots one after the other
     const bool use = s < a.top_k && ev[s] >= 0 && ev[s] < a.n_experts;
-    // the slot's activation fragments (cache-resident), loaded when used:
-    // eight slots' fragments held beside their weights would spill
-    const int xr = a.x_per_slot ? t * a.top_k + min(s, a.top_k - 1) : t;
     XO xs[NU];
+    if constexpr (kPre) {
 #pragma unroll
-    for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lane + 64 * q, units - 1), xs[q]);
+      for (int q = 0; q < NU; ++q) xs[q] = xp[s][q];
+    } else {
+      const int xr = a.x_per_slot ? t * a.top_k + min(s, a.top_k - 1) : t;
+#pragma unroll
+      for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lane + 64 * q, units - 1), xs[q]);
+    }
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -768,7 +785,8 @@ static hipError_t run_moe_flat(const MoeLaunch& a, hipStream_t st) {
     if (a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1) {
       // one token, route-weighted, top_k <= 8: the combine folded into the
       // kernel, one row per wave, every slot's weights in flight (measured
-      // 4096 x 1536 down: one token 11.1 -> 10.7 us; at six tokens the
+      // 4096 x 1536 down: one token 11.1 -> 10.7 us, 10.2 us with every
+      // slot's activation fragments issued up front; at six tokens the
       // per-slot grid and the combine kernel were faster, 39.5 against 43.1)
       const unsigned gx = (unsigned)((a.n_rows + WPB - 1) / WPB);
       hipLaunchKernelGGL((k_moe_flat_comb<F, NU, 1, WPB, 8>), dim3(gx, (unsigned)a.n_tok), dim3(64 * WPB), 0, st, a);
