@@ -786,7 +786,8 @@ static hipError_t run_moe_flat(const MoeLaunch& a, hipStream_t st) {
       // one token, route-weighted, top_k <= 8: the combine folded into the
       // kernel, one row per wave, every slot's weights in flight (measured
       // 4096 x 1536 down: one token 11.1 -> 10.7 us, 10.2 us with every
-      // slot's activation fragments issued up front; at six tokens the
+      // slot's activation fragments issued up front, and no better with two
+      // rows per wave (167 VGPRs, 10.2-10.4 us); at six tokens the
       // per-slot grid and the combine kernel were faster, 39.5 against 43.1)
       const unsigned gx = (unsigned)((a.n_rows + WPB - 1) / WPB);
       hipLaunchKernelGGL((k_moe_flat_comb<F, NU, 1, WPB, 8>), dim3(gx, (unsigned)a.n_tok), dim3(64 * WPB), 0, st, a);
