@@ -7,8 +7,8 @@ replays, must give the bits of the same calls run eagerly.
 The sequence covers the paths with cross-workgroup state or fusion: the
 matrix-core kernel split over workgroups (IQ4_XS, few rows, long K, 16
 tokens, with a workspace), the fused decode step qmv_matvec_x (q4_K, one
-token), and the one-token route-weighted MoE call (the flat kernel with the
-combine folded in), each after its quantizer."""
+token), the router writing the Q8 blocks of the MoE input, and the one-token
+route-weighted MoE call (the flat kernel with the combine folded in) on them."""
 import numpy as np
 import torch
 
@@ -33,6 +33,7 @@ def test_graph_replays_match_eager():
     ids = to_dev(np.array([[3, 7, 0, 12]], np.int32))
     rw = to_dev(np.array([[0.4, 0.3, 0.2, 0.1]], np.float32))
     xh = to_dev(x_host(top_k, kk, "graph/xh"))
+    wrt = to_dev(x_host(n_exp, kk, "graph/wr"))
     wsm = torch.zeros(qmv.moe_workspace_bytes(synth.IQ4_XS, n_exp, nr, kk, 1, top_k), dtype=torch.uint8,
                       device="cuda")
 
@@ -44,13 +45,16 @@ def test_graph_replays_match_eager():
             "y2": torch.empty((1, n2), dtype=torch.float32, device="cuda"),
             "xqh": torch.empty(qmv.act_bytes(top_k, kk), dtype=torch.uint8, device="cuda"),
             "y3": torch.empty((1, nr), dtype=torch.float32, device="cuda"),
+            "rid": torch.empty((top_k, top_k), dtype=torch.int32, device="cuda"),
+            "rw": torch.empty((top_k, top_k), dtype=torch.float32, device="cuda"),
+            "rl": torch.empty((top_k, n_exp), dtype=torch.float32, device="cuda"),
         }
 
     def step(o):
         qmv.quantize_act(x1, out=o["xq1"])
         qmv.matvec(synth.IQ4_XS, w1, n1, k1, o["xq1"], t1, y=o["y1"], ws=ws1)
         qmv.matvec_x(synth.Q4_K, w2, n2, k2, x2, xq=o["xq2"], y=o["y2"])
-        qmv.quantize_act(xh, out=o["xqh"])
+        qmv.router_topk(xh, wrt, top_k, ids=o["rid"], weights=o["rw"], logits=o["rl"], xq=o["xqh"])
         qmv.moe_matvec(synth.IQ4_XS, we, n_exp, nr, kk, o["xqh"], True, ids, rw, wsm, y=o["y3"])
 
     say("graph: eager reference")
@@ -76,8 +80,10 @@ def test_graph_replays_match_eager():
             v.fill_(0)  # the replay must rewrite every output
         g.replay()
         torch.cuda.synchronize()
-        for name in ("y1", "y2", "y3", "xq1", "xq2", "xqh"):
+        for name in ("y1", "y2", "y3", "xq1", "xq2", "rid", "rw", "rl"):
             assert torch.equal(out[name], ref[name]), (rep, name)
+        for got, want in zip(qmv.act_fields(out["xqh"], top_k, kk), qmv.act_fields(ref["xqh"], top_k, kk)):
+            assert torch.equal(got, want), (rep, "xqh")
         step(other)  # eager work on the same weights and workspaces between replays
         torch.cuda.synchronize()
         for name in ("y1", "y2", "y3"):
