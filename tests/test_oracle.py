@@ -258,8 +258,43 @@ def pin_router_topk():
     assert np.array_equal(ids2, ids) and np.allclose(w2, w, rtol=1e-15)
 
 
+def pin_topk_from_logits_ties():
+    """The selection from given fp32 logits, on hand-written cases whose
+    answers are written out here: exact ties inside the picks and across the
+    top-k boundary go to the lower expert index, -0 and +0 compare equal
+    (so they are a tie as well), and the weights are a softmax of the chosen
+    logits (equal for tied picks, ratios exp(l_i - l_j), sum 1)."""
+    nz = np.float32(-0.0)
+    logits = np.array([
+        [2.0, 5.0, 5.0, -1.0, 5.0, 0.0, 0.0, 0.0],   # three-way tie at the top, ties at 0 below
+        [1.0, 3.0, 3.0, 3.0, 0.0, 3.0, -2.0, 3.0],   # the boundary falls inside a five-way tie
+        [nz, 0.0, nz, -3.0, 0.0, -1.0, nz, -0.5],    # signed zeros: all five are one tie
+        [0.0, nz, 0.0, 1.0, nz, -7.0, 0.0, 0.5],
+    ], np.float32)
+    ids, w = oracle.topk_from_logits(logits, 6)
+    assert ids.tolist() == [[1, 2, 4, 0, 5, 6],
+                            [1, 2, 3, 5, 7, 0],
+                            [0, 1, 2, 4, 6, 7],
+                            [3, 7, 0, 1, 2, 4]]
+    ids2, _ = oracle.topk_from_logits(logits, 2)
+    assert ids2.tolist() == [[1, 2], [1, 2], [0, 1], [3, 7]]
+    assert np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+    # row 0 picks 5, 5, 5, 2, 0, 0: weights e^0, e^0, e^0, e^-3, e^-5, e^-5 over their sum
+    z = np.array([1.0, 1.0, 1.0, np.exp(-3.0), np.exp(-5.0), np.exp(-5.0)])
+    assert np.allclose(w[0], z / z.sum(), rtol=1e-15, atol=0)
+    # row 2: five signed zeros and -0.5 -> five equal weights and one e^-0.5 times smaller
+    assert np.allclose(w[2, :5], w[2, 0], rtol=0, atol=0)
+    assert abs(w[2, 0] / w[2, 5] - np.exp(0.5)) < 1e-13
+    # a single expert, and top_k equal to the expert count (a full ordering)
+    one, w1 = oracle.topk_from_logits(np.array([[4.0]], np.float32), 1)
+    assert one.tolist() == [[0]] and w1.tolist() == [[1.0]]
+    full, _ = oracle.topk_from_logits(logits[1:2], 8)
+    assert full.tolist() == [[1, 2, 3, 5, 7, 0, 4, 6]]
+
+
 PINS = [pin_act_cases, pin_act_invariants, pin_integer_special_case, pin_residual, pin_brute_force,
-        pin_quantization_bound, pin_moe_against_dense_loop, pin_swiglu, pin_router_topk]
+        pin_quantization_bound, pin_moe_against_dense_loop, pin_swiglu, pin_router_topk,
+        pin_topk_from_logits_ties]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -310,6 +345,11 @@ MUTANTS = {
     "silu_sign": ("exp(-g);  /*", "exp(g);  /*"),
     "swiglu_up_column": ("gu[r * ldg + n_ff + i]", "gu[r * ldg + i]"),
     "topk_tie_upper": ("if (best < 0 || l[e] > l[best]) best = e;  /* strict", "if (best < 0 || l[e] >= l[best]) best = e;  /* strict"),
+    "logits_topk_tie_upper": ("l[e] > l[best]) best = e;\n", "l[e] >= l[best]) best = e;\n"),
+    "logits_topk_signed_zero": ("l[e] > l[best]) best = e;\n",
+                                "l[e] > l[best] || (l[e] == l[best] && signbit(l[best]) && !signbit(l[e]))) best = e;\n"),
+    "logits_softmax_unnormalized": ("exp((double)l[ids[t * top_k + j]] - m) / sum;",
+                                    "exp((double)l[ids[t * top_k + j]] - m);"),
     "softmax_unnormalized": ("w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m) / sum;\n  }\n  return 0;\n}\n\n/* The selection", "w[t * top_k + j] = exp(l[ids[t * top_k + j]] - m);\n  }\n  return 0;\n}\n\n/* The selection"),
     "residual_dropped": ("y[t * n_rows + n] += rv;", "y[t * n_rows + n] += 0.0;"),
     "residual_columns_reversed": ("(double)res[t * ldr + n];", "(double)res[t * ldr + n_rows - 1 - n];"),
