@@ -56,6 +56,10 @@ WORKLOADS = {
     "q8_0_head_152064x5120": (0, 152064, 5120, (1, 2, 4, 8, 16)),
 }
 FMT_NAME = {0: "Q8_0", 1: "q4_K", 2: "IQ4_XS", 3: "q5_K", 4: "q6_K", 5: "Q8G128"}
+# bytes of one row of 32 / 128 / 256 weights per format, and each workload's
+# weight bytes per matrix (the algorithmic bytes of one launch)
+BLOCK = {0: (32, 34), 1: (256, 144), 2: (256, 136), 3: (256, 176), 4: (256, 210), 5: (128, 130)}
+WEIGHT_BYTES = {wl: v[1] * (v[2] // BLOCK[v[0]][0]) * BLOCK[v[0]][1] for wl, v in WORKLOADS.items()}
 # MoE decode: 128 IQ4_XS experts, gate+up 3072 x 4096 and down 4096 x 1536 per
 # expert, top-8 routing
 MOE = dict(name="moe_iq4_xs_e128", ffn_name="moe_ffn_iq4_xs_e128", experts=128, top_k=8,
@@ -257,37 +261,39 @@ def run_steps(torch, graphs, steps):
         g_tail.replay()
 
 
-def kernel_us(torch, qmv, ring, reps=20):
-    """Average matvec duration: HIP events around back-to-back graph replays
-    of the kernel alone, cycling the weight ring."""
-    per = max(ring.copies, 32)
-    g = capture(torch, lambda i: ring.matvec_only(qmv, i), per)
-    g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+def _replay_samples(torch, g, per, reps):
+    """Per-call time (us) of each of `reps` replays of graph g (`per` calls):
+    HIP events on the current stream around every replay."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
         g.replay()
-    e1.record()
+        ev[r + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * per)
+    return [ev[r].elapsed_time(ev[r + 1]) * 1e3 / per for r in range(reps)]
 
 
-def timed_replays(torch, fn, per, reps=10):
-    """Average time of one fn(i) over back-to-back replays of a graph of
-    `per` calls (HIP events around the replays)."""
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def timed_replays(torch, fn, per, reps=21):
+    """Median per-call time (us) of fn(i) over `reps` back-to-back replays of
+    a graph of `per` calls (each replay timed with HIP events; the graphs are
+    replayed on the stream the events are recorded on)."""
     g = capture(torch, fn, per)
     g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * per)
+    return median(_replay_samples(torch, g, per, reps))
+
+
+def kernel_us(torch, qmv, ring, reps=21):
+    """Median matvec duration: per-launch average of each of `reps` replays
+    of a graph of back-to-back launches of the kernel alone cycling the
+    weight ring, then the median over the replays."""
+    return timed_replays(torch, lambda i: ring.matvec_only(qmv, i), max(ring.copies, 32), reps)
 
 
 def moe_cpu_baseline(ring, min_seconds=10.0, ffn=False):
@@ -407,23 +413,34 @@ def bench_moe(args, torch, qmv, ffn=False):
     return 0
 
 
-def device_info(torch):
-    """The GPU, its runtime and its clocks as the driver reports them (the
-    clocks are read, never set)."""
+def gpu_clocks():
+    """The current shader and memory clock levels of the AMD GPUs the kernel
+    driver lists in sysfs (read, never set; no program is started)."""
+    import glob
+
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            if open(os.path.join(dev, "vendor")).read().strip() != "0x1002":
+                continue
+            cur = {}
+            for f in ("pp_dpm_sclk", "pp_dpm_mclk"):
+                path = os.path.join(dev, f)
+                if os.path.exists(path):
+                    lines = [l.strip() for l in open(path).read().splitlines() if l.strip().endswith("*")]
+                    cur[f[7:]] = lines[0] if lines else None
+            if cur:
+                out[os.path.basename(os.path.dirname(dev))] = cur
+        except OSError:
+            continue
+    return out or None
+
+
+def device_info(torch, clocks):
+    """The GPU and its runtime; the clocks read before the GPU was touched."""
     p = torch.cuda.get_device_properties(0)
-    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
-            "hip": torch.version.hip, "torch": torch.__version__, "clocks": None}
-    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
-        return info  # under a profiler: its preload would follow rocm-smi into a new program
-    try:
-        import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        cards = json.loads(r.stdout) if r.returncode == 0 else {}
-        card = next(iter(cards.values())) if cards else {}
-        info["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()} or None
-    except Exception:  # no rocm-smi or unreadable output: clocks stay unrecorded
-        pass
-    return info
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "clocks": clocks}
 
 
 def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
@@ -470,6 +487,81 @@ def cpu_baseline(fmt, n, k, t, name, min_seconds=10.0, max_seconds=30.0):
             "sample_1_thread": f"rows 0..{rows1 - 1}, matvec only, {reps1} repetitions in {el1:.1f} s"}
 
 
+def trace_summary(path: str) -> int:
+    """Per-kernel summary of a rocprofv3 kernel trace (the *_kernel_trace.csv
+    of --kernel-trace): calls, median, average, min and max duration in us."""
+    import csv
+
+    durs = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("KernelName") or "?"
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            durs.setdefault(name, []).append(d)
+    print(f"{'calls':>7} {'median_us':>10} {'avg_us':>9} {'min_us':>8} {'max_us':>8}  kernel")
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{len(v):7d} {median(v):10.3f} {sum(v) / len(v):9.3f} {min(v):8.3f} {max(v):8.3f}  {name[:150]}")
+    return 0
+
+
+# The metric's token sweep (q4_K and IQ4_XS at 1..16 tokens) and the other
+# workload configurations, reported beside the headline by the default run.
+SWEEP = (("q4_k_14336x4096", (1, 2, 4, 8, 16)), ("iq4_xs_4096x14336", (1, 2, 4, 8, 16)))
+OTHER = (("q8_0_4096x4096", (1,)), ("q8_0_splitk_256x65536", (1,)), ("q8_0_head_152064x5120", (1, 16)))
+
+
+def sweep_rows(torch, qmv, workload, tokens, reps=21):
+    """Matvec kernel time (median over replays) of one workload at each token
+    count, against the plain read of the same bytes; and the whole step
+    (quantize + matvec)."""
+    fmt, n, k, _, *rest = WORKLOADS[workload]
+    rows, read_us = [], None
+    for t in tokens:
+        log(f"bench: {workload} T={t}")
+        r = Ring(torch, qmv, fmt, n, k, t, workload)
+        if read_us is None:
+            sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+            read_us = timed_replays(torch, lambda i: qmv.stream_read(r.w[i % r.copies][0].view(-1), sink),
+                                    max(r.copies, 32), reps)
+        us = kernel_us(torch, qmv, r, reps)
+        step_us = timed_replays(torch, lambda i: r.step(qmv, i), max(r.copies, 32), reps)
+        vi, slices = qmv.matvec_plan(fmt, n, k, t, r.ws is not None)
+        gbs = r.weight_bytes / (us * 1e-6) / 1e9
+        rows.append({"workload": workload, "tokens": t, "kernel_us": round(us, 3), "weight_GBps": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "matvecs_per_s": round(1e6 / us, 1),
+                     "read_ceiling_us": round(read_us, 3), "frac_of_read_ceiling": round(read_us / us, 4),
+                     "step_us": round(step_us, 3),
+                     "step_GBps": round(r.weight_bytes / (step_us * 1e-6) / 1e9, 1),
+                     "int8_TOPS": round(2.0 * n * k * t / (us * 1e-6) / 1e12, 2),
+                     "variant": qmv.variant_name(vi), "k_slices_over_workgroups": slices})
+        del r
+        torch.cuda.empty_cache()
+    return rows
+
+
+def moe_rows(torch, qmv, tokens, reps=5):
+    """The MoE decode step (quantize x, routed gate+up, quantize h, routed
+    and route-weighted down) at each token count: median step time."""
+    rows = []
+    for t in tokens:
+        log(f"bench: MoE step T={t}")
+        ring = MoeRing(torch, qmv, t)
+        per = 16
+        us = timed_replays(torch, lambda i: ring.step(qmv, i), per, reps)
+        gu_us = timed_replays(torch, lambda i: ring.gate_up(qmv, i), per, reps)
+        dn_us = timed_replays(torch, lambda i: ring.down(qmv, i), per, reps)
+        u = ring.avg_bytes(per) / ring.bytes_per_expert
+        b = ring.avg_bytes(per)
+        rows.append({"workload": "MoE IQ4_XS 128 experts top-8, gate+up 3072x4096 + down 4096x1536", "tokens": t,
+                     "avg_distinct_experts": round(u, 2), "weight_bytes_per_step": round(b),
+                     "step_us": round(us, 3), "step_GBps": round(b / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac_step": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "gate_up_us": round(gu_us, 3), "down_us": round(dn_us, 3)})
+        del ring
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,14 +572,22 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=1)
     ap.add_argument("--all-tokens", action="store_true",
                     help="also time the matvec at every token count of the workload")
+    ap.add_argument("--quick", action="store_true",
+                    help="the headline only: no token sweep, no other configurations")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-kernel median/avg/min/max of a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
 
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (the matvec is "
               "measured on one GPU's share of the weights; multi-GPU sharding is not built)",
               file=sys.stderr)
         return 2
+
+    clocks = gpu_clocks()  # read before anything touches the GPU
 
     import torch
 
@@ -523,13 +623,20 @@ def main() -> int:
                       if args.warmup % per else None), args.warmup)
     torch.cuda.synchronize()
 
+    # exactly --steps steps between two device synchronizations; HIP events
+    # on the same stream give their GPU time, the host clock the wall time
     log(f"bench: timing {args.steps} steps")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     run_steps(torch, graphs, args.steps)
+    e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    wall_ms_per_step = elapsed * 1e3 / args.steps
     value = ring.weight_bytes / (ms_per_step * 1e-3) / 1e9
 
     kus = kernel_us(torch, qmv, ring)
@@ -541,7 +648,7 @@ def main() -> int:
     # ring): the practical ceiling of one launch streaming them
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     read_us = timed_replays(torch, lambda i: [qmv.stream_read(w.view(-1), sink) for w in ring.w[i % ring.copies]],
-                            max(ring.copies, 32), reps=20)
+                            max(ring.copies, 32))
     src_hash = kernel_source_hash()
     traffic = recorded_traffic(args.workload, t, src_hash)
     # a batch of equal matrices runs the variant of their stacked rows (each
@@ -572,6 +679,17 @@ def main() -> int:
                 del r2
                 torch.cuda.empty_cache()
 
+    sweep, others, moe = [], [], []
+    default_run = args.workload == "q4_k_14336x4096" and t == 1 and not args.quick and not args.all_tokens
+    if default_run:
+        del ring, g_full, g_tail, graphs
+        torch.cuda.empty_cache()
+        for wl, toks in SWEEP:
+            sweep += sweep_rows(torch, qmv, wl, toks)
+        for wl, toks in OTHER:
+            others += sweep_rows(torch, qmv, wl, toks, reps=11)
+        moe = moe_rows(torch, qmv, (1, 64))
+
     cpu = None
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
@@ -593,28 +711,35 @@ def main() -> int:
         "config": {"workload": (f"{FMT_NAME[fmt]} matvec {n}x{k}, {t} token(s)" if mats == 1 else
                                 f"{mats} sibling {FMT_NAME[fmt]} matvecs {n}x{k} in one launch, {t} token(s)"),
                    "format": FMT_NAME[fmt], "n_rows": n, "k": k, "tokens": t, "matrices": mats,
-                   "weight_bytes": ring.weight_bytes, "ring_copies": ring.copies,
+                   "weight_bytes": ring.weight_bytes if not default_run else WEIGHT_BYTES[args.workload],
                    "step": "qmv_quantize_act + " + ("qmv_matvec" if mats == 1 else "qmv_matvec_batch"),
                    "matvec_variant": variant, "k_slices_over_workgroups": slices},
+        "ms_per_step_wall": round(wall_ms_per_step, 6),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "matvecs_per_s": round(1e3 / ms_per_step, 1),
         **({"matvec_x_step_us": round(fused_us, 3),
-            "matvec_x_step_GBps": round(ring.weight_bytes / (fused_us * 1e-6) / 1e9, 1)} if fused_us else {}),
+            "matvec_x_step_GBps": round(WEIGHT_BYTES.get(args.workload, 0) / (fused_us * 1e-6) / 1e9, 1)}
+           if fused_us and args.workload in WEIGHT_BYTES else {}),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel_us": round(kus, 3),
-                     "algorithmic_bytes_per_launch": ring.weight_bytes,
+                     "traffic": traffic, "kernel_us": round(kus, 3), "kernel_us_stat": "median over replays",
+                     "algorithmic_bytes_per_launch": WEIGHT_BYTES.get(args.workload, 0) * mats,
                      "kernel_sources_sha256_16": src_hash},
         "read_ceiling": {"kernel_us": round(read_us, 3),
-                         "GBps": round(ring.weight_bytes / (read_us * 1e-6) / 1e9, 1),
-                         "frac_of_peak": round(ring.weight_bytes / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "GBps": round(WEIGHT_BYTES.get(args.workload, 0) * mats / (read_us * 1e-6) / 1e9, 1),
+                         "frac_of_peak": round(WEIGHT_BYTES.get(args.workload, 0) * mats / (read_us * 1e-6) / 1e9
+                                               / HBM_PEAK_GBS, 4),
                          "matvec_frac_of_ceiling": round(read_us / kus, 4),
                          "launches": mats},
-        "device": device_info(torch),
+        "device": device_info(torch, clocks),
         "cpu_baseline": cpu,
     }
     if by_tokens:
         out["by_tokens"] = by_tokens
+    if sweep:
+        out["by_tokens"] = sweep
+        out["other_configs"] = others
+        out["moe_steps"] = moe
     print(json.dumps(out), flush=True)
     return 0
 

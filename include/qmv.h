@@ -120,7 +120,9 @@ size_t qmv_act_offset_s(int64_t n_tok, int64_t k);
  *   q = x / d (fp32, correctly rounded) rounded half away from zero,
  *       clamped to [-127, 127],   s = sum of q;
  *   an all-zero block gives d = 0, q = 0, s = 0.
- * x   : fp32 [n_tok][ldx] (device), 4-byte aligned, ldx >= k, finite values.
+ * x   : fp32 [n_tok][ldx] (device), 16-byte aligned, ldx >= k, ldx % 4 == 0
+ *       (else QMV_ERR_MISALIGNED: rows are read with 16-byte loads), finite
+ *       values.
  * xq  : activation buffer of qmv_act_bytes(n_tok, k) bytes (device, 256-byte
  *       aligned); fully overwritten.
  * 1 <= n_tok <= QMV_MAX_ACT_ROWS, k > 0, k % 32 == 0.
@@ -137,7 +139,8 @@ qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, int64_t 
  *   in a gate+up tensor, as qmv_moe_matvec produces them per slot),
  *   h = g / (1 + exp(-g)) * u  in fp32,
  * then the Q8 blocks of h exactly as qmv_quantize_act makes them.
- * gu    : fp32 [rows][ldg] (device), 4-byte aligned, ldg >= 2 n_ff, finite.
+ * gu    : fp32 [rows][ldg] (device), 16-byte aligned, ldg >= 2 n_ff,
+ *         ldg % 4 == 0 (else QMV_ERR_MISALIGNED: 16-byte loads), finite.
  * xq    : activation buffer of qmv_act_bytes(rows, n_ff) bytes (device,
  *         256-byte aligned); fully overwritten.
  * h_out : NULL, or fp32 [rows][n_ff] (device, 16-byte aligned) that receives
@@ -319,13 +322,55 @@ qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t 
                           const void* xq, int64_t n_tok, int32_t* out, void* stream);
 
 /*
+ * qmv_block_dots_mx -- test hook: the same exact block integers as
+ * qmv_block_dots, computed by the matrix-core kernel of qmv_matvec (its
+ * activation staging, weight loads and decode, and the int8 matrix-core
+ * products whose zero-masked activation rows keep every 32-block apart),
+ * which writes each product's integer times the block's integer weight
+ * scale (and, for q4_K, m_j * s_b) instead of applying the fp32 scales.
+ * Castagna Veloce page, "Philosophy" (exact changes verified bit-identical
+ * against a CPU reference).
+ * variant : -1, the matrix-core variant qmv_matvec runs for this shape with
+ *           a workspace (else mx_w16_k4_r2 up to 8 tokens, mx_w8_k1_r4
+ *           beyond); or the index of a matrix-core variant (qmv_variant_name
+ *           "mx_...").
+ * slices  : 0 one pass over K; -1 the K split over workgroups qmv_matvec
+ *           would make with a workspace (none if it would not split);
+ *           2..32 that many K slices (QMV_ERR_UNSUPPORTED if they do not fit).
+ * out     : int32 [n_tok][n_rows][k/32][c] as for qmv_block_dots (device).
+ * Types Q8_0, q4_K, IQ4_XS and Q8G128 (others: QMV_ERR_UNSUPPORTED);
+ * 1 <= n_tok <= QMV_MAX_TOKENS.  No workspace; nothing else is written.
+ */
+qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_rows, int64_t k, const void* xq,
+                             int64_t n_tok, int64_t variant, int slices, int32_t* out, void* stream);
+
+/*
+ * qmv_moe_block_dots -- test hook: the exact block integers of every routed
+ * slot, computed by the matrix-core expert-grouped kernel of qmv_moe_matvec
+ * (its routing sort, slot-row staging, weight loads, decode and int8
+ * matrix-core products) in place of its fp32 outputs.  Castagna Veloce page,
+ * "Kernels for the MI50" (expert-grouped MoE) and "Philosophy".
+ * Arguments as for qmv_moe_matvec (no route weights); slot_rows is the number
+ * of slot rows staged per group: 4 or 8, or 0 for the automatic choice (4 up
+ * to 16 tokens, 8 beyond).
+ * out : int32 [n_tok * top_k][n_rows][k/32][c] (device), c = 2 for q4_K
+ *       else 1: for slot t * top_k + s the integers of W[ids[t][s]] against
+ *       that slot's activation row; the entries of dropped slots are not
+ *       written.  QMV_ERR_UNSUPPORTED if the staged rows do not fit in LDS.
+ */
+qmv_status qmv_moe_block_dots(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows, int64_t k,
+                              const void* xq, int x_per_slot, const int32_t* ids, int64_t n_tok, int64_t top_k,
+                              int64_t slot_rows, int32_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qmv_stream_read -- measurement hook: reads the `bytes` bytes at p (device)
  * once with non-temporal 16-byte loads (256-lane workgroups, four loads per
  * lane in flight, lanes on adjacent pieces: the fastest plain read measured
  * on MI355X), and computes nothing from them: the practical ceiling of a
  * kernel streaming the same bytes.  Decode kernels are measured by weight
- * bytes over kernel time (zhuai.tech GLM-5.3 page, "Performance optimization
- * chain"); this gives the same figure for a kernel with no decode at all.
+ * bytes over kernel time (zhuai.tech GLM-5.3 page, "A faster kernel can
+ * still leave the full chain slower", its bandwidth breakdown); this gives
+ * the same figure for a kernel with no decode at all.
  * sink : one uint32 (device); written only if the fold of the bytes hits a
  *        fixed 32-bit value, so in practice never.
  * bytes a positive multiple of 16 (else QMV_ERR_INVALID_ARG); p 16-byte and

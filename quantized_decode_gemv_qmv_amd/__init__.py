@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "Q8G128", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
-    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots", "stream_read",
+    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots",
+    "block_dots_mx", "moe_block_dots", "stream_read",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "matvec_plan", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
 
@@ -88,6 +89,8 @@ def lib():
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
+        "qmv_block_dots_mx": ([I, P, I64, I64, P, I64, I64, I, P, P], I),
+        "qmv_moe_block_dots": ([I, P, I64, I64, I64, P, I, P, I64, I64, I64, P, P, SZ, P], I),
         "qmv_stream_read": ([P, I64, P, P], I),
         "qmv_set_tuning": ([ctypes.c_char_p, I64], I),
         "qmv_variant_name": ([I64], ctypes.c_char_p),
@@ -344,6 +347,49 @@ def block_dots(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor,
     _need(out, torch.int32, "out")
     _check(lib().qmv_block_dots(fmt, _ptr(w), n_rows, k, _ptr(xq), n_tok, _ptr(out),
                                 _stream(stream)), "qmv_block_dots")
+    return out
+
+
+def block_dots_mx(fmt: int, w: torch.Tensor, n_rows: int, k: int, xq: torch.Tensor, n_tok: int,
+                  variant: int = -1, slices: int = 0, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """The block integers of block_dots, computed by the matrix-core kernel
+    (variant -1: the one qmv_matvec runs; slices 0 unsplit, -1 automatic,
+    n >= 2 forced): int32 [T][N][K/32][c]."""
+    _need(w, torch.uint8, "w")
+    _need(xq, torch.uint8, "xq")
+    nc = 2 if fmt == Q4_K else 1
+    if out is None:
+        out = torch.empty((n_tok, n_rows, k // 32, nc), dtype=torch.int32, device=w.device)
+    _need(out, torch.int32, "out")
+    if out.numel() < n_tok * n_rows * (k // 32) * nc:
+        raise ValueError("out too small")
+    _check(lib().qmv_block_dots_mx(fmt, _ptr(w), n_rows, k, _ptr(xq), n_tok, variant, slices, _ptr(out),
+                                   _stream(stream)), "qmv_block_dots_mx")
+    return out
+
+
+def moe_block_dots(fmt: int, w: torch.Tensor, n_experts: int, n_rows: int, k: int, xq: torch.Tensor,
+                   x_per_slot: bool, ids: torch.Tensor, ws: torch.Tensor, slot_rows: int = 0,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The block integers of every routed slot from the matrix-core MoE
+    kernel: int32 [T * top_k][N][K/32][c] (dropped slots' entries untouched)."""
+    _need(w, torch.uint8, "w")
+    _need(xq, torch.uint8, "xq")
+    _need(ids, torch.int32, "ids")
+    _need(ws, torch.uint8, "ws")
+    n_tok, top_k = ids.shape
+    nc = 2 if fmt == Q4_K else 1
+    if out is None:
+        out = torch.zeros((n_tok * top_k, n_rows, k // 32, nc), dtype=torch.int32, device=w.device)
+    _need(out, torch.int32, "out")
+    if out.numel() < n_tok * top_k * n_rows * (k // 32) * nc:
+        raise ValueError("out too small")
+    if w.numel() < n_experts * n_rows * row_bytes(fmt, k):
+        raise ValueError("w holds fewer than n_experts * n_rows rows")
+    _check(lib().qmv_moe_block_dots(fmt, _ptr(w), n_experts, n_rows, k, _ptr(xq), int(bool(x_per_slot)),
+                                    _ptr(ids), n_tok, top_k, slot_rows, _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "qmv_moe_block_dots")
     return out
 
 

@@ -15,13 +15,17 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqmv.so")
-# (source, object, extra flags): the dense vector kernels are compiled once per
-# weight format so that those instantiations build in parallel
+# (source, object, extra flags): the dense vector and matrix-core kernels are
+# compiled once per weight format so that those instantiations build in
+# parallel
 FORMATS = {0: "q8_0", 1: "q4_k", 2: "iq4_xs", 3: "q5_k", 4: "q6_k", 5: "q8g128"}
+# the formats with a matrix-core decode, whose kernels are compiled per format too
+MX_FORMATS = (0, 1, 2, 5)
 SOURCES = ([(s, os.path.splitext(s)[0], []) for s in
-            ("qmv_api.hip", "qmv_variants.hip", "qmv_quant.hip", "qmv_mfma.hip", "qmv_moe.hip", "qmv_router.hip",
+            ("qmv_api.hip", "qmv_variants.hip", "qmv_quant.hip", "qmv_moe.hip", "qmv_router.hip",
              "qmv_measure.hip")]
-           + [("qmv_matvec.hip", f"qmv_matvec_{n}", [f"-DQMV_MATVEC_FMT={f}"]) for f, n in FORMATS.items()])
+           + [("qmv_matvec.hip", f"qmv_matvec_{n}", [f"-DQMV_MATVEC_FMT={f}"]) for f, n in FORMATS.items()]
+           + [("qmv_mfma.hip", f"qmv_mfma_{FORMATS[f]}", [f"-DQMV_MX_FMT={f}"]) for f in MX_FORMATS])
 ARCH = os.environ.get("QMV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -316,7 +316,7 @@ int split_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const DeviceInfo dv = device_info();
   int ups = 0;
   return mx_split_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].ks, (int)(k / 32), (int)n_rows, dv.cus,
-                       dv.lds_per_cu, &ups) >= 2
+                       dv.lds_per_cu, mx_slices(), &ups) >= 2
              ? v
              : -1;
 }
@@ -338,7 +338,7 @@ Plan make_plan(int type, int64_t n_rows, int64_t k, int64_t n_tok, bool use_ws) 
     const DeviceInfo dv = device_info();
     int ups = 0;
     const int s = mx_split_plan(type, (int)n_tok, kVariants[p.variant].wpb, kVariants[p.variant].ks, (int)(k / 32),
-                                (int)n_rows, dv.cus, dv.lds_per_cu, &ups);
+                                (int)n_rows, dv.cus, dv.lds_per_cu, mx_slices(), &ups);
     p.slices = s >= 2 ? s : 1;
   } else if (kVariants[p.variant].kind == 2 && kVariants[p.variant].xl && flat_split_enabled()) {
     p.slices = flat_split(kVariants[p.variant], n_rows, k / 32, n_tok, &p.ups);
@@ -461,7 +461,8 @@ QMV_API qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, 
   if (x == nullptr || xq == nullptr || n_tok < 1 || k < 1 || k % 32 || ldx < k)
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_ACT_ROWS || k > (int64_t)1 << 24) return QMV_ERR_UNSUPPORTED;
-  if (!aligned(x, 4) || !aligned(xq, 256)) return QMV_ERR_MISALIGNED;
+  // each lane reads four values with one 16-byte load at x + t * ldx + 4j
+  if (!aligned(x, 16) || ldx % 4 || !aligned(xq, 256)) return QMV_ERR_MISALIGNED;
   uint8_t* b = static_cast<uint8_t*>(xq);
   hipError_t e = launch_quantize(x, ldx, static_cast<int>(n_tok), static_cast<int>(k),
                                  reinterpret_cast<int8_t*>(b),
@@ -476,7 +477,8 @@ QMV_API qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t row
   if (gu == nullptr || xq == nullptr || rows < 1 || n_ff < 1 || n_ff % 32 || ldg < 2 * n_ff)
     return QMV_ERR_INVALID_ARG;
   if (rows > QMV_MAX_ACT_ROWS || n_ff > (int64_t)1 << 24) return QMV_ERR_UNSUPPORTED;
-  if (!aligned(gu, 4) || !aligned(xq, 256) || (h_out != nullptr && !aligned(h_out, 16)))
+  // each lane reads four values of g and of u with 16-byte loads
+  if (!aligned(gu, 16) || ldg % 4 || !aligned(xq, 256) || (h_out != nullptr && !aligned(h_out, 16)))
     return QMV_ERR_MISALIGNED;
   uint8_t* b = static_cast<uint8_t*>(xq);
   hipError_t e = launch_swiglu_quantize(gu, ldg, static_cast<int>(rows), static_cast<int>(n_ff),
@@ -729,6 +731,56 @@ QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, 
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 
+QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_rows, int64_t k, const void* xq,
+                                     int64_t n_tok, int64_t variant, int slices, int32_t* out, void* stream) {
+  qmv_status st = check_weights(type, w, n_rows, k);
+  if (st != QMV_OK) return st;
+  if (xq == nullptr || out == nullptr || n_tok < 1 || slices < -1 || slices == 1 || slices > kMaxSlices ||
+      variant < -1 || variant >= kNumVariants || (variant >= 0 && kVariants[variant].kind != 4))
+    return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_TOKENS || !has_mfma(type)) return QMV_ERR_UNSUPPORTED;
+  if (n_tok * n_rows * (k / 32) > INT32_MAX) return QMV_ERR_UNSUPPORTED;
+  if (!aligned(xq, 256) || !aligned(out, 4)) return QMV_ERR_MISALIGNED;
+  int v = static_cast<int>(variant);
+  if (v < 0) {
+    // the matrix-core variant qmv_matvec runs for this shape with a
+    // workspace, if it runs one; else the 16-wave one up to eight tokens
+    // and the 8-wave one beyond
+    const bool use_ws = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok) > 0;
+    const Plan p = make_plan(type, n_rows, k, n_tok, use_ws);
+    v = kVariants[p.variant].kind == 4 ? p.variant : find_variant(n_tok <= 8 ? "mx_w16_k4_r2" : "mx_w8_k1_r4");
+  }
+  const DeviceInfo dv = device_info();
+  if (slices >= 2) {
+    int ups = 0;
+    if (mx_split_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].ks, (int)(k / 32), (int)n_rows, dv.cus,
+                      dv.lds_per_cu, slices, &ups) < 2)
+      return QMV_ERR_UNSUPPORTED;  // that many slices do not fit this shape
+  }
+  MatvecLaunch a{};
+  a.fmt = type;
+  a.w = static_cast<const uint8_t*>(w);
+  a.row_bytes = static_cast<int64_t>(qmv_row_bytes(type, k));
+  a.n_rows = static_cast<int>(n_rows);
+  a.units = static_cast<int>(k / 32);
+  a.x = act_view(xq, n_tok, k);
+  a.n_tok = static_cast<int>(n_tok);
+  a.y = nullptr;
+  a.ldy = n_rows;
+  a.xq = static_cast<const uint8_t*>(xq);
+  a.act_bytes = static_cast<int64_t>(qmv_act_bytes(n_tok, k));
+  a.off_d = static_cast<int64_t>(qmv_act_offset_d(n_tok, k));
+  a.off_s = static_cast<int64_t>(qmv_act_offset_s(n_tok, k));
+  a.cus = dv.cus;
+  a.lds_per_cu = dv.lds_per_cu;
+  a.variant = v;
+  a.slices = 1;
+  a.dots = out;
+  a.dots_slices = slices;
+  hipError_t e = launch_mx(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
 QMV_API qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* stream) {
   if (p == nullptr || sink == nullptr || bytes < 16 || bytes % 16) return QMV_ERR_INVALID_ARG;
   if (bytes / 16 > (int64_t)INT32_MAX * 1024) return QMV_ERR_UNSUPPORTED;  // grid limit
@@ -790,5 +842,51 @@ QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_expert
   a.err = reinterpret_cast<int*>(b);
   a.part = reinterpret_cast<float*>(b + kMoePartOffset);
   hipError_t e = launch_moe(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
+QMV_API qmv_status qmv_moe_block_dots(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows, int64_t k,
+                                      const void* xq, int x_per_slot, const int32_t* ids, int64_t n_tok,
+                                      int64_t top_k, int64_t slot_rows, int32_t* out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  qmv_status st = check_weights(type, w, n_rows, k);
+  if (st != QMV_OK) return st;
+  if (xq == nullptr || ids == nullptr || out == nullptr || ws == nullptr || n_tok < 1 || top_k < 1 ||
+      n_experts < 1 || (x_per_slot != 0 && x_per_slot != 1) || (slot_rows != 0 && slot_rows != 4 && slot_rows != 8))
+    return QMV_ERR_INVALID_ARG;
+  if (n_tok > QMV_MAX_MOE_TOKENS || top_k > QMV_MAX_TOP_K || n_experts > QMV_MAX_EXPERTS ||
+      k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows || !moe_format(type))
+    return QMV_ERR_UNSUPPORTED;
+  if (n_experts * n_rows > INT32_MAX || n_tok * top_k * n_rows * (k / 32) > INT32_MAX / 2)
+    return QMV_ERR_UNSUPPORTED;
+  if (!aligned(xq, 256) || !aligned(ids, 4) || !aligned(out, 4) || !aligned(ws, 256)) return QMV_ERR_MISALIGNED;
+  if (ws_bytes < qmv_moe_workspace_bytes(type, n_experts, n_rows, k, n_tok, top_k)) return QMV_ERR_WORKSPACE;
+  const int64_t x_rows = x_per_slot ? n_tok * top_k : n_tok;
+  MoeLaunch a{};
+  a.fmt = type;
+  a.w = static_cast<const uint8_t*>(w);
+  a.row_bytes = static_cast<int64_t>(qmv_row_bytes(type, k));
+  a.n_experts = static_cast<int>(n_experts);
+  a.n_rows = static_cast<int>(n_rows);
+  a.units = static_cast<int>(k / 32);
+  a.x = act_view(xq, x_rows, k);
+  a.x_rows = static_cast<int>(x_rows);
+  a.x_per_slot = x_per_slot;
+  a.ids = ids;
+  a.rw = nullptr;
+  a.n_tok = static_cast<int>(n_tok);
+  a.top_k = static_cast<int>(top_k);
+  a.y = nullptr;
+  const DeviceInfo dv = device_info();
+  a.cus = dv.cus;
+  a.lds_per_cu = dv.lds_per_cu;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  a.err = reinterpret_cast<int*>(b);
+  a.part = reinterpret_cast<float*>(b + kMoePartOffset);
+  a.dots = out;
+  // the slot rows per group the automatic choice stages: 4 up to 16 tokens, 8 beyond
+  const int tm = slot_rows != 0 ? static_cast<int>(slot_rows) : (n_tok <= 16 ? 4 : 8);
+  hipError_t e = launch_moe_mx_dots(a, tm, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return QMV_ERR_UNSUPPORTED;  // the staged rows do not fit in LDS
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }

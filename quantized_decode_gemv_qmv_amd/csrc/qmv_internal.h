@@ -99,6 +99,10 @@ struct StreamArgs {
   int ups;
   float* part;
   int* cnt;
+  // integer mode of k_mx (the block-dot test hook): the exact integer of
+  // every (token, row, 32-block) goes to dots, int32 [n_tok][n_rows][units][c]
+  // (c = 2 for q4_K: sc * sum q qx, m * s; else 1), and no output is stored
+  int32_t* dots;
 };
 
 #ifdef __HIPCC__
@@ -168,6 +172,11 @@ struct MatvecLaunch {
   int slices;
   float* part;
   int* cnt;
+  // integer mode (launch_mx only): the exact block integers to dots instead
+  // of any output; dots_slices 0 unsplit, -1 the automatic split, n >= 2 n
+  // K slices over workgroups (no workspace: nothing is reduced)
+  int32_t* dots;
+  int dots_slices;
 };
 
 // Rows covered by one 256-thread workgroup of a variant.
@@ -188,8 +197,10 @@ int mx_slices();
 // Cross-workgroup K split of k_mx for format fmt, n_tok tokens and a
 // variant of wpb waves in teams of ks: the slice count (>= 2, units per
 // slice in *ups) or 0 for no split.
+// forced: -1 automatic, 0 never, n >= 2 that many slices (the mx_slices
+// tuning switch supplies it for qmv_matvec).
 int mx_split_plan(int fmt, int n_tok, int wpb, int ks, int units, int n_rows, int cus, int64_t lds_per_cu,
-                  int* ups);
+                  int forced, int* ups);
 
 hipError_t launch_quantize(const float* x, int64_t ldx, int n_tok, int k, int8_t* qs, float* d,
                            int32_t* s, hipStream_t st);
@@ -203,6 +214,9 @@ hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
 template <int F>
 hipError_t launch_vector(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
+// The matrix-core kernels of format F (one translation unit per format).
+template <int F>
+hipError_t launch_mx_fmt(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_stream_read(const uint8_t* p, int64_t bytes, uint32_t key, uint32_t* sink, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const uint8_t* w, int64_t row_bytes, int n_rows, int units,
                              ActView x, int n_tok, int32_t* out, hipStream_t st);
@@ -228,9 +242,17 @@ struct MoeLaunch {
   // workspace
   int* err;     // dropped-slot count of the call
   float* part;  // [n_tok * top_k][n_rows] per-slot outputs (combine only)
+  // integer mode of the matrix-core MoE kernel (the block-dot test hook):
+  // the exact integers of every (slot, row, 32-block) of the slot's expert
+  // go to dots, int32 [n_tok * top_k][n_rows][units][c], and nothing else
+  // is written
+  int32_t* dots;
 };
 
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t st);
+// The matrix-core MoE kernel with tm (4 or 8) staged slot rows per group, in
+// integer mode (a.dots set).
+hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st);
 // Tuning: MoE kernel (0 automatic, 1 vector-ALU, 2 matrix-core).
 void set_moe_kernel(int v);
 

@@ -782,6 +782,10 @@ static StreamArgs stream_args(const MatvecLaunch& a) {
   sa.x = nullptr;
   sa.ldx = 0;
   sa.xq_out = nullptr;
+  sa.ups = 0;
+  sa.part = nullptr;
+  sa.cnt = nullptr;
+  sa.dots = nullptr;
   return sa;
 }
 

@@ -1,7 +1,8 @@
 // qmv_measure.hip -- the plain streaming read behind qmv_stream_read: the
 // practical ceiling against which the matvec kernels' weight streams are
-// judged (the zhuai.tech GLM-5.3 page, "Performance optimization chain",
-// measures decode kernels by weight bytes over kernel time).
+// judged (the zhuai.tech GLM-5.3 page, "A faster kernel can still leave the
+// full chain slower", measures decode kernels by weight bytes over kernel
+// time in its bandwidth breakdown).
 #include "qmv_device.h"
 #include "qmv_internal.h"
 

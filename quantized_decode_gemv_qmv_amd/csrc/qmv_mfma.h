@@ -68,6 +68,9 @@ struct MxDec {
   u32x4 b[2];
   float dw[2];  // weight scale of the output block of half h (IQ4_XS, Q8_0: both the same)
   float wm[2];  // q4_K: dmin * m of that block
+  // the integer scales behind dw and wm (q4_K: the 6-bit sc and m; IQ4_XS:
+  // ls - 32; Q8_0, Q8G128: 1), for the block-dot test hook
+  int isc[2], im[2];
 };
 
 // q4_K: 6-bit (scale, min) of sub-block c (0..7) from the 12 packed bytes.
@@ -94,6 +97,8 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FQ4_K>& r, int p, int s, i
     q4k_scale_min(r.hdr, 4 * p + 2 * (s >> 1) + h, sc, m);
     o.dw[h] = d * static_cast<float>(sc);
     o.wm[h] = dmin * static_cast<float>(m);
+    o.isc[h] = static_cast<int>(sc);
+    o.im[h] = static_cast<int>(m);
   }
 }
 __device__ __forceinline__ void mx_decode(const MxRaw<FIQ4_XS>& r, int p, int s, int, int, MxDec& o) {
@@ -109,8 +114,11 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FIQ4_XS>& r, int p, int s,
   const int c = 4 * p + s;
   const uint32_t lo4 = (r.hdr.y >> (4 * c)) & 15u;
   const uint32_t hi2 = (r.hdr.x >> (16 + 2 * c)) & 3u;
-  o.dw[0] = o.dw[1] = half_bits_to_float(r.hdr.x) * static_cast<float>(static_cast<int>(lo4 | (hi2 << 4)) - 32);
+  const int ls = static_cast<int>(lo4 | (hi2 << 4)) - 32;
+  o.dw[0] = o.dw[1] = half_bits_to_float(r.hdr.x) * static_cast<float>(ls);
   o.wm[0] = o.wm[1] = 0.f;
+  o.isc[0] = o.isc[1] = ls;
+  o.im[0] = o.im[1] = 0;
 }
 __device__ __forceinline__ void mx_decode(const MxRaw<FQ8_0>& r, int p, int s, int u0, int units, MxDec& o) {
   Dec<FQ8_0> d;
@@ -120,6 +128,8 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FQ8_0>& r, int p, int s, i
   const bool ok = u0 + 4 * p + s < units;
   o.dw[0] = o.dw[1] = ok ? d.d : 0.f;
   o.wm[0] = o.wm[1] = 0.f;
+  o.isc[0] = o.isc[1] = 1;
+  o.im[0] = o.im[1] = 0;
 }
 
 __device__ __forceinline__ void mx_decode(const MxRaw<FQ8G128>& r, int p, int s, int u0, int units, MxDec& o) {
@@ -130,6 +140,8 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FQ8G128>& r, int p, int s,
   o.b[1] = u32x4{d.q[4], d.q[5], d.q[6], d.q[7]};
   o.dw[0] = o.dw[1] = d.sc;
   o.wm[0] = o.wm[1] = 0.f;
+  o.isc[0] = o.isc[1] = 1;
+  o.im[0] = o.im[1] = 0;
 }
 
 __device__ __forceinline__ i32x4 mfma64(const u32x4& a, const u32x4& b, i32x4 c) {

@@ -61,9 +61,15 @@ namespace qmv {
 // row.  A chunk holds ipc super-blocks, a multiple of KS, so the wave's
 // super-blocks fall into the chunks in order.  Items q = i * n_it + j are
 // loaded PF items ahead of the one computed.
-template <int F, int TM, int WPB, int KS, int PF, bool CH, bool SEG, bool SPLIT = false>
+//
+// DOTS (the block-dot test hook): the same staging, loads, decode and MFMAs,
+// but each MFMA result -- the exact integer dot of one (token, row, 32-block)
+// -- times the block's integer weight scale goes to a.dots instead of into
+// the fp32 sums, and nothing else is stored.
+template <int F, int TM, int WPB, int KS, int PF, bool CH, bool SEG, bool SPLIT = false, bool DOTS = false>
 __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   static_assert(!SPLIT || (!CH && !SEG), "a split launch stages one chunk of one matrix");
+  static_assert(!DOTS || !SEG, "the integer mode runs one matrix");
   constexpr int TG = mx_tg<F>();
   constexpr int NG = (TM + TG - 1) / TG;  // token groups
   constexpr int TMP = NG * TG;            // staged token rows
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   u32x4 A[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
 
   // One super-block of one row tile: the two spans' MFMAs and scale steps.
-  auto compute = [&](const MxRaw<F>& cur, int sb, int c) {
+  auto compute = [&](const MxRaw<F>& cur, int sb, int c, int tile) {
     const int u0 = 8 * sb;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -242,7 +248,36 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
           A[0] = ld16(xl + ab + g * TG * 32);
           A[1] = ld16(xl + ab + g * TG * 32 + aMu);
         }
-        if constexpr (P2) {
+        if constexpr (DOTS) {
+          // lane (n, s): row tile * 16 + n; result r is block bl + (q4_K:
+          // 2 (s >> 1) + mu; else s) of token (q4_K: 8g + 4 (s & 1) + r;
+          // else 4g + r), as the scale steps below read them
+          const int row = tile * 16 + n;
+#pragma unroll
+          for (int mu = 0; mu < (P2 ? 2 : 1); ++mu) {
+            i32x4 dv;
+            if constexpr (P2) {
+              dv = mfma64(A[mu], dec.b[mu], i32x4{0, 0, 0, 0});
+            } else {
+              dv = mfma64(A[0], dec.b[0], i32x4{0, 0, 0, 0});
+              dv = mfma64(A[1], dec.b[1], dv);
+            }
+            const int lb = u0 + 4 * p + (P2 ? 2 * (s >> 1) + mu : s);  // unit inside the slice
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = P2 ? g * TG + 4 * (s & 1) + r : g * TG + r;
+              if (t < T && row < a.n_rows && lb < units) {
+                const int64_t o = ((int64_t)t * a.n_rows + row) * a.units + ub + lb;
+                if constexpr (Q4K) {
+                  a.dots[2 * o] = dec.isc[mu] * dv[r];
+                  a.dots[2 * o + 1] = dec.im[mu] * gs[t * a.nb + ub + lb];
+                } else {
+                  a.dots[o] = dec.isc[0] * dv[r];
+                }
+              }
+            }
+          }
+        } else if constexpr (P2) {
 #pragma unroll
           for (int mu = 0; mu < 2; ++mu) {
             const i32x4 dv = mfma64(A[mu], dec.b[mu], i32x4{0, 0, 0, 0});
@@ -307,7 +342,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
 #pragma unroll
         for (int kk = 0; kk < PF; ++kk) {
           if (j0 + kk < njc) {
-            compute(ring[kk], sb0 + (j0 + kk) * KS, c);
+            compute(ring[kk], sb0 + (j0 + kk) * KS, c, tile);
             load_next(ring[kk]);
           }
         }
@@ -321,6 +356,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
       }
     }
 
+    if constexpr (DOTS) continue;  // the integers are out; nothing to sum
     // Sum over the lanes that hold the other blocks of the same row and
     // tokens (two blocks per MFMA: lane ^ 32; Q8_0: lanes ^ 16, ^ 32).  Then
     // with two blocks per MFMA lanes s = 0, 1 hold tokens 8g + 4s + r; Q8_0:
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
     }
   }
 
-  if constexpr (SPLIT) {
+  if constexpr (SPLIT && !DOTS) {
     // The last workgroup of this column (its TEAMS row tiles) to finish sums
     // the slices' partials in slice order.  The partials are stored and
     // loaded with device-scope atomic accesses, which the gfx950 L2 writes
@@ -443,15 +479,15 @@ constexpr int64_t kMxLdsBudget = 144 * 1024;
 static int mx_per_unit(int fmt, int tmp) { return (tmp * 32 + 16) + tmp * 4 * (fmt == FQ4_K ? 2 : 1); }
 static int64_t mx_fixed(int wpb, int ks, int tmp) { return 16 + (ks > 1 ? (int64_t)wpb * tmp * 16 * 4 : 0); }
 
+#if QMV_MX_FMT == 0  // host helpers: defined once, in the Q8_0 unit
 int mx_split_plan(int fmt, int n_tok, int wpb, int ks, int units, int n_rows, int cus, int64_t lds_per_cu,
-                  int* ups_out) {
+                  int forced, int* ups_out) {
   const int tg = fmt == FQ4_K ? 8 : 4;
   const int tm = n_tok <= 4 ? 4 : n_tok <= 8 ? 8 : 16;
   const int tmp = (tm + tg - 1) / tg * tg;
   const int per_unit = mx_per_unit(fmt, tmp);
   const int64_t fixed = mx_fixed(wpb, ks, tmp);
   const int step = 8 * ks;
-  const int forced = mx_slices();
   if (forced == 0) return 0;
   // a slice is whole wave shares and fits one chunk in the LDS of 2 (8-wave)
   // or 1 (16-wave) workgroups per compute unit, 64 bytes left for the
@@ -481,6 +517,7 @@ int mx_split_plan(int fmt, int n_tok, int wpb, int ks, int units, int n_rows, in
   *ups_out = ups;
   return slices;
 }
+#endif
 
 template <int F, int TM, int WPB, int KS, int PF>
 static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
@@ -511,9 +548,35 @@ static hipError_t run_mx(const MatvecLaunch& a, hipStream_t st) {
   const size_t lds = (size_t)sa.kc * per_unit + fixed;
   const int64_t tiles = (a.n_rows + 15) / 16;
   const int64_t need = (tiles + TEAMS - 1) / TEAMS;
+  if (a.dots != nullptr) {
+    // integer mode (test hook): the same launch shapes, no workspace
+    sa.dots = a.dots;
+    int ups = 0;
+    const int slices = a.dots_slices == 0 ? 0
+                       : mx_split_plan(F, a.n_tok, WPB, KS, a.units, a.n_rows, a.cus, a.lds_per_cu, a.dots_slices,
+                                       &ups);
+    if (slices >= 2) {
+      sa.kc = ups;
+      sa.ups = ups;
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false, false, true, true>), dim3((unsigned)need, (unsigned)slices),
+                         dim3(64 * WPB), (size_t)ups * per_unit + fixed, st, sa);
+    } else if (a.dots_slices >= 2) {
+      return hipErrorInvalidValue;  // the forced slice count does not fit
+    } else if (sa.kc >= a.units) {
+      const int64_t per_cu = (int64_t)a.lds_per_cu / (int64_t)lds;
+      const int64_t cap = (int64_t)a.cus * (per_cu < 1 ? 1 : per_cu);
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, false, false, false, true>), dim3((unsigned)(need < cap ? need : cap)),
+                         dim3(64 * WPB), lds, st, sa);
+    } else {
+      hipLaunchKernelGGL((k_mx<F, TM, WPB, KS, PF, true, false, false, true>), dim3((unsigned)need), dim3(64 * WPB),
+                         lds, st, sa);
+    }
+    return hipGetLastError();
+  }
   if (a.part != nullptr && a.cnt != nullptr && a.seg.n == 0) {
     int ups = 0;
-    const int slices = mx_split_plan(F, a.n_tok, WPB, KS, a.units, a.n_rows, a.cus, a.lds_per_cu, &ups);
+    const int slices =
+        mx_split_plan(F, a.n_tok, WPB, KS, a.units, a.n_rows, a.cus, a.lds_per_cu, mx_slices(), &ups);
     if (slices >= 2) {
       sa.kc = ups;
       sa.ups = ups;
@@ -571,15 +634,28 @@ static hipError_t run_mx_tokens(const MatvecLaunch& a, const Variant& v, hipStre
   return run_mx_shape<F, 16>(a, v, st);
 }
 
+// This translation unit is compiled once per weight format with a
+// matrix-core decode (QMV_MX_FMT), so that their kernels build in parallel;
+// each copy defines the matrix-core entry of its format, and the Q8_0 copy
+// also the dispatcher and the split plan.
+#ifndef QMV_MX_FMT
+#error "compile qmv_mfma.hip with -DQMV_MX_FMT=<format id>"
+#endif
+template <>
+hipError_t launch_mx_fmt<QMV_MX_FMT>(const MatvecLaunch& a, hipStream_t st) {
+  return run_mx_tokens<QMV_MX_FMT>(a, kVariants[a.variant], st);
+}
+
+#if QMV_MX_FMT == 0
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st) {
-  const Variant& v = kVariants[a.variant];
   switch (a.fmt) {
-    case FQ8_0: return run_mx_tokens<FQ8_0>(a, v, st);
-    case FQ4_K: return run_mx_tokens<FQ4_K>(a, v, st);
-    case FIQ4_XS: return run_mx_tokens<FIQ4_XS>(a, v, st);
-    case FQ8G128: return run_mx_tokens<FQ8G128>(a, v, st);
+    case FQ8_0: return launch_mx_fmt<FQ8_0>(a, st);
+    case FQ4_K: return launch_mx_fmt<FQ4_K>(a, st);
+    case FIQ4_XS: return launch_mx_fmt<FIQ4_XS>(a, st);
+    case FQ8G128: return launch_mx_fmt<FQ8G128>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
+#endif
 
 }  // namespace qmv

@@ -105,7 +105,7 @@ __device__ void moe_route(const MoeLaunch& a, int* s_id, int* s_cnt, int* s_slot
   }
   __syncthreads();
   if (blockIdx.x == 0 && tid == 0) a.err[0] = *s_drop;
-  if (*s_drop > 0 && a.rw == nullptr) {
+  if (*s_drop > 0 && a.rw == nullptr && a.dots == nullptr) {
     for (int i = 0; i < n_slots; ++i)
       if (s_id[i] < 0)
         for (int r = blockIdx.x * NT + tid; r < a.n_rows; r += gridDim.x * NT)
@@ -253,7 +253,12 @@ __global__ __launch_bounds__(64 * WPB) void k_moe(MoeLaunch a) {
 // waves walk the chunk's tiles, each tile over the whole K with the next
 // super-block's weights in flight.  More slots than TMP go in further groups,
 // each reading the expert's rows again.
-template <int F, int TM, int WPB>
+//
+// DOTS (the block-dot test hook): the same routing, staging, loads, decode
+// and MFMAs, but each MFMA result -- the exact integer dot of one (slot, row,
+// 32-block) -- times the block's integer weight scale goes to a.dots, and no
+// output is written.
+template <int F, int TM, int WPB, bool DOTS = false>
 __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
   constexpr int TG = mx_tg<F>();
   constexpr int NG = (TM + TG - 1) / TG;  // token groups
@@ -401,7 +406,37 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
                 A[0] = ld16(xl + ab + g * TG * 32);
                 A[1] = ld16(xl + ab + g * TG * 32 + aMu);
               }
-              if constexpr (P2) {
+              if constexpr (DOTS) {
+                // lane (n, s): row t * 16 + n; result r is block bl + (q4_K:
+                // 2 (s >> 1) + mu; else s) of the group's slot row (q4_K:
+                // 8g + 4 (s & 1) + r; else 4g + r), as in the scale steps below
+                const int row = t * 16 + n;
+#pragma unroll
+                for (int mu = 0; mu < (P2 ? 2 : 1); ++mu) {
+                  i32x4 dv;
+                  if constexpr (P2) {
+                    dv = mfma64(A[mu], dec.b[mu], i32x4{0, 0, 0, 0});
+                  } else {
+                    dv = mfma64(A[0], dec.b[0], i32x4{0, 0, 0, 0});
+                    dv = mfma64(A[1], dec.b[1], dv);
+                  }
+                  const int blk = bl + (P2 ? 2 * (s >> 1) + mu : s);
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) {
+                    const int j = P2 ? g * TG + 4 * (s & 1) + r : g * TG + r;
+                    if (j < ng && row < a.n_rows && blk < units) {
+                      const int slot = s_slot[b0 + g0 + j];
+                      const int64_t o = ((int64_t)slot * a.n_rows + row) * units + blk;
+                      if constexpr (Q4K) {
+                        a.dots[2 * o] = dec.isc[mu] * dv[r];
+                        a.dots[2 * o + 1] = dec.im[mu] * a.x.s[(int64_t)x_row(slot) * nb + blk];
+                      } else {
+                        a.dots[o] = dec.isc[0] * dv[r];
+                      }
+                    }
+                  }
+                }
+              } else if constexpr (P2) {
 #pragma unroll
                 for (int mu = 0; mu < 2; ++mu) {
                   const i32x4 dv = mfma64(A[mu], dec.b[mu], i32x4{0, 0, 0, 0});
@@ -428,6 +463,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
           }
           cur = nxt;
         }
+        if constexpr (DOTS) continue;  // the integers are out; nothing to sum
         // lanes holding the other blocks of the same row and slots, then the
         // slot outputs (see the dense kernel for the lane layout)
         const int row = t * 16 + n;
@@ -737,13 +773,13 @@ static hipError_t run_moe_fmt(const MoeLaunch& a, hipStream_t st) {
 
 // Matrix-core launch: TM staged slot rows per group (TMP after rounding to
 // token groups), 8-wave workgroups, a persistent grid sized by occupancy.
-template <int F, int TM>
+template <int F, int TM, bool DOTS = false>
 static hipError_t run_moe_mx(const MoeLaunch& a0, hipStream_t st) {
   constexpr int WPB = 8;
   constexpr int TG = mx_tg<F>();
   constexpr int TMP = ((TM + TG - 1) / TG) * TG;
   MoeLaunch a = a0;
-  auto kern = k_moe_mx<F, TM, WPB>;
+  auto kern = k_moe_mx<F, TM, WPB, DOTS>;
   const int64_t kb = 8 * (int64_t)((a.units + 7) / 8);
   size_t lds = (size_t)(kb * (TMP * 32 + 16) + 16 + kb * TMP * 4 * (F == FQ4_K ? 2 : 1));
   if (lds < (size_t)kMaxSlots * 4) lds = (size_t)kMaxSlots * 4;  // the ids during the sort
@@ -772,10 +808,20 @@ static hipError_t run_moe_mx(const MoeLaunch& a0, hipStream_t st) {
   const unsigned grid = (unsigned)(max_items < cap ? max_items : cap);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WPB), lds, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.rw == nullptr) return e;
+  if (e != hipSuccess || a.rw == nullptr || DOTS) return e;
   const int64_t outs = (int64_t)a.n_tok * a.n_rows;
   hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st) {
+  if (a.dots == nullptr || (tm != 4 && tm != 8)) return hipErrorInvalidValue;
+  switch (a.fmt) {
+    case FQ8_0: return tm == 4 ? run_moe_mx<FQ8_0, 4, true>(a, st) : run_moe_mx<FQ8_0, 8, true>(a, st);
+    case FQ4_K: return tm == 4 ? run_moe_mx<FQ4_K, 4, true>(a, st) : run_moe_mx<FQ4_K, 8, true>(a, st);
+    case FIQ4_XS: return tm == 4 ? run_moe_mx<FIQ4_XS, 4, true>(a, st) : run_moe_mx<FIQ4_XS, 8, true>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int F, int NU, int R>

@@ -100,6 +100,9 @@ def test_quantize_validation(L):
     assert f(FAKE, 31, 1, 32, FAKE, None) == INVALID
     assert f(FAKE, 32, 65537, 32, FAKE, None) == UNSUPPORTED
     assert f(FAKE + 2, 32, 1, 32, FAKE, None) == MISALIGNED
+    assert f(FAKE + 4, 32, 1, 32, FAKE, None) == MISALIGNED  # rows are read 16 bytes at a time
+    assert f(FAKE, 33, 2, 32, FAKE, None) == MISALIGNED      # an odd row stride breaks that too
+    assert f(FAKE, 34, 2, 32, FAKE, None) == MISALIGNED
     assert f(FAKE, 32, 1, 32, FAKE + 4, None) == MISALIGNED
 
 
@@ -112,6 +115,9 @@ def test_swiglu_quantize_validation(L):
     assert f(FAKE, 63, 1, 32, FAKE, None, None) == INVALID
     assert f(FAKE, 64, 65537, 32, FAKE, None, None) == UNSUPPORTED
     assert f(FAKE + 2, 64, 1, 32, FAKE, None, None) == MISALIGNED
+    assert f(FAKE + 8, 64, 1, 32, FAKE, None, None) == MISALIGNED
+    assert f(FAKE, 65, 2, 32, FAKE, None, None) == MISALIGNED
+    assert f(FAKE, 66, 2, 32, FAKE, None, None) == MISALIGNED
     assert f(FAKE, 64, 1, 32, FAKE + 4, None, None) == MISALIGNED
     assert f(FAKE, 64, 1, 32, FAKE, FAKE + 4, None) == MISALIGNED
 
@@ -175,6 +181,41 @@ def test_block_dots_validation(L):
     assert f(0, None, 4, 32, FAKE, 1, FAKE, None) == INVALID
     assert f(0, FAKE, 4, 32, FAKE, 17, FAKE, None) == UNSUPPORTED
     assert f(0, FAKE, 4, 32, FAKE, 1, FAKE + 1, None) == MISALIGNED
+
+
+def test_block_dots_mx_validation(L):
+    f = L.qmv_block_dots_mx
+    mx = [i for i, n in enumerate(q.variants()) if n.startswith("mx_")]
+    vec = [i for i, n in enumerate(q.variants()) if not n.startswith("mx_")]
+    assert f(1, None, 4, 256, FAKE, 1, -1, 0, FAKE, None) == INVALID
+    assert f(1, FAKE, 4, 256, FAKE, 1, vec[0], 0, FAKE, None) == INVALID  # not a matrix-core variant
+    assert f(1, FAKE, 4, 256, FAKE, 1, len(q.variants()), 0, FAKE, None) == INVALID
+    assert f(1, FAKE, 4, 256, FAKE, 1, mx[0], 1, FAKE, None) == INVALID   # one slice is no split
+    assert f(1, FAKE, 4, 256, FAKE, 1, mx[0], 33, FAKE, None) == INVALID
+    assert f(3, FAKE, 4, 256, FAKE, 1, -1, 0, FAKE, None) == UNSUPPORTED  # q5_K: no matrix-core decode
+    assert f(4, FAKE, 4, 256, FAKE, 1, -1, 0, FAKE, None) == UNSUPPORTED  # nor q6_K
+    assert f(1, FAKE, 4, 256, FAKE, 17, -1, 0, FAKE, None) == UNSUPPORTED
+    assert f(1, FAKE, 4, 256, FAKE, 1, -1, 32, FAKE, None) == UNSUPPORTED  # 32 slices of one super-block
+    assert f(1, FAKE, 4, 256, FAKE + 16, 1, -1, 0, FAKE, None) == MISALIGNED
+    assert f(1, FAKE, 4, 256, FAKE, 1, -1, 0, FAKE + 2, None) == MISALIGNED
+
+
+def test_moe_block_dots_validation(L):
+    f = L.qmv_moe_block_dots
+    ws = q.moe_workspace_bytes(2, 8, 16, 256, 4, 2)
+
+    def call(fmt=2, w=FAKE, e=8, n=16, k=256, xq=FAKE, ps=0, ids=FAKE, t=4, top_k=2, sr=0, out=FAKE,
+             wsp=FAKE, wsb=ws):
+        return f(fmt, w, e, n, k, xq, ps, ids, t, top_k, sr, out, wsp, wsb, None)
+
+    assert call(out=None) == INVALID
+    assert call(wsp=None) == INVALID
+    assert call(sr=5) == INVALID
+    assert call(ps=2) == INVALID
+    assert call(t=65) == UNSUPPORTED
+    assert call(fmt=3) == UNSUPPORTED
+    assert call(out=FAKE + 2) == MISALIGNED
+    assert call(wsb=ws - 1) == WORKSPACE
 
 
 def test_matvec_plan():

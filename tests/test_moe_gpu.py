@@ -181,3 +181,39 @@ def test_moe_other_formats(fmt, moe_kernel):
         yr, mag = oracle.moe_matvec(fmt, w, e_n, n, k, qs, d, s, ids, rw if weighted else None,
                                     per_slot)
         assert_y(y.cpu().numpy().reshape(yr.shape), yr, mag, f"fmt {fmt} per_slot={per_slot}")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS], ids=["q8_0", "q4_K", "iq4_xs"])
+@pytest.mark.parametrize("kernel", [0, 3], ids=["auto", "flat"])
+def test_moe_one_token_weighted(fmt, kernel):
+    """One token with route weights: the flat kernel with the combine folded
+    in (top_k <= 8, rows of up to two units per lane), on every MoE format,
+    for rows of one and two units per lane (K = 512, 1536, 4096), one
+    activation row per token and per slot, top_k 1 and 8, with a dropped id
+    and a duplicate."""
+    qmv = need_gpu()
+    e_n, n = 9, 72
+    qmv.set_tuning("moe_kernel", kernel)
+    try:
+        for k in (512, 1536, 4096):
+            w = synth.make_weights(fmt, e_n * n, k, f"moe1/{fmt}/{k}").data
+            wd = to_dev(w)
+            for ids in (np.array([[4]], np.int32), np.array([[7]], np.int32),
+                        np.array([[2, 8, 0, 5, 1, 6, 3, 4]], np.int32),
+                        np.array([[2, -1, 0, 5, 5, 6, 1000, 4]], np.int32)):
+                top_k = ids.shape[1]
+                rw = synth.normal_f32(synth.stream(f"moe1/rw/{top_k}"), 0, top_k).reshape(1, top_k)
+                for per_slot in (False, True):
+                    say(f"MoE one token {fmt} K={k} ids={ids.tolist()} per_slot={per_slot} kernel={kernel}")
+                    x = x_host(top_k if per_slot else 1, k, f"moe1/x/{k}/{per_slot}")
+                    xq = quantize(qmv, x)
+                    ws = torch.zeros(qmv.moe_workspace_bytes(fmt, e_n, n, k, 1, top_k), dtype=torch.uint8,
+                                     device="cuda")
+                    y = qmv.moe_matvec(fmt, wd, e_n, n, k, xq, per_slot, to_dev(ids), to_dev(rw), ws)
+                    qs, d, s = oracle.quantize_act(x)
+                    yr, mag = oracle.moe_matvec(fmt, w, e_n, n, k, qs, d, s, ids, rw, per_slot)
+                    assert_y(y.cpu().numpy().reshape(yr.shape), yr, mag, f"{fmt} K={k} top_k={top_k}")
+                    dropped = int(((ids < 0) | (ids >= e_n)).sum())
+                    assert int(ws[:4].view(torch.int32)[0]) == dropped
+    finally:
+        qmv.set_tuning("moe_kernel", 0)
