@@ -504,6 +504,29 @@ def trace_summary(path: str) -> int:
     return 0
 
 
+def counter_summary(path: str) -> int:
+    """Per-kernel mean per dispatch of every counter in a rocprofv3 --pmc
+    counter_collection.csv (one row per dispatch and counter)."""
+    import csv
+
+    vals, names = {}, []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            k = row.get("Kernel_Name", "?")
+            c = row.get("Counter_Name", "?")
+            vals.setdefault(k, {}).setdefault(c, []).append(float(row["Counter_Value"]))
+            if c not in names:
+                names.append(c)
+    for k, cs in vals.items():
+        n = max(len(v) for v in cs.values())
+        print(f"{k[:150]}  ({n} dispatches)")
+        for c in names:
+            if c in cs:
+                v = cs[c]
+                print(f"    {c:40s} mean {sum(v) / len(v):16.1f}  median {median(v):16.1f}")
+    return 0
+
+
 # The metric's token sweep (q4_K and IQ4_XS at 1..16 tokens) and the other
 # workload configurations, reported beside the headline by the default run.
 SWEEP = (("q4_k_14336x4096", (1, 2, 4, 8, 16)), ("iq4_xs_4096x14336", (1, 2, 4, 8, 16)))
@@ -577,10 +600,22 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-kernel median/avg/min/max of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="print per-kernel mean counter values of a rocprofv3 --pmc counter_collection.csv and exit")
+    ap.add_argument("--profile-launches", type=int, default=0, metavar="N",
+                    help="for a profiler: run N plain launches of the workload's matvec alone (cycling the "
+                         "weight ring, after N warmup launches) and exit")
+    ap.add_argument("--profile-read", action="store_true",
+                    help="with --profile-launches: launch the plain read of the weight bytes (qmv_stream_read) "
+                         "instead of the matvec")
+    ap.add_argument("--variant", default=None,
+                    help="force a matvec kernel variant by name (qmv_set_tuning 'variant')")
     args = ap.parse_args()
 
-    if args.trace_summary:
+    if args.trace_summary is not None:
         return trace_summary(args.trace_summary)
+    if args.counter_summary is not None:
+        return counter_summary(args.counter_summary)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (the matvec is "
               "measured on one GPU's share of the weights; multi-GPU sharding is not built)",
@@ -610,8 +645,27 @@ def main() -> int:
         print("--tokens must be 1..16", file=sys.stderr)
         return 2
 
+    if args.variant is not None:
+        if args.variant not in qmv.variants():
+            print(f"unknown variant {args.variant}", file=sys.stderr)
+            return 2
+        qmv.set_tuning("variant", qmv.variants().index(args.variant))
     log(f"bench: {args.workload} T={t}: generating inputs")
     ring = Ring(torch, qmv, fmt, n, k, t, args.workload, mats)
+    if args.profile_launches > 0:
+        # plain launches (no graph) so that a profiler sees each dispatch
+        qmv.quantize_act(ring.x[0], out=ring.xq)
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for i in range(2 * args.profile_launches):
+            if args.profile_read:
+                for w in ring.w[i % ring.copies]:
+                    qmv.stream_read(w.view(-1), sink)
+            else:
+                ring.matvec_only(qmv, i)
+        torch.cuda.synchronize()
+        log(f"bench: {args.profile_launches} profiled launches after as many warmup launches, variant "
+            f"{qmv.variant_name(qmv.matvec_plan(fmt, n, k, t, ring.ws is not None)[0]) if mats == 1 else '-'}")
+        return 0
     per = max(ring.copies, 64)
     g_full = capture(torch, lambda i: ring.step(qmv, i), per)
     tail = args.steps % per

@@ -25,7 +25,8 @@ SOURCES = ([(s, os.path.splitext(s)[0], []) for s in
             ("qmv_api.hip", "qmv_variants.hip", "qmv_quant.hip", "qmv_moe.hip", "qmv_router.hip",
              "qmv_measure.hip")]
            + [("qmv_matvec.hip", f"qmv_matvec_{n}", [f"-DQMV_MATVEC_FMT={f}"]) for f, n in FORMATS.items()]
-           + [("qmv_mfma.hip", f"qmv_mfma_{FORMATS[f]}", [f"-DQMV_MX_FMT={f}"]) for f in MX_FORMATS])
+           + [("qmv_mfma.hip", f"qmv_mfma_{FORMATS[f]}", [f"-DQMV_MX_FMT={f}"]) for f in MX_FORMATS]
+           + [("qmv_mxf.hip", f"qmv_mxf_{FORMATS[f]}", [f"-DQMV_MX_FMT={f}"]) for f in MX_FORMATS])
 ARCH = os.environ.get("QMV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "qmv_internal.h"
+#include "qmv_mfma.h"
 #include "qmv.h"
 
 #define QMV_API extern "C" __attribute__((visibility("default")))
@@ -204,6 +205,13 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
            : nu <= 3 ? "fl_w16_r1_u3_l"
            : nu <= 7 ? "fl_w8_r1_u7_l"
                      : "fl_w4_r1_u4_g";
+  } else if (type == QMV_Q4_K && n_tok <= 8 && n_rows >= 8 * (int64_t)cus &&
+             units * mx_per_unit(FQ4_K, 8) <= 140 * 1024) {
+    // q4_K at 3..8 tokens on many rows: the flat matrix-core kernel, one
+    // pass with every weight load of a wave issued at once (14336 x 4096:
+    // 12.0 / 12.1 / 12.2 us at 3 / 4 / 8 tokens against 12.4 (multi-token
+    // vector kernel) / 12.4 / 14.2 us (persistent matrix-core kernel))
+    name = "mf_w8_b4";
   } else if (type == QMV_Q4_K && n_tok == 3 && nu <= 2) {
     name = "fl_w4_r1_u2_l";  // measured 11.25 against 11.59 us for the multi-token kernel
   } else if (type == QMV_Q5_K || type == QMV_Q6_K) {
@@ -241,7 +249,7 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
 
 int choose_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t forced = g_variant.load();
-  if (forced >= 0 && forced < kNumVariants && kVariants[forced].kind == 4 && !has_mfma(type))
+  if (forced >= 0 && forced < kNumVariants && kVariants[forced].kind >= 4 && !has_mfma(type))
     return auto_variant(type, n_rows, k, n_tok);  // no matrix-core decode of this format
   if (forced >= 0 && forced < kNumVariants) {
     // a forced streaming variant whose staging does not fit runs the
@@ -340,6 +348,14 @@ Plan make_plan(int type, int64_t n_rows, int64_t k, int64_t n_tok, bool use_ws) 
     const int s = mx_split_plan(type, (int)n_tok, kVariants[p.variant].wpb, kVariants[p.variant].ks, (int)(k / 32),
                                 (int)n_rows, dv.cus, dv.lds_per_cu, mx_slices(), &ups);
     p.slices = s >= 2 ? s : 1;
+  } else if (kVariants[p.variant].kind == 5) {
+    // the flat matrix-core kernel's own plan (launch_matvec repeats it)
+    const DeviceInfo dv = device_info();
+    MxfPlan mp{};
+    const int s = mxf_plan(type, (int)n_tok, kVariants[p.variant].wpb, kVariants[p.variant].nu, (int)(k / 32),
+                           (int)n_rows, dv.cus, dv.lds_per_cu, mx_slices() != 0, mx_slices() >= 2 ? mx_slices() : 0,
+                           &mp);
+    p.slices = s >= 1 ? s : 1;
   } else if (kVariants[p.variant].kind == 2 && kVariants[p.variant].xl && flat_split_enabled()) {
     p.slices = flat_split(kVariants[p.variant], n_rows, k / 32, n_tok, &p.ups);
   }
@@ -736,7 +752,7 @@ QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_row
   qmv_status st = check_weights(type, w, n_rows, k);
   if (st != QMV_OK) return st;
   if (xq == nullptr || out == nullptr || n_tok < 1 || slices < -1 || slices == 1 || slices > kMaxSlices ||
-      variant < -1 || variant >= kNumVariants || (variant >= 0 && kVariants[variant].kind != 4))
+      variant < -1 || variant >= kNumVariants || (variant >= 0 && kVariants[variant].kind < 4))
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_TOKENS || !has_mfma(type)) return QMV_ERR_UNSUPPORTED;
   if (n_tok * n_rows * (k / 32) > INT32_MAX) return QMV_ERR_UNSUPPORTED;
@@ -748,10 +764,17 @@ QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_row
     // and the 8-wave one beyond
     const bool use_ws = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok) > 0;
     const Plan p = make_plan(type, n_rows, k, n_tok, use_ws);
-    v = kVariants[p.variant].kind == 4 ? p.variant : find_variant(n_tok <= 8 ? "mx_w16_k4_r2" : "mx_w8_k1_r4");
+    v = kVariants[p.variant].kind >= 4 ? p.variant : find_variant(n_tok <= 8 ? "mx_w16_k4_r2" : "mx_w8_k1_r4");
   }
   const DeviceInfo dv = device_info();
-  if (slices >= 2) {
+  MxfPlan mp{};
+  if (kVariants[v].kind == 5) {
+    // the flat matrix-core kernel: its plan with that many slices (-1 the
+    // automatic one, 0 unsplit)
+    if (mxf_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].nu, (int)(k / 32), (int)n_rows, dv.cus,
+                 dv.lds_per_cu, slices != 0, slices >= 2 ? slices : 0, &mp) < 1)
+      return QMV_ERR_UNSUPPORTED;
+  } else if (slices >= 2) {
     int ups = 0;
     if (mx_split_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].ks, (int)(k / 32), (int)n_rows, dv.cus,
                       dv.lds_per_cu, slices, &ups) < 2)
@@ -777,7 +800,8 @@ QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_row
   a.slices = 1;
   a.dots = out;
   a.dots_slices = slices;
-  hipError_t e = launch_mx(a, static_cast<hipStream_t>(stream));
+  hipError_t e = kVariants[v].kind == 5 ? launch_mxf(a, mp, static_cast<hipStream_t>(stream))
+                                        : launch_mx(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
 }
 

@@ -32,7 +32,11 @@ struct ActView {
 //           by chunk;
 //   kind 4: matrix-core kernel (k_mx) -- a wave owns 16 rows, wpb waves per
 //           workgroup in teams of ks waves that split K, int8 MFMA per
-//           32-block, activations staged in LDS chunk by chunk.
+//           32-block, activations staged in LDS chunk by chunk;
+//   kind 5: flat matrix-core kernel (k_mxf) -- the same tile in one pass
+//           over the rows: wpb waves per workgroup, each holding `nu`
+//           super-blocks of one row tile's K slice, all loaded at once
+//           (waves per tile and K slices planned per launch).
 struct Variant {
   int kind;
   int lpr;
@@ -99,6 +103,8 @@ struct StreamArgs {
   int ups;
   float* part;
   int* cnt;
+  // k_mxf: waves per row tile
+  int mx_ks;
   // integer mode of k_mx (the block-dot test hook): the exact integer of
   // every (token, row, 32-block) goes to dots, int32 [n_tok][n_rows][units][c]
   // (c = 2 for q4_K: sc * sum q qx, m * s; else 1), and no output is stored
@@ -214,6 +220,23 @@ hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st);
 template <int F>
 hipError_t launch_vector(const MatvecLaunch& a, hipStream_t st);
 hipError_t launch_mx(const MatvecLaunch& a, hipStream_t st);
+
+// Launch plan of the flat matrix-core kernel k_mxf: K slices over workgroups
+// (1: none) of ups units each, ks waves per row tile, rt row tiles per
+// workgroup, the grid's x size and the dynamic LDS bytes.
+struct MxfPlan {
+  int slices, ups, ks, rt, grid_x;
+  size_t lds;
+};
+// The plan for a variant of wpb waves holding sbw super-blocks each: the
+// fewest K slices whose activations fit one workgroup's LDS (several only if
+// can_split; forced_slices > 0 demands that count).  Returns the slice count,
+// 0 if no plan fits.
+int mxf_plan(int fmt, int n_tok, int wpb, int sbw, int units, int n_rows, int cus, int64_t lds_per_cu,
+             bool can_split, int forced_slices, MxfPlan* p);
+hipError_t launch_mxf(const MatvecLaunch& a, const MxfPlan& p, hipStream_t st);
+template <int F>
+hipError_t launch_mxf_fmt(const MatvecLaunch& a, const MxfPlan& p, hipStream_t st);
 // The matrix-core kernels of format F (one translation unit per format).
 template <int F>
 hipError_t launch_mx_fmt(const MatvecLaunch& a, hipStream_t st);

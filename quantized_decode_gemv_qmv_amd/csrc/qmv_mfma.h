@@ -144,6 +144,11 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FQ8G128>& r, int p, int s,
   o.im[0] = o.im[1] = 0;
 }
 
+// LDS bytes per staged unit (32-block) of the matrix-core kernels'
+// block-major activation copy for tmp token rows: 32 quant bytes per token
+// plus a 16-byte skew, and the fp32 scales d (and for q4_K d * s) per token.
+inline int mx_per_unit(int fmt, int tmp) { return (tmp * 32 + 16) + tmp * 4 * (fmt == FQ4_K ? 2 : 1); }
+
 __device__ __forceinline__ i32x4 mfma64(const u32x4& a, const u32x4& b, i32x4 c) {
   const i32x4 av = __builtin_bit_cast(i32x4, a);
   const i32x4 bv = __builtin_bit_cast(i32x4, b);

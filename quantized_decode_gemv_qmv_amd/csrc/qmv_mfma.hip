@@ -169,13 +169,16 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
         if (idx < total) put(idx, v[i]);
       }
     }
+    // scales: entry (t, b) read in token-major order (consecutive lanes on
+    // consecutive blocks of one token: coalesced), stored block-major
+    const FastDiv dk(kc);
     for (int base = 0; base < kc * TMP; base += 4 * NT) {
       float dv[4];
       int iv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = base + (int)threadIdx.x + i * NT;
-        const int b = idx / TMP, t = idx - b * TMP;  // TMP is a power of two
+        const int t = dk.div(idx), b = idx - t * kc;
         const int gi = min(t, T - 1) * a.nb + ub + c0 + min(b, cu - 1);
         dv[i] = gd[gi];
         iv[i] = gs[gi];
@@ -183,10 +186,11 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = base + (int)threadIdx.x + i * NT;
-        const bool ok = idx / TMP < cu;
+        const int t = dk.div(idx), b = idx - t * kc;
+        const bool ok = b < cu;
         if (idx < kc * TMP) {
-          dl[idx] = ok ? dv[i] : 0.f;
-          if constexpr (Q4K) sl[idx] = ok ? dv[i] * static_cast<float>(iv[i]) : 0.f;
+          dl[b * TMP + t] = ok ? dv[i] : 0.f;
+          if constexpr (Q4K) sl[b * TMP + t] = ok ? dv[i] * static_cast<float>(iv[i]) : 0.f;
         }
       }
     }
@@ -475,8 +479,7 @@ static int mx_chunk_units(int units, int per_unit, int step, int64_t budget) {
 // its row tiles), else chunks.
 constexpr int64_t kMxLdsBudget = 144 * 1024;
 
-// LDS bytes per staged unit and fixed LDS bytes of a k_mx workgroup.
-static int mx_per_unit(int fmt, int tmp) { return (tmp * 32 + 16) + tmp * 4 * (fmt == FQ4_K ? 2 : 1); }
+// Fixed LDS bytes of a k_mx workgroup (mx_per_unit: qmv_mfma.h).
 static int64_t mx_fixed(int wpb, int ks, int tmp) { return 16 + (ks > 1 ? (int64_t)wpb * tmp * 16 * 4 : 0); }
 
 #if QMV_MX_FMT == 0  // host helpers: defined once, in the Q8_0 unit

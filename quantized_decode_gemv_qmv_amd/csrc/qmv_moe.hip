@@ -341,13 +341,17 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
             if (idx < TMP * pr) *reinterpret_cast<u32x4a*>(xl + (pc >> 1) * BS + j * 32 + 16 * (pc & 1)) = v[q];
           }
         }
+        // scales: entry (slot row j, block b) read row-major (consecutive
+        // lanes on consecutive blocks of one row: coalesced), stored
+        // block-major
+        const FastDiv dkb(kb);
         for (int base = 0; base < kb * TMP; base += 4 * NT) {
           float dv[4];
           int iv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int idx = base + tid + q * NT;
-            const int b = idx / TMP, j = idx - b * TMP;  // TMP is a power of two
+            const int j = dkb.div(idx), b = idx - j * kb;
             const int xr = x_row(s_slot[b0 + g0 + min(j, ng - 1)]);
             const int64_t gi = (int64_t)xr * nb + min(b, nb - 1);
             dv[q] = a.x.d[gi];
@@ -356,11 +360,11 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int idx = base + tid + q * NT;
-            const int b = idx / TMP, j = idx - b * TMP;
+            const int j = dkb.div(idx), b = idx - j * kb;
             const bool ok = j < ng && b < nb;
             if (idx < kb * TMP) {
-              dl[idx] = ok ? dv[q] : 0.f;
-              if constexpr (Q4K) sl[idx] = ok ? dv[q] * static_cast<float>(iv[q]) : 0.f;
+              dl[b * TMP + j] = ok ? dv[q] : 0.f;
+              if constexpr (Q4K) sl[b * TMP + j] = ok ? dv[q] * static_cast<float>(iv[q]) : 0.f;
             }
           }
         }

@@ -31,6 +31,8 @@ const Variant kVariants[] = {
     {4, 16, 1, 2, 16, 4, 1, "mx_w16_k4_r2"},  {4, 16, 1, 2, 16, 8, 1, "mx_w16_k8_r2"},
     {4, 16, 1, 2, 16, 16, 1, "mx_w16_k16_r2"}, {4, 16, 1, 4, 8, 1, 1, "mx_w8_k1_r4"},
     {4, 16, 1, 4, 8, 4, 1, "mx_w8_k4_r4"},    {4, 16, 1, 4, 8, 8, 1, "mx_w8_k8_r4"},
+    {5, 16, 1, 4, 16, 0, 1, "mf_w16_b4"},     {5, 16, 1, 2, 16, 0, 1, "mf_w16_b2"},
+    {5, 16, 1, 4, 8, 0, 1, "mf_w8_b4"},       {5, 16, 1, 8, 8, 0, 1, "mf_w8_b8"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -48,8 +50,29 @@ size_t stream_lds_bytes(const Variant& v, int64_t act_bytes, int tm) {
   return static_cast<size_t>(act_bytes + (int64_t)v.ks * v.rows * tm * 4);
 }
 
+static int variant_index(const char* name) {
+  for (int i = 0; i < kNumVariants; ++i)
+    if (__builtin_strcmp(kVariants[i].name, name) == 0) return i;
+  return 0;
+}
+
 hipError_t launch_matvec(const MatvecLaunch& a, hipStream_t st) {
-  if (kVariants[a.variant].kind == 4) return launch_mx(a, st);
+  const Variant& v = kVariants[a.variant];
+  if (v.kind == 5) {
+    // the flat matrix-core kernel, split over workgroups only with a
+    // workspace; without a plan that fits (or for a batched launch) the
+    // persistent matrix-core kernel of the same workgroup size
+    MxfPlan p{};
+    const bool can_split = a.part != nullptr && a.cnt != nullptr && mx_slices() != 0;
+    if (a.seg.n == 0 &&
+        mxf_plan(a.fmt, a.n_tok, v.wpb, v.nu, a.units, a.n_rows, a.cus, a.lds_per_cu, can_split,
+                 mx_slices() >= 2 ? mx_slices() : 0, &p) > 0)
+      return launch_mxf(a, p, st);
+    MatvecLaunch b = a;
+    b.variant = variant_index(v.wpb == 16 ? "mx_w16_k4_r2" : "mx_w8_k4_r4");
+    return launch_mx(b, st);
+  }
+  if (v.kind == 4) return launch_mx(a, st);
   switch (a.fmt) {
     case FQ8_0: return launch_vector<FQ8_0>(a, st);
     case FQ4_K: return launch_vector<FQ4_K>(a, st);

@@ -75,7 +75,7 @@ def test_chunked_variants_long_k(fmt):
     wd = to_dev(w)
     x = x_host(16, k, f"lkx/{fmt}")
     chunked = [v for v in range(len(qmv.variants()))
-               if qmv.variant_name(v).startswith(("mt_", "mx_"))]
+               if qmv.variant_name(v).startswith(("mt_", "mx_", "mf_"))]
     assert chunked
     try:
         for v in chunked:
