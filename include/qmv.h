@@ -310,6 +310,30 @@ qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts, int64
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qmv_moe_matvec_noalloc -- qmv_moe_matvec for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc): the same validation, kernels and results, with
+ * the workspace taken from a device-resident array inside the library
+ * instead of a caller buffer.  It allocates nothing and calls no allocating
+ * routine.
+ *   - The array holds QMV_MOE_NOALLOC_WS_BYTES bytes; a call whose
+ *     qmv_moe_workspace_bytes(...) exceeds that returns QMV_ERR_WORKSPACE
+ *     (e.g. 128 experts, top-8, 4096 rows: fits up to 64 tokens).
+ *   - Each GPU the library runs on holds its own copy until the process
+ *     ends; its address is looked up on the first call on that GPU.
+ *   - Every call on a GPU shares that GPU's copy and leaves it holding the
+ *     call's per-slot outputs: calls that overlap in time on one GPU (on
+ *     different streams) race and must not be issued.
+ *   - The dropped-slot count is not reported (it stays in the array).
+ * All other arguments as for qmv_moe_matvec.
+ */
+#define QMV_MOE_NOALLOC_WS_BYTES ((size_t)17 << 20)
+qmv_status qmv_moe_matvec_noalloc(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows,
+                                  int64_t k, const void* xq, int x_per_slot, const int32_t* ids,
+                                  const float* route_w, int64_t n_tok, int64_t top_k, float* y,
+                                  void* stream);
+
+/*
  * qmv_block_dots -- test hook: the exact integer partial of every 32-weight
  * block, computed by the same device decode and dot routines as qmv_matvec.
  * out : int32 [n_tok][n_rows][k/32][c] (device), c = 2 for q4_K and q5_K

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "Q8G128", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
-    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "block_dots",
+    "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "moe_matvec_noalloc",
+    "block_dots",
     "block_dots_mx", "moe_block_dots", "stream_read",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "matvec_plan", "MAX_TOKENS", "MAX_MOE_TOKENS",
 ]
@@ -88,6 +89,7 @@ def lib():
         "qmv_matvec_x": ([I, P, I64, I64, P, I64, I64, P, I64, P, P, SZ, P], I),
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
+        "qmv_moe_matvec_noalloc": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
         "qmv_block_dots_mx": ([I, P, I64, I64, P, I64, I64, I, P, P], I),
         "qmv_moe_block_dots": ([I, P, I64, I64, I64, P, I, P, I64, I64, I64, P, P, SZ, P], I),
@@ -333,6 +335,30 @@ def moe_matvec(fmt: int, w: torch.Tensor, n_experts: int, n_rows: int, k: int,
     _check(lib().qmv_moe_matvec(fmt, _ptr(w), n_experts, n_rows, k, _ptr(xq), int(bool(x_per_slot)),
                                 _ptr(ids), _ptr(route_w), n_tok, top_k, _ptr(y), _ptr(ws),
                                 ws.numel(), _stream(stream)), "qmv_moe_matvec")
+    return y
+
+
+def moe_matvec_noalloc(fmt: int, w: torch.Tensor, n_experts: int, n_rows: int, k: int,
+                       xq: torch.Tensor, x_per_slot: bool, ids: torch.Tensor,
+                       route_w: torch.Tensor | None, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """moe_matvec on the library's device-resident workspace (no caller
+    workspace; y must be given, so that nothing is allocated)."""
+    _need(w, torch.uint8, "w")
+    _need(xq, torch.uint8, "xq")
+    _need(ids, torch.int32, "ids")
+    _need(y, torch.float32, "y")
+    n_tok, top_k = ids.shape
+    if route_w is not None:
+        _need(route_w, torch.float32, "route_w")
+        if tuple(route_w.shape) != (n_tok, top_k):
+            raise ValueError("route_w must match ids")
+    if y.numel() < n_tok * n_rows * (1 if route_w is not None else top_k):
+        raise ValueError("y too small")
+    if w.numel() < n_experts * n_rows * row_bytes(fmt, k):
+        raise ValueError("w holds fewer than n_experts * n_rows rows")
+    _check(lib().qmv_moe_matvec_noalloc(fmt, _ptr(w), n_experts, n_rows, k, _ptr(xq), int(bool(x_per_slot)),
+                                        _ptr(ids), _ptr(route_w), n_tok, top_k, _ptr(y), _stream(stream)),
+           "qmv_moe_matvec_noalloc")
     return y
 
 

@@ -824,25 +824,28 @@ QMV_API size_t qmv_moe_workspace_bytes(qmv_type type, int64_t n_experts, int64_t
   return static_cast<size_t>(kMoePartOffset + align256(n_tok * top_k * n_rows * 4));
 }
 
-QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts,
-                                  int64_t n_rows, int64_t k, const void* xq, int x_per_slot,
-                                  const int32_t* ids, const float* route_w, int64_t n_tok,
-                                  int64_t top_k, float* y, void* ws, size_t ws_bytes,
-                                  void* stream) {
+// Validation of a qmv_moe_matvec call, the workspace aside.
+static qmv_status moe_check(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows, int64_t k,
+                            const void* xq, int x_per_slot, const int32_t* ids, const float* route_w,
+                            int64_t n_tok, int64_t top_k, float* y) {
   qmv_status st = check_weights(type, w, n_rows, k);
   if (st != QMV_OK) return st;
-  if (xq == nullptr || ids == nullptr || y == nullptr || ws == nullptr || n_tok < 1 ||
-      top_k < 1 || n_experts < 1 || (x_per_slot != 0 && x_per_slot != 1))
+  if (xq == nullptr || ids == nullptr || y == nullptr || n_tok < 1 || top_k < 1 || n_experts < 1 ||
+      (x_per_slot != 0 && x_per_slot != 1))
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_MOE_TOKENS || top_k > QMV_MAX_TOP_K || n_experts > QMV_MAX_EXPERTS ||
       k / 32 > kMoeMaxUnits || n_rows > kMoeMaxRows || !moe_format(type))
     return QMV_ERR_UNSUPPORTED;
   if (n_experts * n_rows > INT32_MAX) return QMV_ERR_UNSUPPORTED;
-  if (!aligned(xq, 256) || !aligned(ids, 4) || !aligned(y, 4) ||
-      (route_w != nullptr && !aligned(route_w, 4)) || !aligned(ws, 256))
+  if (!aligned(xq, 256) || !aligned(ids, 4) || !aligned(y, 4) || (route_w != nullptr && !aligned(route_w, 4)))
     return QMV_ERR_MISALIGNED;
-  const size_t need = qmv_moe_workspace_bytes(type, n_experts, n_rows, k, n_tok, top_k);
-  if (ws_bytes < need) return QMV_ERR_WORKSPACE;
+  return QMV_OK;
+}
+
+// The launch of a validated qmv_moe_matvec call on workspace ws.
+static qmv_status moe_run(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows, int64_t k,
+                          const void* xq, int x_per_slot, const int32_t* ids, const float* route_w, int64_t n_tok,
+                          int64_t top_k, float* y, void* ws, void* stream) {
   const int64_t x_rows = x_per_slot ? n_tok * top_k : n_tok;
   MoeLaunch a{};
   a.fmt = type;
@@ -867,6 +870,61 @@ QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_expert
   a.part = reinterpret_cast<float*>(b + kMoePartOffset);
   hipError_t e = launch_moe(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+}
+
+QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts,
+                                  int64_t n_rows, int64_t k, const void* xq, int x_per_slot,
+                                  const int32_t* ids, const float* route_w, int64_t n_tok,
+                                  int64_t top_k, float* y, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  qmv_status st = moe_check(type, w, n_experts, n_rows, k, xq, x_per_slot, ids, route_w, n_tok, top_k, y);
+  if (st != QMV_OK) return st;
+  if (ws == nullptr) return QMV_ERR_INVALID_ARG;
+  if (!aligned(ws, 256)) return QMV_ERR_MISALIGNED;
+  if (ws_bytes < qmv_moe_workspace_bytes(type, n_experts, n_rows, k, n_tok, top_k)) return QMV_ERR_WORKSPACE;
+  return moe_run(type, w, n_experts, n_rows, k, xq, x_per_slot, ids, route_w, n_tok, top_k, y, ws, stream);
+}
+
+// ------------------------------------------------------ no-allocation MoE
+// The workspace of qmv_moe_matvec_noalloc: a device array of this library,
+// one copy per GPU, alive until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host it only names the symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device.
+// Nothing in it has to start at zero: every call writes the dropped-slot
+// word and the per-slot outputs it reads back.
+static __device__ __align__(256) uint8_t scratch[QMV_MOE_NOALLOC_WS_BYTES];
+
+static void* scratch_address(qmv_status* st) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *st = QMV_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      *st = QMV_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+QMV_API qmv_status qmv_moe_matvec_noalloc(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows,
+                                          int64_t k, const void* xq, int x_per_slot, const int32_t* ids,
+                                          const float* route_w, int64_t n_tok, int64_t top_k, float* y,
+                                          void* stream) {
+  qmv_status st = moe_check(type, w, n_experts, n_rows, k, xq, x_per_slot, ids, route_w, n_tok, top_k, y);
+  if (st != QMV_OK) return st;
+  if (qmv_moe_workspace_bytes(type, n_experts, n_rows, k, n_tok, top_k) > QMV_MOE_NOALLOC_WS_BYTES)
+    return QMV_ERR_WORKSPACE;
+  void* ws = scratch_address(&st);
+  if (ws == nullptr) return st;
+  return moe_run(type, w, n_experts, n_rows, k, xq, x_per_slot, ids, route_w, n_tok, top_k, y, ws, stream);
 }
 
 QMV_API qmv_status qmv_moe_block_dots(qmv_type type, const void* w, int64_t n_experts, int64_t n_rows, int64_t k,

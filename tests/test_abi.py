@@ -366,3 +366,22 @@ def test_matvec_batch_validation(L):
     assert call([it(y=FAKE, res=FAKE + 4096, ldr=4), it(y=FAKE + 4096)]) == INVALID  # another item's output
     assert call([it(y=FAKE, res=FAKE, ldr=8, ldy=4)]) == INVALID  # in place needs the same stride
 
+
+
+def test_moe_noalloc_validation(L):
+    """The no-allocation MoE entry point validates as qmv_moe_matvec does and
+    rejects calls whose workspace would exceed its device-resident array."""
+    f = L.qmv_moe_matvec_noalloc
+
+    def call(fmt=2, w=FAKE, e=128, n=4096, k=1536, xq=FAKE, ps=1, ids=FAKE, rw=FAKE, t=64, top_k=8, y=FAKE):
+        return f(fmt, w, e, n, k, xq, ps, ids, rw, t, top_k, y, None)
+
+    assert call(w=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(ps=2) == INVALID
+    assert call(t=65) == UNSUPPORTED
+    assert call(fmt=3) == UNSUPPORTED
+    assert call(y=FAKE + 2) == MISALIGNED
+    # 64 tokens x top-16 x 8192 rows of per-slot outputs: 32 MiB > the 17 MiB array
+    assert q.moe_workspace_bytes(2, 128, 8192, 1536, 64, 16) > (17 << 20)
+    assert call(n=8192, top_k=16) == WORKSPACE
