@@ -349,6 +349,16 @@ def bench_moe(args, torch, qmv, ffn=False):
     t = args.tokens
     log(f"bench: MoE{' FFN' if ffn else ''} T={t}: generating inputs")
     ring = MoeRing(torch, qmv, t)
+    if args.profile_launches > 0:
+        # plain launches for a profiler: the routed gate+up and down matvecs
+        qmv.quantize_act(ring.x[0], out=ring.xq)
+        qmv.quantize_act(ring.h[0], out=ring.hq)
+        for i in range(2 * args.profile_launches):
+            ring.gate_up(qmv, i)
+            ring.down(qmv, i)
+        torch.cuda.synchronize()
+        log(f"bench: {args.profile_launches} profiled MoE steps after as many warmup steps")
+        return 0
     per = 64
     step = (lambda i: ring.ffn_step(qmv, i)) if ffn else (lambda i: ring.step(qmv, i))
     g_full = capture(torch, step, per)

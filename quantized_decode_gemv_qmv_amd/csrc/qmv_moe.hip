@@ -519,24 +519,43 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
 
 // Few-slot routed matvec (decode): with about one slot per routed expert
 // there is no weight reuse to group for, and k_moe's routing sort and
-// per-item staging only delay the weight stream.  k_moe_flat reads its
-// slot's expert id once and streams that expert's rows as the dense flat
-// kernel does: workgroup (x, y) takes rows x * WPB * R .. of slot y, each
-// lane issuing every weight load of its R rows (NU units per row) at once,
-// behind its activation fragments (cache-resident).  A duplicated expert is
-// read once per slot.  Outputs per slot, written as k_moe writes them (to y,
-// or to the workspace for the combine); a dropped slot's row is zero.
+// per-item staging only delay the weight stream.  k_moe_flat streams each
+// routed expert's rows as the dense flat kernel does: workgroup (x, y) takes
+// rows x * WPB * R .. of the expert of slot y, each lane issuing every weight
+// load of its R rows (NU units per row) at once, behind its activation
+// fragments (cache-resident).  Each expert is read once per call (the
+// grouping the pages ask for, Castagna Veloce page, "Kernels for the MI50"):
+// the workgroups of the first slot routed to an expert also serve every
+// later slot with the same expert, one slot after the other from the same
+// weight registers, and those later slots' workgroups exit at once.  A
+// wave finds them with one ballot per 64 ids.  Outputs per slot, written as
+// k_moe writes them (to y, or to the workspace for the combine); a dropped
+// slot's row is zero.
 template <int F, int NU, int R, int WPB>
 __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = blockIdx.y;
+  const int n_slots = a.n_tok * a.top_k;
   const int e = a.ids[slot];
   const bool valid = e >= 0 && e < a.n_experts;
   const int units = a.units;
   const int row0 = (blockIdx.x * WPB + wave) * R;
   const int xr = a.x_per_slot ? slot : slot / a.top_k;
   const Act gx{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
+  // slots i with the same expert in chunk c (64 ids per chunk), one flag
+  // per lane, the same mask in every lane and every wave
+  auto same_in = [&](int c) -> uint64_t {
+    const int i = c * 64 + lane;
+    const int id = i < n_slots ? a.ids[i] : -1;
+    return __ballot(valid && id == e);
+  };
+  // an earlier slot with the same expert makes this workgroup redundant
+  // (uniform over the workgroup): that slot's workgroups compute this one
+  for (int c = 0; c * 64 < slot; ++c) {
+    const uint64_t lo = slot - c * 64 >= 64 ? ~0ull : ((1ull << (slot - c * 64)) - 1);
+    if (same_in(c) & lo) return;
+  }
   XO xf[NU];
 #pragma unroll
   for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lane + 64 * q, units - 1), xf[q]);
@@ -551,35 +570,64 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
   __builtin_amdgcn_sched_barrier(0);
-  float acc[R];
+  float* out = a.rw == nullptr ? a.y : a.part;
+  // one slot: the rows' sums against activation fragments f, stored at slot s
+  auto apply = [&](const XO (&f)[NU], int s) {
+    float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
-  for (int q = 0; q < NU; ++q) {
-    const int uraw = lane + 64 * q;
-    const bool ok = uraw < units;
-    const int u = ok ? uraw : units - 1;
+    for (int q = 0; q < NU; ++q) {
+      const int uraw = lane + 64 * q;
+      const bool ok = uraw < units;
+      const int u = ok ? uraw : units - 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        DecO<F> dec;
+        decode_own(cur[r][q], u, lane & 1, ok, dec);
+        const int dv = own_pass<F>(own_first(dec, f[q].f));
+        acc[r] = own_apply(dec, own_second(dec, f[q].s, dv), f[q].p, acc[r]);
+      }
+    }
+    float outv = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      DecO<F> dec;
-      decode_own(cur[r][q], u, lane & 1, ok, dec);
-      const int dv = own_pass<F>(own_first(dec, xf[q].f));
-      acc[r] = own_apply(dec, own_second(dec, xf[q].s, dv), xf[q].p, acc[r]);
+      const float sv = wave_sum(acc[r]);
+      outv = lane == r ? sv : outv;
     }
-  }
-  float outv = 0.f;
+    if (lane < R && row0 + lane < a.n_rows) out[(int64_t)s * a.n_rows + row0 + lane] = valid ? outv : 0.f;
+  };
+  apply(xf, slot);
+  if (valid) {
+    // the later slots with the same expert, in slot order
+    for (int c = slot / 64; c * 64 < n_slots; ++c) {
+      const int sh = slot - c * 64;  // 0..63 in the slot's own chunk, < 0 after it
+      uint64_t m = same_in(c) & (sh < 0 ? ~0ull : ~((2ull << sh) - 1));
+      while (m != 0) {  // uniform: the ballot is the same in every lane
+        const int s2 = c * 64 + __builtin_ctzll(m);
+        m &= m - 1;
+        // decode the raw weights again for this slot rather than keep every
+        // decoded unit alive across the slots (that doubled the registers of
+        // the first slot's pass and halved the waves in flight)
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float sv = wave_sum(acc[r]);
-    outv = lane == r ? sv : outv;
-  }
-  if (lane < R && row0 + lane < a.n_rows) {
-    float* out = a.rw == nullptr ? a.y : a.part;
-    out[(int64_t)slot * a.n_rows + row0 + lane] = valid ? outv : 0.f;
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int q = 0; q < NU; ++q) {
+            uint32_t* rw = reinterpret_cast<uint32_t*>(&cur[r][q]);
+#pragma unroll
+            for (int i = 0; i < (int)(sizeof(RawS<F>) / 4); ++i) asm volatile("" : "+v"(rw[i]));
+          }
+        const int xr2 = a.x_per_slot ? s2 : s2 / a.top_k;
+        XO f2[NU];
+#pragma unroll
+        for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr2, min(lane + 64 * q, units - 1), f2[q]);
+        apply(f2, s2);
+      }
+    }
   }
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     int drop = 0;
-    for (int i = 0; i < a.n_tok * a.top_k; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
+    for (int i = 0; i < n_slots; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
     a.err[0] = drop;
   }
 }
