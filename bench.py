@@ -214,16 +214,14 @@ class MoeRing:
 
     def ffn_step(self, qmv, i):
         """The MoE FFN: router and top-k (writing the Q8 blocks of x as well),
-        then the routed gate+up; the down
-        projection's input is SwiGLU of the gate+up output, quantized to Q8
-        in one kernel, and its outputs are combined with the router's
-        weights."""
+        then the routed gate+up with SwiGLU and the Q8 blocks of its output
+        (qmv_moe_gate_up_swiglu, two launches unless one is asked for), then
+        the down projection combined with the router's weights."""
         e, ng, kg, nd, kd = self.shape
         # the router also writes the Q8 blocks of x that the gate+up projection takes
         qmv.router_topk(self.x[i % 8], self.wr, self.top_k, ids=self.r_ids, weights=self.r_w,
                         logits=self.r_logits, xq=self.xq)
-        qmv.moe_matvec(2, self.gu[i % 2], e, ng, kg, self.xq, False, self.r_ids, None, self.ws_gu, y=self.y_gu)
-        qmv.swiglu_quantize(self.y_gu.view(self.t * self.top_k, ng), kd, out=self.hq)
+        qmv.moe_gate_up_swiglu(2, self.gu[i % 2], e, kd, kg, self.xq, self.r_ids, self.ws_gu, hq=self.hq)
         qmv.moe_matvec(2, self.dn[i % 2], e, nd, kd, self.hq, True, self.r_ids, self.r_w, self.ws_dn,
                        y=self.y_dn)
 

@@ -310,6 +310,36 @@ qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts, int64
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qmv_moe_gate_up_swiglu -- the MoE FFN's routed gate+up projection with
+ * SwiGLU and the Q8 blocks of its output: the down projection's input from
+ * one call.  Castagna Veloce page, "Fused operations" (gate/up + SwiGLU; Q8
+ * activations made once).  Either path's result is bit-identical to
+ *   qmv_moe_matvec(type, w, n_experts, 2 n_ff, k, xq, 0, ids, NULL, ...)
+ *   -> gu [n_tok][top_k][2 n_ff], then
+ *   qmv_swiglu_quantize(gu, 2 n_ff, n_tok * top_k, n_ff, hq, NULL, ...).
+ * w    : n_experts gate+up matrices of 2 n_ff rows (gate rows 0 .. n_ff - 1,
+ *        up rows n_ff .. 2 n_ff - 1) by k, back to back (device, 16-byte
+ *        aligned); xq: one activation row per token (qmv_quantize_act).
+ * hq   : activation buffer of qmv_act_bytes(n_tok * top_k, n_ff) bytes
+ *        (device, 256-byte aligned); row t * top_k + s receives Q8(h) of
+ *        slot s of token t, h = silu(gate) * up; dropped slots give zeros.
+ * gu   : NULL, or fp32 [n_tok][top_k][2 n_ff] (device, 16-byte aligned)
+ *        that receives the gate+up outputs.
+ * ws   : the workspace of the routed gate+up call
+ *        (qmv_moe_workspace_bytes(type, n_experts, 2 n_ff, k, n_tok, top_k)).
+ * By default two launches: the routed matvec and qmv_swiglu_quantize (gu,
+ * or without it the workspace's per-slot area, carries the gate+up
+ * outputs), which measured faster than one.  qmv_set_tuning("ffn_fuse", 1)
+ * selects one launch up to 16 tokens on rows of at most 4096 weights: a
+ * few-slot kernel whose workgroup holds 32 gate rows and the matching 32 up
+ * rows and makes that block of h from them in LDS.
+ * n_ff % 32 == 0; other limits and errors as for qmv_moe_matvec.
+ */
+qmv_status qmv_moe_gate_up_swiglu(qmv_type type, const void* w, int64_t n_experts, int64_t n_ff, int64_t k,
+                                  const void* xq, const int32_t* ids, int64_t n_tok, int64_t top_k, void* hq,
+                                  float* gu, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qmv_moe_matvec_noalloc -- qmv_moe_matvec for callers that cannot allocate
  * device memory (code under HIP graph capture, serving loops and harnesses
  * that forbid hipMalloc): the same validation, kernels and results, with
@@ -425,7 +455,9 @@ qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* s
  *               kernel, 2 the matrix-core one (which falls back to the
  *               vector-ALU kernel when its staged rows do not fit in LDS),
  *               3 the few-slot flat kernel (each slot's expert rows
- *               streamed without grouping slots by expert).
+ *               streamed without grouping slots by expert);
+ *   "ffn_fuse": -1 automatic (default: two launches), 0 two launches, 1
+ *               one launch where it applies, for qmv_moe_gate_up_swiglu.
  * The environment variables QMV_SPLITK, QMV_VARIANT and QMV_MOE_KERNEL set
  * the same switches when the library loads.  Returns QMV_ERR_INVALID_ARG for an unknown key or
  * value.

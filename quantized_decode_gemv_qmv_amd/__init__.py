@@ -21,6 +21,7 @@ __all__ = [
     "Q8_0", "Q4_K", "IQ4_XS", "Q5_K", "Q6_K", "Q8G128", "QmvError", "lib", "library_path", "symbols",
     "row_bytes", "act_bytes", "act_offsets", "act_fields", "matvec_workspace_bytes",
     "moe_workspace_bytes", "quantize_act", "matvec", "matvec_x", "matvec_batch", "moe_matvec", "moe_matvec_noalloc",
+    "moe_gate_up_swiglu",
     "block_dots",
     "block_dots_mx", "moe_block_dots", "stream_read",
     "set_tuning", "swiglu_quantize", "router_topk", "variant_name", "variants", "pick_variant", "matvec_plan", "MAX_TOKENS", "MAX_MOE_TOKENS",
@@ -90,6 +91,7 @@ def lib():
         "qmv_moe_workspace_bytes": ([I, I64, I64, I64, I64, I64], SZ),
         "qmv_moe_matvec": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P, SZ, P], I),
         "qmv_moe_matvec_noalloc": ([I, P, I64, I64, I64, P, I, P, P, I64, I64, P, P], I),
+        "qmv_moe_gate_up_swiglu": ([I, P, I64, I64, I64, P, P, I64, I64, P, P, P, SZ, P], I),
         "qmv_block_dots": ([I, P, I64, I64, P, I64, P, P], I),
         "qmv_block_dots_mx": ([I, P, I64, I64, P, I64, I64, I, P, P], I),
         "qmv_moe_block_dots": ([I, P, I64, I64, I64, P, I, P, I64, I64, I64, P, P, SZ, P], I),
@@ -336,6 +338,35 @@ def moe_matvec(fmt: int, w: torch.Tensor, n_experts: int, n_rows: int, k: int,
                                 _ptr(ids), _ptr(route_w), n_tok, top_k, _ptr(y), _ptr(ws),
                                 ws.numel(), _stream(stream)), "qmv_moe_matvec")
     return y
+
+
+def moe_gate_up_swiglu(fmt: int, w: torch.Tensor, n_experts: int, n_ff: int, k: int, xq: torch.Tensor,
+                       ids: torch.Tensor, ws: torch.Tensor, hq: torch.Tensor | None = None,
+                       gu: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Routed gate+up (2 n_ff rows per expert, gate first) with SwiGLU and
+    Q8 folded in: returns hq, the Q8 activation buffer of the n_tok * top_k
+    slot rows of h; gu (fp32 [T][top_k][2 n_ff]), if given, receives the
+    gate+up outputs."""
+    _need(w, torch.uint8, "w")
+    _need(xq, torch.uint8, "xq")
+    _need(ids, torch.int32, "ids")
+    _need(ws, torch.uint8, "ws")
+    n_tok, top_k = ids.shape
+    if hq is None:
+        hq = torch.empty(act_bytes(n_tok * top_k, n_ff), dtype=torch.uint8, device=w.device)
+    _need(hq, torch.uint8, "hq")
+    if hq.numel() < act_bytes(n_tok * top_k, n_ff):
+        raise ValueError("hq too small")
+    if gu is not None:
+        _need(gu, torch.float32, "gu")
+        if gu.numel() < n_tok * top_k * 2 * n_ff:
+            raise ValueError("gu too small")
+    if w.numel() < n_experts * 2 * n_ff * row_bytes(fmt, k):
+        raise ValueError("w holds fewer than n_experts * 2 n_ff rows")
+    _check(lib().qmv_moe_gate_up_swiglu(fmt, _ptr(w), n_experts, n_ff, k, _ptr(xq), _ptr(ids), n_tok, top_k,
+                                        _ptr(hq), _ptr(gu), _ptr(ws), ws.numel(), _stream(stream)),
+           "qmv_moe_gate_up_swiglu")
+    return hq
 
 
 def moe_matvec_noalloc(fmt: int, w: torch.Tensor, n_experts: int, n_rows: int, k: int,

@@ -265,6 +265,12 @@ struct MoeLaunch {
   // workspace
   int* err;     // dropped-slot count of the call
   float* part;  // [n_tok * top_k][n_rows] per-slot outputs (combine only)
+  // the gate+up launch with SwiGLU + Q8 folded in: gate rows 0 .. n_ff-1
+  // and up rows n_ff .. 2 n_ff-1; hq the Q8 buffer it writes, h_off_d and
+  // h_off_s the byte offsets of its d and s (y: NULL, or the gate+up sums)
+  int n_ff;
+  uint8_t* hq;
+  int64_t h_off_d, h_off_s;
   // integer mode of the matrix-core MoE kernel (the block-dot test hook):
   // the exact integers of every (slot, row, 32-block) of the slot's expert
   // go to dots, int32 [n_tok * top_k][n_rows][units][c], and nothing else
@@ -273,10 +279,14 @@ struct MoeLaunch {
 };
 
 hipError_t launch_moe(const MoeLaunch& a, hipStream_t st);
+// The fused MoE gate+up + SwiGLU + Q8 kernel (one activation row per token,
+// rows of at most 4096 weights; hipErrorInvalidValue otherwise).
+hipError_t launch_moe_gate_up_swiglu(const MoeLaunch& a, hipStream_t st);
 // The matrix-core MoE kernel with tm (4 or 8) staged slot rows per group, in
 // integer mode (a.dots set).
 hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st);
 // Tuning: MoE kernel (0 automatic, 1 vector-ALU, 2 matrix-core).
 void set_moe_kernel(int v);
+int moe_kernel();
 
 }  // namespace qmv

@@ -531,6 +531,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
 // wave finds them with one ballot per 64 ids.  Outputs per slot, written as
 // k_moe writes them (to y, or to the workspace for the combine); a dropped
 // slot's row is zero.
+
 template <int F, int NU, int R, int WPB>
 __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
   const int lane = threadIdx.x & 63;
@@ -629,6 +630,165 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
     int drop = 0;
     for (int i = 0; i < n_slots; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
     a.err[0] = drop;
+  }
+}
+
+// The MoE FFN's gate+up projection with SwiGLU and the Q8 blocks of its
+// output folded in (Castagna Veloce page, "Fused operations": gate/up +
+// SwiGLU; Q8 activations made once): the few-slot flat kernel, each of its
+// workgroups taking 32 gate rows 32x .. 32x + 31 of the expert (waves 0-7,
+// four rows each) and the 32 matching up rows n_ff + 32x .. (waves 8-15), so
+// that one workgroup holds both halves of one 32-value block of
+// h = silu(g) * u.  Per slot the 64 wave sums meet in LDS and eight lanes
+// make the block with the quantizer's routine -- the same fp32 operations as
+// k_swiglu_quantize on the gate+up output, so the blocks are bit-identical
+// to the two-launch path.  The gate+up sums themselves go to a.y if it is
+// set.  Expert reads are shared between the slots of one expert as in
+// k_moe_flat.
+template <int F, int NU>
+__global__ __launch_bounds__(1024) void k_moe_gate_up_swiglu(MoeLaunch a) {
+  constexpr int R = 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = blockIdx.y;
+  const int n_slots = a.n_tok * a.top_k;
+  const int e = a.ids[slot];
+  const bool valid = e >= 0 && e < a.n_experts;
+  const int units = a.units;
+  const int n_ff = a.n_ff;
+  const int n_rows = 2 * n_ff;  // gate rows, then up rows
+  const int b = blockIdx.x;     // the 32-value block of h
+  const int row0 = (wave < 8 ? 0 : n_ff) + 32 * b + 4 * (wave & 7);
+  const Act gx{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
+  __shared__ float s_gu[64];
+  auto same_in = [&](int c) -> uint64_t {
+    const int i = c * 64 + lane;
+    const int id = i < n_slots ? a.ids[i] : -1;
+    return __ballot(valid && id == e);
+  };
+  for (int c = 0; c * 64 < slot; ++c) {
+    const uint64_t lo = slot - c * 64 >= 64 ? ~0ull : ((1ull << (slot - c * 64)) - 1);
+    if (same_in(c) & lo) return;  // an earlier slot's workgroups compute this one
+  }
+  const int xr0 = slot / a.top_k;  // one activation row per token
+  XO xf[NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr0, min(lane + 64 * q, units - 1), xf[q]);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = a.w + ((int64_t)(valid ? e : 0) * n_rows + row0 + r) * a.row_bytes;
+  RawS<F> cur[R][NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+  __builtin_amdgcn_sched_barrier(0);
+  const int nb = n_ff / 32;
+  int8_t* h_qs = reinterpret_cast<int8_t*>(a.hq);
+  float* h_d = reinterpret_cast<float*>(a.hq + a.h_off_d);
+  int32_t* h_s = reinterpret_cast<int32_t*>(a.hq + a.h_off_s);
+  auto apply = [&](const XO (&f)[NU], int s) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int uraw = lane + 64 * q;
+      const bool ok = uraw < units;
+      const int u = ok ? uraw : units - 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        DecO<F> dec;
+        decode_own(cur[r][q], u, lane & 1, ok, dec);
+        const int dv = own_pass<F>(own_first(dec, f[q].f));
+        acc[r] = own_apply(dec, own_second(dec, f[q].s, dv), f[q].p, acc[r]);
+      }
+    }
+    float outv = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float sv = wave_sum(acc[r]);
+      outv = lane == r ? sv : outv;
+    }
+    outv = valid ? outv : 0.f;
+    if (lane < R) {
+      s_gu[(wave < 8 ? 0 : 32) + 4 * (wave & 7) + lane] = outv;
+      if (a.y != nullptr) a.y[(int64_t)s * n_rows + row0 + lane] = outv;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane j of each group of 8: values 4j .. 4j + 3 of the block, as
+      // k_swiglu_quantize holds them; lanes 0-7 store the block
+      const int j = lane & 7;
+      float hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = s_gu[4 * j + i], u = s_gu[32 + 4 * j + i];
+        hv[i] = g / (1.0f + expf(-g)) * u;
+      }
+      float db;
+      int sum;
+      const uint32_t packed = q8_block8(hv, db, sum);
+      if (lane < 8) {
+        const int64_t o = (int64_t)s * n_ff + 32 * b + 4 * j;
+        *reinterpret_cast<uint32_t*>(h_qs + o) = packed;
+        if (j == 0) {
+          h_d[(int64_t)s * nb + b] = db;
+          h_s[(int64_t)s * nb + b] = sum;
+        }
+      }
+    }
+    __syncthreads();  // s_gu is reused by the next slot
+  };
+  apply(xf, slot);
+  if (valid) {
+    for (int c = slot / 64; c * 64 < n_slots; ++c) {
+      const int sh = slot - c * 64;
+      uint64_t m = same_in(c) & (sh < 0 ? ~0ull : ~((2ull << sh) - 1));
+      while (m != 0) {  // uniform over the workgroup
+        const int s2 = c * 64 + __builtin_ctzll(m);
+        m &= m - 1;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int q = 0; q < NU; ++q) {
+            uint32_t* rw = reinterpret_cast<uint32_t*>(&cur[r][q]);
+#pragma unroll
+            for (int i = 0; i < (int)(sizeof(RawS<F>) / 4); ++i) asm volatile("" : "+v"(rw[i]));
+          }
+        XO f2[NU];
+#pragma unroll
+        for (int q = 0; q < NU; ++q) load_xo<F>(gx, s2 / a.top_k, min(lane + 64 * q, units - 1), f2[q]);
+        apply(f2, s2);
+      }
+    }
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    int drop = 0;
+    for (int i = 0; i < n_slots; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
+    a.err[0] = drop;
+  }
+}
+
+template <int F>
+static hipError_t run_gate_up_swiglu(const MoeLaunch& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.n_ff / 32), (unsigned)(a.n_tok * a.top_k));
+  if (a.units <= 64)
+    hipLaunchKernelGGL((k_moe_gate_up_swiglu<F, 1>), grid, dim3(1024), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_moe_gate_up_swiglu<F, 2>), grid, dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gate_up_swiglu(const MoeLaunch& a, hipStream_t st) {
+  if (a.units > 128 || a.n_ff % 32 || a.n_rows != 2 * a.n_ff || a.x_per_slot || a.rw != nullptr)
+    return hipErrorInvalidValue;
+  switch (a.fmt) {
+    case FQ8_0: return run_gate_up_swiglu<FQ8_0>(a, st);
+    case FQ4_K: return run_gate_up_swiglu<FQ4_K>(a, st);
+    case FIQ4_XS: return run_gate_up_swiglu<FIQ4_XS>(a, st);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -921,6 +1081,7 @@ static hipError_t run_moe_flat_fmt(const MoeLaunch& a, hipStream_t st) {
 
 static int g_moe_kernel = 0;  // tuning: 0 automatic, 1 vector-ALU, 2 matrix-core, 3 few-slot flat kernel
 void set_moe_kernel(int v) { g_moe_kernel = v; }
+int moe_kernel() { return g_moe_kernel; }
 
 // The few-slot flat kernel while grouping slots by expert saves less than
 // its routing costs (measured on 128 experts, top-8: one activation row per
