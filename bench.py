@@ -64,8 +64,8 @@ WEIGHT_BYTES = {wl: v[1] * (v[2] // BLOCK[v[0]][0]) * BLOCK[v[0]][1] for wl, v i
 # expert, top-8 routing
 MOE = dict(name="moe_iq4_xs_e128", ffn_name="moe_ffn_iq4_xs_e128", experts=128, top_k=8,
            gate_up=(3072, 4096), down=(4096, 1536), tokens=(1, 6, 16, 64))
-KERNEL_SOURCES = ("qmv_device.h", "qmv_internal.h", "qmv_matvec.hip", "qmv_variants.hip", "qmv_mfma.hip",
-                  "qmv_quant.hip", "qmv_api.hip")
+KERNEL_SOURCES = ("qmv_device.h", "qmv_internal.h", "qmv_matvec.hip", "qmv_variants.hip", "qmv_mfma.h",
+                  "qmv_mfma.hip", "qmv_mxf.hip", "qmv_quant.hip", "qmv_api.hip")
 
 
 def log(msg: str) -> None:
@@ -593,6 +593,44 @@ def moe_rows(torch, qmv, tokens, reps=5):
     return rows
 
 
+READ_SWEEP_MB = (1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024)
+
+
+def read_sweep(torch, qmv, reps=15):
+    """The plain read's time (qmv_stream_read, median over replays) at sizes
+    from 1 MiB to 1 GiB, each call on its own slice of a 2 GiB buffer (so
+    that no call finds its bytes in the 256 MB Infinity Cache), and the fit
+    t = t0 + bytes / BW over the sizes from 16 MiB: the fixed cost of one
+    launch streaming from HBM and the rate it approaches.  A launch that
+    reads B bytes can reach at most B / (t0 + B / BW) -- the ceiling the
+    matvec kernels are held to."""
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows = []
+    for mb in READ_SWEEP_MB:
+        size = mb << 20
+        copies = (2 << 30) // size
+        per = max(copies, 32)
+        us = timed_replays(torch, lambda i: qmv.stream_read(pool[(i % copies) * size:(i % copies + 1) * size], sink),
+                           per, reps)
+        rows.append({"MiB": mb, "bytes": size, "us": round(us, 3), "GBps": round(size / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(size / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"bench: read {mb} MiB {us:.2f} us")
+    pts = [(r["bytes"], r["us"]) for r in rows if r["MiB"] >= 16]
+    n = len(pts)
+    mx = sum(b for b, _ in pts) / n
+    my = sum(u for _, u in pts) / n
+    slope = sum((b - mx) * (u - my) for b, u in pts) / sum((b - mx) ** 2 for b, _ in pts)
+    t0 = my - slope * mx
+    bw = 1e-3 / slope  # bytes per us -> GB/s
+    ceil = {wl: round(WEIGHT_BYTES[wl] / (t0 + WEIGHT_BYTES[wl] / (bw * 1e3)) / 1e3 / HBM_PEAK_GBS, 4)
+            for wl in ("q4_k_14336x4096", "iq4_xs_4096x14336", "q8_0_4096x4096", "q8_0_splitk_256x65536")}
+    return {"rows": rows, "fit": {"t0_us": round(t0, 3), "asymptotic_GBps": round(bw, 1),
+                                  "sizes": "16 MiB .. 1 GiB"},
+            "ceiling_frac_of_peak": ceil}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -616,6 +654,9 @@ def main() -> int:
     ap.add_argument("--profile-read", action="store_true",
                     help="with --profile-launches: launch the plain read of the weight bytes (qmv_stream_read) "
                          "instead of the matvec")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="time the plain read (qmv_stream_read) from 1 MiB to 1 GiB, fit its fixed cost and "
+                         "rate, print one JSON line and exit")
     ap.add_argument("--variant", default=None,
                     help="force a matvec kernel variant by name (qmv_set_tuning 'variant')")
     args = ap.parse_args()
@@ -641,6 +682,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.read_sweep:
+        print(json.dumps({"read_sweep": read_sweep(torch, qmv), "device": device_info(torch, clocks)}), flush=True)
+        return 0
     if args.workload in (MOE["name"], MOE["ffn_name"]):
         if not 1 <= args.tokens <= 64:
             print("--tokens must be 1..64 for the MoE workload", file=sys.stderr)
