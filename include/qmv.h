@@ -95,6 +95,11 @@ typedef enum {
 #define QMV_MAX_ACT_ROWS 65536  /* qmv_quantize_act rows per call          */
 
 int qmv_abi_version(void);
+/* The hipError_t code (as an int; 0 if none) of the last HIP runtime error
+ * that an entry point called on this thread reported as QMV_ERR_HIP, and
+ * its name (hipGetErrorName; static storage, never NULL). */
+int qmv_last_hip_error(void);
+const char* qmv_last_hip_error_name(void);
 const char* qmv_status_string(qmv_status status);
 
 /* Host-only size helpers: return 0 for invalid arguments. */

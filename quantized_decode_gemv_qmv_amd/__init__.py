@@ -76,6 +76,8 @@ def lib():
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {
         "qmv_abi_version": ([], I),
+        "qmv_last_hip_error": ([], I),
+        "qmv_last_hip_error_name": ([], ctypes.c_char_p),
         "qmv_status_string": ([I], ctypes.c_char_p),
         "qmv_row_bytes": ([I, I64], SZ),
         "qmv_act_bytes": ([I64, I64], SZ),
@@ -122,6 +124,8 @@ def _stream(stream) -> ctypes.c_void_p:
 
 def _check(status: int, what: str) -> None:
     if status != 0:
+        if status == 5:  # QMV_ERR_HIP: name the runtime's error
+            what = f"{what} ({lib().qmv_last_hip_error_name().decode()})"
         raise QmvError(status, what)
 
 

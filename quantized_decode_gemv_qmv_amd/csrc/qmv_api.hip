@@ -153,10 +153,10 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 // the workload shapes (Q8_0 4096x4096, 14336x4096 and 152064x5120, q4_K,
 // q5_K and q6_K 14336x4096, IQ4_XS 4096x14336, Q8_0 256x65536, Q8G128
 // 152064x5120, 14336x4096, 4096x4096 and 4096x14336; 1..16 tokens):
-//   - up to 1024 rows of at least 256 blocks, few tokens: up to one row
-//     per compute unit the streaming kernel with K split over a 16-wave
-//     workgroup (while its staging fits), else the flat kernel with one
-//     row per wave in four-wave workgroups;
+//   - up to 1024 rows of at least 256 blocks, up to four tokens: the
+//     long-row kernel (a workgroup's waves split one row's K, activation
+//     fragments from global memory), the flat kernel on 1024 rows from three
+//     tokens;
 //   - up to two tokens (four for Q8_0): the flat kernel (one wave per row
 //     group, all loads issued at once), its units per lane sized so that one
 //     chunk covers the row;
@@ -184,15 +184,23 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t rpc = n_rows / cus;  // rows per compute unit
   const int64_t tiles = (n_rows + 15) / 16;
   const char* name;
-  const bool kq = type == QMV_Q4_K || type == QMV_Q5_K || type == QMV_Q6_K;
-  if (n_rows <= 4 * (int64_t)cus && units >= 256 && n_tok <= (kq ? 2 : 4)) {
-    // few rows, long K (measured on 256 x 32768 and 256 x 65536 Q8_0 / q4_K,
-    // 512 x 16384 Q8_0 / IQ4_XS, 1024 x 8192 IQ4_XS at 1..4 tokens): up to
-    // one row per compute unit the streaming kernel with K split over a
-    // 16-wave workgroup, while its LDS staging fits; else the flat kernel
-    // with one row per wave and four-wave workgroups (1024 x 8192 IQ4_XS at
-    // one token: 3.4 us against 7.1 us for the eight-wave variant)
-    name = n_rows <= cus && stream_fits(find_variant("st_k16_r1_u2"), k, n_tok) ? "st_k16_r1_u2" : "fl_w4_r1_u4_g";
+  if (n_rows <= 4 * (int64_t)cus && units >= 256 && n_tok <= 4) {
+    // few rows, long K: the long-row kernel, a workgroup's waves splitting
+    // the K of one row with activation fragments from global memory
+    // (measured at 1 / 2 / 4 tokens, us: Q8_0 256 x 65536 6.09 / 6.75 / 8.95
+    // against 7.29 / 13.91 / 15.86 for the LDS-staged streaming kernel;
+    // q4_K 256 x 65536 4.80 / 5.81 / 8.10 against 6.09 / 12.93 / 14.79;
+    // 512 x 16384 Q8_0 4.08 / 4.58 / 5.67, IQ4_XS 3.57 / 4.13 / 5.19 against
+    // 5.42 / 6.42 / 7.49 and 4.94 / 5.07 / 6.78 for the flat kernel): eight
+    // waves of four units per lane up to one row per compute unit and two
+    // tokens (sixteen of two units at three and four), four of two units up
+    // to two rows per compute unit; on 1024 rows (IQ4_XS x 8192) the same up
+    // to two tokens (3.40 / 3.78 us against 3.44 / 3.86) and the flat kernel
+    // from three (4.60 against 4.76 us at four)
+    if (n_rows <= cus)
+      name = n_tok <= 2 ? "lk_w8_r1_u4" : "lk_w16_r1_u2";
+    else
+      name = n_rows <= 2 * (int64_t)cus || n_tok <= 2 ? "lk_w4_r1_u2" : "fl_w4_r1_u4_g";
   } else if (n_rows < 4 * (int64_t)cus && units >= 256) {
     // the same shapes at more tokens: where the streaming kernel's staging
     // does not fit, the matrix-core kernel (q4_K 256 x 65536 at four tokens:
@@ -251,7 +259,7 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
 
 int choose_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   const int64_t forced = g_variant.load();
-  if (forced >= 0 && forced < kNumVariants && kVariants[forced].kind >= 4 && !has_mfma(type))
+  if (forced >= 0 && forced < kNumVariants && is_mx(kVariants[forced]) && !has_mfma(type))
     return auto_variant(type, n_rows, k, n_tok);  // no matrix-core decode of this format
   if (forced >= 0 && forced < kNumVariants) {
     // a forced streaming variant whose staging does not fit runs the
@@ -381,8 +389,23 @@ constexpr int64_t kMoePartOffset = kMoeStatusBytes + kMoeCounterBytes;
 
 }  // namespace
 
+// The last HIP error an entry point of this thread turned into QMV_ERR_HIP.
+static thread_local hipError_t g_last_hip = hipSuccess;
+
+static qmv_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return QMV_OK;
+  g_last_hip = e;
+  return QMV_ERR_HIP;
+}
+
 // ------------------------------------------------------------------ misc
 QMV_API int qmv_abi_version(void) { return QMV_ABI_VERSION; }
+
+QMV_API int qmv_last_hip_error(void) { return static_cast<int>(g_last_hip); }
+
+QMV_API const char* qmv_last_hip_error_name(void) {
+  return g_last_hip == hipSuccess ? "hipSuccess" : hipGetErrorName(g_last_hip);
+}
 
 QMV_API const char* qmv_status_string(qmv_status st) {
   switch (st) {
@@ -492,7 +515,7 @@ QMV_API qmv_status qmv_quantize_act(const float* x, int64_t ldx, int64_t n_tok, 
                                  reinterpret_cast<float*>(b + qmv_act_offset_d(n_tok, k)),
                                  reinterpret_cast<int32_t*>(b + qmv_act_offset_s(n_tok, k)),
                                  static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 QMV_API qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t rows, int64_t n_ff,
@@ -509,7 +532,7 @@ QMV_API qmv_status qmv_swiglu_quantize(const float* gu, int64_t ldg, int64_t row
                                         reinterpret_cast<float*>(b + qmv_act_offset_d(rows, n_ff)),
                                         reinterpret_cast<int32_t*>(b + qmv_act_offset_s(rows, n_ff)), h_out,
                                         static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 QMV_API qmv_status qmv_router_topk(const float* x, int64_t ldx, int64_t n_tok, int64_t k, const float* wr,
@@ -531,7 +554,7 @@ QMV_API qmv_status qmv_router_topk(const float* x, int64_t ldx, int64_t n_tok, i
                                     static_cast<int>(n_experts), static_cast<int>(top_k), ids, weights, logits,
                                     const_cast<int8_t*>(xv.qs), const_cast<float*>(xv.d),
                                     const_cast<int32_t*>(xv.s), static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 // --------------------------------------------------------------- matvec
@@ -589,7 +612,7 @@ QMV_API qmv_status qmv_matvec(qmv_type type, const void* w, int64_t n_rows, int6
     a.part = reinterpret_cast<float*>(b + kSplitCounterBytes);
   }
   hipError_t e = launch_matvec(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 // The LDS-staged flat variant that quantizes its own activations for a
@@ -659,7 +682,7 @@ QMV_API qmv_status qmv_matvec_x(qmv_type type, const void* w, int64_t n_rows, in
   a.cus = dv.cus;
   a.lds_per_cu = dv.lds_per_cu;
   hipError_t e = launch_matvec(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 // Byte extent [lo, hi) of an fp32 [n_tok][ld] output touching n columns.
@@ -735,7 +758,7 @@ QMV_API qmv_status qmv_matvec_batch(qmv_type type, const qmv_matvec_item* items,
   a.cus = dv.cus;
   a.lds_per_cu = dv.lds_per_cu;
   hipError_t e = launch_matvec(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, int64_t k,
@@ -751,7 +774,7 @@ QMV_API qmv_status qmv_block_dots(qmv_type type, const void* w, int64_t n_rows, 
                                    static_cast<int>(n_rows), static_cast<int>(k / 32),
                                    act_view(xq, n_tok, k), static_cast<int>(n_tok), out,
                                    static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_rows, int64_t k, const void* xq,
@@ -759,7 +782,7 @@ QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_row
   qmv_status st = check_weights(type, w, n_rows, k);
   if (st != QMV_OK) return st;
   if (xq == nullptr || out == nullptr || n_tok < 1 || slices < -1 || slices == 1 || slices > kMaxSlices ||
-      variant < -1 || variant >= kNumVariants || (variant >= 0 && kVariants[variant].kind < 4))
+      variant < -1 || variant >= kNumVariants || (variant >= 0 && !is_mx(kVariants[variant])))
     return QMV_ERR_INVALID_ARG;
   if (n_tok > QMV_MAX_TOKENS || !has_mfma(type)) return QMV_ERR_UNSUPPORTED;
   if (n_tok * n_rows * (k / 32) > INT32_MAX) return QMV_ERR_UNSUPPORTED;
@@ -771,7 +794,7 @@ QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_row
     // and the 8-wave one beyond
     const bool use_ws = qmv_matvec_workspace_bytes(type, n_rows, k, n_tok) > 0;
     const Plan p = make_plan(type, n_rows, k, n_tok, use_ws);
-    v = kVariants[p.variant].kind >= 4 ? p.variant : find_variant(n_tok <= 8 ? "mx_w16_k4_r2" : "mx_w8_k1_r4");
+    v = is_mx(kVariants[p.variant]) ? p.variant : find_variant(n_tok <= 8 ? "mx_w16_k4_r2" : "mx_w8_k1_r4");
   }
   const DeviceInfo dv = device_info();
   MxfPlan mp{};
@@ -809,7 +832,7 @@ QMV_API qmv_status qmv_block_dots_mx(qmv_type type, const void* w, int64_t n_row
   a.dots_slices = slices;
   hipError_t e = kVariants[v].kind == 5 ? launch_mxf(a, mp, static_cast<hipStream_t>(stream))
                                         : launch_mx(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 QMV_API qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* stream) {
@@ -818,7 +841,7 @@ QMV_API qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink,
   if (!aligned(p, 16) || !aligned(sink, 4)) return QMV_ERR_MISALIGNED;
   hipError_t e = launch_stream_read(static_cast<const uint8_t*>(p), bytes, 0x9e3779b9u, sink,
                                     static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 // ------------------------------------------------------------------ MoE
@@ -876,7 +899,7 @@ static qmv_status moe_run(qmv_type type, const void* w, int64_t n_experts, int64
   a.err = reinterpret_cast<int*>(b);
   a.part = reinterpret_cast<float*>(b + kMoePartOffset);
   hipError_t e = launch_moe(a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }
 
 QMV_API qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts,
@@ -938,7 +961,7 @@ QMV_API qmv_status qmv_moe_gate_up_swiglu(qmv_type type, const void* w, int64_t 
     a.h_off_d = static_cast<int64_t>(qmv_act_offset_d(rows, n_ff));
     a.h_off_s = static_cast<int64_t>(qmv_act_offset_s(rows, n_ff));
     hipError_t e = launch_moe_gate_up_swiglu(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+    return hip_status(e);
   }
   // two launches: the routed gate+up into gu (or the workspace's per-slot
   // area, which an unweighted call leaves unused), then SwiGLU + Q8
@@ -961,15 +984,17 @@ static void* scratch_address(qmv_status* st) {
   static std::mutex mu;
   static void* addr[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    *st = QMV_ERR_HIP;
+  const hipError_t ed = hipGetDevice(&dev);
+  if (ed != hipSuccess || dev < 0 || dev >= 64) {
+    *st = ed != hipSuccess ? hip_status(ed) : hip_status(hipErrorInvalidDevice);
     return nullptr;
   }
   std::lock_guard<std::mutex> lock(mu);
   if (addr[dev] == nullptr) {
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
-      *st = QMV_ERR_HIP;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || p == nullptr) {
+      *st = hip_status(es != hipSuccess ? es : hipErrorInvalidSymbol);
       return nullptr;
     }
     addr[dev] = p;
@@ -1033,5 +1058,5 @@ QMV_API qmv_status qmv_moe_block_dots(qmv_type type, const void* w, int64_t n_ex
   const int tm = slot_rows != 0 ? static_cast<int>(slot_rows) : (n_tok <= 16 ? 4 : 8);
   hipError_t e = launch_moe_mx_dots(a, tm, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidValue) return QMV_ERR_UNSUPPORTED;  // the staged rows do not fit in LDS
-  return e == hipSuccess ? QMV_OK : QMV_ERR_HIP;
+  return hip_status(e);
 }

@@ -36,7 +36,10 @@ struct ActView {
 //   kind 5: flat matrix-core kernel (k_mxf) -- the same tile in one pass
 //           over the rows: wpb waves per workgroup, each holding `nu`
 //           super-blocks of one row tile's K slice, all loaded at once
-//           (waves per tile and K slices planned per launch).
+//           (waves per tile and K slices planned per launch);
+//   kind 6: long-row kernel (k_long) -- one workgroup of wpb waves per group
+//           of `rows` rows, its waves splitting K in chunks of `nu` units per
+//           lane, activation fragments loaded from global memory.
 struct Variant {
   int kind;
   int lpr;
@@ -49,6 +52,8 @@ struct Variant {
 };
 
 extern const Variant kVariants[];
+// The matrix-core kinds (integer MFMA tiles).
+inline bool is_mx(const Variant& v) { return v.kind == 4 || v.kind == 5; }
 extern const int kNumVariants;
 
 // The matrix a launch row belongs to: its weights, output and residual, its

@@ -760,6 +760,95 @@ static hipError_t run_mv(const MatvecLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- long-row kernel
+// Few rows, long K (a few hundred rows of tens of thousands of weights): a
+// workgroup of WPB waves takes one group of R rows and its waves split K,
+// wave w taking chunks w, w + WPB, .. of 64 * NU units (one chunk each in the
+// shapes it is chosen for).  Each wave loads the activation fragments of its
+// own chunk straight from global memory, ahead of its weight loads (vector
+// loads return in issue order, and the fragments are cache-resident after
+// the first workgroups), so no workgroup copies the whole activation buffer
+// into LDS: on 256 x 65536 Q8_0 rows that per-workgroup copy, 82 KB for each
+// of 256 workgroups, moved more bytes than the weights.  The waves' sums meet
+// in LDS and are added in wave order.  One matrix per launch (no segments,
+// no residual).
+template <int F, int TM, int R, int NU, int WPB>
+__global__ __launch_bounds__(64 * WPB) void k_long(StreamArgs a) {
+  static_assert(R * TM <= 64 && TM <= 4, "one output per lane, fragments in registers");
+  constexpr int CH = 64 * NU;
+  __shared__ float red[WPB * R * TM];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = (int)blockIdx.x * R;
+  const int units = a.units;
+  const int nch = (units + CH - 1) / CH;
+  const int mine = wave < nch ? (nch - 1 - wave) / WPB + 1 : 0;  // chunks of this wave
+  const Act gx{reinterpret_cast<const int8_t*>(a.xq), reinterpret_cast<const float*>(a.xq + a.off_d),
+               reinterpret_cast<const int32_t*>(a.xq + a.off_s), a.k, a.nb};
+  const uint8_t* wr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wr[r] = a.w + (int64_t)min(row0 + r, a.n_rows - 1) * a.row_bytes;
+
+  float acc[R][TM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[r][t] = 0.f;
+
+  for (int i = 0; i < mine; ++i) {
+    const int c = wave + WPB * i;
+    XO xf[NU][TM];
+#pragma unroll
+    for (int q = 0; q < NU; ++q)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        load_xo<F>(gx, t < a.n_tok ? t : a.n_tok - 1, min(c * CH + lane + 64 * q, units - 1), xf[q][t]);
+    __builtin_amdgcn_sched_barrier(0);
+    RawS<F> cur[R][NU];
+#pragma unroll
+    for (int q = 0; q < NU; ++q)
+#pragma unroll
+      for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(c * CH + lane + 64 * q, units - 1), lane, cur[r][q]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < NU; ++q) {
+      const int uraw = c * CH + lane + 64 * q;
+      const bool ok = uraw < units;
+      const int u = ok ? uraw : units - 1;
+      DecO<F> dec[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) decode_own(cur[r][q], u, lane & 1, ok, dec[r]);
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        int dv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) dv[r] = own_pass<F>(own_first(dec[r], xf[q][t].f));
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          acc[r][t] = own_apply(dec[r], own_second(dec[r], xf[q][t].s, dv[r]), xf[q][t].p, acc[r][t]);
+      }
+    }
+  }
+
+  float outv = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const float sv = wave_sum(acc[r][t]);
+      outv = lane == r * TM + t ? sv : outv;
+    }
+  if (lane < R * TM) red[wave * R * TM + lane] = outv;
+  __syncthreads();
+  if (threadIdx.x < R * TM) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) sum += red[w * R * TM + threadIdx.x];
+    const int r = threadIdx.x / TM, t = threadIdx.x % TM;
+    if (t < a.n_tok && row0 + r < a.n_rows) a.y[(int64_t)t * a.ldy + row0 + r] = sum;
+  }
+}
+
 static StreamArgs stream_args(const MatvecLaunch& a) {
   StreamArgs sa;
   sa.w = a.w;
@@ -907,6 +996,23 @@ static hipError_t run_mt(const MatvecLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The long-row kernel takes one matrix and fragments of at most four tokens
+// held in registers (R * NU * TM <= 8: more spills); a batched launch, or
+// more tokens, runs the multi-token kernel mt_r2_w8_k4 instead (segments,
+// and LDS staging chunked to fit any K).
+template <int F, int TM, int R, int NU, int WPB>
+static hipError_t run_long(const MatvecLaunch& a, hipStream_t st) {
+  if constexpr (TM > 4 || R * NU * TM > 8) {
+    return run_mt<F, TM, 2, 1, 8, 4>(a, st);
+  } else {
+    if (a.seg.n > 0) return run_mt<F, TM, 2, 1, 8, 4>(a, st);
+    const unsigned grid = (unsigned)((a.n_rows + R - 1) / R);
+    StreamArgs sa = stream_args(a);
+    hipLaunchKernelGGL((k_long<F, TM, R, NU, WPB>), dim3(grid), dim3(64 * WPB), 0, st, sa);
+    return hipGetLastError();
+  }
+}
+
 template <int F, int TM>
 static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
   switch (a.variant) {
@@ -944,6 +1050,12 @@ static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
     case 31: return run_mt<F, TM, 2, 2, 4, 1>(a, st);
     case 32: return run_mt<F, TM, 1, 2, 16, 4>(a, st);
     case 33: return run_mt<F, TM, 1, 4, 16, 4>(a, st);
+    // 34..43: the matrix-core kernels (launch_mx, launch_mxf)
+    case 44: return run_long<F, TM, 1, 2, 16>(a, st);
+    case 45: return run_long<F, TM, 1, 4, 8>(a, st);
+    case 46: return run_long<F, TM, 1, 8, 4>(a, st);
+    case 47: return run_long<F, TM, 1, 2, 4>(a, st);
+    case 48: return run_long<F, TM, 2, 2, 16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

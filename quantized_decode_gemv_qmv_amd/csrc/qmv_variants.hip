@@ -33,6 +33,9 @@ const Variant kVariants[] = {
     {4, 16, 1, 4, 8, 4, 1, "mx_w8_k4_r4"},    {4, 16, 1, 4, 8, 8, 1, "mx_w8_k8_r4"},
     {5, 16, 1, 4, 16, 0, 1, "mf_w16_b4"},     {5, 16, 1, 2, 16, 0, 1, "mf_w16_b2"},
     {5, 16, 1, 4, 8, 0, 1, "mf_w8_b4"},       {5, 16, 1, 8, 8, 0, 1, "mf_w8_b8"},
+    {6, 64, 1, 2, 16, 16, 0, "lk_w16_r1_u2"}, {6, 64, 1, 4, 8, 8, 0, "lk_w8_r1_u4"},
+    {6, 64, 1, 8, 4, 4, 0, "lk_w4_r1_u8"},    {6, 64, 1, 2, 4, 4, 0, "lk_w4_r1_u2"},
+    {6, 64, 2, 2, 16, 16, 0, "lk_w16_r2_u2"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

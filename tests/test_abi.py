@@ -244,8 +244,11 @@ PLANS = [
     ((2, 4096, 14336, 16, False), ("mx_w8_k8_r4", 1)),
     ((1, 4096, 14336, 16, True), ("mx_w8_k1_r4", 8)),
     ((0, 4096, 4096, 1, True), ("fl_w4_r1_u2_l", 1)),
-    ((0, 256, 65536, 1, True), ("st_k16_r1_u2", 1)),     # split inside one workgroup
-    ((2, 1024, 8192, 1, True), ("fl_w4_r1_u4_g", 1)),
+    ((0, 256, 65536, 1, True), ("lk_w8_r1_u4", 1)),      # K split inside one workgroup
+    ((0, 256, 65536, 4, True), ("lk_w16_r1_u2", 1)),
+    ((1, 512, 16384, 2, False), ("lk_w4_r1_u2", 1)),
+    ((2, 1024, 8192, 1, True), ("lk_w4_r1_u2", 1)),
+    ((2, 1024, 8192, 4, True), ("fl_w4_r1_u4_g", 1)),
     ((0, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),
     ((5, 152064, 5120, 2, False), ("st_w4_r1_u3", 1)),
     ((5, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),

@@ -90,6 +90,33 @@ def test_chunked_variants_long_k(fmt):
         qmv.set_tuning("variant", -1)
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=[NAMES[f] for f in FMTS])
+def test_long_row_kernel(fmt):
+    """The long-row variants on rows longer than one pass of a workgroup's
+    waves (K = 32768: several chunks per wave for the four- and eight-wave
+    variants), an odd row count (the two-row variant's last group half
+    empty), one to four tokens, and five (more than its registers hold: the
+    multi-token kernel runs instead)."""
+    qmv = need_gpu()
+    n, k = 37, 32768
+    w = synth.make_weights(fmt, n, k, f"lr/{fmt}").data
+    wd = to_dev(w)
+    x = x_host(5, k, f"lrx/{fmt}")
+    long_rows = [v for v in range(len(qmv.variants())) if qmv.variant_name(v).startswith("lk_")]
+    assert long_rows
+    try:
+        for t in (1, 2, 3, 4, 5):
+            xq = quantize(qmv, x[:t])
+            yr, mag = _oracle_y(fmt, w, k, x[:t])
+            for v in long_rows:
+                qmv.set_tuning("variant", v)
+                say(f"matvec long rows {NAMES[fmt]} variant {qmv.variant_name(v)} T={t}")
+                y = qmv.matvec(fmt, wd, n, k, xq, t).cpu().numpy()
+                assert_y(y, yr, mag, f"{NAMES[fmt]} {qmv.variant_name(v)} T={t}")
+    finally:
+        qmv.set_tuning("variant", -1)
+
+
 FULL = [
     ("q8_0_4096x4096", synth.Q8_0, 4096, 4096, (1,)),
     ("q4_k_14336x4096", synth.Q4_K, 14336, 4096, (1, 2, 4, 8, 16)),
