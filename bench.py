@@ -64,8 +64,11 @@ WEIGHT_BYTES = {wl: v[1] * (v[2] // BLOCK[v[0]][0]) * BLOCK[v[0]][1] for wl, v i
 # expert, top-8 routing
 MOE = dict(name="moe_iq4_xs_e128", ffn_name="moe_ffn_iq4_xs_e128", experts=128, top_k=8,
            gate_up=(3072, 4096), down=(4096, 1536), tokens=(1, 6, 16, 64))
-KERNEL_SOURCES = ("qmv_device.h", "qmv_internal.h", "qmv_matvec.hip", "qmv_variants.hip", "qmv_mfma.h",
-                  "qmv_mfma.hip", "qmv_mxf.hip", "qmv_quant.hip", "qmv_api.hip")
+# The device code of the dense kernels: a recorded traffic figure is used
+# only while these files are unchanged and the planned variant is the one it
+# was taken from (host-side dispatch changes are caught by the latter).
+KERNEL_SOURCES = ("qmv_device.h", "qmv_internal.h", "qmv_matvec.hip", "qmv_mfma.h", "qmv_mfma.hip", "qmv_mxf.hip",
+                  "qmv_quant.hip")
 
 
 def log(msg: str) -> None:
@@ -80,16 +83,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, tokens: int, src_hash: str):
+def recorded_traffic(workload: str, tokens: int, src_hash: str, variant: str):
     """HBM bytes per launch from profiles/traffic_<workload>_t<T>.txt, if that
-    summary was taken from the current kernel sources."""
+    summary was taken from the current kernel sources and the same variant."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_t{tokens}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"^kernel_sources_sha256_16:\s*(\S+)", text, re.M)
     m_bytes = re.search(r"^traffic_bytes_per_launch:\s*([0-9.]+)", text, re.M)
-    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+    m_var = re.search(r"^matvec_variant:\s*(\S+)", text, re.M)
+    if not m_hash or not m_bytes or not m_var or m_hash.group(1) != src_hash or m_var.group(1) != variant:
         return None
     return float(m_bytes.group(1))
 
@@ -535,6 +539,70 @@ def counter_summary(path: str) -> int:
     return 0
 
 
+def _counter_rows(path: str):
+    """(kernel name, counter value) of every dispatch in a rocprofv3 --pmc
+    counter_collection.csv."""
+    import csv
+
+    with open(path, newline="") as f:
+        return [(row.get("Kernel_Name", "?"), float(row["Counter_Value"])) for row in csv.DictReader(f)]
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, tokens: int, variant: str) -> int:
+    """The HBM traffic file of one workload (profiles/traffic_<workload>_t<T>.txt)
+    from a FETCH_SIZE and a WRITE_SIZE run of --profile-launches: each counter
+    (KiB per dispatch) is scaled by what it reads for the runtime's copy of the
+    weight tensor in the same run (the ring's clones: exactly the weight bytes
+    read and written), and the matvec's median per dispatch is reported
+    against its algorithmic bytes."""
+    fmt, n, k, *_ = WORKLOADS[workload]
+    wb = WEIGHT_BYTES[workload]
+    out = {}
+    for what, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        copy = [v for name, v in rows if "copyBuffer" in name]
+        mv = {}
+        for name, v in rows:
+            if name.startswith("void qmv::k_") and "quantize" not in name and "stream_read" not in name:
+                mv.setdefault(name, []).append(v)
+        if not copy or not mv:
+            print(f"{path}: no copy or matvec dispatches", file=sys.stderr)
+            return 1
+        kname, vals = max(mv.items(), key=lambda kv: len(kv[1]))
+        scale = wb / (median(copy) * 1024.0)
+        out[what] = (kname, median(copy), len(copy), scale, median(vals), len(vals))
+    kname = out["FETCH_SIZE"][0]
+    c_f, n_f, s_f, v_f, m_f = out["FETCH_SIZE"][1:]
+    c_w, n_w, s_w, v_w, m_w = out["WRITE_SIZE"][1:]
+    rd, wr = v_f * 1024.0 * s_f, v_w * 1024.0 * s_w
+    # the profile mode runs as many warmup launches as profiled ones
+    prof = f"--workload {workload} --tokens {tokens} --profile-launches {m_f // 2}"
+    print(f"# HBM traffic of the {FMT_NAME[fmt]} {n}x{k} matvec at {tokens} token(s)")
+    print(f"# kernel: {kname}")
+    print("#")
+    print("# Commands (each counter in a run of its own, one MI355X):")
+    print("#   cd /tmp && export TMPDIR=/tmp")
+    print(f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- python3 <repo>/bench.py {prof}")
+    print(f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- python3 <repo>/bench.py {prof}")
+    print(f"#   python3 <repo>/bench.py --traffic-summary <fetch csv> <write csv> --workload {workload} --tokens {tokens}")
+    print("#")
+    print(f"# Normalisation: the same runs clone the {wb:,}-byte weight tensor (__amd_rocclr_copyBuffer),")
+    print("# reading and writing exactly that many bytes.")
+    print(f"#   copy FETCH_SIZE median {c_f:.1f} KiB over {n_f} dispatches -> read scale {s_f:.4f}")
+    print(f"#   copy WRITE_SIZE median {c_w:.1f} KiB over {n_w} dispatches -> write scale {s_w:.4f}")
+    print("#")
+    print("# Matvec, per dispatch (median over the run's dispatches):")
+    print(f"#   FETCH_SIZE {v_f:.1f} KiB over {m_f} dispatches -> {rd:.0f} bytes read")
+    print(f"#   WRITE_SIZE {v_w:.1f} KiB over {m_w} dispatches -> {wr:.0f} bytes written "
+          f"(y: {tokens} x {n} x 4 B = {tokens * n * 4})")
+    print(f"#   algorithmic weight bytes per launch: {wb} -> read / algorithmic = {rd / wb:.4f}")
+    print("#")
+    print(f"traffic_bytes_per_launch: {rd + wr:.0f}")
+    print(f"kernel_sources_sha256_16: {kernel_source_hash()}")
+    print(f"matvec_variant: {variant}")
+    return 0
+
+
 # The metric's token sweep (q4_K and IQ4_XS at 1..16 tokens) and the other
 # workload configurations, reported beside the headline by the default run.
 SWEEP = (("q4_k_14336x4096", (1, 2, 4, 8, 16)), ("iq4_xs_4096x14336", (1, 2, 4, 8, 16)))
@@ -648,6 +716,9 @@ def main() -> int:
                     help="print per-kernel median/avg/min/max of a rocprofv3 kernel trace and exit")
     ap.add_argument("--counter-summary", metavar="CSV",
                     help="print per-kernel mean counter values of a rocprofv3 --pmc counter_collection.csv and exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic file of --workload/--tokens from a FETCH_SIZE and a WRITE_SIZE "
+                         "counter run of --profile-launches and exit")
     ap.add_argument("--profile-launches", type=int, default=0, metavar="N",
                     help="for a profiler: run N plain launches of the workload's matvec alone (cycling the "
                          "weight ring, after N warmup launches) and exit")
@@ -665,6 +736,13 @@ def main() -> int:
         return trace_summary(args.trace_summary)
     if args.counter_summary is not None:
         return counter_summary(args.counter_summary)
+    if args.traffic_summary is not None:
+        # the variant qmv_matvec plans for the workload (host-side: no GPU needed)
+        import quantized_decode_gemv_qmv_amd as qmv
+
+        fmt, n, k, *_ = WORKLOADS[args.workload]
+        vi, _ = qmv.matvec_plan(fmt, n, k, args.tokens, qmv.matvec_workspace_bytes(fmt, n, k, args.tokens) > 0)
+        return traffic_summary(*args.traffic_summary, args.workload, args.tokens, qmv.variant_name(vi))
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (the matvec is "
               "measured on one GPU's share of the weights; multi-GPU sharding is not built)",
@@ -756,7 +834,6 @@ def main() -> int:
     read_us = timed_replays(torch, lambda i: [qmv.stream_read(w.view(-1), sink) for w in ring.w[i % ring.copies]],
                             max(ring.copies, 32))
     src_hash = kernel_source_hash()
-    traffic = recorded_traffic(args.workload, t, src_hash)
     # a batch of equal matrices runs the variant of their stacked rows (each
     # matrix padded to a multiple of 64 rows)
     if mats > 1:
@@ -764,6 +841,7 @@ def main() -> int:
     else:
         vi, slices = qmv.matvec_plan(fmt, n, k, t, ring.ws is not None)
         variant = qmv.variant_name(vi)
+    traffic = recorded_traffic(args.workload, t, src_hash, variant)
 
     by_tokens = []
     if args.all_tokens:
