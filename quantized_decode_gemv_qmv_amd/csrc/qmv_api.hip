@@ -188,8 +188,9 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     // few rows, long K: the long-row kernel, a workgroup's waves splitting
     // the K of one row with activation fragments from global memory
     // (measured at 1 / 2 / 4 tokens, us: Q8_0 256 x 65536 6.09 / 6.75 / 8.95
-    // against 7.29 / 13.91 / 15.86 for the LDS-staged streaming kernel;
-    // q4_K 256 x 65536 4.80 / 5.81 / 8.10 against 6.09 / 12.93 / 14.79;
+    // against 7.29 for the LDS-staged streaming kernel and 20.38 / 25.02 for
+    // the flat one (the streaming staging does not fit from two tokens);
+    // q4_K 256 x 65536 4.80 / 5.81 / 8.10 against 6.11 / 13.58 / 15.51;
     // 512 x 16384 Q8_0 4.08 / 4.58 / 5.67, IQ4_XS 3.57 / 4.13 / 5.19 against
     // 5.42 / 6.42 / 7.49 and 4.94 / 5.07 / 6.78 for the flat kernel): eight
     // waves of four units per lane up to one row per compute unit and two
