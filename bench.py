@@ -281,13 +281,31 @@ def median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
+# Untimed work before each measurement.  On MI355X a kernel's time keeps
+# falling for about 0.1 s of continuous work after the GPU was idle (IQ4_XS
+# 4096 x 14336 at one token: 9.3 us at once, 8.6 us from 0.1 s on); the
+# figures are taken at that steady state.
+WARM_SECONDS = 0.15
+
+
+def warm(torch, g, seconds=WARM_SECONDS):
+    """Replay graph g until `seconds` of wall time have passed."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def timed_replays(torch, fn, per, reps=21):
     """Median per-call time (us) of fn(i) over `reps` back-to-back replays of
-    a graph of `per` calls (each replay timed with HIP events; the graphs are
-    replayed on the stream the events are recorded on)."""
+    a graph of `per` calls, after WARM_SECONDS of untimed replays (each replay
+    timed with HIP events; the graphs are replayed on the stream the events
+    are recorded on)."""
     g = capture(torch, fn, per)
-    g.replay()
-    torch.cuda.synchronize()
+    warm(torch, g)
     return median(_replay_samples(torch, g, per, reps))
 
 
@@ -703,7 +721,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20000,
+                    help="untimed steps before the timed ones (the default is about 0.2 s of the one-token "
+                         "q4_K step: the GPU's clocks settle in about 0.1 s of continuous work)")
     ap.add_argument("--workload", default="q4_k_14336x4096",
                     choices=sorted(WORKLOADS) + [MOE["name"], MOE["ffn_name"]])
     ap.add_argument("--tokens", type=int, default=1)
