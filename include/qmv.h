@@ -461,6 +461,10 @@ qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* s
  *               vector-ALU kernel when its staged rows do not fit in LDS),
  *               3 the few-slot flat kernel (each slot's expert rows
  *               streamed without grouping slots by expert);
+ *   "moe_comb": 0 automatic (default), 1 one row per wave, 2 16-lane row
+ *               groups: the kernel qmv_moe_matvec runs for one
+ *               route-weighted token with top_k <= 8 (the second on rows of
+ *               at most 64 blocks);
  *   "ffn_fuse": -1 automatic (default: two launches), 0 two launches, 1
  *               one launch where it applies, for qmv_moe_gate_up_swiglu.
  * The environment variables QMV_SPLITK, QMV_VARIANT and QMV_MOE_KERNEL set

@@ -465,6 +465,11 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
     set_moe_kernel(static_cast<int>(value));
     return QMV_OK;
   }
+  if (!std::strcmp(key, "moe_comb")) {
+    if (value < 0 || value > 2) return QMV_ERR_INVALID_ARG;
+    set_moe_comb(static_cast<int>(value));
+    return QMV_OK;
+  }
   if (!std::strcmp(key, "ffn_fuse")) {
     if (value < -1 || value > 1) return QMV_ERR_INVALID_ARG;
     g_ffn_fuse = value;

@@ -890,6 +890,71 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat_comb(MoeLaunch a) {
   }
 }
 
+// One token, route-weighted, rows of at most 64 units (the down projection,
+// 48 units per row): workgroup (x, t) takes rows 4x .. 4x + 3 for every slot
+// of token t, wave s for slot s (top_k <= 8), each row held by a 16-lane
+// group with NU units per lane, so that all 64 lanes of a wave carry units
+// (one row per wave left 16 of its lanes idle on 48-unit rows) and a
+// workgroup runs eight waves of a few loads each rather than one wave of
+// every slot's loads.  A lane issues its activation fragments (the slot's own
+// row when x is per slot) and then its weight loads; the 16-lane sums of the
+// slots meet in LDS and the route-weighted sum is taken over the valid slots
+// in slot order, as k_moe_combine takes it.
+template <int F, int NU>
+__global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
+  constexpr int RPW = 4;  // rows per workgroup: four 16-lane groups
+  __shared__ float s_part[8][RPW];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the slot
+  const int t = blockIdx.y;
+  const int units = a.units;
+  const int j = lane & 15, rr = lane >> 4;
+  const int row = (int)blockIdx.x * RPW + rr;
+  const int s = min(wave, a.top_k - 1);
+  const int sl = t * a.top_k + s;
+  const int e = a.ids[sl];
+  const bool valid = wave < a.top_k && e >= 0 && e < a.n_experts;
+  const int xr = a.x_per_slot ? sl : t;
+  const Act gx{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
+  XO xf[NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(j + 16 * q, units - 1), xf[q]);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t* wr = a.w + ((int64_t)(valid ? e : 0) * a.n_rows + min(row, a.n_rows - 1)) * a.row_bytes;
+  RawS<F> cur[NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q) load_unit_s(wr, min(j + 16 * q, units - 1), lane, cur[q]);
+  __builtin_amdgcn_sched_barrier(0);
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < NU; ++q) {
+    const int uraw = j + 16 * q;
+    const bool ok = uraw < units;
+    const int u = ok ? uraw : units - 1;
+    DecO<F> dec;
+    decode_own(cur[q], u, lane & 1, ok, dec);
+    const int dv = own_pass<F>(own_first(dec, xf[q].f));
+    acc = own_apply(dec, own_second(dec, xf[q].s, dv), xf[q].p, acc);
+  }
+  const float v = lane_group_sum<16>(acc);
+  if (j == 0) s_part[wave][rr] = valid ? v : 0.f;
+  __syncthreads();
+  if (threadIdx.x < RPW) {
+    const int r2 = (int)blockIdx.x * RPW + threadIdx.x;
+    float sum = 0.f;
+    for (int s2 = 0; s2 < a.top_k; ++s2) {
+      const int e2 = a.ids[t * a.top_k + s2];
+      if (e2 >= 0 && e2 < a.n_experts) sum += a.rw[t * a.top_k + s2] * s_part[s2][threadIdx.x];
+    }
+    if (r2 < a.n_rows) a.y[(int64_t)t * a.n_rows + r2] = sum;
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    int drop = 0;
+    for (int i = 0; i < a.n_tok * a.top_k; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
+    a.err[0] = drop;
+  }
+}
+
 // Lanes per row and units per lane for a row of `units` units.
 static int moe_lpr(int units) { return units <= 64 ? 16 : 64; }
 static int moe_nu(int units) {
@@ -1036,9 +1101,27 @@ hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st) {
   }
 }
 
+static int g_moe_comb = 0;  // tuning: 0 automatic, 1 one row per wave, 2 16-lane row groups
+void set_moe_comb(int v) { g_moe_comb = v; }
+
+template <int F>
+static hipError_t run_comb16(const MoeLaunch& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n_rows + 3) / 4), (unsigned)a.n_tok);
+  switch ((a.units + 15) / 16) {
+    case 1: hipLaunchKernelGGL((k_moe_comb16<F, 1>), grid, dim3(512), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_moe_comb16<F, 2>), grid, dim3(512), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_moe_comb16<F, 3>), grid, dim3(512), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_moe_comb16<F, 4>), grid, dim3(512), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int F, int NU, int R>
 static hipError_t run_moe_flat(const MoeLaunch& a, hipStream_t st) {
   constexpr int WPB = 4;
+  if (a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1 && a.units <= 64 && g_moe_comb != 1)
+    return run_comb16<F>(a, st);
   if constexpr (NU <= 2) {
     if (a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1) {
       // one token, route-weighted, top_k <= 8: the combine folded into the

@@ -184,18 +184,22 @@ def test_moe_other_formats(fmt, moe_kernel):
 
 
 @pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS], ids=["q8_0", "q4_K", "iq4_xs"])
-@pytest.mark.parametrize("kernel", [0, 3], ids=["auto", "flat"])
-def test_moe_one_token_weighted(fmt, kernel):
-    """One token with route weights: the flat kernel with the combine folded
-    in (top_k <= 8, rows of up to two units per lane), on every MoE format,
-    for rows of one and two units per lane (K = 512, 1536, 4096), one
-    activation row per token and per slot, top_k 1 and 8, with a dropped id
-    and a duplicate."""
+@pytest.mark.parametrize("kernel,comb", [(0, 0), (3, 1), (3, 2)], ids=["auto", "flat-row-per-wave", "flat-16-lane"])
+def test_moe_one_token_weighted(fmt, kernel, comb):
+    """One token with route weights: the few-slot kernels with the combine
+    folded in (top_k <= 8) -- one row per wave (rows of up to two units per
+    lane) and 16-lane row groups (rows of up to 64 blocks) -- on every MoE
+    format, for rows of 16 to 128 blocks (K = 512 .. 4096; Q8_0 also 33
+    blocks, a ragged last lane group), a row count that leaves the last
+    workgroup's rows partly empty, one activation row per token and per slot,
+    top_k 1 and 8, with a dropped id and a duplicate."""
     qmv = need_gpu()
-    e_n, n = 9, 72
+    e_n, n = 9, 70
     qmv.set_tuning("moe_kernel", kernel)
+    qmv.set_tuning("moe_comb", comb)
+    ks = (512, 1056, 1536, 2048, 4096) if fmt == synth.Q8_0 else (512, 1536, 2048, 4096)
     try:
-        for k in (512, 1536, 4096):
+        for k in ks:
             w = synth.make_weights(fmt, e_n * n, k, f"moe1/{fmt}/{k}").data
             wd = to_dev(w)
             for ids in (np.array([[4]], np.int32), np.array([[7]], np.int32),
@@ -217,3 +221,4 @@ def test_moe_one_token_weighted(fmt, kernel):
                     assert int(ws[:4].view(torch.int32)[0]) == dropped
     finally:
         qmv.set_tuning("moe_kernel", 0)
+        qmv.set_tuning("moe_comb", 0)
