@@ -335,7 +335,8 @@ qmv_status qmv_moe_matvec(qmv_type type, const void* w, int64_t n_experts, int64
  * By default two launches: the routed matvec and qmv_swiglu_quantize (gu,
  * or without it the workspace's per-slot area, carries the gate+up
  * outputs), which measured faster than one.  qmv_set_tuning("ffn_fuse", 1)
- * selects one launch up to 16 tokens on rows of at most 4096 weights: a
+ * selects one launch up to 16 tokens on rows of at most 4096 weights (with
+ * the automatic or few-slot MoE kernel, see "moe_kernel"): a
  * few-slot kernel whose workgroup holds 32 gate rows and the matching 32 up
  * rows and makes that block of h from them in LDS.
  * n_ff % 32 == 0; other limits and errors as for qmv_moe_matvec.
@@ -461,10 +462,11 @@ qmv_status qmv_stream_read(const void* p, int64_t bytes, uint32_t* sink, void* s
  *               vector-ALU kernel when its staged rows do not fit in LDS),
  *               3 the few-slot flat kernel (each slot's expert rows
  *               streamed without grouping slots by expert);
- *   "moe_comb": 0 automatic (default), 1 one row per wave, 2 16-lane row
- *               groups: the kernel qmv_moe_matvec runs for one
- *               route-weighted token with top_k <= 8 (the second on rows of
- *               at most 64 blocks);
+ *   "moe_row16": 0 (default) the few-slot MoE kernels hold short rows in
+ *               16-lane groups (one activation row per slot and rows of
+ *               fewer than 64 blocks; one route-weighted token with
+ *               top_k <= 8 and rows of at most 64), 1 one row or more per
+ *               wave throughout;
  *   "ffn_fuse": -1 automatic (default: two launches), 0 two launches, 1
  *               one launch where it applies, for qmv_moe_gate_up_swiglu.
  * The environment variables QMV_SPLITK, QMV_VARIANT and QMV_MOE_KERNEL set

@@ -465,9 +465,9 @@ QMV_API qmv_status qmv_set_tuning(const char* key, int64_t value) {
     set_moe_kernel(static_cast<int>(value));
     return QMV_OK;
   }
-  if (!std::strcmp(key, "moe_comb")) {
-    if (value < 0 || value > 2) return QMV_ERR_INVALID_ARG;
-    set_moe_comb(static_cast<int>(value));
+  if (!std::strcmp(key, "moe_row16")) {
+    if (value < 0 || value > 1) return QMV_ERR_INVALID_ARG;
+    set_moe_row16(static_cast<int>(value));
     return QMV_OK;
   }
   if (!std::strcmp(key, "ffn_fuse")) {
@@ -942,7 +942,10 @@ QMV_API qmv_status qmv_moe_gate_up_swiglu(qmv_type type, const void* w, int64_t 
   // cost more than the second launch.  (Counting a block's 16 waves on a
   // device-scope arrival counter instead, in the 256-thread kernel, was
   // slower still: 52.2 / 129.8 / 261.5 us.)
-  const bool fused = g_ffn_fuse.load() == 1 && k / 32 <= 128 && n_tok <= 16;
+  // (only where the routed matvec runs the few-slot kernel, whose sums the
+  // one-launch kernel reproduces bit for bit)
+  const bool fused = g_ffn_fuse.load() == 1 && k / 32 <= 128 && n_tok <= 16 &&
+                     (moe_kernel() == 0 || moe_kernel() == 3);
   if (fused) {
     MoeLaunch a{};
     a.fmt = type;

@@ -292,9 +292,9 @@ hipError_t launch_moe_gate_up_swiglu(const MoeLaunch& a, hipStream_t st);
 hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st);
 // Tuning: MoE kernel (0 automatic, 1 vector-ALU, 2 matrix-core).
 void set_moe_kernel(int v);
-// Tuning: the one-token route-weighted few-slot kernel (0 automatic, 1 one
-// row per wave, 2 16-lane row groups where rows have at most 64 units).
-void set_moe_comb(int v);
+// Tuning: the few-slot MoE kernels' 16-lane row groups on short rows (0, the
+// default) or one row per wave throughout (1).
+void set_moe_row16(int v);
 int moe_kernel();
 
 }  // namespace qmv

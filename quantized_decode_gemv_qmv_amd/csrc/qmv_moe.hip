@@ -532,16 +532,25 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeLaunch a) {
 // k_moe writes them (to y, or to the workspace for the combine); a dropped
 // slot's row is zero.
 
-template <int F, int NU, int R, int WPB>
+//
+// LPR = 16 (rows of fewer than 64 units with one activation row per slot,
+// the down projection's 48): a wave
+// takes four rows, one per 16-lane group, NU units per lane, so that every
+// lane carries units (with one unit per lane a 48-unit row left 16 lanes
+// idle); R is 1 and each group's sum is a 16-lane DPP reduction.
+template <int F, int NU, int R, int WPB, int LPR = 64>
 __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
+  static_assert(LPR == 64 || (LPR == 16 && R == 1), "16-lane groups hold one row each");
+  constexpr int RPW = LPR == 64 ? R : 4;  // rows per wave
   const int lane = threadIdx.x & 63;
+  const int lu = LPR == 64 ? lane : (lane & 15);  // lane index inside its row group
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = blockIdx.y;
   const int n_slots = a.n_tok * a.top_k;
   const int e = a.ids[slot];
   const bool valid = e >= 0 && e < a.n_experts;
   const int units = a.units;
-  const int row0 = (blockIdx.x * WPB + wave) * R;
+  const int row0 = (blockIdx.x * WPB + wave) * RPW + (LPR == 64 ? 0 : (lane >> 4));
   const int xr = a.x_per_slot ? slot : slot / a.top_k;
   const Act gx{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
   // slots i with the same expert in chunk c (64 ids per chunk), one flag
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
   }
   XO xf[NU];
 #pragma unroll
-  for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lane + 64 * q, units - 1), xf[q]);
+  for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(lu + LPR * q, units - 1), xf[q]);
   __builtin_amdgcn_sched_barrier(0);
   const uint8_t* wr[R];
 #pragma unroll
@@ -569,7 +578,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
 #pragma unroll
   for (int q = 0; q < NU; ++q)
 #pragma unroll
-    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lu + LPR * q, units - 1), lane, cur[r][q]);
   __builtin_amdgcn_sched_barrier(0);
   float* out = a.rw == nullptr ? a.y : a.part;
   // one slot: the rows' sums against activation fragments f, stored at slot s
@@ -579,7 +588,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
-      const int uraw = lane + 64 * q;
+      const int uraw = lu + LPR * q;
       const bool ok = uraw < units;
       const int u = ok ? uraw : units - 1;
 #pragma unroll
@@ -590,13 +599,18 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
         acc[r] = own_apply(dec, own_second(dec, f[q].s, dv), f[q].p, acc[r]);
       }
     }
-    float outv = 0.f;
+    if constexpr (LPR == 16) {
+      const float sv = lane_group_sum<16>(acc[0]);
+      if (lu == 0 && row0 < a.n_rows) out[(int64_t)s * a.n_rows + row0] = valid ? sv : 0.f;
+    } else {
+      float outv = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float sv = wave_sum(acc[r]);
-      outv = lane == r ? sv : outv;
+      for (int r = 0; r < R; ++r) {
+        const float sv = wave_sum(acc[r]);
+        outv = lane == r ? sv : outv;
+      }
+      if (lane < R && row0 + lane < a.n_rows) out[(int64_t)s * a.n_rows + row0 + lane] = valid ? outv : 0.f;
     }
-    if (lane < R && row0 + lane < a.n_rows) out[(int64_t)s * a.n_rows + row0 + lane] = valid ? outv : 0.f;
   };
   apply(xf, slot);
   if (valid) {
@@ -621,7 +635,7 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
         const int xr2 = a.x_per_slot ? s2 : s2 / a.top_k;
         XO f2[NU];
 #pragma unroll
-        for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr2, min(lane + 64 * q, units - 1), f2[q]);
+        for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr2, min(lu + LPR * q, units - 1), f2[q]);
         apply(f2, s2);
       }
     }
@@ -1101,8 +1115,8 @@ hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st) {
   }
 }
 
-static int g_moe_comb = 0;  // tuning: 0 automatic, 1 one row per wave, 2 16-lane row groups
-void set_moe_comb(int v) { g_moe_comb = v; }
+static int g_moe_row16 = 0;  // tuning: 0 16-lane row groups on short rows, 1 never
+void set_moe_row16(int v) { g_moe_row16 = v; }
 
 template <int F>
 static hipError_t run_comb16(const MoeLaunch& a, hipStream_t st) {
@@ -1120,7 +1134,7 @@ static hipError_t run_comb16(const MoeLaunch& a, hipStream_t st) {
 template <int F, int NU, int R>
 static hipError_t run_moe_flat(const MoeLaunch& a, hipStream_t st) {
   constexpr int WPB = 4;
-  if (a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1 && a.units <= 64 && g_moe_comb != 1)
+  if (a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1 && a.units <= 64 && g_moe_row16 == 0)
     return run_comb16<F>(a, st);
   if constexpr (NU <= 2) {
     if (a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1) {
@@ -1150,9 +1164,36 @@ static hipError_t run_moe_flat(const MoeLaunch& a, hipStream_t st) {
 // tokens (measured: 4096 x 1536 at six tokens 42.0 -> 39.4 us; 3072 x 4096
 // at one token 12.1 against 12.4 us with four rows, at 16 tokens 144.5 ->
 // 138.9 us).
+// The per-slot grid with 16-lane row groups: rows of fewer than 64 units
+// (the down projection's inputs, one activation row per slot).
+template <int F, int NU16>
+static hipError_t run_moe_flat16(const MoeLaunch& a, hipStream_t st) {
+  constexpr int WPB = 4;
+  const int64_t slots = (int64_t)a.n_tok * a.top_k;
+  const unsigned gx = (unsigned)((a.n_rows + 4 * WPB - 1) / (4 * WPB));
+  hipLaunchKernelGGL((k_moe_flat<F, NU16, 1, WPB, 16>), dim3(gx, (unsigned)slots), dim3(64 * WPB), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.rw == nullptr) return e;
+  const int64_t outs = (int64_t)a.n_tok * a.n_rows;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int F>
 static hipError_t run_moe_flat_fmt(const MoeLaunch& a, hipStream_t st) {
   const int nu = (a.units + 63) / 64;
+  // 16-lane row groups for the per-slot inputs of a down projection; a
+  // gate+up (one activation row per token) keeps the 64-lane rows that the
+  // one-launch FFN kernel reduces the same way, so that its sums are
+  // bit-identical to this path's
+  if (a.units < 64 && a.x_per_slot && g_moe_row16 == 0 && !(a.rw != nullptr && a.top_k <= 8 && a.n_tok == 1)) {
+    switch ((a.units + 15) / 16) {
+      case 1: return run_moe_flat16<F, 1>(a, st);
+      case 2: return run_moe_flat16<F, 2>(a, st);
+      case 3: return run_moe_flat16<F, 3>(a, st);
+      default: return run_moe_flat16<F, 4>(a, st);
+    }
+  }
   switch (nu) {
     case 1: return run_moe_flat<F, 1, 4>(a, st);
     case 2: return a.n_tok >= 6 ? run_moe_flat<F, 2, 4>(a, st) : run_moe_flat<F, 2, 2>(a, st);

@@ -283,8 +283,8 @@ def test_tuning_switches(L):
     assert L.qmv_set_tuning(b"splitk", -1) == OK
     assert L.qmv_set_tuning(b"moe_kernel", 4) == INVALID
     assert L.qmv_set_tuning(b"moe_kernel", 0) == OK
-    assert L.qmv_set_tuning(b"moe_comb", 3) == INVALID
-    assert L.qmv_set_tuning(b"moe_comb", 0) == OK
+    assert L.qmv_set_tuning(b"moe_row16", 2) == INVALID
+    assert L.qmv_set_tuning(b"moe_row16", 0) == OK
     for bad in (-2, 1, 33):
         assert L.qmv_set_tuning(b"mx_slices", bad) == INVALID
     assert L.qmv_set_tuning(b"mx_slices", -1) == OK

@@ -184,8 +184,8 @@ def test_moe_other_formats(fmt, moe_kernel):
 
 
 @pytest.mark.parametrize("fmt", [synth.Q8_0, synth.Q4_K, synth.IQ4_XS], ids=["q8_0", "q4_K", "iq4_xs"])
-@pytest.mark.parametrize("kernel,comb", [(0, 0), (3, 1), (3, 2)], ids=["auto", "flat-row-per-wave", "flat-16-lane"])
-def test_moe_one_token_weighted(fmt, kernel, comb):
+@pytest.mark.parametrize("kernel,row16", [(0, 0), (3, 1), (3, 0)], ids=["auto", "flat-row-per-wave", "flat-16-lane"])
+def test_moe_one_token_weighted(fmt, kernel, row16):
     """One token with route weights: the few-slot kernels with the combine
     folded in (top_k <= 8) -- one row per wave (rows of up to two units per
     lane) and 16-lane row groups (rows of up to 64 blocks) -- on every MoE
@@ -196,7 +196,7 @@ def test_moe_one_token_weighted(fmt, kernel, comb):
     qmv = need_gpu()
     e_n, n = 9, 70
     qmv.set_tuning("moe_kernel", kernel)
-    qmv.set_tuning("moe_comb", comb)
+    qmv.set_tuning("moe_row16", row16)
     ks = (512, 1056, 1536, 2048, 4096) if fmt == synth.Q8_0 else (512, 1536, 2048, 4096)
     try:
         for k in ks:
@@ -221,4 +221,4 @@ def test_moe_one_token_weighted(fmt, kernel, comb):
                     assert int(ws[:4].view(torch.int32)[0]) == dropped
     finally:
         qmv.set_tuning("moe_kernel", 0)
-        qmv.set_tuning("moe_comb", 0)
+        qmv.set_tuning("moe_row16", 0)
