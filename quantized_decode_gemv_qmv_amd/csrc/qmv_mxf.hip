@@ -33,15 +33,24 @@
 
 namespace qmv {
 
+// Token rows of the LDS activation copy: the products' rows, except q4_K
+// up to four tokens (four of its eight).
+constexpr int mxf_staged_rows(int f, int tm) {
+  return f == FQ4_K ? (tm <= 4 ? 4 : (tm + 7) / 8 * 8) : (tm + 3) / 4 * 4;
+}
+
 template <int F, int TM, int WPB, int SBW, bool SPLIT, bool DOTS>
 __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
   constexpr int TG = mx_tg<F>();
   constexpr int NG = (TM + TG - 1) / TG;  // token groups
-  constexpr int TMP = NG * TG;            // staged token rows
+  constexpr int TMP = NG * TG;            // token rows of the products
   constexpr int NT = 64 * WPB;
   constexpr bool Q4K = F == FQ4_K;
   constexpr bool P2 = Q4K;  // two blocks per product (q4_K), else four
-  constexpr int BS = TMP * 32 + 16;
+  // staged token rows: a q4_K product has eight, but up to four tokens only
+  // four are staged and the other four activation rows read the zero bytes
+  constexpr int TMS = mxf_staged_rows(F, TM);
+  constexpr int BS = TMS * 32 + 16;
   // staged 16-byte quant pieces and scale entries per thread whose loads go
   // out ahead of the weights (larger slices load the rest afterwards)
   constexpr int SQ = WPB >= 16 ? 4 : 8;
@@ -69,13 +78,13 @@ __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
   uint8_t* xl = s_mem;
   const int zoff = kc * BS;  // 16 zero bytes
   float* dl = reinterpret_cast<float*>(s_mem + zoff + 16);
-  float* sl = dl + kc * TMP;
+  float* sl = dl + kc * TMS;
   const float* gd = reinterpret_cast<const float*>(a.xq + a.off_d);
   const int32_t* gs = reinterpret_cast<const int32_t*>(a.xq + a.off_s);
 
   // ---- staging loads: the slice's quants of every token row (rows past the
   // call's tokens repeat its last token and are never stored) and the scales
-  const int nq = 2 * units, total = TMP * nq;
+  const int nq = 2 * units, total = TMS * nq;
   const FastDiv dq(nq);
   auto piece = [&](int idx) -> const uint8_t* {
     const int t = dq.div(idx), pc = idx - t * nq;
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
   for (int i = 0; i < SQ; ++i) sv[i] = ld16(piece(min((int)threadIdx.x + i * NT, total - 1)));
   // scale entries (t, b), read in token-major order (consecutive lanes on
   // consecutive blocks of one token: coalesced) and stored block-major
-  const int ns = kc * TMP;
+  const int ns = kc * TMS;
   const FastDiv dk(kc);
   auto sidx = [&](int idx) {
     const int t = dk.div(idx), b = idx - t * kc;
@@ -127,8 +136,8 @@ __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
   auto put_s = [&](int idx, float d, int sx) {
     const int t = dk.div(idx), b = idx - t * kc;
     const bool ok = b < units;  // staged blocks past the slice carry zero scales
-    dl[b * TMP + t] = ok ? d : 0.f;
-    if constexpr (Q4K) sl[b * TMP + t] = ok ? d * static_cast<float>(sx) : 0.f;
+    dl[b * TMS + t] = ok ? d : 0.f;
+    if constexpr (Q4K) sl[b * TMS + t] = ok ? d * static_cast<float>(sx) : 0.f;
   };
 #pragma unroll
   for (int i = 0; i < SD; ++i) {
@@ -149,12 +158,14 @@ __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
   const int m = lane & 15;
   const int jA = P2 ? (m >> 3) : (m >> 2);
   const int tA = P2 ? (m & 7) : (m & 3);
-  const bool vA = P2 ? (jA == (s >> 1)) : (jA == s);
+  // (activation rows past the staged ones take the zero bytes; the lanes of
+  // their outputs read the scales of the first tokens, and are never stored)
+  const bool vA = (P2 ? (jA == (s >> 1)) : (jA == s)) && tA < TMS;
   constexpr int aMu = P2 ? BS : 16;
-  constexpr int oMu = P2 ? TMP * 4 : 0;
+  constexpr int oMu = P2 ? TMS * 4 : 0;
   const int aLane = (P2 ? 2 * jA : jA) * BS + tA * 32 + (P2 ? 16 * (s & 1) : 0);
   const int oTok = P2 ? 4 * (s & 1) : 0;
-  const int oLane = (P2 ? 2 * (s >> 1) : s) * TMP * 4 + oTok * 4;
+  const int oLane = (P2 ? 2 * (s >> 1) : s) * TMS * 4 + (oTok < TMS ? oTok : 0) * 4;
 
   float acc[NG][4];
 #pragma unroll
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
       mx_decode(wv[j], p, s, u0, units, dec);
       const int bl = u0 + 4 * p;  // first block of the span
       const int ab = vA ? bl * BS + aLane : zoff;
-      const int ob = bl * TMP * 4 + oLane;
+      const int ob = bl * TMS * 4 + oLane;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g > 0) __builtin_amdgcn_sched_barrier(0);
@@ -314,7 +325,7 @@ int mxf_plan(int fmt, int n_tok, int wpb, int sbw, int units, int n_rows, int cu
   const int tg = fmt == FQ4_K ? 8 : 4;
   const int tm = n_tok <= 4 ? 4 : n_tok <= 8 ? 8 : 16;
   const int tmp = (tm + tg - 1) / tg * tg;
-  const int per_unit = mx_per_unit(fmt, tmp);
+  const int per_unit = mx_per_unit(fmt, mxf_staged_rows(fmt, tm));
   const int64_t red = (int64_t)wpb * tmp * 16 * 4;
   const int64_t tiles = (n_rows + 15) / 16;
   // slices: the fewest whose LDS copy fits the budget (or the forced count),
