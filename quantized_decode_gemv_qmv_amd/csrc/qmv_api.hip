@@ -212,7 +212,12 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   } else if (type == QMV_Q8G128 && n_tok == 2 && rpc >= 128) {
     name = "st_w4_r1_u3";  // the head at two tokens: 144.0 / 142.0 us against 151.0 / 150.4 (two boxes)
   } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2)) {
-    name = nu <= 2 ? (type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_g")
+    // (q4_K 14336 x 4096 at 1 / 2 tokens, medians of five: two rows per wave
+    // with the activations staged in LDS 7.75 / 8.43 us, with fragments from
+    // global memory 7.80 / 8.97)
+    name = nu <= 2 ? (type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l"
+                      : type == QMV_Q4_K                      ? "fl_w4_r2_u2_l"
+                                                              : "fl_w4_r2_u2_g")
            : nu <= 3 ? "fl_w16_r1_u3_l"
            : nu <= 7 ? "fl_w8_r1_u7_l"
                      : "fl_w4_r1_u4_g";

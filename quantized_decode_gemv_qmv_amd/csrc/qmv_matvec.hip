@@ -1034,6 +1034,11 @@ static hipError_t run_mv_variant(const MatvecLaunch& a, hipStream_t st) {
     case 15: return run_flat<F, TM, 1, 3, 16, true>(a, st);
     case 16: return run_flat<F, TM, 1, 7, 8, true>(a, st);
     case 17: return run_flat<F, TM, 2, 2, 16, true>(a, st);
+    case 49: return run_flat<F, TM, 2, 2, 4, true>(a, st);
+    case 50: return run_flat<F, TM, 4, 2, 4, false>(a, st);
+    case 51: return run_flat<F, TM, 4, 2, 4, true>(a, st);
+    case 52: return run_flat<F, TM, 2, 2, 8, true>(a, st);
+    case 53: return run_flat<F, TM, 2, 2, 2, false>(a, st);
     case 18: return run_mt<F, TM, 2, 1, 8, 2>(a, st);
     case 19: return run_mt<F, TM, 2, 1, 8, 4>(a, st);
     case 20: return run_mt<F, TM, 4, 1, 8, 2>(a, st);

@@ -109,6 +109,11 @@ __global__ __launch_bounds__(64 * WPB) void k_mxf(StreamArgs a) {
     dv[i] = gd[gi];
     iv[i] = Q4K ? gs[gi] : 0;
   }
+  // The activations are read by every workgroup from a few kilobytes, which
+  // sit on a few memory channels: requested behind the weights of the
+  // workgroups already running they queue behind that flood.  So the staging
+  // loads complete before this workgroup requests a weight byte.
+  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- every weight load of the wave (clamped past the end: unconditional)

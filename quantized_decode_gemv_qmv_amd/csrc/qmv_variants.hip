@@ -36,6 +36,9 @@ const Variant kVariants[] = {
     {6, 64, 1, 2, 16, 16, 0, "lk_w16_r1_u2"}, {6, 64, 1, 4, 8, 8, 0, "lk_w8_r1_u4"},
     {6, 64, 1, 8, 4, 4, 0, "lk_w4_r1_u8"},    {6, 64, 1, 2, 4, 4, 0, "lk_w4_r1_u2"},
     {6, 64, 2, 2, 16, 16, 0, "lk_w16_r2_u2"},
+    {2, 64, 2, 2, 4, 1, 1, "fl_w4_r2_u2_l"},  {2, 64, 4, 2, 4, 1, 0, "fl_w4_r4_u2_g"},
+    {2, 64, 4, 2, 4, 1, 1, "fl_w4_r4_u2_l"},  {2, 64, 2, 2, 8, 1, 1, "fl_w8_r2_u2_l"},
+    {2, 64, 2, 2, 2, 1, 0, "fl_w2_r2_u2_g"},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

@@ -235,7 +235,8 @@ def test_matvec_plan():
 # library describes an MI355X when no device is present).  (type, rows, K,
 # tokens, with workspace) -> (variant, slices)
 PLANS = [
-    ((1, 14336, 4096, 1, False), ("fl_w4_r2_u2_g", 1)),
+    ((1, 14336, 4096, 1, False), ("fl_w4_r2_u2_l", 1)),
+    ((1, 14336, 4096, 2, False), ("fl_w4_r2_u2_l", 1)),
     ((1, 14336, 4096, 16, False), ("mx_w8_k4_r4", 1)),
     ((1, 14336, 4096, 8, True), ("mf_w8_b4", 1)),          # flat matrix-core kernel, one pass
     ((1, 14336, 4096, 3, False), ("mf_w8_b4", 1)),
