@@ -211,22 +211,30 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
                                                                 : "mt_r2_w8_k4";
   } else if (type == QMV_Q8G128 && n_tok == 2 && rpc >= 128) {
     name = "st_w4_r1_u3";  // the head at two tokens: 144.0 / 142.0 us against 151.0 / 150.4 (two boxes)
-  } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2)) {
-    // (q4_K 14336 x 4096 at 1 / 2 tokens, medians of five: two rows per wave
-    // with the activations staged in LDS 7.75 / 8.43 us, with fragments from
-    // global memory 7.80 / 8.97)
-    name = nu <= 2 ? (type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l"
-                      : type == QMV_Q4_K                      ? "fl_w4_r2_u2_l"
-                                                              : "fl_w4_r2_u2_g")
-           : nu <= 3 ? "fl_w16_r1_u3_l"
-           : nu <= 7 ? "fl_w8_r1_u7_l"
-                     : "fl_w4_r1_u4_g";
+  } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2) ||
+             (type == QMV_Q4_K && n_tok <= 4 && nu <= 2 && n_rows >= 8 * (int64_t)cus)) {
+    // q4_K 14336 x 4096 at 1 / 2 / 3 / 4 tokens: two rows per wave with the
+    // activations staged in LDS 7.75 / 8.43 / 10.34 / 11.07 us, with
+    // fragments from global memory 7.80 / 8.97 / 12.51 / 12.57, the flat
+    // matrix-core kernel 11.9 at 3 and 4 (medians; at 5..8 tokens the flat
+    // kernel's eight-token instantiation takes 16.5 us and more).  Q8_0
+    // 4096 x 4096 at four tokens: eight waves of two rows 6.07 against 6.39
+    // for one row per wave.
+    if (nu <= 2 && type == QMV_Q8_0 && n_tok == 4 && n_rows <= 16 * (int64_t)cus)
+      name = "fl_w8_r2_u2_l";
+    else if (nu <= 2)
+      name = type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l"
+             : type == QMV_Q4_K                      ? "fl_w4_r2_u2_l"
+                                                     : "fl_w4_r2_u2_g";
+    else
+      name = nu <= 3 ? "fl_w16_r1_u3_l" : nu <= 7 ? "fl_w8_r1_u7_l" : "fl_w4_r1_u4_g";
   } else if (type == QMV_Q4_K && n_tok <= 8 && n_rows >= 8 * (int64_t)cus &&
              units * mx_per_unit(FQ4_K, 8) <= 140 * 1024) {
-    // q4_K at 3..8 tokens on many rows: the flat matrix-core kernel, one
-    // pass with every weight load of a wave issued at once (14336 x 4096:
-    // 12.0 / 12.1 / 12.2 us at 3 / 4 / 8 tokens against 12.4 (multi-token
-    // vector kernel) / 12.4 / 14.2 us (persistent matrix-core kernel))
+    // q4_K at 5..8 tokens on many rows (and 3, 4 on long rows): the flat
+    // matrix-core kernel, one pass with every weight load of a wave issued
+    // at once (14336 x 4096: 12.1 / 12.2 us at 5 / 8 tokens against 16.5 /
+    // 17.8 for the flat vector kernel and 14.2 at 8 for the persistent
+    // matrix-core kernel)
     name = "mf_w8_b4";
   } else if (type == QMV_Q4_K && n_tok == 3 && nu <= 2) {
     name = "fl_w4_r1_u2_l";  // measured 11.25 against 11.59 us for the multi-token kernel

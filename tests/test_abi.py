@@ -239,7 +239,10 @@ PLANS = [
     ((1, 14336, 4096, 2, False), ("fl_w4_r2_u2_l", 1)),
     ((1, 14336, 4096, 16, False), ("mx_w8_k4_r4", 1)),
     ((1, 14336, 4096, 8, True), ("mf_w8_b4", 1)),          # flat matrix-core kernel, one pass
-    ((1, 14336, 4096, 3, False), ("mf_w8_b4", 1)),
+    ((1, 14336, 4096, 3, False), ("fl_w4_r2_u2_l", 1)),
+    ((1, 14336, 4096, 4, True), ("fl_w4_r2_u2_l", 1)),
+    ((1, 14336, 4096, 5, True), ("mf_w8_b4", 1)),
+    ((0, 4096, 4096, 4, True), ("fl_w8_r2_u2_l", 1)),
     ((2, 4096, 14336, 1, True), ("fl_w8_r1_u7_l", 1)),
     ((2, 4096, 14336, 16, True), ("mx_w16_k4_r2", 4)),   # split over workgroups with a workspace
     ((2, 4096, 14336, 16, False), ("mx_w8_k8_r4", 1)),
