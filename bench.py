@@ -117,6 +117,7 @@ class Ring:
         xs = make_x(8 * t, k, f"{name}/x").reshape(8, t, k)
         self.x = [torch.from_numpy(xs[i]).cuda() for i in range(8)]
         self.xq = torch.empty(qmv.act_bytes(t, k), dtype=torch.uint8, device="cuda")
+        qmv.quantize_act(self.x[0], out=self.xq)  # the matvec alone is timed on real activations too
         self.y = [torch.empty((t, n), dtype=torch.float32, device="cuda") for _ in range(mats)]
         wsb = qmv.matvec_workspace_bytes(fmt, n, k, t) if mats == 1 else 0
         self.ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda") if wsb else None
@@ -177,6 +178,8 @@ class MoeRing:
         self.h = [torch.from_numpy(hs[i]).cuda() for i in range(8)]
         self.xq = torch.empty(qmv.act_bytes(t, kg), dtype=torch.uint8, device="cuda")
         self.hq = torch.empty(qmv.act_bytes(t * self.top_k, kd), dtype=torch.uint8, device="cuda")
+        qmv.quantize_act(self.x[0], out=self.xq)  # projections timed alone read real activations
+        qmv.quantize_act(self.h[0], out=self.hq)
         self.y_gu = torch.empty((t, self.top_k, ng), dtype=torch.float32, device="cuda")
         self.y_dn = torch.empty((t, nd), dtype=torch.float32, device="cuda")
         self.ws_gu = torch.zeros(qmv.moe_workspace_bytes(2, e, ng, kg, t, self.top_k),
