@@ -1194,9 +1194,13 @@ static hipError_t run_moe_flat_fmt(const MoeLaunch& a, hipStream_t st) {
       default: return run_moe_flat16<F, 4>(a, st);
     }
   }
+  // rows of up to 128 blocks: four rows per wave (the 128-expert gate+up,
+  // 3072 x 4096 per expert, at 1 / 2 / 4 tokens: 13.99 / 24.19 / 44.39 us with
+  // two rows per wave, whose grid of 12288 waves at one token does not fit
+  // the device at once, against 13.49 / 23.22 / 40.25 with four)
   switch (nu) {
     case 1: return run_moe_flat<F, 1, 4>(a, st);
-    case 2: return a.n_tok >= 6 ? run_moe_flat<F, 2, 4>(a, st) : run_moe_flat<F, 2, 2>(a, st);
+    case 2: return run_moe_flat<F, 2, 4>(a, st);
     case 3: return run_moe_flat<F, 3, 1>(a, st);
     case 4: return run_moe_flat<F, 4, 1>(a, st);
     default: return run_moe_flat<F, 8, 1>(a, st);
