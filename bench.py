@@ -661,7 +661,9 @@ def sweep_rows(torch, qmv, workload, tokens, reps=21):
 
 def moe_rows(torch, qmv, tokens, reps=5):
     """The MoE decode step (quantize x, routed gate+up, quantize h, routed
-    and route-weighted down) at each token count: median step time."""
+    and route-weighted down) at each token count: median step time; and the
+    FFN step (router + top-k, gate+up with SwiGLU and Q8 of its output, down
+    with the router's weights)."""
     rows = []
     for t in tokens:
         log(f"bench: MoE step T={t}")
@@ -670,13 +672,18 @@ def moe_rows(torch, qmv, tokens, reps=5):
         us = timed_replays(torch, lambda i: ring.step(qmv, i), per, reps)
         gu_us = timed_replays(torch, lambda i: ring.gate_up(qmv, i), per, reps)
         dn_us = timed_replays(torch, lambda i: ring.down(qmv, i), per, reps)
+        # the FFN step: router + top-k, gate+up with SwiGLU and Q8, down with the router's weights
+        ffn_us = timed_replays(torch, lambda i: ring.ffn_step(qmv, i), per, reps)
+        fb, fu = ring.ffn_bytes(qmv, per)
         u = ring.avg_bytes(per) / ring.bytes_per_expert
         b = ring.avg_bytes(per)
         rows.append({"workload": "MoE IQ4_XS 128 experts top-8, gate+up 3072x4096 + down 4096x1536", "tokens": t,
                      "avg_distinct_experts": round(u, 2), "weight_bytes_per_step": round(b),
                      "step_us": round(us, 3), "step_GBps": round(b / (us * 1e-6) / 1e9, 1),
                      "hbm_frac_step": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "gate_up_us": round(gu_us, 3), "down_us": round(dn_us, 3)})
+                     "gate_up_us": round(gu_us, 3), "down_us": round(dn_us, 3),
+                     "ffn_step_us": round(ffn_us, 3), "ffn_distinct_experts": round(fu, 2),
+                     "ffn_step_GBps": round(fb / (ffn_us * 1e-6) / 1e9, 1)})
         del ring
         torch.cuda.empty_cache()
     return rows
@@ -895,7 +902,7 @@ def main() -> int:
             sweep += sweep_rows(torch, qmv, wl, toks)
         for wl, toks in OTHER:
             others += sweep_rows(torch, qmv, wl, toks, reps=11)
-        moe = moe_rows(torch, qmv, (1, 64))
+        moe = moe_rows(torch, qmv, (1, 6, 16, 64))
 
     cpu = None
     if not args.no_cpu:
