@@ -321,37 +321,60 @@ constexpr uint32_t pk4(int a, int b, int c, int d) {
   return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
          ((uint32_t)(uint8_t)d << 24);
 }
-constexpr uint32_t IQ4_CB0 = pk4(-127, -104, -83, -65);
-constexpr uint32_t IQ4_CB1 = pk4(-49, -35, -22, -10);
-constexpr uint32_t IQ4_CB2 = pk4(1, 13, 25, 38);
-constexpr uint32_t IQ4_CB3 = pk4(53, 69, 89, 113);
+constexpr int8_t IQ4_CB[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
 
 // Codebook lookup of 4-bit indices (one per byte, 0..15) -> int8 values, four
-// at a time with three byte permutes: entries 0..7 and 8..15 are looked up by
-// the low three index bits, then bit 3 picks between the two results byte by
-// byte (the pick selector is byte i + 4 * bit 3 of index i).
-// The identity byte selector 0x03020100 in a vector register.  gfx9 VOP3
-// instructions take no literal operand, so with the constant in a register the
-// mask-and-or of each pick selector is one v_and_or_b32 (mask from a scalar
-// register) instead of an and and an or with literals.  The asm only hides the
-// value from constant folding; it has no side effect and is hoisted.
-__device__ __forceinline__ uint32_t perm_identity() {
-  uint32_t c;
-  asm("v_mov_b32 %0, 0x3020100" : "=v"(c));
-  return c;
+// at a time with two byte permutes and an xor.
+//
+// v_perm_b32 maps a selector byte s to byte s of its 8-byte table for s < 8,
+// and to a constant for s = 8..15: the sign of table byte 2 (s - 8) + 1
+// replicated over the byte (s = 8..11), 0x00 (s = 12) or 0xFF (s = 13..15).
+// An index i is looked up as s = i in table A and as s = i ^ 8 in table B.
+// Exactly one of the two selectors is below 8, so the other permute returns
+// one of those constants, which depends only on i and on the sign bits of the
+// other table; each table entry is the codebook value xor the constant that
+// the other table returns for the same index, so A ^ B is the value.  The
+// tables depend on each other only through those sign bits, along chains of
+// at most four entries, so four rounds of the assignment below reach its fixed
+// point; the static_assert checks all sixteen indices against the codebook.
+struct Iq4Tabs {
+  uint8_t a[8], b[8];
+};
+constexpr uint8_t perm_byte(const uint8_t (&t)[8], int s) {
+  return s < 8 ? t[s] : s >= 13 ? 0xFF : s == 12 ? 0x00 : (t[2 * (s - 8) + 1] & 0x80) ? 0xFF : 0x00;
+}
+constexpr Iq4Tabs iq4_tabs() {
+  Iq4Tabs t{};
+  for (int round = 0; round < 4; ++round)
+    for (int k = 0; k < 8; ++k) {
+      t.a[k] = static_cast<uint8_t>(IQ4_CB[k]) ^ perm_byte(t.b, k ^ 8);
+      t.b[k] = static_cast<uint8_t>(IQ4_CB[k + 8]) ^ perm_byte(t.a, k + 8);
+    }
+  return t;
+}
+constexpr Iq4Tabs IQ4_T = iq4_tabs();
+constexpr bool iq4_tabs_ok() {
+  for (int i = 0; i < 16; ++i)
+    if ((perm_byte(IQ4_T.a, i) ^ perm_byte(IQ4_T.b, i ^ 8)) != static_cast<uint8_t>(IQ4_CB[i])) return false;
+  return true;
+}
+static_assert(iq4_tabs_ok(), "two-table IQ4_XS codebook lookup");
+constexpr uint32_t tab_dw(const uint8_t (&t)[8], int h) {
+  return pk4((int8_t)t[4 * h], (int8_t)t[4 * h + 1], (int8_t)t[4 * h + 2], (int8_t)t[4 * h + 3]);
+}
+constexpr uint32_t IQ4_A0 = tab_dw(IQ4_T.a, 0), IQ4_A1 = tab_dw(IQ4_T.a, 1);
+constexpr uint32_t IQ4_B0 = tab_dw(IQ4_T.b, 0), IQ4_B1 = tab_dw(IQ4_T.b, 1);
+
+// Four indices (s: one per byte, 0..15) -> their four codebook values.
+__device__ __forceinline__ uint32_t iq4_lookup(uint32_t s) {
+  return __builtin_amdgcn_perm(IQ4_A1, IQ4_A0, s) ^ __builtin_amdgcn_perm(IQ4_B1, IQ4_B0, s ^ 0x08080808u);
 }
 
 // Both nibbles of four index bytes -> the codebook values of the low nibbles
 // (lo) and of the high nibbles (hi).
-__device__ __forceinline__ void iq4_lookup2(uint32_t v, uint32_t ident, uint32_t& lo, uint32_t& hi) {
-  const uint32_t s0 = v & 0x07070707u;
-  const uint32_t p0 = ((v >> 1) & 0x04040404u) | ident;
-  const uint32_t s1 = (v >> 4) & 0x07070707u;
-  const uint32_t p1 = ((v >> 5) & 0x04040404u) | ident;
-  lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(IQ4_CB3, IQ4_CB2, s0),
-                             __builtin_amdgcn_perm(IQ4_CB1, IQ4_CB0, s0), p0);
-  hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(IQ4_CB3, IQ4_CB2, s1),
-                             __builtin_amdgcn_perm(IQ4_CB1, IQ4_CB0, s1), p1);
+__device__ __forceinline__ void iq4_lookup2(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  lo = iq4_lookup(v & 0x0F0F0F0Fu);
+  hi = iq4_lookup((v >> 4) & 0x0F0F0F0Fu);
 }
 
 __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FIQ4_XS>& o) {
@@ -361,11 +384,10 @@ __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FI
   o.ls = static_cast<int>(lo4 | (hi2 << 4)) - 32;
   o.d = half_bits_to_float(r.hdr.x);
   o.dls = o.d * static_cast<float>(o.ls);
-  const uint32_t ident = perm_identity();
   const uint32_t v[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    iq4_lookup2(v[i], ident, o.q[i], o.q[4 + i]);
+    iq4_lookup2(v[i], o.q[i], o.q[4 + i]);
   }
 }
 

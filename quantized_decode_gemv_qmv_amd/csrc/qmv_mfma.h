@@ -103,12 +103,11 @@ __device__ __forceinline__ void mx_decode(const MxRaw<FQ4_K>& r, int p, int s, i
 }
 __device__ __forceinline__ void mx_decode(const MxRaw<FIQ4_XS>& r, int p, int s, int, int, MxDec& o) {
   const u32x4 q = r.q[p];
-  const uint32_t ident = perm_identity();
   uint32_t lo[4], hi[4];
-  iq4_lookup2(q.x, ident, lo[0], hi[0]);
-  iq4_lookup2(q.y, ident, lo[1], hi[1]);
-  iq4_lookup2(q.z, ident, lo[2], hi[2]);
-  iq4_lookup2(q.w, ident, lo[3], hi[3]);
+  iq4_lookup2(q.x, lo[0], hi[0]);
+  iq4_lookup2(q.y, lo[1], hi[1]);
+  iq4_lookup2(q.z, lo[2], hi[2]);
+  iq4_lookup2(q.w, lo[3], hi[3]);
   o.b[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
   o.b[1] = u32x4{hi[0], hi[1], hi[2], hi[3]};
   const int c = 4 * p + s;
