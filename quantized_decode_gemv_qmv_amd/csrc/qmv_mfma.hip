@@ -233,6 +233,9 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
   float acc[NG][4];
   // A operands: zero in the lanes that carry no data, which never load them
   u32x4 A[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  u32x4 Ag[NG][2];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) Ag[g][0] = Ag[g][1] = u32x4{0u, 0u, 0u, 0u};
 
   // One super-block of one row tile: the two spans' MFMAs and scale steps.
   auto compute = [&](const MxRaw<F>& cur, int sb, int c, int tile) {
@@ -245,6 +248,52 @@ __global__ __launch_bounds__(64 * WPB) void k_mx(StreamArgs a) {
       const int bl = 8 * (sb - c * ipc) + 4 * p;  // chunk-local first block of the span
       const int ab = (vA ? bl * BS + aLane : zoff);
       const int ob = bl * TMP * 4 + oLane;
+      if constexpr (!DOTS) {
+        // every token group's A operands, then all the group products, then
+        // the scale steps: the matrix cores work through the later groups'
+        // products while the vector ALU converts and scales the earlier ones
+        if (vA) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            Ag[g][0] = ld16(xl + ab + g * TG * 32);
+            Ag[g][1] = ld16(xl + ab + g * TG * 32 + aMu);
+          }
+        }
+        i32x4 dg[NG][2];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if constexpr (P2) {
+            dg[g][0] = mfma64(Ag[g][0], dec.b[0], i32x4{0, 0, 0, 0});
+            dg[g][1] = mfma64(Ag[g][1], dec.b[1], i32x4{0, 0, 0, 0});
+          } else {
+            dg[g][0] = mfma64(Ag[g][1], dec.b[1], mfma64(Ag[g][0], dec.b[0], i32x4{0, 0, 0, 0}));
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+#pragma unroll
+          for (int mu = 0; mu < (P2 ? 2 : 1); ++mu) {
+            const i32x4 dv = dg[g][mu];
+            const int o = ob + mu * oMu + g * TG * 4;
+            const f32x4 fx = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(dl) + o);
+            const float fxa[4] = {fx.x, fx.y, fx.z, fx.w};
+            if constexpr (Q4K) {
+              const f32x4 fs = *reinterpret_cast<const f32x4*>(reinterpret_cast<const uint8_t*>(sl) + o);
+              const float fsa[4] = {fs.x, fs.y, fs.z, fs.w};
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[mu] * fxa[r], acc[g][r]);
+                acc[g][r] = fmaf(-dec.wm[mu], fsa[r], acc[g][r]);
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[g][r] = fmaf(static_cast<float>(dv[r]), dec.dw[mu] * fxa[r], acc[g][r]);
+            }
+          }
+        }
+        continue;
+      }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g > 0) __builtin_amdgcn_sched_barrier(0);
