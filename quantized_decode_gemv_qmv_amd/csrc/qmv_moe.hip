@@ -489,6 +489,20 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_mx(MoeLaunch a) {
   }
 }
 
+// Slots whose expert id is out of range (dropped), counted by one whole wave:
+// 64 ids per step under a ballot, so that the ids are loaded together rather
+// than one round trip per slot.
+__device__ __forceinline__ int count_dropped(const MoeLaunch& a, int n_slots) {
+  const int lane = threadIdx.x & 63;
+  int drop = 0;
+  for (int i0 = 0; i0 < n_slots; i0 += 64) {
+    const int i = i0 + lane;
+    const int id = i < n_slots ? a.ids[i] : 0;
+    drop += __popcll(__ballot(i < n_slots && (id < 0 || id >= a.n_experts)));
+  }
+  return drop;
+}
+
 // y[t][n] = sum over valid slots s, in slot order, of rw[t][s] * part[t*top_k+s][n].
 // Every slot's id, route weight and output are loaded before any is used (a
 // slot's output row exists whether or not its id is valid), so the loads
@@ -640,10 +654,9 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat(MoeLaunch a) {
       }
     }
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    int drop = 0;
-    for (int i = 0; i < n_slots; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
-    a.err[0] = drop;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {  // wave 0, all lanes (slot 0 never exits early)
+    const int drop = count_dropped(a, n_slots);
+    if (threadIdx.x == 0) a.err[0] = drop;
   }
 }
 
@@ -778,10 +791,9 @@ __global__ __launch_bounds__(1024) void k_moe_gate_up_swiglu(MoeLaunch a) {
       }
     }
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    int drop = 0;
-    for (int i = 0; i < n_slots; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
-    a.err[0] = drop;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {  // wave 0, all lanes (slot 0 never exits early)
+    const int drop = count_dropped(a, n_slots);
+    if (threadIdx.x == 0) a.err[0] = drop;
   }
 }
 
@@ -897,10 +909,9 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat_comb(MoeLaunch a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) outv = lane == r ? sum[r] : outv;
   if (lane < R && row0 + lane < a.n_rows) a.y[(int64_t)t * a.n_rows + row0 + lane] = outv;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    int drop = 0;
-    for (int i = 0; i < a.n_tok * a.top_k; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
-    a.err[0] = drop;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {  // wave 0, all lanes
+    const int drop = count_dropped(a, a.n_tok * a.top_k);
+    if (threadIdx.x == 0) a.err[0] = drop;
   }
 }
 
@@ -918,6 +929,8 @@ template <int F, int NU>
 __global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
   constexpr int RPW = 4;  // rows per workgroup: four 16-lane groups
   __shared__ float s_part[8][RPW];
+  __shared__ float s_w[8];
+  __shared__ int s_ok[8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the slot
   const int t = blockIdx.y;
@@ -927,6 +940,7 @@ __global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
   const int s = min(wave, a.top_k - 1);
   const int sl = t * a.top_k + s;
   const int e = a.ids[sl];
+  const float rw = a.rw[sl];  // loaded beside the id: the final sum reads only LDS
   const bool valid = wave < a.top_k && e >= 0 && e < a.n_experts;
   const int xr = a.x_per_slot ? sl : t;
   const Act gx{a.x.qs, a.x.d, a.x.s, a.x.k, a.x.nb};
@@ -952,20 +966,21 @@ __global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
   }
   const float v = lane_group_sum<16>(acc);
   if (j == 0) s_part[wave][rr] = valid ? v : 0.f;
+  if (lane == 0) {
+    s_w[wave] = rw;
+    s_ok[wave] = valid;
+  }
   __syncthreads();
   if (threadIdx.x < RPW) {
     const int r2 = (int)blockIdx.x * RPW + threadIdx.x;
     float sum = 0.f;
-    for (int s2 = 0; s2 < a.top_k; ++s2) {
-      const int e2 = a.ids[t * a.top_k + s2];
-      if (e2 >= 0 && e2 < a.n_experts) sum += a.rw[t * a.top_k + s2] * s_part[s2][threadIdx.x];
-    }
+    for (int s2 = 0; s2 < a.top_k; ++s2)
+      if (s_ok[s2]) sum += s_w[s2] * s_part[s2][threadIdx.x];
     if (r2 < a.n_rows) a.y[(int64_t)t * a.n_rows + r2] = sum;
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    int drop = 0;
-    for (int i = 0; i < a.n_tok * a.top_k; ++i) drop += (a.ids[i] < 0 || a.ids[i] >= a.n_experts) ? 1 : 0;
-    a.err[0] = drop;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {  // wave 0, all lanes
+    const int drop = count_dropped(a, a.n_tok * a.top_k);
+    if (threadIdx.x == 0) a.err[0] = drop;
   }
 }
 
