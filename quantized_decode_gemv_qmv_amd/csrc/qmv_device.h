@@ -378,9 +378,9 @@ __device__ __forceinline__ void iq4_lookup2(uint32_t v, uint32_t& lo, uint32_t& 
 }
 
 __device__ __forceinline__ void decode_unit(const Raw<FIQ4_XS>& r, int u, Dec<FIQ4_XS>& o) {
-  const int c = u & 7;
-  const uint32_t lo4 = (r.hdr.y >> (4 * c)) & 15u;            // scales_l nibble
-  const uint32_t hi2 = (r.hdr.x >> (16 + 2 * c)) & 3u;        // scales_h bits
+  const uint32_t c = (uint32_t)u & 7;
+  const uint32_t lo4 = __builtin_amdgcn_ubfe(r.hdr.y, 4 * c, 4);       // scales_l nibble
+  const uint32_t hi2 = __builtin_amdgcn_ubfe(r.hdr.x, 16 + 2 * c, 2);  // scales_h bits
   o.ls = static_cast<int>(lo4 | (hi2 << 4)) - 32;
   o.d = half_bits_to_float(r.hdr.x);
   o.dls = o.d * static_cast<float>(o.ls);

@@ -496,9 +496,14 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
       const int uraw = c * CH + lane + 64 * q;
       const bool ok = uraw < units;
       const int u = ok ? uraw : units - 1;
+      // the decode takes the unclamped index: it uses it only for the unit's
+      // place in its super-block, which for a valid unit is the same, and
+      // here is the lane's own (c * CH and 64 q are multiples of 64), so the
+      // header field offsets are fixed per lane; a clamped unit's scales are
+      // zero whatever it decodes
       DecO<F> dec[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) decode_own(cur[r][q], u, lane & 1, ok, dec[r]);
+      for (int r = 0; r < R; ++r) decode_own(cur[r][q], uraw, lane & 1, ok, dec[r]);
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         const int tt = t < a.n_tok ? t : a.n_tok - 1;
