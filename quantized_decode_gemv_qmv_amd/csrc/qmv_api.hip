@@ -171,7 +171,8 @@ bool stream_fits(int v, int64_t k, int64_t n_tok) {
 //     one (q6_K while one chunk of 128 units per lane covers the row);
 //   - Q8_0 at 5..8 tokens, Q8G128 at 3..8 (and both from nine on fewer
 //     than 128 rows per compute unit): by rows per compute unit, the flat kernel with 16-wave
-//     workgroups on many rows (the multi-token one from nine tokens), the
+//     workgroups on many rows (on rows of more than 128 blocks only up to
+//     four tokens, the multi-token one from five), the
 //     multi-token kernel with two rows per lane group in between, and the
 //     flat kernel (or, on long rows from nine tokens, the multi-token one
 //     splitting K four ways) on few rows.
@@ -249,8 +250,16 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     // Q8_0 at 5..8 tokens, Q8G128 at 3..8 (and both beyond on fewer than
     // 128 rows per compute unit, where the matrix-core kernel is slower):
     // measured on 152064x5120, 14336x4096, 4096x4096 and 4096x14336
+    // (the heads, 152064 x 5120, at 5 / 6 / 7 / 8 tokens: the multi-token
+    // kernel with two rows per lane group 175 / 180 / 184 / 188.5 us against
+    // 191.5 / 194 / 195.5 / 198 for the flat one (Q8_0), 183 / 186.5 / 194 /
+    // 196.5 against 193 / 194.5 / 196.7 / 198 (Q8G128); the flat one stays
+    // ahead at 3 and 4 tokens: 149 against 153 us for Q8G128 at three)
     if (rpc >= 128)
-      name = n_tok > 8 ? "mt_r4_w4_k1" : nu <= 2 ? "fl_w16_r1_u2_l" : "fl_w16_r1_u3_l";
+      name = n_tok > 8    ? "mt_r4_w4_k1"
+             : nu <= 2    ? "fl_w16_r1_u2_l"
+             : n_tok >= 5 ? "mt_r2_w4_k1"
+                          : "fl_w16_r1_u3_l";
     else if (rpc >= 32)
       name = "mt_r2_w4_k1";
     else if (nu <= 2 && n_tok <= 4)

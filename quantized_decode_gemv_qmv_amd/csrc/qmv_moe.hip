@@ -1228,15 +1228,16 @@ int moe_kernel() { return g_moe_kernel; }
 
 // The few-slot flat kernel while grouping slots by expert saves less than
 // its routing costs (measured on 128 experts, top-8: one activation row per
-// token, 3072 x 4096 rows, up to 16 tokens -- 16.1 -> 12.3 us at one token,
-// 150.1 -> 145.2 us at 16, 286 against 207 us at 32; one row per slot,
-// 4096 x 1536, up to 8 tokens -- 13.6 -> 11.6 us at one, 49.3 -> 47.6 us at
-// 8, 68.2 against 64.3 us at 12); then the matrix-core kernel when experts
-// receive several slots (from 16 tokens), with 4 (8 from 17 tokens) slot
-// rows per group.
+// token, 3072 x 4096 rows, up to 24 tokens -- 16.1 -> 12.3 us at one token,
+// at 20 / 24 / 32 tokens 153.5 / 180.1 / 232.1 us against 168.6 / 185.1 /
+// 207.0 for the matrix-core kernel; one row per slot, 4096 x 1536, up to 8
+// tokens -- 13.6 -> 11.6 us at one, at 10 / 12 tokens 59.4 / 68.7 us against
+// 55.4 / 63.7 for the vector-ALU grouped kernel); then the matrix-core kernel
+// when experts receive several slots (from 16 tokens), with 4 (8 from 17
+// tokens) slot rows per group.
 template <int F>
 static hipError_t run_moe_any(const MoeLaunch& a, hipStream_t st) {
-  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= (a.x_per_slot ? 8 : 16)))
+  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= (a.x_per_slot ? 8 : 24)))
     return run_moe_flat_fmt<F>(a, st);
   const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && a.n_tok >= 16);
   if (mx) {

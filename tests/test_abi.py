@@ -254,6 +254,9 @@ PLANS = [
     ((2, 1024, 8192, 1, True), ("lk_w4_r1_u2", 1)),
     ((2, 1024, 8192, 4, True), ("fl_w4_r1_u4_g", 1)),
     ((0, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),
+    ((0, 152064, 5120, 8, False), ("mt_r2_w4_k1", 1)),
+    ((5, 152064, 5120, 4, False), ("fl_w16_r1_u3_l", 1)),
+    ((5, 152064, 5120, 5, False), ("mt_r2_w4_k1", 1)),
     ((5, 152064, 5120, 2, False), ("st_w4_r1_u3", 1)),
     ((5, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),
     ((4, 14336, 4096, 16, False), ("fl_w16_r1_u2_l", 1)),  # q6_K: vector kernels only
