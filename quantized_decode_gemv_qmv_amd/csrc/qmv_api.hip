@@ -242,8 +242,18 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
   } else if (type == QMV_Q5_K || type == QMV_Q6_K) {
     // q5_K, q6_K (measured on 14336 x 4096 at 3..16 tokens): q6_K keeps the
     // flat kernel while one chunk covers the row, q5_K the multi-token one
+    // from five tokens (us: q5_K at 3 / 4 two rows per wave 12.8 / 13.4
+    // against 13.6 / 13.8 for the multi-token kernel; q6_K at 3 / 4 two rows
+    // per wave 15.0 / 15.7 against 15.7 / 16.5 for one, at 6 / 8 / 12 / 16
+    // eight waves of two rows 22.0 / 22.4 / 34.3 / 35.4 against 22.6 / 24.0 /
+    // 35.9 / 37.4 for the other flat shapes, at 5 and 9 / 10 four waves of
+    // two rows, 21.4 and 31.8 / 32.2 against 35.5 / 35.5 for sixteen of one)
     if (type == QMV_Q6_K && nu <= 2)
-      name = n_tok > 8 ? "fl_w16_r1_u2_l" : n_tok > 4 ? "fl_w4_r2_u2_g" : "fl_w4_r1_u2_l";
+      name = n_tok <= 4                                       ? "fl_w4_r2_u2_l"
+             : n_tok == 5 || (n_tok >= 9 && n_tok <= 10)      ? "fl_w4_r2_u2_g"
+                                                              : "fl_w8_r2_u2_l";
+    else if (type == QMV_Q5_K && nu <= 2 && n_tok <= 4)
+      name = "fl_w4_r2_u2_l";
     else
       name = n_tok > 8 ? "mt_r4_w8_k2" : "mt_r2_w8_k2";
   } else if ((type == QMV_Q8_0 || type == QMV_Q8G128) && (n_tok <= 8 || rpc < 128)) {
@@ -264,6 +274,8 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
       name = "mt_r2_w4_k1";
     else if (nu <= 2 && n_tok <= 4)
       name = "fl_w4_r1_u2_l";
+    else if (nu <= 2 && n_tok <= 7 && type == QMV_Q8_0)
+      name = "fl_w8_r2_u2_l";  // 4096 x 4096 at 5 / 6 / 7 tokens: 7.46 / 7.54 / 7.69 us against 8.01 / 8.09 / 8.02
     else
       name = n_tok > 8 && nu > 2 ? "mt_r1_w8_k4" : "fl_w16_r1_u2_l";
   } else if (n_tok > 8) {

@@ -259,7 +259,13 @@ PLANS = [
     ((5, 152064, 5120, 5, False), ("mt_r2_w4_k1", 1)),
     ((5, 152064, 5120, 2, False), ("st_w4_r1_u3", 1)),
     ((5, 152064, 5120, 16, False), ("mx_w8_k1_r4", 1)),
-    ((4, 14336, 4096, 16, False), ("fl_w16_r1_u2_l", 1)),  # q6_K: vector kernels only
+    ((4, 14336, 4096, 16, False), ("fl_w8_r2_u2_l", 1)),  # q6_K: vector kernels only
+    ((4, 14336, 4096, 9, False), ("fl_w4_r2_u2_g", 1)),
+    ((4, 14336, 4096, 3, False), ("fl_w4_r2_u2_l", 1)),
+    ((3, 14336, 4096, 4, False), ("fl_w4_r2_u2_l", 1)),   # q5_K
+    ((3, 14336, 4096, 5, False), ("mt_r2_w8_k2", 1)),
+    ((0, 4096, 4096, 6, False), ("fl_w8_r2_u2_l", 1)),
+    ((0, 4096, 4096, 8, False), ("fl_w16_r1_u2_l", 1)),
 ]
 
 
