@@ -210,6 +210,32 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     name = stream_fits(find_variant("st_k16_r1_u2"), k, n_tok) ? "st_k16_r1_u2"
            : has_mfma(type)                                     ? "mx_w8_k8_r4"
                                                                 : "mt_r2_w8_k4";
+  } else if ((type == QMV_Q4_K || type == QMV_IQ4_XS) && nu <= 2 && n_tok <= 16 && rpc >= 16 &&
+             (n_tok > 2 || rpc == 16 || type == QMV_Q4_K)) {
+    // q4_K and IQ4_XS rows of up to 4096 weights (measured on 4096, 8192 and
+    // 14336 rows x 4096, us at 16 / 32 / 56 rows per compute unit):
+    //  - up to 3 tokens the flat kernel, one row per wave on 16 rows per
+    //    compute unit (IQ4_XS at 3 tokens 5.04 against 8.30 for the
+    //    matrix-core kernel, q4_K 5.23 against 5.39 with two rows), else two;
+    //  - 4 tokens eight waves of two rows below 48 rows per compute unit
+    //    (IQ4_XS 8192 rows 7.51 against 10.09, q4_K 7.79 against 8.17);
+    //  - 5..8 tokens the same below 24 rows per compute unit (IQ4_XS 6.80 at
+    //    5 against 8.56), the flat matrix-core kernel from there (IQ4_XS
+    //    14336 rows 13.3 against 14.0, 8192 rows 9.6 against 10.6);
+    //  - 9..16 tokens the flat matrix-core kernel below 48 rows per compute
+    //    unit (8192 rows at 16 tokens: q4_K 9.84 against 12.52, IQ4_XS 10.92
+    //    against 13.25; IQ4_XS keeps the persistent one on 16 rows, 9.98
+    //    against 10.32), then the persistent one (IQ4_XS with 16-wave
+    //    workgroups: 15.37 against 16.36 at 16 tokens on 14336 rows).
+    const bool q4k = type == QMV_Q4_K;
+    if (n_tok <= 3)
+      name = rpc == 16 ? "fl_w4_r1_u2_l" : q4k || n_tok == 3 ? "fl_w4_r2_u2_l" : "fl_w4_r2_u2_g";
+    else if (n_tok == 4)
+      name = rpc < 48 ? "fl_w8_r2_u2_l" : "fl_w4_r2_u2_l";
+    else if (n_tok <= 8)
+      name = rpc < 24 ? "fl_w8_r2_u2_l" : "mf_w8_b4";
+    else
+      name = rpc < 24 && !q4k ? "mx_w8_k8_r4" : rpc < 48 ? "mf_w8_b4" : q4k ? "mx_w8_k4_r4" : "mx_w16_k4_r2";
   } else if (type == QMV_Q8G128 && n_tok == 2 && rpc >= 128) {
     name = "st_w4_r1_u3";  // the head at two tokens: 144.0 / 142.0 us against 151.0 / 150.4 (two boxes)
   } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2) ||
@@ -357,13 +383,14 @@ int flat_split(const Variant& v, int64_t n_rows, int64_t units, int64_t n_tok, i
 
 // With a workspace, rows too long for one LDS chunk on few row tiles run the
 // matrix-core variant measured fastest split over workgroups (4096 x 14336:
-// IQ4_XS 16 tokens 25.3 -> 19.4 us, q4_K 16 tokens 29.8 -> 26.5 us, q4_K
-// 8 tokens 18.5 -> 16.1 us), when its plan splits; -1 otherwise.
+// IQ4_XS 16 tokens 25.3 -> 19.4 us; q4_K at 10 / 16 tokens 22.8 / 25.2 us
+// with eight-wave workgroups, 16.9 / 17.3 with sixteen since the two-phase
+// step fits them in 128 VGPRs; q4_K 8 tokens 18.5 -> 16.1 us), when its plan
+// splits; -1 otherwise.
 int split_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
-  const char* name = type == QMV_IQ4_XS && n_tok > 8 ? "mx_w16_k4_r2"
-                     : type == QMV_Q4_K && n_tok > 8 ? "mx_w8_k1_r4"
-                     : type == QMV_Q4_K && n_tok > 4 ? "mx_w8_k4_r4"
-                                                      : nullptr;
+  const char* name = n_tok > 8 && (type == QMV_IQ4_XS || type == QMV_Q4_K) ? "mx_w16_k4_r2"
+                     : type == QMV_Q4_K && n_tok > 4                       ? "mx_w8_k4_r4"
+                                                                          : nullptr;
   if (name == nullptr) return -1;
   const int v = find_variant(name);
   const DeviceInfo dv = device_info();

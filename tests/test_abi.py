@@ -246,7 +246,13 @@ PLANS = [
     ((2, 4096, 14336, 1, True), ("fl_w8_r1_u7_l", 1)),
     ((2, 4096, 14336, 16, True), ("mx_w16_k4_r2", 4)),   # split over workgroups with a workspace
     ((2, 4096, 14336, 16, False), ("mx_w8_k8_r4", 1)),
-    ((1, 4096, 14336, 16, True), ("mx_w8_k1_r4", 8)),
+    ((1, 4096, 14336, 16, True), ("mx_w16_k4_r2", 4)),
+    ((2, 4096, 4096, 3, False), ("fl_w4_r1_u2_l", 1)),   # rows of 4096 weights, 16 rows per compute unit
+    ((1, 4096, 4096, 6, False), ("fl_w8_r2_u2_l", 1)),
+    ((2, 8192, 4096, 4, False), ("fl_w8_r2_u2_l", 1)),
+    ((2, 8192, 4096, 16, True), ("mf_w8_b4", 1)),
+    ((2, 14336, 4096, 6, True), ("mf_w8_b4", 1)),
+    ((2, 14336, 4096, 16, True), ("mx_w16_k4_r2", 1)),
     ((0, 4096, 4096, 1, True), ("fl_w4_r1_u2_l", 1)),
     ((0, 256, 65536, 1, True), ("lk_w8_r1_u4", 1)),      # K split inside one workgroup
     ((0, 256, 65536, 4, True), ("lk_w16_r1_u2", 1)),
