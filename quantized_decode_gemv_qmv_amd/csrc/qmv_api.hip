@@ -247,8 +247,16 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     // kernel's eight-token instantiation takes 16.5 us and more).  Q8_0
     // 4096 x 4096 at four tokens: eight waves of two rows 6.07 against 6.39
     // for one row per wave.
-    if (nu <= 2 && type == QMV_Q8_0 && n_tok == 4 && n_rows <= 16 * (int64_t)cus)
+    // Q8_0 at four tokens on up to 64 rows per compute unit: eight waves of
+    // two rows (4096 / 8192 / 14336 x 4096: 6.11 / 9.13 / 14.44 us against
+    // 6.38 / 9.84 / 15.20 for one row per wave); rows of 14336 weights on 16
+    // rows per compute unit at two to four tokens: sixteen waves of one row
+    // and two units per lane (13.41 / 14.62 / 14.99 against 14.12 / 17.58 /
+    // 18.85 with seven units per lane)
+    if (nu <= 2 && type == QMV_Q8_0 && n_tok == 4 && rpc <= 64)
       name = "fl_w8_r2_u2_l";
+    else if (type == QMV_Q8_0 && nu >= 4 && nu <= 7 && n_tok >= 2 && rpc <= 16)
+      name = "fl_w16_r1_u2_l";
     else if (nu <= 2)
       name = type == QMV_Q8_0 || type == QMV_Q8G128 ? "fl_w4_r1_u2_l"
              : type == QMV_Q4_K                      ? "fl_w4_r2_u2_l"
@@ -296,6 +304,12 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
              : nu <= 2    ? "fl_w16_r1_u2_l"
              : n_tok >= 5 ? "mt_r2_w4_k1"
                           : "fl_w16_r1_u3_l";
+    else if (rpc >= 32 && rpc < 48 && nu <= 2 && type == QMV_Q8_0)
+      // 8192 x 4096: at 5 / 6 / 8 tokens eight waves of two rows 11.13 /
+      // 11.06 / 12.35 us against 13.23 / 13.51 / 14.44 for the multi-token
+      // kernel, at 10 / 16 the flat matrix-core kernel 15.38 / 15.36 against
+      // 21.49 / 23.68
+      name = n_tok <= 8 ? "fl_w8_r2_u2_l" : "mf_w8_b4";
     else if (rpc >= 32)
       name = "mt_r2_w4_k1";
     else if (nu <= 2 && n_tok <= 4)

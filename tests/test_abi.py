@@ -272,6 +272,12 @@ PLANS = [
     ((3, 14336, 4096, 5, False), ("mt_r2_w8_k2", 1)),
     ((0, 4096, 4096, 6, False), ("fl_w8_r2_u2_l", 1)),
     ((0, 4096, 4096, 8, False), ("fl_w16_r1_u2_l", 1)),
+    ((0, 14336, 4096, 4, False), ("fl_w8_r2_u2_l", 1)),
+    ((0, 8192, 4096, 6, False), ("fl_w8_r2_u2_l", 1)),
+    ((0, 8192, 4096, 16, True), ("mf_w8_b4", 1)),
+    ((0, 14336, 4096, 6, False), ("mt_r2_w4_k1", 1)),
+    ((0, 4096, 14336, 3, False), ("fl_w16_r1_u2_l", 1)),
+    ((0, 4096, 14336, 1, False), ("fl_w8_r1_u7_l", 1)),
 ]
 
 
