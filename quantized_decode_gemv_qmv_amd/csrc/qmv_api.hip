@@ -227,8 +227,15 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     //    against 13.25; IQ4_XS keeps the persistent one on 16 rows, 9.98
     //    against 10.32), then the persistent one (IQ4_XS with 16-wave
     //    workgroups: 15.37 against 16.36 at 16 tokens on 14336 rows).
+    //  - from 96 rows per compute unit (28672 x 4096) the persistent
+    //    matrix-core kernel with one wave per row tile from 5 tokens (q4_K /
+    //    IQ4_XS at 6 tokens 20.0 / 20.5 us against 22.4 / 24.2 for the flat
+    //    one, at 16 tokens 22.3 / 23.6 against 23.0 / 25.8), eight waves of
+    //    two rows at 4 (IQ4_XS 19.3 against 20.5).
     const bool q4k = type == QMV_Q4_K;
-    if (n_tok <= 3)
+    if (rpc >= 96 && n_tok >= 4)
+      name = n_tok == 4 ? "fl_w8_r2_u2_l" : "mx_w8_k1_r4";
+    else if (n_tok <= 3)
       name = rpc == 16 ? "fl_w4_r1_u2_l" : q4k || n_tok == 3 ? "fl_w4_r2_u2_l" : "fl_w4_r2_u2_g";
     else if (n_tok == 4)
       name = rpc < 48 ? "fl_w8_r2_u2_l" : "fl_w4_r2_u2_l";
@@ -320,10 +327,20 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
       name = n_tok > 8 && nu > 2 ? "mt_r1_w8_k4" : "fl_w16_r1_u2_l";
   } else if (n_tok > 8) {
     const int64_t per = 16 * (int64_t)cus / tiles;  // waves of K split per row tile
-    name = per >= 8 ? "mx_w8_k8_r4" : per >= 4 ? "mx_w8_k4_r4" : "mx_w8_k1_r4";
+    // (eight waves splitting K only from 16 waves of K split per row tile:
+    // q4_K and IQ4_XS 8192 x 14336 at 10 / 16 tokens, unsplit, 29.4 / 30.2
+    // and 28.0 / 28.3 us with four against 44.1 / 45.1 and 41.5 / 42.6 with
+    // eight)
+    name = per >= 16 ? "mx_w8_k8_r4" : per >= 4 ? "mx_w8_k4_r4" : "mx_w8_k1_r4";
   } else if (type == QMV_IQ4_XS || (type == QMV_Q4_K && n_tok > 4)) {
+    // (8192 x 14336, 8 waves of K split per tile: q4_K at 5..8 tokens
+    // sixteen-wave workgroups split four ways 21.7 against 22.6 us eight
+    // ways; IQ4_XS at 3..8 eight-wave ones split four ways 18.6 at 3 and 4
+    // tokens, 20.2 at 5, against 19.5 and 21.4 with sixteen split eight ways)
     const int64_t per = 16 * (int64_t)cus / tiles;
-    name = per >= 16 ? "mx_w16_k16_r2" : per >= 8 ? "mx_w16_k8_r2" : "mx_w16_k4_r2";
+    name = per >= 16                        ? "mx_w16_k16_r2"
+           : per >= 8 && type == QMV_IQ4_XS ? "mx_w8_k4_r4"
+                                            : "mx_w16_k4_r2";
   } else {
     name = rpc >= 128 ? "mt_r4_w4_k1" : rpc >= 32 ? "mt_r2_w8_k2" : rpc >= 16 ? "mt_r2_w16_k8" : "mt_r1_w16_k8";
   }
@@ -401,18 +418,24 @@ int flat_split(const Variant& v, int64_t n_rows, int64_t units, int64_t n_tok, i
 // with eight-wave workgroups, 16.9 / 17.3 with sixteen since the two-phase
 // step fits them in 128 VGPRs; q4_K 8 tokens 18.5 -> 16.1 us), when its plan
 // splits; -1 otherwise.
+// At 9-16 tokens the sixteen-wave kernel splits only on few row tiles; on
+// more (8192 x 14336) the eight-wave one with one wave per tile split four
+// ways is next (26.2 / 27.9 us at 10 / 16 tokens against 29.4 / 30.2
+// unsplit).
 int split_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
-  const char* name = n_tok > 8 && (type == QMV_IQ4_XS || type == QMV_Q4_K) ? "mx_w16_k4_r2"
-                     : type == QMV_Q4_K && n_tok > 4                       ? "mx_w8_k4_r4"
-                                                                          : nullptr;
-  if (name == nullptr) return -1;
-  const int v = find_variant(name);
+  const bool k4iq = type == QMV_IQ4_XS || type == QMV_Q4_K;
+  const char* names[2] = {n_tok > 8 && k4iq ? "mx_w16_k4_r2" : type == QMV_Q4_K && n_tok > 4 ? "mx_w8_k4_r4" : nullptr,
+                          n_tok > 8 && k4iq ? "mx_w8_k1_r4" : nullptr};
   const DeviceInfo dv = device_info();
-  int ups = 0;
-  return mx_split_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].ks, (int)(k / 32), (int)n_rows, dv.cus,
-                       dv.lds_per_cu, mx_slices(), &ups) >= 2
-             ? v
-             : -1;
+  for (const char* name : names) {
+    if (name == nullptr) continue;
+    const int v = find_variant(name);
+    int ups = 0;
+    if (mx_split_plan(type, (int)n_tok, kVariants[v].wpb, kVariants[v].ks, (int)(k / 32), (int)n_rows, dv.cus,
+                      dv.lds_per_cu, mx_slices(), &ups) >= 2)
+      return v;
+  }
+  return -1;
 }
 
 Plan make_plan(int type, int64_t n_rows, int64_t k, int64_t n_tok, bool use_ws) {

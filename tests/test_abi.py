@@ -253,6 +253,12 @@ PLANS = [
     ((2, 8192, 4096, 16, True), ("mf_w8_b4", 1)),
     ((2, 14336, 4096, 6, True), ("mf_w8_b4", 1)),
     ((2, 14336, 4096, 16, True), ("mx_w16_k4_r2", 1)),
+    ((1, 8192, 14336, 16, True), ("mx_w8_k1_r4", 4)),    # the sixteen-wave kernel does not split here
+    ((2, 8192, 14336, 10, False), ("mx_w8_k4_r4", 1)),
+    ((2, 8192, 14336, 4, False), ("mx_w8_k4_r4", 1)),
+    ((1, 8192, 14336, 6, False), ("mx_w16_k4_r2", 1)),
+    ((1, 28672, 4096, 6, False), ("mx_w8_k1_r4", 1)),
+    ((2, 28672, 4096, 4, False), ("fl_w8_r2_u2_l", 1)),
     ((0, 4096, 4096, 1, True), ("fl_w4_r1_u2_l", 1)),
     ((0, 256, 65536, 1, True), ("lk_w8_r1_u4", 1)),      # K split inside one workgroup
     ((0, 256, 65536, 4, True), ("lk_w16_r1_u2", 1)),
