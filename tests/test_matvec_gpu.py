@@ -125,6 +125,15 @@ FULL = [
     ("q5_k_14336x4096", synth.Q5_K, 14336, 4096, (1, 2, 4, 8, 16)),
     ("q6_k_14336x4096", synth.Q6_K, 14336, 4096, (1, 2, 4, 8, 16)),
     ("q8g128_head_152064x5120", synth.Q8G128, 152064, 5120, (1, 2, 4, 8, 16)),
+    # other shapes whose automatic choice differs (rows per compute unit, row length)
+    ("q4_k_28672x4096", synth.Q4_K, 28672, 4096, (4, 6, 16)),
+    ("iq4_xs_28672x4096", synth.IQ4_XS, 28672, 4096, (4, 6, 16)),
+    ("q4_k_8192x14336", synth.Q4_K, 8192, 14336, (2, 6, 16)),
+    ("iq4_xs_8192x14336", synth.IQ4_XS, 8192, 14336, (4, 10, 16)),
+    ("iq4_xs_4096x4096", synth.IQ4_XS, 4096, 4096, (3, 6, 16)),
+    ("q4_k_8192x4096", synth.Q4_K, 8192, 4096, (4, 12)),
+    ("q8_0_8192x4096", synth.Q8_0, 8192, 4096, (6, 16)),
+    ("q8_0_4096x14336", synth.Q8_0, 4096, 14336, (3, 16)),
 ]
 
 
