@@ -1228,18 +1228,21 @@ int moe_kernel() { return g_moe_kernel; }
 
 // The few-slot flat kernel while grouping slots by expert saves less than
 // its routing costs (measured on 128 experts, top-8: one activation row per
-// token, 3072 x 4096 rows, up to 24 tokens -- 16.1 -> 12.3 us at one token,
-// at 20 / 24 / 32 tokens 153.5 / 180.1 / 232.1 us against 168.6 / 185.1 /
-// 207.0 for the matrix-core kernel; one row per slot, 4096 x 1536, up to 8
-// tokens -- 13.6 -> 11.6 us at one, at 10 / 12 tokens 59.4 / 68.7 us against
-// 55.4 / 63.7 for the vector-ALU grouped kernel); then the matrix-core kernel
-// when experts receive several slots (from 16 tokens), with 4 (8 from 17
-// tokens) slot rows per group.
+// token, 3072 x 4096 rows, up to 20 tokens -- 16.1 -> 12.3 us at one token,
+// at 20 / 32 tokens 153.5-158.3 / 232.1 us against 168.6-168.9 / 207.0 for
+// the matrix-core kernel, at 24 within 5% either way on two boxes; one row
+// per slot, 4096 x 1536, up to 8 tokens -- 13.6 -> 11.6 us at one); then the
+// vector-ALU grouped kernel, and the matrix-core kernel when experts receive
+// several slots: from 21 tokens with one activation row per token, and with
+// one per slot from 21 too (the vector kernel's down projection at 12 / 16 /
+// 20 tokens 63.5 / 75.4 / 86.4 us against 69.9 / 79.8 / 89.3, at 24 / 32
+// 96.5 / 117.1 against 94.8 / 107.2); 4 (8 from 17 tokens) slot rows per
+// group.
 template <int F>
 static hipError_t run_moe_any(const MoeLaunch& a, hipStream_t st) {
-  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= (a.x_per_slot ? 8 : 24)))
+  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= (a.x_per_slot ? 8 : 20)))
     return run_moe_flat_fmt<F>(a, st);
-  const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && a.n_tok >= 16);
+  const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && a.n_tok >= 21);
   if (mx) {
     const hipError_t e = a.n_tok <= 16 ? run_moe_mx<F, 4>(a, st) : run_moe_mx<F, 8>(a, st);
     if (e != hipErrorInvalidValue) return e;  // else the staged rows do not fit: vector kernel
