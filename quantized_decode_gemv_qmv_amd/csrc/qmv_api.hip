@@ -243,6 +243,39 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
       name = rpc < 24 ? "fl_w8_r2_u2_l" : "mf_w8_b4";
     else
       name = rpc < 24 && !q4k ? "mx_w8_k8_r4" : rpc < 48 ? "mf_w8_b4" : q4k ? "mx_w8_k4_r4" : "mx_w16_k4_r2";
+  } else if ((type == QMV_Q5_K || type == QMV_Q6_K) && n_tok <= 16 && rpc >= 16 && (nu <= 2 || rpc <= 24)) {
+    // q5_K and q6_K (vector kernels only), measured on 4096 / 8192 / 14336
+    // x 4096 and 4096 x 14336 (us):
+    //  - rows of more than 128 blocks (16 rows per compute unit): at one
+    //    token four waves of two units per lane (q5_K one row per wave
+    //    10.48, q6_K two 14.57, against 11.50 / 17.45 with seven units), at
+    //    2..8 tokens sixteen waves of one row (q6_K at 4 18.20 against 29.71
+    //    for the multi-token kernel; q5_K keeps seven units at 2), from 9 the
+    //    multi-token kernel with eight waves splitting K four ways (q6_K at
+    //    16 45.28 against 132.86 with two);
+    //  - rows of up to 128 blocks: two and three tokens (and four for
+    //    q6_K) one row per wave on 16 rows per compute unit, else two (q6_K
+    //    4096 x 4096 at 3 6.38 against 6.86); q5_K at 4 as q4_K, from 5
+    //    the multi-token kernel, one row per lane group and K split four
+    //    ways on 16 rows per compute unit (11.81 against 26.81 at 16
+    //    tokens), two rows below 48 (18.24 against 27.59), four from 9
+    //    tokens above; q6_K from 5 as measured on 14336 x 4096 (below).
+    const bool q6 = type == QMV_Q6_K;
+    if (nu > 2)
+      name = n_tok == 1                ? (q6 ? "fl_w4_r2_u2_l" : "fl_w4_r1_u2_l")
+             : n_tok == 2 && !q6       ? "fl_w8_r1_u7_l"
+             : n_tok <= 8              ? "fl_w16_r1_u2_l"
+                                       : "mt_r1_w8_k4";
+    else if (n_tok == 1)
+      name = "fl_w4_r2_u2_g";
+    else if (n_tok <= 3 || (q6 && n_tok == 4))
+      name = rpc == 16 ? "fl_w4_r1_u2_l" : "fl_w4_r2_u2_l";
+    else if (!q6 && n_tok == 4)
+      name = rpc < 48 ? "fl_w8_r2_u2_l" : "fl_w4_r2_u2_l";
+    else if (q6)
+      name = n_tok == 5 || (n_tok >= 9 && n_tok <= 10) ? "fl_w4_r2_u2_g" : "fl_w8_r2_u2_l";
+    else
+      name = rpc < 24 ? "mt_r1_w8_k4" : rpc < 48 || n_tok <= 8 ? "mt_r2_w8_k2" : "mt_r4_w8_k2";
   } else if (type == QMV_Q8G128 && n_tok == 2 && rpc >= 128) {
     name = "st_w4_r1_u3";  // the head at two tokens: 144.0 / 142.0 us against 151.0 / 150.4 (two boxes)
   } else if (n_tok <= (type == QMV_Q8_0 ? 4 : 2) ||

@@ -276,6 +276,14 @@ PLANS = [
     ((4, 14336, 4096, 3, False), ("fl_w4_r2_u2_l", 1)),
     ((3, 14336, 4096, 4, False), ("fl_w4_r2_u2_l", 1)),   # q5_K
     ((3, 14336, 4096, 5, False), ("mt_r2_w8_k2", 1)),
+    ((3, 14336, 4096, 2, False), ("fl_w4_r2_u2_l", 1)),
+    ((3, 4096, 4096, 16, False), ("mt_r1_w8_k4", 1)),
+    ((3, 8192, 4096, 12, False), ("mt_r2_w8_k2", 1)),
+    ((3, 14336, 4096, 12, False), ("mt_r4_w8_k2", 1)),
+    ((3, 4096, 14336, 6, False), ("fl_w16_r1_u2_l", 1)),
+    ((4, 4096, 14336, 16, False), ("mt_r1_w8_k4", 1)),
+    ((4, 4096, 14336, 1, False), ("fl_w4_r2_u2_l", 1)),
+    ((4, 4096, 4096, 3, False), ("fl_w4_r1_u2_l", 1)),
     ((0, 4096, 4096, 6, False), ("fl_w8_r2_u2_l", 1)),
     ((0, 4096, 4096, 8, False), ("fl_w16_r1_u2_l", 1)),
     ((0, 14336, 4096, 4, False), ("fl_w8_r2_u2_l", 1)),

@@ -134,6 +134,9 @@ FULL = [
     ("q4_k_8192x4096", synth.Q4_K, 8192, 4096, (4, 12)),
     ("q8_0_8192x4096", synth.Q8_0, 8192, 4096, (6, 16)),
     ("q8_0_4096x14336", synth.Q8_0, 4096, 14336, (3, 16)),
+    ("q5_k_4096x14336", synth.Q5_K, 4096, 14336, (1, 4, 16)),
+    ("q6_k_4096x14336", synth.Q6_K, 4096, 14336, (1, 4, 16)),
+    ("q5_k_4096x4096", synth.Q5_K, 4096, 4096, (2, 8, 16)),
 ]
 
 
