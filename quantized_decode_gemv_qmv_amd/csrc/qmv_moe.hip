@@ -1234,15 +1234,33 @@ int moe_kernel() { return g_moe_kernel; }
 // per slot, 4096 x 1536, up to 8 tokens -- 13.6 -> 11.6 us at one); then the
 // vector-ALU grouped kernel, and the matrix-core kernel when experts receive
 // several slots: from 21 tokens with one activation row per token, and with
-// one per slot from 21 too (the vector kernel's down projection at 12 / 16 /
-// 20 tokens 63.5 / 75.4 / 86.4 us against 69.9 / 79.8 / 89.3, at 24 / 32
-// 96.5 / 117.1 against 94.8 / 107.2); 4 (8 from 17 tokens) slot rows per
-// group.
+// one per slot from 21 too, and from 9 for q4_K and for IQ4_XS rows of fewer
+// than 48 blocks.  Down projections at 9..20 tokens, us: IQ4_XS 4096 x 1536
+// (128 experts) at 12 / 16 / 20 tokens 63.0 / 75.6 / 86.5 with the vector
+// kernel against 70.7 / 80.6 / 88.7, Q8_0 2048 x 768 34.0 against 39.8 at 16;
+// but q4_K 4096 x 1536 83.9 against 120.7 at 16 with the matrix-core kernel,
+// q4_K and IQ4_XS 2048 x 768 23.9 / 24.7 against 32.6 / 32.8 (the boundary
+// between 24 and 48 blocks per row is not measured); at 24 / 32 tokens IQ4_XS
+// 4096 x 1536 94.8 / 107.2 against 96.5 / 117.1.  4 (8 from 17 tokens) slot
+// rows per group.
+// Q8_0 experts, whose decode is a byte copy, never gain from the matrix
+// cores up to 64 tokens: gate+up on the few-slot kernel (3072 x 4096 at 24 /
+// 32 / 48 / 64 tokens 231 / 273 / 339 / 400 us against 387 / 417 / 455 / 495),
+// down on the vector kernel from 9 (146 / 167 / 181 / 191 against 181 / 200 /
+// 227 / 237).
+template <int F>
+static bool moe_slots_on_matrix_cores(const MoeLaunch& a) {
+  if (F == FQ8_0) return a.n_tok > 64;
+  if (a.n_tok >= 21) return true;
+  if (!a.x_per_slot || a.n_tok <= 8) return false;
+  return F == FQ4_K || (F == FIQ4_XS && a.units < 48);
+}
 template <int F>
 static hipError_t run_moe_any(const MoeLaunch& a, hipStream_t st) {
-  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= (a.x_per_slot ? 8 : 20)))
+  const int few_slot_max = a.x_per_slot ? 8 : F == FQ8_0 ? 64 : 20;
+  if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= few_slot_max))
     return run_moe_flat_fmt<F>(a, st);
-  const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && a.n_tok >= 21);
+  const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && moe_slots_on_matrix_cores<F>(a));
   if (mx) {
     const hipError_t e = a.n_tok <= 16 ? run_moe_mx<F, 4>(a, st) : run_moe_mx<F, 8>(a, st);
     if (e != hipErrorInvalidValue) return e;  // else the staged rows do not fit: vector kernel
