@@ -195,12 +195,16 @@ int auto_variant(int type, int64_t n_rows, int64_t k, int64_t n_tok) {
     // 512 x 16384 Q8_0 4.08 / 4.58 / 5.67, IQ4_XS 3.57 / 4.13 / 5.19 against
     // 5.42 / 6.42 / 7.49 and 4.94 / 5.07 / 6.78 for the flat kernel): eight
     // waves of four units per lane up to one row per compute unit and two
-    // tokens (sixteen of two units at three and four), four of two units up
+    // tokens (sixteen of two units at three and four, and at one for Q8_0
+    // and for q4_K rows of up to 32768 weights: 5.84 against 6.10 us on Q8_0
+    // 256 x 65536, 3.64 against 3.83 on q4_K 256 x 32768), four of two units up
     // to two rows per compute unit; on 1024 rows (IQ4_XS x 8192) the same up
     // to two tokens (3.40 / 3.78 us against 3.44 / 3.86) and the flat kernel
     // from three (4.60 against 4.76 us at four)
     if (n_rows <= cus)
-      name = n_tok <= 2 ? "lk_w8_r1_u4" : "lk_w16_r1_u2";
+      name = n_tok <= 2 && !(n_tok == 1 && (type == QMV_Q8_0 || (type == QMV_Q4_K && units <= 1024)))
+                 ? "lk_w8_r1_u4"
+                 : "lk_w16_r1_u2";
     else
       name = n_rows <= 2 * (int64_t)cus || n_tok <= 2 ? "lk_w4_r1_u2" : "fl_w4_r1_u4_g";
   } else if (n_rows < 4 * (int64_t)cus && units >= 256) {

@@ -260,7 +260,10 @@ PLANS = [
     ((1, 28672, 4096, 6, False), ("mx_w8_k1_r4", 1)),
     ((2, 28672, 4096, 4, False), ("fl_w8_r2_u2_l", 1)),
     ((0, 4096, 4096, 1, True), ("fl_w4_r1_u2_l", 1)),
-    ((0, 256, 65536, 1, True), ("lk_w8_r1_u4", 1)),      # K split inside one workgroup
+    ((0, 256, 65536, 1, True), ("lk_w16_r1_u2", 1)),     # K split inside one workgroup
+    ((0, 256, 65536, 2, True), ("lk_w8_r1_u4", 1)),
+    ((1, 256, 65536, 1, True), ("lk_w8_r1_u4", 1)),
+    ((1, 256, 32768, 1, True), ("lk_w16_r1_u2", 1)),
     ((0, 256, 65536, 4, True), ("lk_w16_r1_u2", 1)),
     ((1, 512, 16384, 2, False), ("lk_w4_r1_u2", 1)),
     ((2, 1024, 8192, 1, True), ("lk_w4_r1_u2", 1)),
