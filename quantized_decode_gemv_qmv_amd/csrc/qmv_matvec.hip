@@ -401,11 +401,22 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
         load_xo<F>(gx, t < a.n_tok ? t : a.n_tok - 1, min(lane + 64 * q, units - 1), xf[q][t]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // Unit order: each unit's loads, and later its decode and dot products,
+  // are kept apart from the next unit's, so a unit is consumed as soon as its
+  // own loads have arrived rather than when the compiler's interleaving
+  // first needs a later one.  At one token (q4_K 14336 x 4096 7.78 -> 7.60
+  // us, Q8_0 4096 x 4096 5.15 -> 4.96, the Q8_0 head 133.0 -> 126.0) and for
+  // q6_K at two (14.2 -> 13.9); elsewhere it was slower on some GPUs (q6_K
+  // at four tokens 15.7 -> 16.7 us, the two-token quantizing launch 11.6 ->
+  // 12.1, q4_K at two and four tokens faster on one GPU and not on another).
+  constexpr bool in_order = (TM == 1 && !QX) || (F == FQ6_K && TM == 2);
   RawS<F> cur[R][NU];
 #pragma unroll
-  for (int q = 0; q < NU; ++q)
+  for (int q = 0; q < NU; ++q) {
 #pragma unroll
     for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(lane + 64 * q, units - 1), lane, cur[r][q]);
+    if constexpr (in_order) __builtin_amdgcn_sched_barrier(0);
+  }
   // batched launches: the residual of the lane's output, loaded right behind
   // the weights and unconditionally (a branch around a load would wait for
   // every load before it): with no residual the same valid address of the
@@ -493,6 +504,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
     }
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
+      if (in_order && q > 0) __builtin_amdgcn_sched_barrier(0);
       const int uraw = c * CH + lane + 64 * q;
       const bool ok = uraw < units;
       const int u = ok ? uraw : units - 1;
