@@ -137,6 +137,9 @@ FULL = [
     ("q5_k_4096x14336", synth.Q5_K, 4096, 14336, (1, 4, 16)),
     ("q6_k_4096x14336", synth.Q6_K, 4096, 14336, (1, 4, 16)),
     ("q5_k_4096x4096", synth.Q5_K, 4096, 4096, (2, 8, 16)),
+    # few rows, long K: the long-row kernel (sixteen or eight waves per row)
+    ("q8_0_splitk_256x65536", synth.Q8_0, 256, 65536, (1, 2, 4)),
+    ("q4_k_256x32768", synth.Q4_K, 256, 32768, (1, 2)),
 ]
 
 
