@@ -916,18 +916,21 @@ __global__ __launch_bounds__(64 * WPB) void k_moe_flat_comb(MoeLaunch a) {
 }
 
 // One token, route-weighted, rows of at most 64 units (the down projection,
-// 48 units per row): workgroup (x, t) takes rows 4x .. 4x + 3 for every slot
-// of token t, wave s for slot s (top_k <= 8), each row held by a 16-lane
-// group with NU units per lane, so that all 64 lanes of a wave carry units
-// (one row per wave left 16 of its lanes idle on 48-unit rows) and a
+// 48 units per row): workgroup (x, t) takes rows 4Rx .. 4Rx + 4R - 1 for
+// every slot of token t, wave s for slot s (top_k <= 8), each 16-lane group
+// holding R rows with NU units per lane, so that all 64 lanes of a wave carry
+// units (one row per wave left 16 of its lanes idle on 48-unit rows) and a
 // workgroup runs eight waves of a few loads each rather than one wave of
-// every slot's loads.  A lane issues its activation fragments (the slot's own
+// every slot's loads.  Every workgroup reads the activation rows of all its
+// slots, so R = 2 halves those reads against one row per group (IQ4_XS
+// 4096 x 1536: 8.63 -> 8.40 us; four rows per group, 9.10 us, leave too few
+// waves).  A lane issues its activation fragments (the slot's own
 // row when x is per slot) and then its weight loads; the 16-lane sums of the
 // slots meet in LDS and the route-weighted sum is taken over the valid slots
 // in slot order, as k_moe_combine takes it.
-template <int F, int NU>
+template <int F, int NU, int R>
 __global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
-  constexpr int RPW = 4;  // rows per workgroup: four 16-lane groups
+  constexpr int RPW = 4 * R;  // rows per workgroup: four 16-lane groups of R rows
   __shared__ float s_part[8][RPW];
   __shared__ float s_w[8];
   __shared__ int s_ok[8];
@@ -936,7 +939,6 @@ __global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
   const int t = blockIdx.y;
   const int units = a.units;
   const int j = lane & 15, rr = lane >> 4;
-  const int row = (int)blockIdx.x * RPW + rr;
   const int s = min(wave, a.top_k - 1);
   const int sl = t * a.top_k + s;
   const int e = a.ids[sl];
@@ -948,24 +950,40 @@ __global__ __launch_bounds__(512) void k_moe_comb16(MoeLaunch a) {
 #pragma unroll
   for (int q = 0; q < NU; ++q) load_xo<F>(gx, xr, min(j + 16 * q, units - 1), xf[q]);
   __builtin_amdgcn_sched_barrier(0);
-  const uint8_t* wr = a.w + ((int64_t)(valid ? e : 0) * a.n_rows + min(row, a.n_rows - 1)) * a.row_bytes;
-  RawS<F> cur[NU];
+  // row r of group rr is RPW * x + 4 r + rr: the four groups of a wave read
+  // four consecutive rows
+  const uint8_t* wr[R];
 #pragma unroll
-  for (int q = 0; q < NU; ++q) load_unit_s(wr, min(j + 16 * q, units - 1), lane, cur[q]);
+  for (int r = 0; r < R; ++r)
+    wr[r] = a.w + ((int64_t)(valid ? e : 0) * a.n_rows + min((int)blockIdx.x * RPW + 4 * r + rr, a.n_rows - 1)) *
+                      a.row_bytes;
+  RawS<F> cur[R][NU];
+#pragma unroll
+  for (int q = 0; q < NU; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_unit_s(wr[r], min(j + 16 * q, units - 1), lane, cur[r][q]);
   __builtin_amdgcn_sched_barrier(0);
-  float acc = 0.f;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
   for (int q = 0; q < NU; ++q) {
     const int uraw = j + 16 * q;
     const bool ok = uraw < units;
     const int u = ok ? uraw : units - 1;
-    DecO<F> dec;
-    decode_own(cur[q], u, lane & 1, ok, dec);
-    const int dv = own_pass<F>(own_first(dec, xf[q].f));
-    acc = own_apply(dec, own_second(dec, xf[q].s, dv), xf[q].p, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      DecO<F> dec;
+      decode_own(cur[r][q], u, lane & 1, ok, dec);
+      const int dv = own_pass<F>(own_first(dec, xf[q].f));
+      acc[r] = own_apply(dec, own_second(dec, xf[q].s, dv), xf[q].p, acc[r]);
+    }
   }
-  const float v = lane_group_sum<16>(acc);
-  if (j == 0) s_part[wave][rr] = valid ? v : 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float v = lane_group_sum<16>(acc[r]);
+    if (j == 0) s_part[wave][4 * r + rr] = valid ? v : 0.f;
+  }
   if (lane == 0) {
     s_w[wave] = rw;
     s_ok[wave] = valid;
@@ -1133,17 +1151,22 @@ hipError_t launch_moe_mx_dots(const MoeLaunch& a, int tm, hipStream_t st) {
 static int g_moe_row16 = 0;  // tuning: 0 16-lane row groups on short rows, 1 never
 void set_moe_row16(int v) { g_moe_row16 = v; }
 
-template <int F>
-static hipError_t run_comb16(const MoeLaunch& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.n_rows + 3) / 4), (unsigned)a.n_tok);
+template <int F, int R>
+static hipError_t run_comb16_r(const MoeLaunch& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n_rows + 4 * R - 1) / (4 * R)), (unsigned)a.n_tok);
   switch ((a.units + 15) / 16) {
-    case 1: hipLaunchKernelGGL((k_moe_comb16<F, 1>), grid, dim3(512), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_moe_comb16<F, 2>), grid, dim3(512), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_moe_comb16<F, 3>), grid, dim3(512), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_moe_comb16<F, 4>), grid, dim3(512), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_moe_comb16<F, 1, R>), grid, dim3(512), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_moe_comb16<F, 2, R>), grid, dim3(512), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_moe_comb16<F, 3, R>), grid, dim3(512), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_moe_comb16<F, 4, R>), grid, dim3(512), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int F>
+static hipError_t run_comb16(const MoeLaunch& a, hipStream_t st) {
+  return run_comb16_r<F, 2>(a, st);
 }
 
 template <int F, int NU, int R>
