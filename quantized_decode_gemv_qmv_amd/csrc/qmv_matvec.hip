@@ -406,10 +406,11 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(1, OCC
   // own loads have arrived rather than when the compiler's interleaving
   // first needs a later one.  At one token (q4_K 14336 x 4096 7.78 -> 7.60
   // us, Q8_0 4096 x 4096 5.15 -> 4.96, the Q8_0 head 133.0 -> 126.0) and for
-  // q6_K at two (14.2 -> 13.9); elsewhere it was slower on some GPUs (q6_K
-  // at four tokens 15.7 -> 16.7 us, the two-token quantizing launch 11.6 ->
-  // 12.1, q4_K at two and four tokens faster on one GPU and not on another).
-  constexpr bool in_order = (TM == 1 && !QX) || (F == FQ6_K && TM == 2);
+  // q4_K, IQ4_XS and q6_K at two (q4_K 8.37 -> 8.05 on two of three GPUs,
+  // 8.68 -> 8.83 on the third; q6_K 14.2 -> 13.9).  Elsewhere it was slower:
+  // q6_K at four tokens 15.7 -> 16.7 us, Q8_0 rows of 14336 weights at two
+  // 13.41 -> 13.67, the quantizing launch (two tokens 11.6 -> 12.1).
+  constexpr bool in_order = !QX && (TM == 1 || (TM == 2 && (F == FQ4_K || F == FIQ4_XS || F == FQ6_K)));
   RawS<F> cur[R][NU];
 #pragma unroll
   for (int q = 0; q < NU; ++q) {
