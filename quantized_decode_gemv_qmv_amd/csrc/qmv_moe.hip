@@ -1287,7 +1287,11 @@ static bool moe_slots_on_matrix_cores(const MoeLaunch& a) {
 }
 template <int F>
 static hipError_t run_moe_any(const MoeLaunch& a, hipStream_t st) {
-  const int few_slot_max = a.x_per_slot ? 8 : F == FQ8_0 ? 64 : 20;
+  // per-slot inputs: the few-slot kernel up to 8 tokens, and up to 12 on
+  // IQ4_XS rows of 48 blocks, whose two-row 16-lane groups beat the grouped
+  // vector kernel there (4096 x 1536 down at 9 / 12 / 14 / 16 tokens: 48.4 /
+  // 60.0 / 68.7 / 75.9 against 52.7 / 63.7 / 68.7 / 75.1 us)
+  const int few_slot_max = a.x_per_slot ? (F == FIQ4_XS && a.units == 48 ? 12 : 8) : F == FQ8_0 ? 64 : 20;
   if (g_moe_kernel == 3 || (g_moe_kernel == 0 && a.n_tok <= few_slot_max))
     return run_moe_flat_fmt<F>(a, st);
   const bool mx = g_moe_kernel == 2 || (g_moe_kernel == 0 && moe_slots_on_matrix_cores<F>(a));

@@ -52,7 +52,7 @@ def _ws(qmv, n_rows, k, t):
                        dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("t", [1, 6, 16, 20, 64])
+@pytest.mark.parametrize("t", [1, 6, 10, 16, 20, 64])
 def test_moe_workload(experts, t, moe_kernel):
     qmv = need_gpu()
     gu, dn = experts
